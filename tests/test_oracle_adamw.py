@@ -1,0 +1,215 @@
+"""Pins for the oracle's AdamW body and its FlashAdamW step (page
+"code/flashsim/flash_adamw_sim.py", FlashAdamWSim.step = Alg. 4).
+
+* The update alone (fp32 states) is pinned to torch.optim.AdamW, an
+  independent library implementation of decoupled-weight-decay AdamW with bias
+  correction (its operation order differs, so within 1e-6 relative).
+* The declared folding of the bias corrections is pinned to the pages' literal
+  order: identical m and v, the parameter within a few ulps of the update.
+* Step 1 from a zero state has a closed form (m = (1-b1) g, v = (1-b2) g^2,
+  theta1 = theta0 (1 - lr wd) - lr g / (|g| + eps)).
+* With a 32-bit master the split is lossless, so K steps equal an fp32-master
+  run through the (separately pinned) codec; with a 24-bit master each step
+  equals that run teacher-forced from the rebuilt master.
+* The OpenMP slice driver equals the per-tensor step bit for bit.
+The values of a long free-running trajectory have no independent pin beyond
+this composition (parity unpinned for the trajectory itself)."""
+import numpy as np
+import pytest
+import torch
+
+HP = dict(lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01)
+
+
+def _bf16_bits(x32: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("literal", [False, True])
+def test_update_matches_torch_adamw(orc, literal):
+    rng = np.random.default_rng(0)
+    n, steps = 1 << 14, 10
+    theta = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    p = torch.nn.Parameter(torch.from_numpy(theta.copy()))
+    opt = torch.optim.AdamW([p], lr=HP["lr"], betas=HP["betas"], eps=HP["eps"],
+                            weight_decay=HP["weight_decay"], foreach=False, fused=False)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    b1, b2 = HP["betas"]
+    for t in range(1, steps + 1):
+        g = (rng.standard_normal(n) * 1e-3 * np.exp(rng.standard_normal())).astype(np.float32)
+        # teacher forcing: torch starts every step from the oracle's state
+        with torch.no_grad():
+            p.copy_(torch.from_numpy(theta))
+        if t > 1:
+            opt.state[p]["exp_avg"].copy_(torch.from_numpy(m))
+            opt.state[p]["exp_avg_sq"].copy_(torch.from_numpy(v))
+        p.grad = torch.from_numpy(g.copy())
+        opt.step()
+        # torch evaluates m by lerp and v by addcmul: the two orders differ by
+        # ulps of the terms, so tolerances scale with the terms' magnitudes
+        m_terms = b1 * np.abs(m) + (1 - b1) * np.abs(g)
+        th_terms = np.abs(theta) + HP["lr"] * 1.01
+        hp = orc.hparams(**HP, step=t, literal_order=literal)
+        theta, m, v = orc.adamw_update(theta, m, v, g, hp)
+        st = opt.state[p]
+        assert (np.abs(theta - p.detach().numpy()) <= 1e-6 * th_terms).all()
+        assert (np.abs(m - st["exp_avg"].numpy()) <= 1e-6 * m_terms).all()
+        assert np.allclose(v, st["exp_avg_sq"].numpy(), rtol=1e-6, atol=0)
+
+
+def test_folded_equals_literal_to_a_few_ulps(orc):
+    rng = np.random.default_rng(1)
+    n = 1 << 16
+    theta = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    v = ((rng.standard_normal(n) * 1e-3) ** 2).astype(np.float32)
+    g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    for t in (1, 2, 10, 1000):
+        a = orc.adamw_update(theta, m, v, g, orc.hparams(**HP, step=t))
+        b = orc.adamw_update(theta, m, v, g, orc.hparams(**HP, step=t, literal_order=True))
+        assert (a[1] == b[1]).all() and (a[2] == b[2]).all()
+        upd = np.abs(theta * np.float32(1 - HP["lr"] * HP["weight_decay"]) - a[0])
+        tol = 4 * np.spacing(upd) + np.spacing(np.abs(a[0]))
+        assert (np.abs(a[0] - b[0]) <= tol).all()
+
+
+@pytest.mark.parametrize("master_bits", [24, 32])
+def test_step1_closed_form(orc, master_bits):
+    rng = np.random.default_rng(2)
+    n = 4096 + 13
+    p0 = _bf16_bits((rng.standard_normal(n) * 0.02).astype(np.float32))
+    g = _bf16_bits((rng.standard_normal(n) * 1e-3).astype(np.float32))
+    st = orc.State.zeros_like_param(p0, master_bits)
+    orc.adamw_step(st, g, orc.hparams(**HP, step=1, master_bits=master_bits))
+    gf = _bits_to_f32(g).astype(np.float64)
+    th0 = _bits_to_f32(p0).astype(np.float64)
+    lr, wd, eps = HP["lr"], HP["weight_decay"], HP["eps"]
+    want = th0 * (1 - lr * wd) - lr * gf / (np.abs(gf) + eps)
+    got = orc.reconstruct(st.param, st.rho, master_bits).astype(np.float64)
+    # float32 evaluation error is relative to the terms theta0 and lr (they
+    # may cancel); the 24-bit master adds up to 128 units in the last fp32
+    # place of the result (2^-16 relative) from the int8 correction
+    tol = 1e-6 * (np.abs(th0) + lr)
+    if master_bits == 24:
+        tol = tol + 2.0 ** -15 * np.abs(want)
+    assert (np.abs(got - want) <= tol).all()
+    # moments at step 1 are exact products of the gradient
+    c1 = np.float32(1 - HP["betas"][0])
+    c2 = np.float32(1 - HP["betas"][1])
+    g32 = _bits_to_f32(g)
+    m1 = (c1 * g32).astype(np.float32)
+    v1 = ((c2 * g32).astype(np.float32) * g32).astype(np.float32)
+    pad = lambda a: np.concatenate([a, np.zeros((-a.size) % 32, np.float32)]).reshape(-1, 32)
+    assert (st.m_scales == np.abs(pad(m1)).max(1).astype(np.float16).view(np.uint16)).all()
+    assert (st.v_scales == np.sqrt(pad(v1)).max(1).astype(np.float16).view(np.uint16)).all()
+    qm, _ = orc.quantize(m1, orc.MOMENTUM)
+    qv, _ = orc.quantize(v1, orc.VARIANCE)
+    assert (st.m_codes == qm).all() and (st.v_codes == qv).all()
+
+
+def _fp32_master_run(orc, theta, grads, companded, steps):
+    """The step as composition: fp32 master kept outside, states through the
+    codec each step."""
+    n = theta.size
+    ms, vs = (orc.MOMENTUM, orc.VARIANCE) if companded else (orc.MOMENTUM_LINEAR, orc.VARIANCE_LINEAR)
+    mq, msc = np.zeros(n, np.int8), np.zeros((n + 31) // 32, np.uint16)
+    vq, vsc = np.zeros(n, np.uint8), np.zeros((n + 31) // 32, np.uint16)
+    out = []
+    for t in range(1, steps + 1):
+        m = orc.dequantize(mq, msc, ms)
+        v = orc.dequantize(vq, vsc, vs)
+        theta, m, v = orc.adamw_update(theta, m, v, _bits_to_f32(grads[t - 1]),
+                                       orc.hparams(**HP, step=t))
+        mq, msc = orc.quantize(m, ms)
+        vq, vsc = orc.quantize(v, vs)
+        out.append((theta.copy(), mq.copy(), msc.copy(), vq.copy(), vsc.copy()))
+    return out
+
+
+@pytest.mark.parametrize("companded", [True, False])
+def test_32bit_master_equals_fp32_master(orc, companded):
+    rng = np.random.default_rng(3)
+    n, steps = 3000 + 7, 6
+    p0 = _bf16_bits((rng.standard_normal(n) * 0.02).astype(np.float32))
+    grads = [_bf16_bits((rng.standard_normal(n) * 1e-3).astype(np.float32)) for _ in range(steps)]
+    ref = _fp32_master_run(orc, _bits_to_f32(p0), grads, companded, steps)
+    st = orc.State.zeros_like_param(p0, 32)
+    for t in range(1, steps + 1):
+        orc.adamw_step(st, grads[t - 1], orc.hparams(**HP, step=t, master_bits=32,
+                                                      companded=companded))
+        th, mq, msc, vq, vsc = ref[t - 1]
+        assert (orc.reconstruct(st.param, st.rho, 32).view(np.uint32) == th.view(np.uint32)).all()
+        assert (st.m_codes == mq).all() and (st.m_scales == msc).all()
+        assert (st.v_codes == vq).all() and (st.v_scales == vsc).all()
+
+
+def test_24bit_step_is_teacher_forced_composition(orc):
+    rng = np.random.default_rng(4)
+    n, steps = 2048 + 31, 5
+    p0 = _bf16_bits((rng.standard_normal(n) * 0.02).astype(np.float32))
+    st = orc.State.zeros_like_param(p0, 24)
+    for t in range(1, steps + 1):
+        g = _bf16_bits((rng.standard_normal(n) * 1e-3).astype(np.float32))
+        theta = orc.reconstruct(st.param, st.rho, 24)
+        m = orc.dequantize(st.m_codes, st.m_scales, orc.MOMENTUM)
+        v = orc.dequantize(st.v_codes, st.v_scales, orc.VARIANCE)
+        th1, m1, v1 = orc.adamw_update(theta, m, v, _bits_to_f32(g), orc.hparams(**HP, step=t))
+        orc.adamw_step(st, g, orc.hparams(**HP, step=t, master_bits=24))
+        hi, rho = orc.split(th1, 24)
+        assert (st.param == hi).all() and (st.rho == rho).all()
+        qm, sm = orc.quantize(m1, orc.MOMENTUM)
+        qv, sv = orc.quantize(v1, orc.VARIANCE)
+        assert (st.m_codes == qm).all() and (st.m_scales == sm).all()
+        assert (st.v_codes == qv).all() and (st.v_scales == sv).all()
+
+
+def test_unquantized_states_and_plain_param(orc):
+    """quantize_states=False keeps fp32 moments (the weight-splitting-only
+    ablation); master_bits=None rounds the updated parameter to bf16 with
+    torch's cast."""
+    rng = np.random.default_rng(5)
+    n = 1000
+    p0 = _bf16_bits((rng.standard_normal(n) * 0.02).astype(np.float32))
+    g = _bf16_bits((rng.standard_normal(n) * 1e-3).astype(np.float32))
+    st = orc.State.zeros_like_param(p0, None, quantize_states=False)
+    orc.adamw_step(st, g, orc.hparams(**HP, step=1, master_bits=None, quantize_states=False))
+    th, m, v = orc.adamw_update(_bits_to_f32(p0), np.zeros(n), np.zeros(n), _bits_to_f32(g),
+                                orc.hparams(**HP, step=1))
+    assert (st.m_codes == m).all() and (st.v_codes == v).all()
+    assert (st.param == _bf16_bits(th)).all()
+
+
+def test_list_driver_equals_per_tensor_steps(orc):
+    rng = np.random.default_rng(6)
+    sizes = [1, 31, 32, 33, 4096, 70001, 32768 * 2 + 5]
+    for mb in (24, 32):
+        states_a, states_b, grads = [], [], []
+        for n in sizes:
+            p0 = _bf16_bits((rng.standard_normal(n) * 0.02).astype(np.float32))
+            s = orc.State.zeros_like_param(p0, mb)
+            states_a.append(s)
+            states_b.append(s.copy())
+            grads.append(_bf16_bits((rng.standard_normal(n) * 1e-3).astype(np.float32)))
+        for t in (1, 2, 3):
+            hp = orc.hparams(**HP, step=t, master_bits=mb)
+            for s, g in zip(states_a, grads):
+                orc.adamw_step(s, g, hp)
+            used = orc.adamw_step_list(states_b, grads, hp, threads=4)
+            assert used >= 1
+        for a, b in zip(states_a, states_b):
+            for f in ("param", "rho", "m_codes", "m_scales", "v_codes", "v_scales"):
+                assert (getattr(a, f) == getattr(b, f)).all(), f
+
+
+def test_bad_arguments_rejected(orc):
+    p = np.zeros(8, np.uint16)
+    st = orc.State.zeros_like_param(p, 24)
+    with pytest.raises(ValueError):
+        orc.adamw_step(st, p, orc.hparams(step=0))
+    with pytest.raises(ValueError):
+        orc.adamw_step(st, p, orc.hparams(step=1, master_bits=16))
