@@ -1,0 +1,193 @@
+"""Benchmark of the fused FlashAdamW step on one MI355X.
+
+Workload: the 8,030,257,152-parameter decoder-shaped list (290 bf16 tensors:
+embedding and LM head 128256x4096, 32 layers of q/o 4096x4096, k/v
+4096x1024, gate/up 4096x14336, down 14336x4096, two norms of 4096), 24-bit
+master (int8 rho), companded int8/uint8 states with fp16 group-32 scales;
+one multi-tensor launch per step.  Inputs are synthetic and resident in HBM
+before timing starts (bf16 weights ~ N(0, 0.02^2); one bf16 gradient set
+N(0, 1e-3^2) times a per-tensor lognormal factor, reused by every step).
+
+Prints one JSON line: Gparam/s over the K timed steps, the roofline of the
+step kernel (algorithmic 12.25 B/param against 8 TB/s), and the oracle's
+throughput on host cores for a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+from bit_companded_adam_amd import flashopt as F  # noqa: E402
+from bit_companded_adam_amd import workloads as W  # noqa: E402
+
+METRIC = "FlashAdamW step Gparam/s and % of HBM roofline (12.25 B/param), 1 GPU"
+PEAK_HBM_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "bit_companded_adam_amd", "csrc", "flashopt_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "adamw_step_8b_traffic.json")
+
+
+def bytes_per_param(master_bits: int) -> float:
+    """Algorithmic HBM bytes per parameter per step: read bf16 param 2, bf16
+    grad 2, rho 1|2, m code 1, v code 1, two fp16 scales per 32 (2/32 each);
+    write all of them except the grad."""
+    rho = 1 if master_bits == 24 else 2
+    read = 2 + 2 + rho + 1 + 1 + 2 * 2 / 32
+    write = 2 + rho + 1 + 1 + 2 * 2 / 32
+    return read + write
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_per_launch():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha") != kernel_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def build_workload(master_bits: int, companded: bool):
+    shapes = W.decoder_8b_shapes()
+    params = [W.init_param(W.numel(s), device="cuda", seed=W.PARAM_SEED + i)
+              for i, (_, s) in enumerate(shapes)]
+    factors = W.grad_factors(len(shapes)).tolist()
+    grads = [W.make_grad(W.numel(s), 1, device="cuda", stream_id=i, factor=factors[i])
+             for i, (_, s) in enumerate(shapes)]
+    opt = F.FlashAdamW(params, master_bits=master_bits, companded=companded, **W.HP_DEFAULT)
+    return opt, grads
+
+
+def time_steps(opt, grads, steps: int, warmup: int):
+    for _ in range(warmup):
+        opt.step(grads)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        opt.step(grads, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in evs]          # ms, one launch each
+    return wall, per
+
+
+def cpu_baseline(master_bits: int, target_elems: int, threads: int):
+    """The oracle as it is, on host threads, over a bounded sample of the
+    workload: the first target_elems / 32 elements of each of 32 evenly spaced
+    tensors of the 8.0B list (same distributions), step 2 after an untimed
+    step 1."""
+    import oracle
+    oracle.build(force=False)
+    shapes = W.decoder_8b_shapes()
+    pick = np.linspace(0, len(shapes) - 1, 32).astype(int)
+    per = target_elems // 32
+    factors = W.grad_factors(len(shapes)).numpy()
+    states, g1, g2 = [], [], []
+    for k, i in enumerate(pick):
+        n = min(per, W.numel(shapes[i][1]))
+        p = W.init_param(n, seed=W.PARAM_SEED + int(i)).view(torch.int16).numpy().view(np.uint16)
+        states.append(oracle.State.zeros_like_param(p, master_bits))
+        for lst, t in ((g1, 1), (g2, 2)):
+            lst.append(W.make_grad(n, t, stream_id=int(i), factor=float(factors[i]))
+                       .view(torch.int16).numpy().view(np.uint16))
+    hp = dict(lr=W.HP_DEFAULT["lr"], betas=W.HP_DEFAULT["betas"], eps=W.HP_DEFAULT["eps"],
+              weight_decay=W.HP_DEFAULT["weight_decay"], master_bits=master_bits)
+    oracle.adamw_step_list(states, g1, oracle.hparams(step=1, **hp), threads)
+    n_total = sum(s.param.size for s in states)
+    t0 = time.perf_counter()
+    used = oracle.adamw_step_list(states, g2, oracle.hparams(step=2, **hp), threads)
+    dt = time.perf_counter() - t0
+    return {"value": n_total / dt / 1e9, "unit": "Gparam/s", "cores": used, "kind": "oracle",
+            "sample": f"{n_total} params: first {per} elements of 32 of the 290 tensors "
+                      f"of the 8.0B list, one step (step 2), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--master-bits", type=int, default=24, choices=(24, 32))
+    ap.add_argument("--linear", action="store_true", help="linear (non-companded) ablation")
+    ap.add_argument("--cpu-elems", type=int, default=1 << 27,
+                    help="oracle sample size for the CPU baseline (0: skip)")
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the step needs no communication, and this "
+              "build measures one GPU's share (--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    mb, comp = args.master_bits, not args.linear
+    opt, grads = build_workload(mb, comp)
+    n = sum(s.param.numel() for s in opt.states)
+    print(f"# workload ready: {len(opt.states)} tensors, {n} params, "
+          f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated", file=sys.stderr, flush=True)
+
+    wall, per = time_steps(opt, grads, args.steps, args.warmup)
+    ms_step = wall * 1e3 / args.steps
+    ms_launch = float(np.mean(per))
+    bpp = bytes_per_param(mb)
+    alg_bytes = bpp * n
+    achieved = alg_bytes / (ms_launch * 1e-3) / 1e9
+    print(f"# per-launch ms: mean {ms_launch:.3f} median {np.median(per):.3f} "
+          f"min {min(per):.3f} max {max(per):.3f}", file=sys.stderr, flush=True)
+    del opt, grads
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if args.cpu_elems > 0:
+        cpu = cpu_baseline(mb, args.cpu_elems, args.cpu_threads)
+
+    out = {
+        "metric": METRIC,
+        "value": n / (ms_step * 1e-3) / 1e9,
+        "unit": "Gparam/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decoder-8b-list" + ("" if comp else "-linear"),
+                   "params": n, "tensors": 290, "master_bits": mb, "companded": comp,
+                   "bytes_per_param": bpp, "launches_per_step": 1},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": traffic_per_launch() if (mb, comp) == (24, True) else None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,237 @@
+// C-ABI host layer of libflashopt.so: argument validation, the multi-tensor
+// chunk table, step scalars, and kernel launches on the caller's stream.
+// Every entry point validates everything before it enqueues anything, and no
+// C++ exception crosses the ABI.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <new>
+
+#include "flashopt.h"
+#include "flashopt_internal.h"
+
+namespace {
+
+using flashopt::DevTensor;
+using flashopt::StepScalars;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+flashopt_status hip_status(hipError_t e) { return e == hipSuccess ? FLASHOPT_OK : FLASHOPT_EHIP; }
+
+flashopt_status check_codec(const void *elems, int64_t n, unsigned spec, const void *codes,
+                            const uint16_t *scales)
+{
+    if (n < 0 || spec > 7u) return FLASHOPT_EINVAL;
+    if (n == 0) return FLASHOPT_OK;
+    if (!elems || !codes || !scales) return FLASHOPT_EINVAL;
+    if (!aligned(elems, 16) || !aligned(codes, 16) || !aligned(scales, 2)) return FLASHOPT_EALIGN;
+    return FLASHOPT_OK;
+}
+
+flashopt_status check_split(const void *master, int64_t n, int master_bits, const void *param,
+                            const void *rho)
+{
+    if (n < 0 || (master_bits != 24 && master_bits != 32)) return FLASHOPT_EINVAL;
+    if (n == 0) return FLASHOPT_OK;
+    if (!master || !param || !rho) return FLASHOPT_EINVAL;
+    if (!aligned(master, 16) || !aligned(param, 16) || !aligned(rho, 16)) return FLASHOPT_EALIGN;
+    return FLASHOPT_OK;
+}
+
+// Workspace layout: [n DevTensor][n + 1 int32 chunk starts], 16-byte rounded.
+size_t workspace_bytes(int n)
+{
+    if (n <= 0) return 0;
+    size_t b = sizeof(DevTensor) * static_cast<size_t>(n) + sizeof(int32_t) * (static_cast<size_t>(n) + 1);
+    return (b + 15) & ~static_cast<size_t>(15);
+}
+
+// Pinned host staging for the chunk table: a small ring per device, so the
+// host can run a few steps ahead of the GPU.  A slot is reused only after
+// the copy that last read it has completed.
+constexpr int kRingSlots = 4;
+constexpr int kMaxDevices = 64;
+
+struct Slot {
+    void *host = nullptr;
+    size_t cap = 0;
+    hipEvent_t done = nullptr;
+    bool pending = false;
+};
+
+struct Ring {
+    Slot slot[kRingSlots];
+    int next = 0;
+};
+
+std::mutex g_ring_mutex;
+Ring g_rings[kMaxDevices];
+
+}  // namespace
+
+extern "C" {
+
+int flashopt_abi_version(void) { return FLASHOPT_ABI_VERSION; }
+
+const char *flashopt_status_str(flashopt_status s)
+{
+    switch (s) {
+    case FLASHOPT_OK: return "FLASHOPT_OK";
+    case FLASHOPT_EINVAL: return "FLASHOPT_EINVAL: invalid argument";
+    case FLASHOPT_EALIGN: return "FLASHOPT_EALIGN: buffer not aligned (16 B streams, 2 B scales)";
+    case FLASHOPT_EWORKSPACE: return "FLASHOPT_EWORKSPACE: workspace missing or too small";
+    case FLASHOPT_EHIP: return "FLASHOPT_EHIP: HIP runtime error on enqueue";
+    }
+    return "FLASHOPT_UNKNOWN_STATUS";
+}
+
+flashopt_status flashopt_quantize(const float *x, int64_t n, unsigned spec, void *codes,
+                                  uint16_t *scales, void *stream)
+{
+    flashopt_status st = check_codec(x, n, spec, codes, scales);
+    if (st != FLASHOPT_OK || n == 0) return st;
+    return hip_status(flashopt::launch_quantize(x, n, spec, codes, scales,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+flashopt_status flashopt_dequantize(const void *codes, const uint16_t *scales, int64_t n,
+                                    unsigned spec, float *out, void *stream)
+{
+    flashopt_status st = check_codec(out, n, spec, codes, scales);
+    if (st != FLASHOPT_OK || n == 0) return st;
+    return hip_status(flashopt::launch_dequantize(codes, scales, n, spec, out,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+flashopt_status flashopt_split(const float *master, int64_t n, int master_bits,
+                               uint16_t *param_bf16, void *rho, void *stream)
+{
+    flashopt_status st = check_split(master, n, master_bits, param_bf16, rho);
+    if (st != FLASHOPT_OK || n == 0) return st;
+    return hip_status(flashopt::launch_split(master, n, master_bits, param_bf16, rho,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+flashopt_status flashopt_reconstruct(const uint16_t *param_bf16, const void *rho, int64_t n,
+                                     int master_bits, float *master, void *stream)
+{
+    flashopt_status st = check_split(master, n, master_bits, param_bf16, rho);
+    if (st != FLASHOPT_OK || n == 0) return st;
+    return hip_status(flashopt::launch_reconstruct(param_bf16, rho, n, master_bits, master,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
+size_t flashopt_adamw_workspace_bytes(const flashopt_tensor *tensors, int n_tensors)
+{
+    (void)tensors;
+    return workspace_bytes(n_tensors);
+}
+
+flashopt_status flashopt_adamw_step(const flashopt_tensor *tensors, int n_tensors,
+                                    const flashopt_adamw_args *a, void *workspace,
+                                    size_t ws_bytes, void *stream)
+{
+    // ---- hyper-parameters
+    if (n_tensors < 0 || !a) return FLASHOPT_EINVAL;
+    if (n_tensors > 0 && !tensors) return FLASHOPT_EINVAL;
+    if (a->master_bits != 24 && a->master_bits != 32) return FLASHOPT_EINVAL;
+    if (a->companded != 0 && a->companded != 1) return FLASHOPT_EINVAL;
+    if (a->step < 1) return FLASHOPT_EINVAL;
+    if (!(a->lr >= 0.0) || !std::isfinite(a->lr)) return FLASHOPT_EINVAL;
+    if (!(a->beta1 >= 0.0 && a->beta1 < 1.0) || !(a->beta2 >= 0.0 && a->beta2 < 1.0)) return FLASHOPT_EINVAL;
+    if (!(a->eps >= 0.0) || !std::isfinite(a->eps)) return FLASHOPT_EINVAL;
+    if (!std::isfinite(a->weight_decay)) return FLASHOPT_EINVAL;
+
+    // ---- tensors and the chunk count
+    int64_t total = 0;
+    for (int i = 0; i < n_tensors; ++i) {
+        const flashopt_tensor &t = tensors[i];
+        if (t.numel < 0) return FLASHOPT_EINVAL;
+        if (t.numel == 0) continue;
+        if (!t.param || !t.grad || !t.rho || !t.m_codes || !t.m_scales || !t.v_codes || !t.v_scales)
+            return FLASHOPT_EINVAL;
+        if (!aligned(t.param, 16) || !aligned(t.grad, 16) || !aligned(t.rho, 16) ||
+            !aligned(t.m_codes, 16) || !aligned(t.v_codes, 16) || !aligned(t.m_scales, 2) ||
+            !aligned(t.v_scales, 2))
+            return FLASHOPT_EALIGN;
+        total += (t.numel + flashopt::kChunkElems - 1) / flashopt::kChunkElems;
+        if (total > INT32_MAX) return FLASHOPT_EINVAL;
+    }
+    if (total == 0) return FLASHOPT_OK;
+    const size_t need = workspace_bytes(n_tensors);
+    if (!workspace || ws_bytes < need) return FLASHOPT_EWORKSPACE;
+    if (!aligned(workspace, 16)) return FLASHOPT_EALIGN;
+
+    // ---- step scalars: double on the host, rounded once to fp32
+    StepScalars sc;
+    const double t = static_cast<double>(a->step);
+    const double bc1 = 1.0 - std::pow(a->beta1, t);
+    const double bc2 = 1.0 - std::pow(a->beta2, t);
+    sc.cwd = static_cast<float>(1.0 - a->lr * a->weight_decay);
+    sc.b1 = static_cast<float>(a->beta1);
+    sc.c1 = static_cast<float>(1.0 - a->beta1);
+    sc.b2 = static_cast<float>(a->beta2);
+    sc.c2 = static_cast<float>(1.0 - a->beta2);
+    sc.alpha = static_cast<float>(a->lr / bc1);
+    sc.k2 = static_cast<float>(1.0 / std::sqrt(bc2));
+    sc.eps = static_cast<float>(a->eps);
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FLASHOPT_EHIP;
+
+    std::lock_guard<std::mutex> lock(g_ring_mutex);
+    Ring &ring = g_rings[dev];
+    Slot &slot = ring.slot[ring.next];
+    ring.next = (ring.next + 1) % kRingSlots;
+    if (slot.pending) {
+        if (hipEventSynchronize(slot.done) != hipSuccess) return FLASHOPT_EHIP;
+        slot.pending = false;
+    }
+    if (!slot.done && hipEventCreateWithFlags(&slot.done, hipEventDisableTiming) != hipSuccess)
+        return FLASHOPT_EHIP;
+    if (slot.cap < need) {
+        if (slot.host) (void)hipHostFree(slot.host);
+        slot.host = nullptr;
+        slot.cap = 0;
+        if (hipHostMalloc(&slot.host, need, hipHostMallocDefault) != hipSuccess) return FLASHOPT_EHIP;
+        slot.cap = need;
+    }
+
+    // ---- chunk table: descriptors, then chunk starts (prefix sums)
+    DevTensor *desc = static_cast<DevTensor *>(slot.host);
+    int32_t *start = reinterpret_cast<int32_t *>(desc + n_tensors);
+    int32_t acc = 0;
+    for (int i = 0; i < n_tensors; ++i) {
+        const flashopt_tensor &s = tensors[i];
+        DevTensor &d = desc[i];
+        d.param = s.param;
+        d.grad = s.grad;
+        d.rho = s.rho;
+        d.m_codes = s.m_codes;
+        d.m_scales = s.m_scales;
+        d.v_codes = s.v_codes;
+        d.v_scales = s.v_scales;
+        d.numel = s.numel;
+        start[i] = acc;
+        acc += static_cast<int32_t>((s.numel + flashopt::kChunkElems - 1) / flashopt::kChunkElems);
+    }
+    start[n_tensors] = acc;
+
+    if (hipMemcpyAsync(workspace, slot.host, need, hipMemcpyHostToDevice, st) != hipSuccess)
+        return FLASHOPT_EHIP;
+    if (hipEventRecord(slot.done, st) != hipSuccess) return FLASHOPT_EHIP;
+    slot.pending = true;
+
+    const DevTensor *d_desc = static_cast<const DevTensor *>(workspace);
+    const int32_t *d_start = reinterpret_cast<const int32_t *>(d_desc + n_tensors);
+    return hip_status(flashopt::launch_adamw_step(d_desc, d_start, n_tensors, acc, sc,
+                                                  a->master_bits, a->companded != 0, st));
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Internal declarations shared by the kernels (flashopt_kernels.hip) and the
+// C-ABI host layer (flashopt_api.cpp) of libflashopt.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flashopt {
+
+// Work decomposition: one lane owns 16 consecutive elements, a lane pair
+// owns one 32-element quantization group, one wavefront (64 lanes) owns one
+// 1024-element chunk, and a 256-thread workgroup runs four wavefronts.
+constexpr int kLaneElems = 16;
+constexpr int kWaveLanes = 64;
+constexpr int kChunkElems = kLaneElems * kWaveLanes;   // 1024
+constexpr int kBlockThreads = 256;
+constexpr int kGroup = 32;
+
+// Per-tensor descriptor of the multi-tensor step, staged in the workspace.
+struct DevTensor {
+    uint16_t *param;
+    const uint16_t *grad;
+    void *rho;
+    int8_t *m_codes;
+    uint16_t *m_scales;
+    uint8_t *v_codes;
+    uint16_t *v_scales;
+    int64_t numel;
+};
+static_assert(sizeof(DevTensor) == 64, "descriptor layout");
+
+// fp32 scalars of one step, formed in double on the host and rounded once.
+struct StepScalars {
+    float cwd;    // 1 - lr * wd
+    float b1;     // beta1
+    float c1;     // 1 - beta1
+    float b2;     // beta2
+    float c2;     // 1 - beta2
+    float alpha;  // lr / (1 - beta1^t)
+    float k2;     // 1 / sqrt(1 - beta2^t)
+    float eps;
+};
+
+hipError_t launch_quantize(const float *x, int64_t n, unsigned spec, void *codes,
+                           uint16_t *scales, hipStream_t stream);
+hipError_t launch_dequantize(const void *codes, const uint16_t *scales, int64_t n,
+                             unsigned spec, float *out, hipStream_t stream);
+hipError_t launch_split(const float *master, int64_t n, int master_bits,
+                        uint16_t *param, void *rho, hipStream_t stream);
+hipError_t launch_reconstruct(const uint16_t *param, const void *rho, int64_t n,
+                              int master_bits, float *master, hipStream_t stream);
+// tensors / chunk_start are device pointers into the workspace;
+// chunk_start has n_tensors + 1 entries.
+hipError_t launch_adamw_step(const DevTensor *tensors, const int32_t *chunk_start,
+                             int n_tensors, int32_t total_chunks,
+                             const StepScalars &sc, int master_bits, bool companded,
+                             hipStream_t stream);
+
+}  // namespace flashopt

@@ -1,0 +1,241 @@
+"""Thin ctypes binding of libflashopt.so with the C entry points' names.
+
+Argument marshalling only: every computation runs in the HIP kernels of the
+library.  Tensors are torch CUDA (HIP) tensors; outputs are allocated with
+torch when not given.  Work goes to the current torch stream unless a
+stream is passed.  A missing library raises at first use -- there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflashopt.so")
+
+FLASHOPT_OK, FLASHOPT_EINVAL, FLASHOPT_EALIGN, FLASHOPT_EWORKSPACE, FLASHOPT_EHIP = range(5)
+Q_SIGNED, Q_SQRT, Q_SOFTSIGN = 1, 2, 4
+SPEC_MOMENTUM = Q_SIGNED | Q_SOFTSIGN
+SPEC_VARIANCE = Q_SQRT
+SPEC_MOMENTUM_LINEAR = Q_SIGNED
+SPEC_VARIANCE_LINEAR = 0
+GROUP = 32
+CHUNK_ELEMS = 1024
+
+EXPORTS = ("flashopt_quantize", "flashopt_dequantize", "flashopt_split",
+           "flashopt_reconstruct", "flashopt_adamw_workspace_bytes",
+           "flashopt_adamw_step", "flashopt_status_str", "flashopt_abi_version")
+
+
+class FlashoptError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_str(status)}")
+        self.status = status
+
+
+class flashopt_tensor(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p),
+                ("rho", ctypes.c_void_p), ("m_codes", ctypes.c_void_p),
+                ("m_scales", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+                ("v_scales", ctypes.c_void_p), ("numel", ctypes.c_int64)]
+
+
+class flashopt_adamw_args(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double),
+                ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
+                ("weight_decay", ctypes.c_double), ("step", ctypes.c_int64),
+                ("master_bits", ctypes.c_int), ("companded", ctypes.c_int)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i64, u, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint, ctypes.c_int
+        L.flashopt_quantize.argtypes = [vp, i64, u, vp, vp, vp]
+        L.flashopt_dequantize.argtypes = [vp, vp, i64, u, vp, vp]
+        L.flashopt_split.argtypes = [vp, i64, i, vp, vp, vp]
+        L.flashopt_reconstruct.argtypes = [vp, vp, i64, i, vp, vp]
+        L.flashopt_adamw_workspace_bytes.argtypes = [ctypes.POINTER(flashopt_tensor), i]
+        L.flashopt_adamw_workspace_bytes.restype = ctypes.c_size_t
+        L.flashopt_adamw_step.argtypes = [ctypes.POINTER(flashopt_tensor), i,
+                                          ctypes.POINTER(flashopt_adamw_args), vp,
+                                          ctypes.c_size_t, vp]
+        L.flashopt_status_str.argtypes = [i]
+        L.flashopt_status_str.restype = ctypes.c_char_p
+        L.flashopt_abi_version.argtypes = []
+        for name in ("flashopt_quantize", "flashopt_dequantize", "flashopt_split",
+                     "flashopt_reconstruct", "flashopt_adamw_step"):
+            getattr(L, name).restype = i
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().flashopt_status_str(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != FLASHOPT_OK:
+        raise FlashoptError(status, where)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def n_groups(n: int) -> int:
+    return (n + GROUP - 1) // GROUP
+
+
+def flashopt_abi_version() -> int:
+    return lib().flashopt_abi_version()
+
+
+# --------------------------------------------------------------- codec
+
+def flashopt_quantize(x: torch.Tensor, spec: int, codes=None, scales=None, stream=None):
+    """Group-32 quantize x (fp32); returns (codes int8|uint8, scales fp16 as int16 bits)."""
+    n = x.numel()
+    if x.dtype != torch.float32:
+        raise ValueError("x must be float32")
+    if codes is None:
+        codes = torch.empty(n, dtype=torch.int8 if spec & Q_SIGNED else torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(n_groups(n), dtype=torch.int16, device=x.device)
+    _check(lib().flashopt_quantize(_dev(x, "x"), n, spec, _dev(codes, "codes"),
+                                   _dev(scales, "scales"), _stream(stream)), "flashopt_quantize")
+    return codes, scales
+
+
+def flashopt_dequantize(codes: torch.Tensor, scales: torch.Tensor, spec: int, out=None, stream=None):
+    n = codes.numel()
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=codes.device)
+    _check(lib().flashopt_dequantize(_dev(codes, "codes"), _dev(scales, "scales"), n, spec,
+                                     _dev(out, "out"), _stream(stream)), "flashopt_dequantize")
+    return out
+
+
+# --------------------------------------------------------------- split
+
+def rho_dtype(master_bits: int):
+    return {24: torch.int8, 32: torch.int16}[master_bits]
+
+
+def flashopt_split(master: torch.Tensor, master_bits: int, param=None, rho=None, stream=None):
+    """fp32 master -> (bf16 param, rho int8|int16)."""
+    n = master.numel()
+    if master.dtype != torch.float32:
+        raise ValueError("master must be float32")
+    if param is None:
+        param = torch.empty(n, dtype=torch.bfloat16, device=master.device)
+    if rho is None:
+        rho = torch.empty(n, dtype=rho_dtype(master_bits), device=master.device)
+    _check(lib().flashopt_split(_dev(master, "master"), n, master_bits, _dev(param, "param"),
+                                _dev(rho, "rho"), _stream(stream)), "flashopt_split")
+    return param, rho
+
+
+def flashopt_reconstruct(param: torch.Tensor, rho: torch.Tensor, master_bits: int, out=None,
+                         stream=None):
+    n = param.numel()
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=param.device)
+    _check(lib().flashopt_reconstruct(_dev(param, "param"), _dev(rho, "rho"), n, master_bits,
+                                      _dev(out, "out"), _stream(stream)), "flashopt_reconstruct")
+    return out
+
+
+# --------------------------------------------------------------- step
+
+class TensorState:
+    """Device state of one parameter tensor: bf16 param (updated in place),
+    rho, momentum and variance codes and fp16 scales.  Fresh state is zero."""
+
+    def __init__(self, param: torch.Tensor, master_bits: int = 24):
+        if param.dtype != torch.bfloat16 or not param.is_contiguous():
+            raise ValueError("param must be a contiguous bf16 tensor")
+        n, dev = param.numel(), param.device
+        self.param = param
+        self.rho = torch.zeros(n, dtype=rho_dtype(master_bits), device=dev)
+        self.m_codes = torch.zeros(n, dtype=torch.int8, device=dev)
+        self.m_scales = torch.zeros(n_groups(n), dtype=torch.int16, device=dev)
+        self.v_codes = torch.zeros(n, dtype=torch.uint8, device=dev)
+        self.v_scales = torch.zeros(n_groups(n), dtype=torch.int16, device=dev)
+        self.master_bits = master_bits
+
+    def descriptor(self, grad: torch.Tensor) -> flashopt_tensor:
+        if grad.dtype != torch.bfloat16 or grad.numel() != self.param.numel():
+            raise ValueError("grad must be bf16 with the parameter's size")
+        return flashopt_tensor(_dev(self.param, "param"), _dev(grad, "grad"),
+                               _dev(self.rho, "rho"), _dev(self.m_codes, "m_codes"),
+                               _dev(self.m_scales, "m_scales"), _dev(self.v_codes, "v_codes"),
+                               _dev(self.v_scales, "v_scales"), self.param.numel())
+
+
+def make_args(step: int, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0,
+              master_bits=24, companded=True) -> flashopt_adamw_args:
+    return flashopt_adamw_args(lr, betas[0], betas[1], eps, weight_decay, step,
+                               master_bits, int(companded))
+
+
+def flashopt_adamw_workspace_bytes(n_tensors: int) -> int:
+    return lib().flashopt_adamw_workspace_bytes(None, n_tensors)
+
+
+def descriptor_array(states, grads):
+    arr = (flashopt_tensor * len(states))()
+    for i, (s, g) in enumerate(zip(states, grads)):
+        arr[i] = s.descriptor(g)
+    return arr
+
+
+def flashopt_adamw_step(descriptors, args: flashopt_adamw_args, workspace: torch.Tensor,
+                        stream=None):
+    """One fused step over a ctypes array of flashopt_tensor descriptors."""
+    n = len(descriptors)
+    _check(lib().flashopt_adamw_step(descriptors, n, ctypes.byref(args), _dev(workspace, "workspace"),
+                                     workspace.numel() * workspace.element_size(), _stream(stream)),
+           "flashopt_adamw_step")
+
+
+class FlashAdamW:
+    """A list of TensorStates stepped together by one launch per step."""
+
+    def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0,
+                 master_bits=24, companded=True):
+        self.states = [TensorState(p, master_bits) for p in params]
+        self.hp = dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay,
+                       master_bits=master_bits, companded=companded)
+        dev = self.states[0].param.device if self.states else "cuda"
+        nbytes = max(16, flashopt_adamw_workspace_bytes(len(self.states)))
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.t = 0
+        self._grads = None
+        self._desc = None
+
+    def step(self, grads, stream=None):
+        self.t += 1
+        if self._grads is None or any(a is not b for a, b in zip(self._grads, grads)):
+            self._desc = descriptor_array(self.states, grads)
+            self._grads = list(grads)
+        flashopt_adamw_step(self._desc, make_args(self.t, **self.hp), self.workspace, stream)

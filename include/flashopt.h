@@ -1,0 +1,181 @@
+/*
+ * flashopt.h -- C ABI of libflashopt.so, the MI355X (gfx950) FlashAdamW step.
+ *
+ * The method is described on the pages
+ *   "code/flashsim/quantization.py"    (group-32 companded int8/uint8 state codec,
+ *                                      Alg. 2 momentum / Alg. 3 variance),
+ *   "code/flashsim/flash_adamw_sim.py" (FlashAdamWSim.step: Alg. 4, the step),
+ *   "code/gpu/equivalence.py"          (the bf16 parameter and its correction
+ *                                      bits rho, eq_ecc()).
+ *
+ * Conventions for every entry point:
+ *   - Buffer pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates or frees device memory and keeps no state between calls
+ *     except a small cache of pinned host staging buffers (see
+ *     flashopt_adamw_step).
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     default stream).  Results are visible after the stream is synchronized.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     status other than FLASHOPT_OK means nothing was launched.  Faults inside
+ *     a kernel surface at the caller's next synchronization.
+ *   - n == 0 is a no-op that returns FLASHOPT_OK (pointers may then be NULL).
+ *   - Groups of 32 elements start at element 0 of every array; a ragged last
+ *     group behaves as if padded with zeros (page "code/flashsim/quantization.py",
+ *     _grouped()).  Scale arrays hold ceil(n / 32) entries.
+ *   - fp16 and bf16 values are passed as their uint16_t bit patterns.
+ *   - Non-finite inputs are outside the contract; the results stay defined
+ *     (NaN codes are 0) but are not part of the parity guarantee.
+ *   - Input and output buffers must not overlap, except where a call says it
+ *     updates a buffer in place.
+ *   - Alignment: every element stream (fp32, bf16, codes, rho) must start on a
+ *     16-byte boundary, scale arrays on a 2-byte boundary; otherwise
+ *     FLASHOPT_EALIGN.  Allocations from hipMalloc / torch satisfy this.
+ */
+#ifndef FLASHOPT_H
+#define FLASHOPT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FLASHOPT_ABI_VERSION 1
+
+typedef enum {
+    FLASHOPT_OK = 0,
+    FLASHOPT_EINVAL = 1,      /* an argument is out of its documented range      */
+    FLASHOPT_EALIGN = 2,      /* a buffer violates the alignment rule above      */
+    FLASHOPT_EWORKSPACE = 3,  /* the workspace is NULL or smaller than required  */
+    FLASHOPT_EHIP = 4         /* the HIP runtime reported an error on enqueue    */
+} flashopt_status;
+
+/* Quantizer spec bits: the three switches of quantize()/dequantize() on page
+ * "code/flashsim/quantization.py". */
+enum {
+    FLASHOPT_Q_SIGNED = 1u,   /* int8 codes in [-127, 127] from max |x|; else uint8 [0, 255] from max x */
+    FLASHOPT_Q_SQRT = 2u,     /* quantize sqrt(x), dequantize to the square              */
+    FLASHOPT_Q_SOFTSIGN = 4u  /* compand y -> 2y / (1 + |y|), inverse y -> y / (2 - |y|) */
+};
+/* The named specs of that page: Alg. 2 momentum, Alg. 3 variance, and the
+ * linear ablation of both (no companding). */
+#define FLASHOPT_SPEC_MOMENTUM        (FLASHOPT_Q_SIGNED | FLASHOPT_Q_SOFTSIGN)
+#define FLASHOPT_SPEC_VARIANCE        (FLASHOPT_Q_SQRT)
+#define FLASHOPT_SPEC_MOMENTUM_LINEAR (FLASHOPT_Q_SIGNED)
+#define FLASHOPT_SPEC_VARIANCE_LINEAR (0u)
+
+/* Group-32 absmax quantization with optional companding (page
+ * "code/flashsim/quantization.py", quantize(); Alg. 2/3 forward).  Per group:
+ * a = sqrt(x) if SQRT; s = fp16(max |a|) (SIGNED) or fp16(max a); d = 1 if s is
+ * zero else s; y = a / d; y = 2y / (1 + |y|) if SOFTSIGN; code = round half to
+ * even of y*127 clamped to [-127, 127] (SIGNED) or of y*255 clamped to [0, 255].
+ *   x      [n] fp32, read
+ *   spec   any OR of FLASHOPT_Q_* bits (bits above 7 -> EINVAL)
+ *   codes  [n] int8 (SIGNED) or uint8, written
+ *   scales [ceil(n/32)] fp16 bits, written
+ * Errors: EINVAL (n < 0, NULL pointer with n > 0, bad spec), EALIGN, EHIP. */
+flashopt_status flashopt_quantize(const float *x, int64_t n, unsigned spec,
+                                  void *codes, uint16_t *scales, void *stream);
+
+/* Inverse (page "code/flashsim/quantization.py", dequantize()): y = q/127 or
+ * q/255; y = y / (2 - |y|) if SOFTSIGN; out = y * s; out = out * out if SQRT.
+ *   codes [n] int8|uint8 and scales [ceil(n/32)] fp16 bits, read
+ *   out   [n] fp32, written
+ * Errors: as flashopt_quantize. */
+flashopt_status flashopt_dequantize(const void *codes, const uint16_t *scales,
+                                    int64_t n, unsigned spec, float *out,
+                                    void *stream);
+
+/* Weight split, Alg. 1 (called but not printed on page
+ * "code/flashsim/flash_adamw_sim.py"; the bf16 parameter and correction bits
+ * rho of page "code/gpu/equivalence.py", eq_ecc()).  This library's reading:
+ *   theta' = master rounded to the nearest bf16, ties away from zero;
+ *   D      = bit pattern of master minus (bit pattern of theta') << 16,
+ *            D in [-32768, 32767];
+ *   rho    = D (master_bits 32, int16: lossless for every non-NaN input), or
+ *            D/256 rounded half to even and clamped to [-128, 127]
+ *            (master_bits 24, int8: within 128 fp32 ulps, 255 when D >= 32640).
+ *   NaN: theta' keeps the upper half with the quiet bit set, rho = 0.
+ *   master [n] fp32, read;  param_bf16 [n] written;  rho [n] int8|int16 written
+ * Errors: EINVAL (also master_bits not 24 or 32), EALIGN, EHIP. */
+flashopt_status flashopt_split(const float *master, int64_t n, int master_bits,
+                               uint16_t *param_bf16, void *rho, void *stream);
+
+/* Inverse split: bit pattern of master = (theta' << 16) + rho * 2^(16 - w),
+ * w = 8 (24-bit master) or 16 (32-bit), in wrapping 32-bit integer arithmetic.
+ *   param_bf16 [n], rho [n] read;  master [n] fp32 written
+ * Errors: as flashopt_split. */
+flashopt_status flashopt_reconstruct(const uint16_t *param_bf16, const void *rho,
+                                     int64_t n, int master_bits, float *master,
+                                     void *stream);
+
+/* One parameter tensor of a FlashAdamW step (page
+ * "code/flashsim/flash_adamw_sim.py", FlashAdamWSim.step: per-parameter state
+ * m = (codes, scales), v = (codes, scales), rho).  All device pointers.
+ * param, rho, m_*, v_* are read and updated in place; grad is read only.
+ * Fresh state is all zero (codes, scales and rho), which reproduces the
+ * page's state init for a bf16 parameter. */
+typedef struct {
+    uint16_t *param;          /* [numel] bf16 theta'                          */
+    const uint16_t *grad;     /* [numel] bf16 gradient                        */
+    void *rho;                /* [numel] int8 (24-bit) | int16 (32-bit)       */
+    int8_t *m_codes;          /* [numel] momentum codes                       */
+    uint16_t *m_scales;       /* [ceil(numel/32)] fp16 momentum scales        */
+    uint8_t *v_codes;         /* [numel] variance codes                       */
+    uint16_t *v_scales;       /* [ceil(numel/32)] fp16 variance scales        */
+    int64_t numel;            /* >= 0                                         */
+} flashopt_tensor;
+
+/* Step hyper-parameters, as the Python floats of FlashAdamWSim. */
+typedef struct {
+    double lr;                /* >= 0                                         */
+    double beta1, beta2;      /* in [0, 1)                                    */
+    double eps;               /* >= 0                                         */
+    double weight_decay;      /* finite; decoupled: theta *= 1 - lr * wd      */
+    int64_t step;             /* t >= 1, the step count after this step's increment */
+    int master_bits;          /* 24 (int8 rho) | 32 (int16 rho)               */
+    int companded;            /* 1: softsign m, sqrt v (Alg. 2/3); 0: linear ablation */
+} flashopt_adamw_args;
+
+/* Device workspace bytes that flashopt_adamw_step needs for this list (the
+ * per-tensor descriptor and chunk table).  Returns 0 for n_tensors <= 0. */
+size_t flashopt_adamw_workspace_bytes(const flashopt_tensor *tensors, int n_tensors);
+
+/* One fused FlashAdamW step over a list of tensors, one kernel launch (page
+ * "code/flashsim/flash_adamw_sim.py", FlashAdamWSim.step, Alg. 4).  Per
+ * element, in one pass over memory:
+ *   m0 = dequantize(m), v0 = dequantize(v)      (momentum / variance spec, or
+ *                                                 the linear specs if !companded)
+ *   theta = reconstruct(param, rho)
+ *   theta *= 1 - lr*wd;  m1 = b1 m0 + (1-b1) g;  v1 = b2 v0 + ((1-b2) g) g
+ *   theta -= (alpha m1) / (sqrt(v1) k2 + eps),  alpha = lr / (1 - b1^t),
+ *                                               k2 = 1 / sqrt(1 - b2^t)
+ *   (m, v) = quantize(m1), quantize(v1);  (param, rho) = split(theta)
+ * Scalars are formed in double on the host and rounded once to fp32; every
+ * fp32 operation is rounded once, in the order written (no contraction).
+ *   tensors   HOST array of n_tensors descriptors (read during the call only)
+ *   workspace DEVICE buffer of at least flashopt_adamw_workspace_bytes();
+ *             overwritten; it must not be reused by another call until this
+ *             step has run on `stream`
+ * The descriptor table is staged through a pinned host buffer that the
+ * library allocates once and reuses (hipHostMalloc).
+ * Errors: EINVAL (n_tensors < 0, NULL tensors/args, numel < 0, NULL pointer in
+ * a non-empty tensor, master_bits, companded, step < 1, lr < 0, beta outside
+ * [0, 1), eps < 0, non-finite weight_decay, more than 2^31 - 1 chunks of
+ * 1024 elements in total), EALIGN, EWORKSPACE, EHIP. */
+flashopt_status flashopt_adamw_step(const flashopt_tensor *tensors, int n_tensors,
+                                    const flashopt_adamw_args *args,
+                                    void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
+/* Static string naming a status code. */
+const char *flashopt_status_str(flashopt_status status);
+
+/* FLASHOPT_ABI_VERSION of the loaded library. */
+int flashopt_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FLASHOPT_H */

@@ -1,0 +1,128 @@
+"""The C ABI of libflashopt.so without a GPU: the library loads, exports every
+entry point include/flashopt.h declares, and rejects bad arguments with the
+documented status before it touches the HIP runtime (no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_companded_adam_amd import flashopt as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashopt.h")
+
+A16 = 0x10000          # a fake, 16-byte aligned device address (never dereferenced)
+MIS = 0x10001          # a fake misaligned address
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(F._LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return F.lib()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(flashopt_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert set(names) == set(F.EXPORTS)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_abi_version_and_status_strings(L):
+    ver = int(re.search(r"#define FLASHOPT_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert L.flashopt_abi_version() == ver
+    for code in range(5):
+        assert F.status_str(code).startswith("FLASHOPT_")
+    assert "UNKNOWN" in F.status_str(99)
+
+
+def test_codec_validation(L):
+    q = L.flashopt_quantize
+    d = L.flashopt_dequantize
+    assert q(None, 0, 5, None, None, None) == F.FLASHOPT_OK          # n == 0 is a no-op
+    assert q(A16, -1, 5, A16, A16, None) == F.FLASHOPT_EINVAL
+    assert q(A16, 10, 8, A16, A16, None) == F.FLASHOPT_EINVAL         # unknown spec bit
+    assert q(None, 10, 5, A16, A16, None) == F.FLASHOPT_EINVAL
+    assert q(A16, 10, 5, None, A16, None) == F.FLASHOPT_EINVAL
+    assert q(A16, 10, 5, A16, None, None) == F.FLASHOPT_EINVAL
+    assert q(MIS, 10, 5, A16, A16, None) == F.FLASHOPT_EALIGN
+    assert q(A16, 10, 5, A16 + 8, A16, None) == F.FLASHOPT_EALIGN
+    assert q(A16, 10, 5, A16, MIS, None) == F.FLASHOPT_EALIGN
+    assert d(None, None, 0, 2, None, None) == F.FLASHOPT_OK
+    assert d(A16, A16, -5, 2, A16, None) == F.FLASHOPT_EINVAL
+    assert d(A16, A16, 5, 2, MIS, None) == F.FLASHOPT_EALIGN
+
+
+def test_split_validation(L):
+    s = L.flashopt_split
+    r = L.flashopt_reconstruct
+    assert s(None, 0, 24, None, None, None) == F.FLASHOPT_OK
+    assert s(A16, 10, 16, A16, A16, None) == F.FLASHOPT_EINVAL
+    assert s(A16, 10, 0, A16, A16, None) == F.FLASHOPT_EINVAL
+    assert s(A16, -1, 24, A16, A16, None) == F.FLASHOPT_EINVAL
+    assert s(A16, 10, 24, A16, None, None) == F.FLASHOPT_EINVAL
+    assert s(A16, 10, 32, A16 + 2, A16, None) == F.FLASHOPT_EALIGN
+    assert r(A16, A16, 10, 25, A16, None) == F.FLASHOPT_EINVAL
+    assert r(A16, MIS, 10, 24, A16, None) == F.FLASHOPT_EALIGN
+
+
+def _tensor(numel=4096, **over):
+    t = F.flashopt_tensor(A16, A16, A16, A16, A16, A16, A16, numel)
+    for k, v in over.items():
+        setattr(t, k, v)
+    return t
+
+
+def _step(L, tensors, args=None, ws=A16, ws_bytes=1 << 20):
+    arr = (F.flashopt_tensor * max(1, len(tensors)))(*tensors)
+    a = args or F.make_args(1)
+    return L.flashopt_adamw_step(arr if tensors else None, len(tensors), ctypes.byref(a),
+                                 ws, ws_bytes, None)
+
+
+def test_step_validation(L):
+    ok = [_tensor()]
+    # hyper-parameters
+    for bad in (dict(step=0), dict(master_bits=16), dict(companded=2), dict(lr=-1.0),
+                dict(beta1=1.0), dict(beta2=-0.1), dict(eps=-1e-8),
+                dict(weight_decay=float("inf")), dict(lr=float("nan"))):
+        a = F.make_args(1)
+        for k, v in bad.items():
+            setattr(a, k, v)
+        assert _step(L, ok, a) == F.FLASHOPT_EINVAL, bad
+    assert L.flashopt_adamw_step(None, 1, ctypes.byref(F.make_args(1)), A16, 1 << 20, None) == F.FLASHOPT_EINVAL
+    assert L.flashopt_adamw_step(None, -1, ctypes.byref(F.make_args(1)), A16, 1 << 20, None) == F.FLASHOPT_EINVAL
+    # tensors
+    assert _step(L, [_tensor(numel=-1)]) == F.FLASHOPT_EINVAL
+    for field in ("param", "grad", "rho", "m_codes", "m_scales", "v_codes", "v_scales"):
+        assert _step(L, [_tensor(**{field: None})]) == F.FLASHOPT_EINVAL, field
+        bad = MIS if field.endswith("scales") else A16 + 8
+        assert _step(L, [_tensor(**{field: bad})]) == F.FLASHOPT_EALIGN, field
+    # more than 2^31 - 1 chunks of 1024
+    assert _step(L, [_tensor(numel=(1 << 41) + 1)]) == F.FLASHOPT_EINVAL
+    # empty work is a no-op, even with no workspace
+    assert _step(L, []) == F.FLASHOPT_OK
+    assert _step(L, [_tensor(numel=0, param=None)], ws=None, ws_bytes=0) == F.FLASHOPT_OK
+    # workspace
+    need = F.flashopt_adamw_workspace_bytes(3)
+    three = [_tensor(), _tensor(), _tensor()]
+    assert need >= 3 * 64 + 4 * 4
+    assert _step(L, three, ws=None) == F.FLASHOPT_EWORKSPACE
+    assert _step(L, three, ws_bytes=need - 1) == F.FLASHOPT_EWORKSPACE
+    assert _step(L, three, ws=A16 + 4, ws_bytes=need) == F.FLASHOPT_EALIGN
+    assert F.flashopt_adamw_workspace_bytes(0) == 0
+
+
+def test_binding_refuses_host_tensors(L):
+    import torch
+    with pytest.raises(ValueError):
+        F.flashopt_quantize(torch.zeros(64), F.SPEC_MOMENTUM)

@@ -1,0 +1,99 @@
+"""GPU parity of the group-32 codec (flashopt_quantize / flashopt_dequantize,
+page "code/flashsim/quantization.py") against the oracle, element by element,
+through the C ABI.  Bar: scales bit-exact; codes bit-exact (the contract allows
+>= 99.99% equal and never more than 1 apart; this implementation is held to
+equality); dequantized values bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+from bit_companded_adam_amd import flashopt as F
+from bit_companded_adam_amd import workloads as W
+from tests._gpu import code_agreement, host, require_gpu, u16
+
+pytestmark = pytest.mark.gpu
+
+SPECS = {"momentum": F.SPEC_MOMENTUM, "variance": F.SPEC_VARIANCE,
+         "momentum_linear": F.SPEC_MOMENTUM_LINEAR, "variance_linear": F.SPEC_VARIANCE_LINEAR}
+
+
+def _parity(orc, x_np: np.ndarray, spec: int, label: str):
+    x = torch.from_numpy(x_np).cuda()
+    q_d, s_d = F.flashopt_quantize(x, spec)
+    d_d = F.flashopt_dequantize(q_d, s_d, spec)
+    torch.cuda.synchronize()
+    q_o, s_o = orc.quantize(x_np, spec)
+    s_g = u16(s_d)
+    assert (s_g == s_o).all(), f"{label}: scales differ at {np.nonzero(s_g != s_o)[0][:5]}"
+    q_g = host(q_d)
+    agree, worst = code_agreement(q_g, q_o)
+    assert worst <= 1 and agree >= 0.9999, (label, agree, worst)
+    assert agree == 1.0, f"{label}: codes agree on {agree:.8f} (max diff {worst})"
+    d_o = orc.dequantize(q_o, s_o, spec)
+    d_g = host(d_d)
+    same = (d_g.view(np.uint32) == d_o.view(np.uint32)) | (np.isnan(d_g) & np.isnan(d_o))
+    assert same.all(), f"{label}: dequantized values differ at {np.nonzero(~same)[0][:5]}"
+
+
+@pytest.mark.parametrize("name", list(W.battery().keys()))
+def test_battery_named_specs(orc, name):
+    require_gpu()
+    t = W.battery()[name].numpy()
+    print(f"battery {name} n={t.size}", flush=True)
+    _parity(orc, t, F.SPEC_MOMENTUM, f"{name}/momentum")
+    _parity(orc, np.abs(t), F.SPEC_VARIANCE, f"{name}/variance")
+    _parity(orc, t, F.SPEC_MOMENTUM_LINEAR, f"{name}/momentum_linear")
+    _parity(orc, np.abs(t), F.SPEC_VARIANCE_LINEAR, f"{name}/variance_linear")
+
+
+@pytest.mark.parametrize("spec", range(8))
+def test_every_spec_ragged_sizes(orc, spec):
+    require_gpu()
+    rng = np.random.default_rng(100 + spec)
+    for n in (1, 15, 16, 17, 31, 32, 33, 1023, 1024, 1025, 4095, 4097, 50001):
+        x = (rng.standard_normal(n) * np.exp(2 * rng.standard_normal(n))).astype(np.float32)
+        if not spec & F.Q_SIGNED or spec & F.Q_SQRT:
+            x = np.abs(x)
+        _parity(orc, x, spec, f"spec{spec}/n{n}")
+
+
+def test_fp16_scale_rounding_boundaries(orc):
+    """Every fp16 rounding midpoint (and its fp32 neighbours) as a group max:
+    the scale conversion must round to nearest even, keep subnormals and
+    overflow to Inf exactly as the oracle."""
+    require_gpu()
+    h = np.arange(0, 0x7C00, dtype=np.uint32).astype(np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = np.append(lo[1:], 65536.0)              # next fp16 (65536 stands for the overflow edge)
+    mid = ((lo + hi) / 2).astype(np.float32)
+    mids = mid.view(np.uint32)
+    cand = np.concatenate([mids - 1, mids, mids + 1, lo.astype(np.float32).view(np.uint32)])
+    vals = np.unique(cand).view(np.float32)
+    vals = vals[np.isfinite(vals) & (vals >= 0)]
+    x = np.zeros((vals.size, 32), np.float32)
+    x[:, 0] = vals
+    x[:, 1] = vals * np.float32(0.5)
+    _parity(orc, x.reshape(-1), F.SPEC_VARIANCE_LINEAR, "fp16 boundaries")
+    _parity(orc, (-x).reshape(-1), F.SPEC_MOMENTUM, "fp16 boundaries (neg)")
+
+
+def test_all_codes_dequantize(orc):
+    """Every code byte with assorted scales (subnormal, normal, max, Inf)."""
+    require_gpu()
+    scales = np.array([0x0000, 0x0001, 0x03FF, 0x0400, 0x3C00, 0x35EC, 0x7BFF, 0x7C00], np.uint16)
+    for spec in range(8):
+        dt = np.int8 if spec & F.Q_SIGNED else np.uint8
+        codes = np.tile(np.arange(256, dtype=np.uint8), scales.size).view(dt)
+        s = np.repeat(scales, 8)
+        d_g = host(F.flashopt_dequantize(torch.from_numpy(codes).cuda(),
+                                         torch.from_numpy(s.view(np.int16)).cuda(), spec))
+        d_o = orc.dequantize(codes, s, spec)
+        same = (d_g.view(np.uint32) == d_o.view(np.uint32)) | (np.isnan(d_g) & np.isnan(d_o))
+        assert same.all(), spec
+
+
+def test_empty_is_noop():
+    require_gpu()
+    x = torch.empty(0, device="cuda")
+    q, s = F.flashopt_quantize(x, F.SPEC_MOMENTUM)
+    assert q.numel() == 0 and s.numel() == 0
