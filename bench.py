@@ -93,11 +93,11 @@ def time_steps(opt, grads, steps: int, warmup: int):
     return wall, per
 
 
-def cpu_baseline(master_bits: int, target_elems: int, threads: int):
+def cpu_baseline(master_bits: int, target_elems: int, threads: int, min_seconds: float = 10.0):
     """The oracle as it is, on host threads, over a bounded sample of the
     workload: the first target_elems / 32 elements of each of 32 evenly spaced
-    tensors of the 8.0B list (same distributions), step 2 after an untimed
-    step 1."""
+    tensors of the 8.0B list (same distributions), steps 2, 3, ... after an
+    untimed step 1, repeated for about min_seconds."""
     import oracle
     oracle.build(force=False)
     shapes = W.decoder_8b_shapes()
@@ -116,12 +116,52 @@ def cpu_baseline(master_bits: int, target_elems: int, threads: int):
               weight_decay=W.HP_DEFAULT["weight_decay"], master_bits=master_bits)
     oracle.adamw_step_list(states, g1, oracle.hparams(step=1, **hp), threads)
     n_total = sum(s.param.size for s in states)
+    steps, used = 0, 0
     t0 = time.perf_counter()
-    used = oracle.adamw_step_list(states, g2, oracle.hparams(step=2, **hp), threads)
-    dt = time.perf_counter() - t0
-    return {"value": n_total / dt / 1e9, "unit": "Gparam/s", "cores": used, "kind": "oracle",
-            "sample": f"{n_total} params: first {per} elements of 32 of the 290 tensors "
-                      f"of the 8.0B list, one step (step 2), {dt:.1f} s"}
+    while True:                      # steps 2, 3, ... until about min_seconds of work
+        used = oracle.adamw_step_list(states, g2 if steps % 2 == 0 else g1,
+                                      oracle.hparams(step=2 + steps, **hp), threads)
+        steps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": n_total * steps / dt / 1e9, "unit": "Gparam/s", "cores": used, "kind": "oracle",
+            "sample": f"{n_total} params (first {per} elements of 32 of the 290 tensors of the "
+                      f"8.0B list), {steps} steps in {dt:.1f} s"}
+
+
+def copy_reference(gib: float = 8.0, reps: int = 5) -> float:
+    """Context for the roofline: GB/s (read + write) of a plain streaming
+    kernel on this GPU -- torch's elementwise negation of a gib-GiB fp32
+    buffer into another (reads and writes gib GiB each)."""
+    n = int(gib * (1 << 30)) // 4
+    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.neg(a, out=b)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2.0 * n * 4 / (ms * 1e-3) / 1e9
+
+
+def calibrate_copy(gib: float):
+    """One plain streaming kernel of known size (torch's elementwise negation,
+    reading and writing gib GiB each), for scaling rocprofv3 FETCH_SIZE /
+    WRITE_SIZE counters."""
+    n = int(gib * (1 << 30)) // 4
+    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes_read": n * 4, "calibration_copy_bytes_written": n * 4}))
 
 
 def main():
@@ -134,6 +174,10 @@ def main():
     ap.add_argument("--cpu-elems", type=int, default=1 << 27,
                     help="oracle sample size for the CPU baseline (0: skip)")
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
+                    help="only run one device copy of GIB GiB (for counter scaling) and exit")
+    ap.add_argument("--no-copy-ref", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -144,7 +188,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.calibrate_copy > 0:
+        calibrate_copy(args.calibrate_copy)
+        return
+
     mb, comp = args.master_bits, not args.linear
+    copy_gbs = None if args.no_copy_ref else copy_reference()
     opt, grads = build_workload(mb, comp)
     n = sum(s.param.numel() for s in opt.states)
     print(f"# workload ready: {len(opt.states)} tensors, {n} params, "
@@ -163,7 +212,7 @@ def main():
 
     cpu = None
     if args.cpu_elems > 0:
-        cpu = cpu_baseline(mb, args.cpu_elems, args.cpu_threads)
+        cpu = cpu_baseline(mb, args.cpu_elems, args.cpu_threads, args.cpu_seconds)
 
     out = {
         "metric": METRIC,
@@ -183,7 +232,8 @@ def main():
                    "bytes_per_param": bpp, "launches_per_step": 1},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": traffic_per_launch() if (mb, comp) == (24, True) else None},
+                     "traffic": traffic_per_launch() if (mb, comp) == (24, True) else None,
+                     "copy_ref_gbs": copy_gbs},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -21,6 +21,22 @@ HIPCC_FLAGS = [
 ]
 
 
+CHECK_SRC = os.path.join(ROOT, "tests", "hip", "fastmath_check.hip")
+CHECK_LIB = os.path.join(ROOT, "tests", "hip", "libfastmath_check.so")
+
+
+def build_check(verbose: bool = False) -> str:
+    """The GPU checker of the short exact arithmetic sequences (test-only)."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = CHECK_LIB + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", CSRC, CHECK_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(tmp, CHECK_LIB)
+    return CHECK_LIB
+
+
 def build(extra_flags: list[str] | None = None, verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp"
@@ -35,3 +51,4 @@ def build(extra_flags: list[str] | None = None, verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     build(verbose=True)
+    build_check(verbose=True)

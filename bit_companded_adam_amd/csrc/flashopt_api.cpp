@@ -180,6 +180,9 @@ flashopt_status flashopt_adamw_step(const flashopt_tensor *tensors, int n_tensor
     sc.alpha = static_cast<float>(a->lr / bc1);
     sc.k2 = static_cast<float>(1.0 / std::sqrt(bc2));
     sc.eps = static_cast<float>(a->eps);
+    // The kernel's short division is exact for denominators sqrt(v) k2 + eps in
+    // [2^-100, 2^100]; sqrt(v) < 2^32 on its fast path.
+    sc.fast_div = (sc.eps >= 0x1p-100f && sc.k2 <= 0x1p60f) ? 1 : 0;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     int dev = 0;

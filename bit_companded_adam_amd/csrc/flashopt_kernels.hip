@@ -15,8 +15,11 @@
 // table and two 256-entry dequantization tables.
 //
 // Arithmetic: fp32, one IEEE rounding per operation in the written order
-// (built with -ffp-contract=off, correctly rounded / and sqrt, fp32 and fp16
-// denormals preserved), so results match a plain CPU evaluation bit for bit.
+// (built with -ffp-contract=off, fp32 and fp16 denormals preserved), so the
+// results match a plain CPU evaluation bit for bit.  Division by a group
+// scale, the softsign division, the variance sqrt and the byte conversions
+// use the exact short sequences of flashopt_math.h instead of the generic
+// correctly rounded expansions.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -24,6 +27,7 @@
 
 #include "flashopt.h"
 #include "flashopt_internal.h"
+#include "flashopt_math.h"
 
 namespace flashopt {
 namespace {
@@ -93,51 +97,84 @@ __device__ __forceinline__ float dequant_unit(int c)
     return y;
 }
 
-// Code of one element from y = a / d (quantize()): softsign companding if
-// asked, then round half to even of y*127 (signed, clamp [-127, 127]) or
-// y*255 (unsigned, clamp [0, 255]).  A NaN gets code 0.  Returns the byte.
-template <unsigned SPEC>
-__device__ __forceinline__ uint32_t code_byte(float y)
+// A group's divisor d (1 for a zero scale, else the scale) with its
+// correctly rounded reciprocal r.  An infinite scale yields d = r = 0, for
+// which div_by_recip returns a/inf = 0 exactly like the plain division.
+struct GroupDiv {
+    float d, r;
+};
+
+__device__ __forceinline__ GroupDiv group_div(uint32_t s)
 {
-    if (SPEC & FLASHOPT_Q_SOFTSIGN) {
-        const float num = 2.0f * y;
-        const float den = 1.0f + fabsf(y);
-        y = num / den;
-    }
-    if (SPEC & FLASHOPT_Q_SIGNED) {
-        float r = rintf(y * 127.0f);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        const int32_t q = (y != y) ? 0 : static_cast<int32_t>(r);
-        return static_cast<uint32_t>(q) & 0xFFu;
-    } else {
-        float r = rintf(y * 255.0f);
-        r = fminf(fmaxf(r, 0.0f), 255.0f);
-        return (y != y) ? 0u : static_cast<uint32_t>(r);
-    }
+    const uint32_t mag = s & 0x7FFFu;
+    const float d = group_divisor(s);
+    GroupDiv g{d, math::recip_cr(d)};
+    if (mag == 0x7C00u) { g.d = 0.0f; g.r = 0.0f; }
+    return g;
+}
+
+// Signed code (quantize(), SIGNED): round half to even of y*127 after
+// optional softsign companding, clamped to [-127, 127]; NaN -> 0.  Returns
+// the int8 value in an int32.
+template <bool SOFTSIGN>
+__device__ __forceinline__ int32_t code_s8(float y)
+{
+    if (SOFTSIGN) y = math::softsign(y);
+    return math::clamp_i32(math::cvt_i32(rintf(y * 127.0f)), -127, 127);
+}
+
+// Unsigned code (quantize(), not SIGNED): round half to even of y*255
+// clamped to [0, 255], NaN -> 0, written into byte BYTE of acc
+// (v_cvt_pk_u8_f32 does the rounding, clamping and packing in one step).
+template <int BYTE>
+__device__ __forceinline__ uint32_t code_u8(float y, uint32_t acc)
+{
+    return __builtin_amdgcn_cvt_pk_u8_f32(y * 255.0f, BYTE, acc);
+}
+
+// Low bytes of four int32 values packed into one word.
+__device__ __forceinline__ uint32_t pack_bytes(int32_t b0, int32_t b1, int32_t b2, int32_t b3)
+{
+    const uint32_t lo = __builtin_amdgcn_perm(static_cast<uint32_t>(b1), static_cast<uint32_t>(b0), 0x0C0C0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(static_cast<uint32_t>(b3), static_cast<uint32_t>(b2), 0x0C0C0400u);
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+// Upper halves of two words packed into one (two bf16 from two fp32 patterns).
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t w0, uint32_t w1)
+{
+    return __builtin_amdgcn_perm(w1, w0, 0x07060302u);
+}
+
+// Low halves of two words packed into one.
+__device__ __forceinline__ uint32_t pack_lo16(uint32_t w0, uint32_t w1)
+{
+    return __builtin_amdgcn_perm(w1, w0, 0x05040100u);
 }
 
 // Weight split of one fp32 value: theta' = nearest bf16 with ties away from
-// zero, D = pattern(x) - (pattern(theta') << 16) in [-32768, 32767];
-// rho = D (32-bit master) or round-half-even(D / 256) clamped to 127 (24-bit).
-// NaN keeps its upper half, quieted, with rho = 0.
+// zero, D = pattern(x) - (pattern(theta') << 16) in [-32768, 32767], which is
+// the low half of the pattern read as a signed 16-bit integer; rho = D
+// (32-bit master) or round-half-even(D / 256) clamped to 127 (24-bit).
+// Returns pattern(theta') << 16 in `top`.  NaN keeps its upper half, quieted,
+// with rho = 0.
 template <int MB>
-__device__ __forceinline__ void split_elem(float x, uint32_t &hi, uint32_t &rho)
+__device__ __forceinline__ void split_elem(float x, uint32_t &top, int32_t &rho)
 {
     const uint32_t u = __float_as_uint(x);
-    const uint32_t b = (u + 0x8000u) >> 16;
-    const int32_t D = static_cast<int32_t>(u - (b << 16));
-    int32_t r;
+    const int32_t D = static_cast<int32_t>(u << 16) >> 16;
+    top = u - static_cast<uint32_t>(D);
     if (MB == 32) {
-        r = D;
+        rho = D;
     } else {
-        int32_t q = D >> 8;                 // floor(D / 256)
-        const int32_t frac = D & 255;
-        q += (frac > 128) | ((frac == 128) & (q & 1));
-        r = q < 127 ? q : 127;
+        // floor((D + 127 + parity(floor(D / 256))) / 256): ties go to even
+        const int32_t q = (D + 127 + ((D >> 8) & 1)) >> 8;
+        rho = q < 127 ? q : 127;
     }
-    const bool nan = (u & 0x7FFFFFFFu) > 0x7F800000u;
-    hi = nan ? ((u >> 16) | 0x40u) : b;
-    rho = nan ? 0u : (static_cast<uint32_t>(r) & (MB == 32 ? 0xFFFFu : 0xFFu));
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) {
+        top = (u & 0xFFFF0000u) | 0x00400000u;
+        rho = 0;
+    }
 }
 
 // Inverse split: pattern = (theta' << 16) + rho * 2^(16 - w), wrapping.
@@ -156,12 +193,48 @@ __device__ __forceinline__ int lane_count(int64_t n, int64_t e0)
     return rem >= kLaneElems ? kLaneElems : (rem > 0 ? static_cast<int>(rem) : 0);
 }
 
+// Global-address-space views: loads and stores become global_* with an
+// SGPR base and a 32-bit lane offset instead of flat accesses.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4 g_cu4;
+typedef __attribute__((address_space(1))) u32x4 g_u4;
+typedef __attribute__((address_space(1))) const uint16_t g_cu16;
+typedef __attribute__((address_space(1))) uint16_t g_u16;
+typedef __attribute__((address_space(1))) const uint8_t g_cu8;
+typedef __attribute__((address_space(1))) uint8_t g_u8;
+typedef __attribute__((address_space(1))) const float g_cf32;
+typedef __attribute__((address_space(1))) float g_f32;
+
+__device__ __forceinline__ uint4 ld16(const void *p, int k = 0)
+{
+    const u32x4 v = ((g_cu4 *)p)[k];
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st16(void *p, uint4 v, int k = 0)
+{
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    ((g_u4 *)p)[k] = w;
+}
+// Streaming (nontemporal) 16-byte accesses: the step touches every byte once.
+__device__ __forceinline__ uint4 ld16s(const void *p, int k = 0)
+{
+    const u32x4 v = __builtin_nontemporal_load((g_cu4 *)p + k);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st16s(void *p, uint4 v, int k = 0)
+{
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, (g_u4 *)p + k);
+}
+__device__ __forceinline__ uint16_t ld_u16(const uint16_t *p) { return *(g_cu16 *)p; }
+__device__ __forceinline__ void st_u16(uint16_t *p, uint16_t v) { *(g_u16 *)p = v; }
+
 // 16 consecutive 16-bit elements -> 8 words (zero past cnt)
-__device__ __forceinline__ void load_u16x16(const uint16_t *__restrict__ p, int cnt, uint32_t (&w)[8])
+__device__ __forceinline__ void load_u16x16(const uint16_t *p, int cnt, uint32_t (&w)[8])
 {
     if (cnt == kLaneElems) {
-        const uint4 a = reinterpret_cast<const uint4 *>(p)[0];
-        const uint4 b = reinterpret_cast<const uint4 *>(p)[1];
+        const uint4 a = ld16(p, 0);
+        const uint4 b = ld16(p, 1);
         w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
         w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
     } else {
@@ -169,78 +242,170 @@ __device__ __forceinline__ void load_u16x16(const uint16_t *__restrict__ p, int 
         for (int i = 0; i < 8; ++i) w[i] = 0u;
 #pragma unroll
         for (int j = 0; j < kLaneElems; ++j)
-            if (j < cnt) w[j >> 1] |= static_cast<uint32_t>(p[j]) << (16 * (j & 1));
+            if (j < cnt) w[j >> 1] |= static_cast<uint32_t>(((g_cu16 *)p)[j]) << (16 * (j & 1));
     }
 }
 
-__device__ __forceinline__ void store_u16x16(uint16_t *__restrict__ p, int cnt, const uint32_t (&w)[8])
+__device__ __forceinline__ void store_u16x16(uint16_t *p, int cnt, const uint32_t (&w)[8])
 {
     if (cnt == kLaneElems) {
-        reinterpret_cast<uint4 *>(p)[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        reinterpret_cast<uint4 *>(p)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        st16(p, make_uint4(w[0], w[1], w[2], w[3]), 0);
+        st16(p, make_uint4(w[4], w[5], w[6], w[7]), 1);
     } else {
 #pragma unroll
         for (int j = 0; j < kLaneElems; ++j)
-            if (j < cnt) p[j] = static_cast<uint16_t>(w[j >> 1] >> (16 * (j & 1)));
+            if (j < cnt) ((g_u16 *)p)[j] = static_cast<uint16_t>(w[j >> 1] >> (16 * (j & 1)));
     }
 }
 
 // 16 consecutive bytes -> 4 words (zero past cnt)
-__device__ __forceinline__ void load_u8x16(const void *__restrict__ pv, int cnt, uint32_t (&w)[4])
+__device__ __forceinline__ void load_u8x16(const void *p, int cnt, uint32_t (&w)[4])
 {
-    const uint8_t *p = static_cast<const uint8_t *>(pv);
     if (cnt == kLaneElems) {
-        const uint4 a = *reinterpret_cast<const uint4 *>(p);
+        const uint4 a = ld16(p);
         w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[i] = 0u;
 #pragma unroll
         for (int j = 0; j < kLaneElems; ++j)
-            if (j < cnt) w[j >> 2] |= static_cast<uint32_t>(p[j]) << (8 * (j & 3));
+            if (j < cnt) w[j >> 2] |= static_cast<uint32_t>(((g_cu8 *)p)[j]) << (8 * (j & 3));
     }
 }
 
-__device__ __forceinline__ void store_u8x16(void *__restrict__ pv, int cnt, const uint32_t (&w)[4])
+__device__ __forceinline__ void store_u8x16(void *p, int cnt, const uint32_t (&w)[4])
 {
-    uint8_t *p = static_cast<uint8_t *>(pv);
     if (cnt == kLaneElems) {
-        *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+        st16(p, make_uint4(w[0], w[1], w[2], w[3]));
     } else {
 #pragma unroll
         for (int j = 0; j < kLaneElems; ++j)
-            if (j < cnt) p[j] = static_cast<uint8_t>(w[j >> 2] >> (8 * (j & 3)));
+            if (j < cnt) ((g_u8 *)p)[j] = static_cast<uint8_t>(w[j >> 2] >> (8 * (j & 3)));
     }
 }
 
 // 16 consecutive fp32 (zero past cnt)
-__device__ __forceinline__ void load_f32x16(const float *__restrict__ p, int cnt, float (&x)[16])
+__device__ __forceinline__ void load_f32x16(const float *p, int cnt, float (&x)[16])
 {
     if (cnt == kLaneElems) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const float4 v = reinterpret_cast<const float4 *>(p)[k];
-            x[4 * k + 0] = v.x; x[4 * k + 1] = v.y; x[4 * k + 2] = v.z; x[4 * k + 3] = v.w;
+            const uint4 v = ld16(p, k);
+            x[4 * k + 0] = __uint_as_float(v.x); x[4 * k + 1] = __uint_as_float(v.y);
+            x[4 * k + 2] = __uint_as_float(v.z); x[4 * k + 3] = __uint_as_float(v.w);
         }
     } else {
 #pragma unroll
         for (int j = 0; j < kLaneElems; ++j) x[j] = 0.0f;
 #pragma unroll
         for (int j = 0; j < kLaneElems; ++j)
-            if (j < cnt) x[j] = p[j];
+            if (j < cnt) x[j] = ((g_cf32 *)p)[j];
     }
 }
 
-__device__ __forceinline__ void store_f32x16(float *__restrict__ p, int cnt, const float (&x)[16])
+__device__ __forceinline__ void store_f32x16(float *p, int cnt, const float (&x)[16])
 {
     if (cnt == kLaneElems) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            reinterpret_cast<float4 *>(p)[k] = make_float4(x[4 * k], x[4 * k + 1], x[4 * k + 2], x[4 * k + 3]);
+            st16(p, make_uint4(__float_as_uint(x[4 * k]), __float_as_uint(x[4 * k + 1]),
+                               __float_as_uint(x[4 * k + 2]), __float_as_uint(x[4 * k + 3])), k);
     } else {
 #pragma unroll
         for (int j = 0; j < kLaneElems; ++j)
-            if (j < cnt) p[j] = x[j];
+            if (j < cnt) ((g_f32 *)p)[j] = x[j];
+    }
+}
+
+// Codes of a lane's 16 values y_j = a_j / d of one group under SPEC, packed
+// into four words.
+template <unsigned SPEC>
+__device__ __forceinline__ void encode16(const float (&a)[16], const GroupDiv &gd, uint32_t (&out)[4])
+{
+    if (SPEC & FLASHOPT_Q_SIGNED) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            int32_t c[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                c[i] = code_s8<(SPEC & FLASHOPT_Q_SOFTSIGN) != 0>(math::div_by_recip(a[4 * k + i], gd.d, gd.r));
+            out[k] = pack_bytes(c[0], c[1], c[2], c[3]);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float y[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                y[i] = math::div_by_recip(a[4 * k + i], gd.d, gd.r);
+                if (SPEC & FLASHOPT_Q_SOFTSIGN) y[i] = math::softsign(y[i]);
+            }
+            uint32_t w = 0u;
+            w = code_u8<0>(y[0], w);
+            w = code_u8<1>(y[1], w);
+            w = code_u8<2>(y[2], w);
+            w = code_u8<3>(y[3], w);
+            out[k] = w;
+        }
+    }
+}
+
+// Re-split of a lane's 16 fp32 values into packed bf16 words and packed rho
+// words.  theta' (ties away from zero) is the upper half of pattern + 0x8000;
+// D is the lower half of the pattern read as a signed 16-bit integer.  For
+// the 24-bit master, rho = clamp(round-half-even(D / 256), -128, 127) is
+// formed as v_cvt_pk_u8_f32(D / 256 + 128) - 128: D / 256 + 128 is exact, the
+// conversion rounds half to even, clamps to [0, 255] (so D >= 32640 gives
+// 127) and packs the byte in place; the -128 is a per-word XOR.  NaN inputs
+// are not handled here (split_pack_exact covers them).
+template <int MB>
+__device__ __forceinline__ void split_pack(const float (&x)[16], uint32_t (&po)[8],
+                                           uint32_t (&ro)[MB == 32 ? 8 : 4])
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        po[i] = pack_hi16(__float_as_uint(x[2 * i]) + 0x8000u, __float_as_uint(x[2 * i + 1]) + 0x8000u);
+    if constexpr (MB == 32) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            ro[i] = pack_lo16(__float_as_uint(x[2 * i]), __float_as_uint(x[2 * i + 1]));
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t w = 0u;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int32_t D = static_cast<int32_t>(__float_as_uint(x[4 * k + b]) << 16) >> 16;
+                const float f = __builtin_fmaf(static_cast<float>(D), 0x1p-8f, 128.0f);
+                w = (b == 0) ? __builtin_amdgcn_cvt_pk_u8_f32(f, 0, w)
+                  : (b == 1) ? __builtin_amdgcn_cvt_pk_u8_f32(f, 1, w)
+                  : (b == 2) ? __builtin_amdgcn_cvt_pk_u8_f32(f, 2, w)
+                             : __builtin_amdgcn_cvt_pk_u8_f32(f, 3, w);
+            }
+            ro[k] = w ^ 0x80808080u;
+        }
+    }
+}
+
+// The same re-split element by element, NaN included (NaN keeps its upper
+// half, quieted, with rho = 0).
+template <int MB>
+__device__ __forceinline__ void split_pack_exact(const float (&x)[16], uint32_t (&po)[8],
+                                                 uint32_t (&ro)[MB == 32 ? 8 : 4])
+{
+    uint32_t top[16];
+    int32_t rr[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) split_elem<MB>(x[j], top[j], rr[j]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) po[i] = pack_hi16(top[2 * i], top[2 * i + 1]);
+    if constexpr (MB == 32) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            ro[i] = pack_lo16(static_cast<uint32_t>(rr[2 * i]), static_cast<uint32_t>(rr[2 * i + 1]));
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ro[i] = pack_bytes(rr[4 * i], rr[4 * i + 1], rr[4 * i + 2], rr[4 * i + 3]);
     }
 }
 
@@ -258,24 +423,30 @@ quantize_kernel(const float *__restrict__ x, int64_t n, void *__restrict__ codes
     float a[16];
     load_f32x16(x + e0, cnt, a);             // missing elements are the zero pad
     if (SPEC & FLASHOPT_Q_SQRT) {
+        float amax_in = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) a[j] = sqrtf(a[j]);
+        for (int j = 0; j < 16; ++j) amax_in = fmaxf(amax_in, a[j]);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) a[j] = math::sqrt_cr(a[j]);
+        if (!(amax_in < 0x1p64f)) {          // rare: inputs beyond the fast sqrt's range
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                float v = 0.0f;
+                if (j < cnt) v = ((g_cf32 *)(x + e0))[j];
+                a[j] = sqrtf(v);
+            }
+        }
     }
     float amax = kSigned ? 0.0f : -__builtin_inff();
 #pragma unroll
     for (int j = 0; j < 16; ++j) amax = fmaxf(amax, kSigned ? fabsf(a[j]) : a[j]);
     amax = pair_max(amax);
     const uint32_t s = f16_bits(amax);
-    const float d = group_divisor(s);
 
-    uint32_t out[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const float y = a[j] / d;
-        out[j >> 2] |= code_byte<SPEC>(y) << (8 * (j & 3));
-    }
+    uint32_t out[4];
+    encode16<SPEC>(a, group_div(s), out);
     store_u8x16(static_cast<uint8_t *>(codes) + e0, cnt, out);
-    if ((threadIdx.x & 1) == 0 && cnt > 0) scales[e0 / kGroup] = static_cast<uint16_t>(s);
+    if ((threadIdx.x & 1) == 0 && cnt > 0) st_u16(scales + e0 / kGroup, static_cast<uint16_t>(s));
 }
 
 template <unsigned SPEC>
@@ -292,7 +463,7 @@ dequantize_kernel(const void *__restrict__ codes, const uint16_t *__restrict__ s
     if (cnt == 0) return;
     uint32_t w[4];
     load_u8x16(static_cast<const uint8_t *>(codes) + e0, cnt, w);
-    const float s = f16_value(scales[e0 / kGroup]);
+    const float s = f16_value(ld_u16(scales + e0 / kGroup));
     float o[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -315,16 +486,12 @@ split_kernel(const float *__restrict__ master, int64_t n, uint16_t *__restrict__
     if (cnt == 0) return;
     float x[16];
     load_f32x16(master + e0, cnt, x);
-    uint32_t pw[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-    uint32_t rw[MB == 32 ? 8 : 4] = {};
+    uint32_t pw[8], rw[MB == 32 ? 8 : 4];
+    bool any_nan = false;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        uint32_t hi, r;
-        split_elem<MB>(x[j], hi, r);
-        pw[j >> 1] |= hi << (16 * (j & 1));
-        if constexpr (MB == 32) rw[j >> 1] |= r << (16 * (j & 1));
-        else rw[j >> 2] |= r << (8 * (j & 3));
-    }
+    for (int j = 0; j < 16; ++j) any_nan |= x[j] != x[j];
+    if (any_nan) split_pack_exact<MB>(x, pw, rw);
+    else split_pack<MB>(x, pw, rw);
     store_u16x16(param + e0, cnt, pw);
     if constexpr (MB == 32) store_u16x16(static_cast<uint16_t *>(rho) + e0, cnt, rw);
     else store_u8x16(static_cast<uint8_t *>(rho) + e0, cnt, rw);
@@ -356,142 +523,198 @@ reconstruct_kernel(const uint16_t *__restrict__ param, const void *__restrict__ 
 
 // ---------------------------------------------------- fused FlashAdamW step
 
-constexpr int kMaxLdsTensors = 4096;   // chunk table entries kept in LDS
-
-// One persistent grid over all chunks of all tensors.  Wavefront w takes
-// chunks w, w + W, w + 2W, ... (W = wavefronts in the grid); the owning
-// tensor of a chunk is found by walking the chunk table forward from the
-// previous one (chunks only increase).  Per lane and element, in order:
-// dequantize m and v, rebuild the master, AdamW, then the group maxima,
-// codes, scales and the re-split.
-template <int MB, bool COMP>
-__global__ void __launch_bounds__(kBlockThreads)
-adamw_step_kernel(const DevTensor *__restrict__ tensors, const int32_t *__restrict__ chunk_start,
-                  int n_tensors, int32_t total_chunks, StepScalars sc)
+// One 1024-element chunk of one tensor, processed by one wavefront: each lane
+// loads 16 elements of every stream, dequantizes m and v, rebuilds the
+// master, applies AdamW, finds the group maxima (one DPP exchange with the
+// partner lane), and writes scales, codes and the re-split parameter.  FULL
+// chunks (every lane holds 16 elements) use plain 16-byte streaming accesses;
+// the ragged last chunk of a tensor masks per element and pads with zeros.
+template <int MB, bool COMP, bool FULL>
+__device__ __forceinline__ void step_chunk(const DevTensor &d, int64_t off, int lane,
+                                           const StepScalars &sc, const float *s_mu,
+                                           const float *s_vu)
 {
     constexpr unsigned kMSpec = COMP ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
     constexpr unsigned kVSpec = COMP ? FLASHOPT_SPEC_VARIANCE : FLASHOPT_SPEC_VARIANCE_LINEAR;
+    constexpr int kRhoWords = MB == 32 ? 8 : 4;
 
-    extern __shared__ int32_t s_start[];
+    const int lofs = lane * kLaneElems;
+    const int cnt = FULL ? kLaneElems : lane_count(d.numel - off, lofs);
+    uint16_t *const pp = d.param + off + lofs;
+    const uint16_t *const gp = d.grad + off + lofs;
+    uint8_t *const rp = static_cast<uint8_t *>(d.rho) + (off + lofs) * (MB == 32 ? 2 : 1);
+    int8_t *const mp = d.m_codes + off + lofs;
+    uint8_t *const vp = d.v_codes + off + lofs;
+    uint16_t *const msp = d.m_scales + off / kGroup + (lane >> 1);
+    uint16_t *const vsp = d.v_scales + off / kGroup + (lane >> 1);
+
+    // ---- loads (missing elements read as zero)
+    uint32_t pw[8], gw[8], rw[kRhoWords], mw[4], vw[4];
+    uint32_t smb = 0u, svb = 0u;
+    if (FULL) {
+        uint4 q;
+        q = ld16s(pp, 0); pw[0] = q.x; pw[1] = q.y; pw[2] = q.z; pw[3] = q.w;
+        q = ld16s(pp, 1); pw[4] = q.x; pw[5] = q.y; pw[6] = q.z; pw[7] = q.w;
+        q = ld16s(gp, 0); gw[0] = q.x; gw[1] = q.y; gw[2] = q.z; gw[3] = q.w;
+        q = ld16s(gp, 1); gw[4] = q.x; gw[5] = q.y; gw[6] = q.z; gw[7] = q.w;
+        q = ld16s(rp, 0); rw[0] = q.x; rw[1] = q.y; rw[2] = q.z; rw[3] = q.w;
+        if constexpr (MB == 32) { q = ld16s(rp, 1); rw[4] = q.x; rw[5] = q.y; rw[6] = q.z; rw[7] = q.w; }
+        q = ld16s(mp); mw[0] = q.x; mw[1] = q.y; mw[2] = q.z; mw[3] = q.w;
+        q = ld16s(vp); vw[0] = q.x; vw[1] = q.y; vw[2] = q.z; vw[3] = q.w;
+        smb = ld_u16(msp);
+        svb = ld_u16(vsp);
+    } else {
+        load_u16x16(pp, cnt, pw);
+        load_u16x16(gp, cnt, gw);
+        if constexpr (MB == 32) load_u16x16(reinterpret_cast<const uint16_t *>(rp), cnt, rw);
+        else load_u8x16(rp, cnt, rw);
+        load_u8x16(mp, cnt, mw);
+        load_u8x16(vp, cnt, vw);
+        if (cnt > 0) {
+            smb = ld_u16(msp);
+            svb = ld_u16(vsp);
+        }
+    }
+    const float ms = f16_value(smb);
+    const float vs = f16_value(svb);
+
+    // ---- dequantize, reconstruct, moments
+    float thd[16], m1[16], v1[16];
+    float vmax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const uint32_t hs = (j & 1) ? (pw[j >> 1] & 0xFFFF0000u) : (pw[j >> 1] << 16);
+        int32_t r;
+        if constexpr (MB == 32) r = shalf(rw, j);
+        else r = sbyte(rw, j);
+        const float theta = reconstruct_elem<MB>(hs, r);
+        const float g = (j & 1) ? bf16_hi(gw[j >> 1]) : bf16_lo(gw[j >> 1]);
+
+        const float m0 = s_mu[ubyte(mw, j)] * ms;
+        const float a0 = s_vu[ubyte(vw, j)] * vs;
+        const float v0 = COMP ? a0 * a0 : a0;
+
+        thd[j] = theta * sc.cwd;
+        const float m_decay = sc.b1 * m0;
+        const float m_new = sc.c1 * g;
+        m1[j] = m_decay + m_new;
+        const float v_decay = sc.b2 * v0;
+        const float cg = sc.c2 * g;
+        const float v_new = cg * g;
+        v1[j] = v_decay + v_new;
+        vmax = fmaxf(vmax, v1[j]);
+    }
+    if (!FULL) {                            // zero pad of the ragged last group
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (j >= cnt) { m1[j] = 0.0f; v1[j] = 0.0f; }
+    }
+
+    // ---- sqrt(v1) and the update (alpha m1) / (sqrt(v1) k2 + eps)
+    float rt[16], upd[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) rt[j] = math::sqrt_cr(v1[j]);
+    if (!(vmax < 0x1p64f)) {                // rare: v beyond the fast sqrt's range
+#pragma unroll
+        for (int j = 0; j < 16; ++j) rt[j] = sqrtf(v1[j]);
+    }
+    // lane maxima of |m1| and of what the variance quantizer sees
+    float am = 0.0f, av = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        am = fmaxf(am, fabsf(m1[j]));
+        av = fmaxf(av, COMP ? rt[j] : v1[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const float den = rt[j] * sc.k2 + sc.eps;
+        const float num = sc.alpha * m1[j];
+        upd[j] = num / den;
+    }
+    float th1[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) th1[j] = thd[j] - upd[j];
+
+    // ---- group maxima over the lane pair, scales
+    am = pair_max(am);
+    av = pair_max(av);
+    const uint32_t sm_out = f16_bits(am);
+    const uint32_t sv_out = f16_bits(av);
+
+    // ---- codes, re-split, pack
+    uint32_t mo[4], vo[4];
+    encode16<kMSpec>(m1, group_div(sm_out), mo);
+    if constexpr (COMP) encode16<kVSpec>(rt, group_div(sv_out), vo);
+    else encode16<kVSpec>(v1, group_div(sv_out), vo);
+
+    uint32_t po[8], ro[kRhoWords];
+    bool any_nan = false;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) any_nan |= th1[j] != th1[j];
+    if (any_nan) split_pack_exact<MB>(th1, po, ro);   // rare: NaN masters
+    else split_pack<MB>(th1, po, ro);
+
+    // ---- stores
+    if (FULL) {
+        st16s(pp, make_uint4(po[0], po[1], po[2], po[3]), 0);
+        st16s(pp, make_uint4(po[4], po[5], po[6], po[7]), 1);
+        st16s(rp, make_uint4(ro[0], ro[1], ro[2], ro[3]), 0);
+        if constexpr (MB == 32) st16s(rp, make_uint4(ro[4], ro[5], ro[6], ro[7]), 1);
+        st16s(mp, make_uint4(mo[0], mo[1], mo[2], mo[3]));
+        st16s(vp, make_uint4(vo[0], vo[1], vo[2], vo[3]));
+    } else {
+        store_u16x16(pp, cnt, po);
+        if constexpr (MB == 32) store_u16x16(reinterpret_cast<uint16_t *>(rp), cnt, ro);
+        else store_u8x16(rp, cnt, ro);
+        store_u8x16(mp, cnt, mo);
+        store_u8x16(vp, cnt, vo);
+    }
+    if ((lane & 1) == 0 && cnt > 0) {
+        st_u16(msp, static_cast<uint16_t>(sm_out));
+        st_u16(vsp, static_cast<uint16_t>(sv_out));
+    }
+}
+
+// Grid: one wavefront per run of `run` consecutive chunks (the last run may be
+// shorter); a chunk never straddles two tensors.  The wavefront finds the
+// tensor owning its first chunk by binary search over the chunk table
+// (scalar loads, uniform across the wavefront) and walks forward from there.
+// The two 256-entry dequantization tables are built per workgroup in LDS
+// from the exact fp32 operations of dequantize().
+template <int MB, bool COMP>
+__global__ void __launch_bounds__(kBlockThreads)
+adamw_step_kernel(const DevTensor *__restrict__ tensors, const int32_t *__restrict__ chunk_start,
+                  int n_tensors, int32_t total_chunks, int32_t run, StepScalars sc)
+{
+    constexpr unsigned kMSpec = COMP ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
     __shared__ float s_mu[256];   // momentum: q/127 (companded: / (2 - |.|))
     __shared__ float s_vu[256];   // variance: q/255
-    const bool table_in_lds = n_tensors < kMaxLdsTensors;
-    if (table_in_lds)
-        for (int i = threadIdx.x; i <= n_tensors; i += kBlockThreads) s_start[i] = chunk_start[i];
     s_mu[threadIdx.x] = dequant_unit<kMSpec>(static_cast<int>(threadIdx.x));
     s_vu[threadIdx.x] = dequant_unit<0u>(static_cast<int>(threadIdx.x));
     __syncthreads();
 
     const int lane = threadIdx.x & (kWaveLanes - 1);
-    const int32_t wave_stride = static_cast<int32_t>(gridDim.x) * (kBlockThreads / kWaveLanes);
-    int32_t c = __builtin_amdgcn_readfirstlane(
+    const int64_t wave = __builtin_amdgcn_readfirstlane(
         static_cast<int32_t>(blockIdx.x) * (kBlockThreads / kWaveLanes) + (threadIdx.x >> 6));
-    int t = 0;
+    const int64_t c0 = wave * run;
+    if (c0 >= total_chunks) return;
+    const int32_t c1 = static_cast<int32_t>(c0 + run < total_chunks ? c0 + run : total_chunks);
 
-    for (; c < total_chunks; c += wave_stride) {
-        // owning tensor of chunk c (uniform across the wavefront)
-        if (table_in_lds) {
-            while (c >= s_start[t + 1]) ++t;
-        } else {
-            while (c >= chunk_start[t + 1]) ++t;
-        }
+    // last tensor whose first chunk is <= c0
+    int lo = 0, hi = n_tensors - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (chunk_start[mid] <= c0) lo = mid;
+        else hi = mid - 1;
+    }
+    int t = __builtin_amdgcn_readfirstlane(lo);
+    for (int32_t c = static_cast<int32_t>(c0); c < c1; ++c) {
+        while (c >= chunk_start[t + 1]) ++t;
         t = __builtin_amdgcn_readfirstlane(t);
-        const int32_t first = table_in_lds ? s_start[t] : chunk_start[t];
         const DevTensor d = tensors[t];
-        const int64_t e0 = static_cast<int64_t>(c - first) * kChunkElems + lane * kLaneElems;
-        const int cnt = lane_count(d.numel, e0);
-
-        // ---- loads (missing elements read as zero)
-        uint32_t pw[8], gw[8], rw[MB == 32 ? 8 : 4], mw[4], vw[4];
-        load_u16x16(d.param + e0, cnt, pw);
-        load_u16x16(d.grad + e0, cnt, gw);
-        if constexpr (MB == 32) load_u16x16(static_cast<const uint16_t *>(d.rho) + e0, cnt, rw);
-        else load_u8x16(static_cast<const uint8_t *>(d.rho) + e0, cnt, rw);
-        load_u8x16(d.m_codes + e0, cnt, mw);
-        load_u8x16(d.v_codes + e0, cnt, vw);
-        uint32_t smb = 0u, svb = 0u;
-        if (cnt > 0) {
-            smb = d.m_scales[e0 / kGroup];
-            svb = d.v_scales[e0 / kGroup];
-        }
-        const float ms = f16_value(smb);
-        const float vs = f16_value(svb);
-
-        // ---- dequantize, reconstruct, AdamW
-        float m1[16], q1[16], th1[16];      // q1: what the variance quantizer sees
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const uint32_t hs = (j & 1) ? (pw[j >> 1] & 0xFFFF0000u) : (pw[j >> 1] << 16);
-            int32_t r;
-            if constexpr (MB == 32) r = shalf(rw, j);
-            else r = sbyte(rw, j);
-            const float theta = reconstruct_elem<MB>(hs, r);
-            const float g = (j & 1) ? bf16_hi(gw[j >> 1]) : bf16_lo(gw[j >> 1]);
-
-            const float m0 = s_mu[ubyte(mw, j)] * ms;
-            const float a0 = s_vu[ubyte(vw, j)] * vs;
-            const float v0 = COMP ? a0 * a0 : a0;
-
-            const float thd = theta * sc.cwd;
-            const float m_decay = sc.b1 * m0;
-            const float m_new = sc.c1 * g;
-            const float m = m_decay + m_new;
-            const float v_decay = sc.b2 * v0;
-            const float cg = sc.c2 * g;
-            const float v_new = cg * g;
-            const float v = v_decay + v_new;
-            const float rt = sqrtf(v);
-            const float den = rt * sc.k2 + sc.eps;
-            const float num = sc.alpha * m;
-            const float upd = num / den;
-            th1[j] = thd - upd;
-            m1[j] = m;
-            q1[j] = COMP ? rt : v;
-        }
-        if (cnt < kLaneElems) {             // zero pad of the ragged last group
-#pragma unroll
-            for (int j = 0; j < 16; ++j)
-                if (j >= cnt) { m1[j] = 0.0f; q1[j] = 0.0f; }
-        }
-
-        // ---- requantize m and v: group max over the lane pair
-        float am = 0.0f, av = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            am = fmaxf(am, fabsf(m1[j]));
-            av = fmaxf(av, q1[j]);
-        }
-        am = pair_max(am);
-        av = pair_max(av);
-        const uint32_t sm_out = f16_bits(am);
-        const uint32_t sv_out = f16_bits(av);
-        const float dm = group_divisor(sm_out);
-        const float dv = group_divisor(sv_out);
-
-        uint32_t mo[4] = {0u, 0u, 0u, 0u}, vo[4] = {0u, 0u, 0u, 0u};
-        uint32_t po[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-        uint32_t ro[MB == 32 ? 8 : 4] = {};
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            mo[j >> 2] |= code_byte<kMSpec>(m1[j] / dm) << (8 * (j & 3));
-            vo[j >> 2] |= code_byte<kVSpec>(q1[j] / dv) << (8 * (j & 3));
-            uint32_t hi, r;
-            split_elem<MB>(th1[j], hi, r);
-            po[j >> 1] |= hi << (16 * (j & 1));
-            if constexpr (MB == 32) ro[j >> 1] |= r << (16 * (j & 1));
-            else ro[j >> 2] |= r << (8 * (j & 3));
-        }
-
-        // ---- stores
-        store_u16x16(d.param + e0, cnt, po);
-        if constexpr (MB == 32) store_u16x16(static_cast<uint16_t *>(d.rho) + e0, cnt, ro);
-        else store_u8x16(static_cast<uint8_t *>(d.rho) + e0, cnt, ro);
-        store_u8x16(d.m_codes + e0, cnt, mo);
-        store_u8x16(d.v_codes + e0, cnt, vo);
-        if ((lane & 1) == 0 && cnt > 0) {
-            d.m_scales[e0 / kGroup] = static_cast<uint16_t>(sm_out);
-            d.v_scales[e0 / kGroup] = static_cast<uint16_t>(sv_out);
-        }
+        const int64_t off = static_cast<int64_t>(c - chunk_start[t]) * kChunkElems;
+        if (off + kChunkElems <= d.numel) step_chunk<MB, COMP, true>(d, off, lane, sc, s_mu, s_vu);
+        else step_chunk<MB, COMP, false>(d, off, lane, sc, s_mu, s_vu);
     }
 }
 
@@ -580,30 +803,15 @@ namespace {
 
 template <int MB, bool COMP>
 hipError_t step_variant(const DevTensor *tensors, const int32_t *chunk_start, int n_tensors,
-                        int32_t total_chunks, const StepScalars &sc, int blocks_per_cu, int cus,
-                        hipStream_t st)
+                        int32_t total_chunks, int32_t run, const StepScalars &sc, hipStream_t st)
 {
-    const size_t lds = n_tensors < kMaxLdsTensors ? sizeof(int32_t) * (n_tensors + 1) : 0;
+    const int64_t waves = (total_chunks + run - 1) / run;
     const int64_t waves_per_block = kBlockThreads / kWaveLanes;
-    const int64_t need = (total_chunks + waves_per_block - 1) / waves_per_block;
-    int64_t grid = static_cast<int64_t>(blocks_per_cu) * cus;
-    if (grid > need) grid = need;
-    if (grid < 1) grid = 1;
+    const int64_t grid = (waves + waves_per_block - 1) / waves_per_block;
     hipLaunchKernelGGL((adamw_step_kernel<MB, COMP>), dim3(static_cast<unsigned>(grid)),
-                       dim3(kBlockThreads), lds, st, tensors, chunk_start, n_tensors,
-                       total_chunks, sc);
+                       dim3(kBlockThreads), 0, st, tensors, chunk_start, n_tensors,
+                       total_chunks, run, sc);
     return hipGetLastError();
-}
-
-template <int MB, bool COMP>
-int occupancy_blocks(int n_tensors)
-{
-    const size_t lds = n_tensors < kMaxLdsTensors ? sizeof(int32_t) * (n_tensors + 1) : 0;
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, adamw_step_kernel<MB, COMP>,
-                                                     kBlockThreads, lds) != hipSuccess || nb < 1)
-        nb = 1;
-    return nb;
 }
 
 }  // namespace
@@ -613,27 +821,17 @@ hipError_t launch_adamw_step(const DevTensor *tensors, const int32_t *chunk_star
                              bool companded, hipStream_t st)
 {
     if (total_chunks <= 0) return hipSuccess;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    int cus = 0;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-
-    // Workgroups resident per CU: the occupancy limit, unless the tuning
-    // variable FLASHOPT_BLOCKS_PER_CU asks for fewer (or more) of them.
-    int bpc = 0;
-    if (const char *env = getenv("FLASHOPT_BLOCKS_PER_CU")) bpc = atoi(env);
-    const bool m32 = master_bits == 32;
-    if (bpc <= 0) {
-        if (m32) bpc = companded ? occupancy_blocks<32, true>(n_tensors) : occupancy_blocks<32, false>(n_tensors);
-        else bpc = companded ? occupancy_blocks<24, true>(n_tensors) : occupancy_blocks<24, false>(n_tensors);
+    // Consecutive chunks per wavefront; FLASHOPT_CHUNKS_PER_WAVE tunes it.
+    int32_t run = 4;
+    if (const char *env = getenv("FLASHOPT_CHUNKS_PER_WAVE")) {
+        const int v = atoi(env);
+        if (v >= 1 && v <= 1024) run = v;
     }
-    if (m32)
-        return companded ? step_variant<32, true>(tensors, chunk_start, n_tensors, total_chunks, sc, bpc, cus, st)
-                         : step_variant<32, false>(tensors, chunk_start, n_tensors, total_chunks, sc, bpc, cus, st);
-    return companded ? step_variant<24, true>(tensors, chunk_start, n_tensors, total_chunks, sc, bpc, cus, st)
-                     : step_variant<24, false>(tensors, chunk_start, n_tensors, total_chunks, sc, bpc, cus, st);
+    if (master_bits == 32)
+        return companded ? step_variant<32, true>(tensors, chunk_start, n_tensors, total_chunks, run, sc, st)
+                         : step_variant<32, false>(tensors, chunk_start, n_tensors, total_chunks, run, sc, st);
+    return companded ? step_variant<24, true>(tensors, chunk_start, n_tensors, total_chunks, run, sc, st)
+                     : step_variant<24, false>(tensors, chunk_start, n_tensors, total_chunks, run, sc, st);
 }
 
 }  // namespace flashopt

@@ -1,0 +1,93 @@
+// Exact fp32 building blocks for gfx950, used by the codec and step kernels.
+//
+// Every function here returns the same bits as the correctly rounded IEEE
+// operation it replaces, over the stated domain.  The domains were checked
+// exhaustively on gfx950 against the compiler's correctly rounded division
+// and sqrt (tests/hip/fastmath_check.hip, run by the GPU test suite):
+//   recip_cr       every fp32 significand, every positive finite fp16 value;
+//   div_by_recip   every fp16 divisor significand x every fp32 dividend
+//                  significand (2^33 pairs);
+//   softsign       every y in [-1.5, 1.5];
+//   sqrt_cr        every x in [0, 2^64);
+//   byte_u8        every fp32 pattern (v_cvt_pk_u8_f32 == clamp(rint(x), 0, 255),
+//                  NaN -> 0).
+// Only fma, mul, add, v_rcp_f32 / v_rsq_f32 and integer ops are used, so the
+// results do not depend on the FP mode beyond round-to-nearest-even with
+// fp32 denormals kept.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flashopt {
+namespace math {
+
+// Correctly rounded 1/d for d and 1/d normal: hardware reciprocal (1 ulp)
+// refined by one Newton step on the residual.
+__device__ __forceinline__ float recip_cr(float d)
+{
+    const float r0 = __builtin_amdgcn_rcpf(d);
+    const float e = __builtin_fmaf(-d, r0, 1.0f);
+    return __builtin_fmaf(e, r0, r0);
+}
+
+// Correctly rounded a/d given r = recip_cr(d) (Markstein's correction:
+// q0 = a r, then one FMA residual step).  Exact whenever a/d is normal and
+// the residual a - q0 d does not underflow, i.e. for |a/d| >= 2^-100 with
+// d an fp16 scale; smaller quotients may be off by one unit, which cannot
+// change an 8-bit code (they round to code 0 either way).
+__device__ __forceinline__ float div_by_recip(float a, float d, float r)
+{
+    const float q0 = a * r;
+    const float rem = __builtin_fmaf(-q0, d, a);
+    return __builtin_fmaf(rem, r, q0);
+}
+
+// Softsign companding (2y) / (1 + |y|), correctly rounded for |y| <= 1.5
+// (group quotients never exceed 1.5: the fp16 scale is at least 2/3 of the
+// group max).  It runs the unrefined-reciprocal Markstein step on the
+// halved operands y / ((1 + |y|) / 2): halving is exact, the hardware
+// reciprocal of the halved denominator is exactly twice the reciprocal of the
+// full one, so every product and residual is the full-size one scaled by an
+// exact power of two and the result is bit-identical, one multiply cheaper.
+// A zero input returns +0 (the code is 0 either way).
+__device__ __forceinline__ float softsign(float y)
+{
+    const float hden = __builtin_fmaf(fabsf(y), 0.5f, 0.5f);   // (1 + |y|) / 2, exact
+    const float r2 = __builtin_amdgcn_rcpf(hden);               // 2 / (1 + |y|), approx.
+    const float q0 = y * r2;
+    const float rem = __builtin_fmaf(-q0, hden, y);
+    return __builtin_fmaf(rem, r2, q0);
+}
+
+// Correctly rounded sqrt(x) for 0 <= x < 2^64.  The input is first scaled by
+// 2^64 (exact), which puts every denormal into the range where one residual
+// correction of x * rsq(x) is exact; the result is scaled back by 2^-32
+// (exact, sqrt results are normal).  rsq(0) = inf is clamped so that
+// sqrt(0) = 0.
+__device__ __forceinline__ float sqrt_cr(float x)
+{
+    const float xs = x * 0x1p64f;
+    const float y = fminf(__builtin_amdgcn_rsqf(xs), 0x1.fffffep127f);
+    const float s = xs * y;
+    const float h = 0.5f * y;
+    const float r = __builtin_fmaf(-s, s, xs);
+    return __builtin_fmaf(r, h, s) * 0x1p-32f;
+}
+
+// v_cvt_i32_f32: truncation toward zero, saturating, NaN -> 0.
+__device__ __forceinline__ int32_t cvt_i32(float x)
+{
+    int32_t r;
+    asm("v_cvt_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+    return r;
+}
+
+// Clamp to [lo, hi] (v_med3_i32 after instruction selection).
+__device__ __forceinline__ int32_t clamp_i32(int32_t x, int32_t lo, int32_t hi)
+{
+    return x < lo ? lo : (x > hi ? hi : x);
+}
+
+}  // namespace math
+}  // namespace flashopt

@@ -1,0 +1,117 @@
+// GPU check of the short exact fp32 sequences in flashopt_math.h against the
+// compiler's correctly rounded division and sqrt on the same device.  Built
+// in-tree as libfastmath_check.so and driven by tests/test_gpu_fastmath.py.
+// Each entry point runs one exhaustive (or large structured) sweep and returns
+// the number of mismatching inputs, or -1 on a HIP error.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "flashopt_math.h"
+
+using namespace flashopt::math;
+
+namespace {
+
+// per-thread count, one atomic per thread at the end
+__device__ void flush(unsigned long long *bad, unsigned long long c)
+{
+    if (c) atomicAdd(bad, c);
+}
+
+__device__ __forceinline__ bool same(float a, float b) { return __float_as_uint(a) == __float_as_uint(b); }
+
+__global__ void k_sqrt(unsigned long long *bad)
+{
+    unsigned long long c = 0;
+    // every x in [0, 2^64): patterns 0 .. 0x5F7FFFFF
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < 0x5F800000ull;
+         i += (uint64_t)gridDim.x * blockDim.x) {
+        const float x = __uint_as_float((uint32_t)i);
+        c += !same(sqrt_cr(x), sqrtf(x));
+    }
+    flush(bad, c);
+}
+
+__global__ void k_recip(unsigned long long *bad)
+{
+    unsigned long long c = 0;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (1ull << 23);
+         i += (uint64_t)gridDim.x * blockDim.x) {
+        // every significand in [1, 2), at three exponents
+        const float d = __uint_as_float(0x3F800000u | (uint32_t)i);
+        c += !same(recip_cr(d), 1.0f / d);
+        c += !same(recip_cr(d * 0x1p-60f), 1.0f / (d * 0x1p-60f));
+        c += !same(recip_cr(d * 0x1p60f), 1.0f / (d * 0x1p60f));
+        if (i < 0x7C00u && i > 0u) {       // every positive finite fp16 value
+            const float h = (float)__builtin_bit_cast(_Float16, (unsigned short)i);
+            c += !same(recip_cr(h), 1.0f / h);
+        }
+    }
+    flush(bad, c);
+}
+
+__global__ void k_div_by_recip(unsigned long long *bad)
+{
+    unsigned long long c = 0;
+    // every fp16 divisor significand (10 bits) x every dividend significand
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (1ull << 33);
+         i += (uint64_t)gridDim.x * blockDim.x) {
+        const float d = __uint_as_float(0x3F800000u | ((uint32_t)(i >> 23) << 13));
+        const float a = __uint_as_float(0x3F800000u | (uint32_t)(i & 0x7FFFFFu));
+        c += !same(div_by_recip(a, d, recip_cr(d)), a / d);
+    }
+    flush(bad, c);
+}
+
+__global__ void k_softsign(unsigned long long *bad)
+{
+    unsigned long long c = 0;
+    // every y in [0, 1.5] (the sequence is odd-symmetric in y)
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i <= 0x3FC00000ull;
+         i += (uint64_t)gridDim.x * blockDim.x) {
+        const float y = __uint_as_float((uint32_t)i);
+        const float num = 2.0f * y;
+        const float den = 1.0f + fabsf(y);
+        c += !same(softsign(y), num / den);
+        if (y != 0.0f) c += !same(softsign(-y), (-num) / den);
+    }
+    flush(bad, c);
+}
+
+__global__ void k_cvt_pk_u8(unsigned long long *bad)
+{
+    unsigned long long c = 0;
+    // every fp32 pattern: v_cvt_pk_u8_f32 == clamp(rint(x), 0, 255), NaN -> 0
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (1ull << 32);
+         i += (uint64_t)gridDim.x * blockDim.x) {
+        const float x = __uint_as_float((uint32_t)i);
+        const unsigned got = __builtin_amdgcn_cvt_pk_u8_f32(x, 2, 0u) >> 16;
+        unsigned want = 0u;
+        if (x == x) want = (unsigned)fminf(fmaxf(rintf(x), 0.0f), 255.0f);
+        c += got != want;
+    }
+    flush(bad, c);
+}
+
+template <typename K>
+long long run(K kernel, unsigned grid)
+{
+    unsigned long long *d = nullptr, h = 0;
+    if (hipMalloc(&d, sizeof(h)) != hipSuccess) return -1;
+    if (hipMemset(d, 0, sizeof(h)) != hipSuccess) { (void)hipFree(d); return -1; }
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, 0, d);
+    const bool ok = hipGetLastError() == hipSuccess && hipDeviceSynchronize() == hipSuccess &&
+                    hipMemcpy(&h, d, sizeof(h), hipMemcpyDeviceToHost) == hipSuccess;
+    (void)hipFree(d);
+    return ok ? (long long)h : -1;
+}
+
+}  // namespace
+
+extern "C" {
+long long fastmath_check_sqrt(void) { return run(k_sqrt, 65536); }
+long long fastmath_check_recip(void) { return run(k_recip, 8192); }
+long long fastmath_check_div_by_recip(void) { return run(k_div_by_recip, 65536); }
+long long fastmath_check_softsign(void) { return run(k_softsign, 65536); }
+long long fastmath_check_cvt_pk_u8(void) { return run(k_cvt_pk_u8, 65536); }
+}

@@ -1,0 +1,37 @@
+"""GPU check of the short exact fp32 sequences the kernels use instead of the
+generic correctly rounded division / sqrt expansions (flashopt_math.h):
+each sweep compares against the compiler's correctly rounded operation on the
+same device and must find no mismatch.  Sweeps: sqrt over every x in
+[0, 2^64); reciprocal over every significand (three exponents) and every fp16
+value; division by an fp16 scale over every divisor x dividend significand
+pair (2^33); softsign over every |y| <= 1.5; v_cvt_pk_u8_f32 over all 2^32
+patterns."""
+import ctypes
+import os
+
+import pytest
+
+from tests._gpu import require_gpu
+
+pytestmark = pytest.mark.gpu
+
+LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hip", "libfastmath_check.so")
+CHECKS = ["sqrt", "recip", "div_by_recip", "softsign", "cvt_pk_u8"]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    require_gpu()
+    if not os.path.exists(LIB):
+        raise RuntimeError(f"{LIB} is not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(LIB)
+    for c in CHECKS:
+        getattr(L, "fastmath_check_" + c).restype = ctypes.c_longlong
+    return L
+
+
+@pytest.mark.parametrize("check", CHECKS)
+def test_exact(lib, check):
+    bad = getattr(lib, "fastmath_check_" + check)()
+    print(f"fastmath {check}: {bad} mismatches", flush=True)
+    assert bad == 0

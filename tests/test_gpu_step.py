@@ -126,11 +126,11 @@ def test_deterministic_across_runs_and_launch_shapes():
     require_gpu()
     sizes = [1 << 16, 3000, 1 << 18]
     results = []
-    for bpc in (None, "1", "3"):
-        if bpc is None:
-            os.environ.pop("FLASHOPT_BLOCKS_PER_CU", None)
+    for run in (None, "1", "16"):
+        if run is None:
+            os.environ.pop("FLASHOPT_CHUNKS_PER_WAVE", None)
         else:
-            os.environ["FLASHOPT_BLOCKS_PER_CU"] = bpc
+            os.environ["FLASHOPT_CHUNKS_PER_WAVE"] = run
         params = [W.init_param(n, device="cuda", seed=70 + i) for i, n in enumerate(sizes)]
         opt = F.FlashAdamW(params, master_bits=24, **HP)
         for t in range(1, 4):
@@ -139,7 +139,7 @@ def test_deterministic_across_runs_and_launch_shapes():
         results.append([torch.cat([s.param.view(torch.int16).float(), s.rho.float(),
                                    s.m_codes.float(), s.v_codes.float()]).cpu()
                         for s in opt.states])
-    os.environ.pop("FLASHOPT_BLOCKS_PER_CU", None)
+    os.environ.pop("FLASHOPT_CHUNKS_PER_WAVE", None)
     for r in results[1:]:
         for a, b in zip(results[0], r):
             assert torch.equal(a, b)
