@@ -183,6 +183,7 @@ flashopt_status flashopt_adamw_step(const flashopt_tensor *tensors, int n_tensor
     // The kernel's short division is exact for denominators sqrt(v) k2 + eps in
     // [2^-100, 2^100]; sqrt(v) < 2^32 on its fast path.
     sc.fast_div = (sc.eps >= 0x1p-100f && sc.k2 <= 0x1p60f) ? 1 : 0;
+    sc.num_max = sc.fast_div ? sc.eps * 0x1p100f : 0.0f;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     int dev = 0;

@@ -34,6 +34,11 @@ namespace {
 
 // ----------------------------------------------------------------- helpers
 
+// math::sqrt_cr is exact for the bit patterns [0, 0x5F800000): +0 up to
+// below 2^64.  Negative values (sign bit), infinities and NaNs all compare
+// at or above this bound as unsigned patterns.
+constexpr uint32_t kSqrtFastEnd = 0x5F800000u;
+
 // bf16 halves of a 32-bit word holding two consecutive elements
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -409,6 +414,27 @@ __device__ __forceinline__ void split_pack_exact(const float (&x)[16], uint32_t 
     }
 }
 
+// Signed codes of a lane's 16 group quotients with the biased rounding of
+// flashopt_math.h (finite inputs only; callers send lanes holding NaN or
+// infinite values to encode16).
+template <bool SOFTSIGN>
+__device__ __forceinline__ void encode16_s8_finite(const float (&a)[16], const GroupDiv &gd,
+                                                   uint32_t (&out)[4])
+{
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float y = math::div_by_recip(a[4 * k + i], gd.d, gd.r);
+            if (SOFTSIGN) y = math::softsign(y);
+            b[i] = math::biased_code_s8(y * 127.0f);
+        }
+        out[k] = pack_bytes(static_cast<int32_t>(b[0]), static_cast<int32_t>(b[1]),
+                            static_cast<int32_t>(b[2]), static_cast<int32_t>(b[3])) ^ 0x80808080u;
+    }
+}
+
 // ------------------------------------------------------- standalone codec
 
 template <unsigned SPEC>
@@ -423,12 +449,12 @@ quantize_kernel(const float *__restrict__ x, int64_t n, void *__restrict__ codes
     float a[16];
     load_f32x16(x + e0, cnt, a);             // missing elements are the zero pad
     if (SPEC & FLASHOPT_Q_SQRT) {
-        float amax_in = 0.0f;
+        uint32_t ubits = 0u;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) amax_in = fmaxf(amax_in, a[j]);
+        for (int j = 0; j < 16; ++j) ubits = max(ubits, __float_as_uint(a[j]));
 #pragma unroll
         for (int j = 0; j < 16; ++j) a[j] = math::sqrt_cr(a[j]);
-        if (!(amax_in < 0x1p64f)) {          // rare: inputs beyond the fast sqrt's range
+        if (ubits >= kSqrtFastEnd) {         // rare: inputs outside the fast sqrt's range
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 float v = 0.0f;
@@ -437,9 +463,10 @@ quantize_kernel(const float *__restrict__ x, int64_t n, void *__restrict__ codes
             }
         }
     }
-    float amax = kSigned ? 0.0f : -__builtin_inff();
+    // maxNum over the elements: NaNs are ignored unless all are NaN
+    float amax = kSigned ? fabsf(a[0]) : a[0];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) amax = fmaxf(amax, kSigned ? fabsf(a[j]) : a[j]);
+    for (int j = 1; j < 16; ++j) amax = fmaxf(amax, kSigned ? fabsf(a[j]) : a[j]);
     amax = pair_max(amax);
     const uint32_t s = f16_bits(amax);
 
@@ -523,6 +550,59 @@ reconstruct_kernel(const uint16_t *__restrict__ param, const void *__restrict__ 
 
 // ---------------------------------------------------- fused FlashAdamW step
 
+// The generic recomputation of one lane's outputs (see step_chunk): reload
+// the lane's inputs, redo the element arithmetic with correctly rounded
+// division and sqrt, and encode m and split theta with the NaN-safe element
+// routines.  The variance codes and both scales do not depend on these paths.
+template <int MB, bool COMP>
+__device__ __forceinline__ void lane_exact(const DevTensor &d, int64_t off, int lane, int cnt,
+                                        const StepScalars &sc, const float *s_mu,
+                                        const float *s_vu, const GroupDiv &gdm, uint32_t (&mo)[4],
+                                        uint32_t (&po)[8], uint32_t (&ro)[MB == 32 ? 8 : 4])
+{
+    constexpr unsigned kMSpec = COMP ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
+    // an opaque copy of the lane index keeps the compiler from reusing the
+    // common path's loads, whose values would then stay live up to here
+    asm volatile("" : "+v"(lane));
+    const int lofs = lane * kLaneElems;
+    uint32_t pw[8], gw[8], rw[MB == 32 ? 8 : 4], mw[4], vw[4];
+    load_u16x16(d.param + off + lofs, cnt, pw);
+    load_u16x16(d.grad + off + lofs, cnt, gw);
+    const uint8_t *rp = static_cast<const uint8_t *>(d.rho) + (off + lofs) * (MB == 32 ? 2 : 1);
+    if constexpr (MB == 32) load_u16x16(reinterpret_cast<const uint16_t *>(rp), cnt, rw);
+    else load_u8x16(rp, cnt, rw);
+    load_u8x16(d.m_codes + off + lofs, cnt, mw);
+    load_u8x16(d.v_codes + off + lofs, cnt, vw);
+    const float ms = cnt > 0 ? f16_value(ld_u16(d.m_scales + off / kGroup + (lane >> 1))) : 0.0f;
+    const float vs = cnt > 0 ? f16_value(ld_u16(d.v_scales + off / kGroup + (lane >> 1))) : 0.0f;
+    float m1[16], th1[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const uint32_t hs = (j & 1) ? (pw[j >> 1] & 0xFFFF0000u) : (pw[j >> 1] << 16);
+        int32_t r;
+        if constexpr (MB == 32) r = shalf(rw, j);
+        else r = sbyte(rw, j);
+        const float theta = reconstruct_elem<MB>(hs, r);
+        const float g = (j & 1) ? bf16_hi(gw[j >> 1]) : bf16_lo(gw[j >> 1]);
+        const float m0 = s_mu[ubyte(mw, j)] * ms;
+        const float a0 = s_vu[ubyte(vw, j)] * vs;
+        const float v0 = COMP ? a0 * a0 : a0;
+        const float m_decay = sc.b1 * m0;
+        const float m_new = sc.c1 * g;
+        const float m = m_decay + m_new;
+        const float v_decay = sc.b2 * v0;
+        const float cg = sc.c2 * g;
+        const float v_new = cg * g;
+        const float v = v_decay + v_new;
+        const float den = sqrtf(v) * sc.k2 + sc.eps;
+        const float num = sc.alpha * m;
+        th1[j] = theta * sc.cwd - num / den;
+        m1[j] = j < cnt ? m : 0.0f;
+    }
+    encode16<kMSpec>(m1, gdm, mo);
+    split_pack_exact<MB>(th1, po, ro);
+}
+
 // One 1024-element chunk of one tensor, processed by one wavefront: each lane
 // loads 16 elements of every stream, dequantizes m and v, rebuilds the
 // master, applies AdamW, finds the group maxima (one DPP exchange with the
@@ -580,7 +660,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor &d, int64_t off, int 
 
     // ---- dequantize, reconstruct, moments
     float thd[16], m1[16], v1[16];
-    float vmax = 0.0f;
+    uint32_t vbits = 0u;                    // unsigned max of the v1 bit patterns
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const uint32_t hs = (j & 1) ? (pw[j >> 1] & 0xFFFF0000u) : (pw[j >> 1] << 16);
@@ -602,7 +682,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor &d, int64_t off, int 
         const float cg = sc.c2 * g;
         const float v_new = cg * g;
         v1[j] = v_decay + v_new;
-        vmax = fmaxf(vmax, v1[j]);
+        vbits = max(vbits, __float_as_uint(v1[j]));
     }
     if (!FULL) {                            // zero pad of the ragged last group
 #pragma unroll
@@ -610,49 +690,71 @@ __device__ __forceinline__ void step_chunk(const DevTensor &d, int64_t off, int 
             if (j >= cnt) { m1[j] = 0.0f; v1[j] = 0.0f; }
     }
 
-    // ---- sqrt(v1) and the update (alpha m1) / (sqrt(v1) k2 + eps)
-    float rt[16], upd[16];
+    // ---- sqrt(v1)
+    float rt[16];
+    if (vbits < kSqrtFastEnd) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) rt[j] = math::sqrt_cr(v1[j]);
-    if (!(vmax < 0x1p64f)) {                // rare: v beyond the fast sqrt's range
+        for (int j = 0; j < 16; ++j) rt[j] = math::sqrt_cr(v1[j]);
+    } else {                                // rare: v beyond the fast sqrt's range
 #pragma unroll
         for (int j = 0; j < 16; ++j) rt[j] = sqrtf(v1[j]);
     }
-    // lane maxima of |m1| and of what the variance quantizer sees
-    float am = 0.0f, av = 0.0f;
+
+    // ---- lane maxima of |m1|, of what the variance quantizer sees, of sqrt(v1)
+    // (the maxima start from the first element: a group of NaNs only has a
+    // NaN maximum, as the IEEE maxNum reduction over its elements gives)
+    float am = fabsf(m1[0]), av = COMP ? rt[0] : v1[0], rmax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         am = fmaxf(am, fabsf(m1[j]));
-        av = fmaxf(av, COMP ? rt[j] : v1[j]);
+        if (COMP) av = fmaxf(av, rt[j]);
+        else { av = fmaxf(av, v1[j]); rmax = fmaxf(rmax, rt[j]); }
     }
+    if (COMP) rmax = av;
+
+    // ---- the update theta (1 - lr wd) - (alpha m1) / (sqrt(v1) k2 + eps),
+    // with the short division when the lane's numerators and denominators
+    // lie in its exact domain (den <= den_hi, nonzero |num| >= tmin)
+    const float den_hi = rmax * sc.k2 + sc.eps;
+    const float tmin = fmaxf(0x1p-102f, den_hi * 0x1p-126f);
+    const uint32_t tkey = (__float_as_uint(tmin) << 1) - 1u;
+    uint32_t kmin = 0xFFFFFFFFu;          // min over nonzero |num| of its doubled pattern - 1
+    float th1[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const float den = rt[j] * sc.k2 + sc.eps;
         const float num = sc.alpha * m1[j];
-        upd[j] = num / den;
+        th1[j] = thd[j] - math::div_markstein(num, den, math::recip_cr(den));
+        const uint32_t key = (__float_as_uint(num) << 1) - 1u;
+        kmin = key < kmin ? key : kmin;
     }
-    float th1[16];
+    bool any_nan = false;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) th1[j] = thd[j] - upd[j];
+    for (int j = 0; j < 16; ++j) any_nan |= th1[j] != th1[j];
+    const bool exact = sc.fast_div == 0 || vbits >= kSqrtFastEnd || !(sc.alpha * am <= sc.num_max) ||
+                       kmin < tkey || any_nan;
 
     // ---- group maxima over the lane pair, scales
     am = pair_max(am);
     av = pair_max(av);
     const uint32_t sm_out = f16_bits(am);
     const uint32_t sv_out = f16_bits(av);
+    const GroupDiv gdm = group_div(sm_out);
 
-    // ---- codes, re-split, pack
-    uint32_t mo[4], vo[4];
-    encode16<kMSpec>(m1, group_div(sm_out), mo);
+    // ---- codes and the re-split with the short sequences
+    uint32_t mo[4], vo[4], po[8], ro[kRhoWords];
     if constexpr (COMP) encode16<kVSpec>(rt, group_div(sv_out), vo);
     else encode16<kVSpec>(v1, group_div(sv_out), vo);
-
-    uint32_t po[8], ro[kRhoWords];
-    bool any_nan = false;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) any_nan |= th1[j] != th1[j];
-    if (any_nan) split_pack_exact<MB>(th1, po, ro);   // rare: NaN masters
-    else split_pack<MB>(th1, po, ro);
+    if (!exact) {
+        encode16_s8_finite<COMP>(m1, gdm, mo);
+        split_pack<MB>(th1, po, ro);
+    } else {
+        // rare: a lane outside the short sequences' domains (tiny or huge
+        // numerators, NaN or infinite m or theta, unusual hyper-parameters)
+        // is recomputed from memory with the generic operations; nothing has
+        // been stored yet and the group scales above are already exact
+        lane_exact<MB, COMP>(d, off, lane, cnt, sc, s_mu, s_vu, gdm, mo, po, ro);
+    }
 
     // ---- stores
     if (FULL) {

@@ -10,7 +10,11 @@
 //   softsign       every y in [-1.5, 1.5];
 //   sqrt_cr        every x in [0, 2^64);
 //   byte_u8        every fp32 pattern (v_cvt_pk_u8_f32 == clamp(rint(x), 0, 255),
-//                  NaN -> 0).
+//                  NaN -> 0);
+//   div_markstein  2^32 random pairs of its stated domain plus every divisor
+//                  significand at the domain's edges;
+//   biased_code_s8 every fp32 p (low byte == clamp(rint(p), -127, 127) + 128
+//                  for non-NaN p).
 // Only fma, mul, add, v_rcp_f32 / v_rsq_f32 and integer ops are used, so the
 // results do not depend on the FP mode beyond round-to-nearest-even with
 // fp32 denormals kept.
@@ -58,6 +62,31 @@ __device__ __forceinline__ float softsign(float y)
     const float q0 = y * r2;
     const float rem = __builtin_fmaf(-q0, hden, y);
     return __builtin_fmaf(rem, r2, q0);
+}
+
+// Correctly rounded num / den given r = recip_cr(den) (one Markstein residual
+// step, with the residual taken as q0 den - num so that a zero numerator keeps
+// its sign), for den in [2^-100, 2^100] and num either zero or with
+// max(2^-102, 2^-126 den) <= |num| <= 2^100 den: then the residual is exact
+// (|num| >= 2^-102) and the quotient is a normal number, which is what
+// Markstein's theorem needs.  Callers route other numerators to the generic
+// division.
+__device__ __forceinline__ float div_markstein(float num, float den, float r)
+{
+    const float q0 = num * r;
+    const float e = __builtin_fmaf(q0, den, -num);
+    return __builtin_fmaf(-e, r, q0);
+}
+
+// Signed 8-bit code of p = y * 127 in its low byte, biased by +128: clamp to
+// [-127, 127] (v_med3_f32), then adding 1.5 * 2^23 + 128 rounds to an integer
+// with ties to even (the sum lies in [2^23, 2^24), where the fp32 spacing is
+// 1) and leaves rint(p) + 128 in the low byte of the pattern.  NaN inputs are
+// the caller's to route elsewhere.
+__device__ __forceinline__ uint32_t biased_code_s8(float p)
+{
+    const float c = __builtin_amdgcn_fmed3f(p, -127.0f, 127.0f);
+    return __float_as_uint(c + 12583040.0f);
 }
 
 // Correctly rounded sqrt(x) for 0 <= x < 2^64.  The input is first scaled by

@@ -13,7 +13,9 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflashopt.so")
+# FLASHOPT_LIB may point at another build of the same library (experiments).
+_LIB_PATH = os.environ.get("FLASHOPT_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libflashopt.so")
 
 FLASHOPT_OK, FLASHOPT_EINVAL, FLASHOPT_EALIGN, FLASHOPT_EWORKSPACE, FLASHOPT_EHIP = range(5)
 Q_SIGNED, Q_SQRT, Q_SOFTSIGN = 1, 2, 4

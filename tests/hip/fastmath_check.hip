@@ -93,6 +93,65 @@ __global__ void k_cvt_pk_u8(unsigned long long *bad)
     flush(bad, c);
 }
 
+__device__ __forceinline__ uint32_t mix(uint64_t i, uint32_t k)
+{
+    uint32_t h = (uint32_t)i * 2654435761u + k * 0x9E3779B9u + (uint32_t)(i >> 32) * 0x85EBCA6Bu;
+    h ^= h >> 15; h *= 0x2C1B3C6Du; h ^= h >> 12; h *= 0x297A2D39u; h ^= h >> 15;
+    return h;
+}
+
+// a float with random sign and significand and exponent field e (1..254)
+__device__ __forceinline__ float with_exp(uint32_t e, uint32_t h) { return __uint_as_float((h & 0x807FFFFFu) | (e << 23)); }
+
+__global__ void k_div_markstein(unsigned long long *bad)
+{
+    unsigned long long c = 0;
+    // den: exponent field in [27, 227) (2^-100 .. 2^100); num: zero, or an
+    // exponent field in [max(25, e_den - 125), min(254, e_den + 99)], i.e.
+    // max(2^-102, 2^-126 den) <= |num| <= 2^100 den
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (1ull << 32);
+         i += (uint64_t)gridDim.x * blockDim.x) {
+        const uint32_t h1 = mix(i, 1), h2 = mix(i, 2), h3 = mix(i, 3);
+        const uint32_t ed = 27u + h1 % 200u;
+        const float den = __uint_as_float((ed << 23) | (h2 & 0x7FFFFFu));
+        const uint32_t lo = ed >= 150u ? ed - 125u : 25u;
+        const uint32_t hi = ed + 99u < 254u ? ed + 99u : 254u;
+        float num;
+        if ((h1 >> 26) == 0u) num = (h3 >> 31) ? -0.0f : 0.0f;
+        else num = with_exp(lo + (h1 >> 8) % (hi - lo + 1u), h3);
+        c += !same(div_markstein(num, den, recip_cr(den)), num / den);
+    }
+    // every divisor significand, numerators at the edges of the domain
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (1ull << 23);
+         i += (uint64_t)gridDim.x * blockDim.x) {
+        const uint32_t sig = (uint32_t)i;
+        const uint32_t eds[3] = {27u, 127u, 226u};
+        for (int a = 0; a < 3; ++a) {
+            const uint32_t ed = eds[a];
+            const float den = __uint_as_float((ed << 23) | sig);
+            const uint32_t lo = ed >= 150u ? ed - 125u : 25u;
+            const uint32_t hi = ed + 99u < 254u ? ed + 99u : 254u;
+            const float nums[4] = {with_exp(lo, mix(i, 7)), with_exp(lo, 0u), with_exp(hi, mix(i, 8)),
+                                   with_exp(hi, 0x7FFFFFu)};
+            for (int b = 0; b < 4; ++b) c += !same(div_markstein(nums[b], den, recip_cr(den)), nums[b] / den);
+        }
+    }
+    flush(bad, c);
+}
+
+__global__ void k_biased_code(unsigned long long *bad)
+{
+    unsigned long long c = 0;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (1ull << 32);
+         i += (uint64_t)gridDim.x * blockDim.x) {
+        const float p = __uint_as_float((uint32_t)i);
+        if (p != p) continue;
+        const int want = (int)fminf(fmaxf(rintf(p), -127.0f), 127.0f) + 128;
+        c += (int)(biased_code_s8(p) & 0xFFu) != want;
+    }
+    flush(bad, c);
+}
+
 template <typename K>
 long long run(K kernel, unsigned grid)
 {
@@ -114,4 +173,6 @@ long long fastmath_check_recip(void) { return run(k_recip, 8192); }
 long long fastmath_check_div_by_recip(void) { return run(k_div_by_recip, 65536); }
 long long fastmath_check_softsign(void) { return run(k_softsign, 65536); }
 long long fastmath_check_cvt_pk_u8(void) { return run(k_cvt_pk_u8, 65536); }
+long long fastmath_check_div_markstein(void) { return run(k_div_markstein, 65536); }
+long long fastmath_check_biased_code(void) { return run(k_biased_code, 65536); }
 }

@@ -92,6 +92,46 @@ def test_all_codes_dequantize(orc):
         assert same.all(), spec
 
 
+def _f16_nan(s: np.ndarray) -> np.ndarray:
+    return ((s & 0x7C00) == 0x7C00) & ((s & 0x03FF) != 0)
+
+
+@pytest.mark.parametrize("spec", range(8))
+def test_non_finite_groups(orc, spec):
+    """Non-finite inputs lie outside the contract but give defined results:
+    a group maximum is the IEEE maxNum over its elements (NaN only when all
+    of them are NaN), NaN codes are 0, an infinite scale gives codes 0.  A
+    NaN matches any NaN (the pages fix no NaN payload or sign); all else is
+    bit-exact."""
+    require_gpu()
+    nan, inf = np.float32(np.nan), np.float32(np.inf)
+    rng = np.random.default_rng(7 + spec)
+    x = rng.standard_normal((10, 32)).astype(np.float32)
+    x[0, :] = nan                            # a group of NaNs only
+    x[1, 3] = nan                            # one NaN among numbers
+    x[2, 5] = inf
+    x[3, 7] = -inf
+    x[4, :] = -inf
+    x[5, :16] = nan                          # one lane of NaNs, the other lane numbers
+    x[6, 16:] = nan
+    x[7, 0], x[7, 1] = nan, inf
+    x[8, :] = 0.0
+    x[8, 9] = nan
+    tail = rng.standard_normal(17).astype(np.float32)
+    tail[4] = nan                            # ragged last group, zero padded
+    x = np.concatenate([x.reshape(-1), tail])
+    q_d, s_d = F.flashopt_quantize(torch.from_numpy(x).cuda(), spec)
+    d_d = F.flashopt_dequantize(q_d, s_d, spec)
+    torch.cuda.synchronize()
+    q_o, s_o = orc.quantize(x, spec)
+    s_g = u16(s_d)
+    assert ((s_g == s_o) | (_f16_nan(s_g) & _f16_nan(s_o))).all(), (spec, s_g, s_o)
+    assert (host(q_d) == q_o).all(), spec
+    d_o = orc.dequantize(q_o, s_o, spec)
+    d_g = host(d_d)
+    assert ((d_g.view(np.uint32) == d_o.view(np.uint32)) | (np.isnan(d_g) & np.isnan(d_o))).all()
+
+
 def test_empty_is_noop():
     require_gpu()
     x = torch.empty(0, device="cuda")

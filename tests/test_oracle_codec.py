@@ -259,3 +259,22 @@ def test_nmse_closed_forms(orc):
     assert orc.nmse(x, np.zeros_like(x)) == 1.0
     assert orc.nmse(np.zeros_like(x), x) == 0.0
     assert abs(orc.nmse(x, 2 * x) - 1.0) < 1e-12
+
+
+def test_non_finite_group_maxima(orc):
+    """Non-finite inputs (outside the contract): the group maximum is the
+    IEEE maxNum over the group, so a NaN among numbers is ignored and only a
+    group of NaNs has a NaN scale; NaN elements get code 0 either way."""
+    x = np.full((3, 32), 0.25, np.float32)
+    x[0, 7] = np.nan                                # ignored by the maximum
+    x[1, :] = np.nan                                # nothing but NaN
+    x[2, :] = np.float32(-2.0)
+    x[2, 30] = np.nan
+    q, s = orc.quantize(x.reshape(-1), 5)
+    assert s[0] == 0x3400 and s[2] == 0x4000        # fp16 0.25 and 2.0
+    assert (s[1] & 0x7C00) == 0x7C00 and (s[1] & 0x03FF) != 0
+    q = q.reshape(3, 32)
+    assert q[0, 7] == 0 and (q[1] == 0).all() and q[2, 30] == 0
+    # a non-NaN element of a group with a NaN keeps the code it would have had
+    q_clean, _ = orc.quantize(np.full(32, 0.25, np.float32), 5)
+    assert (np.delete(q[0], 7) == q_clean[:31]).all()
