@@ -8,9 +8,15 @@ one multi-tensor launch per step.  Inputs are synthetic and resident in HBM
 before timing starts (bf16 weights ~ N(0, 0.02^2); one bf16 gradient set
 N(0, 1e-3^2) times a per-tensor lognormal factor, reused by every step).
 
+Other configurations (reported beside the default, not as its value):
+--workload decoder-1b-list (199 tensors, 1,195,991,040 params), --master-bits
+32 | 0 (0: no split, the page's master_weight_bits=None), --linear (linear
+codec ablation), --fp32-states (quantize_states=False).
+
 Prints one JSON line: Gparam/s over the K timed steps, the roofline of the
-step kernel (algorithmic 12.25 B/param against 8 TB/s), and the oracle's
-throughput on host cores for a bounded sample of the same workload.
+step kernel (algorithmic bytes per param of the configuration against
+8 TB/s), the oracle's throughput on host cores for a bounded sample of the
+same workload, and the GPU, ROCm and clock readings.
 """
 from __future__ import annotations
 
@@ -36,13 +42,15 @@ KERNEL_SRC = os.path.join(ROOT, "bit_companded_adam_amd", "csrc", "flashopt_kern
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "adamw_step_8b_traffic.json")
 
 
-def bytes_per_param(master_bits: int) -> float:
+def bytes_per_param(master_bits: int, quantize_states: bool = True) -> float:
     """Algorithmic HBM bytes per parameter per step: read bf16 param 2, bf16
-    grad 2, rho 1|2, m code 1, v code 1, two fp16 scales per 32 (2/32 each);
-    write all of them except the grad."""
-    rho = 1 if master_bits == 24 else 2
-    read = 2 + 2 + rho + 1 + 1 + 2 * 2 / 32
-    write = 2 + rho + 1 + 1 + 2 * 2 / 32
+    grad 2, rho 1|2 (none without a split), m and v 1 byte each plus two fp16
+    scales per 32 (2/32 each), or 4 bytes each as fp32; write all of them
+    except the grad."""
+    rho = {24: 1, 32: 2, 0: 0}[master_bits]
+    states = (1 + 1 + 2 * 2 / 32) if quantize_states else 8
+    read = 2 + 2 + rho + states
+    write = 2 + rho + states
     return read + write
 
 
@@ -64,15 +72,50 @@ def traffic_per_launch():
     return rec.get("hbm_bytes_per_launch")
 
 
-def build_workload(master_bits: int, companded: bool):
-    shapes = W.decoder_8b_shapes()
+WORKLOADS = {"decoder-8b-list": W.decoder_8b_shapes, "decoder-1b-list": W.decoder_1b_shapes}
+
+
+def build_workload(master_bits: int, companded: bool, quantize_states: bool = True,
+                   workload: str = "decoder-8b-list"):
+    shapes = WORKLOADS[workload]()
     params = [W.init_param(W.numel(s), device="cuda", seed=W.PARAM_SEED + i)
               for i, (_, s) in enumerate(shapes)]
     factors = W.grad_factors(len(shapes)).tolist()
     grads = [W.make_grad(W.numel(s), 1, device="cuda", stream_id=i, factor=factors[i])
              for i, (_, s) in enumerate(shapes)]
-    opt = F.FlashAdamW(params, master_bits=master_bits, companded=companded, **W.HP_DEFAULT)
+    opt = F.FlashAdamW(params, master_bits=master_bits or None, companded=companded,
+                       quantize_states=quantize_states, **W.HP_DEFAULT)
     return opt, grads
+
+
+def environment() -> dict:
+    """GPU name, compute units, ROCm/HIP version and the live clocks, read
+    from torch and rocm-smi (best effort: fields that cannot be read are
+    omitted)."""
+    env = {}
+    try:
+        prop = torch.cuda.get_device_properties(0)
+        env.update(gpu=prop.name, arch=getattr(prop, "gcnArchName", None),
+                   compute_units=prop.multi_processor_count, hip=torch.version.hip)
+    except Exception:
+        pass
+    if "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        return env                  # no child processes under a profiler's preload
+    try:
+        import subprocess
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
+                             timeout=20).stdout
+        clocks = {}
+        for line in out.splitlines():
+            if "sclk" in line or "mclk" in line or "fclk" in line:
+                key = "sclk" if "sclk" in line else ("mclk" if "mclk" in line else "fclk")
+                mhz = line.split("(")[-1].rstrip(")").strip()
+                clocks.setdefault(key, mhz)
+        if clocks:
+            env["clocks"] = clocks
+    except Exception:
+        pass
+    return env
 
 
 def time_steps(opt, grads, steps: int, warmup: int):
@@ -93,7 +136,8 @@ def time_steps(opt, grads, steps: int, warmup: int):
     return wall, per
 
 
-def cpu_baseline(master_bits: int, target_elems: int, threads: int, min_seconds: float = 10.0):
+def cpu_baseline(master_bits: int, target_elems: int, threads: int, min_seconds: float = 10.0,
+                 companded: bool = True, quantize_states: bool = True):
     """The oracle as it is, on host threads, over a bounded sample of the
     workload: the first target_elems / 32 elements of each of 32 evenly spaced
     tensors of the 8.0B list (same distributions), steps 2, 3, ... after an
@@ -108,12 +152,13 @@ def cpu_baseline(master_bits: int, target_elems: int, threads: int, min_seconds:
     for k, i in enumerate(pick):
         n = min(per, W.numel(shapes[i][1]))
         p = W.init_param(n, seed=W.PARAM_SEED + int(i)).view(torch.int16).numpy().view(np.uint16)
-        states.append(oracle.State.zeros_like_param(p, master_bits))
+        states.append(oracle.State.zeros_like_param(p, master_bits or None, quantize_states))
         for lst, t in ((g1, 1), (g2, 2)):
             lst.append(W.make_grad(n, t, stream_id=int(i), factor=float(factors[i]))
                        .view(torch.int16).numpy().view(np.uint16))
     hp = dict(lr=W.HP_DEFAULT["lr"], betas=W.HP_DEFAULT["betas"], eps=W.HP_DEFAULT["eps"],
-              weight_decay=W.HP_DEFAULT["weight_decay"], master_bits=master_bits)
+              weight_decay=W.HP_DEFAULT["weight_decay"], master_bits=master_bits or None,
+              companded=companded, quantize_states=quantize_states)
     oracle.adamw_step_list(states, g1, oracle.hparams(step=1, **hp), threads)
     n_total = sum(s.param.size for s in states)
     steps, used = 0, 0
@@ -169,8 +214,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--master-bits", type=int, default=24, choices=(24, 32))
+    ap.add_argument("--workload", default="decoder-8b-list", choices=sorted(WORKLOADS))
+    ap.add_argument("--master-bits", type=int, default=24, choices=(24, 32, 0),
+                    help="0: no master split (the parameter is cast back to bf16)")
     ap.add_argument("--linear", action="store_true", help="linear (non-companded) ablation")
+    ap.add_argument("--fp32-states", action="store_true",
+                    help="unquantized fp32 moments (weight-splitting-only ablation)")
     ap.add_argument("--cpu-elems", type=int, default=1 << 27,
                     help="oracle sample size for the CPU baseline (0: skip)")
     ap.add_argument("--cpu-threads", type=int, default=0)
@@ -192,17 +241,19 @@ def main():
         calibrate_copy(args.calibrate_copy)
         return
 
-    mb, comp = args.master_bits, not args.linear
+    mb, comp, qs = args.master_bits, not args.linear, not args.fp32_states
     copy_gbs = None if args.no_copy_ref else copy_reference()
-    opt, grads = build_workload(mb, comp)
+    opt, grads = build_workload(mb, comp, qs, args.workload)
     n = sum(s.param.numel() for s in opt.states)
+    n_tensors = len(opt.states)
     print(f"# workload ready: {len(opt.states)} tensors, {n} params, "
           f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated", file=sys.stderr, flush=True)
 
     wall, per = time_steps(opt, grads, args.steps, args.warmup)
+    env = environment()                     # clocks read right after the timed steps
     ms_step = wall * 1e3 / args.steps
     ms_launch = float(np.mean(per))
-    bpp = bytes_per_param(mb)
+    bpp = bytes_per_param(mb, qs)
     alg_bytes = bpp * n
     achieved = alg_bytes / (ms_launch * 1e-3) / 1e9
     print(f"# per-launch ms: mean {ms_launch:.3f} median {np.median(per):.3f} "
@@ -212,7 +263,10 @@ def main():
 
     cpu = None
     if args.cpu_elems > 0:
-        cpu = cpu_baseline(mb, args.cpu_elems, args.cpu_threads, args.cpu_seconds)
+        cpu = cpu_baseline(mb, args.cpu_elems, args.cpu_threads, args.cpu_seconds, comp, qs)
+    default = (args.workload, mb, comp, qs) == ("decoder-8b-list", 24, True, True)
+    name = args.workload + ("" if comp else "-linear") + ("" if qs else "-fp32-states") + \
+        ("-no-split" if mb == 0 else "")
 
     out = {
         "metric": METRIC,
@@ -227,14 +281,15 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "decoder-8b-list" + ("" if comp else "-linear"),
-                   "params": n, "tensors": 290, "master_bits": mb, "companded": comp,
+        "config": {"workload": name, "params": n, "tensors": n_tensors,
+                   "master_bits": mb, "companded": comp, "quantized_states": qs,
                    "bytes_per_param": bpp, "launches_per_step": 1},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": traffic_per_launch() if (mb, comp) == (24, True) else None,
+                     "traffic": traffic_per_launch() if default else None,
                      "copy_ref_gbs": copy_gbs},
         "cpu_baseline": cpu,
+        "env": env,
     }
     print(json.dumps(out), flush=True)
 

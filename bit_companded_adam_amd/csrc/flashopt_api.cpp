@@ -139,8 +139,12 @@ flashopt_status flashopt_adamw_step(const flashopt_tensor *tensors, int n_tensor
     // ---- hyper-parameters
     if (n_tensors < 0 || !a) return FLASHOPT_EINVAL;
     if (n_tensors > 0 && !tensors) return FLASHOPT_EINVAL;
-    if (a->master_bits != 24 && a->master_bits != 32) return FLASHOPT_EINVAL;
+    if (a->master_bits != 24 && a->master_bits != 32 && a->master_bits != 0) return FLASHOPT_EINVAL;
     if (a->companded != 0 && a->companded != 1) return FLASHOPT_EINVAL;
+    if (a->fp32_states != 0 && a->fp32_states != 1) return FLASHOPT_EINVAL;
+    if (a->reserved != 0) return FLASHOPT_EINVAL;
+    const bool split = a->master_bits != 0;
+    const bool quant = a->fp32_states == 0;
     if (a->step < 1) return FLASHOPT_EINVAL;
     if (!(a->lr >= 0.0) || !std::isfinite(a->lr)) return FLASHOPT_EINVAL;
     if (!(a->beta1 >= 0.0 && a->beta1 < 1.0) || !(a->beta2 >= 0.0 && a->beta2 < 1.0)) return FLASHOPT_EINVAL;
@@ -153,12 +157,14 @@ flashopt_status flashopt_adamw_step(const flashopt_tensor *tensors, int n_tensor
         const flashopt_tensor &t = tensors[i];
         if (t.numel < 0) return FLASHOPT_EINVAL;
         if (t.numel == 0) continue;
-        if (!t.param || !t.grad || !t.rho || !t.m_codes || !t.m_scales || !t.v_codes || !t.v_scales)
-            return FLASHOPT_EINVAL;
-        if (!aligned(t.param, 16) || !aligned(t.grad, 16) || !aligned(t.rho, 16) ||
-            !aligned(t.m_codes, 16) || !aligned(t.v_codes, 16) || !aligned(t.m_scales, 2) ||
-            !aligned(t.v_scales, 2))
+        if (!t.param || !t.grad || !t.m_codes || !t.v_codes) return FLASHOPT_EINVAL;
+        if (split && !t.rho) return FLASHOPT_EINVAL;
+        if (quant && (!t.m_scales || !t.v_scales)) return FLASHOPT_EINVAL;
+        if (!aligned(t.param, 16) || !aligned(t.grad, 16) || !aligned(t.m_codes, 16) ||
+            !aligned(t.v_codes, 16))
             return FLASHOPT_EALIGN;
+        if (split && !aligned(t.rho, 16)) return FLASHOPT_EALIGN;
+        if (quant && (!aligned(t.m_scales, 2) || !aligned(t.v_scales, 2))) return FLASHOPT_EALIGN;
         total += (t.numel + flashopt::kChunkElems - 1) / flashopt::kChunkElems;
         if (total > INT32_MAX) return FLASHOPT_EINVAL;
     }
@@ -234,8 +240,10 @@ flashopt_status flashopt_adamw_step(const flashopt_tensor *tensors, int n_tensor
 
     const DevTensor *d_desc = static_cast<const DevTensor *>(workspace);
     const int32_t *d_start = reinterpret_cast<const int32_t *>(d_desc + n_tensors);
+    const int states = !quant ? flashopt::kStatesFp32
+                     : (a->companded ? flashopt::kStatesCompanded : flashopt::kStatesLinear);
     return hip_status(flashopt::launch_adamw_step(d_desc, d_start, n_tensors, acc, sc,
-                                                  a->master_bits, a->companded != 0, st));
+                                                  a->master_bits, states, st));
 }
 
 }  // extern "C"

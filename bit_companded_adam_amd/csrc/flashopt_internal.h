@@ -16,7 +16,12 @@ constexpr int kChunkElems = kLaneElems * kWaveLanes;   // 1024
 constexpr int kBlockThreads = 256;
 constexpr int kGroup = 32;
 
+// State storage of the step: codes with fp16 group scales under the linear or
+// the companded specs, or plain fp32 moments (the unquantized-states ablation).
+enum : int { kStatesLinear = 0, kStatesCompanded = 1, kStatesFp32 = 2 };
+
 // Per-tensor descriptor of the multi-tensor step, staged in the workspace.
+// With fp32 states m_codes / v_codes point to float arrays.
 struct DevTensor {
     uint16_t *param;
     const uint16_t *grad;
@@ -52,10 +57,11 @@ hipError_t launch_split(const float *master, int64_t n, int master_bits,
 hipError_t launch_reconstruct(const uint16_t *param, const void *rho, int64_t n,
                               int master_bits, float *master, hipStream_t stream);
 // tensors / chunk_start are device pointers into the workspace;
-// chunk_start has n_tensors + 1 entries.
+// chunk_start has n_tensors + 1 entries.  master_bits: 24 | 32 | 0 (no
+// split); states: one of kStates*.
 hipError_t launch_adamw_step(const DevTensor *tensors, const int32_t *chunk_start,
                              int n_tensors, int32_t total_chunks,
-                             const StepScalars &sc, int master_bits, bool companded,
+                             const StepScalars &sc, int master_bits, int states,
                              hipStream_t stream);
 
 }  // namespace flashopt

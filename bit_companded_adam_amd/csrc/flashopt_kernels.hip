@@ -209,6 +209,11 @@ typedef __attribute__((address_space(1))) const uint8_t g_cu8;
 typedef __attribute__((address_space(1))) uint8_t g_u8;
 typedef __attribute__((address_space(1))) const float g_cf32;
 typedef __attribute__((address_space(1))) float g_f32;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) const u32x2 g_cu2;
+typedef __attribute__((address_space(1))) u32x2 g_u2;
+typedef __attribute__((address_space(1))) const uint32_t g_cu32;
+typedef __attribute__((address_space(1))) uint32_t g_u32;
 
 __device__ __forceinline__ uint4 ld16(const void *p, int k = 0)
 {
@@ -231,6 +236,11 @@ __device__ __forceinline__ void st16s(void *p, uint4 v, int k = 0)
     const u32x4 w = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(w, (g_u4 *)p + k);
 }
+// Streaming 8- and 4-byte accesses.
+__device__ __forceinline__ u32x2 ld8s(const void *p) { return __builtin_nontemporal_load((g_cu2 *)p); }
+__device__ __forceinline__ void st8s(void *p, u32x2 v) { __builtin_nontemporal_store(v, (g_u2 *)p); }
+__device__ __forceinline__ uint32_t ld4s(const void *p) { return __builtin_nontemporal_load((g_cu32 *)p); }
+__device__ __forceinline__ void st4s(void *p, uint32_t v) { __builtin_nontemporal_store(v, (g_u32 *)p); }
 __device__ __forceinline__ uint16_t ld_u16(const uint16_t *p) { return *(g_cu16 *)p; }
 __device__ __forceinline__ void st_u16(uint16_t *p, uint16_t v) { *(g_u16 *)p = v; }
 
@@ -550,141 +560,326 @@ reconstruct_kernel(const uint16_t *__restrict__ param, const void *__restrict__ 
 
 // ---------------------------------------------------- fused FlashAdamW step
 
-// The generic recomputation of one lane's outputs (see step_chunk): reload
-// the lane's inputs, redo the element arithmetic with correctly rounded
-// division and sqrt, and encode m and split theta with the NaN-safe element
-// routines.  The variance codes and both scales do not depend on these paths.
-template <int MB, bool COMP>
-__device__ __forceinline__ void lane_exact(const DevTensor &d, int64_t off, int lane, int cnt,
-                                        const StepScalars &sc, const float *s_mu,
-                                        const float *s_vu, const GroupDiv &gdm, uint32_t (&mo)[4],
-                                        uint32_t (&po)[8], uint32_t (&ro)[MB == 32 ? 8 : 4])
+// bf16 of an fp32 pattern rounded to nearest, ties to even (torch's cast, the
+// parameter update without a master split), in the upper half of the result.
+// Finite and infinite values only; NaN is handled by plain_elem.
+__device__ __forceinline__ uint32_t bf16_rne_top(uint32_t u)
 {
-    constexpr unsigned kMSpec = COMP ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
+    return u + 0x7FFFu + ((u >> 16) & 1u);
+}
+
+// The same with NaN kept (upper half, quieted).
+__device__ __forceinline__ uint32_t plain_elem(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u & 0xFFFF0000u) | 0x00400000u;
+    return bf16_rne_top(u);
+}
+
+// The new parameter words (and rho words with a master split) of a lane's 16
+// updated values.  EXACT selects the element-wise NaN-safe routines.
+template <int MB, bool EXACT>
+__device__ __forceinline__ void pack_theta(const float (&x)[16], uint32_t (&po)[8],
+                                           uint32_t (&ro)[MB == 32 ? 8 : 4])
+{
+    if constexpr (MB == 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (EXACT) po[i] = pack_hi16(plain_elem(x[2 * i]), plain_elem(x[2 * i + 1]));
+            else po[i] = pack_hi16(bf16_rne_top(__float_as_uint(x[2 * i])),
+                                   bf16_rne_top(__float_as_uint(x[2 * i + 1])));
+        }
+    } else if constexpr (EXACT) {
+        split_pack_exact<MB>(x, po, ro);
+    } else {
+        split_pack<MB>(x, po, ro);
+    }
+}
+
+// One lane's inputs.  Arrays a variant does not use are removed by the
+// compiler.
+template <int MB, int ST>
+struct LaneIn {
+    uint32_t pw[8], gw[8];
+    uint32_t rw[MB == 32 ? 8 : 4];
+    uint32_t mw[4], vw[4];        // codes (quantized states)
+    float mf[16], vf[16];         // fp32 states
+    uint32_t smb, svb;            // fp16 scale bits of the lane's group
+};
+
+// Element ownership of the fp32-state variants: lane l owns chunk elements
+// 256 q + 4 l + i (q, i in 0..3; the lane's element j is q = j / 4,
+// i = j % 4), so every access instruction of a wavefront covers one
+// contiguous block of each stream (fp32 1 KiB, bf16 512 B, int8 256 B).  A
+// lane owning 16 consecutive elements would make each 16-byte fp32 access
+// cover a quarter of every 64 bytes it touches, which streams at well under
+// half the bandwidth.  These variants have no quantization groups, so the
+// ownership is free.
+__device__ __forceinline__ int64_t q_elem(int lane, int j)
+{
+    return 256 * (j >> 2) + 4 * lane + (j & 3);
+}
+
+template <int MB, int ST, bool FULL>
+__device__ __forceinline__ void load_lane_q(const DevTensor &d, int64_t off, int lane,
+                                            LaneIn<MB, ST> &in)
+{
+    const float *const mp = reinterpret_cast<const float *>(d.m_codes) + off;
+    const float *const vp = reinterpret_cast<const float *>(d.v_codes) + off;
+    const uint8_t *const rp = static_cast<const uint8_t *>(d.rho);
+    in.smb = 0u;
+    in.svb = 0u;
+    if (FULL) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t e = off + 256 * q + 4 * lane;
+            u32x2 w = ld8s(d.param + e);
+            in.pw[2 * q] = w.x; in.pw[2 * q + 1] = w.y;
+            w = ld8s(d.grad + e);
+            in.gw[2 * q] = w.x; in.gw[2 * q + 1] = w.y;
+            if constexpr (MB == 24) in.rw[q] = ld4s(rp + e);
+            if constexpr (MB == 32) {
+                w = ld8s(rp + 2 * e);
+                in.rw[2 * q] = w.x; in.rw[2 * q + 1] = w.y;
+            }
+            const uint4 a = ld16s(mp + 256 * q + 4 * lane);
+            const uint4 b = ld16s(vp + 256 * q + 4 * lane);
+            in.mf[4 * q] = __uint_as_float(a.x); in.mf[4 * q + 1] = __uint_as_float(a.y);
+            in.mf[4 * q + 2] = __uint_as_float(a.z); in.mf[4 * q + 3] = __uint_as_float(a.w);
+            in.vf[4 * q] = __uint_as_float(b.x); in.vf[4 * q + 1] = __uint_as_float(b.y);
+            in.vf[4 * q + 2] = __uint_as_float(b.z); in.vf[4 * q + 3] = __uint_as_float(b.w);
+        }
+    } else {
+        const int64_t rem = d.numel - off;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { in.pw[i] = 0u; in.gw[i] = 0u; }
+#pragma unroll
+        for (int i = 0; i < (MB == 32 ? 8 : 4); ++i) in.rw[i] = 0u;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int64_t k = q_elem(lane, j);
+            in.mf[j] = 0.0f;
+            in.vf[j] = 0.0f;
+            if (k < rem) {
+                const int sh = 16 * (j & 1);
+                in.pw[j >> 1] |= static_cast<uint32_t>(((g_cu16 *)(d.param + off))[k]) << sh;
+                in.gw[j >> 1] |= static_cast<uint32_t>(((g_cu16 *)(d.grad + off))[k]) << sh;
+                if constexpr (MB == 24)
+                    in.rw[j >> 2] |= static_cast<uint32_t>(((g_cu8 *)(rp + off))[k]) << (8 * (j & 3));
+                if constexpr (MB == 32)
+                    in.rw[j >> 1] |= static_cast<uint32_t>(((g_cu16 *)(rp + 2 * off))[k]) << sh;
+                in.mf[j] = ((g_cf32 *)mp)[k];
+                in.vf[j] = ((g_cf32 *)vp)[k];
+            }
+        }
+    }
+}
+
+template <int MB, bool FULL>
+__device__ __forceinline__ void store_lane_q(const DevTensor &d, int64_t off, int lane,
+                                             const uint32_t (&po)[8],
+                                             const uint32_t (&ro)[MB == 32 ? 8 : 4],
+                                             const float (&m1)[16], const float (&v1)[16])
+{
+    float *const mp = reinterpret_cast<float *>(d.m_codes) + off;
+    float *const vp = reinterpret_cast<float *>(d.v_codes) + off;
+    uint8_t *const rp = static_cast<uint8_t *>(d.rho);
+    if (FULL) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t e = off + 256 * q + 4 * lane;
+            st8s(d.param + e, u32x2{po[2 * q], po[2 * q + 1]});
+            if constexpr (MB == 24) st4s(rp + e, ro[q]);
+            if constexpr (MB == 32) st8s(rp + 2 * e, u32x2{ro[2 * q], ro[2 * q + 1]});
+            st16s(mp + 256 * q + 4 * lane,
+                  make_uint4(__float_as_uint(m1[4 * q]), __float_as_uint(m1[4 * q + 1]),
+                             __float_as_uint(m1[4 * q + 2]), __float_as_uint(m1[4 * q + 3])));
+            st16s(vp + 256 * q + 4 * lane,
+                  make_uint4(__float_as_uint(v1[4 * q]), __float_as_uint(v1[4 * q + 1]),
+                             __float_as_uint(v1[4 * q + 2]), __float_as_uint(v1[4 * q + 3])));
+        }
+    } else {
+        const int64_t rem = d.numel - off;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int64_t k = q_elem(lane, j);
+            if (k < rem) {
+                const int sh = 16 * (j & 1);
+                ((g_u16 *)(d.param + off))[k] = static_cast<uint16_t>(po[j >> 1] >> sh);
+                if constexpr (MB == 24)
+                    ((g_u8 *)(rp + off))[k] = static_cast<uint8_t>(ro[j >> 2] >> (8 * (j & 3)));
+                if constexpr (MB == 32)
+                    ((g_u16 *)(rp + 2 * off))[k] = static_cast<uint16_t>(ro[j >> 1] >> sh);
+                ((g_f32 *)mp)[k] = m1[j];
+                ((g_f32 *)vp)[k] = v1[j];
+            }
+        }
+    }
+}
+
+// Loads of a lane's 16 elements of every stream.  FULL: straight-line 16-byte
+// streaming loads; otherwise element-masked loads with zeros past cnt.  The
+// quantized-state variants own 16 consecutive elements per lane (a lane pair
+// is a group); the fp32-state variants use load_lane_q's ownership.
+template <int MB, int ST, bool FULL>
+__device__ __forceinline__ void load_lane(const DevTensor &d, int64_t off, int lane, int cnt,
+                                          LaneIn<MB, ST> &in)
+{
+    if constexpr (ST == kStatesFp32) {
+        (void)cnt;
+        load_lane_q<MB, ST, FULL>(d, off, lane, in);
+        return;
+    }
+    const int64_t e = off + static_cast<int64_t>(lane) * kLaneElems;
+    const uint16_t *const pp = d.param + e;
+    const uint16_t *const gp = d.grad + e;
+    const uint8_t *const rp = static_cast<const uint8_t *>(d.rho) + e * (MB == 32 ? 2 : 1);
+    const uint16_t *const msp = d.m_scales + off / kGroup + (lane >> 1);
+    const uint16_t *const vsp = d.v_scales + off / kGroup + (lane >> 1);
+    in.smb = 0u;
+    in.svb = 0u;
+    if (FULL) {
+        uint4 q;
+        q = ld16s(pp, 0); in.pw[0] = q.x; in.pw[1] = q.y; in.pw[2] = q.z; in.pw[3] = q.w;
+        q = ld16s(pp, 1); in.pw[4] = q.x; in.pw[5] = q.y; in.pw[6] = q.z; in.pw[7] = q.w;
+        q = ld16s(gp, 0); in.gw[0] = q.x; in.gw[1] = q.y; in.gw[2] = q.z; in.gw[3] = q.w;
+        q = ld16s(gp, 1); in.gw[4] = q.x; in.gw[5] = q.y; in.gw[6] = q.z; in.gw[7] = q.w;
+        if constexpr (MB != 0) {
+            q = ld16s(rp, 0); in.rw[0] = q.x; in.rw[1] = q.y; in.rw[2] = q.z; in.rw[3] = q.w;
+        }
+        if constexpr (MB == 32) {
+            q = ld16s(rp, 1); in.rw[4] = q.x; in.rw[5] = q.y; in.rw[6] = q.z; in.rw[7] = q.w;
+        }
+        q = ld16s(d.m_codes + e); in.mw[0] = q.x; in.mw[1] = q.y; in.mw[2] = q.z; in.mw[3] = q.w;
+        q = ld16s(d.v_codes + e); in.vw[0] = q.x; in.vw[1] = q.y; in.vw[2] = q.z; in.vw[3] = q.w;
+        in.smb = ld_u16(msp);
+        in.svb = ld_u16(vsp);
+    } else {
+        load_u16x16(pp, cnt, in.pw);
+        load_u16x16(gp, cnt, in.gw);
+        if constexpr (MB == 32) load_u16x16(reinterpret_cast<const uint16_t *>(rp), cnt, in.rw);
+        else if constexpr (MB == 24) load_u8x16(rp, cnt, in.rw);
+        load_u8x16(d.m_codes + e, cnt, in.mw);
+        load_u8x16(d.v_codes + e, cnt, in.vw);
+        if (cnt > 0) {
+            in.smb = ld_u16(msp);
+            in.svb = ld_u16(vsp);
+        }
+    }
+}
+
+// Element j of a lane: the master theta (reconstructed, or the bf16 value
+// itself without a split), and the new moments m1 = b1 m0 + (1 - b1) g and
+// v1 = b2 v0 + ((1 - b2) g) g from the dequantized (or fp32) old ones.
+template <int MB, int ST>
+__device__ __forceinline__ void element_moments(const LaneIn<MB, ST> &in, int j,
+                                                const StepScalars &sc, const float *s_mu,
+                                                const float *s_vu, float ms, float vs,
+                                                float &theta, float &m, float &v)
+{
+    const uint32_t hs = (j & 1) ? (in.pw[j >> 1] & 0xFFFF0000u) : (in.pw[j >> 1] << 16);
+    if constexpr (MB == 0) {
+        theta = __uint_as_float(hs);
+    } else {
+        int32_t r;
+        if constexpr (MB == 32) r = shalf(in.rw, j);
+        else r = sbyte(in.rw, j);
+        theta = reconstruct_elem<MB>(hs, r);
+    }
+    const float g = (j & 1) ? bf16_hi(in.gw[j >> 1]) : bf16_lo(in.gw[j >> 1]);
+    float m0, v0;
+    if constexpr (ST == kStatesFp32) {
+        m0 = in.mf[j];
+        v0 = in.vf[j];
+    } else {
+        m0 = s_mu[ubyte(in.mw, j)] * ms;
+        const float a0 = s_vu[ubyte(in.vw, j)] * vs;
+        v0 = ST == kStatesCompanded ? a0 * a0 : a0;
+    }
+    const float m_decay = sc.b1 * m0;
+    const float m_new = sc.c1 * g;
+    m = m_decay + m_new;
+    const float v_decay = sc.b2 * v0;
+    const float cg = sc.c2 * g;
+    const float v_new = cg * g;
+    v = v_decay + v_new;
+}
+
+// The generic recomputation of one lane's updated parameter (and momentum
+// codes) for lanes outside the short sequences' domains (see step_chunk):
+// reload the lane's inputs, redo the element arithmetic with correctly
+// rounded division and sqrt, and encode and split with the NaN-safe element
+// routines.  The variance codes, fp32 moments and the group scales do not
+// depend on these paths and are produced by the caller.
+template <int MB, int ST>
+__device__ __forceinline__ void lane_exact(const DevTensor &d, int64_t off, int lane, int cnt,
+                                           const StepScalars &sc, const float *s_mu,
+                                           const float *s_vu, const GroupDiv &gdm,
+                                           uint32_t (&mo)[4], uint32_t (&po)[8],
+                                           uint32_t (&ro)[MB == 32 ? 8 : 4])
+{
+    constexpr unsigned kMSpec =
+        ST == kStatesCompanded ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
     // an opaque copy of the lane index keeps the compiler from reusing the
     // common path's loads, whose values would then stay live up to here
     asm volatile("" : "+v"(lane));
-    const int lofs = lane * kLaneElems;
-    uint32_t pw[8], gw[8], rw[MB == 32 ? 8 : 4], mw[4], vw[4];
-    load_u16x16(d.param + off + lofs, cnt, pw);
-    load_u16x16(d.grad + off + lofs, cnt, gw);
-    const uint8_t *rp = static_cast<const uint8_t *>(d.rho) + (off + lofs) * (MB == 32 ? 2 : 1);
-    if constexpr (MB == 32) load_u16x16(reinterpret_cast<const uint16_t *>(rp), cnt, rw);
-    else load_u8x16(rp, cnt, rw);
-    load_u8x16(d.m_codes + off + lofs, cnt, mw);
-    load_u8x16(d.v_codes + off + lofs, cnt, vw);
-    const float ms = cnt > 0 ? f16_value(ld_u16(d.m_scales + off / kGroup + (lane >> 1))) : 0.0f;
-    const float vs = cnt > 0 ? f16_value(ld_u16(d.v_scales + off / kGroup + (lane >> 1))) : 0.0f;
+    LaneIn<MB, ST> in;
+    load_lane<MB, ST, false>(d, off, lane, cnt, in);
+    const float ms = f16_value(in.smb);
+    const float vs = f16_value(in.svb);
     float m1[16], th1[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-        const uint32_t hs = (j & 1) ? (pw[j >> 1] & 0xFFFF0000u) : (pw[j >> 1] << 16);
-        int32_t r;
-        if constexpr (MB == 32) r = shalf(rw, j);
-        else r = sbyte(rw, j);
-        const float theta = reconstruct_elem<MB>(hs, r);
-        const float g = (j & 1) ? bf16_hi(gw[j >> 1]) : bf16_lo(gw[j >> 1]);
-        const float m0 = s_mu[ubyte(mw, j)] * ms;
-        const float a0 = s_vu[ubyte(vw, j)] * vs;
-        const float v0 = COMP ? a0 * a0 : a0;
-        const float m_decay = sc.b1 * m0;
-        const float m_new = sc.c1 * g;
-        const float m = m_decay + m_new;
-        const float v_decay = sc.b2 * v0;
-        const float cg = sc.c2 * g;
-        const float v_new = cg * g;
-        const float v = v_decay + v_new;
+        float theta, m, v;
+        element_moments<MB, ST>(in, j, sc, s_mu, s_vu, ms, vs, theta, m, v);
         const float den = sqrtf(v) * sc.k2 + sc.eps;
         const float num = sc.alpha * m;
         th1[j] = theta * sc.cwd - num / den;
         m1[j] = j < cnt ? m : 0.0f;
     }
-    encode16<kMSpec>(m1, gdm, mo);
-    split_pack_exact<MB>(th1, po, ro);
+    if constexpr (ST != kStatesFp32) encode16<kMSpec>(m1, gdm, mo);
+    pack_theta<MB, true>(th1, po, ro);
 }
 
 // One 1024-element chunk of one tensor, processed by one wavefront: each lane
-// loads 16 elements of every stream, dequantizes m and v, rebuilds the
-// master, applies AdamW, finds the group maxima (one DPP exchange with the
-// partner lane), and writes scales, codes and the re-split parameter.  FULL
-// chunks (every lane holds 16 elements) use plain 16-byte streaming accesses;
-// the ragged last chunk of a tensor masks per element and pads with zeros.
-template <int MB, bool COMP, bool FULL>
+// loads 16 elements of every stream, dequantizes m and v (or reads them as
+// fp32), rebuilds the master (or widens the bf16 parameter), applies AdamW,
+// finds the group maxima (one DPP exchange with the partner lane), and
+// writes scales and codes (or fp32 moments) and the new parameter (re-split,
+// or cast to bf16).  FULL chunks (every lane holds 16 elements) use plain
+// 16-byte streaming accesses; the ragged last chunk of a tensor masks per
+// element and pads with zeros.
+template <int MB, int ST, bool FULL>
 __device__ __forceinline__ void step_chunk(const DevTensor &d, int64_t off, int lane,
                                            const StepScalars &sc, const float *s_mu,
                                            const float *s_vu)
 {
-    constexpr unsigned kMSpec = COMP ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
-    constexpr unsigned kVSpec = COMP ? FLASHOPT_SPEC_VARIANCE : FLASHOPT_SPEC_VARIANCE_LINEAR;
+    constexpr bool kQuant = ST != kStatesFp32;
+    constexpr bool kComp = ST == kStatesCompanded;
+    constexpr unsigned kVSpec = kComp ? FLASHOPT_SPEC_VARIANCE : FLASHOPT_SPEC_VARIANCE_LINEAR;
     constexpr int kRhoWords = MB == 32 ? 8 : 4;
 
     const int lofs = lane * kLaneElems;
     const int cnt = FULL ? kLaneElems : lane_count(d.numel - off, lofs);
-    uint16_t *const pp = d.param + off + lofs;
-    const uint16_t *const gp = d.grad + off + lofs;
-    uint8_t *const rp = static_cast<uint8_t *>(d.rho) + (off + lofs) * (MB == 32 ? 2 : 1);
-    int8_t *const mp = d.m_codes + off + lofs;
-    uint8_t *const vp = d.v_codes + off + lofs;
-    uint16_t *const msp = d.m_scales + off / kGroup + (lane >> 1);
-    uint16_t *const vsp = d.v_scales + off / kGroup + (lane >> 1);
+    const int64_t e = off + lofs;
 
     // ---- loads (missing elements read as zero)
-    uint32_t pw[8], gw[8], rw[kRhoWords], mw[4], vw[4];
-    uint32_t smb = 0u, svb = 0u;
-    if (FULL) {
-        uint4 q;
-        q = ld16s(pp, 0); pw[0] = q.x; pw[1] = q.y; pw[2] = q.z; pw[3] = q.w;
-        q = ld16s(pp, 1); pw[4] = q.x; pw[5] = q.y; pw[6] = q.z; pw[7] = q.w;
-        q = ld16s(gp, 0); gw[0] = q.x; gw[1] = q.y; gw[2] = q.z; gw[3] = q.w;
-        q = ld16s(gp, 1); gw[4] = q.x; gw[5] = q.y; gw[6] = q.z; gw[7] = q.w;
-        q = ld16s(rp, 0); rw[0] = q.x; rw[1] = q.y; rw[2] = q.z; rw[3] = q.w;
-        if constexpr (MB == 32) { q = ld16s(rp, 1); rw[4] = q.x; rw[5] = q.y; rw[6] = q.z; rw[7] = q.w; }
-        q = ld16s(mp); mw[0] = q.x; mw[1] = q.y; mw[2] = q.z; mw[3] = q.w;
-        q = ld16s(vp); vw[0] = q.x; vw[1] = q.y; vw[2] = q.z; vw[3] = q.w;
-        smb = ld_u16(msp);
-        svb = ld_u16(vsp);
-    } else {
-        load_u16x16(pp, cnt, pw);
-        load_u16x16(gp, cnt, gw);
-        if constexpr (MB == 32) load_u16x16(reinterpret_cast<const uint16_t *>(rp), cnt, rw);
-        else load_u8x16(rp, cnt, rw);
-        load_u8x16(mp, cnt, mw);
-        load_u8x16(vp, cnt, vw);
-        if (cnt > 0) {
-            smb = ld_u16(msp);
-            svb = ld_u16(vsp);
-        }
-    }
-    const float ms = f16_value(smb);
-    const float vs = f16_value(svb);
+    LaneIn<MB, ST> in;
+    load_lane<MB, ST, FULL>(d, off, lane, cnt, in);
+    const float ms = f16_value(in.smb);
+    const float vs = f16_value(in.svb);
 
     // ---- dequantize, reconstruct, moments
     float thd[16], m1[16], v1[16];
     uint32_t vbits = 0u;                    // unsigned max of the v1 bit patterns
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-        const uint32_t hs = (j & 1) ? (pw[j >> 1] & 0xFFFF0000u) : (pw[j >> 1] << 16);
-        int32_t r;
-        if constexpr (MB == 32) r = shalf(rw, j);
-        else r = sbyte(rw, j);
-        const float theta = reconstruct_elem<MB>(hs, r);
-        const float g = (j & 1) ? bf16_hi(gw[j >> 1]) : bf16_lo(gw[j >> 1]);
-
-        const float m0 = s_mu[ubyte(mw, j)] * ms;
-        const float a0 = s_vu[ubyte(vw, j)] * vs;
-        const float v0 = COMP ? a0 * a0 : a0;
-
+        float theta;
+        element_moments<MB, ST>(in, j, sc, s_mu, s_vu, ms, vs, theta, m1[j], v1[j]);
         thd[j] = theta * sc.cwd;
-        const float m_decay = sc.b1 * m0;
-        const float m_new = sc.c1 * g;
-        m1[j] = m_decay + m_new;
-        const float v_decay = sc.b2 * v0;
-        const float cg = sc.c2 * g;
-        const float v_new = cg * g;
-        v1[j] = v_decay + v_new;
         vbits = max(vbits, __float_as_uint(v1[j]));
     }
-    if (!FULL) {                            // zero pad of the ragged last group
+    if (!FULL && kQuant) {                  // zero pad of the ragged last group
 #pragma unroll
         for (int j = 0; j < 16; ++j)
             if (j >= cnt) { m1[j] = 0.0f; v1[j] = 0.0f; }
@@ -695,7 +890,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor &d, int64_t off, int 
     if (vbits < kSqrtFastEnd) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) rt[j] = math::sqrt_cr(v1[j]);
-    } else {                                // rare: v beyond the fast sqrt's range
+    } else {                                // rare: v outside the fast sqrt's range
 #pragma unroll
         for (int j = 0; j < 16; ++j) rt[j] = sqrtf(v1[j]);
     }
@@ -703,14 +898,14 @@ __device__ __forceinline__ void step_chunk(const DevTensor &d, int64_t off, int 
     // ---- lane maxima of |m1|, of what the variance quantizer sees, of sqrt(v1)
     // (the maxima start from the first element: a group of NaNs only has a
     // NaN maximum, as the IEEE maxNum reduction over its elements gives)
-    float am = fabsf(m1[0]), av = COMP ? rt[0] : v1[0], rmax = 0.0f;
+    float am = fabsf(m1[0]), av = kComp ? rt[0] : v1[0], rmax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         am = fmaxf(am, fabsf(m1[j]));
-        if (COMP) av = fmaxf(av, rt[j]);
+        if (kComp) av = fmaxf(av, rt[j]);
         else { av = fmaxf(av, v1[j]); rmax = fmaxf(rmax, rt[j]); }
     }
-    if (COMP) rmax = av;
+    if (kComp) rmax = av;
 
     // ---- the update theta (1 - lr wd) - (alpha m1) / (sqrt(v1) k2 + eps),
     // with the short division when the lane's numerators and denominators
@@ -731,49 +926,60 @@ __device__ __forceinline__ void step_chunk(const DevTensor &d, int64_t off, int 
     bool any_nan = false;
 #pragma unroll
     for (int j = 0; j < 16; ++j) any_nan |= th1[j] != th1[j];
-    const bool exact = sc.fast_div == 0 || vbits >= kSqrtFastEnd || !(sc.alpha * am <= sc.num_max) ||
-                       kmin < tkey || any_nan;
+    const bool exact = sc.fast_div == 0 || vbits >= kSqrtFastEnd ||
+                       !(sc.alpha * am <= sc.num_max) || kmin < tkey || any_nan;
 
-    // ---- group maxima over the lane pair, scales
-    am = pair_max(am);
-    av = pair_max(av);
-    const uint32_t sm_out = f16_bits(am);
-    const uint32_t sv_out = f16_bits(av);
-    const GroupDiv gdm = group_div(sm_out);
-
-    // ---- codes and the re-split with the short sequences
+    // ---- group maxima over the lane pair, scales, variance codes
     uint32_t mo[4], vo[4], po[8], ro[kRhoWords];
-    if constexpr (COMP) encode16<kVSpec>(rt, group_div(sv_out), vo);
-    else encode16<kVSpec>(v1, group_div(sv_out), vo);
+    uint32_t sm_out = 0u, sv_out = 0u;
+    GroupDiv gdm{1.0f, 1.0f};
+    if constexpr (kQuant) {
+        am = pair_max(am);
+        av = pair_max(av);
+        sm_out = f16_bits(am);
+        sv_out = f16_bits(av);
+        gdm = group_div(sm_out);
+        if constexpr (kComp) encode16<kVSpec>(rt, group_div(sv_out), vo);
+        else encode16<kVSpec>(v1, group_div(sv_out), vo);
+    }
+
+    // ---- momentum codes and the new parameter
     if (!exact) {
-        encode16_s8_finite<COMP>(m1, gdm, mo);
-        split_pack<MB>(th1, po, ro);
+        if constexpr (kQuant) encode16_s8_finite<kComp>(m1, gdm, mo);
+        pack_theta<MB, false>(th1, po, ro);
     } else {
         // rare: a lane outside the short sequences' domains (tiny or huge
         // numerators, NaN or infinite m or theta, unusual hyper-parameters)
-        // is recomputed from memory with the generic operations; nothing has
-        // been stored yet and the group scales above are already exact
-        lane_exact<MB, COMP>(d, off, lane, cnt, sc, s_mu, s_vu, gdm, mo, po, ro);
+        // is recomputed from its inputs in memory with the generic
+        // operations; nothing has been stored yet, and the group scales
+        // above are already exact
+        lane_exact<MB, ST>(d, off, lane, cnt, sc, s_mu, s_vu, gdm, mo, po, ro);
     }
 
     // ---- stores
+    if constexpr (!kQuant) {
+        store_lane_q<MB, FULL>(d, off, lane, po, ro, m1, v1);
+        return;
+    }
+    uint16_t *const pp = d.param + e;
+    uint8_t *const rp = static_cast<uint8_t *>(d.rho) + e * (MB == 32 ? 2 : 1);
     if (FULL) {
         st16s(pp, make_uint4(po[0], po[1], po[2], po[3]), 0);
         st16s(pp, make_uint4(po[4], po[5], po[6], po[7]), 1);
-        st16s(rp, make_uint4(ro[0], ro[1], ro[2], ro[3]), 0);
+        if constexpr (MB != 0) st16s(rp, make_uint4(ro[0], ro[1], ro[2], ro[3]), 0);
         if constexpr (MB == 32) st16s(rp, make_uint4(ro[4], ro[5], ro[6], ro[7]), 1);
-        st16s(mp, make_uint4(mo[0], mo[1], mo[2], mo[3]));
-        st16s(vp, make_uint4(vo[0], vo[1], vo[2], vo[3]));
+        st16s(d.m_codes + e, make_uint4(mo[0], mo[1], mo[2], mo[3]));
+        st16s(d.v_codes + e, make_uint4(vo[0], vo[1], vo[2], vo[3]));
     } else {
         store_u16x16(pp, cnt, po);
         if constexpr (MB == 32) store_u16x16(reinterpret_cast<uint16_t *>(rp), cnt, ro);
-        else store_u8x16(rp, cnt, ro);
-        store_u8x16(mp, cnt, mo);
-        store_u8x16(vp, cnt, vo);
+        else if constexpr (MB == 24) store_u8x16(rp, cnt, ro);
+        store_u8x16(d.m_codes + e, cnt, mo);
+        store_u8x16(d.v_codes + e, cnt, vo);
     }
-    if ((lane & 1) == 0 && cnt > 0) {
-        st_u16(msp, static_cast<uint16_t>(sm_out));
-        st_u16(vsp, static_cast<uint16_t>(sv_out));
+    if (kQuant && (lane & 1) == 0 && cnt > 0) {
+        st_u16(d.m_scales + off / kGroup + (lane >> 1), static_cast<uint16_t>(sm_out));
+        st_u16(d.v_scales + off / kGroup + (lane >> 1), static_cast<uint16_t>(sv_out));
     }
 }
 
@@ -781,19 +987,22 @@ __device__ __forceinline__ void step_chunk(const DevTensor &d, int64_t off, int 
 // shorter); a chunk never straddles two tensors.  The wavefront finds the
 // tensor owning its first chunk by binary search over the chunk table
 // (scalar loads, uniform across the wavefront) and walks forward from there.
-// The two 256-entry dequantization tables are built per workgroup in LDS
-// from the exact fp32 operations of dequantize().
-template <int MB, bool COMP>
+// With quantized states the two 256-entry dequantization tables are built per
+// workgroup in LDS from the exact fp32 operations of dequantize().
+template <int MB, int ST>
 __global__ void __launch_bounds__(kBlockThreads)
 adamw_step_kernel(const DevTensor *__restrict__ tensors, const int32_t *__restrict__ chunk_start,
                   int n_tensors, int32_t total_chunks, int32_t run, StepScalars sc)
 {
-    constexpr unsigned kMSpec = COMP ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
+    constexpr unsigned kMSpec =
+        ST == kStatesCompanded ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
     __shared__ float s_mu[256];   // momentum: q/127 (companded: / (2 - |.|))
     __shared__ float s_vu[256];   // variance: q/255
-    s_mu[threadIdx.x] = dequant_unit<kMSpec>(static_cast<int>(threadIdx.x));
-    s_vu[threadIdx.x] = dequant_unit<0u>(static_cast<int>(threadIdx.x));
-    __syncthreads();
+    if constexpr (ST != kStatesFp32) {
+        s_mu[threadIdx.x] = dequant_unit<kMSpec>(static_cast<int>(threadIdx.x));
+        s_vu[threadIdx.x] = dequant_unit<0u>(static_cast<int>(threadIdx.x));
+        __syncthreads();
+    }
 
     const int lane = threadIdx.x & (kWaveLanes - 1);
     const int64_t wave = __builtin_amdgcn_readfirstlane(
@@ -815,8 +1024,8 @@ adamw_step_kernel(const DevTensor *__restrict__ tensors, const int32_t *__restri
         t = __builtin_amdgcn_readfirstlane(t);
         const DevTensor d = tensors[t];
         const int64_t off = static_cast<int64_t>(c - chunk_start[t]) * kChunkElems;
-        if (off + kChunkElems <= d.numel) step_chunk<MB, COMP, true>(d, off, lane, sc, s_mu, s_vu);
-        else step_chunk<MB, COMP, false>(d, off, lane, sc, s_mu, s_vu);
+        if (off + kChunkElems <= d.numel) step_chunk<MB, ST, true>(d, off, lane, sc, s_mu, s_vu);
+        else step_chunk<MB, ST, false>(d, off, lane, sc, s_mu, s_vu);
     }
 }
 
@@ -903,24 +1112,39 @@ hipError_t launch_reconstruct(const uint16_t *param, const void *rho, int64_t n,
 
 namespace {
 
-template <int MB, bool COMP>
+template <int MB, int ST>
 hipError_t step_variant(const DevTensor *tensors, const int32_t *chunk_start, int n_tensors,
                         int32_t total_chunks, int32_t run, const StepScalars &sc, hipStream_t st)
 {
     const int64_t waves = (total_chunks + run - 1) / run;
     const int64_t waves_per_block = kBlockThreads / kWaveLanes;
     const int64_t grid = (waves + waves_per_block - 1) / waves_per_block;
-    hipLaunchKernelGGL((adamw_step_kernel<MB, COMP>), dim3(static_cast<unsigned>(grid)),
+    hipLaunchKernelGGL((adamw_step_kernel<MB, ST>), dim3(static_cast<unsigned>(grid)),
                        dim3(kBlockThreads), 0, st, tensors, chunk_start, n_tensors,
                        total_chunks, run, sc);
     return hipGetLastError();
+}
+
+template <int MB>
+hipError_t step_states(const DevTensor *tensors, const int32_t *chunk_start, int n_tensors,
+                       int32_t total_chunks, int32_t run, const StepScalars &sc, int states,
+                       hipStream_t st)
+{
+    switch (states) {
+    case kStatesCompanded:
+        return step_variant<MB, kStatesCompanded>(tensors, chunk_start, n_tensors, total_chunks, run, sc, st);
+    case kStatesLinear:
+        return step_variant<MB, kStatesLinear>(tensors, chunk_start, n_tensors, total_chunks, run, sc, st);
+    default:
+        return step_variant<MB, kStatesFp32>(tensors, chunk_start, n_tensors, total_chunks, run, sc, st);
+    }
 }
 
 }  // namespace
 
 hipError_t launch_adamw_step(const DevTensor *tensors, const int32_t *chunk_start, int n_tensors,
                              int32_t total_chunks, const StepScalars &sc, int master_bits,
-                             bool companded, hipStream_t st)
+                             int states, hipStream_t st)
 {
     if (total_chunks <= 0) return hipSuccess;
     // Consecutive chunks per wavefront; FLASHOPT_CHUNKS_PER_WAVE tunes it.
@@ -929,11 +1153,11 @@ hipError_t launch_adamw_step(const DevTensor *tensors, const int32_t *chunk_star
         const int v = atoi(env);
         if (v >= 1 && v <= 1024) run = v;
     }
-    if (master_bits == 32)
-        return companded ? step_variant<32, true>(tensors, chunk_start, n_tensors, total_chunks, run, sc, st)
-                         : step_variant<32, false>(tensors, chunk_start, n_tensors, total_chunks, run, sc, st);
-    return companded ? step_variant<24, true>(tensors, chunk_start, n_tensors, total_chunks, run, sc, st)
-                     : step_variant<24, false>(tensors, chunk_start, n_tensors, total_chunks, run, sc, st);
+    switch (master_bits) {
+    case 24: return step_states<24>(tensors, chunk_start, n_tensors, total_chunks, run, sc, states, st);
+    case 32: return step_states<32>(tensors, chunk_start, n_tensors, total_chunks, run, sc, states, st);
+    default: return step_states<0>(tensors, chunk_start, n_tensors, total_chunks, run, sc, states, st);
+    }
 }
 
 }  // namespace flashopt

@@ -48,7 +48,8 @@ class flashopt_adamw_args(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double),
                 ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
                 ("weight_decay", ctypes.c_double), ("step", ctypes.c_int64),
-                ("master_bits", ctypes.c_int), ("companded", ctypes.c_int)]
+                ("master_bits", ctypes.c_int), ("companded", ctypes.c_int),
+                ("fp32_states", ctypes.c_int), ("reserved", ctypes.c_int)]
 
 
 _lib = None
@@ -171,33 +172,46 @@ def flashopt_reconstruct(param: torch.Tensor, rho: torch.Tensor, master_bits: in
 
 class TensorState:
     """Device state of one parameter tensor: bf16 param (updated in place),
-    rho, momentum and variance codes and fp16 scales.  Fresh state is zero."""
+    rho (master_bits 24 | 32; none for master_bits None), and the momentum
+    and variance as codes with fp16 scales, or as fp32 arrays when
+    quantize_states is False.  Fresh state is zero."""
 
-    def __init__(self, param: torch.Tensor, master_bits: int = 24):
+    def __init__(self, param: torch.Tensor, master_bits=24, quantize_states: bool = True):
         if param.dtype != torch.bfloat16 or not param.is_contiguous():
             raise ValueError("param must be a contiguous bf16 tensor")
+        if master_bits not in (24, 32, None):
+            raise ValueError("master_bits must be 24, 32 or None")
         n, dev = param.numel(), param.device
         self.param = param
-        self.rho = torch.zeros(n, dtype=rho_dtype(master_bits), device=dev)
-        self.m_codes = torch.zeros(n, dtype=torch.int8, device=dev)
-        self.m_scales = torch.zeros(n_groups(n), dtype=torch.int16, device=dev)
-        self.v_codes = torch.zeros(n, dtype=torch.uint8, device=dev)
-        self.v_scales = torch.zeros(n_groups(n), dtype=torch.int16, device=dev)
+        self.rho = None if master_bits is None else torch.zeros(n, dtype=rho_dtype(master_bits), device=dev)
+        if quantize_states:
+            self.m_codes = torch.zeros(n, dtype=torch.int8, device=dev)
+            self.m_scales = torch.zeros(n_groups(n), dtype=torch.int16, device=dev)
+            self.v_codes = torch.zeros(n, dtype=torch.uint8, device=dev)
+            self.v_scales = torch.zeros(n_groups(n), dtype=torch.int16, device=dev)
+        else:
+            self.m_codes = torch.zeros(n, dtype=torch.float32, device=dev)
+            self.v_codes = torch.zeros(n, dtype=torch.float32, device=dev)
+            self.m_scales = self.v_scales = None
         self.master_bits = master_bits
+        self.quantize_states = quantize_states
 
     def descriptor(self, grad: torch.Tensor) -> flashopt_tensor:
         if grad.dtype != torch.bfloat16 or grad.numel() != self.param.numel():
             raise ValueError("grad must be bf16 with the parameter's size")
+        opt = lambda t, name: 0 if t is None else _dev(t, name)
         return flashopt_tensor(_dev(self.param, "param"), _dev(grad, "grad"),
-                               _dev(self.rho, "rho"), _dev(self.m_codes, "m_codes"),
-                               _dev(self.m_scales, "m_scales"), _dev(self.v_codes, "v_codes"),
-                               _dev(self.v_scales, "v_scales"), self.param.numel())
+                               opt(self.rho, "rho"), _dev(self.m_codes, "m_codes"),
+                               opt(self.m_scales, "m_scales"), _dev(self.v_codes, "v_codes"),
+                               opt(self.v_scales, "v_scales"), self.param.numel())
 
 
 def make_args(step: int, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0,
-              master_bits=24, companded=True) -> flashopt_adamw_args:
+              master_bits=24, companded=True, quantize_states=True) -> flashopt_adamw_args:
+    """master_bits 24 | 32 | None (no split); quantize_states False: fp32 m, v."""
     return flashopt_adamw_args(lr, betas[0], betas[1], eps, weight_decay, step,
-                               master_bits, int(companded))
+                               0 if master_bits is None else master_bits, int(companded),
+                               0 if quantize_states else 1, 0)
 
 
 def flashopt_adamw_workspace_bytes(n_tensors: int) -> int:
@@ -224,10 +238,11 @@ class FlashAdamW:
     """A list of TensorStates stepped together by one launch per step."""
 
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0,
-                 master_bits=24, companded=True):
-        self.states = [TensorState(p, master_bits) for p in params]
+                 master_bits=24, companded=True, quantize_states=True):
+        self.states = [TensorState(p, master_bits, quantize_states) for p in params]
         self.hp = dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay,
-                       master_bits=master_bits, companded=companded)
+                       master_bits=master_bits, companded=companded,
+                       quantize_states=quantize_states)
         dev = self.states[0].param.device if self.states else "cuda"
         nbytes = max(16, flashopt_adamw_workspace_bytes(len(self.states)))
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)

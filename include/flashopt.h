@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define FLASHOPT_ABI_VERSION 1
+#define FLASHOPT_ABI_VERSION 2
 
 typedef enum {
     FLASHOPT_OK = 0,
@@ -114,15 +114,19 @@ flashopt_status flashopt_reconstruct(const uint16_t *param_bf16, const void *rho
  * "code/flashsim/flash_adamw_sim.py", FlashAdamWSim.step: per-parameter state
  * m = (codes, scales), v = (codes, scales), rho).  All device pointers.
  * param, rho, m_*, v_* are read and updated in place; grad is read only.
- * Fresh state is all zero (codes, scales and rho), which reproduces the
- * page's state init for a bf16 parameter. */
+ * Fresh state is all zero (codes, scales, fp32 moments and rho), which
+ * reproduces the page's state init for a bf16 parameter.
+ * With args.fp32_states = 1 (the page's quantize_states=False ablation),
+ * m_codes and v_codes point to float [numel] moments and the scale pointers
+ * are unused (may be NULL).  With args.master_bits = 0 (the page's
+ * master_weight_bits=None) rho is unused (may be NULL). */
 typedef struct {
     uint16_t *param;          /* [numel] bf16 theta'                          */
     const uint16_t *grad;     /* [numel] bf16 gradient                        */
     void *rho;                /* [numel] int8 (24-bit) | int16 (32-bit)       */
-    int8_t *m_codes;          /* [numel] momentum codes                       */
+    int8_t *m_codes;          /* [numel] momentum codes (fp32 states: float)  */
     uint16_t *m_scales;       /* [ceil(numel/32)] fp16 momentum scales        */
-    uint8_t *v_codes;         /* [numel] variance codes                       */
+    uint8_t *v_codes;         /* [numel] variance codes (fp32 states: float)  */
     uint16_t *v_scales;       /* [ceil(numel/32)] fp16 variance scales        */
     int64_t numel;            /* >= 0                                         */
 } flashopt_tensor;
@@ -134,8 +138,14 @@ typedef struct {
     double eps;               /* >= 0                                         */
     double weight_decay;      /* finite; decoupled: theta *= 1 - lr * wd      */
     int64_t step;             /* t >= 1, the step count after this step's increment */
-    int master_bits;          /* 24 (int8 rho) | 32 (int16 rho)               */
+    int master_bits;          /* 24 (int8 rho) | 32 (int16 rho) | 0: no split,
+                                 the bf16 parameter itself is the master and
+                                 the update is cast back to bf16 rounding to
+                                 nearest even (master_weight_bits=None)      */
     int companded;            /* 1: softsign m, sqrt v (Alg. 2/3); 0: linear ablation */
+    int fp32_states;          /* 0: quantized m, v (codes + fp16 scales);
+                                 1: fp32 m, v (quantize_states=False)         */
+    int reserved;             /* must be 0                                    */
 } flashopt_adamw_args;
 
 /* Device workspace bytes that flashopt_adamw_step needs for this list (the
@@ -146,12 +156,14 @@ size_t flashopt_adamw_workspace_bytes(const flashopt_tensor *tensors, int n_tens
  * "code/flashsim/flash_adamw_sim.py", FlashAdamWSim.step, Alg. 4).  Per
  * element, in one pass over memory:
  *   m0 = dequantize(m), v0 = dequantize(v)      (momentum / variance spec, or
- *                                                 the linear specs if !companded)
- *   theta = reconstruct(param, rho)
+ *                                                 the linear specs if !companded;
+ *                                                 fp32 states are read as is)
+ *   theta = reconstruct(param, rho)             (the bf16 param if master_bits 0)
  *   theta *= 1 - lr*wd;  m1 = b1 m0 + (1-b1) g;  v1 = b2 v0 + ((1-b2) g) g
  *   theta -= (alpha m1) / (sqrt(v1) k2 + eps),  alpha = lr / (1 - b1^t),
  *                                               k2 = 1 / sqrt(1 - b2^t)
  *   (m, v) = quantize(m1), quantize(v1);  (param, rho) = split(theta)
+ *   (fp32 states: m, v = m1, v1;  master_bits 0: param = bf16 RNE of theta)
  * Scalars are formed in double on the host and rounded once to fp32; every
  * fp32 operation is rounded once, in the order written (no contraction).
  *   tensors   HOST array of n_tensors descriptors (read during the call only)
@@ -160,8 +172,9 @@ size_t flashopt_adamw_workspace_bytes(const flashopt_tensor *tensors, int n_tens
  *             step has run on `stream`
  * The descriptor table is staged through a pinned host buffer that the
  * library allocates once and reuses (hipHostMalloc).
- * Errors: EINVAL (n_tensors < 0, NULL tensors/args, numel < 0, NULL pointer in
- * a non-empty tensor, master_bits, companded, step < 1, lr < 0, beta outside
+ * Errors: EINVAL (n_tensors < 0, NULL tensors/args, numel < 0, NULL pointer
+ * that the variant uses in a non-empty tensor, master_bits, companded,
+ * fp32_states, reserved != 0, step < 1, lr < 0, beta outside
  * [0, 1), eps < 0, non-finite weight_decay, more than 2^31 - 1 chunks of
  * 1024 elements in total), EALIGN, EWORKSPACE, EHIP. */
 flashopt_status flashopt_adamw_step(const flashopt_tensor *tensors, int n_tensors,

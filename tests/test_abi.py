@@ -92,7 +92,8 @@ def _step(L, tensors, args=None, ws=A16, ws_bytes=1 << 20):
 def test_step_validation(L):
     ok = [_tensor()]
     # hyper-parameters
-    for bad in (dict(step=0), dict(master_bits=16), dict(companded=2), dict(lr=-1.0),
+    for bad in (dict(step=0), dict(master_bits=16), dict(companded=2), dict(fp32_states=2),
+                dict(reserved=1), dict(lr=-1.0),
                 dict(beta1=1.0), dict(beta2=-0.1), dict(eps=-1e-8),
                 dict(weight_decay=float("inf")), dict(lr=float("nan"))):
         a = F.make_args(1)
@@ -107,6 +108,17 @@ def test_step_validation(L):
         assert _step(L, [_tensor(**{field: None})]) == F.FLASHOPT_EINVAL, field
         bad = MIS if field.endswith("scales") else A16 + 8
         assert _step(L, [_tensor(**{field: bad})]) == F.FLASHOPT_EALIGN, field
+    # buffers a variant does not use may be NULL or unaligned: such calls get
+    # past tensor validation and stop at the (too small) workspace, before
+    # anything is enqueued
+    none_args = F.make_args(1, master_bits=None)
+    assert _step(L, [_tensor(rho=None)], none_args, ws_bytes=0) == F.FLASHOPT_EWORKSPACE
+    assert _step(L, [_tensor(rho=MIS)], none_args, ws_bytes=0) == F.FLASHOPT_EWORKSPACE
+    f32_args = F.make_args(1, quantize_states=False)
+    assert _step(L, [_tensor(m_scales=None, v_scales=None)], f32_args, ws_bytes=0) == F.FLASHOPT_EWORKSPACE
+    assert _step(L, [_tensor(m_scales=MIS)], f32_args, ws_bytes=0) == F.FLASHOPT_EWORKSPACE
+    assert _step(L, [_tensor(rho=None)], f32_args, ws_bytes=0) == F.FLASHOPT_EINVAL
+    assert _step(L, [_tensor(m_codes=A16 + 4)], f32_args, ws_bytes=0) == F.FLASHOPT_EALIGN
     # more than 2^31 - 1 chunks of 1024
     assert _step(L, [_tensor(numel=(1 << 41) + 1)]) == F.FLASHOPT_EINVAL
     # empty work is a no-op, even with no workspace

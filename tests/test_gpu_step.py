@@ -32,30 +32,41 @@ pytestmark = pytest.mark.gpu
 HP = dict(W.HP_DEFAULT)
 
 
-def _orc_hp(t, master_bits, companded):
+def _orc_hp(t, master_bits, companded, quantize_states=True):
     return oracle.hparams(lr=HP["lr"], betas=HP["betas"], eps=HP["eps"],
                           weight_decay=HP["weight_decay"], step=t,
-                          master_bits=master_bits, companded=companded)
+                          master_bits=master_bits, companded=companded,
+                          quantize_states=quantize_states)
 
 
 def _snap(s: F.TensorState, lo=0, hi=None) -> oracle.State:
     """Host copy of a device state slice [lo, hi) (lo, hi multiples of 32)."""
     hi = s.param.numel() if hi is None else hi
     g0, g1 = lo // 32, (hi + 31) // 32
-    return oracle.State(u16(s.param[lo:hi]), host(s.rho[lo:hi]),
-                        host(s.m_codes[lo:hi]), u16(s.m_scales[g0:g1]),
-                        host(s.v_codes[lo:hi]), u16(s.v_scales[g0:g1]))
+    opt = lambda t, f: None if t is None else f(t)
+    return oracle.State(u16(s.param[lo:hi]), opt(s.rho, lambda r: host(r[lo:hi])),
+                        host(s.m_codes[lo:hi]), opt(s.m_scales, lambda t: u16(t[g0:g1])),
+                        host(s.v_codes[lo:hi]), opt(s.v_scales, lambda t: u16(t[g0:g1])))
 
 
-def _compare(got: oracle.State, want: oracle.State, mb: int, label: str):
-    assert (got.m_scales == want.m_scales).all(), f"{label}: m scales"
-    assert (got.v_scales == want.v_scales).all(), f"{label}: v scales"
+def _compare(got: oracle.State, want: oracle.State, mb, label: str):
+    """mb: 24 | 32 | None (no split).  fp32 moments (no scales) compare bit
+    for bit; codes to the contract's bar, held here to equality."""
     assert (got.param == want.param).all(), f"{label}: bf16 param"
+    if want.m_scales is None:
+        for name in ("m_codes", "v_codes"):
+            a, b = getattr(got, name), getattr(want, name)
+            assert (a.view(np.uint32) == b.view(np.uint32)).all(), f"{label}: fp32 {name}"
+    else:
+        assert (got.m_scales == want.m_scales).all(), f"{label}: m scales"
+        assert (got.v_scales == want.v_scales).all(), f"{label}: v scales"
+        for name in ("m_codes", "v_codes"):
+            agree, worst = code_agreement(getattr(got, name), getattr(want, name))
+            assert worst <= 1 and agree >= 0.9999, (label, name, agree, worst)
+            assert agree == 1.0, f"{label}: {name} agree {agree:.8f}"
+    if mb is None:
+        return
     assert (got.rho == want.rho).all(), f"{label}: rho"
-    for name in ("m_codes", "v_codes"):
-        agree, worst = code_agreement(getattr(got, name), getattr(want, name))
-        assert worst <= 1 and agree >= 0.9999, (label, name, agree, worst)
-        assert agree == 1.0, f"{label}: {name} agree {agree:.8f}"
     a = oracle.reconstruct(got.param, got.rho, mb).astype(np.float64)
     b = oracle.reconstruct(want.param, want.rho, mb).astype(np.float64)
     assert (np.abs(a - b) <= 1e-6 * np.abs(b)).all(), f"{label}: master"
@@ -86,11 +97,24 @@ def test_single_tensor_10_steps(orc):
 RAGGED = [0, 1, 17, 31, 32, 33, 1000, 1023, 1024, 1025, 4096 + 5, 70001, 1 << 17]
 
 
-@pytest.mark.parametrize("mb,comp", [(24, True), (32, True), (24, False), (32, False)])
-def test_ragged_list(orc, mb, comp):
+# (master_bits, companded, quantize_states): the method, the linear ablation
+# of the codec, the page's master_weight_bits=None and quantize_states=False
+# ablations, and their combinations
+VARIANTS = [(24, True, True), (32, True, True), (24, False, True), (32, False, True),
+            (None, True, True), (None, False, True), (24, True, False), (32, True, False),
+            (None, True, False)]
+
+
+def _vid(v):
+    mb, comp, qs = v
+    return f"mb{mb}-{'comp' if comp else 'lin'}-{'q' if qs else 'f32'}"
+
+
+@pytest.mark.parametrize("mb,comp,qs", VARIANTS, ids=[_vid(v) for v in VARIANTS])
+def test_ragged_list(orc, mb, comp, qs):
     require_gpu()
     params = [W.init_param(n, device="cuda", seed=10 + i) for i, n in enumerate(RAGGED)]
-    opt = F.FlashAdamW(params, master_bits=mb, companded=comp, **HP)
+    opt = F.FlashAdamW(params, master_bits=mb, companded=comp, quantize_states=qs, **HP)
     for t in range(1, 4):
         grads = [W.make_grad(n, t, device="cuda", stream_id=i, factor=float(np.exp(i - 6)))
                  for i, n in enumerate(RAGGED)]
@@ -98,8 +122,30 @@ def test_ragged_list(orc, mb, comp):
         opt.step(grads)
         torch.cuda.synchronize()
         for i, (s, pre, g) in enumerate(zip(opt.states, pres, grads)):
-            orc.adamw_step(pre, u16(g), _orc_hp(t, mb, comp))
-            _compare(_snap(s), pre, mb, f"mb{mb} comp{comp} t{t} tensor{i} n{RAGGED[i]}")
+            orc.adamw_step(pre, u16(g), _orc_hp(t, mb, comp, qs))
+            _compare(_snap(s), pre, mb, f"{_vid((mb, comp, qs))} t{t} tensor{i} n{RAGGED[i]}")
+
+
+@pytest.mark.parametrize("mb,comp,qs", [(None, True, True), (24, True, False)],
+                         ids=["mb_none", "fp32_states"])
+def test_ablation_10_steps(orc, mb, comp, qs):
+    """The two ablations over 10 steps on 2^18 params, teacher-forced and
+    free-running against the oracle."""
+    require_gpu()
+    n = (1 << 18) + 77
+    p = W.init_param(n, device="cuda", seed=21)
+    opt = F.FlashAdamW([p], master_bits=mb, companded=comp, quantize_states=qs, **HP)
+    free = orc.State.zeros_like_param(u16(p), mb, quantize_states=qs)
+    for t in range(1, 11):
+        g = W.make_grad(n, t, device="cuda")
+        pre = _snap(opt.states[0])
+        opt.step([g])
+        torch.cuda.synchronize()
+        post = _snap(opt.states[0])
+        orc.adamw_step(pre, u16(g), _orc_hp(t, mb, comp, qs))
+        _compare(post, pre, mb, f"{_vid((mb, comp, qs))} teacher-forced step {t}")
+        orc.adamw_step(free, u16(g), _orc_hp(t, mb, comp, qs))
+        _compare(post, free, mb, f"{_vid((mb, comp, qs))} free-running step {t}")
 
 
 def test_zero_and_large_gradients(orc):
@@ -134,12 +180,19 @@ def _compare_nan_aware(got: oracle.State, want: oracle.State, mb: int, label: st
     """Like _compare, but a NaN parameter or scale matches any NaN: the pages
     fix no NaN payload or sign, and the host and the GPU make different
     default NaNs.  Everything else stays bit-exact."""
+    both_nan = _bf16_nan(got.param) & _bf16_nan(want.param)
+    assert ((got.param == want.param) | both_nan).all(), f"{label}: bf16 param"
+    if mb is not None:
+        assert (got.rho == want.rho).all(), f"{label}: rho"
+    if want.m_scales is None:                 # fp32 moments
+        for name in ("m_codes", "v_codes"):
+            a, b = getattr(got, name), getattr(want, name)
+            same = (a.view(np.uint32) == b.view(np.uint32)) | (np.isnan(a) & np.isnan(b))
+            assert same.all(), f"{label}: fp32 {name}"
+        return
     for name in ("m_scales", "v_scales"):
         a, b = getattr(got, name), getattr(want, name)
         assert ((a == b) | (_f16_nan(a) & _f16_nan(b))).all(), f"{label}: {name}"
-    both_nan = _bf16_nan(got.param) & _bf16_nan(want.param)
-    assert ((got.param == want.param) | both_nan).all(), f"{label}: bf16 param"
-    assert (got.rho == want.rho).all(), f"{label}: rho"
     assert (got.m_codes == want.m_codes).all(), f"{label}: m codes"
     assert (got.v_codes == want.v_codes).all(), f"{label}: v codes"
 
@@ -167,9 +220,10 @@ def _edge_grad(case: str, n: int, t: int) -> torch.Tensor:
 EDGE_EPS = {"tiny_mixed": 1e-8, "large_m_small_eps": 1e-30, "eps_zero": 0.0, "nonfinite": 1e-8}
 
 
-@pytest.mark.parametrize("mb,comp", [(24, True), (32, False)])
+@pytest.mark.parametrize("mb,comp,qs", [(24, True, True), (32, False, True), (None, True, False)],
+                         ids=["mb24-comp", "mb32-lin", "mbnone-f32"])
 @pytest.mark.parametrize("case", sorted(EDGE_EPS))
-def test_lanes_outside_short_division_domain(orc, case, mb, comp):
+def test_lanes_outside_short_division_domain(orc, case, mb, comp, qs):
     """Lanes whose numerators or denominators leave the range where the
     kernel's short division is exact, or whose values are not finite, take
     the generic path; their neighbours in the same group do not.  Both must
@@ -178,7 +232,7 @@ def test_lanes_outside_short_division_domain(orc, case, mb, comp):
     n = 16 * 1024 + 77
     hp = dict(HP, eps=EDGE_EPS[case])
     p = W.init_param(n, device="cuda", seed=90)
-    opt = F.FlashAdamW([p], master_bits=mb, companded=comp, **hp)
+    opt = F.FlashAdamW([p], master_bits=mb, companded=comp, quantize_states=qs, **hp)
     for t in range(1, 4):
         g = _edge_grad(case, n, t)
         pre = _snap(opt.states[0])
@@ -186,7 +240,7 @@ def test_lanes_outside_short_division_domain(orc, case, mb, comp):
         torch.cuda.synchronize()
         orc.adamw_step(pre, u16(g), oracle.hparams(
             lr=hp["lr"], betas=hp["betas"], eps=hp["eps"], weight_decay=hp["weight_decay"],
-            step=t, master_bits=mb, companded=comp))
+            step=t, master_bits=mb, companded=comp, quantize_states=qs))
         _compare_nan_aware(_snap(opt.states[0]), pre, mb, f"{case} mb{mb} comp{comp} t{t}")
 
 
@@ -213,10 +267,10 @@ def test_deterministic_across_runs_and_launch_shapes():
             assert torch.equal(a, b)
 
 
-def _build_list(shapes, mb, comp, seed_base):
+def _build_list(shapes, mb, comp, seed_base, qs=True):
     params = [W.init_param(W.numel(s), device="cuda", seed=seed_base + i)
               for i, (_, s) in enumerate(shapes)]
-    return F.FlashAdamW(params, master_bits=mb, companded=comp, **HP)
+    return F.FlashAdamW(params, master_bits=mb, companded=comp, quantize_states=qs, **HP)
 
 
 def _grads(shapes, t, factors):
@@ -234,8 +288,8 @@ def _sample_ranges(n, rng, k=2):
     return r
 
 
-def _sampled_parity(orc, shapes, mb, comp, label):
-    opt = _build_list(shapes, mb, comp, seed_base=1000)
+def _sampled_parity(orc, shapes, mb, comp, label, qs=True):
+    opt = _build_list(shapes, mb, comp, seed_base=1000, qs=qs)
     factors = W.grad_factors(len(shapes)).numpy()
     rng = np.random.default_rng(7)
     opt.step(_grads(shapes, 1, factors))            # step 1: states become non-trivial
@@ -249,7 +303,7 @@ def _sampled_parity(orc, shapes, mb, comp, label):
     checked = 0
     for i, (s, rr) in enumerate(zip(opt.states, ranges)):
         for (lo, hi), pre, g in zip(rr, pres[i], gs[i]):
-            orc.adamw_step(pre, g, _orc_hp(2, mb, comp))
+            orc.adamw_step(pre, g, _orc_hp(2, mb, comp, qs))
             _compare(_snap(s, lo, hi), pre, mb, f"{label} tensor {i} [{lo}, {hi})")
             checked += hi - lo
     print(f"{label}: {checked} sampled elements bit-exact", flush=True)
@@ -260,6 +314,12 @@ def _sampled_parity(orc, shapes, mb, comp, label):
 def test_decoder_1b_sampled(orc):
     require_gpu()
     _sampled_parity(orc, W.decoder_1b_shapes(), 24, True, "1.2B list, 24-bit")
+
+
+@pytest.mark.parametrize("mb,qs", [(None, True), (24, False)], ids=["mb_none", "fp32_states"])
+def test_decoder_1b_sampled_ablations(orc, mb, qs):
+    require_gpu()
+    _sampled_parity(orc, W.decoder_1b_shapes(), mb, True, f"1.2B list, mb {mb}, quantized {qs}", qs=qs)
 
 
 @pytest.mark.parametrize("mb,comp", [(24, True), (32, True), (24, False)])
