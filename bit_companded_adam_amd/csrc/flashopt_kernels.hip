@@ -63,24 +63,40 @@ __device__ __forceinline__ float group_divisor(uint32_t s)
     return (s & 0x7FFFu) ? f16_value(s) : 1.0f;
 }
 
-// Maximum with the partner lane (lane ^ 1): DPP quad_perm [1, 0, 3, 2].
-// Every lane of the wavefront must be active.
-__device__ __forceinline__ float pair_max(float x)
+// Maximum over aligned groups of G lanes (G = 2, 4 or 8) with DPP:
+// quad_perm [1, 0, 3, 2] (lane ^ 1), quad_perm [2, 3, 0, 1] (lane ^ 2),
+// row_half_mirror (the other quad of each 8 lanes).  Every lane of the
+// wavefront must be active.
+template <int G>
+__device__ __forceinline__ float group_max(float x)
 {
-    const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false);
-    return fmaxf(x, __int_as_float(y));
+    int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false);
+    x = fmaxf(x, __int_as_float(y));
+    if (G >= 4) {
+        y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false);
+        x = fmaxf(x, __int_as_float(y));
+    }
+    if (G >= 8) {
+        y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false);
+        x = fmaxf(x, __int_as_float(y));
+    }
+    return x;
 }
 
-// Byte j of a 16-byte register block, zero- or sign-extended.
-__device__ __forceinline__ uint32_t ubyte(const uint32_t (&w)[4], int j)
+// Byte j of a register block, zero- or sign-extended; 16-bit half j,
+// sign-extended.
+template <int W>
+__device__ __forceinline__ uint32_t ubyte(const uint32_t (&w)[W], int j)
 {
     return (w[j >> 2] >> (8 * (j & 3))) & 0xFFu;
 }
-__device__ __forceinline__ int32_t sbyte(const uint32_t (&w)[4], int j)
+template <int W>
+__device__ __forceinline__ int32_t sbyte(const uint32_t (&w)[W], int j)
 {
     return static_cast<int32_t>(w[j >> 2] << (24 - 8 * (j & 3))) >> 24;
 }
-__device__ __forceinline__ int32_t shalf(const uint32_t (&w)[8], int j)
+template <int W>
+__device__ __forceinline__ int32_t shalf(const uint32_t (&w)[W], int j)
 {
     return static_cast<int32_t>(w[j >> 1] << (16 - 16 * (j & 1))) >> 16;
 }
@@ -332,14 +348,15 @@ __device__ __forceinline__ void store_f32x16(float *p, int cnt, const float (&x)
     }
 }
 
-// Codes of a lane's 16 values y_j = a_j / d of one group under SPEC, packed
-// into four words.
-template <unsigned SPEC>
-__device__ __forceinline__ void encode16(const float (&a)[16], const GroupDiv &gd, uint32_t (&out)[4])
+// Codes of N values y_j = a_j / d of one group under SPEC, packed four to a
+// word.
+template <unsigned SPEC, int N>
+__device__ __forceinline__ void encode(const float (&a)[N], const GroupDiv &gd,
+                                       uint32_t (&out)[N / 4])
 {
     if (SPEC & FLASHOPT_Q_SIGNED) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < N / 4; ++k) {
             int32_t c[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -348,7 +365,7 @@ __device__ __forceinline__ void encode16(const float (&a)[16], const GroupDiv &g
         }
     } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < N / 4; ++k) {
             float y[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -365,28 +382,31 @@ __device__ __forceinline__ void encode16(const float (&a)[16], const GroupDiv &g
     }
 }
 
-// Re-split of a lane's 16 fp32 values into packed bf16 words and packed rho
-// words.  theta' (ties away from zero) is the upper half of pattern + 0x8000;
-// D is the lower half of the pattern read as a signed 16-bit integer.  For
-// the 24-bit master, rho = clamp(round-half-even(D / 256), -128, 127) is
-// formed as v_cvt_pk_u8_f32(D / 256 + 128) - 128: D / 256 + 128 is exact, the
+// rho words of N elements: int16 for the 32-bit master, else int8.
+constexpr int rho_words(int mb, int n) { return mb == 32 ? n / 2 : n / 4; }
+
+// Re-split of N fp32 values into packed bf16 words and packed rho words.
+// theta' (ties away from zero) is the upper half of pattern + 0x8000; D is
+// the lower half of the pattern read as a signed 16-bit integer.  For the
+// 24-bit master, rho = clamp(round-half-even(D / 256), -128, 127) is formed
+// as v_cvt_pk_u8_f32(D / 256 + 128) - 128: D / 256 + 128 is exact, the
 // conversion rounds half to even, clamps to [0, 255] (so D >= 32640 gives
 // 127) and packs the byte in place; the -128 is a per-word XOR.  NaN inputs
 // are not handled here (split_pack_exact covers them).
-template <int MB>
-__device__ __forceinline__ void split_pack(const float (&x)[16], uint32_t (&po)[8],
-                                           uint32_t (&ro)[MB == 32 ? 8 : 4])
+template <int MB, int N>
+__device__ __forceinline__ void split_pack(const float (&x)[N], uint32_t (&po)[N / 2],
+                                           uint32_t (&ro)[rho_words(MB, N)])
 {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < N / 2; ++i)
         po[i] = pack_hi16(__float_as_uint(x[2 * i]) + 0x8000u, __float_as_uint(x[2 * i + 1]) + 0x8000u);
     if constexpr (MB == 32) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < N / 2; ++i)
             ro[i] = pack_lo16(__float_as_uint(x[2 * i]), __float_as_uint(x[2 * i + 1]));
     } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < N / 4; ++k) {
             uint32_t w = 0u;
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
@@ -404,35 +424,35 @@ __device__ __forceinline__ void split_pack(const float (&x)[16], uint32_t (&po)[
 
 // The same re-split element by element, NaN included (NaN keeps its upper
 // half, quieted, with rho = 0).
-template <int MB>
-__device__ __forceinline__ void split_pack_exact(const float (&x)[16], uint32_t (&po)[8],
-                                                 uint32_t (&ro)[MB == 32 ? 8 : 4])
+template <int MB, int N>
+__device__ __forceinline__ void split_pack_exact(const float (&x)[N], uint32_t (&po)[N / 2],
+                                                 uint32_t (&ro)[rho_words(MB, N)])
 {
-    uint32_t top[16];
-    int32_t rr[16];
+    uint32_t top[N];
+    int32_t rr[N];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) split_elem<MB>(x[j], top[j], rr[j]);
+    for (int j = 0; j < N; ++j) split_elem<MB>(x[j], top[j], rr[j]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) po[i] = pack_hi16(top[2 * i], top[2 * i + 1]);
+    for (int i = 0; i < N / 2; ++i) po[i] = pack_hi16(top[2 * i], top[2 * i + 1]);
     if constexpr (MB == 32) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < N / 2; ++i)
             ro[i] = pack_lo16(static_cast<uint32_t>(rr[2 * i]), static_cast<uint32_t>(rr[2 * i + 1]));
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ro[i] = pack_bytes(rr[4 * i], rr[4 * i + 1], rr[4 * i + 2], rr[4 * i + 3]);
+        for (int i = 0; i < N / 4; ++i) ro[i] = pack_bytes(rr[4 * i], rr[4 * i + 1], rr[4 * i + 2], rr[4 * i + 3]);
     }
 }
 
-// Signed codes of a lane's 16 group quotients with the biased rounding of
+// Signed codes of N group quotients with the biased rounding of
 // flashopt_math.h (finite inputs only; callers send lanes holding NaN or
-// infinite values to encode16).
-template <bool SOFTSIGN>
-__device__ __forceinline__ void encode16_s8_finite(const float (&a)[16], const GroupDiv &gd,
-                                                   uint32_t (&out)[4])
+// infinite values to encode).
+template <bool SOFTSIGN, int N>
+__device__ __forceinline__ void encode_s8_finite(const float (&a)[N], const GroupDiv &gd,
+                                                 uint32_t (&out)[N / 4])
 {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < N / 4; ++k) {
         uint32_t b[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -477,11 +497,11 @@ quantize_kernel(const float *__restrict__ x, int64_t n, void *__restrict__ codes
     float amax = kSigned ? fabsf(a[0]) : a[0];
 #pragma unroll
     for (int j = 1; j < 16; ++j) amax = fmaxf(amax, kSigned ? fabsf(a[j]) : a[j]);
-    amax = pair_max(amax);
+    amax = group_max<2>(amax);
     const uint32_t s = f16_bits(amax);
 
     uint32_t out[4];
-    encode16<SPEC>(a, group_div(s), out);
+    encode<SPEC, 16>(a, group_div(s), out);
     store_u8x16(static_cast<uint8_t *>(codes) + e0, cnt, out);
     if ((threadIdx.x & 1) == 0 && cnt > 0) st_u16(scales + e0 / kGroup, static_cast<uint16_t>(s));
 }
@@ -527,8 +547,8 @@ split_kernel(const float *__restrict__ master, int64_t n, uint16_t *__restrict__
     bool any_nan = false;
 #pragma unroll
     for (int j = 0; j < 16; ++j) any_nan |= x[j] != x[j];
-    if (any_nan) split_pack_exact<MB>(x, pw, rw);
-    else split_pack<MB>(x, pw, rw);
+    if (any_nan) split_pack_exact<MB, 16>(x, pw, rw);
+    else split_pack<MB, 16>(x, pw, rw);
     store_u16x16(param + e0, cnt, pw);
     if constexpr (MB == 32) store_u16x16(static_cast<uint16_t *>(rho) + e0, cnt, rw);
     else store_u8x16(static_cast<uint8_t *>(rho) + e0, cnt, rw);
@@ -576,203 +596,183 @@ __device__ __forceinline__ uint32_t plain_elem(float x)
     return bf16_rne_top(u);
 }
 
-// The new parameter words (and rho words with a master split) of a lane's 16
-// updated values.  EXACT selects the element-wise NaN-safe routines.
-template <int MB, bool EXACT>
-__device__ __forceinline__ void pack_theta(const float (&x)[16], uint32_t (&po)[8],
-                                           uint32_t (&ro)[MB == 32 ? 8 : 4])
+// The new parameter words (and rho words with a master split) of N updated
+// values.  EXACT selects the element-wise NaN-safe routines.
+template <int MB, bool EXACT, int N>
+__device__ __forceinline__ void pack_theta(const float (&x)[N], uint32_t (&po)[N / 2],
+                                           uint32_t (&ro)[rho_words(MB, N)])
 {
     if constexpr (MB == 0) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < N / 2; ++i) {
             if (EXACT) po[i] = pack_hi16(plain_elem(x[2 * i]), plain_elem(x[2 * i + 1]));
             else po[i] = pack_hi16(bf16_rne_top(__float_as_uint(x[2 * i])),
                                    bf16_rne_top(__float_as_uint(x[2 * i + 1])));
         }
     } else if constexpr (EXACT) {
-        split_pack_exact<MB>(x, po, ro);
+        split_pack_exact<MB, N>(x, po, ro);
     } else {
-        split_pack<MB>(x, po, ro);
+        split_pack<MB, N>(x, po, ro);
     }
 }
 
-// One lane's inputs.  Arrays a variant does not use are removed by the
-// compiler.
-template <int MB, int ST>
-struct LaneIn {
-    uint32_t pw[8], gw[8];
-    uint32_t rw[MB == 32 ? 8 : 4];
-    uint32_t mw[4], vw[4];        // codes (quantized states)
-    float mf[16], vf[16];         // fp32 states
-    uint32_t smb, svb;            // fp16 scale bits of the lane's group
+// ----------------------------------------------------------- lane units
+//
+// A wavefront owns a 1024-element chunk; each lane takes its elements in
+// units of N consecutive elements: unit u of lane l is chunk elements
+// 64 N u + N l + i (i < N), so every access instruction of the wavefront
+// covers one contiguous block of each stream.  A 32-element quantization
+// group is one unit of each of 32 / N adjacent lanes.  The per-variant N
+// (unit_elems) follows from the access shape: a 16-byte access per lane
+// streams best; a lane moving 64 contiguous bytes of one stream in four
+// 16-byte accesses (fp32 moments with N = 16) streams at well under half the
+// bandwidth, and 32 bytes (16-bit streams with N = 16) somewhat below.
+
+// BYTES (4, 8, 16, 32 or 64) consecutive bytes at p into words, streaming.
+template <int BYTES>
+__device__ __forceinline__ void ld_words(const void *p, uint32_t *w)
+{
+    if constexpr (BYTES == 4) {
+        w[0] = ld4s(p);
+    } else if constexpr (BYTES == 8) {
+        const u32x2 v = ld8s(p);
+        w[0] = v.x; w[1] = v.y;
+    } else {
+#pragma unroll
+        for (int k = 0; k < BYTES / 16; ++k) {
+            const uint4 v = ld16s(p, k);
+            w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
+        }
+    }
+}
+
+template <int BYTES>
+__device__ __forceinline__ void st_words(void *p, const uint32_t *w)
+{
+    if constexpr (BYTES == 4) {
+        st4s(p, w[0]);
+    } else if constexpr (BYTES == 8) {
+        st8s(p, u32x2{w[0], w[1]});
+    } else {
+#pragma unroll
+        for (int k = 0; k < BYTES / 16; ++k)
+            st16s(p, make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]), k);
+    }
+}
+
+// The first cnt of N elements of ESZ (1, 2 or 4) bytes at p into words,
+// zeros beyond; and the matching masked store.
+template <int ESZ, int N>
+__device__ __forceinline__ void ld_elems(const void *p, int cnt, uint32_t *w)
+{
+#pragma unroll
+    for (int i = 0; i < N * ESZ / 4; ++i) w[i] = 0u;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        if (j < cnt) {
+            if constexpr (ESZ == 1) w[j >> 2] |= static_cast<uint32_t>(((g_cu8 *)p)[j]) << (8 * (j & 3));
+            if constexpr (ESZ == 2) w[j >> 1] |= static_cast<uint32_t>(((g_cu16 *)p)[j]) << (16 * (j & 1));
+            if constexpr (ESZ == 4) w[j] = ((g_cu32 *)p)[j];
+        }
+    }
+}
+
+template <int ESZ, int N>
+__device__ __forceinline__ void st_elems(void *p, int cnt, const uint32_t *w)
+{
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        if (j < cnt) {
+            if constexpr (ESZ == 1) ((g_u8 *)p)[j] = static_cast<uint8_t>(w[j >> 2] >> (8 * (j & 3)));
+            if constexpr (ESZ == 2) ((g_u16 *)p)[j] = static_cast<uint16_t>(w[j >> 1] >> (16 * (j & 1)));
+            if constexpr (ESZ == 4) ((g_u32 *)p)[j] = w[j];
+        }
+    }
+}
+
+// Elements per unit of each step variant: fp32 moments need N = 4 for
+// 16-byte accesses; the quantized variants use N = 8 (16-bit streams in
+// 16-byte accesses, a lane quad per group).  Measured on the 8.0B list
+// against N = 16: 1.1% faster for the 24-bit master, 8.4% for the 32-bit
+// master, 4.1% for the linear codec.
+constexpr int unit_elems(int mb, int st) { return st == kStatesFp32 ? 4 : 8; }
+
+// One unit's inputs (arrays a variant does not use are removed by the
+// compiler).
+template <int MB, int ST, int N>
+struct UnitIn {
+    uint32_t pw[N / 2], gw[N / 2];
+    uint32_t rw[rho_words(MB, N)];
+    uint32_t mw[N / 4], vw[N / 4];   // codes (quantized states)
+    uint32_t mf[N], vf[N];           // fp32 states, bit patterns
+    uint32_t smb, svb;               // fp16 scale bits of the unit's group
 };
 
-// Element ownership of the fp32-state variants: lane l owns chunk elements
-// 256 q + 4 l + i (q, i in 0..3; the lane's element j is q = j / 4,
-// i = j % 4), so every access instruction of a wavefront covers one
-// contiguous block of each stream (fp32 1 KiB, bf16 512 B, int8 256 B).  A
-// lane owning 16 consecutive elements would make each 16-byte fp32 access
-// cover a quarter of every 64 bytes it touches, which streams at well under
-// half the bandwidth.  These variants have no quantization groups, so the
-// ownership is free.
-__device__ __forceinline__ int64_t q_elem(int lane, int j)
+// First element of unit u of a lane, relative to the chunk.
+template <int N>
+__device__ __forceinline__ int unit_first(int u, int lane)
 {
-    return 256 * (j >> 2) + 4 * lane + (j & 3);
+    return 64 * N * u + N * lane;
 }
 
-template <int MB, int ST, bool FULL>
-__device__ __forceinline__ void load_lane_q(const DevTensor &d, int64_t off, int lane,
-                                            LaneIn<MB, ST> &in)
+// Elements of the unit that exist: N, fewer at a ragged end, or 0.
+template <int N>
+__device__ __forceinline__ int unit_count(int64_t numel, int64_t e)
 {
-    const float *const mp = reinterpret_cast<const float *>(d.m_codes) + off;
-    const float *const vp = reinterpret_cast<const float *>(d.v_codes) + off;
+    const int64_t rem = numel - e;
+    return rem >= N ? N : (rem > 0 ? static_cast<int>(rem) : 0);
+}
+
+// Loads of one unit of every stream.  FULL: straight-line streaming loads;
+// otherwise element-masked loads with zeros for missing elements (and zero
+// scales for a unit with none).
+template <int MB, int ST, int N, bool FULL>
+__device__ __forceinline__ void load_unit(const DevTensor &d, int64_t e, int cnt,
+                                          UnitIn<MB, ST, N> &in)
+{
     const uint8_t *const rp = static_cast<const uint8_t *>(d.rho);
+    const uint32_t *const mfp = reinterpret_cast<const uint32_t *>(d.m_codes);
+    const uint32_t *const vfp = reinterpret_cast<const uint32_t *>(d.v_codes);
     in.smb = 0u;
     in.svb = 0u;
     if (FULL) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int64_t e = off + 256 * q + 4 * lane;
-            u32x2 w = ld8s(d.param + e);
-            in.pw[2 * q] = w.x; in.pw[2 * q + 1] = w.y;
-            w = ld8s(d.grad + e);
-            in.gw[2 * q] = w.x; in.gw[2 * q + 1] = w.y;
-            if constexpr (MB == 24) in.rw[q] = ld4s(rp + e);
-            if constexpr (MB == 32) {
-                w = ld8s(rp + 2 * e);
-                in.rw[2 * q] = w.x; in.rw[2 * q + 1] = w.y;
-            }
-            const uint4 a = ld16s(mp + 256 * q + 4 * lane);
-            const uint4 b = ld16s(vp + 256 * q + 4 * lane);
-            in.mf[4 * q] = __uint_as_float(a.x); in.mf[4 * q + 1] = __uint_as_float(a.y);
-            in.mf[4 * q + 2] = __uint_as_float(a.z); in.mf[4 * q + 3] = __uint_as_float(a.w);
-            in.vf[4 * q] = __uint_as_float(b.x); in.vf[4 * q + 1] = __uint_as_float(b.y);
-            in.vf[4 * q + 2] = __uint_as_float(b.z); in.vf[4 * q + 3] = __uint_as_float(b.w);
+        ld_words<2 * N>(d.param + e, in.pw);
+        ld_words<2 * N>(d.grad + e, in.gw);
+        if constexpr (MB == 24) ld_words<N>(rp + e, in.rw);
+        if constexpr (MB == 32) ld_words<2 * N>(rp + 2 * e, in.rw);
+        if constexpr (ST == kStatesFp32) {
+            ld_words<4 * N>(mfp + e, in.mf);
+            ld_words<4 * N>(vfp + e, in.vf);
+        } else {
+            ld_words<N>(d.m_codes + e, in.mw);
+            ld_words<N>(d.v_codes + e, in.vw);
+            in.smb = ld_u16(d.m_scales + e / kGroup);
+            in.svb = ld_u16(d.v_scales + e / kGroup);
         }
     } else {
-        const int64_t rem = d.numel - off;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) { in.pw[i] = 0u; in.gw[i] = 0u; }
-#pragma unroll
-        for (int i = 0; i < (MB == 32 ? 8 : 4); ++i) in.rw[i] = 0u;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int64_t k = q_elem(lane, j);
-            in.mf[j] = 0.0f;
-            in.vf[j] = 0.0f;
-            if (k < rem) {
-                const int sh = 16 * (j & 1);
-                in.pw[j >> 1] |= static_cast<uint32_t>(((g_cu16 *)(d.param + off))[k]) << sh;
-                in.gw[j >> 1] |= static_cast<uint32_t>(((g_cu16 *)(d.grad + off))[k]) << sh;
-                if constexpr (MB == 24)
-                    in.rw[j >> 2] |= static_cast<uint32_t>(((g_cu8 *)(rp + off))[k]) << (8 * (j & 3));
-                if constexpr (MB == 32)
-                    in.rw[j >> 1] |= static_cast<uint32_t>(((g_cu16 *)(rp + 2 * off))[k]) << sh;
-                in.mf[j] = ((g_cf32 *)mp)[k];
-                in.vf[j] = ((g_cf32 *)vp)[k];
+        ld_elems<2, N>(d.param + e, cnt, in.pw);
+        ld_elems<2, N>(d.grad + e, cnt, in.gw);
+        if constexpr (MB == 24) ld_elems<1, N>(rp + e, cnt, in.rw);
+        if constexpr (MB == 32) ld_elems<2, N>(rp + 2 * e, cnt, in.rw);
+        if constexpr (ST == kStatesFp32) {
+            ld_elems<4, N>(mfp + e, cnt, in.mf);
+            ld_elems<4, N>(vfp + e, cnt, in.vf);
+        } else {
+            ld_elems<1, N>(d.m_codes + e, cnt, in.mw);
+            ld_elems<1, N>(d.v_codes + e, cnt, in.vw);
+            if (cnt > 0) {
+                in.smb = ld_u16(d.m_scales + e / kGroup);
+                in.svb = ld_u16(d.v_scales + e / kGroup);
             }
         }
     }
 }
 
-template <int MB, bool FULL>
-__device__ __forceinline__ void store_lane_q(const DevTensor &d, int64_t off, int lane,
-                                             const uint32_t (&po)[8],
-                                             const uint32_t (&ro)[MB == 32 ? 8 : 4],
-                                             const float (&m1)[16], const float (&v1)[16])
-{
-    float *const mp = reinterpret_cast<float *>(d.m_codes) + off;
-    float *const vp = reinterpret_cast<float *>(d.v_codes) + off;
-    uint8_t *const rp = static_cast<uint8_t *>(d.rho);
-    if (FULL) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int64_t e = off + 256 * q + 4 * lane;
-            st8s(d.param + e, u32x2{po[2 * q], po[2 * q + 1]});
-            if constexpr (MB == 24) st4s(rp + e, ro[q]);
-            if constexpr (MB == 32) st8s(rp + 2 * e, u32x2{ro[2 * q], ro[2 * q + 1]});
-            st16s(mp + 256 * q + 4 * lane,
-                  make_uint4(__float_as_uint(m1[4 * q]), __float_as_uint(m1[4 * q + 1]),
-                             __float_as_uint(m1[4 * q + 2]), __float_as_uint(m1[4 * q + 3])));
-            st16s(vp + 256 * q + 4 * lane,
-                  make_uint4(__float_as_uint(v1[4 * q]), __float_as_uint(v1[4 * q + 1]),
-                             __float_as_uint(v1[4 * q + 2]), __float_as_uint(v1[4 * q + 3])));
-        }
-    } else {
-        const int64_t rem = d.numel - off;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int64_t k = q_elem(lane, j);
-            if (k < rem) {
-                const int sh = 16 * (j & 1);
-                ((g_u16 *)(d.param + off))[k] = static_cast<uint16_t>(po[j >> 1] >> sh);
-                if constexpr (MB == 24)
-                    ((g_u8 *)(rp + off))[k] = static_cast<uint8_t>(ro[j >> 2] >> (8 * (j & 3)));
-                if constexpr (MB == 32)
-                    ((g_u16 *)(rp + 2 * off))[k] = static_cast<uint16_t>(ro[j >> 1] >> sh);
-                ((g_f32 *)mp)[k] = m1[j];
-                ((g_f32 *)vp)[k] = v1[j];
-            }
-        }
-    }
-}
-
-// Loads of a lane's 16 elements of every stream.  FULL: straight-line 16-byte
-// streaming loads; otherwise element-masked loads with zeros past cnt.  The
-// quantized-state variants own 16 consecutive elements per lane (a lane pair
-// is a group); the fp32-state variants use load_lane_q's ownership.
-template <int MB, int ST, bool FULL>
-__device__ __forceinline__ void load_lane(const DevTensor &d, int64_t off, int lane, int cnt,
-                                          LaneIn<MB, ST> &in)
-{
-    if constexpr (ST == kStatesFp32) {
-        (void)cnt;
-        load_lane_q<MB, ST, FULL>(d, off, lane, in);
-        return;
-    }
-    const int64_t e = off + static_cast<int64_t>(lane) * kLaneElems;
-    const uint16_t *const pp = d.param + e;
-    const uint16_t *const gp = d.grad + e;
-    const uint8_t *const rp = static_cast<const uint8_t *>(d.rho) + e * (MB == 32 ? 2 : 1);
-    const uint16_t *const msp = d.m_scales + off / kGroup + (lane >> 1);
-    const uint16_t *const vsp = d.v_scales + off / kGroup + (lane >> 1);
-    in.smb = 0u;
-    in.svb = 0u;
-    if (FULL) {
-        uint4 q;
-        q = ld16s(pp, 0); in.pw[0] = q.x; in.pw[1] = q.y; in.pw[2] = q.z; in.pw[3] = q.w;
-        q = ld16s(pp, 1); in.pw[4] = q.x; in.pw[5] = q.y; in.pw[6] = q.z; in.pw[7] = q.w;
-        q = ld16s(gp, 0); in.gw[0] = q.x; in.gw[1] = q.y; in.gw[2] = q.z; in.gw[3] = q.w;
-        q = ld16s(gp, 1); in.gw[4] = q.x; in.gw[5] = q.y; in.gw[6] = q.z; in.gw[7] = q.w;
-        if constexpr (MB != 0) {
-            q = ld16s(rp, 0); in.rw[0] = q.x; in.rw[1] = q.y; in.rw[2] = q.z; in.rw[3] = q.w;
-        }
-        if constexpr (MB == 32) {
-            q = ld16s(rp, 1); in.rw[4] = q.x; in.rw[5] = q.y; in.rw[6] = q.z; in.rw[7] = q.w;
-        }
-        q = ld16s(d.m_codes + e); in.mw[0] = q.x; in.mw[1] = q.y; in.mw[2] = q.z; in.mw[3] = q.w;
-        q = ld16s(d.v_codes + e); in.vw[0] = q.x; in.vw[1] = q.y; in.vw[2] = q.z; in.vw[3] = q.w;
-        in.smb = ld_u16(msp);
-        in.svb = ld_u16(vsp);
-    } else {
-        load_u16x16(pp, cnt, in.pw);
-        load_u16x16(gp, cnt, in.gw);
-        if constexpr (MB == 32) load_u16x16(reinterpret_cast<const uint16_t *>(rp), cnt, in.rw);
-        else if constexpr (MB == 24) load_u8x16(rp, cnt, in.rw);
-        load_u8x16(d.m_codes + e, cnt, in.mw);
-        load_u8x16(d.v_codes + e, cnt, in.vw);
-        if (cnt > 0) {
-            in.smb = ld_u16(msp);
-            in.svb = ld_u16(vsp);
-        }
-    }
-}
-
-// Element j of a lane: the master theta (reconstructed, or the bf16 value
+// Element j of a unit: the master theta (reconstructed, or the bf16 value
 // itself without a split), and the new moments m1 = b1 m0 + (1 - b1) g and
 // v1 = b2 v0 + ((1 - b2) g) g from the dequantized (or fp32) old ones.
-template <int MB, int ST>
-__device__ __forceinline__ void element_moments(const LaneIn<MB, ST> &in, int j,
+template <int MB, int ST, int N>
+__device__ __forceinline__ void element_moments(const UnitIn<MB, ST, N> &in, int j,
                                                 const StepScalars &sc, const float *s_mu,
                                                 const float *s_vu, float ms, float vs,
                                                 float &theta, float &m, float &v)
@@ -789,8 +789,8 @@ __device__ __forceinline__ void element_moments(const LaneIn<MB, ST> &in, int j,
     const float g = (j & 1) ? bf16_hi(in.gw[j >> 1]) : bf16_lo(in.gw[j >> 1]);
     float m0, v0;
     if constexpr (ST == kStatesFp32) {
-        m0 = in.mf[j];
-        v0 = in.vf[j];
+        m0 = __uint_as_float(in.mf[j]);
+        v0 = __uint_as_float(in.vf[j]);
     } else {
         m0 = s_mu[ubyte(in.mw, j)] * ms;
         const float a0 = s_vu[ubyte(in.vw, j)] * vs;
@@ -805,102 +805,98 @@ __device__ __forceinline__ void element_moments(const LaneIn<MB, ST> &in, int j,
     v = v_decay + v_new;
 }
 
-// The generic recomputation of one lane's updated parameter (and momentum
-// codes) for lanes outside the short sequences' domains (see step_chunk):
-// reload the lane's inputs, redo the element arithmetic with correctly
+// The generic recomputation of one unit's updated parameter (and momentum
+// codes) for lanes outside the short sequences' domains (see step_unit):
+// reload the unit's inputs, redo the element arithmetic with correctly
 // rounded division and sqrt, and encode and split with the NaN-safe element
 // routines.  The variance codes, fp32 moments and the group scales do not
 // depend on these paths and are produced by the caller.
-template <int MB, int ST>
-__device__ __forceinline__ void lane_exact(const DevTensor &d, int64_t off, int lane, int cnt,
+template <int MB, int ST, int N>
+__device__ __forceinline__ void unit_exact(const DevTensor &d, int64_t e, int cnt,
                                            const StepScalars &sc, const float *s_mu,
                                            const float *s_vu, const GroupDiv &gdm,
-                                           uint32_t (&mo)[4], uint32_t (&po)[8],
-                                           uint32_t (&ro)[MB == 32 ? 8 : 4])
+                                           uint32_t (&mo)[N / 4], uint32_t (&po)[N / 2],
+                                           uint32_t (&ro)[rho_words(MB, N)])
 {
     constexpr unsigned kMSpec =
         ST == kStatesCompanded ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
-    // an opaque copy of the lane index keeps the compiler from reusing the
+    // an opaque copy of the element index keeps the compiler from reusing the
     // common path's loads, whose values would then stay live up to here
-    asm volatile("" : "+v"(lane));
-    LaneIn<MB, ST> in;
-    load_lane<MB, ST, false>(d, off, lane, cnt, in);
+    asm volatile("" : "+v"(e));
+    UnitIn<MB, ST, N> in;
+    load_unit<MB, ST, N, false>(d, e, cnt, in);
     const float ms = f16_value(in.smb);
     const float vs = f16_value(in.svb);
-    float m1[16], th1[16];
+    float m1[N], th1[N];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < N; ++j) {
         float theta, m, v;
-        element_moments<MB, ST>(in, j, sc, s_mu, s_vu, ms, vs, theta, m, v);
+        element_moments<MB, ST, N>(in, j, sc, s_mu, s_vu, ms, vs, theta, m, v);
         const float den = sqrtf(v) * sc.k2 + sc.eps;
         const float num = sc.alpha * m;
         th1[j] = theta * sc.cwd - num / den;
         m1[j] = j < cnt ? m : 0.0f;
     }
-    if constexpr (ST != kStatesFp32) encode16<kMSpec>(m1, gdm, mo);
-    pack_theta<MB, true>(th1, po, ro);
+    if constexpr (ST != kStatesFp32) encode<kMSpec, N>(m1, gdm, mo);
+    pack_theta<MB, true, N>(th1, po, ro);
 }
 
-// One 1024-element chunk of one tensor, processed by one wavefront: each lane
-// loads 16 elements of every stream, dequantizes m and v (or reads them as
-// fp32), rebuilds the master (or widens the bf16 parameter), applies AdamW,
-// finds the group maxima (one DPP exchange with the partner lane), and
-// writes scales and codes (or fp32 moments) and the new parameter (re-split,
-// or cast to bf16).  FULL chunks (every lane holds 16 elements) use plain
-// 16-byte streaming accesses; the ragged last chunk of a tensor masks per
-// element and pads with zeros.
-template <int MB, int ST, bool FULL>
-__device__ __forceinline__ void step_chunk(const DevTensor &d, int64_t off, int lane,
-                                           const StepScalars &sc, const float *s_mu,
-                                           const float *s_vu)
+// One unit of one lane: load every stream, dequantize m and v (or read them
+// as fp32), rebuild the master (or widen the bf16 parameter), apply AdamW,
+// find the group maxima (DPP exchanges among the group's lanes), and write
+// scales and codes (or fp32 moments) and the new parameter (re-split, or
+// cast to bf16).  Every lane of the wavefront calls this for the same u.
+// FULL units use straight-line streaming accesses; at the ragged end of a
+// tensor accesses are masked per element and groups padded with zeros.
+template <int MB, int ST, int N, bool FULL>
+__device__ __forceinline__ void step_unit(const DevTensor &d, int64_t off, int u, int lane,
+                                          const StepScalars &sc, const float *s_mu,
+                                          const float *s_vu)
 {
     constexpr bool kQuant = ST != kStatesFp32;
     constexpr bool kComp = ST == kStatesCompanded;
     constexpr unsigned kVSpec = kComp ? FLASHOPT_SPEC_VARIANCE : FLASHOPT_SPEC_VARIANCE_LINEAR;
-    constexpr int kRhoWords = MB == 32 ? 8 : 4;
-
-    const int lofs = lane * kLaneElems;
-    const int cnt = FULL ? kLaneElems : lane_count(d.numel - off, lofs);
-    const int64_t e = off + lofs;
+    const int64_t e = off + unit_first<N>(u, lane);
+    const int cnt = FULL ? N : unit_count<N>(d.numel, e);
 
     // ---- loads (missing elements read as zero)
-    LaneIn<MB, ST> in;
-    load_lane<MB, ST, FULL>(d, off, lane, cnt, in);
+    UnitIn<MB, ST, N> in;
+    load_unit<MB, ST, N, FULL>(d, e, cnt, in);
     const float ms = f16_value(in.smb);
     const float vs = f16_value(in.svb);
 
     // ---- dequantize, reconstruct, moments
-    float thd[16], m1[16], v1[16];
+    float thd[N], m1[N], v1[N];
     uint32_t vbits = 0u;                    // unsigned max of the v1 bit patterns
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < N; ++j) {
         float theta;
-        element_moments<MB, ST>(in, j, sc, s_mu, s_vu, ms, vs, theta, m1[j], v1[j]);
+        element_moments<MB, ST, N>(in, j, sc, s_mu, s_vu, ms, vs, theta, m1[j], v1[j]);
         thd[j] = theta * sc.cwd;
         vbits = max(vbits, __float_as_uint(v1[j]));
     }
     if (!FULL && kQuant) {                  // zero pad of the ragged last group
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
+        for (int j = 0; j < N; ++j)
             if (j >= cnt) { m1[j] = 0.0f; v1[j] = 0.0f; }
     }
 
     // ---- sqrt(v1)
-    float rt[16];
+    float rt[N];
     if (vbits < kSqrtFastEnd) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) rt[j] = math::sqrt_cr(v1[j]);
+        for (int j = 0; j < N; ++j) rt[j] = math::sqrt_cr(v1[j]);
     } else {                                // rare: v outside the fast sqrt's range
 #pragma unroll
-        for (int j = 0; j < 16; ++j) rt[j] = sqrtf(v1[j]);
+        for (int j = 0; j < N; ++j) rt[j] = sqrtf(v1[j]);
     }
 
-    // ---- lane maxima of |m1|, of what the variance quantizer sees, of sqrt(v1)
+    // ---- unit maxima of |m1|, of what the variance quantizer sees, of sqrt(v1)
     // (the maxima start from the first element: a group of NaNs only has a
     // NaN maximum, as the IEEE maxNum reduction over its elements gives)
     float am = fabsf(m1[0]), av = kComp ? rt[0] : v1[0], rmax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < N; ++j) {
         am = fmaxf(am, fabsf(m1[j]));
         if (kComp) av = fmaxf(av, rt[j]);
         else { av = fmaxf(av, v1[j]); rmax = fmaxf(rmax, rt[j]); }
@@ -908,15 +904,15 @@ __device__ __forceinline__ void step_chunk(const DevTensor &d, int64_t off, int 
     if (kComp) rmax = av;
 
     // ---- the update theta (1 - lr wd) - (alpha m1) / (sqrt(v1) k2 + eps),
-    // with the short division when the lane's numerators and denominators
+    // with the short division when the unit's numerators and denominators
     // lie in its exact domain (den <= den_hi, nonzero |num| >= tmin)
     const float den_hi = rmax * sc.k2 + sc.eps;
     const float tmin = fmaxf(0x1p-102f, den_hi * 0x1p-126f);
     const uint32_t tkey = (__float_as_uint(tmin) << 1) - 1u;
     uint32_t kmin = 0xFFFFFFFFu;          // min over nonzero |num| of its doubled pattern - 1
-    float th1[16];
+    float th1[N];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < N; ++j) {
         const float den = rt[j] * sc.k2 + sc.eps;
         const float num = sc.alpha * m1[j];
         th1[j] = thd[j] - math::div_markstein(num, den, math::recip_cr(den));
@@ -925,61 +921,67 @@ __device__ __forceinline__ void step_chunk(const DevTensor &d, int64_t off, int 
     }
     bool any_nan = false;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) any_nan |= th1[j] != th1[j];
+    for (int j = 0; j < N; ++j) any_nan |= th1[j] != th1[j];
     const bool exact = sc.fast_div == 0 || vbits >= kSqrtFastEnd ||
                        !(sc.alpha * am <= sc.num_max) || kmin < tkey || any_nan;
 
-    // ---- group maxima over the lane pair, scales, variance codes
-    uint32_t mo[4], vo[4], po[8], ro[kRhoWords];
+    // ---- group maxima, scales, variance codes
+    uint32_t mo[N / 4], vo[N / 4], po[N / 2], ro[rho_words(MB, N)];
     uint32_t sm_out = 0u, sv_out = 0u;
     GroupDiv gdm{1.0f, 1.0f};
     if constexpr (kQuant) {
-        am = pair_max(am);
-        av = pair_max(av);
-        sm_out = f16_bits(am);
-        sv_out = f16_bits(av);
+        sm_out = f16_bits(group_max<32 / N>(am));
+        sv_out = f16_bits(group_max<32 / N>(av));
         gdm = group_div(sm_out);
-        if constexpr (kComp) encode16<kVSpec>(rt, group_div(sv_out), vo);
-        else encode16<kVSpec>(v1, group_div(sv_out), vo);
+        if constexpr (kComp) encode<kVSpec, N>(rt, group_div(sv_out), vo);
+        else encode<kVSpec, N>(v1, group_div(sv_out), vo);
     }
 
     // ---- momentum codes and the new parameter
     if (!exact) {
-        if constexpr (kQuant) encode16_s8_finite<kComp>(m1, gdm, mo);
-        pack_theta<MB, false>(th1, po, ro);
+        if constexpr (kQuant) encode_s8_finite<kComp, N>(m1, gdm, mo);
+        pack_theta<MB, false, N>(th1, po, ro);
     } else {
-        // rare: a lane outside the short sequences' domains (tiny or huge
+        // rare: a unit outside the short sequences' domains (tiny or huge
         // numerators, NaN or infinite m or theta, unusual hyper-parameters)
         // is recomputed from its inputs in memory with the generic
         // operations; nothing has been stored yet, and the group scales
         // above are already exact
-        lane_exact<MB, ST>(d, off, lane, cnt, sc, s_mu, s_vu, gdm, mo, po, ro);
+        unit_exact<MB, ST, N>(d, e, cnt, sc, s_mu, s_vu, gdm, mo, po, ro);
     }
 
     // ---- stores
-    if constexpr (!kQuant) {
-        store_lane_q<MB, FULL>(d, off, lane, po, ro, m1, v1);
-        return;
-    }
-    uint16_t *const pp = d.param + e;
-    uint8_t *const rp = static_cast<uint8_t *>(d.rho) + e * (MB == 32 ? 2 : 1);
+    uint8_t *const rp = static_cast<uint8_t *>(d.rho);
+    uint32_t mb[N], vb[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) { mb[j] = __float_as_uint(m1[j]); vb[j] = __float_as_uint(v1[j]); }
     if (FULL) {
-        st16s(pp, make_uint4(po[0], po[1], po[2], po[3]), 0);
-        st16s(pp, make_uint4(po[4], po[5], po[6], po[7]), 1);
-        if constexpr (MB != 0) st16s(rp, make_uint4(ro[0], ro[1], ro[2], ro[3]), 0);
-        if constexpr (MB == 32) st16s(rp, make_uint4(ro[4], ro[5], ro[6], ro[7]), 1);
-        st16s(d.m_codes + e, make_uint4(mo[0], mo[1], mo[2], mo[3]));
-        st16s(d.v_codes + e, make_uint4(vo[0], vo[1], vo[2], vo[3]));
+        st_words<2 * N>(d.param + e, po);
+        if constexpr (MB == 24) st_words<N>(rp + e, ro);
+        if constexpr (MB == 32) st_words<2 * N>(rp + 2 * e, ro);
+        if constexpr (kQuant) {
+            st_words<N>(d.m_codes + e, mo);
+            st_words<N>(d.v_codes + e, vo);
+        } else {
+            st_words<4 * N>(reinterpret_cast<uint32_t *>(d.m_codes) + e, mb);
+            st_words<4 * N>(reinterpret_cast<uint32_t *>(d.v_codes) + e, vb);
+        }
     } else {
-        store_u16x16(pp, cnt, po);
-        if constexpr (MB == 32) store_u16x16(reinterpret_cast<uint16_t *>(rp), cnt, ro);
-        else if constexpr (MB == 24) store_u8x16(rp, cnt, ro);
-        store_u8x16(d.m_codes + e, cnt, mo);
-        store_u8x16(d.v_codes + e, cnt, vo);
+        st_elems<2, N>(d.param + e, cnt, po);
+        if constexpr (MB == 24) st_elems<1, N>(rp + e, cnt, ro);
+        if constexpr (MB == 32) st_elems<2, N>(rp + 2 * e, cnt, ro);
+        if constexpr (kQuant) {
+            st_elems<1, N>(d.m_codes + e, cnt, mo);
+            st_elems<1, N>(d.v_codes + e, cnt, vo);
+        } else {
+            st_elems<4, N>(reinterpret_cast<uint32_t *>(d.m_codes) + e, cnt, mb);
+            st_elems<4, N>(reinterpret_cast<uint32_t *>(d.v_codes) + e, cnt, vb);
+        }
     }
-    if (kQuant && (lane & 1) == 0 && cnt > 0) {
-        st_u16(d.m_scales + off / kGroup + (lane >> 1), static_cast<uint16_t>(sm_out));
-        st_u16(d.v_scales + off / kGroup + (lane >> 1), static_cast<uint16_t>(sv_out));
+    // the group's first lane writes its scales
+    if (kQuant && lane % (32 / N) == 0 && cnt > 0) {
+        st_u16(d.m_scales + e / kGroup, static_cast<uint16_t>(sm_out));
+        st_u16(d.v_scales + e / kGroup, static_cast<uint16_t>(sv_out));
     }
 }
 
@@ -996,6 +998,8 @@ adamw_step_kernel(const DevTensor *__restrict__ tensors, const int32_t *__restri
 {
     constexpr unsigned kMSpec =
         ST == kStatesCompanded ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
+    constexpr int kN = unit_elems(MB, ST);
+    constexpr int kUnits = kLaneElems / kN;
     __shared__ float s_mu[256];   // momentum: q/127 (companded: / (2 - |.|))
     __shared__ float s_vu[256];   // variance: q/255
     if constexpr (ST != kStatesFp32) {
@@ -1024,8 +1028,13 @@ adamw_step_kernel(const DevTensor *__restrict__ tensors, const int32_t *__restri
         t = __builtin_amdgcn_readfirstlane(t);
         const DevTensor d = tensors[t];
         const int64_t off = static_cast<int64_t>(c - chunk_start[t]) * kChunkElems;
-        if (off + kChunkElems <= d.numel) step_chunk<MB, ST, true>(d, off, lane, sc, s_mu, s_vu);
-        else step_chunk<MB, ST, false>(d, off, lane, sc, s_mu, s_vu);
+        if (off + kChunkElems <= d.numel) {
+#pragma unroll
+            for (int u = 0; u < kUnits; ++u) step_unit<MB, ST, kN, true>(d, off, u, lane, sc, s_mu, s_vu);
+        } else {
+#pragma unroll
+            for (int u = 0; u < kUnits; ++u) step_unit<MB, ST, kN, false>(d, off, u, lane, sc, s_mu, s_vu);
+        }
     }
 }
 
@@ -1147,8 +1156,9 @@ hipError_t launch_adamw_step(const DevTensor *tensors, const int32_t *chunk_star
                              int states, hipStream_t st)
 {
     if (total_chunks <= 0) return hipSuccess;
-    // Consecutive chunks per wavefront; FLASHOPT_CHUNKS_PER_WAVE tunes it.
-    int32_t run = 4;
+    // Consecutive chunks per wavefront (2 measured best on the 8.0B list for
+    // both master widths); FLASHOPT_CHUNKS_PER_WAVE overrides it.
+    int32_t run = 2;
     if (const char *env = getenv("FLASHOPT_CHUNKS_PER_WAVE")) {
         const int v = atoi(env);
         if (v >= 1 && v <= 1024) run = v;
