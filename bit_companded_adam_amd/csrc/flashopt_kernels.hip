@@ -63,23 +63,40 @@ __device__ __forceinline__ float group_divisor(uint32_t s)
     return (s & 0x7FFFu) ? f16_value(s) : 1.0f;
 }
 
-// Maximum over aligned groups of G lanes (G = 2, 4 or 8) with DPP:
-// quad_perm [1, 0, 3, 2] (lane ^ 1), quad_perm [2, 3, 0, 1] (lane ^ 2),
-// row_half_mirror (the other quad of each 8 lanes).  Every lane of the
-// wavefront must be active.
+// Maximum over aligned groups of G lanes (G = 2, 4 or 8): v_max_f32 with a
+// DPP source, quad_perm [1, 0, 3, 2] (lane ^ 1), quad_perm [2, 3, 0, 1]
+// (lane ^ 2), row_half_mirror (the other quad of each 8 lanes).  The s_nop
+// gives the two wait states a DPP read needs after a VALU write of its
+// source.  v_max_f32 returns the number when one operand is a quiet NaN
+// (IEEE maxNum).  Every lane of the wavefront must be active.
+__device__ __forceinline__ float max_dpp_x1(float x)
+{
+    float r;
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+        : "=v"(r) : "v"(x));
+    return r;
+}
+__device__ __forceinline__ float max_dpp_x2(float x)
+{
+    float r;
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+        : "=v"(r) : "v"(x));
+    return r;
+}
+__device__ __forceinline__ float max_dpp_mirror8(float x)
+{
+    float r;
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0xf"
+        : "=v"(r) : "v"(x));
+    return r;
+}
+
 template <int G>
 __device__ __forceinline__ float group_max(float x)
 {
-    int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false);
-    x = fmaxf(x, __int_as_float(y));
-    if (G >= 4) {
-        y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false);
-        x = fmaxf(x, __int_as_float(y));
-    }
-    if (G >= 8) {
-        y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false);
-        x = fmaxf(x, __int_as_float(y));
-    }
+    x = max_dpp_x1(x);
+    if (G >= 4) x = max_dpp_x2(x);
+    if (G >= 8) x = max_dpp_mirror8(x);
     return x;
 }
 
@@ -444,7 +461,7 @@ __device__ __forceinline__ void split_pack_exact(const float (&x)[N], uint32_t (
     }
 }
 
-// Signed codes of N group quotients with the biased rounding of
+// Signed codes of N group quotients with the magic-number rounding of
 // flashopt_math.h (finite inputs only; callers send lanes holding NaN or
 // infinite values to encode).
 template <bool SOFTSIGN, int N>
@@ -458,10 +475,10 @@ __device__ __forceinline__ void encode_s8_finite(const float (&a)[N], const Grou
         for (int i = 0; i < 4; ++i) {
             float y = math::div_by_recip(a[4 * k + i], gd.d, gd.r);
             if (SOFTSIGN) y = math::softsign(y);
-            b[i] = math::biased_code_s8(y * 127.0f);
+            b[i] = math::code_s8_magic(y * 127.0f);
         }
         out[k] = pack_bytes(static_cast<int32_t>(b[0]), static_cast<int32_t>(b[1]),
-                            static_cast<int32_t>(b[2]), static_cast<int32_t>(b[3])) ^ 0x80808080u;
+                            static_cast<int32_t>(b[2]), static_cast<int32_t>(b[3]));
     }
 }
 
@@ -702,7 +719,7 @@ constexpr int unit_elems(int mb, int st) { return st == kStatesFp32 ? 4 : 8; }
 template <int MB, int ST, int N>
 struct UnitIn {
     uint32_t pw[N / 2], gw[N / 2];
-    uint32_t rw[rho_words(MB, N)];
+    uint32_t rw[rho_words(MB, N)];   // rho words, each value's sign bit flipped
     uint32_t mw[N / 4], vw[N / 4];   // codes (quantized states)
     uint32_t mf[N], vf[N];           // fp32 states, bit patterns
     uint32_t smb, svb;               // fp16 scale bits of the unit's group
@@ -710,62 +727,114 @@ struct UnitIn {
 
 // First element of unit u of a lane, relative to the chunk.
 template <int N>
-__device__ __forceinline__ int unit_first(int u, int lane)
+__device__ __forceinline__ uint32_t unit_first(int u, int lane)
 {
-    return 64 * N * u + N * lane;
+    return static_cast<uint32_t>(64 * N * u + N * lane);
 }
 
-// Elements of the unit that exist: N, fewer at a ragged end, or 0.
+// Stream pointers at the start of one chunk, uniform across the wavefront
+// (scalar registers), so that unit accesses take a scalar base plus a 32-bit
+// lane offset; rem = elements of the chunk that exist, capped at 1024.
+struct ChunkPtrs {
+    uint16_t *param;
+    const uint16_t *grad;
+    uint8_t *rho8;
+    uint16_t *rho16;
+    uint8_t *mc, *vc;
+    uint32_t *mf, *vf;
+    uint16_t *ms, *vs;
+    int rem;
+};
+
+__device__ __forceinline__ ChunkPtrs chunk_ptrs(const DevTensor &d, int64_t off)
+{
+    ChunkPtrs c;
+    c.param = d.param + off;
+    c.grad = d.grad + off;
+    c.rho8 = static_cast<uint8_t *>(d.rho) + off;
+    c.rho16 = static_cast<uint16_t *>(d.rho) + off;
+    c.mc = reinterpret_cast<uint8_t *>(d.m_codes) + off;
+    c.vc = d.v_codes + off;
+    c.mf = reinterpret_cast<uint32_t *>(d.m_codes) + off;
+    c.vf = reinterpret_cast<uint32_t *>(d.v_codes) + off;
+    c.ms = d.m_scales + off / kGroup;
+    c.vs = d.v_scales + off / kGroup;
+    const int64_t rem = d.numel - off;
+    c.rem = rem < kChunkElems ? static_cast<int>(rem) : kChunkElems;
+    return c;
+}
+
+// Elements of the unit at chunk offset r that exist: N, fewer at a ragged
+// end, or 0.
 template <int N>
-__device__ __forceinline__ int unit_count(int64_t numel, int64_t e)
+__device__ __forceinline__ int unit_count(const ChunkPtrs &c, uint32_t r)
 {
-    const int64_t rem = numel - e;
-    return rem >= N ? N : (rem > 0 ? static_cast<int>(rem) : 0);
+    const int rem = c.rem - static_cast<int>(r);
+    return rem >= N ? N : (rem > 0 ? rem : 0);
 }
 
-// Loads of one unit of every stream.  FULL: straight-line streaming loads;
-// otherwise element-masked loads with zeros for missing elements (and zero
-// scales for a unit with none).
+// Loads of one unit of every stream (the unit at chunk offset r).  FULL:
+// straight-line streaming loads; otherwise element-masked loads with zeros
+// for missing elements (and zero scales for a unit with none).
 template <int MB, int ST, int N, bool FULL>
-__device__ __forceinline__ void load_unit(const DevTensor &d, int64_t e, int cnt,
+__device__ __forceinline__ void load_unit(const ChunkPtrs &c, uint32_t r, int cnt,
                                           UnitIn<MB, ST, N> &in)
 {
-    const uint8_t *const rp = static_cast<const uint8_t *>(d.rho);
-    const uint32_t *const mfp = reinterpret_cast<const uint32_t *>(d.m_codes);
-    const uint32_t *const vfp = reinterpret_cast<const uint32_t *>(d.v_codes);
     in.smb = 0u;
     in.svb = 0u;
     if (FULL) {
-        ld_words<2 * N>(d.param + e, in.pw);
-        ld_words<2 * N>(d.grad + e, in.gw);
-        if constexpr (MB == 24) ld_words<N>(rp + e, in.rw);
-        if constexpr (MB == 32) ld_words<2 * N>(rp + 2 * e, in.rw);
+        ld_words<2 * N>(c.param + r, in.pw);
+        ld_words<2 * N>(c.grad + r, in.gw);
+        if constexpr (MB == 24) ld_words<N>(c.rho8 + r, in.rw);
+        if constexpr (MB == 32) ld_words<2 * N>(c.rho16 + r, in.rw);
         if constexpr (ST == kStatesFp32) {
-            ld_words<4 * N>(mfp + e, in.mf);
-            ld_words<4 * N>(vfp + e, in.vf);
+            ld_words<4 * N>(c.mf + r, in.mf);
+            ld_words<4 * N>(c.vf + r, in.vf);
         } else {
-            ld_words<N>(d.m_codes + e, in.mw);
-            ld_words<N>(d.v_codes + e, in.vw);
-            in.smb = ld_u16(d.m_scales + e / kGroup);
-            in.svb = ld_u16(d.v_scales + e / kGroup);
+            ld_words<N>(c.mc + r, in.mw);
+            ld_words<N>(c.vc + r, in.vw);
+            in.smb = ld_u16(c.ms + r / kGroup);
+            in.svb = ld_u16(c.vs + r / kGroup);
         }
     } else {
-        ld_elems<2, N>(d.param + e, cnt, in.pw);
-        ld_elems<2, N>(d.grad + e, cnt, in.gw);
-        if constexpr (MB == 24) ld_elems<1, N>(rp + e, cnt, in.rw);
-        if constexpr (MB == 32) ld_elems<2, N>(rp + 2 * e, cnt, in.rw);
+        ld_elems<2, N>(c.param + r, cnt, in.pw);
+        ld_elems<2, N>(c.grad + r, cnt, in.gw);
+        if constexpr (MB == 24) ld_elems<1, N>(c.rho8 + r, cnt, in.rw);
+        if constexpr (MB == 32) ld_elems<2, N>(c.rho16 + r, cnt, in.rw);
         if constexpr (ST == kStatesFp32) {
-            ld_elems<4, N>(mfp + e, cnt, in.mf);
-            ld_elems<4, N>(vfp + e, cnt, in.vf);
+            ld_elems<4, N>(c.mf + r, cnt, in.mf);
+            ld_elems<4, N>(c.vf + r, cnt, in.vf);
         } else {
-            ld_elems<1, N>(d.m_codes + e, cnt, in.mw);
-            ld_elems<1, N>(d.v_codes + e, cnt, in.vw);
+            ld_elems<1, N>(c.mc + r, cnt, in.mw);
+            ld_elems<1, N>(c.vc + r, cnt, in.vw);
             if (cnt > 0) {
-                in.smb = ld_u16(d.m_scales + e / kGroup);
-                in.svb = ld_u16(d.v_scales + e / kGroup);
+                in.smb = ld_u16(c.ms + r / kGroup);
+                in.svb = ld_u16(c.vs + r / kGroup);
             }
         }
     }
+    // offset-binary rho for reconstruct_perm
+#pragma unroll
+    for (int i = 0; i < rho_words(MB, N); ++i) in.rw[i] ^= (MB == 32 ? 0x80008000u : 0x80808080u);
+}
+
+// Master pattern of element j, (theta' << 16) + rho * 2^(16 - w), from the
+// bf16 words and the offset-binary rho words (rho + 2^(w-1) as an unsigned
+// field): one v_perm places theta' in the upper half and the rho field
+// below it (24-bit: bits 8-15, low byte zero; 32-bit: bits 0-15), which is
+// the pattern plus 2^15; the subtraction removes that in wrapping integer
+// arithmetic.
+template <int MB, int W, int R>
+__device__ __forceinline__ float reconstruct_perm(const uint32_t (&pw)[W], const uint32_t (&rw)[R],
+                                                  int j)
+{
+    const uint32_t hi = 4u + 2u * static_cast<uint32_t>(j & 1);   // theta' bytes in S0
+    uint32_t sel;
+    if constexpr (MB == 24) sel = 0x0Cu | (static_cast<uint32_t>(j & 3) << 8);
+    else sel = (2u * static_cast<uint32_t>(j & 1)) | ((2u * static_cast<uint32_t>(j & 1) + 1u) << 8);
+    sel |= (hi << 16) | ((hi + 1u) << 24);
+    const uint32_t word = MB == 24 ? rw[j >> 2] : rw[j >> 1];
+    return __uint_as_float(__builtin_amdgcn_perm(pw[j >> 1], word, sel) - 0x8000u);
 }
 
 // Element j of a unit: the master theta (reconstructed, or the bf16 value
@@ -777,15 +846,8 @@ __device__ __forceinline__ void element_moments(const UnitIn<MB, ST, N> &in, int
                                                 const float *s_vu, float ms, float vs,
                                                 float &theta, float &m, float &v)
 {
-    const uint32_t hs = (j & 1) ? (in.pw[j >> 1] & 0xFFFF0000u) : (in.pw[j >> 1] << 16);
-    if constexpr (MB == 0) {
-        theta = __uint_as_float(hs);
-    } else {
-        int32_t r;
-        if constexpr (MB == 32) r = shalf(in.rw, j);
-        else r = sbyte(in.rw, j);
-        theta = reconstruct_elem<MB>(hs, r);
-    }
+    if constexpr (MB == 0) theta = (j & 1) ? bf16_hi(in.pw[j >> 1]) : bf16_lo(in.pw[j >> 1]);
+    else theta = reconstruct_perm<MB>(in.pw, in.rw, j);
     const float g = (j & 1) ? bf16_hi(in.gw[j >> 1]) : bf16_lo(in.gw[j >> 1]);
     float m0, v0;
     if constexpr (ST == kStatesFp32) {
@@ -812,7 +874,7 @@ __device__ __forceinline__ void element_moments(const UnitIn<MB, ST, N> &in, int
 // routines.  The variance codes, fp32 moments and the group scales do not
 // depend on these paths and are produced by the caller.
 template <int MB, int ST, int N>
-__device__ __forceinline__ void unit_exact(const DevTensor &d, int64_t e, int cnt,
+__device__ __forceinline__ void unit_exact(const ChunkPtrs &c, uint32_t r, int cnt,
                                            const StepScalars &sc, const float *s_mu,
                                            const float *s_vu, const GroupDiv &gdm,
                                            uint32_t (&mo)[N / 4], uint32_t (&po)[N / 2],
@@ -820,11 +882,11 @@ __device__ __forceinline__ void unit_exact(const DevTensor &d, int64_t e, int cn
 {
     constexpr unsigned kMSpec =
         ST == kStatesCompanded ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
-    // an opaque copy of the element index keeps the compiler from reusing the
+    // an opaque copy of the unit offset keeps the compiler from reusing the
     // common path's loads, whose values would then stay live up to here
-    asm volatile("" : "+v"(e));
+    asm volatile("" : "+v"(r));
     UnitIn<MB, ST, N> in;
-    load_unit<MB, ST, N, false>(d, e, cnt, in);
+    load_unit<MB, ST, N, false>(c, r, cnt, in);
     const float ms = f16_value(in.smb);
     const float vs = f16_value(in.svb);
     float m1[N], th1[N];
@@ -849,19 +911,19 @@ __device__ __forceinline__ void unit_exact(const DevTensor &d, int64_t e, int cn
 // FULL units use straight-line streaming accesses; at the ragged end of a
 // tensor accesses are masked per element and groups padded with zeros.
 template <int MB, int ST, int N, bool FULL>
-__device__ __forceinline__ void step_unit(const DevTensor &d, int64_t off, int u, int lane,
+__device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
                                           const StepScalars &sc, const float *s_mu,
                                           const float *s_vu)
 {
     constexpr bool kQuant = ST != kStatesFp32;
     constexpr bool kComp = ST == kStatesCompanded;
     constexpr unsigned kVSpec = kComp ? FLASHOPT_SPEC_VARIANCE : FLASHOPT_SPEC_VARIANCE_LINEAR;
-    const int64_t e = off + unit_first<N>(u, lane);
-    const int cnt = FULL ? N : unit_count<N>(d.numel, e);
+    const uint32_t r = unit_first<N>(u, lane);
+    const int cnt = FULL ? N : unit_count<N>(c, r);
 
     // ---- loads (missing elements read as zero)
     UnitIn<MB, ST, N> in;
-    load_unit<MB, ST, N, FULL>(d, e, cnt, in);
+    load_unit<MB, ST, N, FULL>(c, r, cnt, in);
     const float ms = f16_value(in.smb);
     const float vs = f16_value(in.svb);
 
@@ -947,41 +1009,40 @@ __device__ __forceinline__ void step_unit(const DevTensor &d, int64_t off, int u
         // is recomputed from its inputs in memory with the generic
         // operations; nothing has been stored yet, and the group scales
         // above are already exact
-        unit_exact<MB, ST, N>(d, e, cnt, sc, s_mu, s_vu, gdm, mo, po, ro);
+        unit_exact<MB, ST, N>(c, r, cnt, sc, s_mu, s_vu, gdm, mo, po, ro);
     }
 
     // ---- stores
-    uint8_t *const rp = static_cast<uint8_t *>(d.rho);
     uint32_t mb[N], vb[N];
 #pragma unroll
     for (int j = 0; j < N; ++j) { mb[j] = __float_as_uint(m1[j]); vb[j] = __float_as_uint(v1[j]); }
     if (FULL) {
-        st_words<2 * N>(d.param + e, po);
-        if constexpr (MB == 24) st_words<N>(rp + e, ro);
-        if constexpr (MB == 32) st_words<2 * N>(rp + 2 * e, ro);
+        st_words<2 * N>(c.param + r, po);
+        if constexpr (MB == 24) st_words<N>(c.rho8 + r, ro);
+        if constexpr (MB == 32) st_words<2 * N>(c.rho16 + r, ro);
         if constexpr (kQuant) {
-            st_words<N>(d.m_codes + e, mo);
-            st_words<N>(d.v_codes + e, vo);
+            st_words<N>(c.mc + r, mo);
+            st_words<N>(c.vc + r, vo);
         } else {
-            st_words<4 * N>(reinterpret_cast<uint32_t *>(d.m_codes) + e, mb);
-            st_words<4 * N>(reinterpret_cast<uint32_t *>(d.v_codes) + e, vb);
+            st_words<4 * N>(c.mf + r, mb);
+            st_words<4 * N>(c.vf + r, vb);
         }
     } else {
-        st_elems<2, N>(d.param + e, cnt, po);
-        if constexpr (MB == 24) st_elems<1, N>(rp + e, cnt, ro);
-        if constexpr (MB == 32) st_elems<2, N>(rp + 2 * e, cnt, ro);
+        st_elems<2, N>(c.param + r, cnt, po);
+        if constexpr (MB == 24) st_elems<1, N>(c.rho8 + r, cnt, ro);
+        if constexpr (MB == 32) st_elems<2, N>(c.rho16 + r, cnt, ro);
         if constexpr (kQuant) {
-            st_elems<1, N>(d.m_codes + e, cnt, mo);
-            st_elems<1, N>(d.v_codes + e, cnt, vo);
+            st_elems<1, N>(c.mc + r, cnt, mo);
+            st_elems<1, N>(c.vc + r, cnt, vo);
         } else {
-            st_elems<4, N>(reinterpret_cast<uint32_t *>(d.m_codes) + e, cnt, mb);
-            st_elems<4, N>(reinterpret_cast<uint32_t *>(d.v_codes) + e, cnt, vb);
+            st_elems<4, N>(c.mf + r, cnt, mb);
+            st_elems<4, N>(c.vf + r, cnt, vb);
         }
     }
     // the group's first lane writes its scales
     if (kQuant && lane % (32 / N) == 0 && cnt > 0) {
-        st_u16(d.m_scales + e / kGroup, static_cast<uint16_t>(sm_out));
-        st_u16(d.v_scales + e / kGroup, static_cast<uint16_t>(sv_out));
+        st_u16(c.ms + r / kGroup, static_cast<uint16_t>(sm_out));
+        st_u16(c.vs + r / kGroup, static_cast<uint16_t>(sv_out));
     }
 }
 
@@ -1028,12 +1089,13 @@ adamw_step_kernel(const DevTensor *__restrict__ tensors, const int32_t *__restri
         t = __builtin_amdgcn_readfirstlane(t);
         const DevTensor d = tensors[t];
         const int64_t off = static_cast<int64_t>(c - chunk_start[t]) * kChunkElems;
-        if (off + kChunkElems <= d.numel) {
+        const ChunkPtrs cp = chunk_ptrs(d, off);
+        if (cp.rem == kChunkElems) {
 #pragma unroll
-            for (int u = 0; u < kUnits; ++u) step_unit<MB, ST, kN, true>(d, off, u, lane, sc, s_mu, s_vu);
+            for (int u = 0; u < kUnits; ++u) step_unit<MB, ST, kN, true>(cp, u, lane, sc, s_mu, s_vu);
         } else {
 #pragma unroll
-            for (int u = 0; u < kUnits; ++u) step_unit<MB, ST, kN, false>(d, off, u, lane, sc, s_mu, s_vu);
+            for (int u = 0; u < kUnits; ++u) step_unit<MB, ST, kN, false>(cp, u, lane, sc, s_mu, s_vu);
         }
     }
 }

@@ -13,8 +13,8 @@
 //                  NaN -> 0);
 //   div_markstein  2^32 random pairs of its stated domain plus every divisor
 //                  significand at the domain's edges;
-//   biased_code_s8 every fp32 p (low byte == clamp(rint(p), -127, 127) + 128
-//                  for non-NaN p).
+//   code_s8_magic  every fp32 p (low byte == clamp(rint(p), -127, 127) as a
+//                  two's-complement byte, for non-NaN p).
 // Only fma, mul, add, v_rcp_f32 / v_rsq_f32 and integer ops are used, so the
 // results do not depend on the FP mode beyond round-to-nearest-even with
 // fp32 denormals kept.
@@ -78,15 +78,16 @@ __device__ __forceinline__ float div_markstein(float num, float den, float r)
     return __builtin_fmaf(-e, r, q0);
 }
 
-// Signed 8-bit code of p = y * 127 in its low byte, biased by +128: clamp to
-// [-127, 127] (v_med3_f32), then adding 1.5 * 2^23 + 128 rounds to an integer
-// with ties to even (the sum lies in [2^23, 2^24), where the fp32 spacing is
-// 1) and leaves rint(p) + 128 in the low byte of the pattern.  NaN inputs are
-// the caller's to route elsewhere.
-__device__ __forceinline__ uint32_t biased_code_s8(float p)
+// Signed 8-bit code of p = y * 127 in the low byte of the result: clamp to
+// [-127, 127] (v_med3_f32), then adding 1.5 * 2^23 rounds to an integer with
+// ties to even (the sum lies in [2^23, 2^24), where the fp32 spacing is 1).
+// The pattern of 1.5 * 2^23 has a zero low byte, so the sum's low byte is
+// rint(p) modulo 256: the code's two's-complement byte.  NaN inputs are the
+// caller's to route elsewhere.
+__device__ __forceinline__ uint32_t code_s8_magic(float p)
 {
     const float c = __builtin_amdgcn_fmed3f(p, -127.0f, 127.0f);
-    return __float_as_uint(c + 12583040.0f);
+    return __float_as_uint(c + 12582912.0f);
 }
 
 // Correctly rounded sqrt(x) for 0 <= x < 2^64.  The input is first scaled by

@@ -139,15 +139,15 @@ __global__ void k_div_markstein(unsigned long long *bad)
     flush(bad, c);
 }
 
-__global__ void k_biased_code(unsigned long long *bad)
+__global__ void k_magic_code(unsigned long long *bad)
 {
     unsigned long long c = 0;
     for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (1ull << 32);
          i += (uint64_t)gridDim.x * blockDim.x) {
         const float p = __uint_as_float((uint32_t)i);
         if (p != p) continue;
-        const int want = (int)fminf(fmaxf(rintf(p), -127.0f), 127.0f) + 128;
-        c += (int)(biased_code_s8(p) & 0xFFu) != want;
+        const int want = (int)fminf(fmaxf(rintf(p), -127.0f), 127.0f);
+        c += (int)(int8_t)(code_s8_magic(p) & 0xFFu) != want;
     }
     flush(bad, c);
 }
@@ -174,5 +174,5 @@ long long fastmath_check_div_by_recip(void) { return run(k_div_by_recip, 65536);
 long long fastmath_check_softsign(void) { return run(k_softsign, 65536); }
 long long fastmath_check_cvt_pk_u8(void) { return run(k_cvt_pk_u8, 65536); }
 long long fastmath_check_div_markstein(void) { return run(k_div_markstein, 65536); }
-long long fastmath_check_biased_code(void) { return run(k_biased_code, 65536); }
+long long fastmath_check_magic_code(void) { return run(k_magic_code, 65536); }
 }

@@ -4,8 +4,8 @@ each sweep compares against the compiler's correctly rounded operation on the
 same device and must find no mismatch.  Sweeps: sqrt over every x in
 [0, 2^64); reciprocal over every significand (three exponents) and every fp16
 value; division by an fp16 scale over every divisor x dividend significand
-pair (2^33); softsign over every |y| <= 1.5; v_cvt_pk_u8_f32 and the biased
-int8 code rounding over all 2^32 patterns; the update division over 2^32
+pair (2^33); softsign over every |y| <= 1.5; v_cvt_pk_u8_f32 and the
+magic-number int8 code rounding over all 2^32 patterns; the update division over 2^32
 random pairs of its stated domain and every divisor significand at the
 domain's edges."""
 import ctypes
@@ -18,7 +18,7 @@ from tests._gpu import require_gpu
 pytestmark = pytest.mark.gpu
 
 LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hip", "libfastmath_check.so")
-CHECKS = ["sqrt", "recip", "div_by_recip", "softsign", "cvt_pk_u8", "div_markstein", "biased_code"]
+CHECKS = ["sqrt", "recip", "div_by_recip", "softsign", "cvt_pk_u8", "div_markstein", "magic_code"]
 
 
 @pytest.fixture(scope="module")
