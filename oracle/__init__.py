@@ -1,4 +1,4 @@
-"""Oracle for the FlashAdamW step: ctypes wrapper around ``liboracle.so``.
+"""Oracle for the FlashAdamW and FlashSGD steps: ctypes wrapper around ``liboracle.so``.
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()`` and
 the CPU-baseline leg of ``bench.py`` may import this package.  The product
@@ -8,6 +8,8 @@ The C source (``flashopt_oracle.c``) follows the method pages:
 ``code/flashsim/quantization.py`` (quantize/dequantize, Alg. 2-3),
 ``code/flashsim/flash_adamw_sim.py`` (FlashAdamWSim.step, Alg. 4) and
 ``code/gpu/equivalence.py`` (the bf16 cast fed to the correction bits).
+FlashSGD appears on the pages only in bytes_per_param; its update is read as
+torch.optim.SGD with momentum (R5 in the C source).
 All arrays here are numpy arrays on the host.
 """
 from __future__ import annotations
@@ -65,6 +67,22 @@ def hparams(lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0, step=1,
                    int(quantize_states), int(literal_order))
 
 
+class SgdHParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("momentum", ctypes.c_double),
+                ("dampening", ctypes.c_double), ("weight_decay", ctypes.c_double),
+                ("step", ctypes.c_int64), ("master_bits", ctypes.c_int),
+                ("companded", ctypes.c_int), ("quantize_states", ctypes.c_int),
+                ("nesterov", ctypes.c_int)]
+
+
+def sgd_hparams(lr=1e-2, momentum=0.9, dampening=0.0, weight_decay=0.0, step=1,
+                master_bits=24, companded=True, quantize_states=True,
+                nesterov=False) -> SgdHParams:
+    return SgdHParams(lr, momentum, dampening, weight_decay, step,
+                      0 if master_bits is None else master_bits, int(companded),
+                      int(quantize_states), int(nesterov))
+
+
 _lib = None
 
 
@@ -93,6 +111,9 @@ def lib():
                                         ctypes.POINTER(HParams)]
         L.oracle_adamw_step_list.argtypes = [ctypes.POINTER(_Tensor), ctypes.c_int,
                                              ctypes.POINTER(HParams), ctypes.c_int]
+        L.oracle_sgd_update.argtypes = [vp, vp, vp, i64, ctypes.POINTER(SgdHParams)]
+        L.oracle_sgd_update.restype = None
+        L.oracle_sgd_step.argtypes = [vp, vp, vp, vp, vp, i64, ctypes.POINTER(SgdHParams)]
         _lib = L
     return _lib
 
@@ -217,6 +238,26 @@ def adamw_step(state: State, grad_bits: np.ndarray, hp: HParams) -> State:
                                 _p(state.m_codes), _p(state.m_scales),
                                 _p(state.v_codes), _p(state.v_scales), n,
                                 ctypes.byref(hp)))
+    return state
+
+
+def sgd_update(theta, buf, g, hp: SgdHParams):
+    """SGD-with-momentum body on fp32 arrays; returns new (theta, buf)."""
+    theta = np.array(theta, dtype=np.float32, copy=True).reshape(-1)
+    buf = np.array(buf, dtype=np.float32, copy=True).reshape(-1)
+    g = np.ascontiguousarray(g, dtype=np.float32).reshape(-1)
+    lib().oracle_sgd_update(_p(theta), _p(buf), _p(g), theta.size, ctypes.byref(hp))
+    return theta, buf
+
+
+def sgd_step(state: State, grad_bits: np.ndarray, hp: SgdHParams) -> State:
+    """One FlashSGD step on a host state (in place; the momentum buffer is
+    state.m_codes / m_scales, v is unused); returns the state."""
+    grad_bits = np.ascontiguousarray(grad_bits, dtype=np.uint16).reshape(-1)
+    n = state.param.size
+    assert grad_bits.size == n
+    _ck(lib().oracle_sgd_step(_p(state.param), _p(grad_bits), _p(state.rho),
+                              _p(state.m_codes), _p(state.m_scales), n, ctypes.byref(hp)))
     return state
 
 

@@ -1,6 +1,6 @@
 /*
- * Oracle for the FlashAdamW optimizer step -- plain CPU C, one element at a
- * time, in the pages' order.  TEST INFRASTRUCTURE ONLY (see the header): the
+ * Oracle for the FlashAdamW and FlashSGD optimizer steps -- plain CPU C, one
+ * element at a time, in the pages' order.  TEST INFRASTRUCTURE ONLY (see the header): the
  * product library neither links nor includes this file.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fopenmp -fPIC -shared
@@ -384,6 +384,80 @@ int oracle_adamw_step(uint16_t *param, const uint16_t *grad, void *rho,
     else for (int64_t i = 0; i < n; ++i) param[i] = bf16_rne(theta[i]);
 
     free(theta); free(m); free(v); free(g);
+    return 0;
+}
+
+/* ------------------------------------------------------------- FlashSGD */
+
+/* FlashSGD appears on the pages only through its memory accounting
+ * ([SIM bytes_per_param()] "flash_sgd": bf16 master + rho + grad + one
+ * group-32 quantized state of 1 + 2/32 bytes).  R5: its update is read as
+ * torch.optim.SGD with momentum (the optimizer the page's "sgd_ref" row
+ * accounts for), one fp32 operation per step, in torch's order:
+ *   d   <- g + wd theta                         (coupled weight decay, if wd)
+ *   buf <- d                                    at step 1,
+ *   buf <- momentum buf + (1 - dampening) d     afterwards
+ *   d   <- d + momentum buf  (nesterov)  or  d <- buf
+ *   theta <- theta - lr d
+ * and the momentum buffer is stored with the momentum spec of the codec
+ * (the linear spec when !companded), the master split as for FlashAdamW. */
+void oracle_sgd_update(float *theta, float *buf, const float *g, int64_t n,
+                       const oracle_sgd_hparams *h)
+{
+    const float lr = (float)h->lr, mu = (float)h->momentum;
+    const float wd = (float)h->weight_decay, cd = (float)(1.0 - h->dampening);
+    for (int64_t i = 0; i < n; ++i) {
+        float d = g[i];
+        if (h->weight_decay != 0.0) {
+            float decay = wd * theta[i];
+            d = d + decay;
+        }
+        float b;
+        if (h->step == 1) {
+            b = d;
+        } else {
+            float kept = mu * buf[i];
+            float added = cd * d;
+            b = kept + added;
+        }
+        float dir;
+        if (h->nesterov) {
+            float look = mu * b;
+            dir = d + look;
+        } else {
+            dir = b;
+        }
+        float upd = lr * dir;
+        theta[i] = theta[i] - upd;
+        buf[i] = b;
+    }
+}
+
+int oracle_sgd_step(uint16_t *param, const uint16_t *grad, void *rho,
+                    void *m_codes, uint16_t *m_scales, int64_t n,
+                    const oracle_sgd_hparams *h)
+{
+    if (n < 0 || h == NULL || h->step < 1) return -1;
+    if (h->master_bits != 0 && h->master_bits != 24 && h->master_bits != 32) return -1;
+    if (n == 0) return 0;
+    size_t bytes = (size_t)n * sizeof(float);
+    float *theta = (float *)malloc(bytes), *m = (float *)malloc(bytes), *g = (float *)malloc(bytes);
+    if (!theta || !m || !g) { free(theta); free(m); free(g); return -1; }
+
+    for (int64_t i = 0; i < n; ++i) g[i] = bf16_to_f32(grad[i]);
+    if (h->quantize_states) oracle_dequantize(m_codes, m_scales, n, momentum_spec(h->companded), m);
+    else memcpy(m, m_codes, bytes);
+    if (h->master_bits) oracle_reconstruct(param, rho, n, h->master_bits, theta);
+    else for (int64_t i = 0; i < n; ++i) theta[i] = bf16_to_f32(param[i]);
+
+    oracle_sgd_update(theta, m, g, n, h);
+
+    if (h->quantize_states) oracle_quantize(m, n, momentum_spec(h->companded), m_codes, m_scales);
+    else memcpy(m_codes, m, bytes);
+    if (h->master_bits) oracle_split(theta, n, h->master_bits, param, rho);
+    else for (int64_t i = 0; i < n; ++i) param[i] = bf16_rne(theta[i]);
+
+    free(theta); free(m); free(g);
     return 0;
 }
 

@@ -97,6 +97,28 @@ int oracle_adamw_step(uint16_t *param, const uint16_t *grad, void *rho,
                       void *v_codes, uint16_t *v_scales,
                       int64_t n, const oracle_hparams *h);
 
+/* FlashSGD hyper-parameters (R5 in flashopt_oracle.c: torch.optim.SGD with
+ * momentum, the momentum buffer stored with the momentum spec). */
+typedef struct {
+    double lr, momentum, dampening, weight_decay;
+    int64_t step;          /* t >= 1; step 1 sets the buffer to the gradient */
+    int master_bits;       /* 24 | 32 | 0 */
+    int companded;         /* 1: softsign momentum spec;  0: linear         */
+    int quantize_states;   /* 1: int8 + fp16 scales;  0: fp32 buffer        */
+    int nesterov;
+} oracle_sgd_hparams;
+
+/* The SGD-with-momentum update alone on fp32 arrays, in place. */
+void oracle_sgd_update(float *theta, float *buf, const float *g, int64_t n,
+                       const oracle_sgd_hparams *h);
+
+/* One FlashSGD step on one tensor, in place (layouts as oracle_adamw_step,
+ * with the momentum buffer in m_codes / m_scales).  Returns 0, or -1 on a
+ * bad argument. */
+int oracle_sgd_step(uint16_t *param, const uint16_t *grad, void *rho,
+                    void *m_codes, uint16_t *m_scales, int64_t n,
+                    const oracle_sgd_hparams *h);
+
 /* The same step over a list of tensors, split into 32-aligned slices that
  * run on `threads` OpenMP threads (<= 0: the runtime default).  Used to time
  * the oracle; the arithmetic is oracle_adamw_step()'s.  Returns the thread
