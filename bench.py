@@ -11,7 +11,8 @@ N(0, 1e-3^2) times a per-tensor lognormal factor, reused by every step).
 Other configurations (reported beside the default, not as its value):
 --workload decoder-1b-list (199 tensors, 1,195,991,040 params), --master-bits
 32 | 0 (0: no split, the page's master_weight_bits=None), --linear (linear
-codec ablation), --fp32-states (quantize_states=False).
+codec ablation), --fp32-states (quantize_states=False), --optimizer sgd (the
+FlashSGD step: lr 1e-2, momentum 0.9, weight decay 0.01).
 
 Prints one JSON line: Gparam/s over the K timed steps, the roofline of the
 step kernel (algorithmic bytes per param of the configuration against
@@ -42,13 +43,13 @@ KERNEL_SRC = os.path.join(ROOT, "bit_companded_adam_amd", "csrc", "flashopt_kern
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "adamw_step_8b_traffic.json")
 
 
-def bytes_per_param(master_bits: int, quantize_states: bool = True) -> float:
+def bytes_per_param(master_bits: int, quantize_states: bool = True, n_states: int = 2) -> float:
     """Algorithmic HBM bytes per parameter per step: read bf16 param 2, bf16
-    grad 2, rho 1|2 (none without a split), m and v 1 byte each plus two fp16
-    scales per 32 (2/32 each), or 4 bytes each as fp32; write all of them
-    except the grad."""
+    grad 2, rho 1|2 (none without a split), each state (m and v for AdamW, the
+    momentum buffer for SGD) 1 byte plus an fp16 scale per 32 (2/32), or 4
+    bytes as fp32; write all of them except the grad."""
     rho = {24: 1, 32: 2, 0: 0}[master_bits]
-    states = (1 + 1 + 2 * 2 / 32) if quantize_states else 8
+    states = n_states * ((1 + 2 / 32) if quantize_states else 4)
     read = 2 + 2 + rho + states
     write = 2 + rho + states
     return read + write
@@ -76,15 +77,19 @@ WORKLOADS = {"decoder-8b-list": W.decoder_8b_shapes, "decoder-1b-list": W.decode
 
 
 def build_workload(master_bits: int, companded: bool, quantize_states: bool = True,
-                   workload: str = "decoder-8b-list"):
+                   workload: str = "decoder-8b-list", optimizer: str = "adamw"):
     shapes = WORKLOADS[workload]()
     params = [W.init_param(W.numel(s), device="cuda", seed=W.PARAM_SEED + i)
               for i, (_, s) in enumerate(shapes)]
     factors = W.grad_factors(len(shapes)).tolist()
     grads = [W.make_grad(W.numel(s), 1, device="cuda", stream_id=i, factor=factors[i])
              for i, (_, s) in enumerate(shapes)]
-    opt = F.FlashAdamW(params, master_bits=master_bits or None, companded=companded,
-                       quantize_states=quantize_states, **W.HP_DEFAULT)
+    if optimizer == "sgd":
+        opt = F.FlashSGD(params, master_bits=master_bits or None, companded=companded,
+                         quantize_states=quantize_states, **W.SGD_DEFAULT)
+    else:
+        opt = F.FlashAdamW(params, master_bits=master_bits or None, companded=companded,
+                           quantize_states=quantize_states, **W.HP_DEFAULT)
     return opt, grads
 
 
@@ -220,6 +225,8 @@ def main():
     ap.add_argument("--linear", action="store_true", help="linear (non-companded) ablation")
     ap.add_argument("--fp32-states", action="store_true",
                     help="unquantized fp32 moments (weight-splitting-only ablation)")
+    ap.add_argument("--optimizer", default="adamw", choices=("adamw", "sgd"),
+                    help="sgd: the FlashSGD step (momentum buffer only)")
     ap.add_argument("--cpu-elems", type=int, default=1 << 27,
                     help="oracle sample size for the CPU baseline (0: skip)")
     ap.add_argument("--cpu-threads", type=int, default=0)
@@ -243,7 +250,7 @@ def main():
 
     mb, comp, qs = args.master_bits, not args.linear, not args.fp32_states
     copy_gbs = None if args.no_copy_ref else copy_reference()
-    opt, grads = build_workload(mb, comp, qs, args.workload)
+    opt, grads = build_workload(mb, comp, qs, args.workload, args.optimizer)
     n = sum(s.param.numel() for s in opt.states)
     n_tensors = len(opt.states)
     print(f"# workload ready: {len(opt.states)} tensors, {n} params, "
@@ -253,7 +260,7 @@ def main():
     env = environment()                     # clocks read right after the timed steps
     ms_step = wall * 1e3 / args.steps
     ms_launch = float(np.mean(per))
-    bpp = bytes_per_param(mb, qs)
+    bpp = bytes_per_param(mb, qs, 1 if args.optimizer == "sgd" else 2)
     alg_bytes = bpp * n
     achieved = alg_bytes / (ms_launch * 1e-3) / 1e9
     print(f"# per-launch ms: mean {ms_launch:.3f} median {np.median(per):.3f} "
@@ -262,11 +269,11 @@ def main():
     torch.cuda.empty_cache()
 
     cpu = None
-    if args.cpu_elems > 0:
+    if args.cpu_elems > 0 and args.optimizer == "adamw":
         cpu = cpu_baseline(mb, args.cpu_elems, args.cpu_threads, args.cpu_seconds, comp, qs)
-    default = (args.workload, mb, comp, qs) == ("decoder-8b-list", 24, True, True)
+    default = (args.workload, mb, comp, qs, args.optimizer) == ("decoder-8b-list", 24, True, True, "adamw")
     name = args.workload + ("" if comp else "-linear") + ("" if qs else "-fp32-states") + \
-        ("-no-split" if mb == 0 else "")
+        ("-no-split" if mb == 0 else "") + ("-flashsgd" if args.optimizer == "sgd" else "")
 
     out = {
         "metric": METRIC,

@@ -17,6 +17,7 @@
 namespace {
 
 using flashopt::DevTensor;
+using flashopt::SgdScalars;
 using flashopt::StepScalars;
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -71,6 +72,89 @@ struct Ring {
 
 std::mutex g_ring_mutex;
 Ring g_rings[kMaxDevices];
+
+// Validation of a step's tensor list, then the chunk table staged through the
+// pinned ring and launch(d_desc, d_chunk_start, total_chunks, stream).  split:
+// rho is used; quant: scales are used; v: the variance streams are used.
+template <typename Launch>
+flashopt_status stage_and_launch(const flashopt_tensor *tensors, int n_tensors, int master_bits,
+                                 bool quant, bool v, void *workspace, size_t ws_bytes,
+                                 void *stream, Launch &&launch)
+{
+    const bool split = master_bits != 0;
+    int64_t total = 0;
+    for (int i = 0; i < n_tensors; ++i) {
+        const flashopt_tensor &t = tensors[i];
+        if (t.numel < 0) return FLASHOPT_EINVAL;
+        if (t.numel == 0) continue;
+        if (!t.param || !t.grad || !t.m_codes) return FLASHOPT_EINVAL;
+        if (v && !t.v_codes) return FLASHOPT_EINVAL;
+        if (split && !t.rho) return FLASHOPT_EINVAL;
+        if (quant && (!t.m_scales || (v && !t.v_scales))) return FLASHOPT_EINVAL;
+        if (!aligned(t.param, 16) || !aligned(t.grad, 16) || !aligned(t.m_codes, 16))
+            return FLASHOPT_EALIGN;
+        if (v && !aligned(t.v_codes, 16)) return FLASHOPT_EALIGN;
+        if (split && !aligned(t.rho, 16)) return FLASHOPT_EALIGN;
+        if (quant && (!aligned(t.m_scales, 2) || (v && !aligned(t.v_scales, 2)))) return FLASHOPT_EALIGN;
+        total += (t.numel + flashopt::kChunkElems - 1) / flashopt::kChunkElems;
+        if (total > INT32_MAX) return FLASHOPT_EINVAL;
+    }
+    if (total == 0) return FLASHOPT_OK;
+    const size_t need = workspace_bytes(n_tensors);
+    if (!workspace || ws_bytes < need) return FLASHOPT_EWORKSPACE;
+    if (!aligned(workspace, 16)) return FLASHOPT_EALIGN;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FLASHOPT_EHIP;
+
+    std::lock_guard<std::mutex> lock(g_ring_mutex);
+    Ring &ring = g_rings[dev];
+    Slot &slot = ring.slot[ring.next];
+    ring.next = (ring.next + 1) % kRingSlots;
+    if (slot.pending) {
+        if (hipEventSynchronize(slot.done) != hipSuccess) return FLASHOPT_EHIP;
+        slot.pending = false;
+    }
+    if (!slot.done && hipEventCreateWithFlags(&slot.done, hipEventDisableTiming) != hipSuccess)
+        return FLASHOPT_EHIP;
+    if (slot.cap < need) {
+        if (slot.host) (void)hipHostFree(slot.host);
+        slot.host = nullptr;
+        slot.cap = 0;
+        if (hipHostMalloc(&slot.host, need, hipHostMallocDefault) != hipSuccess) return FLASHOPT_EHIP;
+        slot.cap = need;
+    }
+
+    // ---- chunk table: descriptors, then chunk starts (prefix sums)
+    DevTensor *desc = static_cast<DevTensor *>(slot.host);
+    int32_t *start = reinterpret_cast<int32_t *>(desc + n_tensors);
+    int32_t acc = 0;
+    for (int i = 0; i < n_tensors; ++i) {
+        const flashopt_tensor &s = tensors[i];
+        DevTensor &d = desc[i];
+        d.param = s.param;
+        d.grad = s.grad;
+        d.rho = s.rho;
+        d.m_codes = s.m_codes;
+        d.m_scales = s.m_scales;
+        d.v_codes = s.v_codes;
+        d.v_scales = s.v_scales;
+        d.numel = s.numel;
+        start[i] = acc;
+        acc += static_cast<int32_t>((s.numel + flashopt::kChunkElems - 1) / flashopt::kChunkElems);
+    }
+    start[n_tensors] = acc;
+
+    if (hipMemcpyAsync(workspace, slot.host, need, hipMemcpyHostToDevice, st) != hipSuccess)
+        return FLASHOPT_EHIP;
+    if (hipEventRecord(slot.done, st) != hipSuccess) return FLASHOPT_EHIP;
+    slot.pending = true;
+
+    const DevTensor *d_desc = static_cast<const DevTensor *>(workspace);
+    const int32_t *d_start = reinterpret_cast<const int32_t *>(d_desc + n_tensors);
+    return hip_status(launch(d_desc, d_start, acc, st));
+}
 
 }  // namespace
 
@@ -143,35 +227,11 @@ flashopt_status flashopt_adamw_step(const flashopt_tensor *tensors, int n_tensor
     if (a->companded != 0 && a->companded != 1) return FLASHOPT_EINVAL;
     if (a->fp32_states != 0 && a->fp32_states != 1) return FLASHOPT_EINVAL;
     if (a->reserved != 0) return FLASHOPT_EINVAL;
-    const bool split = a->master_bits != 0;
-    const bool quant = a->fp32_states == 0;
     if (a->step < 1) return FLASHOPT_EINVAL;
     if (!(a->lr >= 0.0) || !std::isfinite(a->lr)) return FLASHOPT_EINVAL;
     if (!(a->beta1 >= 0.0 && a->beta1 < 1.0) || !(a->beta2 >= 0.0 && a->beta2 < 1.0)) return FLASHOPT_EINVAL;
     if (!(a->eps >= 0.0) || !std::isfinite(a->eps)) return FLASHOPT_EINVAL;
     if (!std::isfinite(a->weight_decay)) return FLASHOPT_EINVAL;
-
-    // ---- tensors and the chunk count
-    int64_t total = 0;
-    for (int i = 0; i < n_tensors; ++i) {
-        const flashopt_tensor &t = tensors[i];
-        if (t.numel < 0) return FLASHOPT_EINVAL;
-        if (t.numel == 0) continue;
-        if (!t.param || !t.grad || !t.m_codes || !t.v_codes) return FLASHOPT_EINVAL;
-        if (split && !t.rho) return FLASHOPT_EINVAL;
-        if (quant && (!t.m_scales || !t.v_scales)) return FLASHOPT_EINVAL;
-        if (!aligned(t.param, 16) || !aligned(t.grad, 16) || !aligned(t.m_codes, 16) ||
-            !aligned(t.v_codes, 16))
-            return FLASHOPT_EALIGN;
-        if (split && !aligned(t.rho, 16)) return FLASHOPT_EALIGN;
-        if (quant && (!aligned(t.m_scales, 2) || !aligned(t.v_scales, 2))) return FLASHOPT_EALIGN;
-        total += (t.numel + flashopt::kChunkElems - 1) / flashopt::kChunkElems;
-        if (total > INT32_MAX) return FLASHOPT_EINVAL;
-    }
-    if (total == 0) return FLASHOPT_OK;
-    const size_t need = workspace_bytes(n_tensors);
-    if (!workspace || ws_bytes < need) return FLASHOPT_EWORKSPACE;
-    if (!aligned(workspace, 16)) return FLASHOPT_EALIGN;
 
     // ---- step scalars: double on the host, rounded once to fp32
     StepScalars sc;
@@ -191,59 +251,55 @@ flashopt_status flashopt_adamw_step(const flashopt_tensor *tensors, int n_tensor
     sc.fast_div = (sc.eps >= 0x1p-100f && sc.k2 <= 0x1p60f) ? 1 : 0;
     sc.num_max = sc.fast_div ? sc.eps * 0x1p100f : 0.0f;
 
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FLASHOPT_EHIP;
-
-    std::lock_guard<std::mutex> lock(g_ring_mutex);
-    Ring &ring = g_rings[dev];
-    Slot &slot = ring.slot[ring.next];
-    ring.next = (ring.next + 1) % kRingSlots;
-    if (slot.pending) {
-        if (hipEventSynchronize(slot.done) != hipSuccess) return FLASHOPT_EHIP;
-        slot.pending = false;
-    }
-    if (!slot.done && hipEventCreateWithFlags(&slot.done, hipEventDisableTiming) != hipSuccess)
-        return FLASHOPT_EHIP;
-    if (slot.cap < need) {
-        if (slot.host) (void)hipHostFree(slot.host);
-        slot.host = nullptr;
-        slot.cap = 0;
-        if (hipHostMalloc(&slot.host, need, hipHostMallocDefault) != hipSuccess) return FLASHOPT_EHIP;
-        slot.cap = need;
-    }
-
-    // ---- chunk table: descriptors, then chunk starts (prefix sums)
-    DevTensor *desc = static_cast<DevTensor *>(slot.host);
-    int32_t *start = reinterpret_cast<int32_t *>(desc + n_tensors);
-    int32_t acc = 0;
-    for (int i = 0; i < n_tensors; ++i) {
-        const flashopt_tensor &s = tensors[i];
-        DevTensor &d = desc[i];
-        d.param = s.param;
-        d.grad = s.grad;
-        d.rho = s.rho;
-        d.m_codes = s.m_codes;
-        d.m_scales = s.m_scales;
-        d.v_codes = s.v_codes;
-        d.v_scales = s.v_scales;
-        d.numel = s.numel;
-        start[i] = acc;
-        acc += static_cast<int32_t>((s.numel + flashopt::kChunkElems - 1) / flashopt::kChunkElems);
-    }
-    start[n_tensors] = acc;
-
-    if (hipMemcpyAsync(workspace, slot.host, need, hipMemcpyHostToDevice, st) != hipSuccess)
-        return FLASHOPT_EHIP;
-    if (hipEventRecord(slot.done, st) != hipSuccess) return FLASHOPT_EHIP;
-    slot.pending = true;
-
-    const DevTensor *d_desc = static_cast<const DevTensor *>(workspace);
-    const int32_t *d_start = reinterpret_cast<const int32_t *>(d_desc + n_tensors);
-    const int states = !quant ? flashopt::kStatesFp32
+    const int states = a->fp32_states ? flashopt::kStatesFp32
                      : (a->companded ? flashopt::kStatesCompanded : flashopt::kStatesLinear);
-    return hip_status(flashopt::launch_adamw_step(d_desc, d_start, n_tensors, acc, sc,
-                                                  a->master_bits, states, st));
+    return stage_and_launch(tensors, n_tensors, a->master_bits, a->fp32_states == 0, true,
+                            workspace, ws_bytes, stream,
+                            [&](const DevTensor *d, const int32_t *cs, int32_t total, hipStream_t st) {
+                                return flashopt::launch_adamw_step(d, cs, n_tensors, total, sc,
+                                                                   a->master_bits, states, st);
+                            });
+}
+
+size_t flashopt_sgd_workspace_bytes(const flashopt_tensor *tensors, int n_tensors)
+{
+    (void)tensors;
+    return workspace_bytes(n_tensors);
+}
+
+flashopt_status flashopt_sgd_step(const flashopt_tensor *tensors, int n_tensors,
+                                  const flashopt_sgd_args *a, void *workspace,
+                                  size_t ws_bytes, void *stream)
+{
+    if (n_tensors < 0 || !a) return FLASHOPT_EINVAL;
+    if (n_tensors > 0 && !tensors) return FLASHOPT_EINVAL;
+    if (a->master_bits != 24 && a->master_bits != 32 && a->master_bits != 0) return FLASHOPT_EINVAL;
+    if (a->companded != 0 && a->companded != 1) return FLASHOPT_EINVAL;
+    if (a->fp32_states != 0 && a->fp32_states != 1) return FLASHOPT_EINVAL;
+    if (a->nesterov != 0 && a->nesterov != 1) return FLASHOPT_EINVAL;
+    if (a->step < 1) return FLASHOPT_EINVAL;
+    if (!(a->lr >= 0.0) || !std::isfinite(a->lr)) return FLASHOPT_EINVAL;
+    if (!(a->momentum > 0.0) || !std::isfinite(a->momentum)) return FLASHOPT_EINVAL;
+    if (!std::isfinite(a->dampening) || !std::isfinite(a->weight_decay)) return FLASHOPT_EINVAL;
+    if (a->nesterov && a->dampening != 0.0) return FLASHOPT_EINVAL;
+
+    SgdScalars sc;
+    sc.lr = static_cast<float>(a->lr);
+    sc.mu = static_cast<float>(a->momentum);
+    sc.cd = static_cast<float>(1.0 - a->dampening);
+    sc.wd = static_cast<float>(a->weight_decay);
+    sc.has_wd = a->weight_decay != 0.0 ? 1 : 0;
+    sc.first = a->step == 1 ? 1 : 0;
+    sc.nesterov = a->nesterov;
+
+    const int states = a->fp32_states ? flashopt::kStatesFp32
+                     : (a->companded ? flashopt::kStatesCompanded : flashopt::kStatesLinear);
+    return stage_and_launch(tensors, n_tensors, a->master_bits, a->fp32_states == 0, false,
+                            workspace, ws_bytes, stream,
+                            [&](const DevTensor *d, const int32_t *cs, int32_t total, hipStream_t st) {
+                                return flashopt::launch_sgd_step(d, cs, n_tensors, total, sc,
+                                                                 a->master_bits, states, st);
+                            });
 }
 
 }  // extern "C"

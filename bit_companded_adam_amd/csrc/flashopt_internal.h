@@ -48,6 +48,18 @@ struct StepScalars {
     int fast_div;  // 1 when every denominator lies in [2^-100, 2^100] (eps >= 2^-100, k2 <= 2^60)
 };
 
+// fp32 scalars of one FlashSGD step (SGD with momentum), formed in double
+// on the host and rounded once.
+struct SgdScalars {
+    float lr;
+    float mu;       // momentum
+    float cd;       // 1 - dampening
+    float wd;       // coupled weight decay
+    int has_wd;     // weight_decay != 0
+    int first;      // step == 1: the buffer is set to the gradient
+    int nesterov;
+};
+
 hipError_t launch_quantize(const float *x, int64_t n, unsigned spec, void *codes,
                            uint16_t *scales, hipStream_t stream);
 hipError_t launch_dequantize(const void *codes, const uint16_t *scales, int64_t n,
@@ -63,5 +75,9 @@ hipError_t launch_adamw_step(const DevTensor *tensors, const int32_t *chunk_star
                              int n_tensors, int32_t total_chunks,
                              const StepScalars &sc, int master_bits, int states,
                              hipStream_t stream);
+hipError_t launch_sgd_step(const DevTensor *tensors, const int32_t *chunk_start,
+                           int n_tensors, int32_t total_chunks,
+                           const SgdScalars &sc, int master_bits, int states,
+                           hipStream_t stream);
 
 }  // namespace flashopt

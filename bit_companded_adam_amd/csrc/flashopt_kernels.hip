@@ -776,7 +776,7 @@ __device__ __forceinline__ int unit_count(const ChunkPtrs &c, uint32_t r)
 // Loads of one unit of every stream (the unit at chunk offset r).  FULL:
 // straight-line streaming loads; otherwise element-masked loads with zeros
 // for missing elements (and zero scales for a unit with none).
-template <int MB, int ST, int N, bool FULL>
+template <int MB, int ST, int N, bool FULL, bool V = true>
 __device__ __forceinline__ void load_unit(const ChunkPtrs &c, uint32_t r, int cnt,
                                           UnitIn<MB, ST, N> &in)
 {
@@ -789,12 +789,14 @@ __device__ __forceinline__ void load_unit(const ChunkPtrs &c, uint32_t r, int cn
         if constexpr (MB == 32) ld_words<2 * N>(c.rho16 + r, in.rw);
         if constexpr (ST == kStatesFp32) {
             ld_words<4 * N>(c.mf + r, in.mf);
-            ld_words<4 * N>(c.vf + r, in.vf);
+            if constexpr (V) ld_words<4 * N>(c.vf + r, in.vf);
         } else {
             ld_words<N>(c.mc + r, in.mw);
-            ld_words<N>(c.vc + r, in.vw);
             in.smb = ld_u16(c.ms + r / kGroup);
-            in.svb = ld_u16(c.vs + r / kGroup);
+            if constexpr (V) {
+                ld_words<N>(c.vc + r, in.vw);
+                in.svb = ld_u16(c.vs + r / kGroup);
+            }
         }
     } else {
         ld_elems<2, N>(c.param + r, cnt, in.pw);
@@ -803,13 +805,13 @@ __device__ __forceinline__ void load_unit(const ChunkPtrs &c, uint32_t r, int cn
         if constexpr (MB == 32) ld_elems<2, N>(c.rho16 + r, cnt, in.rw);
         if constexpr (ST == kStatesFp32) {
             ld_elems<4, N>(c.mf + r, cnt, in.mf);
-            ld_elems<4, N>(c.vf + r, cnt, in.vf);
+            if constexpr (V) ld_elems<4, N>(c.vf + r, cnt, in.vf);
         } else {
             ld_elems<1, N>(c.mc + r, cnt, in.mw);
-            ld_elems<1, N>(c.vc + r, cnt, in.vw);
+            if constexpr (V) ld_elems<1, N>(c.vc + r, cnt, in.vw);
             if (cnt > 0) {
                 in.smb = ld_u16(c.ms + r / kGroup);
-                in.svb = ld_u16(c.vs + r / kGroup);
+                if constexpr (V) in.svb = ld_u16(c.vs + r / kGroup);
             }
         }
     }
@@ -1046,30 +1048,105 @@ __device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
     }
 }
 
+// ------------------------------------------------------------ FlashSGD
+
+// One FlashSGD unit: SGD with momentum (the buffer set to the gradient at
+// step 1, coupled weight decay, optional dampening and Nesterov), the
+// momentum buffer stored as group-32 codes (or fp32), the master re-split.
+// There is no division: only non-finite values need the element-wise
+// NaN-safe encoders, which run on the same registers.
+template <int MB, int ST, int N, bool FULL>
+__device__ __forceinline__ void sgd_unit(const ChunkPtrs &c, int u, int lane,
+                                         const SgdScalars &sc, const float *s_mu)
+{
+    constexpr bool kQuant = ST != kStatesFp32;
+    constexpr bool kComp = ST == kStatesCompanded;
+    constexpr unsigned kMSpec = kComp ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
+    const uint32_t r = unit_first<N>(u, lane);
+    const int cnt = FULL ? N : unit_count<N>(c, r);
+
+    UnitIn<MB, ST, N> in;
+    load_unit<MB, ST, N, FULL, false>(c, r, cnt, in);
+    const float ms = f16_value(in.smb);
+
+    float th1[N], b1[N];
+    bool bad = false;                        // a non-finite buffer value or a NaN result
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        float theta;
+        if constexpr (MB == 0) theta = (j & 1) ? bf16_hi(in.pw[j >> 1]) : bf16_lo(in.pw[j >> 1]);
+        else theta = reconstruct_perm<MB>(in.pw, in.rw, j);
+        float d = (j & 1) ? bf16_hi(in.gw[j >> 1]) : bf16_lo(in.gw[j >> 1]);
+        if (sc.has_wd) {
+            const float decay = sc.wd * theta;
+            d = d + decay;
+        }
+        float b;
+        if (sc.first) {
+            b = d;
+        } else {
+            const float b0 = kQuant ? s_mu[ubyte(in.mw, j)] * ms : __uint_as_float(in.mf[j]);
+            const float kept = sc.mu * b0;
+            const float added = sc.cd * d;
+            b = kept + added;
+        }
+        float dir = b;
+        if (sc.nesterov) {
+            const float look = sc.mu * b;
+            dir = d + look;
+        }
+        const float upd = sc.lr * dir;
+        th1[j] = theta - upd;
+        b1[j] = (!FULL && kQuant && j >= cnt) ? 0.0f : b;   // zero pad of a ragged group
+        bad |= !(fabsf(b1[j]) <= 0x1.fffffep127f) || th1[j] != th1[j];
+    }
+
+    uint32_t mo[N / 4], po[N / 2], ro[rho_words(MB, N)];
+    uint32_t sm_out = 0u;
+    if constexpr (kQuant) {
+        float am = fabsf(b1[0]);
+#pragma unroll
+        for (int j = 1; j < N; ++j) am = fmaxf(am, fabsf(b1[j]));
+        sm_out = f16_bits(group_max<32 / N>(am));
+        const GroupDiv gdm = group_div(sm_out);
+        if (!bad) encode_s8_finite<kComp, N>(b1, gdm, mo);
+        else encode<kMSpec, N>(b1, gdm, mo);
+    }
+    if (!bad) pack_theta<MB, false, N>(th1, po, ro);
+    else pack_theta<MB, true, N>(th1, po, ro);
+
+    uint32_t bb[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) bb[j] = __float_as_uint(b1[j]);
+    if (FULL) {
+        st_words<2 * N>(c.param + r, po);
+        if constexpr (MB == 24) st_words<N>(c.rho8 + r, ro);
+        if constexpr (MB == 32) st_words<2 * N>(c.rho16 + r, ro);
+        if constexpr (kQuant) st_words<N>(c.mc + r, mo);
+        else st_words<4 * N>(c.mf + r, bb);
+    } else {
+        st_elems<2, N>(c.param + r, cnt, po);
+        if constexpr (MB == 24) st_elems<1, N>(c.rho8 + r, cnt, ro);
+        if constexpr (MB == 32) st_elems<2, N>(c.rho16 + r, cnt, ro);
+        if constexpr (kQuant) st_elems<1, N>(c.mc + r, cnt, mo);
+        else st_elems<4, N>(c.mf + r, cnt, bb);
+    }
+    if (kQuant && lane % (32 / N) == 0 && cnt > 0) st_u16(c.ms + r / kGroup, static_cast<uint16_t>(sm_out));
+}
+
+// ------------------------------------------------------------- kernels
+
 // Grid: one wavefront per run of `run` consecutive chunks (the last run may be
 // shorter); a chunk never straddles two tensors.  The wavefront finds the
 // tensor owning its first chunk by binary search over the chunk table
-// (scalar loads, uniform across the wavefront) and walks forward from there.
-// With quantized states the two 256-entry dequantization tables are built per
-// workgroup in LDS from the exact fp32 operations of dequantize().
-template <int MB, int ST>
-__global__ void __launch_bounds__(kBlockThreads)
-adamw_step_kernel(const DevTensor *__restrict__ tensors, const int32_t *__restrict__ chunk_start,
-                  int n_tensors, int32_t total_chunks, int32_t run, StepScalars sc)
+// (scalar loads, uniform across the wavefront) and walks forward from there,
+// calling f(chunk pointers) for each chunk.
+template <typename F>
+__device__ __forceinline__ void for_each_chunk(const DevTensor *__restrict__ tensors,
+                                               const int32_t *__restrict__ chunk_start,
+                                               int n_tensors, int32_t total_chunks, int32_t run,
+                                               F &&f)
 {
-    constexpr unsigned kMSpec =
-        ST == kStatesCompanded ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
-    constexpr int kN = unit_elems(MB, ST);
-    constexpr int kUnits = kLaneElems / kN;
-    __shared__ float s_mu[256];   // momentum: q/127 (companded: / (2 - |.|))
-    __shared__ float s_vu[256];   // variance: q/255
-    if constexpr (ST != kStatesFp32) {
-        s_mu[threadIdx.x] = dequant_unit<kMSpec>(static_cast<int>(threadIdx.x));
-        s_vu[threadIdx.x] = dequant_unit<0u>(static_cast<int>(threadIdx.x));
-        __syncthreads();
-    }
-
-    const int lane = threadIdx.x & (kWaveLanes - 1);
     const int64_t wave = __builtin_amdgcn_readfirstlane(
         static_cast<int32_t>(blockIdx.x) * (kBlockThreads / kWaveLanes) + (threadIdx.x >> 6));
     const int64_t c0 = wave * run;
@@ -1089,7 +1166,31 @@ adamw_step_kernel(const DevTensor *__restrict__ tensors, const int32_t *__restri
         t = __builtin_amdgcn_readfirstlane(t);
         const DevTensor d = tensors[t];
         const int64_t off = static_cast<int64_t>(c - chunk_start[t]) * kChunkElems;
-        const ChunkPtrs cp = chunk_ptrs(d, off);
+        f(chunk_ptrs(d, off));
+    }
+}
+
+// The fused FlashAdamW step.  With quantized states the two 256-entry
+// dequantization tables are built per workgroup in LDS from the exact fp32
+// operations of dequantize().
+template <int MB, int ST>
+__global__ void __launch_bounds__(kBlockThreads)
+adamw_step_kernel(const DevTensor *__restrict__ tensors, const int32_t *__restrict__ chunk_start,
+                  int n_tensors, int32_t total_chunks, int32_t run, StepScalars sc)
+{
+    constexpr unsigned kMSpec =
+        ST == kStatesCompanded ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
+    constexpr int kN = unit_elems(MB, ST);
+    constexpr int kUnits = kLaneElems / kN;
+    __shared__ float s_mu[256];   // momentum: q/127 (companded: / (2 - |.|))
+    __shared__ float s_vu[256];   // variance: q/255
+    if constexpr (ST != kStatesFp32) {
+        s_mu[threadIdx.x] = dequant_unit<kMSpec>(static_cast<int>(threadIdx.x));
+        s_vu[threadIdx.x] = dequant_unit<0u>(static_cast<int>(threadIdx.x));
+        __syncthreads();
+    }
+    const int lane = threadIdx.x & (kWaveLanes - 1);
+    for_each_chunk(tensors, chunk_start, n_tensors, total_chunks, run, [&](const ChunkPtrs &cp) {
         if (cp.rem == kChunkElems) {
 #pragma unroll
             for (int u = 0; u < kUnits; ++u) step_unit<MB, ST, kN, true>(cp, u, lane, sc, s_mu, s_vu);
@@ -1097,7 +1198,34 @@ adamw_step_kernel(const DevTensor *__restrict__ tensors, const int32_t *__restri
 #pragma unroll
             for (int u = 0; u < kUnits; ++u) step_unit<MB, ST, kN, false>(cp, u, lane, sc, s_mu, s_vu);
         }
+    });
+}
+
+// The fused FlashSGD step (same grid and tables, momentum only).
+template <int MB, int ST>
+__global__ void __launch_bounds__(kBlockThreads)
+sgd_step_kernel(const DevTensor *__restrict__ tensors, const int32_t *__restrict__ chunk_start,
+                int n_tensors, int32_t total_chunks, int32_t run, SgdScalars sc)
+{
+    constexpr unsigned kMSpec =
+        ST == kStatesCompanded ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
+    constexpr int kN = unit_elems(MB, ST);
+    constexpr int kUnits = kLaneElems / kN;
+    __shared__ float s_mu[256];
+    if constexpr (ST != kStatesFp32) {
+        s_mu[threadIdx.x] = dequant_unit<kMSpec>(static_cast<int>(threadIdx.x));
+        __syncthreads();
     }
+    const int lane = threadIdx.x & (kWaveLanes - 1);
+    for_each_chunk(tensors, chunk_start, n_tensors, total_chunks, run, [&](const ChunkPtrs &cp) {
+        if (cp.rem == kChunkElems) {
+#pragma unroll
+            for (int u = 0; u < kUnits; ++u) sgd_unit<MB, ST, kN, true>(cp, u, lane, sc, s_mu);
+        } else {
+#pragma unroll
+            for (int u = 0; u < kUnits; ++u) sgd_unit<MB, ST, kN, false>(cp, u, lane, sc, s_mu);
+        }
+    });
 }
 
 // ------------------------------------------------------------- launching
@@ -1183,33 +1311,83 @@ hipError_t launch_reconstruct(const uint16_t *param, const void *rho, int64_t n,
 
 namespace {
 
-template <int MB, int ST>
-hipError_t step_variant(const DevTensor *tensors, const int32_t *chunk_start, int n_tensors,
-                        int32_t total_chunks, int32_t run, const StepScalars &sc, hipStream_t st)
+// Consecutive chunks per wavefront (2 measured best on the 8.0B list for
+// both master widths); FLASHOPT_CHUNKS_PER_WAVE overrides it.
+int32_t chunks_per_wave()
+{
+    int32_t run = 2;
+    if (const char *env = getenv("FLASHOPT_CHUNKS_PER_WAVE")) {
+        const int v = atoi(env);
+        if (v >= 1 && v <= 1024) run = v;
+    }
+    return run;
+}
+
+unsigned step_grid(int32_t total_chunks, int32_t run)
 {
     const int64_t waves = (total_chunks + run - 1) / run;
     const int64_t waves_per_block = kBlockThreads / kWaveLanes;
-    const int64_t grid = (waves + waves_per_block - 1) / waves_per_block;
-    hipLaunchKernelGGL((adamw_step_kernel<MB, ST>), dim3(static_cast<unsigned>(grid)),
+    return static_cast<unsigned>((waves + waves_per_block - 1) / waves_per_block);
+}
+
+template <int MB, int ST>
+hipError_t step_variant(const DevTensor *tensors, const int32_t *chunk_start, int n_tensors,
+                        int32_t total_chunks, const StepScalars &sc, hipStream_t st)
+{
+    const int32_t run = chunks_per_wave();
+    hipLaunchKernelGGL((adamw_step_kernel<MB, ST>), dim3(step_grid(total_chunks, run)),
                        dim3(kBlockThreads), 0, st, tensors, chunk_start, n_tensors,
                        total_chunks, run, sc);
     return hipGetLastError();
 }
 
-template <int MB>
-hipError_t step_states(const DevTensor *tensors, const int32_t *chunk_start, int n_tensors,
-                       int32_t total_chunks, int32_t run, const StepScalars &sc, int states,
-                       hipStream_t st)
+template <int MB, int ST>
+hipError_t sgd_variant(const DevTensor *tensors, const int32_t *chunk_start, int n_tensors,
+                       int32_t total_chunks, const SgdScalars &sc, hipStream_t st)
 {
-    switch (states) {
-    case kStatesCompanded:
-        return step_variant<MB, kStatesCompanded>(tensors, chunk_start, n_tensors, total_chunks, run, sc, st);
-    case kStatesLinear:
-        return step_variant<MB, kStatesLinear>(tensors, chunk_start, n_tensors, total_chunks, run, sc, st);
-    default:
-        return step_variant<MB, kStatesFp32>(tensors, chunk_start, n_tensors, total_chunks, run, sc, st);
+    const int32_t run = chunks_per_wave();
+    hipLaunchKernelGGL((sgd_step_kernel<MB, ST>), dim3(step_grid(total_chunks, run)),
+                       dim3(kBlockThreads), 0, st, tensors, chunk_start, n_tensors,
+                       total_chunks, run, sc);
+    return hipGetLastError();
+}
+
+// The nine (master_bits, states) instantiations of one step kernel family.
+template <template <int, int> class K, typename Sc>
+hipError_t dispatch(int master_bits, int states, const DevTensor *tensors,
+                    const int32_t *chunk_start, int n_tensors, int32_t total_chunks,
+                    const Sc &sc, hipStream_t st)
+{
+    switch (master_bits * 4 + states) {
+    case 24 * 4 + kStatesCompanded: return K<24, kStatesCompanded>::run(tensors, chunk_start, n_tensors, total_chunks, sc, st);
+    case 24 * 4 + kStatesLinear: return K<24, kStatesLinear>::run(tensors, chunk_start, n_tensors, total_chunks, sc, st);
+    case 24 * 4 + kStatesFp32: return K<24, kStatesFp32>::run(tensors, chunk_start, n_tensors, total_chunks, sc, st);
+    case 32 * 4 + kStatesCompanded: return K<32, kStatesCompanded>::run(tensors, chunk_start, n_tensors, total_chunks, sc, st);
+    case 32 * 4 + kStatesLinear: return K<32, kStatesLinear>::run(tensors, chunk_start, n_tensors, total_chunks, sc, st);
+    case 32 * 4 + kStatesFp32: return K<32, kStatesFp32>::run(tensors, chunk_start, n_tensors, total_chunks, sc, st);
+    case kStatesCompanded: return K<0, kStatesCompanded>::run(tensors, chunk_start, n_tensors, total_chunks, sc, st);
+    case kStatesLinear: return K<0, kStatesLinear>::run(tensors, chunk_start, n_tensors, total_chunks, sc, st);
+    default: return K<0, kStatesFp32>::run(tensors, chunk_start, n_tensors, total_chunks, sc, st);
     }
 }
+
+template <int MB, int ST>
+struct AdamWLaunch {
+    static hipError_t run(const DevTensor *t, const int32_t *cs, int n, int32_t total,
+                          const StepScalars &sc, hipStream_t st)
+    {
+        return step_variant<MB, ST>(t, cs, n, total, sc, st);
+    }
+};
+
+template <int MB, int ST>
+struct SgdLaunch {
+    static hipError_t run(const DevTensor *t, const int32_t *cs, int n, int32_t total,
+                          const SgdScalars &sc, hipStream_t st)
+    {
+        return sgd_variant<MB, ST>(t, cs, n, total, sc, st);
+    }
+};
 
 }  // namespace
 
@@ -1218,18 +1396,17 @@ hipError_t launch_adamw_step(const DevTensor *tensors, const int32_t *chunk_star
                              int states, hipStream_t st)
 {
     if (total_chunks <= 0) return hipSuccess;
-    // Consecutive chunks per wavefront (2 measured best on the 8.0B list for
-    // both master widths); FLASHOPT_CHUNKS_PER_WAVE overrides it.
-    int32_t run = 2;
-    if (const char *env = getenv("FLASHOPT_CHUNKS_PER_WAVE")) {
-        const int v = atoi(env);
-        if (v >= 1 && v <= 1024) run = v;
-    }
-    switch (master_bits) {
-    case 24: return step_states<24>(tensors, chunk_start, n_tensors, total_chunks, run, sc, states, st);
-    case 32: return step_states<32>(tensors, chunk_start, n_tensors, total_chunks, run, sc, states, st);
-    default: return step_states<0>(tensors, chunk_start, n_tensors, total_chunks, run, sc, states, st);
-    }
+    return dispatch<AdamWLaunch>(master_bits, states, tensors, chunk_start, n_tensors,
+                                 total_chunks, sc, st);
+}
+
+hipError_t launch_sgd_step(const DevTensor *tensors, const int32_t *chunk_start, int n_tensors,
+                           int32_t total_chunks, const SgdScalars &sc, int master_bits,
+                           int states, hipStream_t st)
+{
+    if (total_chunks <= 0) return hipSuccess;
+    return dispatch<SgdLaunch>(master_bits, states, tensors, chunk_start, n_tensors,
+                               total_chunks, sc, st);
 }
 
 }  // namespace flashopt

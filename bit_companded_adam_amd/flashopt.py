@@ -1,4 +1,5 @@
-"""Thin ctypes binding of libflashopt.so with the C entry points' names.
+"""Thin ctypes binding of libflashopt.so with the C entry points' names
+(FlashAdamW and FlashSGD steps, the codec and the weight split).
 
 Argument marshalling only: every computation runs in the HIP kernels of the
 library.  Tensors are torch CUDA (HIP) tensors; outputs are allocated with
@@ -28,7 +29,8 @@ CHUNK_ELEMS = 1024
 
 EXPORTS = ("flashopt_quantize", "flashopt_dequantize", "flashopt_split",
            "flashopt_reconstruct", "flashopt_adamw_workspace_bytes",
-           "flashopt_adamw_step", "flashopt_status_str", "flashopt_abi_version")
+           "flashopt_adamw_step", "flashopt_sgd_workspace_bytes", "flashopt_sgd_step",
+           "flashopt_status_str", "flashopt_abi_version")
 
 
 class FlashoptError(RuntimeError):
@@ -52,6 +54,14 @@ class flashopt_adamw_args(ctypes.Structure):
                 ("fp32_states", ctypes.c_int), ("reserved", ctypes.c_int)]
 
 
+class flashopt_sgd_args(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("momentum", ctypes.c_double),
+                ("dampening", ctypes.c_double), ("weight_decay", ctypes.c_double),
+                ("step", ctypes.c_int64), ("master_bits", ctypes.c_int),
+                ("companded", ctypes.c_int), ("fp32_states", ctypes.c_int),
+                ("nesterov", ctypes.c_int)]
+
+
 _lib = None
 
 
@@ -72,11 +82,16 @@ def lib() -> ctypes.CDLL:
         L.flashopt_adamw_step.argtypes = [ctypes.POINTER(flashopt_tensor), i,
                                           ctypes.POINTER(flashopt_adamw_args), vp,
                                           ctypes.c_size_t, vp]
+        L.flashopt_sgd_workspace_bytes.argtypes = [ctypes.POINTER(flashopt_tensor), i]
+        L.flashopt_sgd_workspace_bytes.restype = ctypes.c_size_t
+        L.flashopt_sgd_step.argtypes = [ctypes.POINTER(flashopt_tensor), i,
+                                        ctypes.POINTER(flashopt_sgd_args), vp,
+                                        ctypes.c_size_t, vp]
         L.flashopt_status_str.argtypes = [i]
         L.flashopt_status_str.restype = ctypes.c_char_p
         L.flashopt_abi_version.argtypes = []
         for name in ("flashopt_quantize", "flashopt_dequantize", "flashopt_split",
-                     "flashopt_reconstruct", "flashopt_adamw_step"):
+                     "flashopt_reconstruct", "flashopt_adamw_step", "flashopt_sgd_step"):
             getattr(L, name).restype = i
         _lib = L
     return _lib
@@ -176,7 +191,8 @@ class TensorState:
     and variance as codes with fp16 scales, or as fp32 arrays when
     quantize_states is False.  Fresh state is zero."""
 
-    def __init__(self, param: torch.Tensor, master_bits=24, quantize_states: bool = True):
+    def __init__(self, param: torch.Tensor, master_bits=24, quantize_states: bool = True,
+                 variance: bool = True):
         if param.dtype != torch.bfloat16 or not param.is_contiguous():
             raise ValueError("param must be a contiguous bf16 tensor")
         if master_bits not in (24, 32, None):
@@ -187,11 +203,11 @@ class TensorState:
         if quantize_states:
             self.m_codes = torch.zeros(n, dtype=torch.int8, device=dev)
             self.m_scales = torch.zeros(n_groups(n), dtype=torch.int16, device=dev)
-            self.v_codes = torch.zeros(n, dtype=torch.uint8, device=dev)
-            self.v_scales = torch.zeros(n_groups(n), dtype=torch.int16, device=dev)
+            self.v_codes = torch.zeros(n, dtype=torch.uint8, device=dev) if variance else None
+            self.v_scales = torch.zeros(n_groups(n), dtype=torch.int16, device=dev) if variance else None
         else:
             self.m_codes = torch.zeros(n, dtype=torch.float32, device=dev)
-            self.v_codes = torch.zeros(n, dtype=torch.float32, device=dev)
+            self.v_codes = torch.zeros(n, dtype=torch.float32, device=dev) if variance else None
             self.m_scales = self.v_scales = None
         self.master_bits = master_bits
         self.quantize_states = quantize_states
@@ -202,7 +218,7 @@ class TensorState:
         opt = lambda t, name: 0 if t is None else _dev(t, name)
         return flashopt_tensor(_dev(self.param, "param"), _dev(grad, "grad"),
                                opt(self.rho, "rho"), _dev(self.m_codes, "m_codes"),
-                               opt(self.m_scales, "m_scales"), _dev(self.v_codes, "v_codes"),
+                               opt(self.m_scales, "m_scales"), opt(self.v_codes, "v_codes"),
                                opt(self.v_scales, "v_scales"), self.param.numel())
 
 
@@ -256,3 +272,51 @@ class FlashAdamW:
             self._desc = descriptor_array(self.states, grads)
             self._grads = list(grads)
         flashopt_adamw_step(self._desc, make_args(self.t, **self.hp), self.workspace, stream)
+
+
+# --------------------------------------------------------------- FlashSGD
+
+def make_sgd_args(step: int, lr=1e-2, momentum=0.9, dampening=0.0, weight_decay=0.0,
+                  nesterov=False, master_bits=24, companded=True,
+                  quantize_states=True) -> flashopt_sgd_args:
+    return flashopt_sgd_args(lr, momentum, dampening, weight_decay, step,
+                             0 if master_bits is None else master_bits, int(companded),
+                             0 if quantize_states else 1, int(nesterov))
+
+
+def flashopt_sgd_workspace_bytes(n_tensors: int) -> int:
+    return lib().flashopt_sgd_workspace_bytes(None, n_tensors)
+
+
+def flashopt_sgd_step(descriptors, args: flashopt_sgd_args, workspace: torch.Tensor,
+                      stream=None):
+    """One fused FlashSGD step over a ctypes array of flashopt_tensor descriptors."""
+    n = len(descriptors)
+    _check(lib().flashopt_sgd_step(descriptors, n, ctypes.byref(args), _dev(workspace, "workspace"),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)),
+           "flashopt_sgd_step")
+
+
+class FlashSGD:
+    """A list of TensorStates (momentum buffer only) stepped together by one
+    launch per step."""
+
+    def __init__(self, params, lr=1e-2, momentum=0.9, dampening=0.0, weight_decay=0.0,
+                 nesterov=False, master_bits=24, companded=True, quantize_states=True):
+        self.states = [TensorState(p, master_bits, quantize_states, variance=False) for p in params]
+        self.hp = dict(lr=lr, momentum=momentum, dampening=dampening, weight_decay=weight_decay,
+                       nesterov=nesterov, master_bits=master_bits, companded=companded,
+                       quantize_states=quantize_states)
+        dev = self.states[0].param.device if self.states else "cuda"
+        nbytes = max(16, flashopt_sgd_workspace_bytes(len(self.states)))
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.t = 0
+        self._grads = None
+        self._desc = None
+
+    def step(self, grads, stream=None):
+        self.t += 1
+        if self._grads is None or any(a is not b for a, b in zip(self._grads, grads)):
+            self._desc = descriptor_array(self.states, grads)
+            self._grads = list(grads)
+        flashopt_sgd_step(self._desc, make_sgd_args(self.t, **self.hp), self.workspace, stream)

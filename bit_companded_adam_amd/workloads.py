@@ -28,6 +28,8 @@ FACTOR_SEED = 4321
 
 # Step hyper-parameters of the single-tensor workload (2^20 params, 10 steps).
 HP_DEFAULT = dict(lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01)
+# FlashSGD step hyper-parameters (SGD with momentum)
+SGD_DEFAULT = dict(lr=1e-2, momentum=0.9, dampening=0.0, weight_decay=0.01, nesterov=False)
 
 
 def battery() -> dict[str, torch.Tensor]:

@@ -1,5 +1,6 @@
 /*
- * flashopt.h -- C ABI of libflashopt.so, the MI355X (gfx950) FlashAdamW step.
+ * flashopt.h -- C ABI of libflashopt.so, the MI355X (gfx950) FlashAdamW and
+ * FlashSGD steps.
  *
  * The method is described on the pages
  *   "code/flashsim/quantization.py"    (group-32 companded int8/uint8 state codec,
@@ -41,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FLASHOPT_ABI_VERSION 2
+#define FLASHOPT_ABI_VERSION 3
 
 typedef enum {
     FLASHOPT_OK = 0,
@@ -181,6 +182,46 @@ flashopt_status flashopt_adamw_step(const flashopt_tensor *tensors, int n_tensor
                                     const flashopt_adamw_args *args,
                                     void *workspace, size_t workspace_bytes,
                                     void *stream);
+
+/* FlashSGD hyper-parameters.  FlashSGD appears on page
+ * "code/flashsim/flash_adamw_sim.py" only in bytes_per_param ("flash_sgd":
+ * bf16 master + rho + grad + one group-32 state of 1 + 2/32 bytes); this
+ * library reads its update as torch.optim.SGD with momentum, in torch's
+ * order, one fp32 rounding per operation:
+ *   d   = g + weight_decay * theta                 (coupled; skipped if 0)
+ *   buf = d at step 1, else momentum * buf + (1 - dampening) * d
+ *   dir = d + momentum * buf if nesterov, else buf
+ *   theta = theta - lr * dir
+ * with the buffer stored under the momentum spec (softsign int8, or the
+ * linear spec if !companded) or as fp32, and the master split as for
+ * flashopt_adamw_step. */
+typedef struct {
+    double lr;                /* >= 0                                         */
+    double momentum;          /* > 0 (plain SGD keeps no state to compress)   */
+    double dampening;         /* finite; must be 0 with nesterov              */
+    double weight_decay;      /* finite                                       */
+    int64_t step;             /* t >= 1; step 1 sets the buffer to d          */
+    int master_bits;          /* 24 | 32 | 0 (no split), as flashopt_adamw_args */
+    int companded;            /* 1: softsign momentum spec; 0: linear         */
+    int fp32_states;          /* 0: codes + fp16 scales; 1: fp32 buffer       */
+    int nesterov;             /* 0 | 1                                        */
+} flashopt_sgd_args;
+
+/* Device workspace bytes that flashopt_sgd_step needs for this list. */
+size_t flashopt_sgd_workspace_bytes(const flashopt_tensor *tensors, int n_tensors);
+
+/* One fused FlashSGD step over a list of tensors, one kernel launch.  The
+ * momentum buffer lives in each descriptor's m_codes / m_scales; v_codes and
+ * v_scales are unused (may be NULL).  Ownership, staging, workspace and
+ * alignment rules as flashopt_adamw_step.
+ * Errors: EINVAL (as flashopt_adamw_step for the list; momentum <= 0,
+ * non-finite dampening or weight_decay, nesterov with dampening != 0, bad
+ * nesterov / companded / fp32_states / master_bits, step < 1, lr < 0),
+ * EALIGN, EWORKSPACE, EHIP. */
+flashopt_status flashopt_sgd_step(const flashopt_tensor *tensors, int n_tensors,
+                                  const flashopt_sgd_args *args,
+                                  void *workspace, size_t workspace_bytes,
+                                  void *stream);
 
 /* Static string naming a status code. */
 const char *flashopt_status_str(flashopt_status status);

@@ -138,3 +138,28 @@ def test_binding_refuses_host_tensors(L):
     import torch
     with pytest.raises(ValueError):
         F.flashopt_quantize(torch.zeros(64), F.SPEC_MOMENTUM)
+
+
+def test_sgd_step_validation(L):
+    def sgd(tensors, args, ws=A16, ws_bytes=1 << 20):
+        arr = (F.flashopt_tensor * max(1, len(tensors)))(*tensors)
+        return L.flashopt_sgd_step(arr, len(tensors), ctypes.byref(args), ws, ws_bytes, None)
+
+    ok = [_tensor()]
+    for bad in (dict(step=0), dict(momentum=0.0), dict(momentum=float("nan")), dict(lr=-1.0),
+                dict(dampening=float("inf")), dict(weight_decay=float("nan")),
+                dict(master_bits=16), dict(companded=2), dict(fp32_states=2), dict(nesterov=2)):
+        a = F.make_sgd_args(1)
+        for k, v in bad.items():
+            setattr(a, k, v)
+        assert sgd(ok, a) == F.FLASHOPT_EINVAL, bad
+    a = F.make_sgd_args(1, nesterov=True, dampening=0.1)
+    assert sgd(ok, a) == F.FLASHOPT_EINVAL                       # nesterov needs dampening 0
+    # the variance streams are unused: NULL passes validation and the call
+    # stops at the (too small) workspace, before anything is enqueued
+    assert sgd([_tensor(v_codes=None, v_scales=None)], F.make_sgd_args(1), ws_bytes=0) == F.FLASHOPT_EWORKSPACE
+    assert sgd([_tensor(m_scales=None)], F.make_sgd_args(1), ws_bytes=0) == F.FLASHOPT_EINVAL
+    assert sgd([_tensor(m_scales=None)], F.make_sgd_args(1, quantize_states=False),
+               ws_bytes=0) == F.FLASHOPT_EWORKSPACE
+    assert sgd([_tensor(m_codes=A16 + 8)], F.make_sgd_args(1), ws_bytes=0) == F.FLASHOPT_EALIGN
+    assert F.flashopt_sgd_workspace_bytes(3) == F.flashopt_adamw_workspace_bytes(3)

@@ -1,0 +1,165 @@
+"""GPU parity of the fused FlashSGD step (flashopt_sgd_step) against the
+oracle, through the C ABI.  FlashSGD appears on page
+"code/flashsim/flash_adamw_sim.py" only in bytes_per_param; the library and
+the oracle read its update as torch.optim.SGD with momentum, the buffer stored
+with the momentum spec.  Bar as for the AdamW step: scales, rho and the bf16
+parameter bit-exact, codes (or the fp32 buffer) bit-exact.
+  * ragged lists (sizes 0 .. 2^17) for five storage variants and four
+    momentum settings (plain, weight decay, Nesterov, dampening), 3 steps,
+    teacher-forced;
+  * 2^20 params x 10 steps, teacher-forced and free-running;
+  * non-finite gradients next to finite lanes (NaN matches any NaN);
+  * the 1.2B list on group-aligned samples in the benchmark's launch shape.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_companded_adam_amd import flashopt as F
+from bit_companded_adam_amd import workloads as W
+from tests._gpu import host, require_gpu, u16
+
+pytestmark = pytest.mark.gpu
+
+HP = dict(lr=1e-2, momentum=0.9, dampening=0.0, weight_decay=0.0, nesterov=False)
+SETTINGS = {"plain": {}, "wd": dict(weight_decay=0.01), "nesterov": dict(nesterov=True, weight_decay=0.01),
+            "dampening": dict(dampening=0.1)}
+STORAGE = [(24, True, True), (32, False, True), (None, True, True), (24, True, False), (None, True, False)]
+RAGGED = [0, 1, 17, 31, 32, 33, 1000, 1023, 1024, 1025, 4096 + 5, 70001, 1 << 17]
+
+
+def _sid(v):
+    mb, comp, qs = v
+    return f"mb{mb}-{'comp' if comp else 'lin'}-{'q' if qs else 'f32'}"
+
+
+def _snap(s: F.TensorState, lo=0, hi=None) -> oracle.State:
+    hi = s.param.numel() if hi is None else hi
+    g0, g1 = lo // 32, (hi + 31) // 32
+    rho = None if s.rho is None else host(s.rho[lo:hi])
+    ms = None if s.m_scales is None else u16(s.m_scales[g0:g1])
+    return oracle.State(u16(s.param[lo:hi]), rho, host(s.m_codes[lo:hi]), ms, None, None)
+
+
+def _f16_nan(a):
+    return ((a & 0x7C00) == 0x7C00) & ((a & 0x03FF) != 0)
+
+
+def _bf16_nan(a):
+    return ((a & 0x7F80) == 0x7F80) & ((a & 0x7F) != 0)
+
+
+def _compare(got: oracle.State, want: oracle.State, label: str, nan_ok=False):
+    same = got.param == want.param
+    if nan_ok:
+        same |= _bf16_nan(got.param) & _bf16_nan(want.param)
+    assert same.all(), f"{label}: bf16 param"
+    if want.rho is not None:
+        assert (got.rho == want.rho).all(), f"{label}: rho"
+    if want.m_scales is None:
+        a, b = got.m_codes.view(np.uint32), want.m_codes.view(np.uint32)
+        same = a == b
+        if nan_ok:
+            same |= np.isnan(got.m_codes) & np.isnan(want.m_codes)
+        assert same.all(), f"{label}: fp32 buffer"
+    else:
+        same = got.m_scales == want.m_scales
+        if nan_ok:
+            same |= _f16_nan(got.m_scales) & _f16_nan(want.m_scales)
+        assert same.all(), f"{label}: m scales"
+        assert (got.m_codes == want.m_codes).all(), f"{label}: m codes"
+
+
+def _orc_hp(t, hp, mb, comp, qs):
+    return oracle.sgd_hparams(lr=hp["lr"], momentum=hp["momentum"], dampening=hp["dampening"],
+                              weight_decay=hp["weight_decay"], nesterov=hp["nesterov"], step=t,
+                              master_bits=mb, companded=comp, quantize_states=qs)
+
+
+@pytest.mark.parametrize("setting", sorted(SETTINGS))
+@pytest.mark.parametrize("mb,comp,qs", STORAGE, ids=[_sid(v) for v in STORAGE])
+def test_ragged_list(orc, mb, comp, qs, setting):
+    require_gpu()
+    hp = dict(HP, **SETTINGS[setting])
+    params = [W.init_param(n, device="cuda", seed=200 + i) for i, n in enumerate(RAGGED)]
+    opt = F.FlashSGD(params, master_bits=mb, companded=comp, quantize_states=qs, **hp)
+    for t in range(1, 4):
+        grads = [W.make_grad(n, t, device="cuda", stream_id=i, factor=float(np.exp(i - 6)))
+                 for i, n in enumerate(RAGGED)]
+        pres = [_snap(s) for s in opt.states]
+        opt.step(grads)
+        torch.cuda.synchronize()
+        for i, (s, pre, g) in enumerate(zip(opt.states, pres, grads)):
+            orc.sgd_step(pre, u16(g), _orc_hp(t, hp, mb, comp, qs))
+            _compare(_snap(s), pre, f"{_sid((mb, comp, qs))} {setting} t{t} tensor{i} n{RAGGED[i]}")
+
+
+def test_single_tensor_10_steps(orc):
+    require_gpu()
+    n = 1 << 20
+    hp = dict(HP, weight_decay=0.01)
+    p = W.init_param(n, device="cuda", seed=31)
+    opt = F.FlashSGD([p], **hp)
+    free = orc.State.zeros_like_param(u16(p), 24)
+    free.v_codes = free.v_scales = None
+    for t in range(1, 11):
+        g = W.make_grad(n, t, device="cuda")
+        pre = _snap(opt.states[0])
+        opt.step([g])
+        torch.cuda.synchronize()
+        post = _snap(opt.states[0])
+        orc.sgd_step(pre, u16(g), _orc_hp(t, hp, 24, True, True))
+        _compare(post, pre, f"teacher-forced step {t}")
+        orc.sgd_step(free, u16(g), _orc_hp(t, hp, 24, True, True))
+        _compare(post, free, f"free-running step {t}")
+
+
+@pytest.mark.parametrize("mb,comp,qs", [(24, True, True), (None, True, False)], ids=["q", "f32"])
+def test_non_finite_gradients(orc, mb, comp, qs):
+    """Outside the contract but defined: non-finite buffers take the
+    element-wise encoders; their neighbours in the same group do not."""
+    require_gpu()
+    n = 16 * 1024 + 77
+    p = W.init_param(n, device="cuda", seed=41)
+    opt = F.FlashSGD([p], master_bits=mb, companded=comp, quantize_states=qs, **HP)
+    for t in range(1, 4):
+        g = W.make_grad(n, t).float()
+        g[1603] = float("inf")
+        g[2091] = float("nan")
+        g[64 * 32:65 * 32] = 1e30
+        g = g.to(torch.bfloat16).to("cuda")
+        pre = _snap(opt.states[0])
+        opt.step([g])
+        torch.cuda.synchronize()
+        orc.sgd_step(pre, u16(g), _orc_hp(t, HP, mb, comp, qs))
+        _compare(_snap(opt.states[0]), pre, f"non-finite t{t}", nan_ok=True)
+
+
+def test_decoder_1b_sampled(orc):
+    require_gpu()
+    shapes = W.decoder_1b_shapes()
+    params = [W.init_param(W.numel(s), device="cuda", seed=1000 + i) for i, (_, s) in enumerate(shapes)]
+    opt = F.FlashSGD(params, **dict(HP, weight_decay=0.01))
+    factors = W.grad_factors(len(shapes)).numpy()
+    grads = lambda t: [W.make_grad(W.numel(s), t, device="cuda", stream_id=i, factor=float(factors[i]))
+                       for i, (_, s) in enumerate(shapes)]
+    opt.step(grads(1))
+    g2 = grads(2)
+    rng = np.random.default_rng(9)
+    torch.cuda.synchronize()
+    ranges = []
+    for s in opt.states:
+        n = s.param.numel()
+        r = [(0, min(n, 1 << 16)), (max(0, ((n - (1 << 16)) // 32) * 32), n)]
+        if n > 4096:
+            r += [(int(c) * 1024, int(c) * 1024 + 1024) for c in rng.integers(0, n // 1024 - 1, 2)]
+        ranges.append(r)
+    pres = [[_snap(s, lo, hi) for lo, hi in rr] for s, rr in zip(opt.states, ranges)]
+    gs = [[u16(g[lo:hi]) for lo, hi in rr] for g, rr in zip(g2, ranges)]
+    opt.step(g2)
+    torch.cuda.synchronize()
+    for i, (s, rr) in enumerate(zip(opt.states, ranges)):
+        for (lo, hi), pre, g in zip(rr, pres[i], gs[i]):
+            orc.sgd_step(pre, g, _orc_hp(2, dict(HP, weight_decay=0.01), 24, True, True))
+            _compare(_snap(s, lo, hi), pre, f"1.2B tensor {i} [{lo}, {hi})")
