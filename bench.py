@@ -12,7 +12,8 @@ Other configurations (reported beside the default, not as its value):
 --workload decoder-1b-list (199 tensors, 1,195,991,040 params), --master-bits
 32 | 0 (0: no split, the page's master_weight_bits=None), --linear (linear
 codec ablation), --fp32-states (quantize_states=False), --optimizer sgd (the
-FlashSGD step: lr 1e-2, momentum 0.9, weight decay 0.01).
+FlashSGD step: lr 1e-2, momentum 0.9, weight decay 0.01), --grad-release (one
+single-tensor launch per tensor, the gradient-release launch pattern).
 
 Prints one JSON line: Gparam/s over the K timed steps, the roofline of the
 step kernel (algorithmic bytes per param of the configuration against
@@ -123,9 +124,18 @@ def environment() -> dict:
     return env
 
 
-def time_steps(opt, grads, steps: int, warmup: int):
+def time_steps(opt, grads, steps: int, warmup: int, per_tensor: bool = False):
+    """per_tensor: the gradient-release launch pattern, one single-tensor
+    launch per tensor (the step is then the whole sequence of launches)."""
+    def one_step(stream=None):
+        if per_tensor:
+            for i, g in enumerate(grads):
+                opt.step_tensor(i, g, stream)
+        else:
+            opt.step(grads, stream)
+
     for _ in range(warmup):
-        opt.step(grads)
+        one_step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -133,7 +143,7 @@ def time_steps(opt, grads, steps: int, warmup: int):
     t0 = time.perf_counter()
     for a, b in evs:
         a.record(stream)
-        opt.step(grads, stream)
+        one_step(stream)
         b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -227,6 +237,8 @@ def main():
                     help="unquantized fp32 moments (weight-splitting-only ablation)")
     ap.add_argument("--optimizer", default="adamw", choices=("adamw", "sgd"),
                     help="sgd: the FlashSGD step (momentum buffer only)")
+    ap.add_argument("--grad-release", action="store_true",
+                    help="one single-tensor launch per tensor (the gradient-release pattern)")
     ap.add_argument("--cpu-elems", type=int, default=1 << 27,
                     help="oracle sample size for the CPU baseline (0: skip)")
     ap.add_argument("--cpu-threads", type=int, default=0)
@@ -256,7 +268,7 @@ def main():
     print(f"# workload ready: {len(opt.states)} tensors, {n} params, "
           f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated", file=sys.stderr, flush=True)
 
-    wall, per = time_steps(opt, grads, args.steps, args.warmup)
+    wall, per = time_steps(opt, grads, args.steps, args.warmup, args.grad_release)
     env = environment()                     # clocks read right after the timed steps
     ms_step = wall * 1e3 / args.steps
     ms_launch = float(np.mean(per))
@@ -271,9 +283,11 @@ def main():
     cpu = None
     if args.cpu_elems > 0 and args.optimizer == "adamw":
         cpu = cpu_baseline(mb, args.cpu_elems, args.cpu_threads, args.cpu_seconds, comp, qs)
-    default = (args.workload, mb, comp, qs, args.optimizer) == ("decoder-8b-list", 24, True, True, "adamw")
+    default = (args.workload, mb, comp, qs, args.optimizer, args.grad_release) == \
+        ("decoder-8b-list", 24, True, True, "adamw", False)
     name = args.workload + ("" if comp else "-linear") + ("" if qs else "-fp32-states") + \
-        ("-no-split" if mb == 0 else "") + ("-flashsgd" if args.optimizer == "sgd" else "")
+        ("-no-split" if mb == 0 else "") + ("-flashsgd" if args.optimizer == "sgd" else "") + \
+        ("-per-tensor-launches" if args.grad_release else "")
 
     out = {
         "metric": METRIC,
@@ -290,7 +304,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "params": n, "tensors": n_tensors,
                    "master_bits": mb, "companded": comp, "quantized_states": qs,
-                   "bytes_per_param": bpp, "launches_per_step": 1},
+                   "bytes_per_param": bpp,
+                   "launches_per_step": n_tensors if args.grad_release else 1},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": traffic_per_launch() if default else None,

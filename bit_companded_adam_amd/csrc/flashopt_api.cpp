@@ -73,6 +73,99 @@ struct Ring {
 std::mutex g_ring_mutex;
 Ring g_rings[kMaxDevices];
 
+// Validation of one tensor of a step.  split: rho is used; quant: scales are
+// used; v: the variance streams are used.
+flashopt_status check_tensor(const flashopt_tensor &t, bool split, bool quant, bool v)
+{
+    if (t.numel < 0) return FLASHOPT_EINVAL;
+    if (t.numel == 0) return FLASHOPT_OK;
+    if (!t.param || !t.grad || !t.m_codes) return FLASHOPT_EINVAL;
+    if (v && !t.v_codes) return FLASHOPT_EINVAL;
+    if (split && !t.rho) return FLASHOPT_EINVAL;
+    if (quant && (!t.m_scales || (v && !t.v_scales))) return FLASHOPT_EINVAL;
+    if (!aligned(t.param, 16) || !aligned(t.grad, 16) || !aligned(t.m_codes, 16))
+        return FLASHOPT_EALIGN;
+    if (v && !aligned(t.v_codes, 16)) return FLASHOPT_EALIGN;
+    if (split && !aligned(t.rho, 16)) return FLASHOPT_EALIGN;
+    if (quant && (!aligned(t.m_scales, 2) || (v && !aligned(t.v_scales, 2)))) return FLASHOPT_EALIGN;
+    if ((t.numel + flashopt::kChunkElems - 1) / flashopt::kChunkElems > INT32_MAX) return FLASHOPT_EINVAL;
+    return FLASHOPT_OK;
+}
+
+DevTensor device_descriptor(const flashopt_tensor &s)
+{
+    DevTensor d;
+    d.param = s.param;
+    d.grad = s.grad;
+    d.rho = s.rho;
+    d.m_codes = s.m_codes;
+    d.m_scales = s.m_scales;
+    d.v_codes = s.v_codes;
+    d.v_scales = s.v_scales;
+    d.numel = s.numel;
+    return d;
+}
+
+int states_of(int fp32_states, int companded)
+{
+    return fp32_states ? flashopt::kStatesFp32
+                       : (companded ? flashopt::kStatesCompanded : flashopt::kStatesLinear);
+}
+
+// AdamW hyper-parameters checked, then the step's fp32 scalars formed in
+// double and rounded once.
+flashopt_status adamw_scalars(const flashopt_adamw_args *a, StepScalars &sc)
+{
+    if (!a) return FLASHOPT_EINVAL;
+    if (a->master_bits != 24 && a->master_bits != 32 && a->master_bits != 0) return FLASHOPT_EINVAL;
+    if (a->companded != 0 && a->companded != 1) return FLASHOPT_EINVAL;
+    if (a->fp32_states != 0 && a->fp32_states != 1) return FLASHOPT_EINVAL;
+    if (a->reserved != 0) return FLASHOPT_EINVAL;
+    if (a->step < 1) return FLASHOPT_EINVAL;
+    if (!(a->lr >= 0.0) || !std::isfinite(a->lr)) return FLASHOPT_EINVAL;
+    if (!(a->beta1 >= 0.0 && a->beta1 < 1.0) || !(a->beta2 >= 0.0 && a->beta2 < 1.0)) return FLASHOPT_EINVAL;
+    if (!(a->eps >= 0.0) || !std::isfinite(a->eps)) return FLASHOPT_EINVAL;
+    if (!std::isfinite(a->weight_decay)) return FLASHOPT_EINVAL;
+    const double t = static_cast<double>(a->step);
+    const double bc1 = 1.0 - std::pow(a->beta1, t);
+    const double bc2 = 1.0 - std::pow(a->beta2, t);
+    sc.cwd = static_cast<float>(1.0 - a->lr * a->weight_decay);
+    sc.b1 = static_cast<float>(a->beta1);
+    sc.c1 = static_cast<float>(1.0 - a->beta1);
+    sc.b2 = static_cast<float>(a->beta2);
+    sc.c2 = static_cast<float>(1.0 - a->beta2);
+    sc.alpha = static_cast<float>(a->lr / bc1);
+    sc.k2 = static_cast<float>(1.0 / std::sqrt(bc2));
+    sc.eps = static_cast<float>(a->eps);
+    // The kernel's short division is exact for denominators sqrt(v) k2 + eps in
+    // [2^-100, 2^100]; sqrt(v) < 2^32 on its fast path.
+    sc.fast_div = (sc.eps >= 0x1p-100f && sc.k2 <= 0x1p60f) ? 1 : 0;
+    sc.num_max = sc.fast_div ? sc.eps * 0x1p100f : 0.0f;
+    return FLASHOPT_OK;
+}
+
+flashopt_status sgd_scalars(const flashopt_sgd_args *a, SgdScalars &sc)
+{
+    if (!a) return FLASHOPT_EINVAL;
+    if (a->master_bits != 24 && a->master_bits != 32 && a->master_bits != 0) return FLASHOPT_EINVAL;
+    if (a->companded != 0 && a->companded != 1) return FLASHOPT_EINVAL;
+    if (a->fp32_states != 0 && a->fp32_states != 1) return FLASHOPT_EINVAL;
+    if (a->nesterov != 0 && a->nesterov != 1) return FLASHOPT_EINVAL;
+    if (a->step < 1) return FLASHOPT_EINVAL;
+    if (!(a->lr >= 0.0) || !std::isfinite(a->lr)) return FLASHOPT_EINVAL;
+    if (!(a->momentum > 0.0) || !std::isfinite(a->momentum)) return FLASHOPT_EINVAL;
+    if (!std::isfinite(a->dampening) || !std::isfinite(a->weight_decay)) return FLASHOPT_EINVAL;
+    if (a->nesterov && a->dampening != 0.0) return FLASHOPT_EINVAL;
+    sc.lr = static_cast<float>(a->lr);
+    sc.mu = static_cast<float>(a->momentum);
+    sc.cd = static_cast<float>(1.0 - a->dampening);
+    sc.wd = static_cast<float>(a->weight_decay);
+    sc.has_wd = a->weight_decay != 0.0 ? 1 : 0;
+    sc.first = a->step == 1 ? 1 : 0;
+    sc.nesterov = a->nesterov;
+    return FLASHOPT_OK;
+}
+
 // Validation of a step's tensor list, then the chunk table staged through the
 // pinned ring and launch(d_desc, d_chunk_start, total_chunks, stream).  split:
 // rho is used; quant: scales are used; v: the variance streams are used.
@@ -84,19 +177,9 @@ flashopt_status stage_and_launch(const flashopt_tensor *tensors, int n_tensors, 
     const bool split = master_bits != 0;
     int64_t total = 0;
     for (int i = 0; i < n_tensors; ++i) {
-        const flashopt_tensor &t = tensors[i];
-        if (t.numel < 0) return FLASHOPT_EINVAL;
-        if (t.numel == 0) continue;
-        if (!t.param || !t.grad || !t.m_codes) return FLASHOPT_EINVAL;
-        if (v && !t.v_codes) return FLASHOPT_EINVAL;
-        if (split && !t.rho) return FLASHOPT_EINVAL;
-        if (quant && (!t.m_scales || (v && !t.v_scales))) return FLASHOPT_EINVAL;
-        if (!aligned(t.param, 16) || !aligned(t.grad, 16) || !aligned(t.m_codes, 16))
-            return FLASHOPT_EALIGN;
-        if (v && !aligned(t.v_codes, 16)) return FLASHOPT_EALIGN;
-        if (split && !aligned(t.rho, 16)) return FLASHOPT_EALIGN;
-        if (quant && (!aligned(t.m_scales, 2) || (v && !aligned(t.v_scales, 2)))) return FLASHOPT_EALIGN;
-        total += (t.numel + flashopt::kChunkElems - 1) / flashopt::kChunkElems;
+        const flashopt_status st = check_tensor(tensors[i], split, quant, v);
+        if (st != FLASHOPT_OK) return st;
+        total += (tensors[i].numel + flashopt::kChunkElems - 1) / flashopt::kChunkElems;
         if (total > INT32_MAX) return FLASHOPT_EINVAL;
     }
     if (total == 0) return FLASHOPT_OK;
@@ -131,18 +214,9 @@ flashopt_status stage_and_launch(const flashopt_tensor *tensors, int n_tensors, 
     int32_t *start = reinterpret_cast<int32_t *>(desc + n_tensors);
     int32_t acc = 0;
     for (int i = 0; i < n_tensors; ++i) {
-        const flashopt_tensor &s = tensors[i];
-        DevTensor &d = desc[i];
-        d.param = s.param;
-        d.grad = s.grad;
-        d.rho = s.rho;
-        d.m_codes = s.m_codes;
-        d.m_scales = s.m_scales;
-        d.v_codes = s.v_codes;
-        d.v_scales = s.v_scales;
-        d.numel = s.numel;
+        desc[i] = device_descriptor(tensors[i]);
         start[i] = acc;
-        acc += static_cast<int32_t>((s.numel + flashopt::kChunkElems - 1) / flashopt::kChunkElems);
+        acc += static_cast<int32_t>((tensors[i].numel + flashopt::kChunkElems - 1) / flashopt::kChunkElems);
     }
     start[n_tensors] = acc;
 
@@ -220,45 +294,31 @@ flashopt_status flashopt_adamw_step(const flashopt_tensor *tensors, int n_tensor
                                     const flashopt_adamw_args *a, void *workspace,
                                     size_t ws_bytes, void *stream)
 {
-    // ---- hyper-parameters
-    if (n_tensors < 0 || !a) return FLASHOPT_EINVAL;
-    if (n_tensors > 0 && !tensors) return FLASHOPT_EINVAL;
-    if (a->master_bits != 24 && a->master_bits != 32 && a->master_bits != 0) return FLASHOPT_EINVAL;
-    if (a->companded != 0 && a->companded != 1) return FLASHOPT_EINVAL;
-    if (a->fp32_states != 0 && a->fp32_states != 1) return FLASHOPT_EINVAL;
-    if (a->reserved != 0) return FLASHOPT_EINVAL;
-    if (a->step < 1) return FLASHOPT_EINVAL;
-    if (!(a->lr >= 0.0) || !std::isfinite(a->lr)) return FLASHOPT_EINVAL;
-    if (!(a->beta1 >= 0.0 && a->beta1 < 1.0) || !(a->beta2 >= 0.0 && a->beta2 < 1.0)) return FLASHOPT_EINVAL;
-    if (!(a->eps >= 0.0) || !std::isfinite(a->eps)) return FLASHOPT_EINVAL;
-    if (!std::isfinite(a->weight_decay)) return FLASHOPT_EINVAL;
-
-    // ---- step scalars: double on the host, rounded once to fp32
+    if (n_tensors < 0 || (n_tensors > 0 && !tensors)) return FLASHOPT_EINVAL;
     StepScalars sc;
-    const double t = static_cast<double>(a->step);
-    const double bc1 = 1.0 - std::pow(a->beta1, t);
-    const double bc2 = 1.0 - std::pow(a->beta2, t);
-    sc.cwd = static_cast<float>(1.0 - a->lr * a->weight_decay);
-    sc.b1 = static_cast<float>(a->beta1);
-    sc.c1 = static_cast<float>(1.0 - a->beta1);
-    sc.b2 = static_cast<float>(a->beta2);
-    sc.c2 = static_cast<float>(1.0 - a->beta2);
-    sc.alpha = static_cast<float>(a->lr / bc1);
-    sc.k2 = static_cast<float>(1.0 / std::sqrt(bc2));
-    sc.eps = static_cast<float>(a->eps);
-    // The kernel's short division is exact for denominators sqrt(v) k2 + eps in
-    // [2^-100, 2^100]; sqrt(v) < 2^32 on its fast path.
-    sc.fast_div = (sc.eps >= 0x1p-100f && sc.k2 <= 0x1p60f) ? 1 : 0;
-    sc.num_max = sc.fast_div ? sc.eps * 0x1p100f : 0.0f;
-
-    const int states = a->fp32_states ? flashopt::kStatesFp32
-                     : (a->companded ? flashopt::kStatesCompanded : flashopt::kStatesLinear);
+    const flashopt_status hs = adamw_scalars(a, sc);
+    if (hs != FLASHOPT_OK) return hs;
+    const int states = states_of(a->fp32_states, a->companded);
     return stage_and_launch(tensors, n_tensors, a->master_bits, a->fp32_states == 0, true,
                             workspace, ws_bytes, stream,
                             [&](const DevTensor *d, const int32_t *cs, int32_t total, hipStream_t st) {
                                 return flashopt::launch_adamw_step(d, cs, n_tensors, total, sc,
                                                                    a->master_bits, states, st);
                             });
+}
+
+flashopt_status flashopt_adamw_step_tensor(const flashopt_tensor *tensor,
+                                           const flashopt_adamw_args *a, void *stream)
+{
+    if (!tensor) return FLASHOPT_EINVAL;
+    StepScalars sc;
+    const flashopt_status hs = adamw_scalars(a, sc);
+    if (hs != FLASHOPT_OK) return hs;
+    const flashopt_status ts = check_tensor(*tensor, a->master_bits != 0, a->fp32_states == 0, true);
+    if (ts != FLASHOPT_OK || tensor->numel == 0) return ts;
+    return hip_status(flashopt::launch_adamw_tensor(device_descriptor(*tensor), sc, a->master_bits,
+                                                    states_of(a->fp32_states, a->companded),
+                                                    static_cast<hipStream_t>(stream)));
 }
 
 size_t flashopt_sgd_workspace_bytes(const flashopt_tensor *tensors, int n_tensors)
@@ -271,35 +331,31 @@ flashopt_status flashopt_sgd_step(const flashopt_tensor *tensors, int n_tensors,
                                   const flashopt_sgd_args *a, void *workspace,
                                   size_t ws_bytes, void *stream)
 {
-    if (n_tensors < 0 || !a) return FLASHOPT_EINVAL;
-    if (n_tensors > 0 && !tensors) return FLASHOPT_EINVAL;
-    if (a->master_bits != 24 && a->master_bits != 32 && a->master_bits != 0) return FLASHOPT_EINVAL;
-    if (a->companded != 0 && a->companded != 1) return FLASHOPT_EINVAL;
-    if (a->fp32_states != 0 && a->fp32_states != 1) return FLASHOPT_EINVAL;
-    if (a->nesterov != 0 && a->nesterov != 1) return FLASHOPT_EINVAL;
-    if (a->step < 1) return FLASHOPT_EINVAL;
-    if (!(a->lr >= 0.0) || !std::isfinite(a->lr)) return FLASHOPT_EINVAL;
-    if (!(a->momentum > 0.0) || !std::isfinite(a->momentum)) return FLASHOPT_EINVAL;
-    if (!std::isfinite(a->dampening) || !std::isfinite(a->weight_decay)) return FLASHOPT_EINVAL;
-    if (a->nesterov && a->dampening != 0.0) return FLASHOPT_EINVAL;
-
+    if (n_tensors < 0 || (n_tensors > 0 && !tensors)) return FLASHOPT_EINVAL;
     SgdScalars sc;
-    sc.lr = static_cast<float>(a->lr);
-    sc.mu = static_cast<float>(a->momentum);
-    sc.cd = static_cast<float>(1.0 - a->dampening);
-    sc.wd = static_cast<float>(a->weight_decay);
-    sc.has_wd = a->weight_decay != 0.0 ? 1 : 0;
-    sc.first = a->step == 1 ? 1 : 0;
-    sc.nesterov = a->nesterov;
-
-    const int states = a->fp32_states ? flashopt::kStatesFp32
-                     : (a->companded ? flashopt::kStatesCompanded : flashopt::kStatesLinear);
+    const flashopt_status hs = sgd_scalars(a, sc);
+    if (hs != FLASHOPT_OK) return hs;
+    const int states = states_of(a->fp32_states, a->companded);
     return stage_and_launch(tensors, n_tensors, a->master_bits, a->fp32_states == 0, false,
                             workspace, ws_bytes, stream,
                             [&](const DevTensor *d, const int32_t *cs, int32_t total, hipStream_t st) {
                                 return flashopt::launch_sgd_step(d, cs, n_tensors, total, sc,
                                                                  a->master_bits, states, st);
                             });
+}
+
+flashopt_status flashopt_sgd_step_tensor(const flashopt_tensor *tensor,
+                                         const flashopt_sgd_args *a, void *stream)
+{
+    if (!tensor) return FLASHOPT_EINVAL;
+    SgdScalars sc;
+    const flashopt_status hs = sgd_scalars(a, sc);
+    if (hs != FLASHOPT_OK) return hs;
+    const flashopt_status ts = check_tensor(*tensor, a->master_bits != 0, a->fp32_states == 0, false);
+    if (ts != FLASHOPT_OK || tensor->numel == 0) return ts;
+    return hip_status(flashopt::launch_sgd_tensor(device_descriptor(*tensor), sc, a->master_bits,
+                                                  states_of(a->fp32_states, a->companded),
+                                                  static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -79,5 +79,10 @@ hipError_t launch_sgd_step(const DevTensor *tensors, const int32_t *chunk_start,
                            int n_tensors, int32_t total_chunks,
                            const SgdScalars &sc, int master_bits, int states,
                            hipStream_t stream);
+// One tensor, its descriptor passed in the kernel arguments (no workspace).
+hipError_t launch_adamw_tensor(const DevTensor &d, const StepScalars &sc, int master_bits,
+                               int states, hipStream_t stream);
+hipError_t launch_sgd_tensor(const DevTensor &d, const SgdScalars &sc, int master_bits,
+                             int states, hipStream_t stream);
 
 }  // namespace flashopt

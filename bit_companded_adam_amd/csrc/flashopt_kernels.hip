@@ -1228,6 +1228,73 @@ sgd_step_kernel(const DevTensor *__restrict__ tensors, const int32_t *__restrict
     });
 }
 
+// Single-tensor forms (the descriptor travels in the kernel arguments, no
+// chunk table): chunk c of the tensor starts at element 1024 c.
+template <typename F>
+__device__ __forceinline__ void for_each_chunk_of(const DevTensor &d, int32_t total_chunks,
+                                                  int32_t run, F &&f)
+{
+    const int64_t wave = __builtin_amdgcn_readfirstlane(
+        static_cast<int32_t>(blockIdx.x) * (kBlockThreads / kWaveLanes) + (threadIdx.x >> 6));
+    const int64_t c0 = wave * run;
+    if (c0 >= total_chunks) return;
+    const int32_t c1 = static_cast<int32_t>(c0 + run < total_chunks ? c0 + run : total_chunks);
+    for (int32_t c = static_cast<int32_t>(c0); c < c1; ++c)
+        f(chunk_ptrs(d, static_cast<int64_t>(c) * kChunkElems));
+}
+
+template <int MB, int ST>
+__global__ void __launch_bounds__(kBlockThreads)
+adamw_tensor_kernel(DevTensor d, int32_t total_chunks, int32_t run, StepScalars sc)
+{
+    constexpr unsigned kMSpec =
+        ST == kStatesCompanded ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
+    constexpr int kN = unit_elems(MB, ST);
+    constexpr int kUnits = kLaneElems / kN;
+    __shared__ float s_mu[256];
+    __shared__ float s_vu[256];
+    if constexpr (ST != kStatesFp32) {
+        s_mu[threadIdx.x] = dequant_unit<kMSpec>(static_cast<int>(threadIdx.x));
+        s_vu[threadIdx.x] = dequant_unit<0u>(static_cast<int>(threadIdx.x));
+        __syncthreads();
+    }
+    const int lane = threadIdx.x & (kWaveLanes - 1);
+    for_each_chunk_of(d, total_chunks, run, [&](const ChunkPtrs &cp) {
+        if (cp.rem == kChunkElems) {
+#pragma unroll
+            for (int u = 0; u < kUnits; ++u) step_unit<MB, ST, kN, true>(cp, u, lane, sc, s_mu, s_vu);
+        } else {
+#pragma unroll
+            for (int u = 0; u < kUnits; ++u) step_unit<MB, ST, kN, false>(cp, u, lane, sc, s_mu, s_vu);
+        }
+    });
+}
+
+template <int MB, int ST>
+__global__ void __launch_bounds__(kBlockThreads)
+sgd_tensor_kernel(DevTensor d, int32_t total_chunks, int32_t run, SgdScalars sc)
+{
+    constexpr unsigned kMSpec =
+        ST == kStatesCompanded ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
+    constexpr int kN = unit_elems(MB, ST);
+    constexpr int kUnits = kLaneElems / kN;
+    __shared__ float s_mu[256];
+    if constexpr (ST != kStatesFp32) {
+        s_mu[threadIdx.x] = dequant_unit<kMSpec>(static_cast<int>(threadIdx.x));
+        __syncthreads();
+    }
+    const int lane = threadIdx.x & (kWaveLanes - 1);
+    for_each_chunk_of(d, total_chunks, run, [&](const ChunkPtrs &cp) {
+        if (cp.rem == kChunkElems) {
+#pragma unroll
+            for (int u = 0; u < kUnits; ++u) sgd_unit<MB, ST, kN, true>(cp, u, lane, sc, s_mu);
+        } else {
+#pragma unroll
+            for (int u = 0; u < kUnits; ++u) sgd_unit<MB, ST, kN, false>(cp, u, lane, sc, s_mu);
+        }
+    });
+}
+
 // ------------------------------------------------------------- launching
 
 unsigned grid_for(int64_t n)
@@ -1389,6 +1456,31 @@ struct SgdLaunch {
     }
 };
 
+// Single-tensor launches: t points to a host descriptor passed by value.
+template <int MB, int ST>
+struct AdamWTensorLaunch {
+    static hipError_t run(const DevTensor *t, const int32_t *, int, int32_t total,
+                          const StepScalars &sc, hipStream_t st)
+    {
+        const int32_t run = chunks_per_wave();
+        hipLaunchKernelGGL((adamw_tensor_kernel<MB, ST>), dim3(step_grid(total, run)),
+                           dim3(kBlockThreads), 0, st, *t, total, run, sc);
+        return hipGetLastError();
+    }
+};
+
+template <int MB, int ST>
+struct SgdTensorLaunch {
+    static hipError_t run(const DevTensor *t, const int32_t *, int, int32_t total,
+                          const SgdScalars &sc, hipStream_t st)
+    {
+        const int32_t run = chunks_per_wave();
+        hipLaunchKernelGGL((sgd_tensor_kernel<MB, ST>), dim3(step_grid(total, run)),
+                           dim3(kBlockThreads), 0, st, *t, total, run, sc);
+        return hipGetLastError();
+    }
+};
+
 }  // namespace
 
 hipError_t launch_adamw_step(const DevTensor *tensors, const int32_t *chunk_start, int n_tensors,
@@ -1407,6 +1499,24 @@ hipError_t launch_sgd_step(const DevTensor *tensors, const int32_t *chunk_start,
     if (total_chunks <= 0) return hipSuccess;
     return dispatch<SgdLaunch>(master_bits, states, tensors, chunk_start, n_tensors,
                                total_chunks, sc, st);
+}
+
+hipError_t launch_adamw_tensor(const DevTensor &d, const StepScalars &sc, int master_bits,
+                               int states, hipStream_t st)
+{
+    const int64_t chunks = (d.numel + kChunkElems - 1) / kChunkElems;
+    if (chunks <= 0) return hipSuccess;
+    return dispatch<AdamWTensorLaunch>(master_bits, states, &d, nullptr, 1,
+                                       static_cast<int32_t>(chunks), sc, st);
+}
+
+hipError_t launch_sgd_tensor(const DevTensor &d, const SgdScalars &sc, int master_bits,
+                             int states, hipStream_t st)
+{
+    const int64_t chunks = (d.numel + kChunkElems - 1) / kChunkElems;
+    if (chunks <= 0) return hipSuccess;
+    return dispatch<SgdTensorLaunch>(master_bits, states, &d, nullptr, 1,
+                                     static_cast<int32_t>(chunks), sc, st);
 }
 
 }  // namespace flashopt

@@ -29,8 +29,9 @@ CHUNK_ELEMS = 1024
 
 EXPORTS = ("flashopt_quantize", "flashopt_dequantize", "flashopt_split",
            "flashopt_reconstruct", "flashopt_adamw_workspace_bytes",
-           "flashopt_adamw_step", "flashopt_sgd_workspace_bytes", "flashopt_sgd_step",
-           "flashopt_status_str", "flashopt_abi_version")
+           "flashopt_adamw_step", "flashopt_adamw_step_tensor", "flashopt_sgd_workspace_bytes",
+           "flashopt_sgd_step", "flashopt_sgd_step_tensor", "flashopt_status_str",
+           "flashopt_abi_version")
 
 
 class FlashoptError(RuntimeError):
@@ -87,11 +88,16 @@ def lib() -> ctypes.CDLL:
         L.flashopt_sgd_step.argtypes = [ctypes.POINTER(flashopt_tensor), i,
                                         ctypes.POINTER(flashopt_sgd_args), vp,
                                         ctypes.c_size_t, vp]
+        L.flashopt_adamw_step_tensor.argtypes = [ctypes.POINTER(flashopt_tensor),
+                                                 ctypes.POINTER(flashopt_adamw_args), vp]
+        L.flashopt_sgd_step_tensor.argtypes = [ctypes.POINTER(flashopt_tensor),
+                                               ctypes.POINTER(flashopt_sgd_args), vp]
         L.flashopt_status_str.argtypes = [i]
         L.flashopt_status_str.restype = ctypes.c_char_p
         L.flashopt_abi_version.argtypes = []
         for name in ("flashopt_quantize", "flashopt_dequantize", "flashopt_split",
-                     "flashopt_reconstruct", "flashopt_adamw_step", "flashopt_sgd_step"):
+                     "flashopt_reconstruct", "flashopt_adamw_step", "flashopt_sgd_step",
+                     "flashopt_adamw_step_tensor", "flashopt_sgd_step_tensor"):
             getattr(L, name).restype = i
         _lib = L
     return _lib
@@ -250,7 +256,52 @@ def flashopt_adamw_step(descriptors, args: flashopt_adamw_args, workspace: torch
            "flashopt_adamw_step")
 
 
-class FlashAdamW:
+def flashopt_adamw_step_tensor(desc: flashopt_tensor, args: flashopt_adamw_args, stream=None):
+    """One tensor's step, descriptor in the kernel arguments (no workspace)."""
+    _check(lib().flashopt_adamw_step_tensor(ctypes.byref(desc), ctypes.byref(args), _stream(stream)),
+           "flashopt_adamw_step_tensor")
+
+
+class _Stepper:
+    """Common driver of FlashAdamW / FlashSGD: a list step (one launch for all
+    tensors) and a per-tensor step (one launch for one tensor, each tensor
+    counting its own steps as the pages' per-parameter state does)."""
+
+    def _init_common(self):
+        self.t = 0
+        self.ts = [0] * len(self.states)
+        self._grads = None
+        self._desc = None
+
+    def step(self, grads, stream=None):
+        self.t += 1
+        self.ts = [self.t] * len(self.states)
+        if self._grads is None or any(a is not b for a, b in zip(self._grads, grads)):
+            self._desc = descriptor_array(self.states, grads)
+            self._grads = list(grads)
+        self._list_step(self._desc, self.t, stream)
+
+    def step_tensor(self, i: int, grad: torch.Tensor, stream=None):
+        self.ts[i] += 1
+        self._tensor_step(self.states[i].descriptor(grad), self.ts[i], stream)
+
+
+def attach_grad_release(opt, params):
+    """Gradient release: register a post-accumulate-grad hook on every
+    parameter that runs that tensor's step as soon as its gradient is
+    complete and then frees the gradient, so a full set of gradients is never
+    held.  params are the optimizer's parameters, in its order.  Returns the
+    hook handles."""
+    index = {id(p): i for i, p in enumerate(params)}
+
+    def hook(p):
+        opt.step_tensor(index[id(p)], p.grad)
+        p.grad = None
+
+    return [p.register_post_accumulate_grad_hook(hook) for p in params]
+
+
+class FlashAdamW(_Stepper):
     """A list of TensorStates stepped together by one launch per step."""
 
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0,
@@ -262,16 +313,13 @@ class FlashAdamW:
         dev = self.states[0].param.device if self.states else "cuda"
         nbytes = max(16, flashopt_adamw_workspace_bytes(len(self.states)))
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        self.t = 0
-        self._grads = None
-        self._desc = None
+        self._init_common()
 
-    def step(self, grads, stream=None):
-        self.t += 1
-        if self._grads is None or any(a is not b for a, b in zip(self._grads, grads)):
-            self._desc = descriptor_array(self.states, grads)
-            self._grads = list(grads)
-        flashopt_adamw_step(self._desc, make_args(self.t, **self.hp), self.workspace, stream)
+    def _list_step(self, desc, t, stream):
+        flashopt_adamw_step(desc, make_args(t, **self.hp), self.workspace, stream)
+
+    def _tensor_step(self, desc, t, stream):
+        flashopt_adamw_step_tensor(desc, make_args(t, **self.hp), stream)
 
 
 # --------------------------------------------------------------- FlashSGD
@@ -288,6 +336,12 @@ def flashopt_sgd_workspace_bytes(n_tensors: int) -> int:
     return lib().flashopt_sgd_workspace_bytes(None, n_tensors)
 
 
+def flashopt_sgd_step_tensor(desc: flashopt_tensor, args: flashopt_sgd_args, stream=None):
+    """One tensor's FlashSGD step, descriptor in the kernel arguments."""
+    _check(lib().flashopt_sgd_step_tensor(ctypes.byref(desc), ctypes.byref(args), _stream(stream)),
+           "flashopt_sgd_step_tensor")
+
+
 def flashopt_sgd_step(descriptors, args: flashopt_sgd_args, workspace: torch.Tensor,
                       stream=None):
     """One fused FlashSGD step over a ctypes array of flashopt_tensor descriptors."""
@@ -297,7 +351,7 @@ def flashopt_sgd_step(descriptors, args: flashopt_sgd_args, workspace: torch.Ten
            "flashopt_sgd_step")
 
 
-class FlashSGD:
+class FlashSGD(_Stepper):
     """A list of TensorStates (momentum buffer only) stepped together by one
     launch per step."""
 
@@ -310,13 +364,10 @@ class FlashSGD:
         dev = self.states[0].param.device if self.states else "cuda"
         nbytes = max(16, flashopt_sgd_workspace_bytes(len(self.states)))
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        self.t = 0
-        self._grads = None
-        self._desc = None
+        self._init_common()
 
-    def step(self, grads, stream=None):
-        self.t += 1
-        if self._grads is None or any(a is not b for a, b in zip(self._grads, grads)):
-            self._desc = descriptor_array(self.states, grads)
-            self._grads = list(grads)
-        flashopt_sgd_step(self._desc, make_sgd_args(self.t, **self.hp), self.workspace, stream)
+    def _list_step(self, desc, t, stream):
+        flashopt_sgd_step(desc, make_sgd_args(t, **self.hp), self.workspace, stream)
+
+    def _tensor_step(self, desc, t, stream):
+        flashopt_sgd_step_tensor(desc, make_sgd_args(t, **self.hp), stream)

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FLASHOPT_ABI_VERSION 3
+#define FLASHOPT_ABI_VERSION 4
 
 typedef enum {
     FLASHOPT_OK = 0,
@@ -222,6 +222,21 @@ flashopt_status flashopt_sgd_step(const flashopt_tensor *tensors, int n_tensors,
                                   const flashopt_sgd_args *args,
                                   void *workspace, size_t workspace_bytes,
                                   void *stream);
+
+/* One tensor's FlashAdamW / FlashSGD step without a workspace: the
+ * descriptor travels in the kernel arguments, so the call stages nothing and
+ * enqueues exactly one kernel.  Meant for launching each tensor's step as
+ * soon as its gradient is complete (gradient release: a post-accumulate-grad
+ * hook steps the parameter and frees its gradient, so a full set of
+ * gradients is never held; page "code/flashsim/flash_adamw_sim.py",
+ * bytes_per_param(gradient_release=True)).  Results are identical to the
+ * list forms for that tensor.
+ *   tensor  HOST pointer to one descriptor (read during the call only)
+ * Errors: as the list forms (EINVAL, EALIGN, EHIP; no EWORKSPACE). */
+flashopt_status flashopt_adamw_step_tensor(const flashopt_tensor *tensor,
+                                           const flashopt_adamw_args *args, void *stream);
+flashopt_status flashopt_sgd_step_tensor(const flashopt_tensor *tensor,
+                                         const flashopt_sgd_args *args, void *stream);
 
 /* Static string naming a status code. */
 const char *flashopt_status_str(flashopt_status status);

@@ -163,3 +163,25 @@ def test_sgd_step_validation(L):
                ws_bytes=0) == F.FLASHOPT_EWORKSPACE
     assert sgd([_tensor(m_codes=A16 + 8)], F.make_sgd_args(1), ws_bytes=0) == F.FLASHOPT_EALIGN
     assert F.flashopt_sgd_workspace_bytes(3) == F.flashopt_adamw_workspace_bytes(3)
+
+
+def test_single_tensor_validation(L):
+    """The workspace-free single-tensor entry points validate like the list
+    forms; an empty tensor is a no-op.  (No call here reaches a launch.)"""
+    st = L.flashopt_adamw_step_tensor
+    sg = L.flashopt_sgd_step_tensor
+    a, s = F.make_args(1), F.make_sgd_args(1)
+    assert st(None, ctypes.byref(a), None) == F.FLASHOPT_EINVAL
+    assert st(ctypes.byref(_tensor()), None, None) == F.FLASHOPT_EINVAL
+    assert st(ctypes.byref(_tensor(numel=0, param=None)), ctypes.byref(a), None) == F.FLASHOPT_OK
+    assert st(ctypes.byref(_tensor(numel=-1)), ctypes.byref(a), None) == F.FLASHOPT_EINVAL
+    assert st(ctypes.byref(_tensor(grad=None)), ctypes.byref(a), None) == F.FLASHOPT_EINVAL
+    assert st(ctypes.byref(_tensor(rho=A16 + 8)), ctypes.byref(a), None) == F.FLASHOPT_EALIGN
+    assert st(ctypes.byref(_tensor(numel=(1 << 41) + 1)), ctypes.byref(a), None) == F.FLASHOPT_EINVAL
+    bad = F.make_args(0)
+    assert st(ctypes.byref(_tensor()), ctypes.byref(bad), None) == F.FLASHOPT_EINVAL
+    assert sg(None, ctypes.byref(s), None) == F.FLASHOPT_EINVAL
+    assert sg(ctypes.byref(_tensor(numel=0, param=None)), ctypes.byref(s), None) == F.FLASHOPT_OK
+    assert sg(ctypes.byref(_tensor(m_codes=A16 + 8)), ctypes.byref(s), None) == F.FLASHOPT_EALIGN
+    bad_s = F.make_sgd_args(1, momentum=0.0)
+    assert sg(ctypes.byref(_tensor()), ctypes.byref(bad_s), None) == F.FLASHOPT_EINVAL

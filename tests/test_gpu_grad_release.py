@@ -1,0 +1,114 @@
+"""Gradient release (page "code/flashsim/flash_adamw_sim.py",
+bytes_per_param(gradient_release=True): the gradient is not kept for a whole
+step): each tensor is stepped by its own launch as soon as its gradient is
+complete, then the gradient is freed.  The single-tensor entry points must
+give exactly the list step's results, and a bf16 model's backward with the
+hooks attached must free every gradient and leave exactly the state a list
+step gives with the same gradients (checked against the oracle too)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_companded_adam_amd import flashopt as F
+from bit_companded_adam_amd import workloads as W
+from tests._gpu import host, require_gpu, u16
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [1, 31, 33, 1000, 1024, 1025, 70001, 1 << 17]
+VARIANTS = [("adamw", 24, True), ("adamw", None, True), ("adamw", 24, False),
+            ("sgd", 24, True), ("sgd", 32, True), ("sgd", None, False)]
+
+
+def _make(kind, params, mb, qs):
+    if kind == "adamw":
+        return F.FlashAdamW(params, master_bits=mb, quantize_states=qs, **W.HP_DEFAULT)
+    return F.FlashSGD(params, master_bits=mb, quantize_states=qs, **W.SGD_DEFAULT)
+
+
+def _arrays(s: F.TensorState):
+    out = [s.param, s.rho, s.m_codes, s.m_scales, s.v_codes, s.v_scales]
+    return [None if t is None else host(t.view(torch.int16) if t.dtype == torch.bfloat16 else t)
+            for t in out]
+
+
+def _assert_same(a: F.TensorState, b: F.TensorState, label):
+    for x, y, name in zip(_arrays(a), _arrays(b), ("param", "rho", "m", "m_scales", "v", "v_scales")):
+        if x is None:
+            assert y is None
+            continue
+        assert x.tobytes() == y.tobytes(), f"{label}: {name}"
+
+
+@pytest.mark.parametrize("kind,mb,qs", VARIANTS, ids=[f"{k}-mb{m}-{'q' if q else 'f32'}" for k, m, q in VARIANTS])
+def test_tensor_step_equals_list_step(kind, mb, qs):
+    require_gpu()
+    pa = [W.init_param(n, device="cuda", seed=300 + i) for i, n in enumerate(RAGGED)]
+    pb = [p.clone() for p in pa]
+    a, b = _make(kind, pa, mb, qs), _make(kind, pb, mb, qs)
+    for t in range(1, 4):
+        grads = [W.make_grad(n, t, device="cuda", stream_id=i, factor=float(np.exp(i - 4)))
+                 for i, n in enumerate(RAGGED)]
+        for i, g in enumerate(grads):
+            a.step_tensor(i, g)
+        b.step(grads)
+        torch.cuda.synchronize()
+        for i, (sa, sb) in enumerate(zip(a.states, b.states)):
+            _assert_same(sa, sb, f"{kind} t{t} tensor{i}")
+
+
+def _mlp(seed):
+    torch.manual_seed(seed)
+    m = torch.nn.Sequential(torch.nn.Linear(192, 384), torch.nn.GELU(),
+                            torch.nn.Linear(384, 1017), torch.nn.GELU(),
+                            torch.nn.Linear(1017, 64))
+    return m.to(device="cuda", dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("kind", ["adamw", "sgd"])
+def test_hooks_free_gradients_and_match_list_step(orc, kind):
+    require_gpu()
+    model = _mlp(5)
+    params = list(model.parameters())
+    init = [p.detach().clone() for p in params]
+    opt = _make(kind, params, 24, True)
+    seen = {}
+
+    def record(p):
+        seen.setdefault(id(p), []).append(p.grad.detach().clone())
+
+    rec = [p.register_post_accumulate_grad_hook(record) for p in params]   # runs first
+    handles = F.attach_grad_release(opt, params)
+    ref = _make(kind, [q.clone() for q in init], 24, True)
+    gen = torch.Generator(device="cuda").manual_seed(17)
+    for step in range(3):
+        x = torch.randn(32, 192, device="cuda", generator=gen).to(torch.bfloat16)
+        model(x).float().square().mean().backward()
+        torch.cuda.synchronize()
+        assert all(p.grad is None for p in params), "gradients must be freed by the hooks"
+        grads = [seen[id(p)][step] for p in params]
+        ref.step(grads)
+        torch.cuda.synchronize()
+        for i, (sa, sb) in enumerate(zip(opt.states, ref.states)):
+            _assert_same(sa, sb, f"{kind} step {step} tensor {i}")
+    for h in handles + rec:
+        h.remove()
+    # the oracle agrees with the hook-driven result for one tensor, replayed
+    i = 2
+    st = oracle.State.zeros_like_param(u16(init[i]), 24)
+    if kind == "sgd":
+        st.v_codes = st.v_scales = None
+    for step in range(3):
+        g = u16(seen[id(params[i])][step])
+        if kind == "adamw":
+            orc.adamw_step(st, g, orc.hparams(lr=W.HP_DEFAULT["lr"], betas=W.HP_DEFAULT["betas"],
+                                              eps=W.HP_DEFAULT["eps"], step=step + 1,
+                                              weight_decay=W.HP_DEFAULT["weight_decay"]))
+        else:
+            hp = W.SGD_DEFAULT
+            orc.sgd_step(st, g, orc.sgd_hparams(lr=hp["lr"], momentum=hp["momentum"],
+                                                weight_decay=hp["weight_decay"], step=step + 1))
+    assert (u16(opt.states[i].param) == st.param).all()
+    assert (host(opt.states[i].rho) == st.rho).all()
+    assert (host(opt.states[i].m_codes) == st.m_codes).all()
