@@ -136,6 +136,7 @@ flashopt_status adamw_scalars(const flashopt_adamw_args *a, StepScalars &sc)
     sc.c2 = static_cast<float>(1.0 - a->beta2);
     sc.alpha = static_cast<float>(a->lr / bc1);
     sc.k2 = static_cast<float>(1.0 / std::sqrt(bc2));
+    sc.k2s = sc.k2 * 0x1p-32f;
     sc.eps = static_cast<float>(a->eps);
     // The kernel's short division is exact for denominators sqrt(v) k2 + eps in
     // [2^-100, 2^100]; sqrt(v) < 2^32 on its fast path.

@@ -43,6 +43,7 @@ struct StepScalars {
     float c2;     // 1 - beta2
     float alpha;  // lr / (1 - beta1^t)
     float k2;     // 1 / sqrt(1 - beta2^t)
+    float k2s;    // k2 2^-32 (exact): the factor for sqrt(v) 2^32
     float eps;
     float num_max; // 2^100 eps: numerators up to this stay in the short division's domain
     int fast_div;  // 1 when every denominator lies in [2^-100, 2^100] (eps >= 2^-100, k2 <= 2^60)

@@ -945,14 +945,17 @@ __device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
             if (j >= cnt) { m1[j] = 0.0f; v1[j] = 0.0f; }
     }
 
-    // ---- sqrt(v1)
+    // ---- rt = sqrt(v1) 2^32.  Every use of rt takes the factor back in an
+    // exact power-of-two scaling of its other operand (k2 2^-32 in the
+    // denominator; the variance group maximum and divisor), so each rounded
+    // result is the one sqrt(v1) itself would give.
     float rt[N];
     if (vbits < kSqrtFastEnd) {
 #pragma unroll
-        for (int j = 0; j < N; ++j) rt[j] = math::sqrt_cr(v1[j]);
+        for (int j = 0; j < N; ++j) rt[j] = math::sqrt_cr_x2p32(v1[j]);
     } else {                                // rare: v outside the fast sqrt's range
 #pragma unroll
-        for (int j = 0; j < N; ++j) rt[j] = sqrtf(v1[j]);
+        for (int j = 0; j < N; ++j) rt[j] = sqrtf(v1[j]) * 0x1p32f;
     }
 
     // ---- unit maxima of |m1|, of what the variance quantizer sees, of sqrt(v1)
@@ -970,14 +973,14 @@ __device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
     // ---- the update theta (1 - lr wd) - (alpha m1) / (sqrt(v1) k2 + eps),
     // with the short division when the unit's numerators and denominators
     // lie in its exact domain (den <= den_hi, nonzero |num| >= tmin)
-    const float den_hi = rmax * sc.k2 + sc.eps;
+    const float den_hi = rmax * sc.k2s + sc.eps;
     const float tmin = fmaxf(0x1p-102f, den_hi * 0x1p-126f);
     const uint32_t tkey = (__float_as_uint(tmin) << 1) - 1u;
     uint32_t kmin = 0xFFFFFFFFu;          // min over nonzero |num| of its doubled pattern - 1
     float th1[N];
 #pragma unroll
     for (int j = 0; j < N; ++j) {
-        const float den = rt[j] * sc.k2 + sc.eps;
+        const float den = rt[j] * sc.k2s + sc.eps;
         const float num = sc.alpha * m1[j];
         th1[j] = thd[j] - math::div_markstein(num, den, math::recip_cr(den));
         const uint32_t key = (__float_as_uint(num) << 1) - 1u;
@@ -995,10 +998,17 @@ __device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
     GroupDiv gdm{1.0f, 1.0f};
     if constexpr (kQuant) {
         sm_out = f16_bits(group_max<32 / N>(am));
-        sv_out = f16_bits(group_max<32 / N>(av));
+        if constexpr (kComp) {
+            sv_out = f16_bits(group_max<32 / N>(av) * 0x1p-32f);
+            GroupDiv gdv = group_div(sv_out);
+            gdv.d *= 0x1p32f;                // rt / d = (rt 2^32) / (d 2^32), same rounding
+            gdv.r *= 0x1p-32f;
+            encode<kVSpec, N>(rt, gdv, vo);
+        } else {
+            sv_out = f16_bits(group_max<32 / N>(av));
+            encode<kVSpec, N>(v1, group_div(sv_out), vo);
+        }
         gdm = group_div(sm_out);
-        if constexpr (kComp) encode<kVSpec, N>(rt, group_div(sv_out), vo);
-        else encode<kVSpec, N>(v1, group_div(sv_out), vo);
     }
 
     // ---- momentum codes and the new parameter

@@ -90,19 +90,27 @@ __device__ __forceinline__ uint32_t code_s8_magic(float p)
     return __float_as_uint(c + 12582912.0f);
 }
 
-// Correctly rounded sqrt(x) for 0 <= x < 2^64.  The input is first scaled by
-// 2^64 (exact), which puts every denormal into the range where one residual
-// correction of x * rsq(x) is exact; the result is scaled back by 2^-32
-// (exact, sqrt results are normal).  rsq(0) = inf is clamped so that
-// sqrt(0) = 0.
-__device__ __forceinline__ float sqrt_cr(float x)
+// 2^32 times the correctly rounded sqrt(x), for 0 <= x < 2^64: the input is
+// scaled by 2^64 (exact), which puts every denormal into the range where one
+// residual correction of x * rsq(x) is exact, and sqrt(x 2^64) = sqrt(x) 2^32
+// exactly.  rsq(0) = inf is clamped so that the result for 0 is 0.  Callers
+// that can fold the factor 2^32 into later exact power-of-two scalings use
+// this form; sqrt_cr applies it.
+__device__ __forceinline__ float sqrt_cr_x2p32(float x)
 {
     const float xs = x * 0x1p64f;
     const float y = fminf(__builtin_amdgcn_rsqf(xs), 0x1.fffffep127f);
     const float s = xs * y;
     const float h = 0.5f * y;
     const float r = __builtin_fmaf(-s, s, xs);
-    return __builtin_fmaf(r, h, s) * 0x1p-32f;
+    return __builtin_fmaf(r, h, s);
+}
+
+// Correctly rounded sqrt(x) for 0 <= x < 2^64 (the scaling back by 2^-32 is
+// exact: the results are normal).
+__device__ __forceinline__ float sqrt_cr(float x)
+{
+    return sqrt_cr_x2p32(x) * 0x1p-32f;
 }
 
 // v_cvt_i32_f32: truncation toward zero, saturating, NaN -> 0.
