@@ -986,9 +986,11 @@ __device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
         const uint32_t key = (__float_as_uint(num) << 1) - 1u;
         kmin = key < kmin ? key : kmin;
     }
-    bool any_nan = false;
+    // NaN-propagating maximum (v_maximum3_f32): NaN iff some th1 is NaN
+    float tnan = th1[0];
 #pragma unroll
-    for (int j = 0; j < N; ++j) any_nan |= th1[j] != th1[j];
+    for (int j = 1; j < N; ++j) tnan = __builtin_elementwise_maximum(tnan, th1[j]);
+    const bool any_nan = tnan != tnan;
     const bool exact = sc.fast_div == 0 || vbits >= kSqrtFastEnd ||
                        !(sc.alpha * am <= sc.num_max) || kmin < tkey || any_nan;
 
