@@ -9,7 +9,8 @@ parameter bit-exact, codes (or the fp32 buffer) bit-exact.
     teacher-forced;
   * 2^20 params x 10 steps, teacher-forced and free-running;
   * non-finite gradients next to finite lanes (NaN matches any NaN);
-  * the 1.2B list on group-aligned samples in the benchmark's launch shape.
+  * the 1.2B and 8.0B lists on group-aligned samples in the benchmark's launch
+    shape.
 """
 import numpy as np
 import pytest
@@ -136,9 +137,12 @@ def test_non_finite_gradients(orc, mb, comp, qs):
         _compare(_snap(opt.states[0]), pre, f"non-finite t{t}", nan_ok=True)
 
 
-def test_decoder_1b_sampled(orc):
+def _sampled_parity(orc, shapes, label):
+    """Two steps over a whole decoder list in one list launch (the benchmark's
+    launch shape); the second step is checked against the oracle on
+    group-aligned samples of every tensor: its first and last 2^16 elements
+    and two random 1024-element chunks."""
     require_gpu()
-    shapes = W.decoder_1b_shapes()
     params = [W.init_param(W.numel(s), device="cuda", seed=1000 + i) for i, (_, s) in enumerate(shapes)]
     opt = F.FlashSGD(params, **dict(HP, weight_decay=0.01))
     factors = W.grad_factors(len(shapes)).numpy()
@@ -162,4 +166,12 @@ def test_decoder_1b_sampled(orc):
     for i, (s, rr) in enumerate(zip(opt.states, ranges)):
         for (lo, hi), pre, g in zip(rr, pres[i], gs[i]):
             orc.sgd_step(pre, g, _orc_hp(2, dict(HP, weight_decay=0.01), 24, True, True))
-            _compare(_snap(s, lo, hi), pre, f"1.2B tensor {i} [{lo}, {hi})")
+            _compare(_snap(s, lo, hi), pre, f"{label} tensor {i} [{lo}, {hi})")
+
+
+def test_decoder_1b_sampled(orc):
+    _sampled_parity(orc, W.decoder_1b_shapes(), "1.2B")
+
+
+def test_decoder_8b_sampled(orc):
+    _sampled_parity(orc, W.decoder_8b_shapes(), "8.0B")
