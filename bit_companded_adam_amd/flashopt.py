@@ -270,15 +270,23 @@ class _Stepper:
     def _init_common(self):
         self.t = 0
         self.ts = [0] * len(self.states)
-        self._grads = None
+        self._key = None
         self._desc = None
 
     def step(self, grads, stream=None):
+        """One launch over every tensor; grads[i] is the bf16 gradient of
+        tensor i.  The descriptor table is rebuilt (and the grads validated)
+        whenever a grad's address, size, dtype, device or contiguity differs
+        from the previous step's; no reference to the grads is kept."""
+        grads = list(grads)
+        if len(grads) != len(self.states):
+            raise ValueError(f"{len(grads)} gradients for {len(self.states)} parameters")
+        key = tuple((g.data_ptr(), g.numel(), g.dtype, g.device, g.is_contiguous()) for g in grads)
+        if key != self._key:
+            self._desc = descriptor_array(self.states, grads)
+            self._key = key
         self.t += 1
         self.ts = [self.t] * len(self.states)
-        if self._grads is None or any(a is not b for a, b in zip(self._grads, grads)):
-            self._desc = descriptor_array(self.states, grads)
-            self._grads = list(grads)
         self._list_step(self._desc, self.t, stream)
 
     def step_tensor(self, i: int, grad: torch.Tensor, stream=None):

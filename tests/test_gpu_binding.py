@@ -1,0 +1,86 @@
+"""The Python binding's step driver on the GPU: the descriptor table it caches
+between list steps is rebuilt whenever a gradient's storage changes, the
+gradients are validated before anything is launched, and no reference to
+them outlives the call."""
+import gc
+import weakref
+
+import pytest
+import torch
+
+from bit_companded_adam_amd import flashopt as F
+from bit_companded_adam_amd import workloads as W
+from tests._gpu import require_gpu, u16
+
+pytestmark = pytest.mark.gpu
+
+HP = dict(lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01)
+SIZES = [4096 + 5, 1 << 15]
+
+
+def _params(seed):
+    return [W.init_param(n, device="cuda", seed=seed + i) for i, n in enumerate(SIZES)]
+
+
+def _grads(t):
+    return [W.make_grad(n, t, device="cuda", stream_id=i) for i, n in enumerate(SIZES)]
+
+
+def _state_bits(opt):
+    out = []
+    for s in opt.states:
+        out += [u16(s.param), s.rho.cpu().numpy(), s.m_codes.cpu().numpy(), u16(s.m_scales),
+                s.v_codes.cpu().numpy(), u16(s.v_scales)]
+    return out
+
+
+def test_new_gradient_tensors_rebuild_the_table():
+    """Step 2 with freshly allocated gradients gives the same bits as step 2
+    with the step-1 tensors refilled in place (whose cached table stays
+    valid)."""
+    require_gpu()
+    fresh = F.FlashAdamW(_params(10), **HP)
+    inplace = F.FlashAdamW(_params(10), **HP)
+    g1 = _grads(1)
+    fresh.step(g1)
+    keep = [g.clone() for g in g1]
+    inplace.step(keep)
+    g2 = _grads(2)
+    fresh.step(g2)                       # new storage: the table is rebuilt
+    for k, g in zip(keep, g2):
+        k.copy_(g)                       # same storage, new values
+    inplace.step(keep)
+    torch.cuda.synchronize()
+    for a, b in zip(_state_bits(fresh), _state_bits(inplace)):
+        assert (a == b).all()
+
+
+def test_gradient_count_and_layout_are_checked_before_launch():
+    require_gpu()
+    opt = F.FlashAdamW(_params(20), **HP)
+    g = _grads(1)
+    with pytest.raises(ValueError):
+        opt.step(g[:1])
+    assert opt.t == 0
+    opt.step(g)
+    # the same storage, size and dtype seen as a non-contiguous view
+    side = 64
+    p2 = W.init_param(side * side, device="cuda", seed=30)
+    opt2 = F.FlashAdamW([p2], **HP)
+    g2 = W.make_grad(side * side, 1, device="cuda").view(side, side)
+    opt2.step([g2.reshape(-1)])
+    with pytest.raises(ValueError):
+        opt2.step([g2.t()])
+    assert opt2.t == 1
+
+
+def test_gradients_are_not_kept_alive():
+    require_gpu()
+    opt = F.FlashSGD(_params(40), lr=1e-2, momentum=0.9)
+    g = _grads(1)
+    refs = [weakref.ref(x) for x in g]
+    opt.step(g)
+    torch.cuda.synchronize()
+    del g
+    gc.collect()
+    assert all(r() is None for r in refs)
