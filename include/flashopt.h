@@ -16,6 +16,8 @@
  *     flashopt_adamw_step).
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *     default stream).  Results are visible after the stream is synchronized.
+ *     The stream and every buffer belong to the calling thread's current HIP
+ *     device (hipSetDevice); calls from several threads are safe.
  *   - Arguments are validated on the host before anything is enqueued; a
  *     status other than FLASHOPT_OK means nothing was launched.  Faults inside
  *     a kernel surface at the caller's next synchronization.
