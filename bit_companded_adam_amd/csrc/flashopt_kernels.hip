@@ -482,6 +482,27 @@ __device__ __forceinline__ void encode_s8_finite(const float (&a)[N], const Grou
     }
 }
 
+// Companded momentum codes of N finite values of one group through
+// softsign_code_fast; a lane with a value near a code's rounding boundary,
+// or with an infinite scale (d = 0), recomputes its codes with the correctly
+// rounded chain of encode_s8_finite.  Both give the same bits.
+template <int N>
+__device__ __forceinline__ void encode_s8_softsign_fast(const float (&a)[N], const GroupDiv &gd,
+                                                        uint32_t (&out)[N / 4])
+{
+    const float c0 = gd.d * math::kInv254;
+    float dev = 0.0f;
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) {
+        uint32_t b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b[i] = math::softsign_code_fast(a[4 * k + i], c0, dev);
+        out[k] = pack_bytes(static_cast<int32_t>(b[0]), static_cast<int32_t>(b[1]),
+                            static_cast<int32_t>(b[2]), static_cast<int32_t>(b[3]));
+    }
+    if (dev > math::kCodeTieGuard || gd.d == 0.0f) encode_s8_finite<true, N>(a, gd, out);
+}
+
 // ------------------------------------------------------- standalone codec
 
 template <unsigned SPEC>
@@ -1015,7 +1036,8 @@ __device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
 
     // ---- momentum codes and the new parameter
     if (!exact) {
-        if constexpr (kQuant) encode_s8_finite<kComp, N>(m1, gdm, mo);
+        if constexpr (kComp) encode_s8_softsign_fast<N>(m1, gdm, mo);
+        else if constexpr (kQuant) encode_s8_finite<false, N>(m1, gdm, mo);
         pack_theta<MB, false, N>(th1, po, ro);
     } else {
         // rare: a unit outside the short sequences' domains (tiny or huge
@@ -1121,7 +1143,10 @@ __device__ __forceinline__ void sgd_unit(const ChunkPtrs &c, int u, int lane,
         for (int j = 1; j < N; ++j) am = fmaxf(am, fabsf(b1[j]));
         sm_out = f16_bits(group_max<32 / N>(am));
         const GroupDiv gdm = group_div(sm_out);
-        if (!bad) encode_s8_finite<kComp, N>(b1, gdm, mo);
+        if (!bad) {
+            if constexpr (kComp) encode_s8_softsign_fast<N>(b1, gdm, mo);
+            else encode_s8_finite<false, N>(b1, gdm, mo);
+        }
         else encode<kMSpec, N>(b1, gdm, mo);
     }
     if (!bad) pack_theta<MB, false, N>(th1, po, ro);

@@ -14,7 +14,11 @@
 //   div_markstein  2^32 random pairs of its stated domain plus every divisor
 //                  significand at the domain's edges;
 //   code_s8_magic  every fp32 p (low byte == clamp(rint(p), -127, 127) as a
-//                  two's-complement byte, for non-NaN p).
+//                  two's-complement byte, for non-NaN p);
+//   softsign_code_fast  (not exact itself: guarded) 4095 fp16 divisors x
+//                  4096 dividends around each of the 127 code boundaries, and
+//                  2^18 random dividends each: no code it trusts differs from
+//                  the correctly rounded chain's (without the guard 414571 do).
 // Only fma, mul, add, v_rcp_f32 / v_rsq_f32 and integer ops are used, so the
 // results do not depend on the FP mode beyond round-to-nearest-even with
 // fp32 denormals kept.
@@ -88,6 +92,35 @@ __device__ __forceinline__ uint32_t code_s8_magic(float p)
 {
     const float c = __builtin_amdgcn_fmed3f(p, -127.0f, 127.0f);
     return __float_as_uint(c + 12582912.0f);
+}
+
+// 1/254 rounded to fp32 (relative error 2^-28).
+constexpr float kInv254 = 0x1.020408p-8f;
+
+// softsign_code_fast's result is trusted where its p lies at least 1e-4 from
+// a code's rounding boundary (dev <= kCodeTieGuard).
+constexpr float kCodeTieGuard = 0.5f - 1e-4f;
+
+// The companded int8 momentum code of m in a group with divisor d, without
+// the correctly rounded chain y = m / d, y'' = 2y / (1 + |y|), p = 127 y''.
+// In exact arithmetic p = 254 m / (d + |m|); here p = m rcp(t) with
+// t = fma(|m|, 1/254, c0) and c0 = d kInv254 (formed once per group).  The
+// relative error of this p is at most 5.1 units of 2^-24 (kInv254, c0, the
+// fma, v_rcp_f32's one ulp and the product), that of the correctly rounded
+// chain's at most 4 units (four roundings, none amplified: d y''/dy y / y''
+// <= 1), so the two differ by less than 9.1 2^-24 127.5 < 7e-5 wherever a
+// code can depend on it (|p| <= 127.5).  Returns the magic sum of the
+// clamped p, as code_s8_magic (low byte = the code), and raises dev to the
+// distance |p - rint(p)|: where dev <= kCodeTieGuard the code equals the
+// correctly rounded chain's.  Finite m and positive finite d only.
+__device__ __forceinline__ uint32_t softsign_code_fast(float m, float c0, float &dev)
+{
+    const float t = __builtin_fmaf(fabsf(m), kInv254, c0);
+    const float p = m * __builtin_amdgcn_rcpf(t);
+    const float c = __builtin_amdgcn_fmed3f(p, -127.0f, 127.0f);
+    const float s = c + 12582912.0f;
+    dev = fmaxf(dev, fabsf(c - (s - 12582912.0f)));
+    return __float_as_uint(s);
 }
 
 // 2^32 times the correctly rounded sqrt(x), for 0 <= x < 2^64: the input is

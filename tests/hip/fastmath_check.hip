@@ -152,6 +152,55 @@ __global__ void k_magic_code(unsigned long long *bad)
     flush(bad, c);
 }
 
+// Group divisors for the code check: every positive fp16 subnormal and every
+// fp16 significand at three exponents (2^-10, 2^0, 2^14): 4095 values.
+__device__ __forceinline__ float code_divisor(uint32_t i)
+{
+    if (i < 1023u) return (float)__builtin_bit_cast(_Float16, (unsigned short)(i + 1u));
+    const uint32_t j = i - 1023u;
+    const uint32_t e = (j >> 10) == 0 ? 5u : ((j >> 10) == 1 ? 15u : 29u);   // fp16 exponent field
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)((e << 10) | (j & 1023u)));
+}
+
+// The correctly rounded chain's code (encode_s8_finite's sequence).
+__device__ __forceinline__ int exact_code(float m, float d)
+{
+    const float y = softsign(div_by_recip(m, d, recip_cr(d)));
+    return (int)(int8_t)(code_s8_magic(y * 127.0f) & 0xFFu);
+}
+
+// softsign_code_fast against the exact chain wherever its guard trusts it
+// (GUARDED), or everywhere (to show that the sweep reaches inputs where the
+// unguarded codes differ): for every divisor, 2 x 2048 dividends around each
+// of the 127 positive rounding boundaries p = k + 1/2 (the map is odd), then
+// 2^18 hashed dividends over [-1.5 d, 1.5 d].
+template <bool GUARDED>
+__global__ void k_softsign_code(unsigned long long *bad)
+{
+    constexpr uint64_t kW = 2048, kTies = 4095ull * 127ull * 2ull * kW, kRand = 4095ull << 18;
+    unsigned long long c = 0;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < kTies + kRand;
+         i += (uint64_t)gridDim.x * blockDim.x) {
+        float d, m;
+        if (i < kTies) {
+            d = code_divisor((uint32_t)(i / (127ull * 2ull * kW)));
+            const double pk = (double)((i / (2ull * kW)) % 127ull) + 0.5;
+            const float ms = (float)(pk * (double)d / (254.0 - pk));     // p(ms) = k + 1/2
+            m = __uint_as_float(__float_as_uint(ms) + (uint32_t)(i % (2ull * kW)) - (uint32_t)kW);
+        } else {
+            const uint64_t j = i - kTies;
+            d = code_divisor((uint32_t)(j >> 18));
+            uint32_t h = (uint32_t)j * 2654435761u;
+            h ^= h >> 15; h *= 2246822519u; h ^= h >> 13;
+            m = d * ((float)(h >> 8) * 0x1p-24f * 3.0f - 1.5f);
+        }
+        float dev = 0.0f;
+        const uint32_t s = softsign_code_fast(m, d * kInv254, dev);
+        if (!GUARDED || dev <= kCodeTieGuard) c += (int)(int8_t)(s & 0xFFu) != exact_code(m, d);
+    }
+    flush(bad, c);
+}
+
 template <typename K>
 long long run(K kernel, unsigned grid)
 {
@@ -175,4 +224,6 @@ long long fastmath_check_softsign(void) { return run(k_softsign, 65536); }
 long long fastmath_check_cvt_pk_u8(void) { return run(k_cvt_pk_u8, 65536); }
 long long fastmath_check_div_markstein(void) { return run(k_div_markstein, 65536); }
 long long fastmath_check_magic_code(void) { return run(k_magic_code, 65536); }
+long long fastmath_check_softsign_code(void) { return run(k_softsign_code<true>, 65536); }
+long long fastmath_softsign_code_unguarded(void) { return run(k_softsign_code<false>, 65536); }
 }

@@ -7,7 +7,8 @@ value; division by an fp16 scale over every divisor x dividend significand
 pair (2^33); softsign over every |y| <= 1.5; v_cvt_pk_u8_f32 and the
 magic-number int8 code rounding over all 2^32 patterns; the update division over 2^32
 random pairs of its stated domain and every divisor significand at the
-domain's edges."""
+domain's edges; the guarded companded momentum code against the correctly
+rounded chain around every rounding boundary for 4095 fp16 divisors."""
 import ctypes
 import os
 
@@ -18,7 +19,8 @@ from tests._gpu import require_gpu
 pytestmark = pytest.mark.gpu
 
 LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hip", "libfastmath_check.so")
-CHECKS = ["sqrt", "recip", "div_by_recip", "softsign", "cvt_pk_u8", "div_markstein", "magic_code"]
+CHECKS = ["sqrt", "recip", "div_by_recip", "softsign", "cvt_pk_u8", "div_markstein", "magic_code",
+          "softsign_code"]
 
 
 @pytest.fixture(scope="module")
@@ -37,3 +39,13 @@ def test_exact(lib, check):
     bad = getattr(lib, "fastmath_check_" + check)()
     print(f"fastmath {check}: {bad} mismatches", flush=True)
     assert bad == 0
+
+
+def test_softsign_code_sweep_is_sensitive(lib):
+    """Without its guard, softsign_code_fast disagrees with the correctly
+    rounded chain on some of the swept inputs: the sweep reaches the
+    boundaries where the guard matters."""
+    lib.fastmath_softsign_code_unguarded.restype = ctypes.c_longlong
+    diff = lib.fastmath_softsign_code_unguarded()
+    print(f"unguarded softsign_code: {diff} disagreements", flush=True)
+    assert diff > 0
