@@ -139,8 +139,10 @@ flashopt_status adamw_scalars(const flashopt_adamw_args *a, StepScalars &sc)
     sc.k2s = sc.k2 * 0x1p-32f;
     sc.eps = static_cast<float>(a->eps);
     // The kernel's short division is exact for denominators sqrt(v) k2 + eps in
-    // [2^-100, 2^100]; sqrt(v) < 2^32 on its fast path.
-    sc.fast_div = (sc.eps >= 0x1p-100f && sc.k2 <= 0x1p60f) ? 1 : 0;
+    // [2^-100, 2^100]; sqrt(v) < 2^32 on its fast path.  Its short sqrt gives
+    // 2^-95 for v = 0, which adds nothing to eps while k2 <= eps 2^70.
+    sc.fast_div = (sc.eps >= 0x1p-100f && sc.k2 <= 0x1p60f &&
+                   static_cast<double>(sc.k2) <= static_cast<double>(sc.eps) * 0x1p70) ? 1 : 0;
     sc.num_max = sc.fast_div ? sc.eps * 0x1p100f : 0.0f;
     return FLASHOPT_OK;
 }

@@ -971,9 +971,9 @@ __device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
     // denominator; the variance group maximum and divisor), so each rounded
     // result is the one sqrt(v1) itself would give.
     float rt[N];
-    if (vbits < kSqrtFastEnd) {
+    if (vbits < kSqrtFastEnd) {             // (v1 = 0 gives rt = 2^-63, absorbed downstream)
 #pragma unroll
-        for (int j = 0; j < N; ++j) rt[j] = math::sqrt_cr_x2p32(v1[j]);
+        for (int j = 0; j < N; ++j) rt[j] = math::sqrt_x2p32_zero_tiny(v1[j]);
     } else {                                // rare: v outside the fast sqrt's range
 #pragma unroll
         for (int j = 0; j < N; ++j) rt[j] = sqrtf(v1[j]) * 0x1p32f;

@@ -8,7 +8,7 @@
 //   div_by_recip   every fp16 divisor significand x every fp32 dividend
 //                  significand (2^33 pairs);
 //   softsign       every y in [-1.5, 1.5];
-//   sqrt_cr        every x in [0, 2^64);
+//   sqrt_cr        every x in [0, 2^64) (and sqrt_x2p32_zero_tiny against it);
 //   byte_u8        every fp32 pattern (v_cvt_pk_u8_f32 == clamp(rint(x), 0, 255),
 //                  NaN -> 0);
 //   div_markstein  2^32 random pairs of its stated domain plus every divisor
@@ -133,6 +133,23 @@ __device__ __forceinline__ float sqrt_cr_x2p32(float x)
 {
     const float xs = x * 0x1p64f;
     const float y = fminf(__builtin_amdgcn_rsqf(xs), 0x1.fffffep127f);
+    const float s = xs * y;
+    const float h = 0.5f * y;
+    const float r = __builtin_fmaf(-s, s, xs);
+    return __builtin_fmaf(r, h, s);
+}
+
+// sqrt_cr_x2p32 without the clamp, for the step: the input is scaled as
+// fma(x, 2^64, 2^-126).  For every x > 0 the added 2^-126 vanishes (x 2^64 >=
+// 2^-85, whose half ulp is 2^-109), so the result is sqrt_cr_x2p32(x); at
+// x = 0 it keeps rsq finite and the result is 2^-63 instead of 0.  A caller
+// has to absorb that value: in the step it adds at most k2 2^-95 to
+// eps, which leaves eps unchanged while k2 <= eps 2^70, and its variance
+// code and group scale round to 0 as for 0.
+__device__ __forceinline__ float sqrt_x2p32_zero_tiny(float x)
+{
+    const float xs = __builtin_fmaf(x, 0x1p64f, 0x1p-126f);
+    const float y = __builtin_amdgcn_rsqf(xs);
     const float s = xs * y;
     const float h = 0.5f * y;
     const float r = __builtin_fmaf(-s, s, xs);

@@ -28,6 +28,7 @@ __global__ void k_sqrt(unsigned long long *bad)
          i += (uint64_t)gridDim.x * blockDim.x) {
         const float x = __uint_as_float((uint32_t)i);
         c += !same(sqrt_cr(x), sqrtf(x));
+        c += !same(sqrt_x2p32_zero_tiny(x), i == 0 ? 0x1p-63f : sqrt_cr_x2p32(x));
     }
     flush(bad, c);
 }
