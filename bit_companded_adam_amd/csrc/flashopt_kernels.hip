@@ -223,14 +223,6 @@ __device__ __forceinline__ float reconstruct_elem(uint32_t hi_shifted, int32_t r
     return __uint_as_float(hi_shifted + add);
 }
 
-// The number of this lane's elements that exist: 16, a partial count at a
-// ragged end, or 0 past it.
-__device__ __forceinline__ int lane_count(int64_t n, int64_t e0)
-{
-    const int64_t rem = n - e0;
-    return rem >= kLaneElems ? kLaneElems : (rem > 0 ? static_cast<int>(rem) : 0);
-}
-
 // Global-address-space views: loads and stores become global_* with an
 // SGPR base and a 32-bit lane offset instead of flat accesses.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -248,16 +240,6 @@ typedef __attribute__((address_space(1))) u32x2 g_u2;
 typedef __attribute__((address_space(1))) const uint32_t g_cu32;
 typedef __attribute__((address_space(1))) uint32_t g_u32;
 
-__device__ __forceinline__ uint4 ld16(const void *p, int k = 0)
-{
-    const u32x4 v = ((g_cu4 *)p)[k];
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ void st16(void *p, uint4 v, int k = 0)
-{
-    const u32x4 w = {v.x, v.y, v.z, v.w};
-    ((g_u4 *)p)[k] = w;
-}
 // Streaming (nontemporal) 16-byte accesses: the step touches every byte once.
 __device__ __forceinline__ uint4 ld16s(const void *p, int k = 0)
 {
@@ -276,94 +258,6 @@ __device__ __forceinline__ uint32_t ld4s(const void *p) { return __builtin_nonte
 __device__ __forceinline__ void st4s(void *p, uint32_t v) { __builtin_nontemporal_store(v, (g_u32 *)p); }
 __device__ __forceinline__ uint16_t ld_u16(const uint16_t *p) { return *(g_cu16 *)p; }
 __device__ __forceinline__ void st_u16(uint16_t *p, uint16_t v) { *(g_u16 *)p = v; }
-
-// 16 consecutive 16-bit elements -> 8 words (zero past cnt)
-__device__ __forceinline__ void load_u16x16(const uint16_t *p, int cnt, uint32_t (&w)[8])
-{
-    if (cnt == kLaneElems) {
-        const uint4 a = ld16(p, 0);
-        const uint4 b = ld16(p, 1);
-        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = 0u;
-#pragma unroll
-        for (int j = 0; j < kLaneElems; ++j)
-            if (j < cnt) w[j >> 1] |= static_cast<uint32_t>(((g_cu16 *)p)[j]) << (16 * (j & 1));
-    }
-}
-
-__device__ __forceinline__ void store_u16x16(uint16_t *p, int cnt, const uint32_t (&w)[8])
-{
-    if (cnt == kLaneElems) {
-        st16(p, make_uint4(w[0], w[1], w[2], w[3]), 0);
-        st16(p, make_uint4(w[4], w[5], w[6], w[7]), 1);
-    } else {
-#pragma unroll
-        for (int j = 0; j < kLaneElems; ++j)
-            if (j < cnt) ((g_u16 *)p)[j] = static_cast<uint16_t>(w[j >> 1] >> (16 * (j & 1)));
-    }
-}
-
-// 16 consecutive bytes -> 4 words (zero past cnt)
-__device__ __forceinline__ void load_u8x16(const void *p, int cnt, uint32_t (&w)[4])
-{
-    if (cnt == kLaneElems) {
-        const uint4 a = ld16(p);
-        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = 0u;
-#pragma unroll
-        for (int j = 0; j < kLaneElems; ++j)
-            if (j < cnt) w[j >> 2] |= static_cast<uint32_t>(((g_cu8 *)p)[j]) << (8 * (j & 3));
-    }
-}
-
-__device__ __forceinline__ void store_u8x16(void *p, int cnt, const uint32_t (&w)[4])
-{
-    if (cnt == kLaneElems) {
-        st16(p, make_uint4(w[0], w[1], w[2], w[3]));
-    } else {
-#pragma unroll
-        for (int j = 0; j < kLaneElems; ++j)
-            if (j < cnt) ((g_u8 *)p)[j] = static_cast<uint8_t>(w[j >> 2] >> (8 * (j & 3)));
-    }
-}
-
-// 16 consecutive fp32 (zero past cnt)
-__device__ __forceinline__ void load_f32x16(const float *p, int cnt, float (&x)[16])
-{
-    if (cnt == kLaneElems) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint4 v = ld16(p, k);
-            x[4 * k + 0] = __uint_as_float(v.x); x[4 * k + 1] = __uint_as_float(v.y);
-            x[4 * k + 2] = __uint_as_float(v.z); x[4 * k + 3] = __uint_as_float(v.w);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < kLaneElems; ++j) x[j] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < kLaneElems; ++j)
-            if (j < cnt) x[j] = ((g_cf32 *)p)[j];
-    }
-}
-
-__device__ __forceinline__ void store_f32x16(float *p, int cnt, const float (&x)[16])
-{
-    if (cnt == kLaneElems) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            st16(p, make_uint4(__float_as_uint(x[4 * k]), __float_as_uint(x[4 * k + 1]),
-                               __float_as_uint(x[4 * k + 2]), __float_as_uint(x[4 * k + 3])), k);
-    } else {
-#pragma unroll
-        for (int j = 0; j < kLaneElems; ++j)
-            if (j < cnt) ((g_f32 *)p)[j] = x[j];
-    }
-}
 
 // Codes of N values y_j = a_j / d of one group under SPEC, packed four to a
 // word.
@@ -505,43 +399,82 @@ __device__ __forceinline__ void encode_s8_softsign_fast(const float (&a)[N], con
 
 // ------------------------------------------------------- standalone codec
 
+// Element offset of unit u (0..3) of the calling lane in its wavefront's
+// 1024-element chunk: 4 consecutive elements, the 64 lanes of a unit covering
+// 256 consecutive elements, so that every access instruction of the
+// wavefront touches one contiguous block of each stream.  The codec
+// and split kernels use it (16 bytes of fp32 per lane and unit).
+__device__ __forceinline__ int64_t quad_first(int u)
+{
+    const int64_t chunk =
+        (static_cast<int64_t>(blockIdx.x) * (kBlockThreads / kWaveLanes) + (threadIdx.x >> 6)) *
+        kChunkElems;
+    return chunk + 256 * u + 4 * static_cast<int>(threadIdx.x & 63u);
+}
+
+__device__ __forceinline__ int quad_count(int64_t n, int64_t e)
+{
+    const int64_t r = n - e;
+    return r >= 4 ? 4 : (r > 0 ? static_cast<int>(r) : 0);
+}
+
 template <unsigned SPEC>
 __global__ void __launch_bounds__(kBlockThreads)
 quantize_kernel(const float *__restrict__ x, int64_t n, void *__restrict__ codes,
                 uint16_t *__restrict__ scales)
 {
     constexpr bool kSigned = (SPEC & FLASHOPT_Q_SIGNED) != 0;
-    const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * kBlockThreads + threadIdx.x) * kLaneElems;
-    const int cnt = lane_count(n, e0);
-
-    float a[16];
-    load_f32x16(x + e0, cnt, a);             // missing elements are the zero pad
-    if (SPEC & FLASHOPT_Q_SQRT) {
-        uint32_t ubits = 0u;
+    uint8_t *cb = static_cast<uint8_t *>(codes);
+    // every lane runs every unit (the group maximum exchanges values between
+    // lanes); elements past n are the zero pad
 #pragma unroll
-        for (int j = 0; j < 16; ++j) ubits = max(ubits, __float_as_uint(a[j]));
+    for (int u = 0; u < 4; ++u) {
+        const int64_t e = quad_first(u);
+        const int cnt = quad_count(n, e);
+        float a[4];
+        if (cnt == 4) {
+            const uint4 v = ld16s(x + e);
+            a[0] = __uint_as_float(v.x); a[1] = __uint_as_float(v.y);
+            a[2] = __uint_as_float(v.z); a[3] = __uint_as_float(v.w);
+        } else {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) a[j] = math::sqrt_cr(a[j]);
-        if (ubits >= kSqrtFastEnd) {         // rare: inputs outside the fast sqrt's range
+            for (int j = 0; j < 4; ++j) a[j] = j < cnt ? ((g_cf32 *)(x + e))[j] : 0.0f;
+        }
+        if (SPEC & FLASHOPT_Q_SQRT) {
+            uint32_t ubits = 0u;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                float v = 0.0f;
-                if (j < cnt) v = ((g_cf32 *)(x + e0))[j];
-                a[j] = sqrtf(v);
+            for (int j = 0; j < 4; ++j) ubits = max(ubits, __float_as_uint(a[j]));
+            if (ubits < kSqrtFastEnd) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) a[j] = math::sqrt_cr(a[j]);
+            } else {                         // rare: inputs outside the fast sqrt's range
+#pragma unroll
+                for (int j = 0; j < 4; ++j) a[j] = sqrtf(a[j]);
             }
         }
-    }
-    // maxNum over the elements: NaNs are ignored unless all are NaN
-    float amax = kSigned ? fabsf(a[0]) : a[0];
+        // maxNum over the group's elements: NaNs are ignored unless all are NaN
+        float amax = kSigned ? fabsf(a[0]) : a[0];
 #pragma unroll
-    for (int j = 1; j < 16; ++j) amax = fmaxf(amax, kSigned ? fabsf(a[j]) : a[j]);
-    amax = group_max<2>(amax);
-    const uint32_t s = f16_bits(amax);
-
-    uint32_t out[4];
-    encode<SPEC, 16>(a, group_div(s), out);
-    store_u8x16(static_cast<uint8_t *>(codes) + e0, cnt, out);
-    if ((threadIdx.x & 1) == 0 && cnt > 0) st_u16(scales + e0 / kGroup, static_cast<uint16_t>(s));
+        for (int j = 1; j < 4; ++j) amax = fmaxf(amax, kSigned ? fabsf(a[j]) : a[j]);
+        amax = group_max<8>(amax);
+        const uint32_t s = f16_bits(amax);
+        uint32_t w[1];
+        const GroupDiv gd = group_div(s);
+        if constexpr (SPEC == FLASHOPT_SPEC_MOMENTUM) {
+            // finite values take the guarded short code sequence
+            bool finite = true;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) finite &= fabsf(a[j]) <= 0x1.fffffep127f;
+            if (finite) encode_s8_softsign_fast<4>(a, gd, w);
+            else encode<SPEC, 4>(a, gd, w);
+        } else {
+            encode<SPEC, 4>(a, gd, w);
+        }
+        if (cnt == 4) st4s(cb + e, w[0]);
+        else
+            for (int j = 0; j < cnt; ++j) ((g_u8 *)(cb + e))[j] = static_cast<uint8_t>(w[0] >> (8 * j));
+        if ((threadIdx.x & 7u) == 0 && cnt > 0) st_u16(scales + e / kGroup, static_cast<uint16_t>(s));
+    }
 }
 
 template <unsigned SPEC>
@@ -553,20 +486,29 @@ dequantize_kernel(const void *__restrict__ codes, const uint16_t *__restrict__ s
     unit[threadIdx.x] = dequant_unit<SPEC>(static_cast<int>(threadIdx.x));
     __syncthreads();
 
-    const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * kBlockThreads + threadIdx.x) * kLaneElems;
-    const int cnt = lane_count(n, e0);
-    if (cnt == 0) return;
-    uint32_t w[4];
-    load_u8x16(static_cast<const uint8_t *>(codes) + e0, cnt, w);
-    const float s = f16_value(ld_u16(scales + e0 / kGroup));
-    float o[16];
+    const uint8_t *cb = static_cast<const uint8_t *>(codes);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        float v = unit[ubyte(w, j)] * s;
-        if (SPEC & FLASHOPT_Q_SQRT) v = v * v;
-        o[j] = v;
+    for (int u = 0; u < 4; ++u) {
+        const int64_t e = quad_first(u);
+        const int cnt = quad_count(n, e);
+        if (cnt == 0) continue;
+        uint32_t w[1] = {0u};
+        if (cnt == 4) w[0] = ld4s(cb + e);
+        else
+            for (int j = 0; j < cnt; ++j) w[0] |= static_cast<uint32_t>(((g_cu8 *)(cb + e))[j]) << (8 * j);
+        const float s = f16_value(ld_u16(scales + e / kGroup));
+        float o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float v = unit[ubyte(w, j)] * s;
+            if (SPEC & FLASHOPT_Q_SQRT) v = v * v;
+            o[j] = v;
+        }
+        if (cnt == 4) st16s(out + e, make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]),
+                                                __float_as_uint(o[2]), __float_as_uint(o[3])));
+        else
+            for (int j = 0; j < cnt; ++j) ((g_f32 *)(out + e))[j] = o[j];
     }
-    store_f32x16(out + e0, cnt, o);
 }
 
 // ------------------------------------------------------- standalone split
@@ -576,20 +518,41 @@ __global__ void __launch_bounds__(kBlockThreads)
 split_kernel(const float *__restrict__ master, int64_t n, uint16_t *__restrict__ param,
              void *__restrict__ rho)
 {
-    const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * kBlockThreads + threadIdx.x) * kLaneElems;
-    const int cnt = lane_count(n, e0);
-    if (cnt == 0) return;
-    float x[16];
-    load_f32x16(master + e0, cnt, x);
-    uint32_t pw[8], rw[MB == 32 ? 8 : 4];
-    bool any_nan = false;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) any_nan |= x[j] != x[j];
-    if (any_nan) split_pack_exact<MB, 16>(x, pw, rw);
-    else split_pack<MB, 16>(x, pw, rw);
-    store_u16x16(param + e0, cnt, pw);
-    if constexpr (MB == 32) store_u16x16(static_cast<uint16_t *>(rho) + e0, cnt, rw);
-    else store_u8x16(static_cast<uint8_t *>(rho) + e0, cnt, rw);
+    for (int u = 0; u < 4; ++u) {
+        const int64_t e = quad_first(u);
+        const int cnt = quad_count(n, e);
+        if (cnt == 0) continue;
+        float x[4];
+        if (cnt == 4) {
+            const uint4 v = ld16s(master + e);
+            x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
+            x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = j < cnt ? ((g_cf32 *)(master + e))[j] : 0.0f;
+        }
+        uint32_t pw[2], rw[rho_words(MB, 4)];
+        bool any_nan = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) any_nan |= x[j] != x[j];
+        if (any_nan) split_pack_exact<MB, 4>(x, pw, rw);
+        else split_pack<MB, 4>(x, pw, rw);
+        if (cnt == 4) {
+            st8s(param + e, u32x2{pw[0], pw[1]});
+            if constexpr (MB == 32) st8s(static_cast<uint16_t *>(rho) + e, u32x2{rw[0], rw[1]});
+            else st4s(static_cast<uint8_t *>(rho) + e, rw[0]);
+        } else {
+            for (int j = 0; j < cnt; ++j) {
+                ((g_u16 *)(param + e))[j] = static_cast<uint16_t>(pw[j >> 1] >> (16 * (j & 1)));
+                if constexpr (MB == 32)
+                    ((g_u16 *)(static_cast<uint16_t *>(rho) + e))[j] =
+                        static_cast<uint16_t>(rw[j >> 1] >> (16 * (j & 1)));
+                else
+                    ((g_u8 *)(static_cast<uint8_t *>(rho) + e))[j] = static_cast<uint8_t>(rw[0] >> (8 * j));
+            }
+        }
+    }
 }
 
 template <int MB>
@@ -597,23 +560,46 @@ __global__ void __launch_bounds__(kBlockThreads)
 reconstruct_kernel(const uint16_t *__restrict__ param, const void *__restrict__ rho, int64_t n,
                    float *__restrict__ master)
 {
-    const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * kBlockThreads + threadIdx.x) * kLaneElems;
-    const int cnt = lane_count(n, e0);
-    if (cnt == 0) return;
-    uint32_t pw[8], rw[MB == 32 ? 8 : 4];
-    load_u16x16(param + e0, cnt, pw);
-    if constexpr (MB == 32) load_u16x16(static_cast<const uint16_t *>(rho) + e0, cnt, rw);
-    else load_u8x16(static_cast<const uint8_t *>(rho) + e0, cnt, rw);
-    float x[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const uint32_t hs = (j & 1) ? (pw[j >> 1] & 0xFFFF0000u) : (pw[j >> 1] << 16);
-        int32_t r;
-        if constexpr (MB == 32) r = shalf(rw, j);
-        else r = sbyte(rw, j);
-        x[j] = reconstruct_elem<MB>(hs, r);
+    for (int u = 0; u < 4; ++u) {
+        const int64_t e = quad_first(u);
+        const int cnt = quad_count(n, e);
+        if (cnt == 0) continue;
+        uint32_t pw[2] = {0u, 0u}, rw[MB == 32 ? 2 : 1] = {};
+        if (cnt == 4) {
+            const u32x2 p2 = ld8s(param + e);
+            pw[0] = p2.x; pw[1] = p2.y;
+            if constexpr (MB == 32) {
+                const u32x2 r2 = ld8s(static_cast<const uint16_t *>(rho) + e);
+                rw[0] = r2.x; rw[1] = r2.y;
+            } else {
+                rw[0] = ld4s(static_cast<const uint8_t *>(rho) + e);
+            }
+        } else {
+            for (int j = 0; j < cnt; ++j) {
+                pw[j >> 1] |= static_cast<uint32_t>(((g_cu16 *)(param + e))[j]) << (16 * (j & 1));
+                if constexpr (MB == 32)
+                    rw[j >> 1] |= static_cast<uint32_t>(((g_cu16 *)(static_cast<const uint16_t *>(rho) + e))[j])
+                                  << (16 * (j & 1));
+                else
+                    rw[0] |= static_cast<uint32_t>(((g_cu8 *)(static_cast<const uint8_t *>(rho) + e))[j])
+                             << (8 * j);
+            }
+        }
+        float x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t hs = (j & 1) ? (pw[j >> 1] & 0xFFFF0000u) : (pw[j >> 1] << 16);
+            int32_t r;
+            if constexpr (MB == 32) r = shalf(rw, j);
+            else r = sbyte(rw, j);
+            x[j] = reconstruct_elem<MB>(hs, r);
+        }
+        if (cnt == 4) st16s(master + e, make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]),
+                                                   __float_as_uint(x[2]), __float_as_uint(x[3])));
+        else
+            for (int j = 0; j < cnt; ++j) ((g_f32 *)(master + e))[j] = x[j];
     }
-    store_f32x16(master + e0, cnt, x);
 }
 
 // ---------------------------------------------------- fused FlashAdamW step
