@@ -14,6 +14,7 @@ Other configurations (reported beside the default, not as its value):
 codec ablation), --fp32-states (quantize_states=False), --optimizer sgd (the
 FlashSGD step: lr 1e-2, momentum 0.9, weight decay 0.01), --grad-release (one
 single-tensor launch per tensor, the gradient-release launch pattern).
+--codec times the codec and split entry points instead (one JSON line each).
 
 Prints one JSON line: Gparam/s over the K timed steps, the roofline of the
 step kernel (algorithmic bytes per param of the configuration against
@@ -224,6 +225,63 @@ def calibrate_copy(gib: float):
     print(json.dumps({"calibration_copy_bytes_read": n * 4, "calibration_copy_bytes_written": n * 4}))
 
 
+def bench_codec(n: int, reps: int, warmup: int):
+    """Per-launch time of flashopt_quantize / dequantize (both specs) and
+    flashopt_split / reconstruct (both widths) over one flat tensor of n
+    elements: fp32 N(0, 1e-3^2) values (their squares for the variance
+    spec).  Algorithmic bytes per element: quantize and dequantize 4 + 1 +
+    2/32; split and reconstruct 4 + 2 + 1 (24-bit) or 4 + 2 + 2 (32-bit)."""
+    g = torch.Generator(device="cuda").manual_seed(W.PARAM_SEED)
+    x = torch.randn(n, generator=g, device="cuda") * 1e-3
+    xa = x * x
+    codes = torch.empty(n, dtype=torch.int8, device="cuda")
+    scales = torch.empty(F.n_groups(n), dtype=torch.int16, device="cuda")
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    param = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    rho = {24: torch.empty(n, dtype=torch.int8, device="cuda"),
+           32: torch.empty(n, dtype=torch.int16, device="cuda")}
+    codec = 4 + 1 + 2 / 32
+    cases = [
+        ("flashopt_quantize", "momentum", codec,
+         lambda: F.flashopt_quantize(x, F.SPEC_MOMENTUM, codes, scales)),
+        ("flashopt_dequantize", "momentum", codec,
+         lambda: F.flashopt_dequantize(codes, scales, F.SPEC_MOMENTUM, out)),
+        ("flashopt_quantize", "variance", codec,
+         lambda: F.flashopt_quantize(xa, F.SPEC_VARIANCE, codes.view(torch.uint8), scales)),
+        ("flashopt_dequantize", "variance", codec,
+         lambda: F.flashopt_dequantize(codes.view(torch.uint8), scales, F.SPEC_VARIANCE, out)),
+        ("flashopt_split", "24-bit", 7.0, lambda: F.flashopt_split(x, 24, param, rho[24])),
+        ("flashopt_reconstruct", "24-bit", 7.0,
+         lambda: F.flashopt_reconstruct(param, rho[24], 24, out)),
+        ("flashopt_split", "32-bit", 8.0, lambda: F.flashopt_split(x, 32, param, rho[32])),
+        ("flashopt_reconstruct", "32-bit", 8.0,
+         lambda: F.flashopt_reconstruct(param, rho[32], 32, out)),
+    ]
+    stream = torch.cuda.current_stream()
+    for op, variant, bpe, fn in cases:
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        gbs = n * bpe / (ms * 1e-3) / 1e9
+        print(json.dumps({
+            "metric": f"{op} ({variant}) GB/s, 1 GPU", "value": gbs, "unit": "GB/s",
+            "n_gpus": 1, "steps": reps, "warmup": warmup, "ms_per_step": ms,
+            "higher_is_better": True, "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": f"flat tensor of {n} elements", "op": op, "variant": variant,
+                       "bytes_per_element": bpe},
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "traffic": None},
+        }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,6 +304,10 @@ def main():
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
                     help="only run one device copy of GIB GiB (for counter scaling) and exit")
     ap.add_argument("--no-copy-ref", action="store_true")
+    ap.add_argument("--codec", action="store_true",
+                    help="instead of the step, time the codec and split entry points on one "
+                         "flat tensor (one JSON line each)")
+    ap.add_argument("--codec-elems", type=int, default=1 << 29)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -258,6 +320,9 @@ def main():
 
     if args.calibrate_copy > 0:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.codec:
+        bench_codec(args.codec_elems, args.steps, args.warmup)
         return
 
     mb, comp, qs = args.master_bits, not args.linear, not args.fp32_states
