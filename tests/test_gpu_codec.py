@@ -77,6 +77,37 @@ def test_fp16_scale_rounding_boundaries(orc):
     _parity(orc, (-x).reshape(-1), F.SPEC_MOMENTUM, "fp16 boundaries (neg)")
 
 
+def test_momentum_codes_at_rounding_boundaries(orc):
+    """Momentum values placed around every code boundary: p = 127 softsign(m/d)
+    = k + 1/2 for k = 0..126, at fp32 offsets of 0..7 and 2^9..2^11 units from
+    the boundary on both sides, for 12 group scales.  Those near a boundary
+    take the short code sequence's correctly rounded fallback, the farther ones
+    its short path; both must give the oracle's codes."""
+    require_gpu()
+    scales = [1.0, 0.75, 1.4990234375, 1.0009765625, 2.0 ** -10 * 1.3330078125, 2.0 ** -14,
+              2.0 ** -20, 3.0 ** 5, 1000.5, 65504.0, 0.1000976562, 6.103515625e-05 * 1.5]
+    offsets = np.array([0, 1, 2, 3, 5, 7, 512, 1024, 2048], np.int64)
+    offsets = np.concatenate([-offsets[::-1], offsets[1:]])
+    rng = np.random.default_rng(21)
+    groups = []
+    for d in scales:
+        d32 = np.float32(np.float16(d))
+        k = np.arange(127, dtype=np.float64) + 0.5
+        m_star = (k * np.float64(d32) / (254.0 - k)).astype(np.float32).view(np.int32)
+        m = (m_star[:, None] + offsets[None, :]).reshape(-1).view(np.float32)
+        m = m[np.abs(m) < d32]
+        m = m * rng.choice(np.array([-1.0, 1.0], np.float32), m.size)
+        pad = (-m.size) % 31
+        m = np.concatenate([m, np.zeros(pad, np.float32)]).reshape(-1, 31)
+        g = np.empty((m.shape[0], 32), np.float32)
+        g[:, 0] = d32                                     # the group maximum: scale = d
+        g[:, 1:] = m
+        groups.append(g)
+    x = np.concatenate(groups).reshape(-1)
+    print(f"{x.size // 32} groups at code boundaries", flush=True)
+    _parity(orc, x, F.SPEC_MOMENTUM, "code boundaries")
+
+
 def test_all_codes_dequantize(orc):
     """Every code byte with assorted scales (subnormal, normal, max, Inf)."""
     require_gpu()
