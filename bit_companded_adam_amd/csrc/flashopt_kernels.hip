@@ -376,15 +376,18 @@ __device__ __forceinline__ void encode_s8_finite(const float (&a)[N], const Grou
     }
 }
 
-// Companded momentum codes of N finite values of one group through
-// softsign_code_fast; a lane with a value near a code's rounding boundary,
-// or with an infinite scale (d = 0), recomputes its codes with the correctly
-// rounded chain of encode_s8_finite.  Both give the same bits.
+// Companded momentum codes of N finite values of one group with fp16 scale
+// bits s, through softsign_code_fast; a lane with a value near a code's
+// rounding boundary, or with an infinite scale, recomputes its codes with
+// the correctly rounded chain of encode_s8_finite (whose reciprocal of the
+// divisor only that path needs).  Both give the same bits.
 template <int N>
-__device__ __forceinline__ void encode_s8_softsign_fast(const float (&a)[N], const GroupDiv &gd,
+__device__ __forceinline__ void encode_s8_softsign_fast(const float (&a)[N], uint32_t s,
                                                         uint32_t (&out)[N / 4])
 {
-    const float c0 = gd.d * math::kInv254;
+    const uint32_t mag = s & 0x7FFFu;
+    const float d = group_divisor(s);
+    const float c0 = d * math::kInv254;
     float dev = 0.0f;
 #pragma unroll
     for (int k = 0; k < N / 4; ++k) {
@@ -394,7 +397,7 @@ __device__ __forceinline__ void encode_s8_softsign_fast(const float (&a)[N], con
         out[k] = pack_bytes(static_cast<int32_t>(b[0]), static_cast<int32_t>(b[1]),
                             static_cast<int32_t>(b[2]), static_cast<int32_t>(b[3]));
     }
-    if (dev > math::kCodeTieGuard || gd.d == 0.0f) encode_s8_finite<true, N>(a, gd, out);
+    if (dev > math::kCodeTieGuard || mag == 0x7C00u) encode_s8_finite<true, N>(a, group_div(s), out);
 }
 
 // ------------------------------------------------------- standalone codec
@@ -459,16 +462,15 @@ quantize_kernel(const float *__restrict__ x, int64_t n, void *__restrict__ codes
         amax = group_max<8>(amax);
         const uint32_t s = f16_bits(amax);
         uint32_t w[1];
-        const GroupDiv gd = group_div(s);
         if constexpr (SPEC == FLASHOPT_SPEC_MOMENTUM) {
             // finite values take the guarded short code sequence
             bool finite = true;
 #pragma unroll
             for (int j = 0; j < 4; ++j) finite &= fabsf(a[j]) <= 0x1.fffffep127f;
-            if (finite) encode_s8_softsign_fast<4>(a, gd, w);
-            else encode<SPEC, 4>(a, gd, w);
+            if (finite) encode_s8_softsign_fast<4>(a, s, w);
+            else encode<SPEC, 4>(a, group_div(s), w);
         } else {
-            encode<SPEC, 4>(a, gd, w);
+            encode<SPEC, 4>(a, group_div(s), w);
         }
         if (cnt == 4) st4s(cb + e, w[0]);
         else
@@ -885,7 +887,7 @@ __device__ __forceinline__ void element_moments(const UnitIn<MB, ST, N> &in, int
 template <int MB, int ST, int N>
 __device__ __forceinline__ void unit_exact(const ChunkPtrs &c, uint32_t r, int cnt,
                                            const StepScalars &sc, const float *s_mu,
-                                           const float *s_vu, const GroupDiv &gdm,
+                                           const float *s_vu, uint32_t sm,
                                            uint32_t (&mo)[N / 4], uint32_t (&po)[N / 2],
                                            uint32_t (&ro)[rho_words(MB, N)])
 {
@@ -908,7 +910,7 @@ __device__ __forceinline__ void unit_exact(const ChunkPtrs &c, uint32_t r, int c
         th1[j] = theta * sc.cwd - num / den;
         m1[j] = j < cnt ? m : 0.0f;
     }
-    if constexpr (ST != kStatesFp32) encode<kMSpec, N>(m1, gdm, mo);
+    if constexpr (ST != kStatesFp32) encode<kMSpec, N>(m1, group_div(sm), mo);
     pack_theta<MB, true, N>(th1, po, ro);
 }
 
@@ -1004,7 +1006,6 @@ __device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
     // ---- group maxima, scales, variance codes
     uint32_t mo[N / 4], vo[N / 4], po[N / 2], ro[rho_words(MB, N)];
     uint32_t sm_out = 0u, sv_out = 0u;
-    GroupDiv gdm{1.0f, 1.0f};
     if constexpr (kQuant) {
         sm_out = f16_bits(group_max<32 / N>(am));
         if constexpr (kComp) {
@@ -1017,13 +1018,12 @@ __device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
             sv_out = f16_bits(group_max<32 / N>(av));
             encode<kVSpec, N>(v1, group_div(sv_out), vo);
         }
-        gdm = group_div(sm_out);
     }
 
     // ---- momentum codes and the new parameter
     if (!exact) {
-        if constexpr (kComp) encode_s8_softsign_fast<N>(m1, gdm, mo);
-        else if constexpr (kQuant) encode_s8_finite<false, N>(m1, gdm, mo);
+        if constexpr (kComp) encode_s8_softsign_fast<N>(m1, sm_out, mo);
+        else if constexpr (kQuant) encode_s8_finite<false, N>(m1, group_div(sm_out), mo);
         pack_theta<MB, false, N>(th1, po, ro);
     } else {
         // rare: a unit outside the short sequences' domains (tiny or huge
@@ -1031,7 +1031,7 @@ __device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
         // is recomputed from its inputs in memory with the generic
         // operations; nothing has been stored yet, and the group scales
         // above are already exact
-        unit_exact<MB, ST, N>(c, r, cnt, sc, s_mu, s_vu, gdm, mo, po, ro);
+        unit_exact<MB, ST, N>(c, r, cnt, sc, s_mu, s_vu, sm_out, mo, po, ro);
     }
 
     // ---- stores
@@ -1128,12 +1128,11 @@ __device__ __forceinline__ void sgd_unit(const ChunkPtrs &c, int u, int lane,
 #pragma unroll
         for (int j = 1; j < N; ++j) am = fmaxf(am, fabsf(b1[j]));
         sm_out = f16_bits(group_max<32 / N>(am));
-        const GroupDiv gdm = group_div(sm_out);
         if (!bad) {
-            if constexpr (kComp) encode_s8_softsign_fast<N>(b1, gdm, mo);
-            else encode_s8_finite<false, N>(b1, gdm, mo);
+            if constexpr (kComp) encode_s8_softsign_fast<N>(b1, sm_out, mo);
+            else encode_s8_finite<false, N>(b1, group_div(sm_out), mo);
         }
-        else encode<kMSpec, N>(b1, gdm, mo);
+        else encode<kMSpec, N>(b1, group_div(sm_out), mo);
     }
     if (!bad) pack_theta<MB, false, N>(th1, po, ro);
     else pack_theta<MB, true, N>(th1, po, ro);
