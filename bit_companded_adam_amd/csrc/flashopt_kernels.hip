@@ -119,20 +119,39 @@ __device__ __forceinline__ int32_t shalf(const uint32_t (&w)[W], int j)
 }
 
 // Dequantization before the scale: y = q/127 or q/255, then the softsign
-// inverse y / (2 - |y|) (dequantize()).  Built once per workgroup into LDS;
-// the table entries are these exact fp32 operations.
+// inverse y / (2 - |y|) (dequantize()).  The 256 entries of each spec are
+// constants, evaluated at compile time with these fp32 operations (constant
+// evaluation rounds each one to nearest even, as the device does); every
+// workgroup copies the tables it uses into LDS.
+template <unsigned SPEC>
+struct DequantTable {
+    float v[256];
+};
+
+template <unsigned SPEC>
+constexpr DequantTable<SPEC> make_dequant_table()
+{
+    constexpr bool kSigned = (SPEC & FLASHOPT_Q_SIGNED) != 0;
+    DequantTable<SPEC> t{};
+    for (int c = 0; c < 256; ++c) {
+        const float q = kSigned ? static_cast<float>(static_cast<int8_t>(c)) : static_cast<float>(c);
+        float y = q / (kSigned ? 127.0f : 255.0f);
+        if (SPEC & FLASHOPT_Q_SOFTSIGN) {
+            const float den = 2.0f - (y < 0.0f ? -y : y);
+            y = y / den;
+        }
+        t.v[c] = y;
+    }
+    return t;
+}
+
+template <unsigned SPEC>
+__device__ const DequantTable<SPEC> kDequantTable = make_dequant_table<SPEC>();
+
 template <unsigned SPEC>
 __device__ __forceinline__ float dequant_unit(int c)
 {
-    constexpr bool kSigned = (SPEC & FLASHOPT_Q_SIGNED) != 0;
-    const float q = kSigned ? static_cast<float>(static_cast<int8_t>(c))
-                            : static_cast<float>(static_cast<uint8_t>(c));
-    float y = q / (kSigned ? 127.0f : 255.0f);
-    if (SPEC & FLASHOPT_Q_SOFTSIGN) {
-        const float den = 2.0f - fabsf(y);
-        y = y / den;
-    }
-    return y;
+    return kDequantTable<SPEC>.v[c];
 }
 
 // A group's divisor d (1 for a zero scale, else the scale) with its
