@@ -774,8 +774,12 @@ struct ChunkPtrs {
     int rem;
 };
 
-__device__ __forceinline__ ChunkPtrs chunk_ptrs(const DevTensor &d, int64_t off)
+// Pointers of chunk k of a tensor.  Whether the chunk is full is decided on
+// 32-bit chunk indices (scalar compares; gfx9 has no 64-bit scalar
+// less-than).
+__device__ __forceinline__ ChunkPtrs chunk_ptrs(const DevTensor &d, int32_t k)
 {
+    const int64_t off = static_cast<int64_t>(k) * kChunkElems;
     ChunkPtrs c;
     c.param = d.param + off;
     c.grad = d.grad + off;
@@ -787,8 +791,8 @@ __device__ __forceinline__ ChunkPtrs chunk_ptrs(const DevTensor &d, int64_t off)
     c.vf = reinterpret_cast<uint32_t *>(d.v_codes) + off;
     c.ms = d.m_scales + off / kGroup;
     c.vs = d.v_scales + off / kGroup;
-    const int64_t rem = d.numel - off;
-    c.rem = rem < kChunkElems ? static_cast<int>(rem) : kChunkElems;
+    const int32_t full = static_cast<int32_t>(d.numel / kChunkElems);
+    c.rem = k < full ? kChunkElems : static_cast<int>(d.numel % kChunkElems);
     return c;
 }
 
@@ -1190,9 +1194,12 @@ __device__ __forceinline__ void for_each_chunk(const DevTensor *__restrict__ ten
 {
     const int64_t wave = __builtin_amdgcn_readfirstlane(
         static_cast<int32_t>(blockIdx.x) * (kBlockThreads / kWaveLanes) + (threadIdx.x >> 6));
-    const int64_t c0 = wave * run;
-    if (c0 >= total_chunks) return;
-    const int32_t c1 = static_cast<int32_t>(c0 + run < total_chunks ? c0 + run : total_chunks);
+    const int64_t first = wave * run;
+    if (first >= total_chunks) return;
+    // chunk indices fit in int32 (the host caps the total), so the search
+    // below compares in scalar registers
+    const int32_t c0 = static_cast<int32_t>(first);
+    const int32_t c1 = static_cast<int32_t>(first + run < total_chunks ? first + run : total_chunks);
 
     // last tensor whose first chunk is <= c0
     int lo = 0, hi = n_tensors - 1;
@@ -1202,12 +1209,11 @@ __device__ __forceinline__ void for_each_chunk(const DevTensor *__restrict__ ten
         else hi = mid - 1;
     }
     int t = __builtin_amdgcn_readfirstlane(lo);
-    for (int32_t c = static_cast<int32_t>(c0); c < c1; ++c) {
+    for (int32_t c = c0; c < c1; ++c) {
         while (c >= chunk_start[t + 1]) ++t;
         t = __builtin_amdgcn_readfirstlane(t);
         const DevTensor d = tensors[t];
-        const int64_t off = static_cast<int64_t>(c - chunk_start[t]) * kChunkElems;
-        f(chunk_ptrs(d, off));
+        f(chunk_ptrs(d, c - chunk_start[t]));
     }
 }
 
@@ -1280,8 +1286,7 @@ __device__ __forceinline__ void for_each_chunk_of(const DevTensor &d, int32_t to
     const int64_t c0 = wave * run;
     if (c0 >= total_chunks) return;
     const int32_t c1 = static_cast<int32_t>(c0 + run < total_chunks ? c0 + run : total_chunks);
-    for (int32_t c = static_cast<int32_t>(c0); c < c1; ++c)
-        f(chunk_ptrs(d, static_cast<int64_t>(c) * kChunkElems));
+    for (int32_t c = static_cast<int32_t>(c0); c < c1; ++c) f(chunk_ptrs(d, c));
 }
 
 template <int MB, int ST>
