@@ -326,3 +326,11 @@ def test_decoder_1b_sampled_ablations(orc, mb, qs):
 def test_decoder_8b_sampled(orc, mb, comp):
     require_gpu()
     _sampled_parity(orc, W.decoder_8b_shapes(), mb, comp, f"8.0B list, {mb}-bit, companded={comp}")
+
+
+@pytest.mark.parametrize("mb,qs", [(None, True), (24, False)], ids=["mb_none", "fp32_states"])
+def test_decoder_8b_sampled_ablations(orc, mb, qs):
+    """The two ablations on the 8.0B list, in the launch the benchmark times
+    for them (--master-bits 0, --fp32-states)."""
+    require_gpu()
+    _sampled_parity(orc, W.decoder_8b_shapes(), mb, True, f"8.0B list, mb {mb}, quantized {qs}", qs=qs)
