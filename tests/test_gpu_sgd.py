@@ -137,14 +137,14 @@ def test_non_finite_gradients(orc, mb, comp, qs):
         _compare(_snap(opt.states[0]), pre, f"non-finite t{t}", nan_ok=True)
 
 
-def _sampled_parity(orc, shapes, label):
+def _sampled_parity(orc, shapes, label, mb=24, qs=True):
     """Two steps over a whole decoder list in one list launch (the benchmark's
     launch shape); the second step is checked against the oracle on
     group-aligned samples of every tensor: its first and last 2^16 elements
     and two random 1024-element chunks."""
     require_gpu()
     params = [W.init_param(W.numel(s), device="cuda", seed=1000 + i) for i, (_, s) in enumerate(shapes)]
-    opt = F.FlashSGD(params, **dict(HP, weight_decay=0.01))
+    opt = F.FlashSGD(params, master_bits=mb, quantize_states=qs, **dict(HP, weight_decay=0.01))
     factors = W.grad_factors(len(shapes)).numpy()
     grads = lambda t: [W.make_grad(W.numel(s), t, device="cuda", stream_id=i, factor=float(factors[i]))
                        for i, (_, s) in enumerate(shapes)]
@@ -165,7 +165,7 @@ def _sampled_parity(orc, shapes, label):
     torch.cuda.synchronize()
     for i, (s, rr) in enumerate(zip(opt.states, ranges)):
         for (lo, hi), pre, g in zip(rr, pres[i], gs[i]):
-            orc.sgd_step(pre, g, _orc_hp(2, dict(HP, weight_decay=0.01), 24, True, True))
+            orc.sgd_step(pre, g, _orc_hp(2, dict(HP, weight_decay=0.01), mb, True, qs))
             _compare(_snap(s, lo, hi), pre, f"{label} tensor {i} [{lo}, {hi})")
 
 
@@ -173,5 +173,7 @@ def test_decoder_1b_sampled(orc):
     _sampled_parity(orc, W.decoder_1b_shapes(), "1.2B")
 
 
-def test_decoder_8b_sampled(orc):
-    _sampled_parity(orc, W.decoder_8b_shapes(), "8.0B")
+@pytest.mark.parametrize("mb,qs", [(24, True), (32, True), (24, False)],
+                         ids=["mb24", "mb32", "fp32_buffer"])
+def test_decoder_8b_sampled(orc, mb, qs):
+    _sampled_parity(orc, W.decoder_8b_shapes(), f"8.0B, mb {mb}, quantized {qs}", mb, qs)
