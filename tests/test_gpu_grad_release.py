@@ -58,6 +58,41 @@ def test_tensor_step_equals_list_step(kind, mb, qs):
             _assert_same(sa, sb, f"{kind} t{t} tensor{i}")
 
 
+def _bits(t):
+    if t is None:
+        return None
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else (
+        t.view(torch.int32) if t.dtype == torch.float32 else t)
+
+
+def test_decoder_8b_tensor_launches_equal_list_launch():
+    """The 8.0B list with one launch per tensor (the benchmark's
+    --grad-release pattern) leaves every state byte equal to the list
+    launch's, over two steps; compared on the device (the list launch is
+    checked against the oracle at this size elsewhere)."""
+    require_gpu()
+    shapes = W.decoder_8b_shapes()
+    pa = [W.init_param(W.numel(s), device="cuda", seed=1000 + i) for i, (_, s) in enumerate(shapes)]
+    pb = [p.clone() for p in pa]
+    a, b = _make("adamw", pa, 24, True), _make("adamw", pb, 24, True)
+    factors = W.grad_factors(len(shapes)).numpy()
+    for t in (1, 2):
+        grads = [W.make_grad(W.numel(s), t, device="cuda", stream_id=i, factor=float(factors[i]))
+                 for i, (_, s) in enumerate(shapes)]
+        for i, g in enumerate(grads):
+            a.step_tensor(i, g)
+        b.step(grads)
+        del grads
+    torch.cuda.synchronize()
+    for i, (sa, sb) in enumerate(zip(a.states, b.states)):
+        for name in ("param", "rho", "m_codes", "m_scales", "v_codes", "v_scales"):
+            x, y = _bits(getattr(sa, name)), _bits(getattr(sb, name))
+            assert torch.equal(x, y), f"tensor {i} {name}"
+    print(f"8.0B list: {len(shapes)} single-tensor launches equal the list launch", flush=True)
+    del a, b, pa, pb
+    torch.cuda.empty_cache()
+
+
 def _mlp(seed):
     torch.manual_seed(seed)
     m = torch.nn.Sequential(torch.nn.Linear(192, 384), torch.nn.GELU(),
