@@ -1436,6 +1436,16 @@ int32_t chunks_per_wave()
     return run;
 }
 
+// Chunks per wavefront for a single-tensor launch: a tensor too small to
+// fill the GPU twice over at the default run (256 CUs x 28 resident
+// wavefronts x 2 chunks) gets one chunk per wavefront, doubling the
+// wavefronts that share its work.
+int32_t tensor_chunks_per_wave(int32_t total_chunks)
+{
+    constexpr int32_t kFillChunks = 256 * 28 * 2;
+    return total_chunks < kFillChunks ? 1 : chunks_per_wave();
+}
+
 unsigned step_grid(int32_t total_chunks, int32_t run)
 {
     const int64_t waves = (total_chunks + run - 1) / run;
@@ -1508,7 +1518,7 @@ struct AdamWTensorLaunch {
     static hipError_t run(const DevTensor *t, const int32_t *, int, int32_t total,
                           const StepScalars &sc, hipStream_t st)
     {
-        const int32_t run = chunks_per_wave();
+        const int32_t run = tensor_chunks_per_wave(total);
         hipLaunchKernelGGL((adamw_tensor_kernel<MB, ST>), dim3(step_grid(total, run)),
                            dim3(kBlockThreads), 0, st, *t, total, run, sc);
         return hipGetLastError();
@@ -1520,7 +1530,7 @@ struct SgdTensorLaunch {
     static hipError_t run(const DevTensor *t, const int32_t *, int, int32_t total,
                           const SgdScalars &sc, hipStream_t st)
     {
-        const int32_t run = chunks_per_wave();
+        const int32_t run = tensor_chunks_per_wave(total);
         hipLaunchKernelGGL((sgd_tensor_kernel<MB, ST>), dim3(step_grid(total, run)),
                            dim3(kBlockThreads), 0, st, *t, total, run, sc);
         return hipGetLastError();
