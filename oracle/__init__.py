@@ -9,7 +9,7 @@ The C source (``flashopt_oracle.c``) follows the method pages:
 ``code/flashsim/flash_adamw_sim.py`` (FlashAdamWSim.step, Alg. 4) and
 ``code/gpu/equivalence.py`` (the bf16 cast fed to the correction bits).
 FlashSGD appears on the pages only in bytes_per_param; its update is read as
-torch.optim.SGD with momentum (R5 in the C source).
+torch.optim.SGD with momentum (R16 in the C source).
 All arrays here are numpy arrays on the host.
 """
 from __future__ import annotations

@@ -12,8 +12,10 @@
  *   R2  "round" in quantize() is torch.round: half to even.
  *   R3  the AdamW body uses the declared bias-correction folding unless
  *       literal_order is set; both forms give identical m, v and codes.
- *   R4  non-finite values are out of contract; NaN is given code 0 / quiet
+ *   R12 non-finite values are out of contract; NaN is given code 0 / quiet
  *       NaN so that both sides of a parity test stay defined.
+ *   R16 FlashSGD's update (given only as a bytes_per_param row) is
+ *       torch.optim.SGD with momentum, in torch's order.
  */
 #include "flashopt_oracle.h"
 
@@ -176,7 +178,7 @@ int oracle_reconstruct(const uint16_t *theta_bf16, const void *rho, int64_t n,
  *   s = fp16(amax); d = 1 if s == 0 else float(s);
  *   y_i = a_i / d; with SOFTSIGN y_i = (2 y_i) / (1 + |y_i|);
  *   q_i = clamp(round(y_i * 127), -127, 127) or clamp(round(y_i * 255), 0, 255)
- * (R2: round half to even).  NaN codes are 0 (R4). */
+ * (R2: round half to even).  NaN codes are 0 (R12). */
 int oracle_quantize(const float *x, int64_t n, unsigned spec,
                     void *codes, uint16_t *scales)
 {
@@ -391,7 +393,7 @@ int oracle_adamw_step(uint16_t *param, const uint16_t *grad, void *rho,
 
 /* FlashSGD appears on the pages only through its memory accounting
  * ([SIM bytes_per_param()] "flash_sgd": bf16 master + rho + grad + one
- * group-32 quantized state of 1 + 2/32 bytes).  R5: its update is read as
+ * group-32 quantized state of 1 + 2/32 bytes).  R16: its update is read as
  * torch.optim.SGD with momentum (the optimizer the page's "sgd_ref" row
  * accounts for), one fp32 operation per step, in torch's order:
  *   d   <- g + wd theta                         (coupled weight decay, if wd)

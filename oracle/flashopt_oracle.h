@@ -97,7 +97,7 @@ int oracle_adamw_step(uint16_t *param, const uint16_t *grad, void *rho,
                       void *v_codes, uint16_t *v_scales,
                       int64_t n, const oracle_hparams *h);
 
-/* FlashSGD hyper-parameters (R5 in flashopt_oracle.c: torch.optim.SGD with
+/* FlashSGD hyper-parameters (R16 in flashopt_oracle.c: torch.optim.SGD with
  * momentum, the momentum buffer stored with the momentum spec). */
 typedef struct {
     double lr, momentum, dampening, weight_decay;
