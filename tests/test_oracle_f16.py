@@ -21,7 +21,8 @@ def _check(orc, lo_bits, hi_bits):
         u = np.arange(start, min(start + CHUNK, hi_bits), dtype=np.uint64).astype(np.uint32)
         x = u.view(np.float32)
         got = orc.f16_bits(x)
-        ref = x.astype(np.float16).view(np.uint16)
+        with np.errstate(over="ignore"):       # overflow to Inf is part of what is pinned
+            ref = x.astype(np.float16).view(np.uint16)
         bad = np.nonzero(got != ref)[0]
         return (int(u[bad[0]]), int(got[bad[0]]), int(ref[bad[0]])) if bad.size else None
 
@@ -43,7 +44,9 @@ def test_f16_sampled_everywhere(orc):
     x = u.view(np.float32)
     keep = ~np.isnan(x)
     x = x[keep]
-    assert (orc.f16_bits(x) == x.astype(np.float16).view(np.uint16)).all()
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert (orc.f16_bits(x) == ref).all()
 
 
 def test_f16_named_cases(orc):
