@@ -62,17 +62,41 @@ def kernel_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_per_launch():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None if the kernel source changed since the counters were taken."""
+# Peak VALU issue of MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one
+# (non-packed) instruction per lane per cycle; a wavefront instruction
+# takes 4 cycles of a SIMD.
+PEAK_VALU_LANE_INSTS = 256 * 4 * 16 * 2.4e9
+
+
+def _counter_record():
+    """The committed rocprofv3 counter record of the default step, or None if
+    the kernel source changed since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_sha") != kernel_sha():
+    return rec if rec.get("kernel_sha") == kernel_sha() else None
+
+
+def traffic_per_launch():
+    """HBM bytes per launch from the committed counter record (or None)."""
+    rec = _counter_record()
+    return None if rec is None else rec.get("hbm_bytes_per_launch")
+
+
+def valu_roofline(ms_launch: float):
+    """The step's second roof: its VALU wavefront instructions per launch
+    (committed counter record) at the peak issue rate, against the measured
+    launch time; None when the record is stale."""
+    rec = _counter_record()
+    if rec is None or not rec.get("valu_insts_per_launch"):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    lane_insts = rec["valu_insts_per_launch"] * 64
+    achieved = lane_insts / (ms_launch * 1e-3)
+    return {"bound": "alu", "achieved": achieved, "peak": PEAK_VALU_LANE_INSTS,
+            "unit": "VALU lane-instructions/s", "frac": achieved / PEAK_VALU_LANE_INSTS,
+            "ms_at_peak": lane_insts / PEAK_VALU_LANE_INSTS * 1e3}
 
 
 WORKLOADS = {"decoder-8b-list": W.decoder_8b_shapes, "decoder-1b-list": W.decoder_1b_shapes}
@@ -378,6 +402,7 @@ def main():
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": traffic_per_launch() if default else None,
                      "copy_ref_gbs": copy_gbs},
+        "valu_roofline": valu_roofline(ms_launch) if default else None,
         "cpu_baseline": cpu,
         "env": env,
     }
