@@ -126,6 +126,47 @@ def test_ragged_list(orc, mb, comp, qs):
             _compare(_snap(s), pre, mb, f"{_vid((mb, comp, qs))} t{t} tensor{i} n{RAGGED[i]}")
 
 
+# Hyper-parameter settings away from the default: (name, overrides, first
+# step).  beta 0 (no averaging), a large k2 = 1/sqrt(1 - 0.9999) = 100, bias
+# corrections at 1 (step 10^6), learning rates from 1e-6 to 1, no weight
+# decay, a large eps.
+HP_GRID = [
+    ("betas_zero", dict(betas=(0.0, 0.0)), 1),
+    ("beta2_0.9999", dict(betas=(0.5, 0.9999)), 1),
+    ("step_1e6", dict(betas=(0.95, 0.99)), 1_000_000),
+    ("step_100", dict(), 100),
+    ("lr_1_wd_0.1", dict(lr=1.0, weight_decay=0.1), 1),
+    ("lr_1e-6_wd_0", dict(lr=1e-6, weight_decay=0.0), 5),
+    ("eps_1e-3", dict(eps=1e-3), 2),
+]
+
+
+@pytest.mark.parametrize("mb,comp,qs", [(24, True, True), (32, False, True), (24, True, False)],
+                         ids=["mb24-comp", "mb32-lin", "mb24-f32"])
+@pytest.mark.parametrize("name,over,t0", HP_GRID, ids=[h[0] for h in HP_GRID])
+def test_hyper_parameter_grid(orc, name, over, t0, mb, comp, qs):
+    """Three teacher-forced steps from step t0 under each setting: the host's
+    scalars, the short division's domain checks and the codec across the
+    hyper-parameter range."""
+    require_gpu()
+    hp = dict(HP, **over)
+    sizes = [4096 + 5, 70001, 1 << 15]
+    params = [W.init_param(n, device="cuda", seed=40 + i) for i, n in enumerate(sizes)]
+    opt = F.FlashAdamW(params, master_bits=mb, companded=comp, quantize_states=qs, **hp)
+    opt.t = t0 - 1
+    for t in range(t0, t0 + 3):
+        grads = [W.make_grad(n, t, device="cuda", stream_id=i, factor=float(np.exp(i - 1)))
+                 for i, n in enumerate(sizes)]
+        pres = [_snap(s) for s in opt.states]
+        opt.step(grads)
+        torch.cuda.synchronize()
+        for i, (st, pre, g) in enumerate(zip(opt.states, pres, grads)):
+            orc.adamw_step(pre, u16(g), oracle.hparams(
+                lr=hp["lr"], betas=hp["betas"], eps=hp["eps"], weight_decay=hp["weight_decay"],
+                step=t, master_bits=mb, companded=comp, quantize_states=qs))
+            _compare(_snap(st), pre, mb, f"{name} t{t} tensor{i}")
+
+
 @pytest.mark.parametrize("mb,comp,qs", [(None, True, True), (24, True, False)],
                          ids=["mb_none", "fp32_states"])
 def test_ablation_10_steps(orc, mb, comp, qs):
