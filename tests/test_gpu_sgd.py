@@ -96,6 +96,38 @@ def test_ragged_list(orc, mb, comp, qs, setting):
             _compare(_snap(s), pre, f"{_sid((mb, comp, qs))} {setting} t{t} tensor{i} n{RAGGED[i]}")
 
 
+SGD_GRID = [
+    ("momentum_0.5", dict(momentum=0.5), 1),
+    ("momentum_0.99_step_1e6", dict(momentum=0.99, weight_decay=0.01), 1_000_000),
+    ("lr_1", dict(lr=1.0, weight_decay=0.1), 1),
+    ("lr_1e-6", dict(lr=1e-6), 3),
+    ("nesterov_0.95", dict(momentum=0.95, nesterov=True, weight_decay=0.001), 2),
+]
+
+
+@pytest.mark.parametrize("mb,comp,qs", [(24, True, True), (32, False, True), (24, True, False)],
+                         ids=["mb24-comp", "mb32-lin", "mb24-f32"])
+@pytest.mark.parametrize("name,over,t0", SGD_GRID, ids=[h[0] for h in SGD_GRID])
+def test_hyper_parameter_grid(orc, name, over, t0, mb, comp, qs):
+    """Three teacher-forced steps from step t0 (the first is the buffer's
+    initialisation only when t0 = 1) under each setting."""
+    require_gpu()
+    hp = dict(HP, **over)
+    sizes = [4096 + 5, 70001]
+    params = [W.init_param(n, device="cuda", seed=60 + i) for i, n in enumerate(sizes)]
+    opt = F.FlashSGD(params, master_bits=mb, companded=comp, quantize_states=qs, **hp)
+    opt.t = t0 - 1
+    for t in range(t0, t0 + 3):
+        grads = [W.make_grad(n, t, device="cuda", stream_id=i, factor=float(np.exp(i)))
+                 for i, n in enumerate(sizes)]
+        pres = [_snap(s) for s in opt.states]
+        opt.step(grads)
+        torch.cuda.synchronize()
+        for i, (st, pre, g) in enumerate(zip(opt.states, pres, grads)):
+            orc.sgd_step(pre, u16(g), _orc_hp(t, hp, mb, comp, qs))
+            _compare(_snap(st), pre, f"{name} t{t} tensor{i}")
+
+
 def test_single_tensor_10_steps(orc):
     require_gpu()
     n = 1 << 20
