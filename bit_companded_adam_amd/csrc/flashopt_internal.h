@@ -7,9 +7,10 @@
 
 namespace flashopt {
 
-// Work decomposition: one lane owns 16 consecutive elements, a lane pair
-// owns one 32-element quantization group, one wavefront (64 lanes) owns one
-// 1024-element chunk, and a 256-thread workgroup runs four wavefronts.
+// Work decomposition: one wavefront (64 lanes) owns a 1024-element chunk, 16
+// elements per lane (processed in units of consecutive elements, see the
+// kernels); quantization groups are 32 elements; a 256-thread workgroup runs
+// four wavefronts.
 constexpr int kLaneElems = 16;
 constexpr int kWaveLanes = 64;
 constexpr int kChunkElems = kLaneElems * kWaveLanes;   // 1024

@@ -1,25 +1,30 @@
 // HIP kernels of libflashopt.so for gfx950 (MI355X): the group-32 state codec,
-// the bf16 + rho weight split, and the fused FlashAdamW step.
+// the bf16 + rho weight split, and the fused FlashAdamW and FlashSGD steps.
 //
 // Method pages: "code/flashsim/quantization.py" (Alg. 2/3: quantize(),
 // dequantize()), "code/flashsim/flash_adamw_sim.py" (Alg. 4:
-// FlashAdamWSim.step()), "code/gpu/equivalence.py" (bf16 parameter and
-// correction bits, eq_ecc()).
+// FlashAdamWSim.step(), bytes_per_param), "code/gpu/equivalence.py" (bf16
+// parameter and correction bits, eq_ecc()).
 //
-// Layout of the work: a lane owns 16 consecutive elements, so each element
-// stream is read and written with 16-byte vector accesses (two for 16-bit
-// streams, four for fp32); the lane pair (2k, 2k+1) owns one 32-element
-// group and finishes the group max with one DPP exchange; a wavefront owns a
-// 1024-element chunk.  The step is elementwise and memory-bound, so there is
-// no MFMA and no LDS staging of data; LDS holds only the per-tensor chunk
-// table and two 256-entry dequantization tables.
+// Layout of the work: a wavefront owns 1024-element chunks (two in a row for
+// the multi-tensor steps) and each lane 16 elements of a chunk, taken as
+// units of N consecutive elements placed so that every memory instruction of
+// the wavefront covers one contiguous block of each stream (unit u of lane l
+// starts at element 64 N u + N l).  The quantized steps use N = 8 (a lane
+// quad owns a 32-element group; its maximum takes two DPP exchanges); fp32
+// states and the codec and split kernels use N = 4 (quantize's group
+// maximum spans 8 lanes).  The path is elementwise, so there is no MFMA; LDS
+// holds only the two 256-entry dequantization tables (compile-time constants
+// copied in per workgroup), and the per-tensor chunk table is read with
+// scalar loads.
 //
 // Arithmetic: fp32, one IEEE rounding per operation in the written order
 // (built with -ffp-contract=off, fp32 and fp16 denormals preserved), so the
 // results match a plain CPU evaluation bit for bit.  Division by a group
-// scale, the softsign division, the variance sqrt and the byte conversions
-// use the exact short sequences of flashopt_math.h instead of the generic
-// correctly rounded expansions.
+// scale, the softsign division, the update division, the variance sqrt and
+// the byte conversions use the exact short sequences of flashopt_math.h
+// instead of the generic correctly rounded expansions; the momentum code uses
+// a guarded short sequence whose fallback is the correctly rounded chain.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
