@@ -26,7 +26,7 @@ CHECK_LIB = os.path.join(ROOT, "tests", "hip", "libfastmath_check.so")
 
 
 def build_check(verbose: bool = False) -> str:
-    """The GPU checker of the short exact arithmetic sequences (test-only)."""
+    """The GPU test library that verifies the short exact arithmetic sequences (test-only)."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = CHECK_LIB + ".tmp"
     cmd = [hipcc, *HIPCC_FLAGS, "-I", CSRC, CHECK_SRC, "-o", tmp]
