@@ -168,3 +168,34 @@ def test_empty_is_noop():
     x = torch.empty(0, device="cuda")
     q, s = F.flashopt_quantize(x, F.SPEC_MOMENTUM)
     assert q.numel() == 0 and s.numel() == 0
+
+
+@pytest.mark.parametrize("spec", [F.SPEC_MOMENTUM, F.SPEC_VARIANCE], ids=["momentum", "variance"])
+def test_tensor_past_2_31_elements(orc, spec):
+    """2^31 + 1101 fp32 values (seeded N(0, 1e-3^2) on the device; squared for
+    the variance spec): the fp32 stream passes 2^32 bytes at element 2^30 and
+    the code stream 2^31 bytes at element 2^31.  Checked on group-aligned
+    samples at the start, around elements 2^30 and 2^31, and on the ragged
+    tail."""
+    require_gpu()
+    n = (1 << 31) + 1024 + 77
+    gen = torch.Generator(device="cuda").manual_seed(91)
+    x = torch.randn(n, generator=gen, device="cuda").mul_(1e-3)
+    if spec == F.SPEC_VARIANCE:
+        x.square_()
+    q_d, s_d = F.flashopt_quantize(x, spec)
+    d_d = F.flashopt_dequantize(q_d, s_d, spec)
+    torch.cuda.synchronize()
+    k = 1 << 12
+    rr = [(0, k), ((1 << 30) - k, (1 << 30) + k), ((1 << 31) - k, (1 << 31) + k),
+          (((n - k) // 32) * 32, n)]
+    for lo, hi in rr:
+        x_np = host(x[lo:hi])
+        q_o, s_o = orc.quantize(x_np, spec)
+        assert (u16(s_d[lo // 32:(hi + 31) // 32]) == s_o).all(), f"[{lo}, {hi}): scales"
+        assert (host(q_d[lo:hi]) == q_o).all(), f"[{lo}, {hi}): codes"
+        d_o = orc.dequantize(q_o, s_o, spec)
+        assert (host(d_d[lo:hi]).view(np.uint32) == d_o.view(np.uint32)).all(), f"[{lo}, {hi}): values"
+    print(f"codec spec {spec}, 2^31 + 1101 elements: samples bit-exact", flush=True)
+    del x, q_d, s_d, d_d
+    torch.cuda.empty_cache()

@@ -3,11 +3,12 @@ oracle, through the C ABI.  FlashSGD appears on page
 "code/flashsim/flash_adamw_sim.py" only in bytes_per_param; the library and
 the oracle read its update as torch.optim.SGD with momentum, the buffer stored
 with the momentum spec.  Bar as for the AdamW step: scales, rho and the bf16
-parameter bit-exact, codes (or the fp32 buffer) bit-exact.
+parameter bit-exact, codes (or the fp32 buffer) bit-exact.  Every comparison
+is free-running: the oracle steps its own state from the same seeded
+parameters and zero buffer, with the same seeded gradients.
   * ragged lists (sizes 0 .. 2^17) for five storage variants and four
-    momentum settings (plain, weight decay, Nesterov, dampening), 3 steps,
-    teacher-forced;
-  * 2^20 params x 10 steps, teacher-forced and free-running;
+    momentum settings (plain, weight decay, Nesterov, dampening), 3 steps;
+  * 2^20 params x 10 steps;
   * non-finite gradients next to finite lanes (NaN matches any NaN);
   * the 1.2B and 8.0B lists on group-aligned samples in the benchmark's launch
     shape.
@@ -41,6 +42,17 @@ def _snap(s: F.TensorState, lo=0, hi=None) -> oracle.State:
     rho = None if s.rho is None else host(s.rho[lo:hi])
     ms = None if s.m_scales is None else u16(s.m_scales[g0:g1])
     return oracle.State(u16(s.param[lo:hi]), rho, host(s.m_codes[lo:hi]), ms, None, None)
+
+
+def _start(params, mb, qs):
+    """The oracle's starting states: the seeded bf16 parameters (copied before
+    any step), zero correction bits and a zero momentum buffer."""
+    out = []
+    for p in params:
+        st = oracle.State.zeros_like_param(u16(p), mb, quantize_states=qs)
+        st.v_codes = st.v_scales = None
+        out.append(st)
+    return out
 
 
 def _f16_nan(a):
@@ -84,16 +96,16 @@ def test_ragged_list(orc, mb, comp, qs, setting):
     require_gpu()
     hp = dict(HP, **SETTINGS[setting])
     params = [W.init_param(n, device="cuda", seed=200 + i) for i, n in enumerate(RAGGED)]
+    want = _start(params, mb, qs)
     opt = F.FlashSGD(params, master_bits=mb, companded=comp, quantize_states=qs, **hp)
     for t in range(1, 4):
         grads = [W.make_grad(n, t, device="cuda", stream_id=i, factor=float(np.exp(i - 6)))
                  for i, n in enumerate(RAGGED)]
-        pres = [_snap(s) for s in opt.states]
         opt.step(grads)
         torch.cuda.synchronize()
-        for i, (s, pre, g) in enumerate(zip(opt.states, pres, grads)):
-            orc.sgd_step(pre, u16(g), _orc_hp(t, hp, mb, comp, qs))
-            _compare(_snap(s), pre, f"{_sid((mb, comp, qs))} {setting} t{t} tensor{i} n{RAGGED[i]}")
+        for i, (s, w, g) in enumerate(zip(opt.states, want, grads)):
+            orc.sgd_step(w, u16(g), _orc_hp(t, hp, mb, comp, qs))
+            _compare(_snap(s), w, f"{_sid((mb, comp, qs))} {setting} t{t} tensor{i} n{RAGGED[i]}")
 
 
 SGD_GRID = [
@@ -109,23 +121,23 @@ SGD_GRID = [
                          ids=["mb24-comp", "mb32-lin", "mb24-f32"])
 @pytest.mark.parametrize("name,over,t0", SGD_GRID, ids=[h[0] for h in SGD_GRID])
 def test_hyper_parameter_grid(orc, name, over, t0, mb, comp, qs):
-    """Three teacher-forced steps from step t0 (the first is the buffer's
+    """Three steps from a zero buffer at step t0 (the first is the buffer's
     initialisation only when t0 = 1) under each setting."""
     require_gpu()
     hp = dict(HP, **over)
     sizes = [4096 + 5, 70001]
     params = [W.init_param(n, device="cuda", seed=60 + i) for i, n in enumerate(sizes)]
+    want = _start(params, mb, qs)
     opt = F.FlashSGD(params, master_bits=mb, companded=comp, quantize_states=qs, **hp)
     opt.t = t0 - 1
     for t in range(t0, t0 + 3):
         grads = [W.make_grad(n, t, device="cuda", stream_id=i, factor=float(np.exp(i)))
                  for i, n in enumerate(sizes)]
-        pres = [_snap(s) for s in opt.states]
         opt.step(grads)
         torch.cuda.synchronize()
-        for i, (st, pre, g) in enumerate(zip(opt.states, pres, grads)):
-            orc.sgd_step(pre, u16(g), _orc_hp(t, hp, mb, comp, qs))
-            _compare(_snap(st), pre, f"{name} t{t} tensor{i}")
+        for i, (st, w, g) in enumerate(zip(opt.states, want, grads)):
+            orc.sgd_step(w, u16(g), _orc_hp(t, hp, mb, comp, qs))
+            _compare(_snap(st), w, f"{name} t{t} tensor{i}")
 
 
 def test_single_tensor_10_steps(orc):
@@ -133,19 +145,14 @@ def test_single_tensor_10_steps(orc):
     n = 1 << 20
     hp = dict(HP, weight_decay=0.01)
     p = W.init_param(n, device="cuda", seed=31)
+    (free,) = _start([p], 24, True)
     opt = F.FlashSGD([p], **hp)
-    free = orc.State.zeros_like_param(u16(p), 24)
-    free.v_codes = free.v_scales = None
     for t in range(1, 11):
         g = W.make_grad(n, t, device="cuda")
-        pre = _snap(opt.states[0])
         opt.step([g])
         torch.cuda.synchronize()
-        post = _snap(opt.states[0])
-        orc.sgd_step(pre, u16(g), _orc_hp(t, hp, 24, True, True))
-        _compare(post, pre, f"teacher-forced step {t}")
         orc.sgd_step(free, u16(g), _orc_hp(t, hp, 24, True, True))
-        _compare(post, free, f"free-running step {t}")
+        _compare(_snap(opt.states[0]), free, f"step {t}")
 
 
 @pytest.mark.parametrize("mb,comp,qs", [(24, True, True), (None, True, False)], ids=["q", "f32"])
@@ -155,6 +162,7 @@ def test_non_finite_gradients(orc, mb, comp, qs):
     require_gpu()
     n = 16 * 1024 + 77
     p = W.init_param(n, device="cuda", seed=41)
+    (want,) = _start([p], mb, qs)
     opt = F.FlashSGD([p], master_bits=mb, companded=comp, quantize_states=qs, **HP)
     for t in range(1, 4):
         g = W.make_grad(n, t).float()
@@ -162,28 +170,25 @@ def test_non_finite_gradients(orc, mb, comp, qs):
         g[2091] = float("nan")
         g[64 * 32:65 * 32] = 1e30
         g = g.to(torch.bfloat16).to("cuda")
-        pre = _snap(opt.states[0])
         opt.step([g])
         torch.cuda.synchronize()
-        orc.sgd_step(pre, u16(g), _orc_hp(t, HP, mb, comp, qs))
-        _compare(_snap(opt.states[0]), pre, f"non-finite t{t}", nan_ok=True)
+        orc.sgd_step(want, u16(g), _orc_hp(t, HP, mb, comp, qs))
+        _compare(_snap(opt.states[0]), want, f"non-finite t{t}", nan_ok=True)
 
 
 def _sampled_parity(orc, shapes, label, mb=24, qs=True):
     """Two steps over a whole decoder list in one list launch (the benchmark's
-    launch shape); the second step is checked against the oracle on
-    group-aligned samples of every tensor: its first and last 2^16 elements
-    and two random 1024-element chunks."""
+    launch shape); after each, group-aligned samples of every tensor (its
+    first and last 2^16 elements and two random 1024-element chunks) are
+    checked against the oracle stepping those slices from the same seeded
+    start (step 1 initialises the buffer, step 2 reads it back)."""
     require_gpu()
     params = [W.init_param(W.numel(s), device="cuda", seed=1000 + i) for i, (_, s) in enumerate(shapes)]
     opt = F.FlashSGD(params, master_bits=mb, quantize_states=qs, **dict(HP, weight_decay=0.01))
     factors = W.grad_factors(len(shapes)).numpy()
     grads = lambda t: [W.make_grad(W.numel(s), t, device="cuda", stream_id=i, factor=float(factors[i]))
                        for i, (_, s) in enumerate(shapes)]
-    opt.step(grads(1))
-    g2 = grads(2)
     rng = np.random.default_rng(9)
-    torch.cuda.synchronize()
     ranges = []
     for s in opt.states:
         n = s.param.numel()
@@ -191,14 +196,17 @@ def _sampled_parity(orc, shapes, label, mb=24, qs=True):
         if n > 4096:
             r += [(int(c) * 1024, int(c) * 1024 + 1024) for c in rng.integers(0, n // 1024 - 1, 2)]
         ranges.append(r)
-    pres = [[_snap(s, lo, hi) for lo, hi in rr] for s, rr in zip(opt.states, ranges)]
-    gs = [[u16(g[lo:hi]) for lo, hi in rr] for g, rr in zip(g2, ranges)]
-    opt.step(g2)
-    torch.cuda.synchronize()
-    for i, (s, rr) in enumerate(zip(opt.states, ranges)):
-        for (lo, hi), pre, g in zip(rr, pres[i], gs[i]):
-            orc.sgd_step(pre, g, _orc_hp(2, dict(HP, weight_decay=0.01), mb, True, qs))
-            _compare(_snap(s, lo, hi), pre, f"{label} tensor {i} [{lo}, {hi})")
+    want = [_start([s.param[lo:hi] for lo, hi in rr], mb, qs) for s, rr in zip(opt.states, ranges)]
+    for t in (1, 2):
+        g_t = grads(t)
+        gs = [[u16(g[lo:hi]) for lo, hi in rr] for g, rr in zip(g_t, ranges)]
+        opt.step(g_t)
+        del g_t
+        torch.cuda.synchronize()
+        for i, (s, rr) in enumerate(zip(opt.states, ranges)):
+            for (lo, hi), w, g in zip(rr, want[i], gs[i]):
+                orc.sgd_step(w, g, _orc_hp(t, dict(HP, weight_decay=0.01), mb, True, qs))
+                _compare(_snap(s, lo, hi), w, f"{label} step {t} tensor {i} [{lo}, {hi})")
 
 
 def test_decoder_1b_sampled(orc):
@@ -209,3 +217,33 @@ def test_decoder_1b_sampled(orc):
                          ids=["mb24", "mb32", "fp32_buffer"])
 def test_decoder_8b_sampled(orc, mb, qs):
     _sampled_parity(orc, W.decoder_8b_shapes(), f"8.0B, mb {mb}, quantized {qs}", mb, qs)
+
+
+def test_tensor_past_2_31_elements(orc):
+    """One tensor of 2^31 + 1101 elements (offsets past 32-bit range): step 1
+    through the list entry point, step 2 through the single-tensor one,
+    checked at the start, on both sides of element 2^31 and on the ragged
+    tail."""
+    require_gpu()
+    n = (1 << 31) + 1024 + 77
+    mid = 1 << 31
+    rr = [(0, 1 << 12), (mid - (1 << 12), mid + (1 << 12)), (((n - (1 << 12)) // 32) * 32, n)]
+    hp = dict(HP, weight_decay=0.01)
+    p = W.init_param(n, device="cuda", seed=78)
+    want = _start([p[lo:hi] for lo, hi in rr], 24, True)
+    opt = F.FlashSGD([p], **hp)
+    for t in (1, 2):
+        g = W.make_grad(n, t, device="cuda")
+        gs = [u16(g[lo:hi]) for lo, hi in rr]
+        if t == 1:
+            opt.step([g])
+        else:
+            opt.step_tensor(0, g)
+        del g
+        torch.cuda.synchronize()
+        for (lo, hi), w, gb in zip(rr, want, gs):
+            orc.sgd_step(w, gb, _orc_hp(t, hp, 24, True, True))
+            _compare(_snap(opt.states[0], lo, hi), w, f"n = 2^31 + 1101, step {t}, [{lo}, {hi})")
+        print(f"2^31 + 1101 elements, step {t}: samples bit-exact", flush=True)
+    del opt, p
+    torch.cuda.empty_cache()

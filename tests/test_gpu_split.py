@@ -95,3 +95,27 @@ def test_bf16_exact_values_and_zero():
         assert int((r != 0).sum()) == 0
         assert torch.equal(p.view(torch.int16).to(torch.int32) & 0xFFFF,
                            (x.view(torch.int32) >> 16) & 0xFFFF)
+
+
+@pytest.mark.parametrize("mb", [24, 32])
+def test_tensor_past_2_31_elements(orc, mb):
+    """Split and reconstruct of 2^31 + 1101 seeded fp32 masters (N(0, 0.02^2)
+    on the device), checked against the oracle at the start, around elements
+    2^30 (the fp32 stream passes 2^32 bytes) and 2^31 (the bf16 stream
+    does), and on the ragged tail."""
+    require_gpu()
+    n = (1 << 31) + 1024 + 77
+    gen = torch.Generator(device="cuda").manual_seed(92 + mb)
+    x = torch.randn(n, generator=gen, device="cuda").mul_(0.02)
+    p, r = F.flashopt_split(x, mb)
+    back = F.flashopt_reconstruct(p, r, mb)
+    torch.cuda.synchronize()
+    k = 1 << 12
+    for lo, hi in [(0, k), ((1 << 30) - k, (1 << 30) + k), ((1 << 31) - k, (1 << 31) + k), (n - k, n)]:
+        hp, hr = orc.split(host(x[lo:hi]), mb)
+        assert (u16(p[lo:hi]) == hp).all() and (host(r[lo:hi]) == hr).all(), f"[{lo}, {hi})"
+        ob = orc.reconstruct(hp, hr, mb)
+        assert (host(back[lo:hi]).view(np.uint32) == ob.view(np.uint32)).all(), f"[{lo}, {hi})"
+    print(f"split {mb}-bit, 2^31 + 1101 elements: samples bit-exact", flush=True)
+    del x, p, r, back
+    torch.cuda.empty_cache()

@@ -2,11 +2,15 @@
 "code/flashsim/flash_adamw_sim.py", FlashAdamWSim.step / Alg. 4) against the
 oracle, through the C ABI.
 
+Every comparison is free-running: the oracle starts from the same seeded
+parameters with zero moments (the state both sides begin from) and steps its
+own state with the same seeded gradients; no value the GPU computed is ever
+an input of the oracle.
+
 Bar: fp16 scales, rho and the bf16 parameter bit-exact; codes bit-exact
 (contract: >= 99.99% and never more than 1 apart); reconstructed fp32 master
 within 1e-6 relative (implied by bit-exact param and rho).
-  * 2^20 single tensor, 10 steps, 24-bit companded: teacher-forced (the oracle
-    starts every step from the GPU's state) and free-running.
+  * 2^20 single tensor, 10 steps, 24-bit companded; two tensors over 64 steps.
   * ragged multi-tensor lists (sizes 0, 1, 17, ..., 70001) in one launch, all
     master widths and both companding modes, 3 steps.
   * determinism across runs and launch shapes.
@@ -14,7 +18,7 @@ within 1e-6 relative (implied by bit-exact param and rho).
     configuration the benchmark times, checked on group-aligned samples: the
     first and last 2^16 elements of every tensor and random 1024-element
     chunks; the step is elementwise with group-local maxima, so any aligned
-    slice is checked exactly by the oracle on that slice alone.
+    slice is checked exactly by the oracle stepping that slice alone.
 """
 import os
 
@@ -49,6 +53,13 @@ def _snap(s: F.TensorState, lo=0, hi=None) -> oracle.State:
                         host(s.v_codes[lo:hi]), opt(s.v_scales, lambda t: u16(t[g0:g1])))
 
 
+def _start(params, mb, qs=True):
+    """The oracle's starting states: the seeded bf16 parameters (copied before
+    any step) with zero correction bits and zero moments, as the binding
+    allocates them."""
+    return [oracle.State.zeros_like_param(u16(p), mb, quantize_states=qs) for p in params]
+
+
 def _compare(got: oracle.State, want: oracle.State, mb, label: str):
     """mb: 24 | 32 | None (no split).  fp32 moments (no scales) compare bit
     for bit; codes to the contract's bar, held here to equality."""
@@ -78,19 +89,14 @@ def test_single_tensor_10_steps(orc):
     require_gpu()
     n = 1 << 20
     p = W.init_param(n, device="cuda")
+    (free,) = _start([p], 24)
     opt = F.FlashAdamW([p], master_bits=24, companded=True, **HP)
-    free = orc.State.zeros_like_param(u16(p), 24)
     for t in range(1, 11):
         g = W.make_grad(n, t, device="cuda")
-        pre = _snap(opt.states[0])
         opt.step([g])
         torch.cuda.synchronize()
-        post = _snap(opt.states[0])
-        gb = u16(g)
-        orc.adamw_step(pre, gb, _orc_hp(t, 24, True))
-        _compare(post, pre, 24, f"teacher-forced step {t}")
-        orc.adamw_step(free, gb, _orc_hp(t, 24, True))
-        _compare(post, free, 24, f"free-running step {t}")
+        orc.adamw_step(free, u16(g), _orc_hp(t, 24, True))
+        _compare(_snap(opt.states[0]), free, 24, f"step {t}")
         print(f"step {t}: parity ok", flush=True)
 
 
@@ -103,8 +109,8 @@ def test_free_running_64_steps(orc, mb, comp, qs):
     require_gpu()
     sizes = [1 << 17, 50001]
     params = [W.init_param(n, device="cuda", seed=70 + i) for i, n in enumerate(sizes)]
+    host_states = _start(params, mb, qs)
     opt = F.FlashAdamW(params, master_bits=mb, companded=comp, quantize_states=qs, **HP)
-    host_states = [_snap(s) for s in opt.states]
     for t in range(1, 65):
         grads = [W.make_grad(n, t, device="cuda", stream_id=i, factor=float(np.exp(i)))
                  for i, n in enumerate(sizes)]
@@ -138,16 +144,16 @@ def _vid(v):
 def test_ragged_list(orc, mb, comp, qs):
     require_gpu()
     params = [W.init_param(n, device="cuda", seed=10 + i) for i, n in enumerate(RAGGED)]
+    want = _start(params, mb, qs)
     opt = F.FlashAdamW(params, master_bits=mb, companded=comp, quantize_states=qs, **HP)
     for t in range(1, 4):
         grads = [W.make_grad(n, t, device="cuda", stream_id=i, factor=float(np.exp(i - 6)))
                  for i, n in enumerate(RAGGED)]
-        pres = [_snap(s) for s in opt.states]
         opt.step(grads)
         torch.cuda.synchronize()
-        for i, (s, pre, g) in enumerate(zip(opt.states, pres, grads)):
-            orc.adamw_step(pre, u16(g), _orc_hp(t, mb, comp, qs))
-            _compare(_snap(s), pre, mb, f"{_vid((mb, comp, qs))} t{t} tensor{i} n{RAGGED[i]}")
+        for i, (s, w, g) in enumerate(zip(opt.states, want, grads)):
+            orc.adamw_step(w, u16(g), _orc_hp(t, mb, comp, qs))
+            _compare(_snap(s), w, mb, f"{_vid((mb, comp, qs))} t{t} tensor{i} n{RAGGED[i]}")
 
 
 # Hyper-parameter settings away from the default: (name, overrides, first
@@ -169,48 +175,44 @@ HP_GRID = [
                          ids=["mb24-comp", "mb32-lin", "mb24-f32"])
 @pytest.mark.parametrize("name,over,t0", HP_GRID, ids=[h[0] for h in HP_GRID])
 def test_hyper_parameter_grid(orc, name, over, t0, mb, comp, qs):
-    """Three teacher-forced steps from step t0 under each setting: the host's
+    """Three steps from zero moments at step t0 under each setting: the host's
     scalars, the short division's domain checks and the codec across the
     hyper-parameter range."""
     require_gpu()
     hp = dict(HP, **over)
     sizes = [4096 + 5, 70001, 1 << 15]
     params = [W.init_param(n, device="cuda", seed=40 + i) for i, n in enumerate(sizes)]
+    want = _start(params, mb, qs)
     opt = F.FlashAdamW(params, master_bits=mb, companded=comp, quantize_states=qs, **hp)
     opt.t = t0 - 1
     for t in range(t0, t0 + 3):
         grads = [W.make_grad(n, t, device="cuda", stream_id=i, factor=float(np.exp(i - 1)))
                  for i, n in enumerate(sizes)]
-        pres = [_snap(s) for s in opt.states]
         opt.step(grads)
         torch.cuda.synchronize()
-        for i, (st, pre, g) in enumerate(zip(opt.states, pres, grads)):
-            orc.adamw_step(pre, u16(g), oracle.hparams(
+        for i, (st, w, g) in enumerate(zip(opt.states, want, grads)):
+            orc.adamw_step(w, u16(g), oracle.hparams(
                 lr=hp["lr"], betas=hp["betas"], eps=hp["eps"], weight_decay=hp["weight_decay"],
                 step=t, master_bits=mb, companded=comp, quantize_states=qs))
-            _compare(_snap(st), pre, mb, f"{name} t{t} tensor{i}")
+            _compare(_snap(st), w, mb, f"{name} t{t} tensor{i}")
 
 
 @pytest.mark.parametrize("mb,comp,qs", [(None, True, True), (24, True, False)],
                          ids=["mb_none", "fp32_states"])
 def test_ablation_10_steps(orc, mb, comp, qs):
-    """The two ablations over 10 steps on 2^18 params, teacher-forced and
-    free-running against the oracle."""
+    """The two ablations over 10 steps on 2^18 + 77 params against the
+    oracle."""
     require_gpu()
     n = (1 << 18) + 77
     p = W.init_param(n, device="cuda", seed=21)
+    (free,) = _start([p], mb, qs)
     opt = F.FlashAdamW([p], master_bits=mb, companded=comp, quantize_states=qs, **HP)
-    free = orc.State.zeros_like_param(u16(p), mb, quantize_states=qs)
     for t in range(1, 11):
         g = W.make_grad(n, t, device="cuda")
-        pre = _snap(opt.states[0])
         opt.step([g])
         torch.cuda.synchronize()
-        post = _snap(opt.states[0])
-        orc.adamw_step(pre, u16(g), _orc_hp(t, mb, comp, qs))
-        _compare(post, pre, mb, f"{_vid((mb, comp, qs))} teacher-forced step {t}")
         orc.adamw_step(free, u16(g), _orc_hp(t, mb, comp, qs))
-        _compare(post, free, mb, f"{_vid((mb, comp, qs))} free-running step {t}")
+        _compare(_snap(opt.states[0]), free, mb, f"{_vid((mb, comp, qs))} step {t}")
 
 
 def test_zero_and_large_gradients(orc):
@@ -219,17 +221,17 @@ def test_zero_and_large_gradients(orc):
     require_gpu()
     sizes = [4096, 4096, 4096]
     params = [W.init_param(n, device="cuda", seed=40 + i) for i, n in enumerate(sizes)]
+    want = _start(params, 24)
     opt = F.FlashAdamW(params, master_bits=24, **HP)
     for t in range(1, 3):
         grads = [torch.zeros(4096, dtype=torch.bfloat16, device="cuda"),
                  W.make_grad(4096, t, device="cuda", scale=1e2),
                  W.make_grad(4096, t, device="cuda", scale=1e-30)]
-        pres = [_snap(s) for s in opt.states]
         opt.step(grads)
         torch.cuda.synchronize()
-        for i, (s, pre, g) in enumerate(zip(opt.states, pres, grads)):
-            orc.adamw_step(pre, u16(g), _orc_hp(t, 24, True))
-            _compare(_snap(s), pre, 24, f"t{t} tensor{i}")
+        for i, (s, w, g) in enumerate(zip(opt.states, want, grads)):
+            orc.adamw_step(w, u16(g), _orc_hp(t, 24, True))
+            _compare(_snap(s), w, 24, f"t{t} tensor{i}")
     assert int(opt.states[0].m_scales.abs().sum()) == 0
 
 
@@ -297,16 +299,16 @@ def test_lanes_outside_short_division_domain(orc, case, mb, comp, qs):
     n = 16 * 1024 + 77
     hp = dict(HP, eps=EDGE_EPS[case])
     p = W.init_param(n, device="cuda", seed=90)
+    (want,) = _start([p], mb, qs)
     opt = F.FlashAdamW([p], master_bits=mb, companded=comp, quantize_states=qs, **hp)
     for t in range(1, 4):
         g = _edge_grad(case, n, t)
-        pre = _snap(opt.states[0])
         opt.step([g])
         torch.cuda.synchronize()
-        orc.adamw_step(pre, u16(g), oracle.hparams(
+        orc.adamw_step(want, u16(g), oracle.hparams(
             lr=hp["lr"], betas=hp["betas"], eps=hp["eps"], weight_decay=hp["weight_decay"],
             step=t, master_bits=mb, companded=comp, quantize_states=qs))
-        _compare_nan_aware(_snap(opt.states[0]), pre, mb, f"{case} mb{mb} comp{comp} t{t}")
+        _compare_nan_aware(_snap(opt.states[0]), want, mb, f"{case} mb{mb} comp{comp} t{t}")
 
 
 def test_deterministic_across_runs_and_launch_shapes():
@@ -354,25 +356,29 @@ def _sample_ranges(n, rng, k=2):
 
 
 def _sampled_parity(orc, shapes, mb, comp, label, qs=True):
+    """Two list steps over the whole list; after each, every sample is
+    compared with the oracle stepping that slice from the same seeded start
+    (step 1 starts from zero moments, step 2 from non-trivial ones)."""
     opt = _build_list(shapes, mb, comp, seed_base=1000, qs=qs)
     factors = W.grad_factors(len(shapes)).numpy()
     rng = np.random.default_rng(7)
-    opt.step(_grads(shapes, 1, factors))            # step 1: states become non-trivial
-    grads = _grads(shapes, 2, factors)
     ranges = [_sample_ranges(s.param.numel(), rng) for s in opt.states]
-    torch.cuda.synchronize()
-    pres = [[_snap(s, lo, hi) for lo, hi in rr] for s, rr in zip(opt.states, ranges)]
-    gs = [[u16(g[lo:hi]) for lo, hi in rr] for g, rr in zip(grads, ranges)]
-    opt.step(grads)
-    torch.cuda.synchronize()
+    want = [[oracle.State.zeros_like_param(u16(s.param[lo:hi]), mb, quantize_states=qs)
+             for lo, hi in rr] for s, rr in zip(opt.states, ranges)]
     checked = 0
-    for i, (s, rr) in enumerate(zip(opt.states, ranges)):
-        for (lo, hi), pre, g in zip(rr, pres[i], gs[i]):
-            orc.adamw_step(pre, g, _orc_hp(2, mb, comp, qs))
-            _compare(_snap(s, lo, hi), pre, mb, f"{label} tensor {i} [{lo}, {hi})")
-            checked += hi - lo
-    print(f"{label}: {checked} sampled elements bit-exact", flush=True)
-    del opt, grads
+    for t in (1, 2):
+        grads = _grads(shapes, t, factors)
+        gs = [[u16(g[lo:hi]) for lo, hi in rr] for g, rr in zip(grads, ranges)]
+        opt.step(grads)
+        del grads
+        torch.cuda.synchronize()
+        for i, (s, rr) in enumerate(zip(opt.states, ranges)):
+            for (lo, hi), w, g in zip(rr, want[i], gs[i]):
+                orc.adamw_step(w, g, _orc_hp(t, mb, comp, qs))
+                _compare(_snap(s, lo, hi), w, mb, f"{label} step {t} tensor {i} [{lo}, {hi})")
+                checked += hi - lo
+    print(f"{label}: {checked} sampled elements bit-exact over two steps", flush=True)
+    del opt
     torch.cuda.empty_cache()
 
 
@@ -399,3 +405,41 @@ def test_decoder_8b_sampled_ablations(orc, mb, qs):
     for them (--master-bits 0, --fp32-states)."""
     require_gpu()
     _sampled_parity(orc, W.decoder_8b_shapes(), mb, True, f"8.0B list, mb {mb}, quantized {qs}", qs=qs)
+
+
+# One tensor past 2^31 elements: element offsets, the byte offsets of the
+# 16-bit streams (past 2^32 bytes at element 2^31) and the chunk arithmetic
+# leave 32-bit range.  Samples: the start, both sides of element 2^31, and
+# the ragged tail (the last chunk holds 77 elements).
+N_PAST_2_31 = (1 << 31) + 1024 + 77
+
+
+def _past_2_31_ranges(n):
+    mid = 1 << 31
+    return [(0, 1 << 12), (mid - (1 << 12), mid + (1 << 12)), (((n - (1 << 12)) // 32) * 32, n)]
+
+
+def test_tensor_past_2_31_elements(orc):
+    """Step 1 through the list entry point, step 2 through the single-tensor
+    entry point, each checked against the oracle on the samples."""
+    require_gpu()
+    n = N_PAST_2_31
+    p = W.init_param(n, device="cuda", seed=77)
+    rr = _past_2_31_ranges(n)
+    want = [oracle.State.zeros_like_param(u16(p[lo:hi]), 24) for lo, hi in rr]
+    opt = F.FlashAdamW([p], master_bits=24, companded=True, **HP)
+    for t in (1, 2):
+        g = W.make_grad(n, t, device="cuda")
+        gs = [u16(g[lo:hi]) for lo, hi in rr]
+        if t == 1:
+            opt.step([g])
+        else:
+            opt.step_tensor(0, g)
+        del g
+        torch.cuda.synchronize()
+        for (lo, hi), w, gb in zip(rr, want, gs):
+            orc.adamw_step(w, gb, _orc_hp(t, 24, True))
+            _compare(_snap(opt.states[0], lo, hi), w, 24, f"n = 2^31 + 1101, step {t}, [{lo}, {hi})")
+        print(f"2^31 + 1101 elements, step {t}: samples bit-exact", flush=True)
+    del opt, p
+    torch.cuda.empty_cache()
