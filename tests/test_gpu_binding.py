@@ -1,7 +1,8 @@
 """The Python binding's step driver on the GPU: the descriptor table it caches
 between list steps is rebuilt whenever a gradient's storage changes, the
-gradients are validated before anything is launched, and no reference to
-them outlives the call."""
+gradients are validated before anything is launched, no reference to them
+outlives the call, and optimizers stepped from several threads on their own
+streams at once give the same bits as one at a time."""
 import gc
 import weakref
 
@@ -84,3 +85,60 @@ def test_gradients_are_not_kept_alive():
     del g
     gc.collect()
     assert all(r() is None for r in refs)
+
+
+def test_threads_on_their_own_streams_match_sequential_steps():
+    """Four host threads, each stepping its own optimizer on its own stream
+    (default priority) at once, share the library's pinned staging ring:
+    every state must equal the same steps run one optimizer at a time."""
+    import threading
+
+    require_gpu()
+    kinds = ["adamw", "sgd", "adamw", "sgd"]
+
+    def make(k, seed):
+        params = [W.init_param(n, device="cuda", seed=seed + i) for i, n in enumerate(SIZES)]
+        if k == "adamw":
+            return F.FlashAdamW(params, **HP)
+        return F.FlashSGD(params, lr=1e-2, momentum=0.9, weight_decay=0.01)
+
+    grads = [[[W.make_grad(n, t, device="cuda", stream_id=10 * j + i) for i, n in enumerate(SIZES)]
+              for t in range(1, 9)] for j in range(len(kinds))]
+    torch.cuda.synchronize()
+    seq = [make(k, 100 + 10 * j) for j, k in enumerate(kinds)]
+    for j, opt in enumerate(seq):
+        for g in grads[j]:
+            opt.step(g)
+    torch.cuda.synchronize()
+
+    par = [make(k, 100 + 10 * j) for j, k in enumerate(kinds)]
+    streams = [torch.cuda.Stream() for _ in kinds]
+    torch.cuda.synchronize()
+    errors = []
+
+    def run(j):
+        try:
+            with torch.cuda.stream(streams[j]):
+                for g in grads[j]:
+                    par[j].step(g)
+        except Exception as e:          # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(j,)) for j in range(len(kinds))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for j, (a, b) in enumerate(zip(seq, par)):
+        for x, y in zip(_state_bits(a) if kinds[j] == "adamw" else _sgd_bits(a),
+                        _state_bits(b) if kinds[j] == "adamw" else _sgd_bits(b)):
+            assert (x == y).all(), f"optimizer {j} ({kinds[j]})"
+
+
+def _sgd_bits(opt):
+    out = []
+    for s in opt.states:
+        out += [u16(s.param), s.rho.cpu().numpy(), s.m_codes.cpu().numpy(), u16(s.m_scales)]
+    return out
