@@ -174,7 +174,11 @@ size_t flashopt_adamw_workspace_bytes(const flashopt_tensor *tensors, int n_tens
  *             overwritten; it must not be reused by another call until this
  *             step has run on `stream`
  * The descriptor table is staged through a pinned host buffer that the
- * library allocates once and reuses (hipHostMalloc).
+ * library allocates once and reuses (hipHostMalloc).  That staging is an
+ * ordinary asynchronous host-to-device copy from reused memory, so a call
+ * captured into a HIP graph would replay whatever the buffer holds at replay
+ * time: do not capture this call.  flashopt_adamw_step_tensor launches one
+ * kernel with its arguments by value and stages nothing.
  * Errors: EINVAL (n_tensors < 0, NULL tensors/args, numel < 0, NULL pointer
  * that the variant uses in a non-empty tensor, master_bits, companded,
  * fp32_states, reserved != 0, step < 1, lr < 0, beta outside

@@ -175,3 +175,33 @@ def test_hook_driven_steps_match_oracle(orc, kind):
                 assert (u16(s.v_scales) == st.v_scales).all(), f"{kind} t{t} tensor {i}: v scales"
     for h in handles:
         h.remove()
+
+
+@pytest.mark.parametrize("kind", ["adamw", "sgd"])
+def test_tensor_steps_replay_from_a_hip_graph(kind):
+    """The single-tensor entry points stage nothing, so their launches can be
+    captured into a HIP graph: three replays, with eager work and a
+    synchronize between them, each equal the same eager launches (the step
+    count, a kernel argument, is the captured one: t = 1 every time)."""
+    require_gpu()
+    sizes = [4096 + 5, 70001, 33]
+    pa = [W.init_param(n, device="cuda", seed=600 + i) for i, n in enumerate(sizes)]
+    pb = [p.clone() for p in pa]
+    a, b = _make(kind, pa, 24, True), _make(kind, pb, 24, True)
+    grads = [W.make_grad(n, 1, device="cuda", stream_id=i) for i, n in enumerate(sizes)]
+    side = torch.randn(1 << 20, device="cuda")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i, g in enumerate(grads):
+            a.step_tensor(i, g)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        graph.replay()
+        side.mul_(1.0001).add_(rep)                 # eager work between replays
+        for i, g in enumerate(grads):
+            b.ts[i] = 0                             # the captured launches step with t = 1
+            b.step_tensor(i, g)
+        torch.cuda.synchronize()
+        for i, (sa, sb) in enumerate(zip(a.states, b.states)):
+            _assert_same(sa, sb, f"{kind} replay {rep} tensor {i}")
