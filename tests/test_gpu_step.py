@@ -443,3 +443,32 @@ def test_tensor_past_2_31_elements(orc):
         print(f"2^31 + 1101 elements, step {t}: samples bit-exact", flush=True)
     del opt, p
     torch.cuda.empty_cache()
+
+
+def test_shards_of_a_tensor_equal_the_whole_tensor():
+    """The sharded design steps 32-aligned ranges of a tensor independently
+    (each rank owns one range and its state).  Eight uneven shards stepped as
+    views of one parameter, in one list launch, must leave the parameter,
+    and states equal to the slices of the whole tensor's state, bit for bit."""
+    require_gpu()
+    n = (1 << 20) + 77
+    cuts = [0, 32 * 1000, 32 * 1001, 32 * 7777, 32 * 8000, 32 * 15000, 32 * 20000, 32 * 32000, n]
+    pw = W.init_param(n, device="cuda", seed=55)
+    ps = pw.clone()
+    whole = F.FlashAdamW([pw], master_bits=24, companded=True, **HP)
+    shards = F.FlashAdamW([ps[a:b] for a, b in zip(cuts[:-1], cuts[1:])], master_bits=24,
+                          companded=True, **HP)
+    for t in range(1, 4):
+        g = W.make_grad(n, t, device="cuda")
+        whole.step([g])
+        shards.step([g[a:b] for a, b in zip(cuts[:-1], cuts[1:])])
+        torch.cuda.synchronize()
+        assert torch.equal(pw.view(torch.int16), ps.view(torch.int16)), f"t{t}: param"
+        ws = whole.states[0]
+        for k, (a, b) in enumerate(zip(cuts[:-1], cuts[1:])):
+            s = shards.states[k]
+            for name in ("rho", "m_codes", "v_codes"):
+                assert torch.equal(getattr(s, name), getattr(ws, name)[a:b]), f"t{t} shard {k}: {name}"
+            for name in ("m_scales", "v_scales"):
+                assert torch.equal(getattr(s, name), getattr(ws, name)[a // 32:(b + 31) // 32]), \
+                    f"t{t} shard {k}: {name}"
