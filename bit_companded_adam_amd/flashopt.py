@@ -199,8 +199,8 @@ class TensorState:
 
     def __init__(self, param: torch.Tensor, master_bits=24, quantize_states: bool = True,
                  variance: bool = True):
-        if param.dtype != torch.bfloat16 or not param.is_contiguous():
-            raise ValueError("param must be a contiguous bf16 tensor")
+        if param.dtype != torch.bfloat16 or not param.is_contiguous() or not param.is_cuda:
+            raise ValueError("param must be a contiguous bf16 device tensor")
         if master_bits not in (24, 32, None):
             raise ValueError("master_bits must be 24, 32 or None")
         n, dev = param.numel(), param.device
@@ -221,6 +221,8 @@ class TensorState:
     def descriptor(self, grad: torch.Tensor) -> flashopt_tensor:
         if grad.dtype != torch.bfloat16 or grad.numel() != self.param.numel():
             raise ValueError("grad must be bf16 with the parameter's size")
+        if grad.device != self.param.device:
+            raise ValueError(f"grad is on {grad.device}, its parameter on {self.param.device}")
         opt = lambda t, name: 0 if t is None else _dev(t, name)
         return flashopt_tensor(_dev(self.param, "param"), _dev(grad, "grad"),
                                opt(self.rho, "rho"), _dev(self.m_codes, "m_codes"),
@@ -268,6 +270,10 @@ class _Stepper:
     counting its own steps as the pages' per-parameter state does)."""
 
     def _init_common(self):
+        devices = {s.param.device for s in self.states}
+        if len(devices) > 1:
+            raise ValueError(f"all parameters must be on one device, got {sorted(map(str, devices))}")
+        self.device = devices.pop() if devices else None
         self.t = 0
         self.ts = [0] * len(self.states)
         self._key = None
@@ -285,13 +291,23 @@ class _Stepper:
         if key != self._key:
             self._desc = descriptor_array(self.states, grads)
             self._key = key
+        self._check_stream(stream)
         self.t += 1
         self.ts = [self.t] * len(self.states)
-        self._list_step(self._desc, self.t, stream)
+        with torch.cuda.device(self.device):    # the library launches on the current device
+            self._list_step(self._desc, self.t, stream)
 
     def step_tensor(self, i: int, grad: torch.Tensor, stream=None):
+        desc = self.states[i].descriptor(grad)
+        self._check_stream(stream)
         self.ts[i] += 1
-        self._tensor_step(self.states[i].descriptor(grad), self.ts[i], stream)
+        with torch.cuda.device(self.device):
+            self._tensor_step(desc, self.ts[i], stream)
+
+    def _check_stream(self, stream):
+        dev = getattr(stream, "device", None)
+        if dev is not None and self.device is not None and dev != self.device:
+            raise ValueError(f"stream is on {dev}, the parameters on {self.device}")
 
 
 def attach_grad_release(opt, params):
@@ -318,10 +334,9 @@ class FlashAdamW(_Stepper):
         self.hp = dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay,
                        master_bits=master_bits, companded=companded,
                        quantize_states=quantize_states)
-        dev = self.states[0].param.device if self.states else "cuda"
-        nbytes = max(16, flashopt_adamw_workspace_bytes(len(self.states)))
-        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         self._init_common()
+        nbytes = max(16, flashopt_adamw_workspace_bytes(len(self.states)))
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device or "cuda")
 
     def _list_step(self, desc, t, stream):
         flashopt_adamw_step(desc, make_args(t, **self.hp), self.workspace, stream)
@@ -369,10 +384,9 @@ class FlashSGD(_Stepper):
         self.hp = dict(lr=lr, momentum=momentum, dampening=dampening, weight_decay=weight_decay,
                        nesterov=nesterov, master_bits=master_bits, companded=companded,
                        quantize_states=quantize_states)
-        dev = self.states[0].param.device if self.states else "cuda"
-        nbytes = max(16, flashopt_sgd_workspace_bytes(len(self.states)))
-        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         self._init_common()
+        nbytes = max(16, flashopt_sgd_workspace_bytes(len(self.states)))
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device or "cuda")
 
     def _list_step(self, desc, t, stream):
         flashopt_sgd_step(desc, make_sgd_args(t, **self.hp), self.workspace, stream)

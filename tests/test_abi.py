@@ -138,6 +138,9 @@ def test_binding_refuses_host_tensors(L):
     import torch
     with pytest.raises(ValueError):
         F.flashopt_quantize(torch.zeros(64), F.SPEC_MOMENTUM)
+    for make in (F.FlashAdamW, F.FlashSGD):            # host parameters: refused at construction
+        with pytest.raises(ValueError):
+            make([torch.zeros(64, dtype=torch.bfloat16)])
 
 
 def test_sgd_step_validation(L):
