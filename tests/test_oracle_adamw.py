@@ -12,8 +12,10 @@
   run through the (separately pinned) codec; with a 24-bit master each step
   equals that run teacher-forced from the rebuilt master.
 * The OpenMP slice driver equals the per-tensor step bit for bit.
-The values of a long free-running trajectory have no independent pin beyond
-this composition (parity unpinned for the trajectory itself)."""
+* 300 free-running steps with fp32 moments and the 32-bit master track
+  torch.optim.AdamW within a derived rounding bound.
+A long trajectory with quantized states or the 24-bit master has no
+independent pin beyond this composition (parity unpinned for it)."""
 import numpy as np
 import pytest
 import torch
@@ -213,3 +215,34 @@ def test_bad_arguments_rejected(orc):
         orc.adamw_step(st, p, orc.hparams(step=0))
     with pytest.raises(ValueError):
         orc.adamw_step(st, p, orc.hparams(step=1, master_bits=16))
+
+
+def test_long_trajectory_tracks_torch_adamw(orc):
+    """300 free-running steps of the oracle's step with fp32 moments and the
+    lossless 32-bit master (so its master is a plain fp32 AdamW parameter)
+    against torch.optim.AdamW fed the same bf16 gradients.  Per step the two
+    thetas drift apart by rounding only: the decay product and the final
+    subtraction round once each (at most 2^-23 |theta| together, |theta| <
+    0.25 here), the update (|u| <= 10 lr) differs by a few of its own ulps,
+    and a v that differs by at most ~500 ulps (rounding error decaying with
+    beta2) changes the update by under 2e-8.  Summed over 300 steps that is
+    below 3e-5 absolute; a wrong bias correction, coupled weight decay or a
+    dropped term moves theta by 1e-4 or more."""
+    rng = np.random.default_rng(8)
+    n, steps = 1 << 14, 300
+    p0 = _bf16_bits((rng.standard_normal(n) * 0.02).astype(np.float32))
+    st = orc.State.zeros_like_param(p0, 32, quantize_states=False)
+    p = torch.nn.Parameter(torch.from_numpy(_bits_to_f32(p0).copy()))
+    opt = torch.optim.AdamW([p], lr=HP["lr"], betas=HP["betas"], eps=HP["eps"],
+                            weight_decay=HP["weight_decay"], foreach=False, fused=False)
+    for t in range(1, steps + 1):
+        g = _bf16_bits((rng.standard_normal(n) * 1e-3 * np.exp(rng.standard_normal())).astype(np.float32))
+        orc.adamw_step(st, g, orc.hparams(**HP, step=t, master_bits=32, quantize_states=False))
+        p.grad = torch.from_numpy(_bits_to_f32(g).copy())
+        opt.step()
+        if t in (1, 10, 100, steps):
+            th = orc.reconstruct(st.param, st.rho, 32).astype(np.float64)
+            assert np.abs(th).max() < 0.25
+            assert (np.abs(th - p.detach().numpy()) <= 3e-5).all(), t
+            v_ref = opt.state[p]["exp_avg_sq"].numpy().astype(np.float64)
+            assert (np.abs(st.v_codes - v_ref) <= 1e-4 * v_ref).all(), t
