@@ -11,8 +11,10 @@ torch.optim.SGD with momentum, the buffer stored with the momentum spec.
   composition of the (separately pinned) codec and update.
 * Without quantization and without a split, the parameter is torch's bf16
   cast of the fp32 update.
-The values of a long free-running trajectory have no independent pin beyond
-this composition (parity unpinned for the trajectory itself)."""
+* 300 free-running steps with an fp32 buffer and the 32-bit master track
+  torch.optim.SGD within a derived rounding bound.
+A long trajectory with a quantized buffer or the 24-bit master has no
+independent pin beyond this composition (parity unpinned for it)."""
 import numpy as np
 import pytest
 import torch
@@ -125,3 +127,34 @@ def test_bad_arguments_rejected(orc):
         orc.sgd_step(st, g, orc.sgd_hparams(step=0))
     with pytest.raises(ValueError):
         orc.sgd_step(st, g, orc.sgd_hparams(master_bits=16))
+
+
+@pytest.mark.parametrize("dampening,nesterov,wd", [(0.0, False, 0.01), (0.0, True, 0.01), (0.1, False, 0.0)])
+def test_long_trajectory_tracks_torch_sgd(orc, dampening, nesterov, wd):
+    """300 free-running steps of the oracle's FlashSGD step with an fp32
+    buffer and the lossless 32-bit master against torch.optim.SGD fed the
+    same bf16 gradients.  The thetas drift apart by rounding only: the final
+    subtraction rounds once per step (at most 2^-24 |theta|, |theta| < 0.25
+    here), and the buffers' rounding differences decay with the momentum
+    (a steady ~10 ulps of the buffer, times lr, per step).  Over 300 steps
+    that stays below 1e-5; a dropped or misplaced momentum, dampening or
+    weight-decay term moves theta by far more."""
+    rng = np.random.default_rng(12)
+    n, steps, lr, mu = 1 << 14, 300, 1e-2, 0.9
+    p0 = _bf16_bits((rng.standard_normal(n) * 0.02).astype(np.float32))
+    st = orc.State.zeros_like_param(p0, 32, quantize_states=False)
+    st.v_codes = st.v_scales = None
+    p = torch.nn.Parameter(torch.from_numpy(_bits_to_f32(p0).copy()))
+    opt = torch.optim.SGD([p], lr=lr, momentum=mu, dampening=dampening, nesterov=nesterov,
+                          weight_decay=wd, foreach=False)
+    for t in range(1, steps + 1):
+        g = _bf16_bits((rng.standard_normal(n) * 1e-3 * np.exp(rng.standard_normal())).astype(np.float32))
+        orc.sgd_step(st, g, orc.sgd_hparams(lr=lr, momentum=mu, dampening=dampening, weight_decay=wd,
+                                            nesterov=nesterov, step=t, master_bits=32,
+                                            quantize_states=False))
+        p.grad = torch.from_numpy(_bits_to_f32(g).copy())
+        opt.step()
+        if t in (1, 10, 100, steps):
+            th = orc.reconstruct(st.param, st.rho, 32).astype(np.float64)
+            assert np.abs(th).max() < 0.25
+            assert (np.abs(th - p.detach().numpy()) <= 1e-5).all(), t
