@@ -114,6 +114,7 @@ SGD_GRID = [
     ("lr_1", dict(lr=1.0, weight_decay=0.1), 1),
     ("lr_1e-6", dict(lr=1e-6), 3),
     ("nesterov_0.95", dict(momentum=0.95, nesterov=True, weight_decay=0.001), 2),
+    ("lr_0", dict(lr=0.0, weight_decay=0.01), 1),
 ]
 
 

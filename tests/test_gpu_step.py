@@ -158,7 +158,7 @@ def test_ragged_list(orc, mb, comp, qs):
 
 # Hyper-parameter settings away from the default: (name, overrides, first
 # step).  beta 0 (no averaging), a large k2 = 1/sqrt(1 - 0.9999) = 100, bias
-# corrections at 1 (step 10^6), learning rates from 1e-6 to 1, no weight
+# corrections at 1 (step 10^6), learning rates 0 and 1e-6 to 1, no weight
 # decay, a large eps.
 HP_GRID = [
     ("betas_zero", dict(betas=(0.0, 0.0)), 1),
@@ -168,6 +168,7 @@ HP_GRID = [
     ("lr_1_wd_0.1", dict(lr=1.0, weight_decay=0.1), 1),
     ("lr_1e-6_wd_0", dict(lr=1e-6, weight_decay=0.0), 5),
     ("eps_1e-3", dict(eps=1e-3), 2),
+    ("lr_0", dict(lr=0.0, weight_decay=0.1), 1),       # the master must come back unchanged
 ]
 
 
@@ -183,6 +184,7 @@ def test_hyper_parameter_grid(orc, name, over, t0, mb, comp, qs):
     sizes = [4096 + 5, 70001, 1 << 15]
     params = [W.init_param(n, device="cuda", seed=40 + i) for i, n in enumerate(sizes)]
     want = _start(params, mb, qs)
+    init = [w.param.copy() for w in want]
     opt = F.FlashAdamW(params, master_bits=mb, companded=comp, quantize_states=qs, **hp)
     opt.t = t0 - 1
     for t in range(t0, t0 + 3):
@@ -195,6 +197,8 @@ def test_hyper_parameter_grid(orc, name, over, t0, mb, comp, qs):
                 lr=hp["lr"], betas=hp["betas"], eps=hp["eps"], weight_decay=hp["weight_decay"],
                 step=t, master_bits=mb, companded=comp, quantize_states=qs))
             _compare(_snap(st), w, mb, f"{name} t{t} tensor{i}")
+            if hp["lr"] == 0.0:
+                assert (u16(st.param) == init[i]).all(), f"{name}: lr 0 changed the parameter"
 
 
 @pytest.mark.parametrize("mb,comp,qs", [(None, True, True), (24, True, False)],
