@@ -149,13 +149,21 @@ def environment() -> dict:
     return env
 
 
-def time_steps(opt, grads, steps: int, warmup: int, per_tensor: bool = False):
+def time_steps(opt, grads, steps: int, warmup: int, per_tensor: bool = False,
+               batch_below: int = 0):
     """per_tensor: the gradient-release launch pattern, one single-tensor
-    launch per tensor (the step is then the whole sequence of launches)."""
+    launch per tensor (the step is then the whole sequence of launches);
+    tensors with fewer than batch_below elements are instead stepped together
+    in one list launch after the others (attach_grad_release's batching)."""
+    small = [i for i, g in enumerate(grads) if g.numel() < batch_below]
+    large = [i for i, g in enumerate(grads) if g.numel() >= batch_below]
+
     def one_step(stream=None):
         if per_tensor:
-            for i, g in enumerate(grads):
-                opt.step_tensor(i, g, stream)
+            for i in large:
+                opt.step_tensor(i, grads[i], stream)
+            if small:
+                opt.step_tensors(small, [grads[i] for i in small], stream)
         else:
             opt.step(grads, stream)
 
@@ -319,6 +327,8 @@ def main():
                     help="unquantized fp32 moments (weight-splitting-only ablation)")
     ap.add_argument("--optimizer", default="adamw", choices=("adamw", "sgd"),
                     help="sgd: the FlashSGD step (momentum buffer only)")
+    ap.add_argument("--batch-below", type=int, default=0,
+                    help="with --grad-release: step tensors below this many elements together")
     ap.add_argument("--grad-release", action="store_true",
                     help="one single-tensor launch per tensor (the gradient-release pattern)")
     ap.add_argument("--cpu-elems", type=int, default=1 << 27,
@@ -357,7 +367,7 @@ def main():
     print(f"# workload ready: {len(opt.states)} tensors, {n} params, "
           f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated", file=sys.stderr, flush=True)
 
-    wall, per = time_steps(opt, grads, args.steps, args.warmup, args.grad_release)
+    wall, per = time_steps(opt, grads, args.steps, args.warmup, args.grad_release, args.batch_below)
     env = environment()                     # clocks read right after the timed steps
     ms_step = wall * 1e3 / args.steps
     ms_launch = float(np.mean(per))
@@ -366,6 +376,7 @@ def main():
     achieved = alg_bytes / (ms_launch * 1e-3) / 1e9
     print(f"# per-launch ms: mean {ms_launch:.3f} median {np.median(per):.3f} "
           f"min {min(per):.3f} max {max(per):.3f}", file=sys.stderr, flush=True)
+    sizes = [s.param.numel() for s in opt.states]
     del opt, grads
     torch.cuda.empty_cache()
 
@@ -376,8 +387,13 @@ def main():
         ("decoder-8b-list", 24, True, True, "adamw", False)
     name = args.workload + ("" if comp else "-linear") + ("" if qs else "-fp32-states") + \
         ("-no-split" if mb == 0 else "") + ("-flashsgd" if args.optimizer == "sgd" else "") + \
-        ("-per-tensor-launches" if args.grad_release else "")
+        ("-per-tensor-launches" if args.grad_release else "") + \
+        (f"-batched-below-{args.batch_below}" if args.grad_release and args.batch_below else "")
 
+    launches = 1
+    if args.grad_release:
+        small = sum(1 for n in sizes if n < args.batch_below)
+        launches = len(sizes) - small + (1 if small else 0)
     metric = METRIC
     if args.optimizer == "sgd":      # same measure for the FlashSGD step, at its own bytes/param
         metric = f"FlashSGD step Gparam/s and % of HBM roofline ({bpp:g} B/param), 1 GPU"
@@ -397,7 +413,7 @@ def main():
         "config": {"workload": name, "params": n, "tensors": n_tensors,
                    "master_bits": mb, "companded": comp, "quantized_states": qs,
                    "bytes_per_param": bpp,
-                   "launches_per_step": n_tensors if args.grad_release else 1},
+                   "launches_per_step": launches},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": traffic_per_launch() if default else None,

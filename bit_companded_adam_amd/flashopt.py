@@ -304,22 +304,58 @@ class _Stepper:
         with torch.cuda.device(self.device):
             self._tensor_step(desc, self.ts[i], stream)
 
+    def step_tensors(self, indices, grads, stream=None):
+        """Step a subset of the tensors (indices, each at most once) with one
+        list launch per distinct step count: the same results as
+        step_tensor() on each, in fewer launches."""
+        indices, grads = list(indices), list(grads)
+        if len(indices) != len(grads) or len(set(indices)) != len(indices):
+            raise ValueError("indices must be distinct and match the gradients")
+        descs = [self.states[i].descriptor(g) for i, g in zip(indices, grads)]
+        self._check_stream(stream)
+        by_t = {}
+        for i, d in zip(indices, descs):
+            self.ts[i] += 1
+            by_t.setdefault(self.ts[i], []).append(d)
+        with torch.cuda.device(self.device):
+            for t, ds in by_t.items():
+                arr = (flashopt_tensor * len(ds))(*ds)
+                self._list_step(arr, t, stream)
+
     def _check_stream(self, stream):
         dev = getattr(stream, "device", None)
         if dev is not None and self.device is not None and dev != self.device:
             raise ValueError(f"stream is on {dev}, the parameters on {self.device}")
 
 
-def attach_grad_release(opt, params):
+def attach_grad_release(opt, params, batch_below: int = 0):
     """Gradient release: register a post-accumulate-grad hook on every
     parameter that runs that tensor's step as soon as its gradient is
     complete and then frees the gradient, so a full set of gradients is never
-    held.  params are the optimizer's parameters, in its order.  Returns the
-    hook handles."""
+    held.  params are the optimizer's parameters, in its order.
+
+    batch_below > 0: a parameter with fewer elements is not launched on its
+    own; its (small) gradient is kept until the backward pass ends and all
+    such parameters are stepped together in one list launch, which saves a
+    kernel launch per small tensor (norm vectors, biases).  The results are
+    the same bits.  Returns the hook handles."""
     index = {id(p): i for i, p in enumerate(params)}
+    pending = []
+
+    def flush():
+        if pending:
+            idx, grads = zip(*pending)
+            pending.clear()
+            opt.step_tensors(idx, grads)
 
     def hook(p):
-        opt.step_tensor(index[id(p)], p.grad)
+        i = index[id(p)]
+        if p.numel() < batch_below:
+            if not pending:        # run once when this backward pass ends
+                torch.autograd.Variable._execution_engine.queue_callback(flush)
+            pending.append((i, p.grad))
+        else:
+            opt.step_tensor(i, p.grad)
         p.grad = None
 
     return [p.register_post_accumulate_grad_hook(hook) for p in params]

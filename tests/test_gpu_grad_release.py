@@ -205,3 +205,58 @@ def test_tensor_steps_replay_from_a_hip_graph(kind):
         torch.cuda.synchronize()
         for i, (sa, sb) in enumerate(zip(a.states, b.states)):
             _assert_same(sa, sb, f"{kind} replay {rep} tensor {i}")
+
+
+@pytest.mark.parametrize("kind", ["adamw", "sgd"])
+def test_step_tensors_equals_single_tensor_steps(kind):
+    """A subset stepped by step_tensors (one list launch per step count)
+    leaves the bits step_tensor gives tensor by tensor, also when the subset
+    mixes step counts."""
+    require_gpu()
+    pa = [W.init_param(n, device="cuda", seed=700 + i) for i, n in enumerate(RAGGED)]
+    pb = [p.clone() for p in pa]
+    a, b = _make(kind, pa, 24, True), _make(kind, pb, 24, True)
+    for t in range(1, 4):
+        grads = [W.make_grad(n, t, device="cuda", stream_id=i) for i, n in enumerate(RAGGED)]
+        subset = [i for i in range(len(RAGGED)) if (i + t) % 3 != 0]   # counts drift apart
+        a.step_tensors(subset, [grads[i] for i in subset])
+        for i in subset:
+            b.step_tensor(i, grads[i])
+        torch.cuda.synchronize()
+        assert a.ts == b.ts
+        for i, (sa, sb) in enumerate(zip(a.states, b.states)):
+            _assert_same(sa, sb, f"{kind} t{t} tensor{i}")
+
+
+@pytest.mark.parametrize("kind", ["adamw", "sgd"])
+def test_batched_small_tensors_match_list_step(kind):
+    """attach_grad_release with batch_below: the biases (64 to 1017
+    elements) are stepped together in one launch when the backward pass
+    ends, the weights one by one as their gradients complete; every
+    gradient is freed and the states equal a list step's."""
+    require_gpu()
+    model = _mlp(6)
+    params = list(model.parameters())
+    init = [p.detach().clone() for p in params]
+    opt = _make(kind, params, 24, True)
+    seen = {}
+
+    def record(p):
+        seen.setdefault(id(p), []).append(p.grad.detach().clone())
+
+    rec = [p.register_post_accumulate_grad_hook(record) for p in params]
+    handles = F.attach_grad_release(opt, params, batch_below=2048)
+    ref = _make(kind, [q.clone() for q in init], 24, True)
+    gen = torch.Generator(device="cuda").manual_seed(18)
+    for step in range(3):
+        x = torch.randn(32, 192, device="cuda", generator=gen).to(torch.bfloat16)
+        model(x).float().square().mean().backward()
+        torch.cuda.synchronize()
+        assert all(p.grad is None for p in params), "gradients must be freed"
+        assert opt.ts == [step + 1] * len(params)
+        ref.step([seen[id(p)][step] for p in params])
+        torch.cuda.synchronize()
+        for i, (sa, sb) in enumerate(zip(opt.states, ref.states)):
+            _assert_same(sa, sb, f"{kind} step {step} tensor {i}")
+    for h in handles + rec:
+        h.remove()
