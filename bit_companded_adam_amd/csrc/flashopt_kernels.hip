@@ -7,7 +7,8 @@
 // parameter and correction bits, eq_ecc()).
 //
 // Layout of the work: a wavefront owns 1024-element chunks (two in a row for
-// the multi-tensor steps) and each lane 16 elements of a chunk, taken as
+// the multi-tensor steps, with workgroups renumbered so that each XCD streams
+// one contiguous region) and each lane 16 elements of a chunk, taken as
 // units of N consecutive elements placed so that every memory instruction of
 // the wavefront covers one contiguous block of each stream (unit u of lane l
 // starts at element 64 N u + N l).  The quantized steps use N = 8 (a lane
@@ -1186,11 +1187,27 @@ __device__ __forceinline__ void sgd_unit(const ChunkPtrs &c, int u, int lane,
 
 // ------------------------------------------------------------- kernels
 
+// Workgroup index renumbered so that each of the 8 XCDs takes one contiguous
+// eighth of the grid: the dispatcher hands workgroups to the XCDs round-robin
+// by index, so workgroup b runs on XCD b % 8, and with this order every XCD's
+// L2 streams through a single contiguous region of the chunk space.  A
+// permutation of [0, gridDim.x): XCD x takes `per` (or, when the grid is not
+// a multiple of 8 and x > nb % 8, per - 1) consecutive numbers.
+__device__ __forceinline__ uint32_t xcd_contiguous_block()
+{
+    const uint32_t nb = gridDim.x, b = blockIdx.x, x = b % 8u;
+    const uint32_t per = (nb + 7u) / 8u, full = nb % 8u;
+    uint32_t lb = x * per + b / 8u;
+    if (full != 0u && x > full) lb -= x - full;
+    return lb;
+}
+
 // Grid: one wavefront per run of `run` consecutive chunks (the last run may be
 // shorter); a chunk never straddles two tensors.  The wavefront finds the
 // tensor owning its first chunk by binary search over the chunk table
 // (scalar loads, uniform across the wavefront) and walks forward from there,
-// calling f(chunk pointers) for each chunk.
+// calling f(chunk pointers) for each chunk.  Runs are numbered in
+// xcd_contiguous_block() order.
 template <typename F>
 __device__ __forceinline__ void for_each_chunk(const DevTensor *__restrict__ tensors,
                                                const int32_t *__restrict__ chunk_start,
@@ -1198,7 +1215,8 @@ __device__ __forceinline__ void for_each_chunk(const DevTensor *__restrict__ ten
                                                F &&f)
 {
     const int64_t wave = __builtin_amdgcn_readfirstlane(
-        static_cast<int32_t>(blockIdx.x) * (kBlockThreads / kWaveLanes) + (threadIdx.x >> 6));
+        static_cast<int32_t>(xcd_contiguous_block()) * (kBlockThreads / kWaveLanes) +
+        (threadIdx.x >> 6));
     const int64_t first = wave * run;
     if (first >= total_chunks) return;
     // chunk indices fit in int32 (the host caps the total), so the search
