@@ -6,9 +6,10 @@
 // FlashAdamWSim.step(), bytes_per_param), "code/gpu/equivalence.py" (bf16
 // parameter and correction bits, eq_ecc()).
 //
-// Layout of the work: a wavefront owns 1024-element chunks (two in a row for
-// the multi-tensor steps, with workgroups renumbered so that each XCD streams
-// one contiguous region) and each lane 16 elements of a chunk, taken as
+// Layout of the work: a wavefront owns 1024-element chunks (one for the
+// multi-tensor steps, whose workgroups are renumbered so that each XCD
+// streams one contiguous region; two in a row for large single-tensor
+// launches) and each lane 16 elements of a chunk, taken as
 // units of N consecutive elements placed so that every memory instruction of
 // the wavefront covers one contiguous block of each stream (unit u of lane l
 // starts at element 64 N u + N l).  The quantized steps use N = 8 (a lane
@@ -1447,11 +1448,14 @@ hipError_t launch_reconstruct(const uint16_t *param, const void *rho, int64_t n,
 
 namespace {
 
-// Consecutive chunks per wavefront (2 measured best on the 8.0B list for
-// both master widths); FLASHOPT_CHUNKS_PER_WAVE overrides it.
-int32_t chunks_per_wave()
+// Consecutive chunks per wavefront; FLASHOPT_CHUNKS_PER_WAVE overrides the
+// default.  The list steps (workgroups in XCD-contiguous order) take one
+// chunk per wavefront: on the 8.0B list that was 2.6-3.3% faster than two
+// where the buffers landed in a slow placement and up to 0.9% slower in a
+// fast one.  Single-tensor launches (plain order) of large tensors take two.
+int32_t chunks_per_wave(int32_t fallback)
 {
-    int32_t run = 2;
+    int32_t run = fallback;
     if (const char *env = getenv("FLASHOPT_CHUNKS_PER_WAVE")) {
         const int v = atoi(env);
         if (v >= 1 && v <= 1024) run = v;
@@ -1459,14 +1463,17 @@ int32_t chunks_per_wave()
     return run;
 }
 
+constexpr int32_t kListRun = 1;
+constexpr int32_t kTensorRun = 2;
+
 // Chunks per wavefront for a single-tensor launch: a tensor too small to
-// fill the GPU twice over at the default run (256 CUs x 28 resident
-// wavefronts x 2 chunks) gets one chunk per wavefront, doubling the
+// fill the GPU twice over at two chunks per wavefront (256 CUs x 28
+// resident wavefronts x 2 chunks) gets one chunk per wavefront, doubling the
 // wavefronts that share its work.
 int32_t tensor_chunks_per_wave(int32_t total_chunks)
 {
     constexpr int32_t kFillChunks = 256 * 28 * 2;
-    return total_chunks < kFillChunks ? 1 : chunks_per_wave();
+    return total_chunks < kFillChunks ? 1 : chunks_per_wave(kTensorRun);
 }
 
 unsigned step_grid(int32_t total_chunks, int32_t run)
@@ -1480,7 +1487,7 @@ template <int MB, int ST>
 hipError_t step_variant(const DevTensor *tensors, const int32_t *chunk_start, int n_tensors,
                         int32_t total_chunks, const StepScalars &sc, hipStream_t st)
 {
-    const int32_t run = chunks_per_wave();
+    const int32_t run = chunks_per_wave(kListRun);
     hipLaunchKernelGGL((adamw_step_kernel<MB, ST>), dim3(step_grid(total_chunks, run)),
                        dim3(kBlockThreads), 0, st, tensors, chunk_start, n_tensors,
                        total_chunks, run, sc);
@@ -1491,7 +1498,7 @@ template <int MB, int ST>
 hipError_t sgd_variant(const DevTensor *tensors, const int32_t *chunk_start, int n_tensors,
                        int32_t total_chunks, const SgdScalars &sc, hipStream_t st)
 {
-    const int32_t run = chunks_per_wave();
+    const int32_t run = chunks_per_wave(kListRun);
     hipLaunchKernelGGL((sgd_step_kernel<MB, ST>), dim3(step_grid(total_chunks, run)),
                        dim3(kBlockThreads), 0, st, tensors, chunk_start, n_tensors,
                        total_chunks, run, sc);
