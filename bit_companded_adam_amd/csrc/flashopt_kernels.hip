@@ -6,10 +6,9 @@
 // FlashAdamWSim.step(), bytes_per_param), "code/gpu/equivalence.py" (bf16
 // parameter and correction bits, eq_ecc()).
 //
-// Layout of the work: a wavefront owns 1024-element chunks (one for the
-// multi-tensor steps, whose workgroups are renumbered so that each XCD
-// streams one contiguous region; two in a row for large single-tensor
-// launches) and each lane 16 elements of a chunk, taken as
+// Layout of the work: a wavefront owns a 1024-element chunk (the
+// multi-tensor steps renumber their workgroups so that each XCD streams one
+// contiguous region) and each lane 16 elements of it, taken as
 // units of N consecutive elements placed so that every memory instruction of
 // the wavefront covers one contiguous block of each stream (unit u of lane l
 // starts at element 64 N u + N l).  The quantized steps use N = 8 (a lane
@@ -1448,32 +1447,19 @@ hipError_t launch_reconstruct(const uint16_t *param, const void *rho, int64_t n,
 
 namespace {
 
-// Consecutive chunks per wavefront; FLASHOPT_CHUNKS_PER_WAVE overrides the
-// default.  The list steps (workgroups in XCD-contiguous order) take one
-// chunk per wavefront: on the 8.0B list that was 2.6-3.3% faster than two
-// where the buffers landed in a slow placement and up to 0.9% slower in a
-// fast one.  Single-tensor launches (plain order) of large tensors take two.
-int32_t chunks_per_wave(int32_t fallback)
+// Consecutive chunks per wavefront: one (FLASHOPT_CHUNKS_PER_WAVE overrides
+// it).  On the 8.0B list one chunk beat two by 2.6-3.4% where the buffers
+// landed in a slow placement, for the list steps (workgroups in
+// XCD-contiguous order) and for single-tensor launches (plain order), and
+// lost at most 0.9% in fast placements.
+int32_t chunks_per_wave()
 {
-    int32_t run = fallback;
+    int32_t run = 1;
     if (const char *env = getenv("FLASHOPT_CHUNKS_PER_WAVE")) {
         const int v = atoi(env);
         if (v >= 1 && v <= 1024) run = v;
     }
     return run;
-}
-
-constexpr int32_t kListRun = 1;
-constexpr int32_t kTensorRun = 2;
-
-// Chunks per wavefront for a single-tensor launch: a tensor too small to
-// fill the GPU twice over at two chunks per wavefront (256 CUs x 28
-// resident wavefronts x 2 chunks) gets one chunk per wavefront, doubling the
-// wavefronts that share its work.
-int32_t tensor_chunks_per_wave(int32_t total_chunks)
-{
-    constexpr int32_t kFillChunks = 256 * 28 * 2;
-    return total_chunks < kFillChunks ? 1 : chunks_per_wave(kTensorRun);
 }
 
 unsigned step_grid(int32_t total_chunks, int32_t run)
@@ -1487,7 +1473,7 @@ template <int MB, int ST>
 hipError_t step_variant(const DevTensor *tensors, const int32_t *chunk_start, int n_tensors,
                         int32_t total_chunks, const StepScalars &sc, hipStream_t st)
 {
-    const int32_t run = chunks_per_wave(kListRun);
+    const int32_t run = chunks_per_wave();
     hipLaunchKernelGGL((adamw_step_kernel<MB, ST>), dim3(step_grid(total_chunks, run)),
                        dim3(kBlockThreads), 0, st, tensors, chunk_start, n_tensors,
                        total_chunks, run, sc);
@@ -1498,7 +1484,7 @@ template <int MB, int ST>
 hipError_t sgd_variant(const DevTensor *tensors, const int32_t *chunk_start, int n_tensors,
                        int32_t total_chunks, const SgdScalars &sc, hipStream_t st)
 {
-    const int32_t run = chunks_per_wave(kListRun);
+    const int32_t run = chunks_per_wave();
     hipLaunchKernelGGL((sgd_step_kernel<MB, ST>), dim3(step_grid(total_chunks, run)),
                        dim3(kBlockThreads), 0, st, tensors, chunk_start, n_tensors,
                        total_chunks, run, sc);
@@ -1548,7 +1534,7 @@ struct AdamWTensorLaunch {
     static hipError_t run(const DevTensor *t, const int32_t *, int, int32_t total,
                           const StepScalars &sc, hipStream_t st)
     {
-        const int32_t run = tensor_chunks_per_wave(total);
+        const int32_t run = chunks_per_wave();
         hipLaunchKernelGGL((adamw_tensor_kernel<MB, ST>), dim3(step_grid(total, run)),
                            dim3(kBlockThreads), 0, st, *t, total, run, sc);
         return hipGetLastError();
@@ -1560,7 +1546,7 @@ struct SgdTensorLaunch {
     static hipError_t run(const DevTensor *t, const int32_t *, int, int32_t total,
                           const SgdScalars &sc, hipStream_t st)
     {
-        const int32_t run = tensor_chunks_per_wave(total);
+        const int32_t run = chunks_per_wave();
         hipLaunchKernelGGL((sgd_tensor_kernel<MB, ST>), dim3(step_grid(total, run)),
                            dim3(kBlockThreads), 0, st, *t, total, run, sc);
         return hipGetLastError();
