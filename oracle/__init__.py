@@ -56,15 +56,17 @@ class HParams(ctypes.Structure):
                 ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
                 ("weight_decay", ctypes.c_double), ("step", ctypes.c_int64),
                 ("master_bits", ctypes.c_int), ("companded", ctypes.c_int),
-                ("quantize_states", ctypes.c_int), ("literal_order", ctypes.c_int)]
+                ("quantize_states", ctypes.c_int), ("fp32_param", ctypes.c_int)]
 
 
 def hparams(lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0, step=1,
             master_bits=24, companded=True, quantize_states=True,
-            literal_order=False) -> HParams:
+            fp32_param=False) -> HParams:
+    """Step hyper-parameters.  fp32_param: the parameter and its gradient are
+    float32 arrays and are never split (master_bits must then be None/0)."""
     return HParams(lr, betas[0], betas[1], eps, weight_decay, step,
                    0 if master_bits is None else master_bits, int(companded),
-                   int(quantize_states), int(literal_order))
+                   int(quantize_states), int(fp32_param))
 
 
 class SgdHParams(ctypes.Structure):
@@ -214,6 +216,10 @@ class State:
 
     @classmethod
     def zeros_like_param(cls, param_bits: np.ndarray, master_bits=24, quantize_states=True):
+        """Fresh state for a parameter given as bf16 bits (uint16) or, for an
+        fp32 parameter, as a float32 array (then master_bits must be None)."""
+        if param_bits.dtype == np.float32:
+            assert not master_bits
         n = param_bits.size
         g = (n + GROUP - 1) // GROUP
         rho = None if not master_bits else np.zeros(n, dtype=rho_dtype(master_bits))
@@ -230,8 +236,11 @@ class State:
 
 
 def adamw_step(state: State, grad_bits: np.ndarray, hp: HParams) -> State:
-    """One FlashAdamW step on a host state (in place); returns the state."""
-    grad_bits = np.ascontiguousarray(grad_bits, dtype=np.uint16).reshape(-1)
+    """One FlashAdamW step on a host state (in place); returns the state.  The
+    gradient is bf16 bits (uint16), or float32 for an fp32 parameter."""
+    fp32 = state.param.dtype == np.float32
+    assert fp32 == bool(hp.fp32_param)
+    grad_bits = np.ascontiguousarray(grad_bits, dtype=np.float32 if fp32 else np.uint16).reshape(-1)
     n = state.param.size
     assert grad_bits.size == n
     _ck(lib().oracle_adamw_step(_p(state.param), _p(grad_bits), _p(state.rho),
@@ -265,7 +274,7 @@ def adamw_step_list(states, grads, hp: HParams, threads: int = 0) -> int:
     """Step a list of host states with the OpenMP slice driver; returns threads used."""
     arr = (_Tensor * len(states))()
     for i, (s, g) in enumerate(zip(states, grads)):
-        assert g.dtype == np.uint16 and g.flags.c_contiguous and g.size == s.param.size
+        assert g.dtype == s.param.dtype and g.flags.c_contiguous and g.size == s.param.size
         arr[i] = _Tensor(_p(s.param), _p(g), _p(s.rho), _p(s.m_codes), _p(s.m_scales),
                          _p(s.v_codes), _p(s.v_scales), s.param.size)
     return _ck(lib().oracle_adamw_step_list(arr, len(states), ctypes.byref(hp), threads))

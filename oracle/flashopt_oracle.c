@@ -10,8 +10,8 @@
  * Readings of the pages that this file fixes (each is argued where it is used):
  *   R1  weight split (Alg. 1) -- not printed; ties away from zero, integer residual.
  *   R2  "round" in quantize() is torch.round: half to even.
- *   R3  the AdamW body uses the declared bias-correction folding unless
- *       literal_order is set; both forms give identical m, v and codes.
+ *   R3  the AdamW body follows the page's printed operation order exactly
+ *       (bias corrections as divisions, then lr * mhat over sqrt(vhat) + eps).
  *   R12 non-finite values are out of contract; NaN is given code 0 / quiet
  *       NaN so that both sides of a parity test stay defined.
  *   R16 FlashSGD's update (given only as a bytes_per_param row) is
@@ -265,16 +265,15 @@ double oracle_nmse(const float *orig, const float *recon, int64_t n)
 /* ------------------------------------------------------ O5: AdamW step */
 
 typedef struct {
-    float cwd, b1, c1, b2, c2, lr, eps, bc1, bc2, alpha, k2;
+    float cwd, b1, c1, b2, c2, lr, eps, bc1, bc2;
 } step_scalars;
 
 /* Python floats are doubles; each scalar meets the float32 tensors rounded
- * once to float ([SIM step()]: `1 - lr * wd`, `1 - beta1`, `1 - beta1 ** t`). */
+ * once to float ([SIM step()]: `1 - lr * wd`, `1 - beta1`, `1 - beta1 ** t`,
+ * `lr`, `eps`).  Python's float ** int is the C library's pow() on doubles. */
 static void make_scalars(const oracle_hparams *h, step_scalars *s)
 {
     double t = (double)h->step;
-    double bc1 = 1.0 - pow(h->beta1, t);
-    double bc2 = 1.0 - pow(h->beta2, t);
     s->cwd = (float)(1.0 - h->lr * h->weight_decay);
     s->b1 = (float)h->beta1;
     s->c1 = (float)(1.0 - h->beta1);
@@ -282,24 +281,20 @@ static void make_scalars(const oracle_hparams *h, step_scalars *s)
     s->c2 = (float)(1.0 - h->beta2);
     s->lr = (float)h->lr;
     s->eps = (float)h->eps;
-    s->bc1 = (float)bc1;
-    s->bc2 = (float)bc2;
-    s->alpha = (float)(h->lr / bc1);          /* lr / (1 - beta1^t)      */
-    s->k2 = (float)(1.0 / sqrt(bc2));         /* 1 / sqrt(1 - beta2^t)   */
+    s->bc1 = (float)(1.0 - pow(h->beta1, t));
+    s->bc2 = (float)(1.0 - pow(h->beta2, t));
 }
 
-/* Body of Alg. 4 [SIM step()], decoupled weight decay, torch convention:
- *   theta <- theta (1 - lr wd)
- *   m     <- beta1 m + (1 - beta1) g
- *   v     <- beta2 v + ((1 - beta2) g) g         (Python's left-to-right order)
- *   theta <- theta - lr mhat / (sqrt(vhat) + eps),  mhat = m / (1 - beta1^t),
- *                                                   vhat = v / (1 - beta2^t)
- * R3: by default the bias corrections are folded into two scalars,
- *   theta <- theta - (alpha m) / (sqrt(v) k2 + eps),
- *   alpha = lr / (1 - beta1^t), k2 = 1 / sqrt(1 - beta2^t),
- * which equals the page's expression in real arithmetic and differs from its
- * float32 evaluation by a few units in the last place of the update term.
- * m and v (hence every code) are the same in both forms. */
+/* Body of Alg. 4 [SIM step()], "Standard AdamW update", decoupled weight
+ * decay, torch convention, one float32 rounding per operation in the order
+ * the page writes it (Python evaluates left to right):
+ *   theta <- theta * (1 - lr wd)                 (skipped by `if wd:`; R11:
+ *                                                 a factor of 1.0 is exact)
+ *   m     <- beta1 * m + (1 - beta1) * g
+ *   v     <- beta2 * v + ((1 - beta2) * g) * g
+ *   mhat  <- m / (1 - beta1^t)
+ *   vhat  <- v / (1 - beta2^t)
+ *   theta <- theta - (lr * mhat) / (sqrt(vhat) + eps) */
 void oracle_adamw_update(float *theta, float *m, float *v, const float *g,
                          int64_t n, const oracle_hparams *h)
 {
@@ -314,17 +309,10 @@ void oracle_adamw_update(float *theta, float *m, float *v, const float *g,
         float cg = s.c2 * g[i];
         float v_new = cg * g[i];
         float v1 = v_decay + v_new;
-        float step_num, den;
-        if (h->literal_order) {
-            float mhat = m1 / s.bc1;
-            float vhat = v1 / s.bc2;
-            den = sqrtf(vhat) + s.eps;
-            step_num = s.lr * mhat;
-        } else {
-            float r = sqrtf(v1);
-            den = r * s.k2 + s.eps;
-            step_num = s.alpha * m1;
-        }
+        float mhat = m1 / s.bc1;
+        float vhat = v1 / s.bc2;
+        float den = sqrtf(vhat) + s.eps;
+        float step_num = s.lr * mhat;
         float upd = step_num / den;
         theta[i] = th - upd;
         m[i] = m1;
@@ -345,21 +333,29 @@ static unsigned variance_spec(int companded)
 /* One step of [SIM step()] on one tensor: dequantize m and v, rebuild theta,
  * update, requantize m and v, re-split theta.  State init (zero codes and
  * scales, rho from splitting the bf16 parameter, i.e. rho = 0) is the
- * caller's; a zero-filled state reproduces it. */
-int oracle_adamw_step(uint16_t *param, const uint16_t *grad, void *rho,
+ * caller's; a zero-filled state reproduces it.
+ * Which theta: `use_split = master_weight_bits is not None and p.dtype !=
+ * torch.float32`.  With a split, theta = decompress(param, rho) and the
+ * update is split again; without one and a bf16 parameter, theta is the bf16
+ * value widened and the update is cast back with torch's bf16 cast (R14);
+ * with an fp32 parameter (fp32_param), theta is the parameter itself, its
+ * gradient is fp32, and `p.copy_(theta)` stores the update unchanged. */
+int oracle_adamw_step(void *param, const void *grad, void *rho,
                       void *m_codes, uint16_t *m_scales,
                       void *v_codes, uint16_t *v_scales,
                       int64_t n, const oracle_hparams *h)
 {
     if (n < 0 || h == NULL || h->step < 1) return -1;
     if (h->master_bits != 0 && h->master_bits != 24 && h->master_bits != 32) return -1;
+    if (h->fp32_param && h->master_bits != 0) return -1;
     if (n == 0) return 0;
     size_t bytes = (size_t)n * sizeof(float);
     float *theta = (float *)malloc(bytes), *m = (float *)malloc(bytes);
     float *v = (float *)malloc(bytes), *g = (float *)malloc(bytes);
     if (!theta || !m || !v || !g) { free(theta); free(m); free(v); free(g); return -1; }
 
-    for (int64_t i = 0; i < n; ++i) g[i] = bf16_to_f32(grad[i]);
+    if (h->fp32_param) memcpy(g, grad, bytes);
+    else for (int64_t i = 0; i < n; ++i) g[i] = bf16_to_f32(((const uint16_t *)grad)[i]);
 
     if (h->quantize_states) {
         oracle_dequantize(m_codes, m_scales, n, momentum_spec(h->companded), m);
@@ -369,8 +365,9 @@ int oracle_adamw_step(uint16_t *param, const uint16_t *grad, void *rho,
         memcpy(v, v_codes, bytes);
     }
 
-    if (h->master_bits) oracle_reconstruct(param, rho, n, h->master_bits, theta);
-    else for (int64_t i = 0; i < n; ++i) theta[i] = bf16_to_f32(param[i]);
+    if (h->fp32_param) memcpy(theta, param, bytes);
+    else if (h->master_bits) oracle_reconstruct((const uint16_t *)param, rho, n, h->master_bits, theta);
+    else for (int64_t i = 0; i < n; ++i) theta[i] = bf16_to_f32(((const uint16_t *)param)[i]);
 
     oracle_adamw_update(theta, m, v, g, n, h);
 
@@ -382,8 +379,9 @@ int oracle_adamw_step(uint16_t *param, const uint16_t *grad, void *rho,
         memcpy(v_codes, v, bytes);
     }
 
-    if (h->master_bits) oracle_split(theta, n, h->master_bits, param, rho);
-    else for (int64_t i = 0; i < n; ++i) param[i] = bf16_rne(theta[i]);
+    if (h->fp32_param) memcpy(param, theta, bytes);
+    else if (h->master_bits) oracle_split(theta, n, h->master_bits, (uint16_t *)param, rho);
+    else for (int64_t i = 0; i < n; ++i) ((uint16_t *)param)[i] = bf16_rne(theta[i]);
 
     free(theta); free(m); free(v); free(g);
     return 0;
@@ -473,11 +471,13 @@ static int run_slice(const oracle_tensor *q, int64_t s0, const oracle_hparams *h
 {
     size_t rho_elem = (h->master_bits == 32) ? 2 : 1;
     size_t state_elem = h->quantize_states ? 1 : sizeof(float);
+    size_t param_elem = h->fp32_param ? sizeof(float) : sizeof(uint16_t);
     int64_t len = q->numel - s0 < SLICE ? q->numel - s0 : SLICE;
     void *rho = q->rho ? (char *)q->rho + (size_t)s0 * rho_elem : NULL;
     uint16_t *ms = h->quantize_states ? q->m_scales + s0 / GROUP : NULL;
     uint16_t *vs = h->quantize_states ? q->v_scales + s0 / GROUP : NULL;
-    return oracle_adamw_step(q->param + s0, q->grad + s0, rho,
+    return oracle_adamw_step((char *)q->param + (size_t)s0 * param_elem,
+                             (const char *)q->grad + (size_t)s0 * param_elem, rho,
                              (char *)q->m_codes + (size_t)s0 * state_elem, ms,
                              (char *)q->v_codes + (size_t)s0 * state_elem, vs,
                              len, h);

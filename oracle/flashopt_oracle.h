@@ -21,12 +21,16 @@
  * -fno-fast-math.
  *
  * Parity status: every function below is pinned by tests that do not re-type
- * its formula (closed forms, worked examples, invariants, exhaustive checks,
- * library routines).  The multi-step values of oracle_adamw_step() with
- * quantized states or the 24-bit master are pinned only by composition of
- * pinned parts (parity unpinned for that composite trajectory itself); with
- * fp32 moments and the 32-bit master a 300-step trajectory is pinned to
- * torch.optim.AdamW within a rounding bound.
+ * its formula (closed forms, worked examples derived by hand under
+ * tests/golden/, invariants, exhaustive checks, library routines).  The AdamW
+ * body's operation order is pinned bit for bit by six hand-derived elements
+ * whose stored bf16 half and rho change under each plausible reordering.
+ * The multi-step values of oracle_adamw_step() with quantized states or the
+ * 24-bit master are pinned only by composition of pinned parts (parity
+ * unpinned for that composite trajectory itself); with fp32 moments and the
+ * 32-bit master a 300-step trajectory is pinned to torch.optim.AdamW within a
+ * rounding bound, and the fp32-parameter step equals the lossless 32-bit
+ * master step bit for bit.
  */
 #ifndef FLASHOPT_ORACLE_H
 #define FLASHOPT_ORACLE_H
@@ -79,8 +83,8 @@ typedef struct {
     int master_bits;       /* 24 | 32 | 0 (0 = no split, plain bf16 param) */
     int companded;         /* 1: softsign m / sqrt v;  0: linear ablation */
     int quantize_states;   /* 1: int8/uint8 + fp16 scales;  0: fp32 m, v  */
-    int literal_order;     /* 0: the declared bias-correction folding;
-                              1: the pages' literal operation order        */
+    int fp32_param;        /* 1: fp32 parameter and gradient, never split
+                              (needs master_bits 0);  0: bf16              */
 } oracle_hparams;
 
 /* The AdamW update alone (body of Alg. 4 [SIM step()]) on fp32 arrays, in
@@ -89,12 +93,12 @@ void oracle_adamw_update(float *theta, float *m, float *v, const float *g,
                          int64_t n, const oracle_hparams *h);
 
 /* One FlashAdamW step on one parameter tensor [SIM step()], in place.
- * param/grad: bf16 bits [n].  rho: int8 [n] (24) or int16 [n] (32), unused
- * when master_bits == 0.  With quantize_states: m_codes int8 [n], m_scales
+ * param/grad: bf16 bits [n], or float [n] with fp32_param.  rho: int8 [n]
+ * (24) or int16 [n] (32), unused when master_bits == 0.  With quantize_states: m_codes int8 [n], m_scales
  * fp16 [ceil(n/32)], v_codes uint8 [n], v_scales fp16 [ceil(n/32)].  Without:
  * m_codes and v_codes point to float [n] states and the scale pointers are
  * unused.  Returns 0, or -1 on a bad argument. */
-int oracle_adamw_step(uint16_t *param, const uint16_t *grad, void *rho,
+int oracle_adamw_step(void *param, const void *grad, void *rho,
                       void *m_codes, uint16_t *m_scales,
                       void *v_codes, uint16_t *v_scales,
                       int64_t n, const oracle_hparams *h);
@@ -126,7 +130,7 @@ int oracle_sgd_step(uint16_t *param, const uint16_t *grad, void *rho,
  * the oracle; the arithmetic is oracle_adamw_step()'s.  Returns the thread
  * count used, or -1 on a bad argument. */
 typedef struct {
-    uint16_t *param; const uint16_t *grad; void *rho;
+    void *param; const void *grad; void *rho;
     void *m_codes; uint16_t *m_scales; void *v_codes; uint16_t *v_scales;
     int64_t numel;
 } oracle_tensor;

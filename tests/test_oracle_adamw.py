@@ -4,8 +4,10 @@
 * The update alone (fp32 states) is pinned to torch.optim.AdamW, an
   independent library implementation of decoupled-weight-decay AdamW with bias
   correction (its operation order differs, so within 1e-6 relative).
-* The declared folding of the bias corrections is pinned to the pages' literal
-  order: identical m and v, the parameter within a few ulps of the update.
+* The page's operation order (bias corrections as divisions, then
+  (lr * mhat) / (sqrt(vhat) + eps)) is pinned bit for bit by a worked example
+  derived by hand (tests/golden/adamw_literal_order.txt) in which the
+  textbook folding of the bias corrections stores a different rho.
 * Step 1 from a zero state has a closed form (m = (1-b1) g, v = (1-b2) g^2,
   theta1 = theta0 (1 - lr wd) - lr g / (|g| + eps)).
 * With a 32-bit master the split is lossless, so K steps equal an fp32-master
@@ -16,6 +18,8 @@
   torch.optim.AdamW within a derived rounding bound.
 A long trajectory with quantized states or the 24-bit master has no
 independent pin beyond this composition (parity unpinned for it)."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -31,8 +35,7 @@ def _bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
-@pytest.mark.parametrize("literal", [False, True])
-def test_update_matches_torch_adamw(orc, literal):
+def test_update_matches_torch_adamw(orc):
     rng = np.random.default_rng(0)
     n, steps = 1 << 14, 10
     theta = (rng.standard_normal(n) * 0.02).astype(np.float32)
@@ -56,7 +59,7 @@ def test_update_matches_torch_adamw(orc, literal):
         # ulps of the terms, so tolerances scale with the terms' magnitudes
         m_terms = b1 * np.abs(m) + (1 - b1) * np.abs(g)
         th_terms = np.abs(theta) + HP["lr"] * 1.01
-        hp = orc.hparams(**HP, step=t, literal_order=literal)
+        hp = orc.hparams(**HP, step=t)
         theta, m, v = orc.adamw_update(theta, m, v, g, hp)
         st = opt.state[p]
         assert (np.abs(theta - p.detach().numpy()) <= 1e-6 * th_terms).all()
@@ -64,20 +67,22 @@ def test_update_matches_torch_adamw(orc, literal):
         assert np.allclose(v, st["exp_avg_sq"].numpy(), rtol=1e-6, atol=0)
 
 
-def test_folded_equals_literal_to_a_few_ulps(orc):
-    rng = np.random.default_rng(1)
-    n = 1 << 16
-    theta = (rng.standard_normal(n) * 0.02).astype(np.float32)
-    m = (rng.standard_normal(n) * 1e-3).astype(np.float32)
-    v = ((rng.standard_normal(n) * 1e-3) ** 2).astype(np.float32)
-    g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
-    for t in (1, 2, 10, 1000):
-        a = orc.adamw_update(theta, m, v, g, orc.hparams(**HP, step=t))
-        b = orc.adamw_update(theta, m, v, g, orc.hparams(**HP, step=t, literal_order=True))
-        assert (a[1] == b[1]).all() and (a[2] == b[2]).all()
-        upd = np.abs(theta * np.float32(1 - HP["lr"] * HP["weight_decay"]) - a[0])
-        tol = 4 * np.spacing(upd) + np.spacing(np.abs(a[0]))
-        assert (np.abs(a[0] - b[0]) <= tol).all()
+def test_golden_literal_order(orc):
+    """Six elements' updates, every rounding derived by hand in the fixture
+    (page "code/flashsim/flash_adamw_sim.py", FlashAdamWSim.step): their
+    stored theta', rho pin the operation order, since the textbook folding
+    of the bias corrections, either fold alone, a reciprocal multiply for a
+    bias correction, a double-precision bias correction, lr applied last or
+    the decay applied last each change at least one of them."""
+    path = os.path.join(os.path.dirname(__file__), "golden", "adamw_literal_order.txt")
+    rows = [ln.split() for ln in open(path) if ln.strip() and not ln.startswith("#")]
+    assert len(rows) == 6
+    f32 = lambda h: np.array([int(h, 16)], np.uint32).view(np.float32)
+    for th, g, m, v, step, th1, m1, v1, hi, rho in rows:
+        out = orc.adamw_update(f32(th), f32(m), f32(v), f32(g), orc.hparams(**HP, step=int(step)))
+        assert [int(a.view(np.uint32)[0]) for a in out] == [int(th1, 16), int(m1, 16), int(v1, 16)]
+        b, r = orc.split(out[0], 24)
+        assert int(b[0]) == int(hi, 16) and int(r[0]) == int(rho)
 
 
 @pytest.mark.parametrize("master_bits", [24, 32])
@@ -186,6 +191,32 @@ def test_unquantized_states_and_plain_param(orc):
     assert (st.param == _bf16_bits(th)).all()
 
 
+@pytest.mark.parametrize("companded,quantized", [(True, True), (False, True), (True, False)])
+def test_fp32_param_equals_lossless_32bit_master(orc, companded, quantized):
+    """An fp32 parameter is never split (use_split is false for it on page
+    "code/flashsim/flash_adamw_sim.py", FlashAdamWSim.step): theta is the
+    parameter and the update is stored unchanged.  The 32-bit master split is
+    lossless, so with gradients that bf16 holds exactly the two must agree
+    bit for bit at every step, the states included."""
+    rng = np.random.default_rng(9)
+    n, steps = 4096 + 45, 5
+    theta = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    hi, rho = orc.split(theta, 32)
+    a = orc.State.zeros_like_param(theta.copy(), None, quantize_states=quantized)
+    b = orc.State.zeros_like_param(hi, 32, quantize_states=quantized)
+    b.rho[:] = rho
+    for t in range(1, steps + 1):
+        g = _bf16_bits((rng.standard_normal(n) * 1e-3 * np.exp(rng.standard_normal())).astype(np.float32))
+        orc.adamw_step(a, _bits_to_f32(g), orc.hparams(**HP, step=t, master_bits=None, companded=companded,
+                                                       quantize_states=quantized, fp32_param=True))
+        orc.adamw_step(b, g, orc.hparams(**HP, step=t, master_bits=32, companded=companded,
+                                         quantize_states=quantized))
+        assert (a.param.view(np.uint32) == orc.reconstruct(b.param, b.rho, 32).view(np.uint32)).all()
+        for f in ("m_codes", "m_scales", "v_codes", "v_scales"):
+            x, y = getattr(a, f), getattr(b, f)
+            assert (x is None and y is None) or (x.view(np.uint8) == y.view(np.uint8)).all(), f
+
+
 def test_list_driver_equals_per_tensor_steps(orc):
     rng = np.random.default_rng(6)
     sizes = [1, 31, 32, 33, 4096, 70001, 32768 * 2 + 5]
@@ -215,6 +246,14 @@ def test_bad_arguments_rejected(orc):
         orc.adamw_step(st, p, orc.hparams(step=0))
     with pytest.raises(ValueError):
         orc.adamw_step(st, p, orc.hparams(step=1, master_bits=16))
+    # an fp32 parameter is never split, so a master width is rejected for it
+    f = orc.State.zeros_like_param(np.zeros(8, np.float32), None)
+    hp = orc.hparams(step=1, master_bits=24, fp32_param=True)
+    rc = orc.lib().oracle_adamw_step(f.param.ctypes.data, f.param.ctypes.data, None,
+                                     f.m_codes.ctypes.data, f.m_scales.ctypes.data,
+                                     f.v_codes.ctypes.data, f.v_scales.ctypes.data, 8,
+                                     orc.ctypes.byref(hp))
+    assert rc == -1
 
 
 def test_long_trajectory_tracks_torch_adamw(orc):

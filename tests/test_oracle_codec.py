@@ -44,6 +44,34 @@ def test_golden_small_groups(orc):
         assert list(q.astype(np.int64)) == [int(c) for c in codes.split(",")], spec_name
 
 
+def test_golden_dequant_interior_codes(orc):
+    """Interior codes of all four specs at three scales (one fp16-subnormal),
+    each value derived by hand in the fixture: pins the division q/127 (or
+    q/255) and the softsign inverse's division bit for bit."""
+    rows = _rows("dequant_interior_codes.txt")
+    assert len(rows) == 96
+    for spec_name, sbits, code, want in rows:
+        spec = SPECS[spec_name]
+        dt = np.int8 if spec & 1 else np.uint8
+        d = orc.dequantize(np.array([int(code)], dtype=dt), np.array([int(sbits, 16)], np.uint16), spec)
+        assert d.view(np.uint32)[0] == int(want, 16), (spec_name, sbits, code)
+
+
+def test_golden_quantize_near_ties(orc):
+    """Groups whose elements land on (or just off) a code's rounding boundary
+    through the page's chain of roundings; each code derived by hand in the
+    fixture.  A reordered companding or a rounding other than half to even
+    changes some of them."""
+    rows = _rows("quantize_near_ties.txt")
+    assert [r[0] for r in rows] == list(SPECS)
+    for spec_name, sbits, inputs, codes in rows:
+        spec = SPECS[spec_name]
+        x = np.array([int(h, 16) for h in inputs.split(",")], dtype=np.uint32).view(np.float32)
+        q, s = orc.quantize(x, spec)
+        assert list(s) == [int(sbits, 16)], spec_name
+        assert list(q.astype(np.int64)) == [int(c) for c in codes.split(",")], spec_name
+
+
 def test_dequant_closed_forms(orc):
     rng = np.random.default_rng(1)
     # finite fp16 scales across the whole range, subnormals included
