@@ -127,23 +127,47 @@ flashopt_status adamw_scalars(const flashopt_adamw_args *a, StepScalars &sc)
     if (!(a->eps >= 0.0) || !std::isfinite(a->eps)) return FLASHOPT_EINVAL;
     if (!std::isfinite(a->weight_decay)) return FLASHOPT_EINVAL;
     const double t = static_cast<double>(a->step);
-    const double bc1 = 1.0 - std::pow(a->beta1, t);
-    const double bc2 = 1.0 - std::pow(a->beta2, t);
     sc.cwd = static_cast<float>(1.0 - a->lr * a->weight_decay);
     sc.b1 = static_cast<float>(a->beta1);
     sc.c1 = static_cast<float>(1.0 - a->beta1);
     sc.b2 = static_cast<float>(a->beta2);
     sc.c2 = static_cast<float>(1.0 - a->beta2);
-    sc.alpha = static_cast<float>(a->lr / bc1);
-    sc.k2 = static_cast<float>(1.0 / std::sqrt(bc2));
-    sc.k2s = sc.k2 * 0x1p-32f;
+    sc.bc1 = static_cast<float>(1.0 - std::pow(a->beta1, t));
+    sc.bc2 = static_cast<float>(1.0 - std::pow(a->beta2, t));
+    sc.lr = static_cast<float>(a->lr);
     sc.eps = static_cast<float>(a->eps);
-    // The kernel's short division is exact for denominators sqrt(v) k2 + eps in
-    // [2^-100, 2^100]; sqrt(v) < 2^32 on its fast path.  Its short sqrt gives
-    // 2^-95 for v = 0, which adds nothing to eps while k2 <= eps 2^70.
-    sc.fast_div = (sc.eps >= 0x1p-100f && sc.k2 <= 0x1p60f &&
-                   static_cast<double>(sc.k2) <= static_cast<double>(sc.eps) * 0x1p70) ? 1 : 0;
-    sc.num_max = sc.fast_div ? sc.eps * 0x1p100f : 0.0f;
+    // 1 - beta^t >= 1 - beta >= 2^-53 for beta in [0, 1): positive and normal
+    sc.inv_bc1 = 1.0 / static_cast<double>(sc.bc1);
+    sc.inv_bc2 = 1.0 / static_cast<double>(sc.bc2);
+    sc.lr2 = sc.lr * 0x1p32f;
+    sc.eps2 = sc.eps * 0x1p32f;
+    // The kernel's short route (see step_unit): its sqrt returns sqrt(vhat)
+    // 2^32, and 2^-63 (not 0) for vhat = 0, which vanishes next to eps2 (half
+    // an ulp of eps2 is at least 2^-62 while eps >= 2^-70); the short division
+    // needs denominators in [2^-100, 2^100] (eps2 >= 2^-38 and sqrt(vhat)
+    // 2^32 < 2^64) and numerators of at most 2^100 eps2 and, when nonzero, at
+    // least 2^-61.
+    sc.fast = (sc.eps >= 0x1p-70f && sc.eps <= 0x1p60f) ? 1 : 0;
+    // vhat = v1 / bc2 < 2^63  <=  v1 < 2^63 bc2 (rounded down to fp32)
+    {
+        float vb = static_cast<float>(0x1p63 * static_cast<double>(sc.bc2));
+        if (static_cast<double>(vb) > 0x1p63 * static_cast<double>(sc.bc2))
+            vb = std::nextafter(vb, 0.0f);
+        uint32_t bits;
+        std::memcpy(&bits, &vb, 4);
+        sc.v1_bound = bits;
+    }
+    // |lr2 mhat| <= 2^100 eps2 holds when lr2 |m1| / bc1 (1 + 2^-20) does
+    sc.m1_max = sc.lr2 > 0.0f
+        ? static_cast<float>(0x1p100 * static_cast<double>(sc.eps2) * static_cast<double>(sc.bc1) /
+                             (static_cast<double>(sc.lr2) * (1.0 + 0x1p-20)))
+        : INFINITY;
+    {
+        const float tmin = 0x1p-61f;
+        uint32_t bits;
+        std::memcpy(&bits, &tmin, 4);
+        sc.num_key = (bits << 1) - 1u;
+    }
     return FLASHOPT_OK;
 }
 

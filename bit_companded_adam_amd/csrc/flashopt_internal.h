@@ -35,21 +35,29 @@ struct DevTensor {
 };
 static_assert(sizeof(DevTensor) == 64, "descriptor layout");
 
-// fp32 scalars of one step, formed in double on the host and rounded once.
+// Scalars of one step.  The fp32 ones are formed in double on the host and
+// rounded once (a Python float meeting a float32 tensor); the fp64 ones are
+// the reciprocals of the fp32 bias corrections, for the exact quotient route
+// of the kernel (div_by_f64_recip).
 struct StepScalars {
-    float cwd;    // 1 - lr * wd
-    float b1;     // beta1
-    float c1;     // 1 - beta1
-    float b2;     // beta2
-    float c2;     // 1 - beta2
-    float alpha;  // lr / (1 - beta1^t)
-    float k2;     // 1 / sqrt(1 - beta2^t)
-    float k2s;    // k2 2^-32 (exact): the factor for sqrt(v) 2^32
+    double inv_bc1;     // 1 / bc1 in double (bc1 the fp32 value below)
+    double inv_bc2;     // 1 / bc2 in double
+    float cwd;          // 1 - lr * wd
+    float b1;           // beta1
+    float c1;           // 1 - beta1
+    float b2;           // beta2
+    float c2;           // 1 - beta2
+    float bc1;          // 1 - beta1^t
+    float bc2;          // 1 - beta2^t
+    float lr;
     float eps;
-    float num_max; // 2^100 eps: numerators up to this stay in the short division's domain
-    int fast_div;  // 1 when every denominator lies in [2^-100, 2^100] (eps >= 2^-100, k2 <= 2^60)
+    float lr2;          // lr 2^32 (exact): the numerator's scale on the short route
+    float eps2;         // eps 2^32 (exact): the denominator's scale on the short route
+    float m1_max;       // |m1| up to this keeps every |lr mhat 2^32| <= 2^100 eps2
+    uint32_t v1_bound;  // v1 bit patterns below this keep vhat below 2^63
+    uint32_t num_key;   // (pattern << 1) - 1 of the smallest nonzero |lr mhat 2^32| allowed
+    int fast;           // 1 when eps lets the short route absorb vhat = 0 (eps >= 2^-70)
 };
-
 // fp32 scalars of one FlashSGD step (SGD with momentum), formed in double
 // on the host and rounded once.
 struct SgdScalars {

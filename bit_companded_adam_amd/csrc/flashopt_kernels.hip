@@ -934,9 +934,12 @@ __device__ __forceinline__ void unit_exact(const ChunkPtrs &c, uint32_t r, int c
     for (int j = 0; j < N; ++j) {
         float theta, m, v;
         element_moments<MB, ST, N>(in, j, sc, s_mu, s_vu, ms, vs, theta, m, v);
-        const float den = sqrtf(v) * sc.k2 + sc.eps;
-        const float num = sc.alpha * m;
-        th1[j] = theta * sc.cwd - num / den;
+        const float thd = theta * sc.cwd;
+        const float mhat = m / sc.bc1;
+        const float vhat = v / sc.bc2;
+        const float den = sqrtf(vhat) + sc.eps;
+        const float num = sc.lr * mhat;
+        th1[j] = thd - num / den;
         m1[j] = j < cnt ? m : 0.0f;
     }
     if constexpr (ST != kStatesFp32) encode<kMSpec, N>(m1, group_div(sm), mo);
@@ -983,43 +986,52 @@ __device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
             if (j >= cnt) { m1[j] = 0.0f; v1[j] = 0.0f; }
     }
 
-    // ---- rt = sqrt(v1) 2^32.  Every use of rt takes the factor back in an
-    // exact power-of-two scaling of its other operand (k2 2^-32 in the
-    // denominator; the variance group maximum and divisor), so each rounded
-    // result is the one sqrt(v1) itself would give.
+    // ---- rt = sqrt(v1) 2^32, for the variance codes: every use of rt takes
+    // the factor back in an exact power-of-two scaling of its other operand
+    // (the variance group maximum and divisor), so each rounded result is the
+    // one sqrt(v1) itself would give.  The linear codec and fp32 moments do
+    // not need it.
     float rt[N];
-    if (vbits < kSqrtFastEnd) {             // (v1 = 0 gives rt = 2^-63, absorbed downstream)
+    if constexpr (kComp) {
+        if (vbits < kSqrtFastEnd) {         // (v1 = 0 gives rt = 2^-63, which rounds to a zero code and scale)
 #pragma unroll
-        for (int j = 0; j < N; ++j) rt[j] = math::sqrt_x2p32_zero_tiny(v1[j]);
-    } else {                                // rare: v outside the fast sqrt's range
+            for (int j = 0; j < N; ++j) rt[j] = math::sqrt_x2p32_zero_tiny(v1[j]);
+        } else {                            // rare: v outside the fast sqrt's range
 #pragma unroll
-        for (int j = 0; j < N; ++j) rt[j] = sqrtf(v1[j]) * 0x1p32f;
+            for (int j = 0; j < N; ++j) rt[j] = sqrtf(v1[j]) * 0x1p32f;
+        }
     }
 
-    // ---- unit maxima of |m1|, of what the variance quantizer sees, of sqrt(v1)
-    // (the maxima start from the first element: a group of NaNs only has a
-    // NaN maximum, as the IEEE maxNum reduction over its elements gives)
-    float am = fabsf(m1[0]), av = kComp ? rt[0] : v1[0], rmax = 0.0f;
+    // ---- unit maxima of |m1| and of what the variance quantizer sees (the
+    // maxima start from the first element: a group of NaNs only has a NaN
+    // maximum, as the IEEE maxNum reduction over its elements gives)
+    float am = fabsf(m1[0]), av = 0.0f;
+    if constexpr (kComp) av = rt[0];
+    else av = v1[0];
 #pragma unroll
     for (int j = 0; j < N; ++j) {
         am = fmaxf(am, fabsf(m1[j]));
-        if (kComp) av = fmaxf(av, rt[j]);
-        else { av = fmaxf(av, v1[j]); rmax = fmaxf(rmax, rt[j]); }
+        av = fmaxf(av, kComp ? rt[j] : v1[j]);
     }
-    if (kComp) rmax = av;
 
-    // ---- the update theta (1 - lr wd) - (alpha m1) / (sqrt(v1) k2 + eps),
-    // with the short division when the unit's numerators and denominators
-    // lie in its exact domain (den <= den_hi, nonzero |num| >= tmin)
-    const float den_hi = rmax * sc.k2s + sc.eps;
-    const float tmin = fmaxf(0x1p-102f, den_hi * 0x1p-126f);
-    const uint32_t tkey = (__float_as_uint(tmin) << 1) - 1u;
+    // ---- the update in the page's order: mhat = m1 / bc1, vhat = v1 / bc2,
+    // theta1 = thd - (lr mhat) / (sqrt(vhat) + eps).  The two bias
+    // corrections are exact fp64-reciprocal quotients; sqrt(vhat) is the short
+    // sqrt in its 2^32-scaled form, and the division runs on the 2^32-scaled
+    // numerator lr2 mhat and denominator sqrt(vhat) 2^32 + eps2 (the same
+    // quotient), through the short division where its domain holds: every v1
+    // below v1_bound (vhat < 2^63, so the denominator stays below 2^64),
+    // |m1| <= m1_max (numerators at most 2^100 eps2) and every nonzero
+    // numerator at least 2^-61 (>= 2^-126 times any denominator, and the
+    // unscaled product lr mhat is normal, so scaling it was exact)
     uint32_t kmin = 0xFFFFFFFFu;          // min over nonzero |num| of its doubled pattern - 1
     float th1[N];
 #pragma unroll
     for (int j = 0; j < N; ++j) {
-        const float den = rt[j] * sc.k2s + sc.eps;
-        const float num = sc.alpha * m1[j];
+        const float mhat = math::div_by_f64_recip(m1[j], sc.inv_bc1);
+        const float vhat = math::div_by_f64_recip(v1[j], sc.inv_bc2);
+        const float den = math::sqrt_x2p32_zero_tiny(vhat) + sc.eps2;
+        const float num = sc.lr2 * mhat;
         th1[j] = thd[j] - math::div_markstein(num, den, math::recip_cr(den));
         const uint32_t key = (__float_as_uint(num) << 1) - 1u;
         kmin = key < kmin ? key : kmin;
@@ -1029,8 +1041,8 @@ __device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
 #pragma unroll
     for (int j = 1; j < N; ++j) tnan = __builtin_elementwise_maximum(tnan, th1[j]);
     const bool any_nan = tnan != tnan;
-    const bool exact = sc.fast_div == 0 || vbits >= kSqrtFastEnd ||
-                       !(sc.alpha * am <= sc.num_max) || kmin < tkey || any_nan;
+    const bool exact = sc.fast == 0 || vbits >= sc.v1_bound || !(am <= sc.m1_max) ||
+                       kmin < sc.num_key || any_nan;
 
     // ---- group maxima, scales, variance codes
     uint32_t mo[N / 4], vo[N / 4], po[N / 2], ro[rho_words(MB, N)];

@@ -13,15 +13,17 @@
 //                  NaN -> 0);
 //   div_markstein  2^32 random pairs of its stated domain plus every divisor
 //                  significand at the domain's edges;
+//   div_by_f64_recip  every fp32 dividend significand (both signs, normal and
+//                  subnormal) x a set of bias-correction and random divisors;
 //   code_s8_magic  every fp32 p (low byte == clamp(rint(p), -127, 127) as a
 //                  two's-complement byte, for non-NaN p);
 //   softsign_code_fast  (not exact itself: guarded) 4095 fp16 divisors x
 //                  4096 dividends around each of the 127 code boundaries, and
 //                  2^18 random dividends each: no code it trusts differs from
 //                  the correctly rounded chain's (without the guard 414571 do).
-// Only fma, mul, add, v_rcp_f32 / v_rsq_f32 and integer ops are used, so the
-// results do not depend on the FP mode beyond round-to-nearest-even with
-// fp32 denormals kept.
+// Only fma, mul, add, v_rcp_f32 / v_rsq_f32, fp32 <-> fp64 conversions, an
+// fp64 multiply and integer ops are used, so the results do not depend on the
+// FP mode beyond round-to-nearest-even with fp32 and fp64 denormals kept.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -80,6 +82,20 @@ __device__ __forceinline__ float div_markstein(float num, float den, float r)
     const float q0 = num * r;
     const float e = __builtin_fmaf(q0, den, -num);
     return __builtin_fmaf(-e, r, q0);
+}
+
+// Correctly rounded fp32 quotient a / b for an fp32 divisor b > 0, given
+// inv = 1 / b rounded to double: the double product a inv lies within
+// 2^-51.9 |a / b| of the quotient, while no quotient of two fp32 numbers lies
+// that close to a rounding boundary of fp32 without being on it (for a
+// midpoint M of the result's binade, a - b M is a nonzero multiple of
+// ulp(b) ulp(M) / 2, so |a / b - M| > 2^-25 ulp(M) >= 2^-49 |a / b|; in the
+// subnormal range the bound is absolute and far larger than the error).
+// Rounding the product to fp32 therefore gives a / b correctly rounded, for
+// every fp32 a: subnormal quotients, signed zeros, overflow to infinity.
+__device__ __forceinline__ float div_by_f64_recip(float a, double inv)
+{
+    return static_cast<float>(static_cast<double>(a) * inv);
 }
 
 // Signed 8-bit code of p = y * 127 in the low byte of the result: clamp to

@@ -202,6 +202,43 @@ __global__ void k_softsign_code(unsigned long long *bad)
     flush(bad, c);
 }
 
+// Divisor k of the fp64-reciprocal division check: the fp32 bias
+// corrections 1 - beta^t of eight betas for t = 1 .. 512 (4096 values), then
+// 4096 hashed significands at exponents 2^-20 .. 2^0.
+__device__ __forceinline__ float bias_divisor(uint32_t k)
+{
+    if (k < 4096u) {
+        const double betas[8] = {0.9, 0.95, 0.99, 0.8, 0.999, 0.9999, 0.98, 0.5};
+        return (float)(1.0 - pow(betas[k >> 9], (double)((k & 511u) + 1u)));
+    }
+    const uint32_t h = mix(k, 11);
+    return __uint_as_float(((107u + h % 21u) << 23) | (h >> 9));
+}
+
+// div_by_f64_recip against the correctly rounded division for every divisor
+// above x every dividend significand in [1, 2) with both signs, plus 2^16
+// subnormal dividends per divisor and dividends near the top of the range.
+__global__ void k_div_f64_recip(unsigned long long *bad)
+{
+    unsigned long long c = 0;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (8192ull << 23);
+         i += (uint64_t)gridDim.x * blockDim.x) {
+        const float d = bias_divisor((uint32_t)(i >> 23));
+        const double inv = 1.0 / (double)d;
+        const uint32_t sig = (uint32_t)i & 0x7FFFFFu;
+        const float a = __uint_as_float(0x3F800000u | sig);
+        c += !same(div_by_f64_recip(a, inv), a / d);
+        c += !same(div_by_f64_recip(-a, inv), (-a) / d);
+        if (sig < 65536u) {
+            const float s = __uint_as_float(mix(i, 5) & 0x807FFFFFu);          // subnormal or zero
+            c += !same(div_by_f64_recip(s, inv), s / d);
+            const float big = __uint_as_float(0x7E800000u | (mix(i, 6) & 0x807FFFFFu));  // 2^126 .. 2^127
+            c += !same(div_by_f64_recip(big, inv), big / d);
+        }
+    }
+    flush(bad, c);
+}
+
 template <typename K>
 long long run(K kernel, unsigned grid)
 {
@@ -224,6 +261,7 @@ long long fastmath_check_div_by_recip(void) { return run(k_div_by_recip, 65536);
 long long fastmath_check_softsign(void) { return run(k_softsign, 65536); }
 long long fastmath_check_cvt_pk_u8(void) { return run(k_cvt_pk_u8, 65536); }
 long long fastmath_check_div_markstein(void) { return run(k_div_markstein, 65536); }
+long long fastmath_check_div_f64_recip(void) { return run(k_div_f64_recip, 65536); }
 long long fastmath_check_magic_code(void) { return run(k_magic_code, 65536); }
 long long fastmath_check_softsign_code(void) { return run(k_softsign_code<true>, 65536); }
 long long fastmath_softsign_code_unguarded(void) { return run(k_softsign_code<false>, 65536); }

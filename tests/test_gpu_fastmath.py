@@ -7,7 +7,9 @@ value; division by an fp16 scale over every divisor x dividend significand
 pair (2^33); softsign over every |y| <= 1.5; v_cvt_pk_u8_f32 and the
 magic-number int8 code rounding over all 2^32 patterns; the update division over 2^32
 random pairs of its stated domain and every divisor significand at the
-domain's edges; the guarded companded momentum code against the correctly
+domain's edges; the bias-correction division through an fp64 reciprocal over
+every dividend significand for 8192 divisors (the fp32 bias corrections of
+eight betas up to t = 512, and hashed ones); the guarded companded momentum code against the correctly
 rounded chain around every rounding boundary for 4095 fp16 divisors."""
 import ctypes
 import os
@@ -19,8 +21,8 @@ from tests._gpu import require_gpu
 pytestmark = pytest.mark.gpu
 
 LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hip", "libfastmath_check.so")
-CHECKS = ["sqrt", "recip", "div_by_recip", "softsign", "cvt_pk_u8", "div_markstein", "magic_code",
-          "softsign_code"]
+CHECKS = ["sqrt", "recip", "div_by_recip", "softsign", "cvt_pk_u8", "div_markstein", "div_f64_recip",
+          "magic_code", "softsign_code"]
 
 
 @pytest.fixture(scope="module")
