@@ -163,8 +163,9 @@ size_t flashopt_adamw_workspace_bytes(const flashopt_tensor *tensors, int n_tens
  *                                                 fp32 states are read as is)
  *   theta = reconstruct(param, rho)             (the bf16 param if master_bits 0)
  *   theta *= 1 - lr*wd;  m1 = b1 m0 + (1-b1) g;  v1 = b2 v0 + ((1-b2) g) g
- *   theta -= (alpha m1) / (sqrt(v1) k2 + eps),  alpha = lr / (1 - b1^t),
- *                                               k2 = 1 / sqrt(1 - b2^t)
+ *   mhat = m1 / (1 - b1^t);  vhat = v1 / (1 - b2^t)
+ *   theta -= (lr mhat) / (sqrt(vhat) + eps)     (the page's order, "Standard
+ *                                                 AdamW update")
  *   (m, v) = quantize(m1), quantize(v1);  (param, rho) = split(theta)
  *   (fp32 states: m, v = m1, v1;  master_bits 0: param = bf16 RNE of theta)
  * Scalars are formed in double on the host and rounded once to fp32; every
