@@ -193,22 +193,49 @@ flashopt_status sgd_scalars(const flashopt_sgd_args *a, SgdScalars &sc)
     return FLASHOPT_OK;
 }
 
-// Validation of a step's tensor list, then the chunk table staged through the
-// pinned ring and launch(d_desc, d_chunk_start, total_chunks, stream).  split:
-// rho is used; quant: scales are used; v: the variance streams are used.
-template <typename Launch>
-flashopt_status stage_and_launch(const flashopt_tensor *tensors, int n_tensors, int master_bits,
-                                 bool quant, bool v, void *workspace, size_t ws_bytes,
-                                 void *stream, Launch &&launch)
+// Validation of a step's tensor list; total = its chunks of 1024 elements.
+// split: rho is used; quant: scales are used; v: the variance streams are
+// used.
+flashopt_status check_list(const flashopt_tensor *tensors, int n_tensors, int master_bits,
+                           bool quant, bool v, int64_t &total)
 {
     const bool split = master_bits != 0;
-    int64_t total = 0;
+    total = 0;
     for (int i = 0; i < n_tensors; ++i) {
         const flashopt_status st = check_tensor(tensors[i], split, quant, v);
         if (st != FLASHOPT_OK) return st;
         total += (tensors[i].numel + flashopt::kChunkElems - 1) / flashopt::kChunkElems;
         if (total > INT32_MAX) return FLASHOPT_EINVAL;
     }
+    return FLASHOPT_OK;
+}
+
+// The chunk table of a list: n descriptors, then n + 1 chunk starts (prefix
+// sums of the tensors' chunk counts), at `table`.  Returns the total.
+int32_t fill_table(const flashopt_tensor *tensors, int n_tensors, void *table)
+{
+    DevTensor *desc = static_cast<DevTensor *>(table);
+    int32_t *start = reinterpret_cast<int32_t *>(desc + n_tensors);
+    int32_t acc = 0;
+    for (int i = 0; i < n_tensors; ++i) {
+        desc[i] = device_descriptor(tensors[i]);
+        start[i] = acc;
+        acc += static_cast<int32_t>((tensors[i].numel + flashopt::kChunkElems - 1) / flashopt::kChunkElems);
+    }
+    start[n_tensors] = acc;
+    return acc;
+}
+
+// Validation of a step's tensor list, then the chunk table staged through the
+// pinned ring and launch(d_desc, d_chunk_start, total_chunks, stream).
+template <typename Launch>
+flashopt_status stage_and_launch(const flashopt_tensor *tensors, int n_tensors, int master_bits,
+                                 bool quant, bool v, void *workspace, size_t ws_bytes,
+                                 void *stream, Launch &&launch)
+{
+    int64_t total = 0;
+    const flashopt_status cs = check_list(tensors, n_tensors, master_bits, quant, v, total);
+    if (cs != FLASHOPT_OK) return cs;
     if (total == 0) return FLASHOPT_OK;
     const size_t need = workspace_bytes(n_tensors);
     if (!workspace || ws_bytes < need) return FLASHOPT_EWORKSPACE;
@@ -236,17 +263,7 @@ flashopt_status stage_and_launch(const flashopt_tensor *tensors, int n_tensors, 
         slot.cap = need;
     }
 
-    // ---- chunk table: descriptors, then chunk starts (prefix sums)
-    DevTensor *desc = static_cast<DevTensor *>(slot.host);
-    int32_t *start = reinterpret_cast<int32_t *>(desc + n_tensors);
-    int32_t acc = 0;
-    for (int i = 0; i < n_tensors; ++i) {
-        desc[i] = device_descriptor(tensors[i]);
-        start[i] = acc;
-        acc += static_cast<int32_t>((tensors[i].numel + flashopt::kChunkElems - 1) / flashopt::kChunkElems);
-    }
-    start[n_tensors] = acc;
-
+    const int32_t acc = fill_table(tensors, n_tensors, slot.host);
     if (hipMemcpyAsync(workspace, slot.host, need, hipMemcpyHostToDevice, st) != hipSuccess)
         return FLASHOPT_EHIP;
     if (hipEventRecord(slot.done, st) != hipSuccess) return FLASHOPT_EHIP;
@@ -256,6 +273,12 @@ flashopt_status stage_and_launch(const flashopt_tensor *tensors, int n_tensors, 
     const int32_t *d_start = reinterpret_cast<const int32_t *>(d_desc + n_tensors);
     return hip_status(launch(d_desc, d_start, acc, st));
 }
+
+// Host image of the allocation-free step's chunk table: built under the
+// mutex and copied (pageable hipMemcpyAsync, which has consumed the buffer
+// when it returns) into the device scratch array.
+std::mutex g_noalloc_mutex;
+alignas(64) unsigned char g_noalloc_table[flashopt::kScratchBytes];
 
 }  // namespace
 
@@ -346,6 +369,36 @@ flashopt_status flashopt_adamw_step_tensor(const flashopt_tensor *tensor,
     return hip_status(flashopt::launch_adamw_tensor(device_descriptor(*tensor), sc, a->master_bits,
                                                     states_of(a->fp32_states, a->companded),
                                                     static_cast<hipStream_t>(stream)));
+}
+
+flashopt_status flashopt_adamw_step_noalloc(const flashopt_tensor *tensors, int n_tensors,
+                                            const flashopt_adamw_args *a, void *stream)
+{
+    if (n_tensors < 0 || (n_tensors > 0 && !tensors)) return FLASHOPT_EINVAL;
+    if (n_tensors > flashopt::kScratchTensors) return FLASHOPT_EWORKSPACE;
+    StepScalars sc;
+    const flashopt_status hs = adamw_scalars(a, sc);
+    if (hs != FLASHOPT_OK) return hs;
+    int64_t total = 0;
+    const flashopt_status cs = check_list(tensors, n_tensors, a->master_bits, a->fp32_states == 0,
+                                          true, total);
+    if (cs != FLASHOPT_OK || total == 0) return cs;
+    void *scratch = nullptr;
+    if (flashopt::scratch_address(&scratch) != hipSuccess) return FLASHOPT_EHIP;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t acc = 0;
+    {
+        std::lock_guard<std::mutex> lock(g_noalloc_mutex);
+        acc = fill_table(tensors, n_tensors, g_noalloc_table);
+        if (hipMemcpyAsync(scratch, g_noalloc_table, workspace_bytes(n_tensors),
+                           hipMemcpyHostToDevice, st) != hipSuccess)
+            return FLASHOPT_EHIP;
+    }
+    const DevTensor *d_desc = static_cast<const DevTensor *>(scratch);
+    const int32_t *d_start = reinterpret_cast<const int32_t *>(d_desc + n_tensors);
+    return hip_status(flashopt::launch_adamw_step(d_desc, d_start, n_tensors, acc, sc,
+                                                  a->master_bits,
+                                                  states_of(a->fp32_states, a->companded), st));
 }
 
 size_t flashopt_sgd_workspace_bytes(const flashopt_tensor *tensors, int n_tensors)

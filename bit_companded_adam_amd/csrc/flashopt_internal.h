@@ -70,6 +70,15 @@ struct SgdScalars {
     int nesterov;
 };
 
+// Allocation-free list step: its chunk table (kScratchTensors descriptors,
+// then kScratchTensors + 1 chunk starts) lives in a device array of the
+// library, kScratchBytes long.  scratch_address returns that array's address
+// on the current device (looked up once per device).
+constexpr int kScratchTensors = 1024;
+constexpr size_t kScratchBytes =
+    (sizeof(DevTensor) * kScratchTensors + sizeof(int32_t) * (kScratchTensors + 1) + 255) & ~size_t(255);
+hipError_t scratch_address(void **ptr);
+
 hipError_t launch_quantize(const float *x, int64_t n, unsigned spec, void *codes,
                            uint16_t *scales, hipStream_t stream);
 hipError_t launch_dequantize(const void *codes, const uint16_t *scales, int64_t n,

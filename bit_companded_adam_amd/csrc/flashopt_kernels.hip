@@ -31,6 +31,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "flashopt.h"
 #include "flashopt_internal.h"
 #include "flashopt_math.h"
@@ -1566,6 +1568,36 @@ struct SgdTensorLaunch {
 };
 
 }  // namespace
+
+// ------------------------------------ scratch of the allocation-free step
+
+// The chunk table of flashopt_adamw_step_noalloc: a device array of this
+// file instead of a caller's workspace.  Every GPU the library runs on holds
+// its own copy until the process ends.  In host code the name stands for a
+// host-side shadow, not a device address, so host code reaches the array only
+// through the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_address(void **ptr)
+{
+    constexpr int kDevices = 64;
+    static std::mutex mu;
+    static void *addr[kDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_adamw_step(const DevTensor *tensors, const int32_t *chunk_start, int n_tensors,
                              int32_t total_chunks, const StepScalars &sc, int master_bits,

@@ -31,7 +31,7 @@ EXPORTS = ("flashopt_quantize", "flashopt_dequantize", "flashopt_split",
            "flashopt_reconstruct", "flashopt_adamw_workspace_bytes",
            "flashopt_adamw_step", "flashopt_adamw_step_tensor", "flashopt_sgd_workspace_bytes",
            "flashopt_sgd_step", "flashopt_sgd_step_tensor", "flashopt_status_str",
-           "flashopt_abi_version")
+           "flashopt_abi_version", "flashopt_adamw_step_noalloc")
 
 
 class FlashoptError(RuntimeError):
@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
                                         ctypes.c_size_t, vp]
         L.flashopt_adamw_step_tensor.argtypes = [ctypes.POINTER(flashopt_tensor),
                                                  ctypes.POINTER(flashopt_adamw_args), vp]
+        L.flashopt_adamw_step_noalloc.argtypes = [ctypes.POINTER(flashopt_tensor), i,
+                                                  ctypes.POINTER(flashopt_adamw_args), vp]
         L.flashopt_sgd_step_tensor.argtypes = [ctypes.POINTER(flashopt_tensor),
                                                ctypes.POINTER(flashopt_sgd_args), vp]
         L.flashopt_status_str.argtypes = [i]
@@ -97,7 +99,8 @@ def lib() -> ctypes.CDLL:
         L.flashopt_abi_version.argtypes = []
         for name in ("flashopt_quantize", "flashopt_dequantize", "flashopt_split",
                      "flashopt_reconstruct", "flashopt_adamw_step", "flashopt_sgd_step",
-                     "flashopt_adamw_step_tensor", "flashopt_sgd_step_tensor"):
+                     "flashopt_adamw_step_tensor", "flashopt_sgd_step_tensor",
+                     "flashopt_adamw_step_noalloc"):
             getattr(L, name).restype = i
         _lib = L
     return _lib

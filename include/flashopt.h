@@ -190,6 +190,25 @@ flashopt_status flashopt_adamw_step(const flashopt_tensor *tensors, int n_tensor
                                     void *workspace, size_t workspace_bytes,
                                     void *stream);
 
+/* flashopt_adamw_step for callers that cannot allocate: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, results and validation as flashopt_adamw_step, without a
+ * workspace: the chunk table goes to a device array inside the library (68
+ * KiB per GPU, held until the process ends) through one pageable
+ * hipMemcpyAsync from a static host buffer, and the call allocates nothing
+ * (no hipMalloc, hipHostMalloc, hipFree or event creation; the first call on
+ * a device looks the array's address up once).
+ * Limit: at most 1024 tensors per call (more -> FLASHOPT_EWORKSPACE, nothing
+ * launched).  Every call on a GPU shares that GPU's array, which keeps the
+ * last call's table: calls on one stream are ordered, but calls that overlap
+ * on one GPU (different streams, or a second process thread's stream before
+ * the first call's kernel ran) race on it.  The host buffer is guarded by a
+ * mutex; the copy reads host memory at the call, so the call is not
+ * capturable into a graph as is.
+ * Errors: as flashopt_adamw_step (EWORKSPACE only for n_tensors > 1024). */
+flashopt_status flashopt_adamw_step_noalloc(const flashopt_tensor *tensors, int n_tensors,
+                                            const flashopt_adamw_args *args, void *stream);
+
 /* FlashSGD hyper-parameters.  FlashSGD appears on page
  * "code/flashsim/flash_adamw_sim.py" only in bytes_per_param ("flash_sgd":
  * bf16 master + rho + grad + one group-32 state of 1 + 2/32 bytes); this

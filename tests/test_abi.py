@@ -134,6 +134,25 @@ def test_step_validation(L):
     assert F.flashopt_adamw_workspace_bytes(0) == 0
 
 
+def test_noalloc_step_validation(L):
+    """The allocation-free step validates like the list step, before any HIP
+    call: more than 1024 tensors is EWORKSPACE (its fixed table's limit)."""
+    def step(tensors, args=None, n=None):
+        arr = (F.flashopt_tensor * max(1, len(tensors)))(*tensors)
+        return L.flashopt_adamw_step_noalloc(arr if tensors else None,
+                                             len(tensors) if n is None else n,
+                                             ctypes.byref(args or F.make_args(1)), None)
+    assert step([_tensor()] * 1025) == F.FLASHOPT_EWORKSPACE
+    assert step([]) == F.FLASHOPT_OK
+    assert step([_tensor(numel=0, param=None)]) == F.FLASHOPT_OK
+    assert step([], n=-1) == F.FLASHOPT_EINVAL
+    assert step([_tensor()], F.make_args(0)) == F.FLASHOPT_EINVAL
+    assert step([_tensor(numel=-1)]) == F.FLASHOPT_EINVAL
+    assert step([_tensor(grad=None)]) == F.FLASHOPT_EINVAL
+    assert step([_tensor(v_codes=A16 + 8)]) == F.FLASHOPT_EALIGN
+    assert step([_tensor(numel=(1 << 41) + 1)]) == F.FLASHOPT_EINVAL
+
+
 def test_binding_refuses_host_tensors(L):
     import torch
     with pytest.raises(ValueError):
