@@ -141,6 +141,7 @@ flashopt_status adamw_scalars(const flashopt_adamw_args *a, StepScalars &sc)
     sc.inv_bc2 = 1.0 / static_cast<double>(sc.bc2);
     sc.lr2 = sc.lr * 0x1p32f;
     sc.eps2 = sc.eps * 0x1p32f;
+    sc.kv = static_cast<float>(255.0 * std::sqrt(static_cast<double>(sc.bc2)) * 0x1p-32);
     // The kernel's short route (see step_unit): its sqrt returns sqrt(vhat)
     // 2^32, and 2^-63 (not 0) for vhat = 0, which vanishes next to eps2 (half
     // an ulp of eps2 is at least 2^-62 while eps >= 2^-70); the short division

@@ -53,6 +53,7 @@ struct StepScalars {
     float eps;
     float lr2;          // lr 2^32 (exact): the numerator's scale on the short route
     float eps2;         // eps 2^32 (exact): the denominator's scale on the short route
+    float kv;           // 255 sqrt(bc2) 2^-32: the variance codes' factor from sqrt(vhat) 2^32
     float m1_max;       // |m1| up to this keeps every |lr mhat 2^32| <= 2^100 eps2
     uint32_t v1_bound;  // v1 bit patterns below this keep vhat below 2^63
     uint32_t num_key;   // (pattern << 1) - 1 of the smallest nonzero |lr mhat 2^32| allowed

@@ -382,6 +382,25 @@ __device__ __forceinline__ void split_pack_exact(const float (&x)[N], uint32_t (
     }
 }
 
+// The exact signed code word (four int8 codes) of four values of one group:
+// y = a / d, softsign y if SOFTSIGN, round half to even of y * 127 clamped to
+// [-127, 127] (magic-number rounding, flashopt_math.h).  Finite values only.
+template <bool SOFTSIGN>
+__device__ __forceinline__ uint32_t s8_word_exact(float a0, float a1, float a2, float a3,
+                                                  const GroupDiv &gd)
+{
+    float y[4] = {a0, a1, a2, a3};
+    uint32_t b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float q = math::div_by_recip(y[i], gd.d, gd.r);
+        if (SOFTSIGN) q = math::softsign(q);
+        b[i] = math::code_s8_magic(q * 127.0f);
+    }
+    return pack_bytes(static_cast<int32_t>(b[0]), static_cast<int32_t>(b[1]),
+                      static_cast<int32_t>(b[2]), static_cast<int32_t>(b[3]));
+}
+
 // Signed codes of N group quotients with the magic-number rounding of
 // flashopt_math.h (finite inputs only; callers send lanes holding NaN or
 // infinite values to encode).
@@ -390,41 +409,43 @@ __device__ __forceinline__ void encode_s8_finite(const float (&a)[N], const Grou
                                                  uint32_t (&out)[N / 4])
 {
 #pragma unroll
-    for (int k = 0; k < N / 4; ++k) {
-        uint32_t b[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float y = math::div_by_recip(a[4 * k + i], gd.d, gd.r);
-            if (SOFTSIGN) y = math::softsign(y);
-            b[i] = math::code_s8_magic(y * 127.0f);
-        }
-        out[k] = pack_bytes(static_cast<int32_t>(b[0]), static_cast<int32_t>(b[1]),
-                            static_cast<int32_t>(b[2]), static_cast<int32_t>(b[3]));
-    }
+    for (int k = 0; k < N / 4; ++k)
+        out[k] = s8_word_exact<SOFTSIGN>(a[4 * k], a[4 * k + 1], a[4 * k + 2], a[4 * k + 3], gd);
 }
 
 // Companded momentum codes of N finite values of one group with fp16 scale
-// bits s, through softsign_code_fast; a lane with a value near a code's
-// rounding boundary, or with an infinite scale, recomputes its codes with
-// the correctly rounded chain of encode_s8_finite (whose reciprocal of the
-// divisor only that path needs).  Both give the same bits.
+// bits s, through the two-sided short form (math::softsign_code_bytes): a
+// word (four codes) whose two evaluations disagree, i.e. with a value within
+// 1e-4 of a code's rounding boundary, is recomputed with the correctly
+// rounded chain, whose reciprocal of the divisor only that path needs.  An
+// fp16-subnormal scale (its rounding may leave |m / d| up to 1.5, beyond the
+// short form's unclamped range) or an infinite one takes the chain for the
+// whole unit.  Both routes give the same bits.
 template <int N>
 __device__ __forceinline__ void encode_s8_softsign_fast(const float (&a)[N], uint32_t s,
                                                         uint32_t (&out)[N / 4])
 {
     const uint32_t mag = s & 0x7FFFu;
-    const float d = group_divisor(s);
-    const float c0 = d * math::kInv254;
-    float dev = 0.0f;
+    if ((mag != 0u && mag < 0x0400u) || mag == 0x7C00u) {
+        encode_s8_finite<true, N>(a, group_div(s), out);
+        return;
+    }
+    const float c0 = group_divisor(s) * math::kInv254;
+    bool amb[N / 4], any = false;
 #pragma unroll
     for (int k = 0; k < N / 4; ++k) {
-        uint32_t b[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) b[i] = math::softsign_code_fast(a[4 * k + i], c0, dev);
-        out[k] = pack_bytes(static_cast<int32_t>(b[0]), static_cast<int32_t>(b[1]),
-                            static_cast<int32_t>(b[2]), static_cast<int32_t>(b[3]));
+        uint32_t hi, lo;
+        math::softsign_code_bytes(a[4 * k], a[4 * k + 1], a[4 * k + 2], a[4 * k + 3], c0, hi, lo);
+        out[k] = hi ^ 0x80808080u;            // byte = code + 128 -> the code's two's-complement byte
+        amb[k] = hi != lo;
+        any |= amb[k];
     }
-    if (dev > math::kCodeTieGuard || mag == 0x7C00u) encode_s8_finite<true, N>(a, group_div(s), out);
+    if (any) {                                 // rare: a code within 1e-4 of a rounding boundary
+        const GroupDiv gd = group_div(s);
+#pragma unroll
+        for (int k = 0; k < N / 4; ++k)
+            if (amb[k]) out[k] = s8_word_exact<true>(a[4 * k], a[4 * k + 1], a[4 * k + 2], a[4 * k + 3], gd);
+    }
 }
 
 // ------------------------------------------------------- standalone codec
@@ -948,6 +969,62 @@ __device__ __forceinline__ void unit_exact(const ChunkPtrs &c, uint32_t r, int c
     pack_theta<MB, true, N>(th1, po, ro);
 }
 
+// Variance codes (the sqrt spec) of N values of one group with fp16 scale
+// bits s.  The chain quantizes rt = sqrt(v1): y = rt / d, p = y * 255.  The
+// update has already formed sq = sqrt(vhat) 2^32 with vhat = v1 / bc2, so
+// p is taken as sq cv with cv = kv / d per group and kv = 255 sqrt(bc2) 2^-32
+// (host, rounded once): relative error at most 3.5 units of 2^-24 (vhat's
+// rounding halved by the sqrt, sq, kv, cv; the product is exact inside the
+// fma) against at most 3 for the chain (rt, y, p), so the two differ by less
+// than 6.5 2^-24 255.2 < 9.9e-5 (p <= 255.2 below the clamp).  Each code is
+// converted twice, at p + and - kVarianceBand = 1.5e-4 (each fma adds at most
+// 2^-17); where the two bytes agree no rounding boundary lies within 9.9e-5
+// of p and the byte is the chain's code.  Words that disagree, and all words
+// when exact_all (some v1 outside the range where the update formed sq),
+// take the chain.
+template <int N>
+__device__ __forceinline__ void variance_codes(const float (&sq)[N], const float (&v1)[N], uint32_t s,
+                                               float kv, bool exact_all, uint32_t (&out)[N / 4])
+{
+    const GroupDiv gd = group_div(s);
+    const float cv = math::div_by_recip(kv, gd.d, gd.r);    // 0 for an infinite scale: codes 0
+    constexpr float up = math::kVarianceBand, dn = -math::kVarianceBand;
+    bool amb[N / 4], any = exact_all;
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) {
+        uint32_t hi = 0u, lo = 0u;
+        hi = math::cvt_u8<0>(__builtin_fmaf(sq[4 * k], cv, up), hi);
+        lo = math::cvt_u8<0>(__builtin_fmaf(sq[4 * k], cv, dn), lo);
+        hi = math::cvt_u8<1>(__builtin_fmaf(sq[4 * k + 1], cv, up), hi);
+        lo = math::cvt_u8<1>(__builtin_fmaf(sq[4 * k + 1], cv, dn), lo);
+        hi = math::cvt_u8<2>(__builtin_fmaf(sq[4 * k + 2], cv, up), hi);
+        lo = math::cvt_u8<2>(__builtin_fmaf(sq[4 * k + 2], cv, dn), lo);
+        hi = math::cvt_u8<3>(__builtin_fmaf(sq[4 * k + 3], cv, up), hi);
+        lo = math::cvt_u8<3>(__builtin_fmaf(sq[4 * k + 3], cv, dn), lo);
+        out[k] = hi;
+        amb[k] = exact_all || hi != lo;
+        any |= amb[k];
+    }
+    if (any) {                                  // rare: the correctly rounded chain for those words
+        GroupDiv g2 = gd;
+        g2.d *= 0x1p32f;                        // rt / d = (rt 2^32) / (d 2^32), same rounding
+        g2.r *= 0x1p-32f;
+#pragma unroll
+        for (int k = 0; k < N / 4; ++k) {
+            if (!amb[k]) continue;
+            float rt[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float v = v1[4 * k + i];
+                rt[i] = __float_as_uint(v) < kSqrtFastEnd ? math::sqrt_x2p32_zero_tiny(v) : sqrtf(v) * 0x1p32f;
+            }
+            uint32_t w[1];
+            encode<FLASHOPT_SPEC_VARIANCE, 4>(rt, g2, w);
+            out[k] = w[0];
+        }
+    }
+}
+
 // One unit of one lane: load every stream, dequantize m and v (or read them
 // as fp32), rebuild the master (or widen the bf16 parameter), apply AdamW,
 // find the group maxima (DPP exchanges among the group's lanes), and write
@@ -988,51 +1065,31 @@ __device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
             if (j >= cnt) { m1[j] = 0.0f; v1[j] = 0.0f; }
     }
 
-    // ---- rt = sqrt(v1) 2^32, for the variance codes: every use of rt takes
-    // the factor back in an exact power-of-two scaling of its other operand
-    // (the variance group maximum and divisor), so each rounded result is the
-    // one sqrt(v1) itself would give.  The linear codec and fp32 moments do
-    // not need it.
-    float rt[N];
-    if constexpr (kComp) {
-        if (vbits < kSqrtFastEnd) {         // (v1 = 0 gives rt = 2^-63, which rounds to a zero code and scale)
+    // ---- unit maximum of |m1| (the maxima start from the first element: a
+    // group of NaNs only has a NaN maximum, as the IEEE maxNum reduction over
+    // its elements gives)
+    float am = fabsf(m1[0]);
 #pragma unroll
-            for (int j = 0; j < N; ++j) rt[j] = math::sqrt_x2p32_zero_tiny(v1[j]);
-        } else {                            // rare: v outside the fast sqrt's range
-#pragma unroll
-            for (int j = 0; j < N; ++j) rt[j] = sqrtf(v1[j]) * 0x1p32f;
-        }
-    }
-
-    // ---- unit maxima of |m1| and of what the variance quantizer sees (the
-    // maxima start from the first element: a group of NaNs only has a NaN
-    // maximum, as the IEEE maxNum reduction over its elements gives)
-    float am = fabsf(m1[0]), av = 0.0f;
-    if constexpr (kComp) av = rt[0];
-    else av = v1[0];
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-        am = fmaxf(am, fabsf(m1[j]));
-        av = fmaxf(av, kComp ? rt[j] : v1[j]);
-    }
+    for (int j = 1; j < N; ++j) am = fmaxf(am, fabsf(m1[j]));
 
     // ---- the update in the page's order: mhat = m1 / bc1, vhat = v1 / bc2,
     // theta1 = thd - (lr mhat) / (sqrt(vhat) + eps).  The two bias
-    // corrections are exact fp64-reciprocal quotients; sqrt(vhat) is the short
-    // sqrt in its 2^32-scaled form, and the division runs on the 2^32-scaled
-    // numerator lr2 mhat and denominator sqrt(vhat) 2^32 + eps2 (the same
+    // corrections are exact fp64-reciprocal quotients; sq = sqrt(vhat) 2^32 is
+    // the short sqrt in its 2^32-scaled form, and the division runs on the
+    // 2^32-scaled numerator lr2 mhat and denominator sq + eps2 (the same
     // quotient), through the short division where its domain holds: every v1
     // below v1_bound (vhat < 2^63, so the denominator stays below 2^64),
     // |m1| <= m1_max (numerators at most 2^100 eps2) and every nonzero
     // numerator at least 2^-61 (>= 2^-126 times any denominator, and the
     // unscaled product lr mhat is normal, so scaling it was exact)
     uint32_t kmin = 0xFFFFFFFFu;          // min over nonzero |num| of its doubled pattern - 1
-    float th1[N];
+    float th1[N], sq[N];
 #pragma unroll
     for (int j = 0; j < N; ++j) {
         const float mhat = math::div_by_f64_recip(m1[j], sc.inv_bc1);
         const float vhat = math::div_by_f64_recip(v1[j], sc.inv_bc2);
-        const float den = math::sqrt_x2p32_zero_tiny(vhat) + sc.eps2;
+        sq[j] = math::sqrt_x2p32_zero_tiny(vhat);
+        const float den = sq[j] + sc.eps2;
         const float num = sc.lr2 * mhat;
         th1[j] = thd[j] - math::div_markstein(num, den, math::recip_cr(den));
         const uint32_t key = (__float_as_uint(num) << 1) - 1u;
@@ -1043,8 +1100,8 @@ __device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
 #pragma unroll
     for (int j = 1; j < N; ++j) tnan = __builtin_elementwise_maximum(tnan, th1[j]);
     const bool any_nan = tnan != tnan;
-    const bool exact = sc.fast == 0 || vbits >= sc.v1_bound || !(am <= sc.m1_max) ||
-                       kmin < sc.num_key || any_nan;
+    const bool vfast = vbits < sc.v1_bound;   // the update's and the short variance codes' v range
+    const bool exact = sc.fast == 0 || !vfast || !(am <= sc.m1_max) || kmin < sc.num_key || any_nan;
 
     // ---- group maxima, scales, variance codes
     uint32_t mo[N / 4], vo[N / 4], po[N / 2], ro[rho_words(MB, N)];
@@ -1052,12 +1109,22 @@ __device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
     if constexpr (kQuant) {
         sm_out = f16_bits(group_max<32 / N>(am));
         if constexpr (kComp) {
-            sv_out = f16_bits(group_max<32 / N>(av) * 0x1p-32f);
-            GroupDiv gdv = group_div(sv_out);
-            gdv.d *= 0x1p32f;                // rt / d = (rt 2^32) / (d 2^32), same rounding
-            gdv.r *= 0x1p-32f;
-            encode<kVSpec, N>(rt, gdv, vo);
+            // the group's largest sqrt(v1), 2^32-scaled: sqrt of the largest
+            // v1 (sqrt is monotone; v1 = 0 gives 2^-63, whose scale is 0)
+            float rmax;
+            if (vbits < kSqrtFastEnd) {
+                rmax = math::sqrt_x2p32_zero_tiny(__uint_as_float(vbits));
+            } else {                            // rare: some v1 outside [0, 2^64): maxNum of the sqrts
+                rmax = sqrtf(v1[0]) * 0x1p32f;
+#pragma unroll
+                for (int j = 1; j < N; ++j) rmax = fmaxf(rmax, sqrtf(v1[j]) * 0x1p32f);
+            }
+            sv_out = f16_bits(group_max<32 / N>(rmax) * 0x1p-32f);
+            variance_codes<N>(sq, v1, sv_out, sc.kv, !vfast, vo);
         } else {
+            float av = v1[0];
+#pragma unroll
+            for (int j = 1; j < N; ++j) av = fmaxf(av, v1[j]);
             sv_out = f16_bits(group_max<32 / N>(av));
             encode<kVSpec, N>(v1, group_div(sv_out), vo);
         }

@@ -17,10 +17,11 @@
 //                  subnormal) x a set of bias-correction and random divisors;
 //   code_s8_magic  every fp32 p (low byte == clamp(rint(p), -127, 127) as a
 //                  two's-complement byte, for non-NaN p);
-//   softsign_code_fast  (not exact itself: guarded) 4095 fp16 divisors x
+//   softsign_code_bytes  (not exact itself: two-sided) 4095 fp16 divisors x
 //                  4096 dividends around each of the 127 code boundaries, and
-//                  2^18 random dividends each: no code it trusts differs from
-//                  the correctly rounded chain's (without the guard 414571 do).
+//                  2^18 random dividends each: wherever its two bytes agree,
+//                  the byte is the correctly rounded chain's code (and the
+//                  sweep reaches inputs where the bytes disagree).
 // Only fma, mul, add, v_rcp_f32 / v_rsq_f32, fp32 <-> fp64 conversions, an
 // fp64 multiply and integer ops are used, so the results do not depend on the
 // FP mode beyond round-to-nearest-even with fp32 and fp64 denormals kept.
@@ -113,31 +114,55 @@ __device__ __forceinline__ uint32_t code_s8_magic(float p)
 // 1/254 rounded to fp32 (relative error 2^-28).
 constexpr float kInv254 = 0x1.020408p-8f;
 
-// softsign_code_fast's result is trusted where its p lies at least 1e-4 from
-// a code's rounding boundary (dev <= kCodeTieGuard).
-constexpr float kCodeTieGuard = 0.5f - 1e-4f;
-
-// The companded int8 momentum code of m in a group with divisor d, without
-// the correctly rounded chain y = m / d, y'' = 2y / (1 + |y|), p = 127 y''.
-// In exact arithmetic p = 254 m / (d + |m|); here p = m rcp(t) with
-// t = fma(|m|, 1/254, c0) and c0 = d kInv254 (formed once per group).  The
-// relative error of this p is at most 5.1 units of 2^-24 (kInv254, c0, the
-// fma, v_rcp_f32's one ulp and the product), that of the correctly rounded
-// chain's at most 4 units (four roundings, none amplified: d y''/dy y / y''
-// <= 1), so the two differ by less than 9.1 2^-24 127.5 < 7e-5 wherever a
-// code can depend on it (|p| <= 127.5).  Returns the magic sum of the
-// clamped p, as code_s8_magic (low byte = the code), and raises dev to the
-// distance |p - rint(p)|: where dev <= kCodeTieGuard the code equals the
-// correctly rounded chain's.  Finite m and positive finite d only.
-__device__ __forceinline__ uint32_t softsign_code_fast(float m, float c0, float &dev)
+// v_cvt_pk_u8_f32 into byte I of acc: clamp(rint(x), 0, 255) with ties to
+// even, NaN -> 0.
+template <int I>
+__device__ __forceinline__ uint32_t cvt_u8(float x, uint32_t acc)
 {
-    const float t = __builtin_fmaf(fabsf(m), kInv254, c0);
-    const float p = m * __builtin_amdgcn_rcpf(t);
-    const float c = __builtin_amdgcn_fmed3f(p, -127.0f, 127.0f);
-    const float s = c + 12582912.0f;
-    dev = fmaxf(dev, fabsf(c - (s - 12582912.0f)));
-    return __float_as_uint(s);
+    return __builtin_amdgcn_cvt_pk_u8_f32(x, I, acc);
 }
+
+// Half-width, in code units, of the band around the fast momentum code's p
+// that softsign_code_bytes evaluates.
+constexpr float kMomentumBand = 1e-4f;
+
+// The companded int8 momentum codes of four finite values m of one group with
+// divisor d, without the correctly rounded chain y = m / d, y'' = 2y /
+// (1 + |y|), p = 127 y''.  In exact arithmetic p = 254 m / (d + |m|); here
+// p = m rcp(t) with t = fma(|m|, 1/254, c0) and c0 = d kInv254 (formed once
+// per group), whose relative error is at most 4.1 units of 2^-24 (kInv254, c0,
+// the fma, v_rcp_f32's one ulp), against at most 4 for the chain (four
+// roundings, none amplified: d y''/dy y / y'' <= 1): the two differ by less
+// than 8.1 2^-24 127.5 < 6.2e-5 wherever a code can depend on it.  Each code
+// is converted twice, from fma(m, rcp(t), 128 + kMomentumBand) into `hi` and
+// from fma(m, rcp(t), 128 - kMomentumBand) into `lo` (byte i, round half to
+// even, clamped to [0, 255]); each fma adds at most half an ulp below 256
+// (2^-17).  Where the two bytes agree, no rounding boundary lies within
+// 1e-4 - 2^-17 > 6.2e-5 of p, so the byte is the chain's code plus 128.  The
+// caller needs |m / d| <= 1 + 2^-11 (true for a normal fp16 scale of the
+// group's maximum), so that |p| < 127.5 and no clamp is needed.
+__device__ __forceinline__ void softsign_code_bytes(float m0, float m1, float m2, float m3, float c0,
+                                                    uint32_t &hi, uint32_t &lo)
+{
+    const float r0 = __builtin_amdgcn_rcpf(__builtin_fmaf(fabsf(m0), kInv254, c0));
+    const float r1 = __builtin_amdgcn_rcpf(__builtin_fmaf(fabsf(m1), kInv254, c0));
+    const float r2 = __builtin_amdgcn_rcpf(__builtin_fmaf(fabsf(m2), kInv254, c0));
+    const float r3 = __builtin_amdgcn_rcpf(__builtin_fmaf(fabsf(m3), kInv254, c0));
+    constexpr float up = 128.0f + kMomentumBand, dn = 128.0f - kMomentumBand;
+    hi = cvt_u8<0>(__builtin_fmaf(m0, r0, up), 0u);
+    lo = cvt_u8<0>(__builtin_fmaf(m0, r0, dn), 0u);
+    hi = cvt_u8<1>(__builtin_fmaf(m1, r1, up), hi);
+    lo = cvt_u8<1>(__builtin_fmaf(m1, r1, dn), lo);
+    hi = cvt_u8<2>(__builtin_fmaf(m2, r2, up), hi);
+    lo = cvt_u8<2>(__builtin_fmaf(m2, r2, dn), lo);
+    hi = cvt_u8<3>(__builtin_fmaf(m3, r3, up), hi);
+    lo = cvt_u8<3>(__builtin_fmaf(m3, r3, dn), lo);
+}
+
+// Half-width, in code units, of the band around the variance code's p that
+// the step evaluates when it forms the codes from sqrt(vhat) (see
+// flashopt_kernels.hip, variance_codes).
+constexpr float kVarianceBand = 1.5e-4f;
 
 // 2^32 times the correctly rounded sqrt(x), for 0 <= x < 2^64: the input is
 // scaled by 2^64 (exact), which puts every denormal into the range where one

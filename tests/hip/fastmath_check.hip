@@ -170,11 +170,13 @@ __device__ __forceinline__ int exact_code(float m, float d)
     return (int)(int8_t)(code_s8_magic(y * 127.0f) & 0xFFu);
 }
 
-// softsign_code_fast against the exact chain wherever its guard trusts it
-// (GUARDED), or everywhere (to show that the sweep reaches inputs where the
-// unguarded codes differ): for every divisor, 2 x 2048 dividends around each
-// of the 127 positive rounding boundaries p = k + 1/2 (the map is odd), then
-// 2^18 hashed dividends over [-1.5 d, 1.5 d].
+// softsign_code_bytes against the exact chain wherever its two bytes agree
+// (GUARDED), or its upper byte everywhere (to show that the sweep reaches
+// inputs where the short form alone would differ): for every divisor,
+// 2 x 2048 dividends around each of the 127 positive rounding boundaries
+// p = k + 1/2 (the map is odd), then 2^18 hashed dividends over
+// [-d, d] (normal fp16 divisors: |m / d| <= 1 + 2^-11, the caller's range;
+// the subnormal ones over [-(1 + 2^-11) d, (1 + 2^-11) d] as well).
 template <bool GUARDED>
 __global__ void k_softsign_code(unsigned long long *bad)
 {
@@ -193,11 +195,13 @@ __global__ void k_softsign_code(unsigned long long *bad)
             d = code_divisor((uint32_t)(j >> 18));
             uint32_t h = (uint32_t)j * 2654435761u;
             h ^= h >> 15; h *= 2246822519u; h ^= h >> 13;
-            m = d * ((float)(h >> 8) * 0x1p-24f * 3.0f - 1.5f);
+            m = d * ((float)(h >> 8) * 0x1p-23f - 1.0f) * (1.0f + 0x1p-11f);
         }
-        float dev = 0.0f;
-        const uint32_t s = softsign_code_fast(m, d * kInv254, dev);
-        if (!GUARDED || dev <= kCodeTieGuard) c += (int)(int8_t)(s & 0xFFu) != exact_code(m, d);
+        if (!(fabsf(m) <= d * (1.0f + 0x1p-11f))) continue;
+        uint32_t hi, lo;
+        softsign_code_bytes(m, m, m, m, d * kInv254, hi, lo);
+        const int code = (int)(hi & 0xFFu) - 128;
+        if (!GUARDED || hi == lo) c += code != exact_code(m, d);
     }
     flush(bad, c);
 }

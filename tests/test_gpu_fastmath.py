@@ -10,7 +10,8 @@ random pairs of its stated domain and every divisor significand at the
 domain's edges; the bias-correction division through an fp64 reciprocal over
 every dividend significand for 8192 divisors (the fp32 bias corrections of
 eight betas up to t = 512, and hashed ones); the guarded companded momentum code against the correctly
-rounded chain around every rounding boundary for 4095 fp16 divisors."""
+rounded chain around every rounding boundary for 4095 fp16 divisors
+(two-sided short form: trusted where its two evaluations agree)."""
 import ctypes
 import os
 
@@ -44,9 +45,10 @@ def test_exact(lib, check):
 
 
 def test_softsign_code_sweep_is_sensitive(lib):
-    """Without its guard, softsign_code_fast disagrees with the correctly
-    rounded chain on some of the swept inputs: the sweep reaches the
-    boundaries where the guard matters."""
+    """Taken alone (without comparing its two evaluations), the short
+    momentum code disagrees with the correctly rounded chain on some of the
+    swept inputs: the sweep reaches the boundaries where the two-sided test
+    matters."""
     lib.fastmath_softsign_code_unguarded.restype = ctypes.c_longlong
     diff = lib.fastmath_softsign_code_unguarded()
     print(f"unguarded softsign_code: {diff} disagreements", flush=True)
