@@ -139,16 +139,18 @@ flashopt_status adamw_scalars(const flashopt_adamw_args *a, StepScalars &sc)
     // 1 - beta^t >= 1 - beta >= 2^-53 for beta in [0, 1): positive and normal
     sc.inv_bc1 = 1.0 / static_cast<double>(sc.bc1);
     sc.inv_bc2 = 1.0 / static_cast<double>(sc.bc2);
+    sc.inv_bc2s = 0x1p64 / static_cast<double>(sc.bc2);
     sc.lr2 = sc.lr * 0x1p32f;
     sc.eps2 = sc.eps * 0x1p32f;
     sc.kv = static_cast<float>(255.0 * std::sqrt(static_cast<double>(sc.bc2)) * 0x1p-32);
     // The kernel's short route (see step_unit): its sqrt returns sqrt(vhat)
-    // 2^32, and 2^-63 (not 0) for vhat = 0, which vanishes next to eps2 (half
-    // an ulp of eps2 is at least 2^-62 while eps >= 2^-70); the short division
-    // needs denominators in [2^-100, 2^100] (eps2 >= 2^-38 and sqrt(vhat)
+    // 2^32, except a value below 2^-31 (not the exact root) for a subnormal or
+    // zero vhat, which vanishes next to eps2 (half an ulp of eps2 is at least
+    // 2^-30 while eps >= 2^-38); the short division
+    // needs denominators in [2^-100, 2^100] (eps2 >= 2^-6 and sqrt(vhat)
     // 2^32 < 2^64) and numerators of at most 2^100 eps2 and, when nonzero, at
     // least 2^-61.
-    sc.fast = (sc.eps >= 0x1p-70f && sc.eps <= 0x1p60f) ? 1 : 0;
+    sc.fast = (sc.eps >= 0x1p-38f && sc.eps <= 0x1p60f) ? 1 : 0;
     // vhat = v1 / bc2 < 2^63  <=  v1 < 2^63 bc2 (rounded down to fp32)
     {
         float vb = static_cast<float>(0x1p63 * static_cast<double>(sc.bc2));

@@ -42,6 +42,7 @@ static_assert(sizeof(DevTensor) == 64, "descriptor layout");
 struct StepScalars {
     double inv_bc1;     // 1 / bc1 in double (bc1 the fp32 value below)
     double inv_bc2;     // 1 / bc2 in double
+    double inv_bc2s;    // 2^64 / bc2 in double: vhat 2^64 inside sqrt_quot_x2p32
     float cwd;          // 1 - lr * wd
     float b1;           // beta1
     float c1;           // 1 - beta1
@@ -57,7 +58,7 @@ struct StepScalars {
     float m1_max;       // |m1| up to this keeps every |lr mhat 2^32| <= 2^100 eps2
     uint32_t v1_bound;  // v1 bit patterns below this keep vhat below 2^63
     uint32_t num_key;   // (pattern << 1) - 1 of the smallest nonzero |lr mhat 2^32| allowed
-    int fast;           // 1 when eps lets the short route absorb vhat = 0 (eps >= 2^-70)
+    int fast;           // 1 when eps lets the short route absorb vhat = 0 and subnormal vhat (eps >= 2^-38)
 };
 // fp32 scalars of one FlashSGD step (SGD with momentum), formed in double
 // on the host and rounded once.

@@ -1073,9 +1073,11 @@ __device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
     for (int j = 1; j < N; ++j) am = fmaxf(am, fabsf(m1[j]));
 
     // ---- the update in the page's order: mhat = m1 / bc1, vhat = v1 / bc2,
-    // theta1 = thd - (lr mhat) / (sqrt(vhat) + eps).  The two bias
-    // corrections are exact fp64-reciprocal quotients; sq = sqrt(vhat) 2^32 is
-    // the short sqrt in its 2^32-scaled form, and the division runs on the
+    // theta1 = thd - (lr mhat) / (sqrt(vhat) + eps).  mhat is an exact
+    // fp64-reciprocal quotient; sq = sqrt(vhat) 2^32 comes from
+    // sqrt_quot_x2p32 (vhat formed inside it; a subnormal or zero vhat gives
+    // sq below 2^-31 instead of its exact root, lost in sq + eps2 while
+    // eps >= 2^-38), and the division runs on the
     // 2^32-scaled numerator lr2 mhat and denominator sq + eps2 (the same
     // quotient), through the short division where its domain holds: every v1
     // below v1_bound (vhat < 2^63, so the denominator stays below 2^64),
@@ -1087,8 +1089,7 @@ __device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
 #pragma unroll
     for (int j = 0; j < N; ++j) {
         const float mhat = math::div_by_f64_recip(m1[j], sc.inv_bc1);
-        const float vhat = math::div_by_f64_recip(v1[j], sc.inv_bc2);
-        sq[j] = math::sqrt_x2p32_zero_tiny(vhat);
+        sq[j] = math::sqrt_quot_x2p32(v1[j], sc.inv_bc2s);
         const float den = sq[j] + sc.eps2;
         const float num = sc.lr2 * mhat;
         th1[j] = thd[j] - math::div_markstein(num, den, math::recip_cr(den));

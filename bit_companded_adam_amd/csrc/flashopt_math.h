@@ -9,6 +9,8 @@
 //                  significand (2^33 pairs);
 //   softsign       every y in [-1.5, 1.5];
 //   sqrt_cr        every x in [0, 2^64) (and sqrt_x2p32_zero_tiny against it);
+//   sqrt_quot_x2p32  every v with fl(v / b) in [2^-126, 2^63), for the bias
+//                  correction divisors b of eight betas, and v = 0;
 //   byte_u8        every fp32 pattern (v_cvt_pk_u8_f32 == clamp(rint(x), 0, 255),
 //                  NaN -> 0);
 //   div_markstein  2^32 random pairs of its stated domain plus every divisor
@@ -190,6 +192,26 @@ __device__ __forceinline__ float sqrt_cr_x2p32(float x)
 __device__ __forceinline__ float sqrt_x2p32_zero_tiny(float x)
 {
     const float xs = __builtin_fmaf(x, 0x1p64f, 0x1p-126f);
+    const float y = __builtin_amdgcn_rsqf(xs);
+    const float s = xs * y;
+    const float h = 0.5f * y;
+    const float r = __builtin_fmaf(-s, s, xs);
+    return __builtin_fmaf(r, h, s);
+}
+
+// 2^32 sqrt(q) for q = fl(v / b), the correctly rounded fp32 quotient of
+// v >= 0 by an fp32 b > 0, given inv_s = 2^64 / b rounded to double.  The
+// quotient and the 2^64 input scaling of sqrt_cr_x2p32 come out of one fp64
+// fma: xs = fl(v inv_s + 2^-126).  Where q is normal, v inv_s >= 2^-62, so
+// the added 2^-126 moves it by at most 2^-64 relative and the double result
+// lies within 2^-51.9 + 2^-64 relative of the scaled quotient, closer than
+// any fp32 rounding boundary (div_by_f64_recip): xs = q 2^64 exactly.  Where
+// q is subnormal or zero, xs <= 2^-62 (2^-126 for v = 0, a normal number,
+// which keeps v_rsq_f32 finite: it flushes subnormal inputs) and the result
+// is below 2^-31 rather than q's exact root.  Domain: q < 2^63.
+__device__ __forceinline__ float sqrt_quot_x2p32(float v, double inv_s)
+{
+    const float xs = static_cast<float>(__builtin_fma(static_cast<double>(v), inv_s, 0x1p-126));
     const float y = __builtin_amdgcn_rsqf(xs);
     const float s = xs * y;
     const float h = 0.5f * y;

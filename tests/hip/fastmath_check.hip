@@ -243,6 +243,28 @@ __global__ void k_div_f64_recip(unsigned long long *bad)
     flush(bad, c);
 }
 
+// sqrt_quot_x2p32 for 16 bias-correction divisors (bias_divisor: t = 1, 2,
+// 3, 512 of four betas) over every v pattern in [0, 2^64): where fl(v / b) is
+// normal and below 2^63 it must equal sqrt_cr_x2p32(fl(v / b)); where the
+// quotient is zero or subnormal it must be finite and below 2^-31.
+__global__ void k_sqrt_quot(unsigned long long *bad)
+{
+    unsigned long long c = 0;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (16ull * 0x5F800000ull);
+         i += (uint64_t)gridDim.x * blockDim.x) {
+        const uint32_t k = (uint32_t)(i / 0x5F800000ull);
+        const uint32_t sel[4] = {0u, 1u, 2u, 511u};
+        const float b = bias_divisor(((k >> 2) << 9) + sel[k & 3u]);
+        const float v = __uint_as_float((uint32_t)(i % 0x5F800000ull));
+        const float q = v / b;
+        if (!(q < 0x1p63f)) continue;
+        const float got = sqrt_quot_x2p32(v, 0x1p64 / (double)b);
+        if (q >= 0x1p-126f) c += !same(got, sqrt_cr_x2p32(q));
+        else c += !(got >= 0.0f && got < 0x1p-31f);
+    }
+    flush(bad, c);
+}
+
 template <typename K>
 long long run(K kernel, unsigned grid)
 {
@@ -266,6 +288,7 @@ long long fastmath_check_softsign(void) { return run(k_softsign, 65536); }
 long long fastmath_check_cvt_pk_u8(void) { return run(k_cvt_pk_u8, 65536); }
 long long fastmath_check_div_markstein(void) { return run(k_div_markstein, 65536); }
 long long fastmath_check_div_f64_recip(void) { return run(k_div_f64_recip, 65536); }
+long long fastmath_check_sqrt_quot(void) { return run(k_sqrt_quot, 65536); }
 long long fastmath_check_magic_code(void) { return run(k_magic_code, 65536); }
 long long fastmath_check_softsign_code(void) { return run(k_softsign_code<true>, 65536); }
 long long fastmath_softsign_code_unguarded(void) { return run(k_softsign_code<false>, 65536); }

@@ -9,7 +9,9 @@ magic-number int8 code rounding over all 2^32 patterns; the update division over
 random pairs of its stated domain and every divisor significand at the
 domain's edges; the bias-correction division through an fp64 reciprocal over
 every dividend significand for 8192 divisors (the fp32 bias corrections of
-eight betas up to t = 512, and hashed ones); the guarded companded momentum code against the correctly
+eight betas up to t = 512, and hashed ones); the sqrt of that quotient with
+the input scaling folded into one fp64 fma, over every dividend for 16 bias
+corrections; the guarded companded momentum code against the correctly
 rounded chain around every rounding boundary for 4095 fp16 divisors
 (two-sided short form: trusted where its two evaluations agree)."""
 import ctypes
@@ -23,7 +25,7 @@ pytestmark = pytest.mark.gpu
 
 LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hip", "libfastmath_check.so")
 CHECKS = ["sqrt", "recip", "div_by_recip", "softsign", "cvt_pk_u8", "div_markstein", "div_f64_recip",
-          "magic_code", "softsign_code"]
+          "sqrt_quot", "magic_code", "softsign_code"]
 
 
 @pytest.fixture(scope="module")
