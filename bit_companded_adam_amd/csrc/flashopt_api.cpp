@@ -112,6 +112,12 @@ int states_of(int fp32_states, int companded)
                        : (companded ? flashopt::kStatesCompanded : flashopt::kStatesLinear);
 }
 
+// The step kernels' parameter format: the master width, or kParamF32.
+int kernel_format(const flashopt_adamw_args &a)
+{
+    return a.param_fp32 ? flashopt::kParamF32 : a.master_bits;
+}
+
 // AdamW hyper-parameters checked, then the step's fp32 scalars formed in
 // double and rounded once.
 flashopt_status adamw_scalars(const flashopt_adamw_args *a, StepScalars &sc)
@@ -120,7 +126,8 @@ flashopt_status adamw_scalars(const flashopt_adamw_args *a, StepScalars &sc)
     if (a->master_bits != 24 && a->master_bits != 32 && a->master_bits != 0) return FLASHOPT_EINVAL;
     if (a->companded != 0 && a->companded != 1) return FLASHOPT_EINVAL;
     if (a->fp32_states != 0 && a->fp32_states != 1) return FLASHOPT_EINVAL;
-    if (a->reserved != 0) return FLASHOPT_EINVAL;
+    if (a->param_fp32 != 0 && a->param_fp32 != 1) return FLASHOPT_EINVAL;
+    if (a->param_fp32 && a->master_bits != 0) return FLASHOPT_EINVAL;
     if (a->step < 1) return FLASHOPT_EINVAL;
     if (!(a->lr >= 0.0) || !std::isfinite(a->lr)) return FLASHOPT_EINVAL;
     if (!(a->beta1 >= 0.0 && a->beta1 < 1.0) || !(a->beta2 >= 0.0 && a->beta2 < 1.0)) return FLASHOPT_EINVAL;
@@ -356,7 +363,7 @@ flashopt_status flashopt_adamw_step(const flashopt_tensor *tensors, int n_tensor
                             workspace, ws_bytes, stream,
                             [&](const DevTensor *d, const int32_t *cs, int32_t total, hipStream_t st) {
                                 return flashopt::launch_adamw_step(d, cs, n_tensors, total, sc,
-                                                                   a->master_bits, states, st);
+                                                                   kernel_format(*a), states, st);
                             });
 }
 
@@ -369,7 +376,7 @@ flashopt_status flashopt_adamw_step_tensor(const flashopt_tensor *tensor,
     if (hs != FLASHOPT_OK) return hs;
     const flashopt_status ts = check_tensor(*tensor, a->master_bits != 0, a->fp32_states == 0, true);
     if (ts != FLASHOPT_OK || tensor->numel == 0) return ts;
-    return hip_status(flashopt::launch_adamw_tensor(device_descriptor(*tensor), sc, a->master_bits,
+    return hip_status(flashopt::launch_adamw_tensor(device_descriptor(*tensor), sc, kernel_format(*a),
                                                     states_of(a->fp32_states, a->companded),
                                                     static_cast<hipStream_t>(stream)));
 }
@@ -400,7 +407,7 @@ flashopt_status flashopt_adamw_step_noalloc(const flashopt_tensor *tensors, int 
     const DevTensor *d_desc = static_cast<const DevTensor *>(scratch);
     const int32_t *d_start = reinterpret_cast<const int32_t *>(d_desc + n_tensors);
     return hip_status(flashopt::launch_adamw_step(d_desc, d_start, n_tensors, acc, sc,
-                                                  a->master_bits,
+                                                  kernel_format(*a),
                                                   states_of(a->fp32_states, a->companded), st));
 }
 

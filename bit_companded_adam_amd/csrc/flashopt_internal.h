@@ -21,6 +21,12 @@ constexpr int kGroup = 32;
 // the companded specs, or plain fp32 moments (the unquantized-states ablation).
 enum : int { kStatesLinear = 0, kStatesCompanded = 1, kStatesFp32 = 2 };
 
+// The step kernels' parameter formats, as their master-bits argument: 24 and
+// 32 split a bf16 parameter with int8 / int16 rho, 0 updates a bf16
+// parameter without a split, kParamF32 updates an fp32 parameter (with an
+// fp32 gradient) in place, never split.
+constexpr int kParamF32 = 1;
+
 // Per-tensor descriptor of the multi-tensor step, staged in the workspace.
 // With fp32 states m_codes / v_codes point to float arrays.
 struct DevTensor {
@@ -91,7 +97,7 @@ hipError_t launch_reconstruct(const uint16_t *param, const void *rho, int64_t n,
                               int master_bits, float *master, hipStream_t stream);
 // tensors / chunk_start are device pointers into the workspace;
 // chunk_start has n_tensors + 1 entries.  master_bits: 24 | 32 | 0 (no
-// split); states: one of kStates*.
+// split) | kParamF32 (AdamW only); states: one of kStates*.
 hipError_t launch_adamw_step(const DevTensor *tensors, const int32_t *chunk_start,
                              int n_tensors, int32_t total_chunks,
                              const StepScalars &sc, int master_bits, int states,

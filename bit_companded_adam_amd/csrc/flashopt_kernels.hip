@@ -323,6 +323,9 @@ __device__ __forceinline__ void encode(const float (&a)[N], const GroupDiv &gd,
 // rho words of N elements: int16 for the 32-bit master, else int8.
 constexpr int rho_words(int mb, int n) { return mb == 32 ? n / 2 : n / 4; }
 
+// parameter (and gradient) words of N elements: fp32, or two bf16 per word.
+constexpr int param_words(int mb, int n) { return mb == kParamF32 ? n : n / 2; }
+
 // Re-split of N fp32 values into packed bf16 words and packed rho words.
 // theta' (ties away from zero) is the upper half of pattern + 0x8000; D is
 // the lower half of the pattern read as a signed 16-bit integer.  For the
@@ -671,12 +674,16 @@ __device__ __forceinline__ uint32_t plain_elem(float x)
 }
 
 // The new parameter words (and rho words with a master split) of N updated
-// values.  EXACT selects the element-wise NaN-safe routines.
+// values: the split, the bf16 cast, or the fp32 value itself.  EXACT selects
+// the element-wise NaN-safe routines.
 template <int MB, bool EXACT, int N>
-__device__ __forceinline__ void pack_theta(const float (&x)[N], uint32_t (&po)[N / 2],
+__device__ __forceinline__ void pack_theta(const float (&x)[N], uint32_t (&po)[param_words(MB, N)],
                                            uint32_t (&ro)[rho_words(MB, N)])
 {
-    if constexpr (MB == 0) {
+    if constexpr (MB == kParamF32) {          // an fp32 parameter keeps the update as is
+#pragma unroll
+        for (int i = 0; i < N; ++i) po[i] = __float_as_uint(x[i]);
+    } else if constexpr (MB == 0) {
 #pragma unroll
         for (int i = 0; i < N / 2; ++i) {
             if (EXACT) po[i] = pack_hi16(plain_elem(x[2 * i]), plain_elem(x[2 * i + 1]));
@@ -764,18 +771,18 @@ __device__ __forceinline__ void st_elems(void *p, int cnt, const uint32_t *w)
     }
 }
 
-// Elements per unit of each step variant: fp32 moments need N = 4 for
-// 16-byte accesses; the quantized variants use N = 8 (16-bit streams in
+// Elements per unit of each step variant: fp32 moments and fp32 parameters
+// need N = 4 for 16-byte accesses; the quantized variants use N = 8 (16-bit streams in
 // 16-byte accesses, a lane quad per group).  Measured on the 8.0B list
 // against N = 16: 1.1% faster for the 24-bit master, 8.4% for the 32-bit
 // master, 4.1% for the linear codec.
-constexpr int unit_elems(int mb, int st) { return st == kStatesFp32 ? 4 : 8; }
+constexpr int unit_elems(int mb, int st) { return (st == kStatesFp32 || mb == kParamF32) ? 4 : 8; }
 
 // One unit's inputs (arrays a variant does not use are removed by the
 // compiler).
 template <int MB, int ST, int N>
 struct UnitIn {
-    uint32_t pw[N / 2], gw[N / 2];
+    uint32_t pw[param_words(MB, N)], gw[param_words(MB, N)];
     uint32_t rw[rho_words(MB, N)];   // rho words, each value's sign bit flipped
     uint32_t mw[N / 4], vw[N / 4];   // codes (quantized states)
     uint32_t mf[N], vf[N];           // fp32 states, bit patterns
@@ -795,6 +802,8 @@ __device__ __forceinline__ uint32_t unit_first(int u, int lane)
 struct ChunkPtrs {
     uint16_t *param;
     const uint16_t *grad;
+    uint32_t *param32;          // the same streams as fp32 (kParamF32)
+    const uint32_t *grad32;
     uint8_t *rho8;
     uint16_t *rho16;
     uint8_t *mc, *vc;
@@ -812,6 +821,8 @@ __device__ __forceinline__ ChunkPtrs chunk_ptrs(const DevTensor &d, int32_t k)
     ChunkPtrs c;
     c.param = d.param + off;
     c.grad = d.grad + off;
+    c.param32 = reinterpret_cast<uint32_t *>(d.param) + off;
+    c.grad32 = reinterpret_cast<const uint32_t *>(d.grad) + off;
     c.rho8 = static_cast<uint8_t *>(d.rho) + off;
     c.rho16 = static_cast<uint16_t *>(d.rho) + off;
     c.mc = reinterpret_cast<uint8_t *>(d.m_codes) + off;
@@ -844,8 +855,13 @@ __device__ __forceinline__ void load_unit(const ChunkPtrs &c, uint32_t r, int cn
     in.smb = 0u;
     in.svb = 0u;
     if (FULL) {
-        ld_words<2 * N>(c.param + r, in.pw);
-        ld_words<2 * N>(c.grad + r, in.gw);
+        if constexpr (MB == kParamF32) {
+            ld_words<4 * N>(c.param32 + r, in.pw);
+            ld_words<4 * N>(c.grad32 + r, in.gw);
+        } else {
+            ld_words<2 * N>(c.param + r, in.pw);
+            ld_words<2 * N>(c.grad + r, in.gw);
+        }
         if constexpr (MB == 24) ld_words<N>(c.rho8 + r, in.rw);
         if constexpr (MB == 32) ld_words<2 * N>(c.rho16 + r, in.rw);
         if constexpr (ST == kStatesFp32) {
@@ -860,8 +876,13 @@ __device__ __forceinline__ void load_unit(const ChunkPtrs &c, uint32_t r, int cn
             }
         }
     } else {
-        ld_elems<2, N>(c.param + r, cnt, in.pw);
-        ld_elems<2, N>(c.grad + r, cnt, in.gw);
+        if constexpr (MB == kParamF32) {
+            ld_elems<4, N>(c.param32 + r, cnt, in.pw);
+            ld_elems<4, N>(c.grad32 + r, cnt, in.gw);
+        } else {
+            ld_elems<2, N>(c.param + r, cnt, in.pw);
+            ld_elems<2, N>(c.grad + r, cnt, in.gw);
+        }
         if constexpr (MB == 24) ld_elems<1, N>(c.rho8 + r, cnt, in.rw);
         if constexpr (MB == 32) ld_elems<2, N>(c.rho16 + r, cnt, in.rw);
         if constexpr (ST == kStatesFp32) {
@@ -909,9 +930,15 @@ __device__ __forceinline__ void element_moments(const UnitIn<MB, ST, N> &in, int
                                                 const float *s_vu, float ms, float vs,
                                                 float &theta, float &m, float &v)
 {
-    if constexpr (MB == 0) theta = (j & 1) ? bf16_hi(in.pw[j >> 1]) : bf16_lo(in.pw[j >> 1]);
-    else theta = reconstruct_perm<MB>(in.pw, in.rw, j);
-    const float g = (j & 1) ? bf16_hi(in.gw[j >> 1]) : bf16_lo(in.gw[j >> 1]);
+    float g;
+    if constexpr (MB == kParamF32) {
+        theta = __uint_as_float(in.pw[j]);
+        g = __uint_as_float(in.gw[j]);
+    } else {
+        if constexpr (MB == 0) theta = (j & 1) ? bf16_hi(in.pw[j >> 1]) : bf16_lo(in.pw[j >> 1]);
+        else theta = reconstruct_perm<MB>(in.pw, in.rw, j);
+        g = (j & 1) ? bf16_hi(in.gw[j >> 1]) : bf16_lo(in.gw[j >> 1]);
+    }
     float m0, v0;
     if constexpr (ST == kStatesFp32) {
         m0 = __uint_as_float(in.mf[j]);
@@ -940,7 +967,7 @@ template <int MB, int ST, int N>
 __device__ __forceinline__ void unit_exact(const ChunkPtrs &c, uint32_t r, int cnt,
                                            const StepScalars &sc, const float *s_mu,
                                            const float *s_vu, uint32_t sm,
-                                           uint32_t (&mo)[N / 4], uint32_t (&po)[N / 2],
+                                           uint32_t (&mo)[N / 4], uint32_t (&po)[param_words(MB, N)],
                                            uint32_t (&ro)[rho_words(MB, N)])
 {
     constexpr unsigned kMSpec =
@@ -1105,7 +1132,7 @@ __device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
     const bool exact = sc.fast == 0 || !vfast || !(am <= sc.m1_max) || kmin < sc.num_key || any_nan;
 
     // ---- group maxima, scales, variance codes
-    uint32_t mo[N / 4], vo[N / 4], po[N / 2], ro[rho_words(MB, N)];
+    uint32_t mo[N / 4], vo[N / 4], po[param_words(MB, N)], ro[rho_words(MB, N)];
     uint32_t sm_out = 0u, sv_out = 0u;
     if constexpr (kQuant) {
         sm_out = f16_bits(group_max<32 / N>(am));
@@ -1150,7 +1177,8 @@ __device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
 #pragma unroll
     for (int j = 0; j < N; ++j) { mb[j] = __float_as_uint(m1[j]); vb[j] = __float_as_uint(v1[j]); }
     if (FULL) {
-        st_words<2 * N>(c.param + r, po);
+        if constexpr (MB == kParamF32) st_words<4 * N>(c.param32 + r, po);
+        else st_words<2 * N>(c.param + r, po);
         if constexpr (MB == 24) st_words<N>(c.rho8 + r, ro);
         if constexpr (MB == 32) st_words<2 * N>(c.rho16 + r, ro);
         if constexpr (kQuant) {
@@ -1161,7 +1189,8 @@ __device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
             st_words<4 * N>(c.vf + r, vb);
         }
     } else {
-        st_elems<2, N>(c.param + r, cnt, po);
+        if constexpr (MB == kParamF32) st_elems<4, N>(c.param32 + r, cnt, po);
+        else st_elems<2, N>(c.param + r, cnt, po);
         if constexpr (MB == 24) st_elems<1, N>(c.rho8 + r, cnt, ro);
         if constexpr (MB == 32) st_elems<2, N>(c.rho16 + r, cnt, ro);
         if constexpr (kQuant) {
@@ -1573,7 +1602,8 @@ hipError_t sgd_variant(const DevTensor *tensors, const int32_t *chunk_start, int
     return hipGetLastError();
 }
 
-// The nine (master_bits, states) instantiations of one step kernel family.
+// The (master_bits, states) instantiations of one step kernel family: nine,
+// plus the three fp32-parameter ones where the family has them.
 template <template <int, int> class K, typename Sc>
 hipError_t dispatch(int master_bits, int states, const DevTensor *tensors,
                     const int32_t *chunk_start, int n_tensors, int32_t total_chunks,
@@ -1588,12 +1618,23 @@ hipError_t dispatch(int master_bits, int states, const DevTensor *tensors,
     case 32 * 4 + kStatesFp32: return K<32, kStatesFp32>::run(tensors, chunk_start, n_tensors, total_chunks, sc, st);
     case kStatesCompanded: return K<0, kStatesCompanded>::run(tensors, chunk_start, n_tensors, total_chunks, sc, st);
     case kStatesLinear: return K<0, kStatesLinear>::run(tensors, chunk_start, n_tensors, total_chunks, sc, st);
-    default: return K<0, kStatesFp32>::run(tensors, chunk_start, n_tensors, total_chunks, sc, st);
+    case kStatesFp32: return K<0, kStatesFp32>::run(tensors, chunk_start, n_tensors, total_chunks, sc, st);
+    default: break;
     }
+    if constexpr (K<0, kStatesFp32>::kFp32Params) {
+        switch (master_bits * 4 + states) {
+        case kParamF32 * 4 + kStatesCompanded: return K<kParamF32, kStatesCompanded>::run(tensors, chunk_start, n_tensors, total_chunks, sc, st);
+        case kParamF32 * 4 + kStatesLinear: return K<kParamF32, kStatesLinear>::run(tensors, chunk_start, n_tensors, total_chunks, sc, st);
+        case kParamF32 * 4 + kStatesFp32: return K<kParamF32, kStatesFp32>::run(tensors, chunk_start, n_tensors, total_chunks, sc, st);
+        default: break;
+        }
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int MB, int ST>
 struct AdamWLaunch {
+    static constexpr bool kFp32Params = true;
     static hipError_t run(const DevTensor *t, const int32_t *cs, int n, int32_t total,
                           const StepScalars &sc, hipStream_t st)
     {
@@ -1603,6 +1644,7 @@ struct AdamWLaunch {
 
 template <int MB, int ST>
 struct SgdLaunch {
+    static constexpr bool kFp32Params = false;
     static hipError_t run(const DevTensor *t, const int32_t *cs, int n, int32_t total,
                           const SgdScalars &sc, hipStream_t st)
     {
@@ -1613,6 +1655,7 @@ struct SgdLaunch {
 // Single-tensor launches: t points to a host descriptor passed by value.
 template <int MB, int ST>
 struct AdamWTensorLaunch {
+    static constexpr bool kFp32Params = true;
     static hipError_t run(const DevTensor *t, const int32_t *, int, int32_t total,
                           const StepScalars &sc, hipStream_t st)
     {
@@ -1625,6 +1668,7 @@ struct AdamWTensorLaunch {
 
 template <int MB, int ST>
 struct SgdTensorLaunch {
+    static constexpr bool kFp32Params = false;
     static hipError_t run(const DevTensor *t, const int32_t *, int, int32_t total,
                           const SgdScalars &sc, hipStream_t st)
     {

@@ -52,7 +52,7 @@ class flashopt_adamw_args(ctypes.Structure):
                 ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
                 ("weight_decay", ctypes.c_double), ("step", ctypes.c_int64),
                 ("master_bits", ctypes.c_int), ("companded", ctypes.c_int),
-                ("fp32_states", ctypes.c_int), ("reserved", ctypes.c_int)]
+                ("fp32_states", ctypes.c_int), ("param_fp32", ctypes.c_int)]
 
 
 class flashopt_sgd_args(ctypes.Structure):
@@ -195,17 +195,21 @@ def flashopt_reconstruct(param: torch.Tensor, rho: torch.Tensor, master_bits: in
 # --------------------------------------------------------------- step
 
 class TensorState:
-    """Device state of one parameter tensor: bf16 param (updated in place),
-    rho (master_bits 24 | 32; none for master_bits None), and the momentum
+    """Device state of one parameter tensor: bf16 or fp32 param (updated in
+    place; fp32 only without a split), rho (master_bits 24 | 32; none for
+    master_bits None), and the momentum
     and variance as codes with fp16 scales, or as fp32 arrays when
     quantize_states is False.  Fresh state is zero."""
 
     def __init__(self, param: torch.Tensor, master_bits=24, quantize_states: bool = True,
                  variance: bool = True):
-        if param.dtype != torch.bfloat16 or not param.is_contiguous() or not param.is_cuda:
-            raise ValueError("param must be a contiguous bf16 device tensor")
+        if param.dtype not in (torch.bfloat16, torch.float32) or not param.is_contiguous() \
+                or not param.is_cuda:
+            raise ValueError("param must be a contiguous bf16 or fp32 device tensor")
         if master_bits not in (24, 32, None):
             raise ValueError("master_bits must be 24, 32 or None")
+        if param.dtype == torch.float32 and master_bits is not None:
+            raise ValueError("an fp32 parameter is never split: use master_bits=None")
         n, dev = param.numel(), param.device
         self.param = param
         self.rho = None if master_bits is None else torch.zeros(n, dtype=rho_dtype(master_bits), device=dev)
@@ -222,8 +226,8 @@ class TensorState:
         self.quantize_states = quantize_states
 
     def descriptor(self, grad: torch.Tensor) -> flashopt_tensor:
-        if grad.dtype != torch.bfloat16 or grad.numel() != self.param.numel():
-            raise ValueError("grad must be bf16 with the parameter's size")
+        if grad.dtype != self.param.dtype or grad.numel() != self.param.numel():
+            raise ValueError(f"grad must be {self.param.dtype} with the parameter's size")
         if grad.device != self.param.device:
             raise ValueError(f"grad is on {grad.device}, its parameter on {self.param.device}")
         opt = lambda t, name: 0 if t is None else _dev(t, name)
@@ -234,11 +238,13 @@ class TensorState:
 
 
 def make_args(step: int, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0,
-              master_bits=24, companded=True, quantize_states=True) -> flashopt_adamw_args:
-    """master_bits 24 | 32 | None (no split); quantize_states False: fp32 m, v."""
+              master_bits=24, companded=True, quantize_states=True,
+              param_fp32=False) -> flashopt_adamw_args:
+    """master_bits 24 | 32 | None (no split); quantize_states False: fp32 m, v;
+    param_fp32: fp32 parameters and gradients (needs master_bits None)."""
     return flashopt_adamw_args(lr, betas[0], betas[1], eps, weight_decay, step,
                                0 if master_bits is None else master_bits, int(companded),
-                               0 if quantize_states else 1, 0)
+                               0 if quantize_states else 1, int(param_fp32))
 
 
 def flashopt_adamw_workspace_bytes(n_tensors: int) -> int:
@@ -365,14 +371,20 @@ def attach_grad_release(opt, params, batch_below: int = 0):
 
 
 class FlashAdamW(_Stepper):
-    """A list of TensorStates stepped together by one launch per step."""
+    """A list of TensorStates stepped together by one launch per step.  The
+    parameters share one dtype: bf16 (split per master_bits, or cast back
+    with master_bits None) or fp32 (master_bits None; fp32 gradients)."""
 
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0,
                  master_bits=24, companded=True, quantize_states=True):
         self.states = [TensorState(p, master_bits, quantize_states) for p in params]
+        dtypes = {s.param.dtype for s in self.states}
+        if len(dtypes) > 1:
+            raise ValueError("all parameters of one FlashAdamW must share a dtype (bf16 or fp32)")
         self.hp = dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay,
                        master_bits=master_bits, companded=companded,
-                       quantize_states=quantize_states)
+                       quantize_states=quantize_states,
+                       param_fp32=dtypes == {torch.float32})
         self._init_common()
         nbytes = max(16, flashopt_adamw_workspace_bytes(len(self.states)))
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device or "cuda")

@@ -102,10 +102,12 @@ def numel(shape) -> int:
     return n
 
 
-def init_param(n: int, device="cpu", seed: int = PARAM_SEED, std: float = 0.02) -> torch.Tensor:
-    """bf16 weights, torch's round-to-nearest-even cast of N(0, std^2) fp32."""
+def init_param(n: int, device="cpu", seed: int = PARAM_SEED, std: float = 0.02,
+               dtype=torch.bfloat16) -> torch.Tensor:
+    """Weights N(0, std^2) drawn in fp32, cast to dtype (bf16: torch's
+    round-to-nearest-even cast; fp32: as drawn)."""
     g = torch.Generator(device=device).manual_seed(seed)
-    return (torch.randn(n, generator=g, device=device) * std).to(torch.bfloat16)
+    return (torch.randn(n, generator=g, device=device) * std).to(dtype)
 
 
 def grad_factors(count: int, seed: int = FACTOR_SEED) -> torch.Tensor:
@@ -115,11 +117,13 @@ def grad_factors(count: int, seed: int = FACTOR_SEED) -> torch.Tensor:
 
 
 def make_grad(n: int, step: int, device="cpu", seed: int = GRAD_SEED,
-              scale: float = 1e-3, factor: float = 1.0, stream_id: int = 0) -> torch.Tensor:
-    """bf16 gradient of one tensor at one step: N(0, 1) * scale * factor,
-    freshly drawn from (seed, stream_id, step)."""
+              scale: float = 1e-3, factor: float = 1.0, stream_id: int = 0,
+              dtype=torch.bfloat16) -> torch.Tensor:
+    """Gradient of one tensor at one step: N(0, 1) * scale * factor in fp32,
+    freshly drawn from (seed, stream_id, step), cast to dtype (bf16 by
+    default; fp32 for an fp32 parameter)."""
     g = torch.Generator(device=device).manual_seed(seed + 1_000_003 * stream_id + step)
-    return (torch.randn(n, generator=g, device=device) * (scale * factor)).to(torch.bfloat16)
+    return (torch.randn(n, generator=g, device=device) * (scale * factor)).to(dtype)
 
 
 def bf16_bits(t: torch.Tensor) -> torch.Tensor:

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define FLASHOPT_ABI_VERSION 4
+#define FLASHOPT_ABI_VERSION 5
 
 typedef enum {
     FLASHOPT_OK = 0,
@@ -148,7 +148,13 @@ typedef struct {
     int companded;            /* 1: softsign m, sqrt v (Alg. 2/3); 0: linear ablation */
     int fp32_states;          /* 0: quantized m, v (codes + fp16 scales);
                                  1: fp32 m, v (quantize_states=False)         */
-    int reserved;             /* must be 0                                    */
+    int param_fp32;           /* 0: bf16 parameters and gradients;
+                                 1: fp32 parameters and fp32 gradients (param
+                                 and grad point to float [numel]), never split
+                                 (the page's use_split is false for an fp32
+                                 parameter): theta is the parameter and the
+                                 update is stored unchanged; needs
+                                 master_bits 0 (rho unused)                   */
 } flashopt_adamw_args;
 
 /* Device workspace bytes that flashopt_adamw_step needs for this list (the
@@ -167,7 +173,8 @@ size_t flashopt_adamw_workspace_bytes(const flashopt_tensor *tensors, int n_tens
  *   theta -= (lr mhat) / (sqrt(vhat) + eps)     (the page's order, "Standard
  *                                                 AdamW update")
  *   (m, v) = quantize(m1), quantize(v1);  (param, rho) = split(theta)
- *   (fp32 states: m, v = m1, v1;  master_bits 0: param = bf16 RNE of theta)
+ *   (fp32 states: m, v = m1, v1;  master_bits 0: param = bf16 RNE of theta;
+ *    param_fp32: theta = param, param = theta)
  * Scalars are formed in double on the host and rounded once to fp32; every
  * fp32 operation is rounded once, in the order written (no contraction).
  *   tensors   HOST array of n_tensors descriptors (read during the call only)
@@ -182,7 +189,8 @@ size_t flashopt_adamw_workspace_bytes(const flashopt_tensor *tensors, int n_tens
  * kernel with its arguments by value and stages nothing.
  * Errors: EINVAL (n_tensors < 0, NULL tensors/args, numel < 0, NULL pointer
  * that the variant uses in a non-empty tensor, master_bits, companded,
- * fp32_states, reserved != 0, step < 1, lr < 0, beta outside
+ * fp32_states, param_fp32 not 0 or 1, param_fp32 with master_bits != 0,
+ * step < 1, lr < 0, beta outside
  * [0, 1), eps < 0, non-finite weight_decay, more than 2^31 - 1 chunks of
  * 1024 elements in total), EALIGN, EWORKSPACE, EHIP. */
 flashopt_status flashopt_adamw_step(const flashopt_tensor *tensors, int n_tensors,

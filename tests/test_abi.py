@@ -93,7 +93,7 @@ def test_step_validation(L):
     ok = [_tensor()]
     # hyper-parameters
     for bad in (dict(step=0), dict(master_bits=16), dict(companded=2), dict(fp32_states=2),
-                dict(reserved=1), dict(lr=-1.0),
+                dict(param_fp32=2), dict(param_fp32=1), dict(lr=-1.0),
                 dict(beta1=1.0), dict(beta2=-0.1), dict(eps=-1e-8),
                 dict(weight_decay=float("inf")), dict(lr=float("nan"))):
         a = F.make_args(1)

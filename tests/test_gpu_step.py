@@ -14,6 +14,7 @@ within 1e-6 relative (implied by bit-exact param and rho).
   * ragged multi-tensor lists (sizes 0, 1, 17, ..., 70001) in one launch, all
     master widths and both companding modes, 3 steps.
   * determinism across runs and launch shapes.
+  * the full 1.2B decoder list, every element, after each of two steps.
   * full-size decoder lists (1.2B and 8.0B parameters) in the launch
     configuration the benchmark times, checked on group-aligned samples: the
     first and last 2^16 elements of every tensor and random 1024-element
@@ -219,6 +220,45 @@ def test_ablation_10_steps(orc, mb, comp, qs):
         _compare(_snap(opt.states[0]), free, mb, f"{_vid((mb, comp, qs))} step {t}")
 
 
+@pytest.mark.parametrize("comp,qs", [(True, True), (False, True), (True, False)],
+                         ids=["comp", "lin", "f32-states"])
+def test_fp32_params_10_steps(orc, comp, qs):
+    """fp32 parameters with fp32 gradients, never split (FlashAdamWSim.step's
+    use_split is false for an fp32 parameter): a ragged list over 10
+    free-running steps against the oracle, every stored bit equal; the
+    single-tensor launches of a second copy give the same bits."""
+    require_gpu()
+    sizes = [1, 33, 4096 + 5, 70001, (1 << 18) + 77]
+    mk = lambda: [W.init_param(n, device="cuda", seed=300 + i, dtype=torch.float32)
+                  for i, n in enumerate(sizes)]
+    params, params_b = mk(), mk()
+    want = [oracle.State.zeros_like_param(host(p).copy(), None, quantize_states=qs) for p in params]
+    opt = F.FlashAdamW(params, master_bits=None, companded=comp, quantize_states=qs, **HP)
+    opt_b = F.FlashAdamW(params_b, master_bits=None, companded=comp, quantize_states=qs, **HP)
+    for t in range(1, 11):
+        grads = [W.make_grad(n, t, device="cuda", stream_id=i, factor=float(np.exp(i - 2)),
+                             dtype=torch.float32) for i, n in enumerate(sizes)]
+        opt.step(grads)
+        for i, g in enumerate(grads):
+            opt_b.step_tensor(i, g)
+        torch.cuda.synchronize()
+        for i, (s, sb, w, g) in enumerate(zip(opt.states, opt_b.states, want, grads)):
+            orc.adamw_step(w, host(g), oracle.hparams(
+                lr=HP["lr"], betas=HP["betas"], eps=HP["eps"], weight_decay=HP["weight_decay"],
+                step=t, master_bits=None, companded=comp, quantize_states=qs, fp32_param=True))
+            label = f"fp32 params comp{comp} qs{qs} t{t} tensor{i}"
+            assert (host(s.param).view(np.uint32) == w.param.view(np.uint32)).all(), label
+            for name in ("m_codes", "m_scales", "v_codes", "v_scales"):
+                a, b = getattr(s, name), getattr(w, name)
+                if b is None:
+                    continue
+                assert (host(a).view(np.uint8) == b.view(np.uint8)).all(), f"{label}: {name}"
+                assert (host(getattr(sb, name)).view(np.uint8) == b.view(np.uint8)).all(), \
+                    f"{label}: {name} (single-tensor launch)"
+            assert (host(sb.param).view(np.uint32) == w.param.view(np.uint32)).all(), \
+                f"{label}: single-tensor launch"
+
+
 def test_zero_and_large_gradients(orc):
     """All-zero gradients keep zero scales and codes; gradients of very
     different magnitude across tensors."""
@@ -389,6 +429,33 @@ def _sampled_parity(orc, shapes, mb, comp, label, qs=True):
 def test_decoder_1b_sampled(orc):
     require_gpu()
     _sampled_parity(orc, W.decoder_1b_shapes(), 24, True, "1.2B list, 24-bit")
+
+
+def test_decoder_1b_full(orc):
+    """The whole 1.2B list (199 tensors, 1,195,991,040 elements) in one list
+    launch per step, as the benchmark times it, every stored element compared
+    with the oracle's OpenMP list driver (the same per-element arithmetic as
+    its single-tensor step) after each of two steps."""
+    require_gpu()
+    shapes = W.decoder_1b_shapes()
+    opt = _build_list(shapes, 24, True, seed_base=1000)
+    factors = W.grad_factors(len(shapes)).numpy()
+    want = [oracle.State.zeros_like_param(u16(s.param), 24) for s in opt.states]
+    n = sum(s.param.numel() for s in opt.states)
+    for t in (1, 2):
+        grads = _grads(shapes, t, factors)
+        gh = [u16(g) for g in grads]
+        opt.step(grads)
+        del grads
+        torch.cuda.synchronize()
+        threads = orc.adamw_step_list(want, gh, _orc_hp(t, 24, True))
+        del gh
+        for i, (s, w) in enumerate(zip(opt.states, want)):
+            _compare(_snap(s), w, 24, f"1.2B full list, step {t}, tensor {i}")
+        print(f"1.2B list, step {t}: all {n} elements bit-exact (oracle on {threads} threads)",
+              flush=True)
+    del opt
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("mb,qs", [(None, True), (24, False)], ids=["mb_none", "fp32_states"])
