@@ -9,8 +9,10 @@ before timing starts (bf16 weights ~ N(0, 0.02^2); one bf16 gradient set
 N(0, 1e-3^2) times a per-tensor lognormal factor, reused by every step).
 
 Other configurations (reported beside the default, not as its value):
---workload decoder-1b-list (199 tensors, 1,195,991,040 params), --master-bits
-32 | 0 (0: no split, the page's master_weight_bits=None), --linear (linear
+--workload decoder-1b-list (199 tensors, 1,195,991,040 params), --workload
+flat-2^20 (one tensor of 2^20 params: cache-resident, a latency figure),
+--master-bits 32 | 0 (0: no split, the page's master_weight_bits=None),
+--param-fp32 (fp32 parameters, never split), --linear (linear
 codec ablation), --fp32-states (quantize_states=False), --optimizer sgd (the
 FlashSGD step: lr 1e-2, momentum 0.9, weight decay 0.01), --grad-release (one
 single-tensor launch per tensor, the gradient-release launch pattern).
@@ -18,8 +20,9 @@ single-tensor launch per tensor, the gradient-release launch pattern).
 
 Prints one JSON line: Gparam/s over the K timed steps, the roofline of the
 step kernel (algorithmic bytes per param of the configuration against
-8 TB/s), the oracle's throughput on host cores for a bounded sample of the
-same workload, and the GPU, ROCm and clock readings.
+8 TB/s), the oracle's throughput on host cores (the 1.2B list in full on all
+threads, and a sixteenth of it on one thread), and the GPU, CPU, ROCm and
+clock readings.
 """
 from __future__ import annotations
 
@@ -45,15 +48,17 @@ KERNEL_SRC = os.path.join(ROOT, "bit_companded_adam_amd", "csrc", "flashopt_kern
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "adamw_step_8b_traffic.json")
 
 
-def bytes_per_param(master_bits: int, quantize_states: bool = True, n_states: int = 2) -> float:
-    """Algorithmic HBM bytes per parameter per step: read bf16 param 2, bf16
-    grad 2, rho 1|2 (none without a split), each state (m and v for AdamW, the
-    momentum buffer for SGD) 1 byte plus an fp16 scale per 32 (2/32), or 4
-    bytes as fp32; write all of them except the grad."""
+def bytes_per_param(master_bits: int, quantize_states: bool = True, n_states: int = 2,
+                    param_bytes: int = 2) -> float:
+    """Algorithmic HBM bytes per parameter per step: read the param and its
+    grad (bf16: 2 bytes each; fp32 parameters: 4), rho 1|2 (none without a
+    split), each state (m and v for AdamW, the momentum buffer for SGD) 1
+    byte plus an fp16 scale per 32 (2/32), or 4 bytes as fp32; write all of
+    them except the grad."""
     rho = {24: 1, 32: 2, 0: 0}[master_bits]
     states = n_states * ((1 + 2 / 32) if quantize_states else 4)
-    read = 2 + 2 + rho + states
-    write = 2 + rho + states
+    read = 2 * param_bytes + rho + states
+    write = param_bytes + rho + states
     return read + write
 
 
@@ -85,30 +90,41 @@ def traffic_per_launch():
     return None if rec is None else rec.get("hbm_bytes_per_launch")
 
 
-def valu_roofline(ms_launch: float):
+def valu_roofline(ms_launch: float, sclk_mhz=None):
     """The step's second roof: its VALU wavefront instructions per launch
     (committed counter record) at the peak issue rate, against the measured
-    launch time; None when the record is stale."""
+    launch time; also at the shader clock the GPU reported right after the
+    timed steps (the chip runs below 2.4 GHz under this load).  None when the
+    record is stale."""
     rec = _counter_record()
     if rec is None or not rec.get("valu_insts_per_launch"):
         return None
     lane_insts = rec["valu_insts_per_launch"] * 64
     achieved = lane_insts / (ms_launch * 1e-3)
-    return {"bound": "alu", "achieved": achieved, "peak": PEAK_VALU_LANE_INSTS,
-            "unit": "VALU lane-instructions/s", "frac": achieved / PEAK_VALU_LANE_INSTS,
-            "ms_at_peak": lane_insts / PEAK_VALU_LANE_INSTS * 1e3}
+    out = {"bound": "alu", "achieved": achieved, "peak": PEAK_VALU_LANE_INSTS,
+           "unit": "VALU lane-instructions/s", "frac": achieved / PEAK_VALU_LANE_INSTS,
+           "ms_at_peak": lane_insts / PEAK_VALU_LANE_INSTS * 1e3,
+           "valu_per_element_lane": rec.get("valu_per_element_lane")}
+    if sclk_mhz:
+        peak_clk = PEAK_VALU_LANE_INSTS * sclk_mhz / 2400.0
+        out.update(sclk_mhz=sclk_mhz, peak_at_sclk=peak_clk, frac_at_sclk=achieved / peak_clk,
+                   ms_at_sclk=lane_insts / peak_clk * 1e3)
+    return out
 
 
-WORKLOADS = {"decoder-8b-list": W.decoder_8b_shapes, "decoder-1b-list": W.decoder_1b_shapes}
+WORKLOADS = {"decoder-8b-list": W.decoder_8b_shapes, "decoder-1b-list": W.decoder_1b_shapes,
+             "flat-2^20": lambda: [("flat", (1 << 20,))]}
 
 
 def build_workload(master_bits: int, companded: bool, quantize_states: bool = True,
-                   workload: str = "decoder-8b-list", optimizer: str = "adamw"):
+                   workload: str = "decoder-8b-list", optimizer: str = "adamw",
+                   param_fp32: bool = False):
     shapes = WORKLOADS[workload]()
-    params = [W.init_param(W.numel(s), device="cuda", seed=W.PARAM_SEED + i)
+    dt = torch.float32 if param_fp32 else torch.bfloat16
+    params = [W.init_param(W.numel(s), device="cuda", seed=W.PARAM_SEED + i, dtype=dt)
               for i, (_, s) in enumerate(shapes)]
     factors = W.grad_factors(len(shapes)).tolist()
-    grads = [W.make_grad(W.numel(s), 1, device="cuda", stream_id=i, factor=factors[i])
+    grads = [W.make_grad(W.numel(s), 1, device="cuda", stream_id=i, factor=factors[i], dtype=dt)
              for i, (_, s) in enumerate(shapes)]
     if optimizer == "sgd":
         opt = F.FlashSGD(params, master_bits=master_bits or None, companded=companded,
@@ -127,9 +143,15 @@ def environment() -> dict:
     try:
         prop = torch.cuda.get_device_properties(0)
         env.update(gpu=prop.name, arch=getattr(prop, "gcnArchName", None),
-                   compute_units=prop.multi_processor_count, hip=torch.version.hip)
+                   compute_units=prop.multi_processor_count, hip_torch_build=torch.version.hip)
     except Exception:
         pass
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm_runtime"] = f.read().strip()
+    except OSError:
+        pass
+    env["cpu_model"] = cpu_model()
     if "rocprof" in os.environ.get("LD_PRELOAD", ""):
         return env                  # no child processes under a profiler's preload
     try:
@@ -147,6 +169,14 @@ def environment() -> dict:
     except Exception:
         pass
     return env
+
+
+def _mhz(text):
+    """'2157Mhz' -> 2157.0 (None if unreadable)."""
+    try:
+        return float(str(text).lower().replace("mhz", "").strip())
+    except (TypeError, ValueError):
+        return None
 
 
 def time_steps(opt, grads, steps: int, warmup: int, per_tensor: bool = False,
@@ -184,43 +214,81 @@ def time_steps(opt, grads, steps: int, warmup: int, per_tensor: bool = False,
     return wall, per
 
 
-def cpu_baseline(master_bits: int, target_elems: int, threads: int, min_seconds: float = 10.0,
-                 companded: bool = True, quantize_states: bool = True):
-    """The oracle as it is, on host threads, over a bounded sample of the
-    workload: the first target_elems / 32 elements of each of 32 evenly spaced
-    tensors of the 8.0B list (same distributions), steps 2, 3, ... after an
-    untimed step 1, repeated for about min_seconds."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _host_list(shapes, frac: int, master_bits, quantize_states, param_fp32=False):
+    """Host copies of the seeded workload's parameters (the first 1/frac of
+    each tensor, 32-aligned) with fresh oracle states, and one seeded
+    gradient set; generated on the GPU with the benchmark's seeds."""
+    import oracle
+    factors = W.grad_factors(len(shapes)).tolist()
+    dt = torch.float32 if param_fp32 else torch.bfloat16
+    host = (lambda t: t.cpu().numpy()) if param_fp32 else \
+        (lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16))
+    states, grads = [], []
+    for i, (_, shp) in enumerate(shapes):
+        n = W.numel(shp)
+        m = n if frac == 1 else max(32, (n // frac) // 32 * 32)
+        p = W.init_param(n, device="cuda", seed=W.PARAM_SEED + i, dtype=dt)[:m]
+        g = W.make_grad(n, 1, device="cuda", stream_id=i, factor=factors[i], dtype=dt)[:m]
+        states.append(oracle.State.zeros_like_param(host(p).copy(), master_bits or None,
+                                                    quantize_states))
+        grads.append(np.ascontiguousarray(host(g)))
+        del p, g
+    torch.cuda.empty_cache()
+    return states, grads
+
+
+def _time_oracle(states, grads, hp, threads, steps=3):
+    """Median seconds of `steps` timed list steps (after one untimed step)."""
+    import oracle
+    oracle.adamw_step_list(states, grads, oracle.hparams(step=1, **hp), threads)
+    times, used = [], 0
+    for k in range(steps):
+        t0 = time.perf_counter()
+        used = oracle.adamw_step_list(states, grads, oracle.hparams(step=2 + k, **hp), threads)
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times)), used
+
+
+def cpu_baseline(master_bits: int, companded: bool = True, quantize_states: bool = True,
+                 threads: int = 0, single_frac: int = 16, param_fp32: bool = False):
+    """The oracle as it is (its OpenMP list driver, unchanged) on the host's
+    cores over the 1.2B decoder list in full -- the shapes of one GPU's share
+    of the 8.0B list on 8 GPUs; the step is elementwise, so its rate per
+    parameter is the 8.0B list's -- with the benchmark's seeded inputs: one
+    untimed step, then the median of three timed steps at all host threads.
+    The same on one thread over the first 1/single_frac of every tensor (the
+    whole list takes about 30 s per step on one thread)."""
     import oracle
     oracle.build(force=False)
-    shapes = W.decoder_8b_shapes()
-    pick = np.linspace(0, len(shapes) - 1, 32).astype(int)
-    per = target_elems // 32
-    factors = W.grad_factors(len(shapes)).numpy()
-    states, g1, g2 = [], [], []
-    for k, i in enumerate(pick):
-        n = min(per, W.numel(shapes[i][1]))
-        p = W.init_param(n, seed=W.PARAM_SEED + int(i)).view(torch.int16).numpy().view(np.uint16)
-        states.append(oracle.State.zeros_like_param(p, master_bits or None, quantize_states))
-        for lst, t in ((g1, 1), (g2, 2)):
-            lst.append(W.make_grad(n, t, stream_id=int(i), factor=float(factors[i]))
-                       .view(torch.int16).numpy().view(np.uint16))
+    shapes = W.decoder_1b_shapes()
     hp = dict(lr=W.HP_DEFAULT["lr"], betas=W.HP_DEFAULT["betas"], eps=W.HP_DEFAULT["eps"],
               weight_decay=W.HP_DEFAULT["weight_decay"], master_bits=master_bits or None,
-              companded=companded, quantize_states=quantize_states)
-    oracle.adamw_step_list(states, g1, oracle.hparams(step=1, **hp), threads)
-    n_total = sum(s.param.size for s in states)
-    steps, used = 0, 0
-    t0 = time.perf_counter()
-    while True:                      # steps 2, 3, ... until about min_seconds of work
-        used = oracle.adamw_step_list(states, g2 if steps % 2 == 0 else g1,
-                                      oracle.hparams(step=2 + steps, **hp), threads)
-        steps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
-    return {"value": n_total * steps / dt / 1e9, "unit": "Gparam/s", "cores": used, "kind": "oracle",
-            "sample": f"{n_total} params (first {per} elements of 32 of the 290 tensors of the "
-                      f"8.0B list), {steps} steps in {dt:.1f} s"}
+              companded=companded, quantize_states=quantize_states, fp32_param=param_fp32)
+    states, grads = _host_list(shapes, 1, master_bits, quantize_states, param_fp32)
+    n_all = sum(s.param.size for s in states)
+    dt_all, used = _time_oracle(states, grads, hp, threads)
+    del states, grads
+    states, grads = _host_list(shapes, single_frac, master_bits, quantize_states, param_fp32)
+    n_one = sum(s.param.size for s in states)
+    dt_one, _ = _time_oracle(states, grads, hp, 1)
+    return {"value": n_all / dt_all / 1e9, "unit": "Gparam/s", "cores": used, "kind": "oracle",
+            "sample": f"the 1.2B decoder list in full ({n_all} params, 199 tensors), median of "
+                      f"3 steps ({dt_all:.2f} s each) on {used} threads",
+            "single_thread": {"value": n_one / dt_one / 1e9, "unit": "Gparam/s", "cores": 1,
+                              "sample": f"first 1/{single_frac} of every tensor of the 1.2B list "
+                                        f"({n_one} params), median of 3 steps ({dt_one:.2f} s each)"},
+            "cpu_model": cpu_model(), "host_threads": os.cpu_count()}
 
 
 def copy_reference(gib: float = 8.0, reps: int = 5) -> float:
@@ -289,6 +357,14 @@ def bench_codec(n: int, reps: int, warmup: int):
         ("flashopt_reconstruct", "32-bit", 8.0,
          lambda: F.flashopt_reconstruct(param, rho[32], 32, out)),
     ]
+    # context: plain torch streams over the same n-element fp32 buffers -- a
+    # write-only fill and a read + write negation -- to show the memory
+    # system's ceilings for the shapes above (dequantize writes 4 of its 5.06
+    # bytes per element)
+    cases += [
+        ("reference: torch fill_ (write-only)", "fp32", 4.0, lambda: out.fill_(0.5)),
+        ("reference: torch neg (read + write)", "fp32", 8.0, lambda: torch.neg(x, out=out)),
+    ]
     stream = torch.cuda.current_stream()
     for op, variant, bpe, fn in cases:
         for _ in range(warmup):
@@ -331,10 +407,12 @@ def main():
                     help="with --grad-release: step tensors below this many elements together")
     ap.add_argument("--grad-release", action="store_true",
                     help="one single-tensor launch per tensor (the gradient-release pattern)")
-    ap.add_argument("--cpu-elems", type=int, default=1 << 27,
-                    help="oracle sample size for the CPU baseline (0: skip)")
-    ap.add_argument("--cpu-threads", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip timing the oracle on the host cores")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="host threads for the oracle's all-core timing (0: all)")
+    ap.add_argument("--param-fp32", action="store_true",
+                    help="fp32 parameters and gradients (never split; needs --master-bits 0)")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
                     help="only run one device copy of GIB GiB (for counter scaling) and exit")
     ap.add_argument("--no-copy-ref", action="store_true")
@@ -360,8 +438,11 @@ def main():
         return
 
     mb, comp, qs = args.master_bits, not args.linear, not args.fp32_states
+    if args.param_fp32 and (mb != 0 or args.optimizer != "adamw"):
+        print("--param-fp32 needs --master-bits 0 and the AdamW step", file=sys.stderr)
+        sys.exit(2)
     copy_gbs = None if args.no_copy_ref else copy_reference()
-    opt, grads = build_workload(mb, comp, qs, args.workload, args.optimizer)
+    opt, grads = build_workload(mb, comp, qs, args.workload, args.optimizer, args.param_fp32)
     n = sum(s.param.numel() for s in opt.states)
     n_tensors = len(opt.states)
     print(f"# workload ready: {len(opt.states)} tensors, {n} params, "
@@ -371,7 +452,7 @@ def main():
     env = environment()                     # clocks read right after the timed steps
     ms_step = wall * 1e3 / args.steps
     ms_launch = float(np.mean(per))
-    bpp = bytes_per_param(mb, qs, 1 if args.optimizer == "sgd" else 2)
+    bpp = bytes_per_param(mb, qs, 1 if args.optimizer == "sgd" else 2, 4 if args.param_fp32 else 2)
     alg_bytes = bpp * n
     achieved = alg_bytes / (ms_launch * 1e-3) / 1e9
     print(f"# per-launch ms: mean {ms_launch:.3f} median {np.median(per):.3f} "
@@ -381,12 +462,13 @@ def main():
     torch.cuda.empty_cache()
 
     cpu = None
-    if args.cpu_elems > 0 and args.optimizer == "adamw":
-        cpu = cpu_baseline(mb, args.cpu_elems, args.cpu_threads, args.cpu_seconds, comp, qs)
-    default = (args.workload, mb, comp, qs, args.optimizer, args.grad_release) == \
-        ("decoder-8b-list", 24, True, True, "adamw", False)
+    if not args.no_cpu_baseline and args.optimizer == "adamw":
+        cpu = cpu_baseline(mb, comp, qs, args.cpu_threads, param_fp32=args.param_fp32)
+    default = (args.workload, mb, comp, qs, args.optimizer, args.grad_release, args.param_fp32) == \
+        ("decoder-8b-list", 24, True, True, "adamw", False, False)
     name = args.workload + ("" if comp else "-linear") + ("" if qs else "-fp32-states") + \
-        ("-no-split" if mb == 0 else "") + ("-flashsgd" if args.optimizer == "sgd" else "") + \
+        ("-fp32-params" if args.param_fp32 else ("-no-split" if mb == 0 else "")) + \
+        ("-flashsgd" if args.optimizer == "sgd" else "") + \
         ("-per-tensor-launches" if args.grad_release else "") + \
         (f"-batched-below-{args.batch_below}" if args.grad_release and args.batch_below else "")
 
@@ -412,13 +494,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "params": n, "tensors": n_tensors,
                    "master_bits": mb, "companded": comp, "quantized_states": qs,
+                   "param_dtype": "fp32" if args.param_fp32 else "bf16",
                    "bytes_per_param": bpp,
                    "launches_per_step": launches},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": traffic_per_launch() if default else None,
                      "copy_ref_gbs": copy_gbs},
-        "valu_roofline": valu_roofline(ms_launch) if default else None,
+        "valu_roofline": valu_roofline(ms_launch, _mhz(env.get("clocks", {}).get("sclk")))
+                         if default else None,
         "cpu_baseline": cpu,
         "env": env,
     }

@@ -287,6 +287,20 @@ class _Stepper:
         self.ts = [0] * len(self.states)
         self._key = None
         self._desc = None
+        self._workspaces = {}
+
+    def workspace(self, stream=None) -> torch.Tensor:
+        """The device workspace of list launches on `stream` (the current
+        stream if None): one per stream, so that a launch on one stream never
+        rewrites the chunk table that a kernel still running on another
+        stream reads (a launch only reuses its own stream's workspace, after
+        that stream's earlier work)."""
+        key = _stream(stream)
+        ws = self._workspaces.get(key)
+        if ws is None:
+            ws = torch.empty(self._workspace_bytes, dtype=torch.uint8, device=self.device or "cuda")
+            self._workspaces[key] = ws
+        return ws
 
     def step(self, grads, stream=None):
         """One launch over every tensor; grads[i] is the bf16 gradient of
@@ -386,11 +400,10 @@ class FlashAdamW(_Stepper):
                        quantize_states=quantize_states,
                        param_fp32=dtypes == {torch.float32})
         self._init_common()
-        nbytes = max(16, flashopt_adamw_workspace_bytes(len(self.states)))
-        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device or "cuda")
+        self._workspace_bytes = max(16, flashopt_adamw_workspace_bytes(len(self.states)))
 
     def _list_step(self, desc, t, stream):
-        flashopt_adamw_step(desc, make_args(t, **self.hp), self.workspace, stream)
+        flashopt_adamw_step(desc, make_args(t, **self.hp), self.workspace(stream), stream)
 
     def _tensor_step(self, desc, t, stream):
         flashopt_adamw_step_tensor(desc, make_args(t, **self.hp), stream)
@@ -436,11 +449,10 @@ class FlashSGD(_Stepper):
                        nesterov=nesterov, master_bits=master_bits, companded=companded,
                        quantize_states=quantize_states)
         self._init_common()
-        nbytes = max(16, flashopt_sgd_workspace_bytes(len(self.states)))
-        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device or "cuda")
+        self._workspace_bytes = max(16, flashopt_sgd_workspace_bytes(len(self.states)))
 
     def _list_step(self, desc, t, stream):
-        flashopt_sgd_step(desc, make_sgd_args(t, **self.hp), self.workspace, stream)
+        flashopt_sgd_step(desc, make_sgd_args(t, **self.hp), self.workspace(stream), stream)
 
     def _tensor_step(self, desc, t, stream):
         flashopt_sgd_step_tensor(desc, make_sgd_args(t, **self.hp), stream)

@@ -142,3 +142,33 @@ def _sgd_bits(opt):
     for s in opt.states:
         out += [u16(s.param), s.rho.cpu().numpy(), s.m_codes.cpu().numpy(), u16(s.m_scales)]
     return out
+
+
+def test_list_launches_on_two_streams_use_their_own_workspaces():
+    """One optimizer steps two disjoint halves of its tensors as list launches
+    on two streams, alternating, with no synchronization between them: each
+    stream's launches keep their own chunk table, so the results equal the
+    same subset steps issued on one stream."""
+    require_gpu()
+    sizes = [1 << 18, 70001, 4096 + 5, 1 << 17, 3000, (1 << 18) + 77]
+    half_a, half_b = [0, 2, 4], [1, 3, 5]
+    mk = lambda: F.FlashAdamW([W.init_param(n, device="cuda", seed=600 + i)
+                               for i, n in enumerate(sizes)], **W.HP_DEFAULT)
+    two, one = mk(), mk()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    keep = []                                # no gradient memory is reused while a stream reads it
+    for t in range(1, 5):
+        grads = [W.make_grad(n, t, device="cuda", stream_id=i) for i, n in enumerate(sizes)]
+        keep.append(grads)
+        torch.cuda.synchronize()             # the gradients exist before either stream reads them
+        two.step_tensors(half_a, [grads[i] for i in half_a], stream=sa)
+        two.step_tensors(half_b, [grads[i] for i in half_b], stream=sb)
+        one.step_tensors(half_a, [grads[i] for i in half_a])
+        one.step_tensors(half_b, [grads[i] for i in half_b])
+    torch.cuda.synchronize()
+    assert len(two._workspaces) == 2
+    for i, (x, y) in enumerate(zip(two.states, one.states)):
+        for name in ("param", "rho", "m_codes", "m_scales", "v_codes", "v_scales"):
+            a, b = getattr(x, name), getattr(y, name)
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"tensor {i} {name}"
