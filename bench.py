@@ -180,20 +180,29 @@ def _mhz(text):
 
 
 def time_steps(opt, grads, steps: int, warmup: int, per_tensor: bool = False,
-               batch_below: int = 0):
+               batch_below: int = 0, n_streams: int = 1):
     """per_tensor: the gradient-release launch pattern, one single-tensor
     launch per tensor (the step is then the whole sequence of launches);
     tensors with fewer than batch_below elements are instead stepped together
-    in one list launch after the others (attach_grad_release's batching)."""
+    in one list launch after the others (attach_grad_release's batching).
+    n_streams > 1: the single-tensor launches go round-robin to that many
+    side streams, which start after and are joined back into the timed
+    stream (attach_grad_release's streams)."""
     small = [i for i, g in enumerate(grads) if g.numel() < batch_below]
     large = [i for i, g in enumerate(grads) if g.numel() >= batch_below]
+    side = [torch.cuda.Stream() for _ in range(n_streams)] if per_tensor and n_streams > 1 else []
 
     def one_step(stream=None):
         if per_tensor:
-            for i in large:
-                opt.step_tensor(i, grads[i], stream)
+            cur = stream or torch.cuda.current_stream()
+            for s in side:
+                s.wait_stream(cur)
+            for k, i in enumerate(large):
+                opt.step_tensor(i, grads[i], side[k % len(side)] if side else stream)
             if small:
                 opt.step_tensors(small, [grads[i] for i in small], stream)
+            for s in side:
+                cur.wait_stream(s)
         else:
             opt.step(grads, stream)
 
@@ -407,6 +416,8 @@ def main():
                     help="with --grad-release: step tensors below this many elements together")
     ap.add_argument("--grad-release", action="store_true",
                     help="one single-tensor launch per tensor (the gradient-release pattern)")
+    ap.add_argument("--release-streams", type=int, default=1,
+                    help="with --grad-release: spread the launches over this many streams")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the oracle on the host cores")
     ap.add_argument("--cpu-threads", type=int, default=0,
@@ -448,7 +459,8 @@ def main():
     print(f"# workload ready: {len(opt.states)} tensors, {n} params, "
           f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated", file=sys.stderr, flush=True)
 
-    wall, per = time_steps(opt, grads, args.steps, args.warmup, args.grad_release, args.batch_below)
+    wall, per = time_steps(opt, grads, args.steps, args.warmup, args.grad_release, args.batch_below,
+                           args.release_streams)
     env = environment()                     # clocks read right after the timed steps
     ms_step = wall * 1e3 / args.steps
     ms_launch = float(np.mean(per))
@@ -470,7 +482,8 @@ def main():
         ("-fp32-params" if args.param_fp32 else ("-no-split" if mb == 0 else "")) + \
         ("-flashsgd" if args.optimizer == "sgd" else "") + \
         ("-per-tensor-launches" if args.grad_release else "") + \
-        (f"-batched-below-{args.batch_below}" if args.grad_release and args.batch_below else "")
+        (f"-batched-below-{args.batch_below}" if args.grad_release and args.batch_below else "") + \
+        (f"-{args.release_streams}-streams" if args.grad_release and args.release_streams > 1 else "")
 
     launches = 1
     if args.grad_release:

@@ -351,7 +351,7 @@ class _Stepper:
             raise ValueError(f"stream is on {dev}, the parameters on {self.device}")
 
 
-def attach_grad_release(opt, params, batch_below: int = 0):
+def attach_grad_release(opt, params, batch_below: int = 0, streams: int = 1):
     """Gradient release: register a post-accumulate-grad hook on every
     parameter that runs that tensor's step as soon as its gradient is
     complete and then frees the gradient, so a full set of gradients is never
@@ -361,22 +361,46 @@ def attach_grad_release(opt, params, batch_below: int = 0):
     own; its (small) gradient is kept until the backward pass ends and all
     such parameters are stepped together in one list launch, which saves a
     kernel launch per small tensor (norm vectors, biases).  The results are
-    the same bits.  Returns the hook handles."""
+    the same bits.
+
+    streams > 1: the single-tensor launches go round-robin to that many side
+    streams, each first waiting for the backward stream's work up to the
+    hook, so that the launches of tensors too small to fill the GPU overlap
+    instead of running one at a time (tensors are independent).  Each
+    gradient's memory is kept until its side stream has used it
+    (record_stream), and when the backward pass ends the backward stream
+    waits for every side stream, so later work sees the updated parameters.
+    Returns the hook handles."""
     index = {id(p): i for i, p in enumerate(params)}
     pending = []
+    side = [torch.cuda.Stream(device=opt.device) for _ in range(streams)] if streams > 1 else []
+    turn = [0]
+    queued = [False]
 
-    def flush():
+    def end_of_backward():
+        queued[0] = False
         if pending:
             idx, grads = zip(*pending)
             pending.clear()
             opt.step_tensors(idx, grads)
+        if side:
+            cur = torch.cuda.current_stream(opt.device)
+            for s in side:
+                cur.wait_stream(s)
 
     def hook(p):
+        if not queued[0]:              # run once when this backward pass ends
+            torch.autograd.Variable._execution_engine.queue_callback(end_of_backward)
+            queued[0] = True
         i = index[id(p)]
         if p.numel() < batch_below:
-            if not pending:        # run once when this backward pass ends
-                torch.autograd.Variable._execution_engine.queue_callback(flush)
             pending.append((i, p.grad))
+        elif side:
+            s = side[turn[0] % len(side)]
+            turn[0] += 1
+            s.wait_stream(torch.cuda.current_stream(opt.device))
+            opt.step_tensor(i, p.grad, stream=s)
+            p.grad.record_stream(s)
         else:
             opt.step_tensor(i, p.grad)
         p.grad = None

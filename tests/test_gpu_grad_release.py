@@ -228,6 +228,44 @@ def test_step_tensors_equals_single_tensor_steps(kind):
             _assert_same(sa, sb, f"{kind} t{t} tensor{i}")
 
 
+@pytest.mark.parametrize("kind,streams,batch", [("adamw", 3, 0), ("sgd", 2, 2048), ("adamw", 4, 2048)])
+def test_hooks_on_side_streams_match_list_step(kind, streams, batch):
+    """attach_grad_release with the single-tensor launches spread over side
+    streams (and the small tensors batched, for two of the cases): every
+    gradient is freed, the states equal a list step's, and work issued after
+    the backward pass on its stream sees the updated parameters."""
+    require_gpu()
+    model = _mlp(7)
+    params = list(model.parameters())
+    init = [p.detach().clone() for p in params]
+    opt = _make(kind, params, 24, True)
+    seen = {}
+
+    def record(p):
+        seen.setdefault(id(p), []).append(p.grad.detach().clone())
+
+    rec = [p.register_post_accumulate_grad_hook(record) for p in params]
+    handles = F.attach_grad_release(opt, params, batch_below=batch, streams=streams)
+    ref = _make(kind, [q.clone() for q in init], 24, True)
+    gen = torch.Generator(device="cuda").manual_seed(19)
+    for step in range(3):
+        x = torch.randn(32, 192, device="cuda", generator=gen).to(torch.bfloat16)
+        model(x).float().square().mean().backward()
+        # no host synchronization: the copies below are ordered after the
+        # side streams' updates by the end-of-backward join alone
+        after = [p.detach().clone() for p in params]
+        torch.cuda.synchronize()
+        assert all(p.grad is None for p in params), "gradients must be freed"
+        ref.step([seen[id(p)][step] for p in params])
+        torch.cuda.synchronize()
+        for i, (sa, sb) in enumerate(zip(opt.states, ref.states)):
+            _assert_same(sa, sb, f"{kind} streams {streams} step {step} tensor {i}")
+            assert torch.equal(after[i].view(torch.int16), sb.param.view(torch.int16)), \
+                f"{kind} streams {streams} step {step} tensor {i}: copy after backward"
+    for h in handles + rec:
+        h.remove()
+
+
 @pytest.mark.parametrize("kind", ["adamw", "sgd"])
 def test_batched_small_tensors_match_list_step(kind):
     """attach_grad_release with batch_below: the biases (64 to 1017
