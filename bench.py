@@ -422,6 +422,9 @@ def main():
                     help="skip timing the oracle on the host cores")
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="host threads for the oracle's all-core timing (0: all)")
+    ap.add_argument("--first-step", type=int, default=1,
+                    help="step count of the first (warm-up) step; from about 17321 on, with the "
+                         "default betas, both bias corrections are 1 in fp32")
     ap.add_argument("--param-fp32", action="store_true",
                     help="fp32 parameters and gradients (never split; needs --master-bits 0)")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
@@ -454,6 +457,8 @@ def main():
         sys.exit(2)
     copy_gbs = None if args.no_copy_ref else copy_reference()
     opt, grads = build_workload(mb, comp, qs, args.workload, args.optimizer, args.param_fp32)
+    opt.t = args.first_step - 1
+    opt.ts = [opt.t] * len(opt.states)
     n = sum(s.param.numel() for s in opt.states)
     n_tensors = len(opt.states)
     print(f"# workload ready: {len(opt.states)} tensors, {n} params, "
@@ -476,14 +481,15 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and args.optimizer == "adamw":
         cpu = cpu_baseline(mb, comp, qs, args.cpu_threads, param_fp32=args.param_fp32)
-    default = (args.workload, mb, comp, qs, args.optimizer, args.grad_release, args.param_fp32) == \
-        ("decoder-8b-list", 24, True, True, "adamw", False, False)
+    default = (args.workload, mb, comp, qs, args.optimizer, args.grad_release, args.param_fp32,
+               args.first_step) == ("decoder-8b-list", 24, True, True, "adamw", False, False, 1)
     name = args.workload + ("" if comp else "-linear") + ("" if qs else "-fp32-states") + \
         ("-fp32-params" if args.param_fp32 else ("-no-split" if mb == 0 else "")) + \
         ("-flashsgd" if args.optimizer == "sgd" else "") + \
         ("-per-tensor-launches" if args.grad_release else "") + \
         (f"-batched-below-{args.batch_below}" if args.grad_release and args.batch_below else "") + \
-        (f"-{args.release_streams}-streams" if args.grad_release and args.release_streams > 1 else "")
+        (f"-{args.release_streams}-streams" if args.grad_release and args.release_streams > 1 else "") + \
+        (f"-from-step-{args.first_step}" if args.first_step != 1 else "")
 
     launches = 1
     if args.grad_release:
@@ -508,6 +514,7 @@ def main():
         "config": {"workload": name, "params": n, "tensors": n_tensors,
                    "master_bits": mb, "companded": comp, "quantized_states": qs,
                    "param_dtype": "fp32" if args.param_fp32 else "bf16",
+                   "first_step": args.first_step,
                    "bytes_per_param": bpp,
                    "launches_per_step": launches},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,

@@ -65,6 +65,7 @@ struct StepScalars {
     uint32_t v1_bound;  // v1 bit patterns below this keep vhat below 2^63
     uint32_t num_key;   // (pattern << 1) - 1 of the smallest nonzero |lr mhat 2^32| allowed
     int fast;           // 1 when eps lets the short route absorb vhat = 0 and subnormal vhat (eps >= 2^-38)
+    int unit_bc;        // 1 when bc1 and bc2 are both exactly 1 (late in training)
 };
 // fp32 scalars of one FlashSGD step (SGD with momentum), formed in double
 // on the host and rounded once.

@@ -1113,15 +1113,30 @@ __device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
     // unscaled product lr mhat is normal, so scaling it was exact)
     uint32_t kmin = 0xFFFFFFFFu;          // min over nonzero |num| of its doubled pattern - 1
     float th1[N], sq[N];
+    if (sc.unit_bc) {
+        // late in training both bias corrections round to 1 in fp32, and
+        // dividing by 1 is exact: mhat = m1, vhat = v1 (the short sqrt takes
+        // v1 itself, subnormal values included)
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
-        const float mhat = math::div_by_f64_recip(m1[j], sc.inv_bc1);
-        sq[j] = math::sqrt_quot_x2p32(v1[j], sc.inv_bc2s);
-        const float den = sq[j] + sc.eps2;
-        const float num = sc.lr2 * mhat;
-        th1[j] = thd[j] - math::div_markstein(num, den, math::recip_cr(den));
-        const uint32_t key = (__float_as_uint(num) << 1) - 1u;
-        kmin = key < kmin ? key : kmin;
+        for (int j = 0; j < N; ++j) {
+            sq[j] = math::sqrt_x2p32_zero_tiny(v1[j]);
+            const float den = sq[j] + sc.eps2;
+            const float num = sc.lr2 * m1[j];
+            th1[j] = thd[j] - math::div_markstein(num, den, math::recip_cr(den));
+            const uint32_t key = (__float_as_uint(num) << 1) - 1u;
+            kmin = key < kmin ? key : kmin;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const float mhat = math::div_by_f64_recip(m1[j], sc.inv_bc1);
+            sq[j] = math::sqrt_quot_x2p32(v1[j], sc.inv_bc2s);
+            const float den = sq[j] + sc.eps2;
+            const float num = sc.lr2 * mhat;
+            th1[j] = thd[j] - math::div_markstein(num, den, math::recip_cr(den));
+            const uint32_t key = (__float_as_uint(num) << 1) - 1u;
+            kmin = key < kmin ? key : kmin;
+        }
     }
     // NaN-propagating maximum (v_maximum3_f32): NaN iff some th1 is NaN
     float tnan = th1[0];

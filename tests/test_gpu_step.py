@@ -158,14 +158,16 @@ def test_ragged_list(orc, mb, comp, qs):
 
 
 # Hyper-parameter settings away from the default: (name, overrides, first
-# step).  beta 0 (no averaging), a large k2 = 1/sqrt(1 - 0.9999) = 100, bias
-# corrections at 1 (step 10^6), learning rates 0 and 1e-6 to 1, no weight
-# decay, a large eps.
+# step).  beta 0 (no averaging), beta2 0.9999 (a small bias correction),
+# bias corrections at 1 (step 10^6; and steps 17320-17322, where the second
+# one reaches 1 and the step switches to its late-training route), learning
+# rates 0 and 1e-6 to 1, no weight decay, a large eps.
 HP_GRID = [
     ("betas_zero", dict(betas=(0.0, 0.0)), 1),
     ("beta2_0.9999", dict(betas=(0.5, 0.9999)), 1),
     ("step_1e6", dict(betas=(0.95, 0.99)), 1_000_000),
     ("step_100", dict(), 100),
+    ("step_17320", dict(), 17320),     # 1 - 0.999^t reaches 1 in fp32 at t = 17321
     ("lr_1_wd_0.1", dict(lr=1.0, weight_decay=0.1), 1),
     ("lr_1e-6_wd_0", dict(lr=1e-6, weight_decay=0.0), 5),
     ("eps_1e-3", dict(eps=1e-3), 2),
