@@ -224,14 +224,23 @@ def time_steps(opt, grads, steps: int, warmup: int, per_tensor: bool = False,
 
 
 def cpu_model() -> str:
+    """The host CPU's model name with its family/model/stepping numbers (a
+    virtual machine may report only the vendor's product line by name)."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" not in line:
+                    if fields:
+                        break                   # the first processor's block is enough
+                    continue
+                k, v = (x.strip() for x in line.split(":", 1))
+                fields.setdefault(k, v)
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = fields.get("model name", "unknown")
+    ids = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields]
+    return f"{name} ({', '.join(ids)})" if ids else name
 
 
 def _host_list(shapes, frac: int, master_bits, quantize_states, param_fp32=False):
