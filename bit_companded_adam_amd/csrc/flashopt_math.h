@@ -186,9 +186,9 @@ __device__ __forceinline__ float sqrt_cr_x2p32(float x)
 // fma(x, 2^64, 2^-126).  For every x > 0 the added 2^-126 vanishes (x 2^64 >=
 // 2^-85, whose half ulp is 2^-109), so the result is sqrt_cr_x2p32(x); at
 // x = 0 it keeps rsq finite and the result is 2^-63 instead of 0.  A caller
-// has to absorb that value: in the step it adds at most k2 2^-95 to
-// eps, which leaves eps unchanged while k2 <= eps 2^70, and its variance
-// code and group scale round to 0 as for 0.
+// has to absorb that value: the step adds it to eps 2^32 >= 2^-6 (the short
+// route needs eps >= 2^-38), whose half ulp is at least 2^-30, so the sum is
+// eps 2^32 itself; its variance code and group scale round to 0 as for 0.
 __device__ __forceinline__ float sqrt_x2p32_zero_tiny(float x)
 {
     const float xs = __builtin_fmaf(x, 0x1p64f, 0x1p-126f);

@@ -320,7 +320,8 @@ def _edge_grad(case: str, n: int, t: int) -> torch.Tensor:
         g[(lane % 3 == 0) & (idx % 16 == 5)] *= 1e-27     # one tiny numerator in a lane
         g[lane % 7 == 1] *= 1e-30                         # whole lanes of tiny numerators
     elif case == "large_m_small_eps":
-        g[lane % 5 == 2] *= 1e6                           # alpha |m| above eps 2^100
+        g[lane % 5 == 2] *= 1e6                           # large |m|; eps 1e-30 is below the
+                                                          # short routes' range: all lanes generic
     elif case == "eps_zero":
         g[lane % 4 == 3] = 0.0                            # 0 / 0 without eps
     elif case == "nonfinite":
