@@ -44,12 +44,29 @@ flashopt_status check_split(const void *master, int64_t n, int master_bits, cons
     return FLASHOPT_OK;
 }
 
-// Workspace layout: [n DevTensor][n + 1 int32 chunk starts], 16-byte rounded.
-size_t workspace_bytes(int n)
+// Table layout: [n DevTensor][n + 1 int32 chunk starts], 16-byte rounded.
+size_t table_bytes(int n)
 {
     if (n <= 0) return 0;
     size_t b = sizeof(DevTensor) * static_cast<size_t>(n) + sizeof(int32_t) * (static_cast<size_t>(n) + 1);
     return (b + 15) & ~static_cast<size_t>(15);
+}
+
+// Staged bytes of a list step: a header, then the table.  The AdamW steps
+// stage their scalar block (kScalarsBytes) as the header, FlashSGD passes
+// its scalars by value and stages none.
+size_t staged_bytes(int n, size_t header_bytes)
+{
+    return n <= 0 ? 0 : header_bytes + table_bytes(n);
+}
+
+constexpr size_t kAdamwHeader = flashopt::kScalarsBytes;
+
+// The scalar block of an AdamW step: the StepScalars, zero padded.
+void fill_scalars(const StepScalars &sc, void *dst)
+{
+    std::memset(dst, 0, kAdamwHeader);
+    std::memcpy(dst, &sc, sizeof(sc));
 }
 
 // Pinned host staging for the chunk table: a small ring per device, so the
@@ -237,22 +254,12 @@ int32_t fill_table(const flashopt_tensor *tensors, int n_tensors, void *table)
     return acc;
 }
 
-// Validation of a step's tensor list, then the chunk table staged through the
-// pinned ring and launch(d_desc, d_chunk_start, total_chunks, stream).
-template <typename Launch>
-flashopt_status stage_and_launch(const flashopt_tensor *tensors, int n_tensors, int master_bits,
-                                 bool quant, bool v, void *workspace, size_t ws_bytes,
-                                 void *stream, Launch &&launch)
+// Copies `bytes` of host data, which fill(host) writes into a pinned ring
+// slot, to device memory `dst` on stream st (the slot is reused once that
+// copy has completed).  Returns what fill returned through `out`.
+template <typename Fill>
+flashopt_status stage_copy(void *dst, size_t bytes, hipStream_t st, Fill &&fill)
 {
-    int64_t total = 0;
-    const flashopt_status cs = check_list(tensors, n_tensors, master_bits, quant, v, total);
-    if (cs != FLASHOPT_OK) return cs;
-    if (total == 0) return FLASHOPT_OK;
-    const size_t need = workspace_bytes(n_tensors);
-    if (!workspace || ws_bytes < need) return FLASHOPT_EWORKSPACE;
-    if (!aligned(workspace, 16)) return FLASHOPT_EALIGN;
-
-    hipStream_t st = static_cast<hipStream_t>(stream);
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FLASHOPT_EHIP;
 
@@ -266,28 +273,70 @@ flashopt_status stage_and_launch(const flashopt_tensor *tensors, int n_tensors, 
     }
     if (!slot.done && hipEventCreateWithFlags(&slot.done, hipEventDisableTiming) != hipSuccess)
         return FLASHOPT_EHIP;
-    if (slot.cap < need) {
+    if (slot.cap < bytes) {
         if (slot.host) (void)hipHostFree(slot.host);
         slot.host = nullptr;
         slot.cap = 0;
-        if (hipHostMalloc(&slot.host, need, hipHostMallocDefault) != hipSuccess) return FLASHOPT_EHIP;
-        slot.cap = need;
+        if (hipHostMalloc(&slot.host, bytes, hipHostMallocDefault) != hipSuccess) return FLASHOPT_EHIP;
+        slot.cap = bytes;
     }
-
-    const int32_t acc = fill_table(tensors, n_tensors, slot.host);
-    if (hipMemcpyAsync(workspace, slot.host, need, hipMemcpyHostToDevice, st) != hipSuccess)
+    fill(slot.host);
+    if (hipMemcpyAsync(dst, slot.host, bytes, hipMemcpyHostToDevice, st) != hipSuccess)
         return FLASHOPT_EHIP;
     if (hipEventRecord(slot.done, st) != hipSuccess) return FLASHOPT_EHIP;
     slot.pending = true;
-
-    const DevTensor *d_desc = static_cast<const DevTensor *>(workspace);
-    const int32_t *d_start = reinterpret_cast<const int32_t *>(d_desc + n_tensors);
-    return hip_status(launch(d_desc, d_start, acc, st));
+    return FLASHOPT_OK;
 }
 
-// Host image of the allocation-free step's chunk table: built under the
-// mutex and copied (pageable hipMemcpyAsync, which has consumed the buffer
-// when it returns) into the device scratch array.
+// Validation of a step's tensor list, then the header (header_bytes of
+// `header`, none for 0) and the chunk table staged through the pinned ring
+// into the workspace, and launch(d_header, d_desc, d_chunk_start,
+// total_chunks, stream).
+template <typename Launch>
+flashopt_status stage_and_launch(const flashopt_tensor *tensors, int n_tensors, int master_bits,
+                                 bool quant, bool v, const void *header, size_t header_bytes,
+                                 void *workspace, size_t ws_bytes, void *stream, Launch &&launch)
+{
+    int64_t total = 0;
+    const flashopt_status cs = check_list(tensors, n_tensors, master_bits, quant, v, total);
+    if (cs != FLASHOPT_OK) return cs;
+    if (total == 0) return FLASHOPT_OK;
+    const size_t need = staged_bytes(n_tensors, header_bytes);
+    if (!workspace || ws_bytes < need) return FLASHOPT_EWORKSPACE;
+    if (!aligned(workspace, 16)) return FLASHOPT_EALIGN;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t acc = 0;
+    const flashopt_status ss = stage_copy(workspace, need, st, [&](void *host) {
+        if (header_bytes) std::memcpy(host, header, header_bytes);
+        acc = fill_table(tensors, n_tensors, static_cast<unsigned char *>(host) + header_bytes);
+    });
+    if (ss != FLASHOPT_OK) return ss;
+
+    const unsigned char *base = static_cast<const unsigned char *>(workspace);
+    const DevTensor *d_desc = reinterpret_cast<const DevTensor *>(base + header_bytes);
+    const int32_t *d_start = reinterpret_cast<const int32_t *>(d_desc + n_tensors);
+    return hip_status(launch(base, d_desc, d_start, acc, st));
+}
+
+// The plan's variant fields, from step arguments.
+void plan_variant(const flashopt_adamw_args &a, flashopt_adamw_plan_info &info)
+{
+    info.master_bits = a.master_bits;
+    info.companded = a.companded;
+    info.fp32_states = a.fp32_states;
+    info.param_fp32 = a.param_fp32;
+}
+
+bool same_variant(const flashopt_adamw_args &a, const flashopt_adamw_plan_info &info)
+{
+    return info.master_bits == a.master_bits && info.companded == a.companded &&
+           info.fp32_states == a.fp32_states && info.param_fp32 == a.param_fp32;
+}
+
+// Host image of the allocation-free step's scalar block and chunk table:
+// built under the mutex and copied (pageable hipMemcpyAsync, which has
+// consumed the buffer when it returns) into the device scratch array.
 std::mutex g_noalloc_mutex;
 alignas(64) unsigned char g_noalloc_table[flashopt::kScratchBytes];
 
@@ -348,7 +397,7 @@ flashopt_status flashopt_reconstruct(const uint16_t *param_bf16, const void *rho
 size_t flashopt_adamw_workspace_bytes(const flashopt_tensor *tensors, int n_tensors)
 {
     (void)tensors;
-    return workspace_bytes(n_tensors);
+    return staged_bytes(n_tensors, kAdamwHeader);
 }
 
 flashopt_status flashopt_adamw_step(const flashopt_tensor *tensors, int n_tensors,
@@ -360,11 +409,15 @@ flashopt_status flashopt_adamw_step(const flashopt_tensor *tensors, int n_tensor
     const flashopt_status hs = adamw_scalars(a, sc);
     if (hs != FLASHOPT_OK) return hs;
     const int states = states_of(a->fp32_states, a->companded);
+    alignas(16) unsigned char header[kAdamwHeader];
+    fill_scalars(sc, header);
     return stage_and_launch(tensors, n_tensors, a->master_bits, a->fp32_states == 0, true,
-                            workspace, ws_bytes, stream,
-                            [&](const DevTensor *d, const int32_t *cs, int32_t total, hipStream_t st) {
-                                return flashopt::launch_adamw_step(d, cs, n_tensors, total, sc,
-                                                                   kernel_format(*a), states, st);
+                            header, kAdamwHeader, workspace, ws_bytes, stream,
+                            [&](const unsigned char *h, const DevTensor *d, const int32_t *cs,
+                                int32_t total, hipStream_t st) {
+                                return flashopt::launch_adamw_step(
+                                    reinterpret_cast<const StepScalars *>(h), d, cs, n_tensors,
+                                    total, kernel_format(*a), states, st);
                             });
 }
 
@@ -400,22 +453,100 @@ flashopt_status flashopt_adamw_step_noalloc(const flashopt_tensor *tensors, int 
     int32_t acc = 0;
     {
         std::lock_guard<std::mutex> lock(g_noalloc_mutex);
-        acc = fill_table(tensors, n_tensors, g_noalloc_table);
-        if (hipMemcpyAsync(scratch, g_noalloc_table, workspace_bytes(n_tensors),
+        fill_scalars(sc, g_noalloc_table);
+        acc = fill_table(tensors, n_tensors, g_noalloc_table + kAdamwHeader);
+        if (hipMemcpyAsync(scratch, g_noalloc_table, staged_bytes(n_tensors, kAdamwHeader),
                            hipMemcpyHostToDevice, st) != hipSuccess)
             return FLASHOPT_EHIP;
     }
-    const DevTensor *d_desc = static_cast<const DevTensor *>(scratch);
+    const unsigned char *base = static_cast<const unsigned char *>(scratch);
+    const DevTensor *d_desc = reinterpret_cast<const DevTensor *>(base + kAdamwHeader);
     const int32_t *d_start = reinterpret_cast<const int32_t *>(d_desc + n_tensors);
-    return hip_status(flashopt::launch_adamw_step(d_desc, d_start, n_tensors, acc, sc,
-                                                  kernel_format(*a),
+    return hip_status(flashopt::launch_adamw_step(reinterpret_cast<const StepScalars *>(base), d_desc,
+                                                  d_start, n_tensors, acc, kernel_format(*a),
                                                   states_of(a->fp32_states, a->companded), st));
+}
+
+size_t flashopt_adamw_plan_bytes(int n_tensors)
+{
+    return staged_bytes(n_tensors, kAdamwHeader);
+}
+
+flashopt_status flashopt_adamw_plan(const flashopt_tensor *tensors, int n_tensors,
+                                    const flashopt_adamw_args *a, void *plan, size_t plan_bytes,
+                                    flashopt_adamw_plan_info *info, void *stream)
+{
+    if (!info || n_tensors < 0 || (n_tensors > 0 && !tensors)) return FLASHOPT_EINVAL;
+    StepScalars sc;
+    const flashopt_status hs = adamw_scalars(a, sc);
+    if (hs != FLASHOPT_OK) return hs;
+    int64_t total = 0;
+    const flashopt_status cs = check_list(tensors, n_tensors, a->master_bits, a->fp32_states == 0,
+                                          true, total);
+    if (cs != FLASHOPT_OK) return cs;
+    const size_t need = staged_bytes(n_tensors, kAdamwHeader);
+    if (need > 0 && (!plan || plan_bytes < need)) return FLASHOPT_EWORKSPACE;
+    if (need > 0 && !aligned(plan, 16)) return FLASHOPT_EALIGN;
+    flashopt_adamw_plan_info out{};
+    out.n_tensors = n_tensors;
+    out.total_chunks = static_cast<int32_t>(total);
+    plan_variant(*a, out);
+    if (need > 0) {
+        const flashopt_status ss = stage_copy(plan, need, static_cast<hipStream_t>(stream), [&](void *host) {
+            fill_scalars(sc, host);
+            (void)fill_table(tensors, n_tensors, static_cast<unsigned char *>(host) + kAdamwHeader);
+        });
+        if (ss != FLASHOPT_OK) return ss;
+    }
+    *info = out;
+    return FLASHOPT_OK;
+}
+
+flashopt_status flashopt_adamw_plan_set_step(const flashopt_adamw_plan_info *info,
+                                             const flashopt_adamw_args *a, void *plan, void *stream)
+{
+    if (!info || !a || !same_variant(*a, *info)) return FLASHOPT_EINVAL;
+    StepScalars sc;
+    const flashopt_status hs = adamw_scalars(a, sc);
+    if (hs != FLASHOPT_OK) return hs;
+    if (info->n_tensors <= 0) return info->n_tensors == 0 ? FLASHOPT_OK : FLASHOPT_EINVAL;
+    if (!plan) return FLASHOPT_EWORKSPACE;
+    if (!aligned(plan, 16)) return FLASHOPT_EALIGN;
+    return stage_copy(plan, kAdamwHeader, static_cast<hipStream_t>(stream),
+                      [&](void *host) { fill_scalars(sc, host); });
+}
+
+flashopt_status flashopt_adamw_plan_launch(const flashopt_adamw_plan_info *info, const void *plan,
+                                           void *stream)
+{
+    if (!info || info->n_tensors < 0 || info->total_chunks < 0) return FLASHOPT_EINVAL;
+    flashopt_adamw_args a{};
+    a.master_bits = info->master_bits;
+    a.companded = info->companded;
+    a.fp32_states = info->fp32_states;
+    a.param_fp32 = info->param_fp32;
+    if ((a.master_bits != 24 && a.master_bits != 32 && a.master_bits != 0) ||
+        (a.companded != 0 && a.companded != 1) || (a.fp32_states != 0 && a.fp32_states != 1) ||
+        (a.param_fp32 != 0 && a.param_fp32 != 1) || (a.param_fp32 && a.master_bits != 0))
+        return FLASHOPT_EINVAL;
+    if (info->total_chunks == 0) return FLASHOPT_OK;
+    if (info->n_tensors == 0) return FLASHOPT_EINVAL;
+    if (!plan) return FLASHOPT_EWORKSPACE;
+    if (!aligned(plan, 16)) return FLASHOPT_EALIGN;
+    const unsigned char *base = static_cast<const unsigned char *>(plan);
+    const DevTensor *d_desc = reinterpret_cast<const DevTensor *>(base + kAdamwHeader);
+    const int32_t *d_start = reinterpret_cast<const int32_t *>(d_desc + info->n_tensors);
+    return hip_status(flashopt::launch_adamw_step(reinterpret_cast<const StepScalars *>(base), d_desc,
+                                                  d_start, info->n_tensors, info->total_chunks,
+                                                  kernel_format(a),
+                                                  states_of(a.fp32_states, a.companded),
+                                                  static_cast<hipStream_t>(stream)));
 }
 
 size_t flashopt_sgd_workspace_bytes(const flashopt_tensor *tensors, int n_tensors)
 {
     (void)tensors;
-    return workspace_bytes(n_tensors);
+    return staged_bytes(n_tensors, 0);
 }
 
 flashopt_status flashopt_sgd_step(const flashopt_tensor *tensors, int n_tensors,
@@ -428,8 +559,9 @@ flashopt_status flashopt_sgd_step(const flashopt_tensor *tensors, int n_tensors,
     if (hs != FLASHOPT_OK) return hs;
     const int states = states_of(a->fp32_states, a->companded);
     return stage_and_launch(tensors, n_tensors, a->master_bits, a->fp32_states == 0, false,
-                            workspace, ws_bytes, stream,
-                            [&](const DevTensor *d, const int32_t *cs, int32_t total, hipStream_t st) {
+                            nullptr, 0, workspace, ws_bytes, stream,
+                            [&](const unsigned char *, const DevTensor *d, const int32_t *cs,
+                                int32_t total, hipStream_t st) {
                                 return flashopt::launch_sgd_step(d, cs, n_tensors, total, sc,
                                                                  a->master_bits, states, st);
                             });

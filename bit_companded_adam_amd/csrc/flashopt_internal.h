@@ -67,6 +67,13 @@ struct StepScalars {
     int fast;           // 1 when eps lets the short route absorb vhat = 0 and subnormal vhat (eps >= 2^-38)
     int unit_bc;        // 1 when bc1 and bc2 are both exactly 1 (late in training)
 };
+// The list AdamW kernels read their StepScalars from device memory: a block
+// of kScalarsBytes at the start of the staged table (the workspace, the
+// allocation-free scratch array or a caller's plan), written by the same
+// host-to-device copy as the table or by a later one, so that a launch can
+// be captured once and replayed with new scalars.
+constexpr size_t kScalarsBytes = 128;
+static_assert(sizeof(StepScalars) <= kScalarsBytes, "scalar block");
 // fp32 scalars of one FlashSGD step (SGD with momentum), formed in double
 // on the host and rounded once.
 struct SgdScalars {
@@ -79,13 +86,14 @@ struct SgdScalars {
     int nesterov;
 };
 
-// Allocation-free list step: its chunk table (kScratchTensors descriptors,
-// then kScratchTensors + 1 chunk starts) lives in a device array of the
-// library, kScratchBytes long.  scratch_address returns that array's address
-// on the current device (looked up once per device).
+// Allocation-free list step: its scalar block and chunk table (up to
+// kScratchTensors descriptors, then their chunk starts) live in a device
+// array of the library, kScratchBytes long.  scratch_address returns that
+// array's address on the current device (looked up once per device).
 constexpr int kScratchTensors = 1024;
 constexpr size_t kScratchBytes =
-    (sizeof(DevTensor) * kScratchTensors + sizeof(int32_t) * (kScratchTensors + 1) + 255) & ~size_t(255);
+    (kScalarsBytes + sizeof(DevTensor) * kScratchTensors + sizeof(int32_t) * (kScratchTensors + 1) + 255) &
+    ~size_t(255);
 hipError_t scratch_address(void **ptr);
 
 hipError_t launch_quantize(const float *x, int64_t n, unsigned spec, void *codes,
@@ -96,13 +104,12 @@ hipError_t launch_split(const float *master, int64_t n, int master_bits,
                         uint16_t *param, void *rho, hipStream_t stream);
 hipError_t launch_reconstruct(const uint16_t *param, const void *rho, int64_t n,
                               int master_bits, float *master, hipStream_t stream);
-// tensors / chunk_start are device pointers into the workspace;
-// chunk_start has n_tensors + 1 entries.  master_bits: 24 | 32 | 0 (no
-// split) | kParamF32 (AdamW only); states: one of kStates*.
-hipError_t launch_adamw_step(const DevTensor *tensors, const int32_t *chunk_start,
-                             int n_tensors, int32_t total_chunks,
-                             const StepScalars &sc, int master_bits, int states,
-                             hipStream_t stream);
+// scalars / tensors / chunk_start are device pointers into the staged
+// table; chunk_start has n_tensors + 1 entries.  master_bits: 24 | 32 | 0
+// (no split) | kParamF32 (AdamW only); states: one of kStates*.
+hipError_t launch_adamw_step(const StepScalars *scalars, const DevTensor *tensors,
+                             const int32_t *chunk_start, int n_tensors, int32_t total_chunks,
+                             int master_bits, int states, hipStream_t stream);
 hipError_t launch_sgd_step(const DevTensor *tensors, const int32_t *chunk_start,
                            int n_tensors, int32_t total_chunks,
                            const SgdScalars &sc, int master_bits, int states,

@@ -1368,12 +1368,17 @@ __device__ __forceinline__ void for_each_chunk(const DevTensor *__restrict__ ten
 
 // The fused FlashAdamW step.  With quantized states the two 256-entry
 // dequantization tables are built per workgroup in LDS from the exact fp32
-// operations of dequantize().
+// operations of dequantize().  The step's scalars are read from the staged
+// table (scalar loads, uniform across the wavefront), not from the kernel
+// arguments, so that a captured launch steps with whatever scalars were
+// written there before it runs.
 template <int MB, int ST>
 __global__ void __launch_bounds__(kBlockThreads)
-adamw_step_kernel(const DevTensor *__restrict__ tensors, const int32_t *__restrict__ chunk_start,
-                  int n_tensors, int32_t total_chunks, int32_t run, StepScalars sc)
+adamw_step_kernel(const StepScalars *__restrict__ scalars, const DevTensor *__restrict__ tensors,
+                  const int32_t *__restrict__ chunk_start, int n_tensors, int32_t total_chunks,
+                  int32_t run)
 {
+    const StepScalars sc = *scalars;
     constexpr unsigned kMSpec =
         ST == kStatesCompanded ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
     constexpr int kN = unit_elems(MB, ST);
@@ -1597,12 +1602,12 @@ unsigned step_grid(int32_t total_chunks, int32_t run)
 
 template <int MB, int ST>
 hipError_t step_variant(const DevTensor *tensors, const int32_t *chunk_start, int n_tensors,
-                        int32_t total_chunks, const StepScalars &sc, hipStream_t st)
+                        int32_t total_chunks, const StepScalars *scalars, hipStream_t st)
 {
     const int32_t run = chunks_per_wave();
     hipLaunchKernelGGL((adamw_step_kernel<MB, ST>), dim3(step_grid(total_chunks, run)),
-                       dim3(kBlockThreads), 0, st, tensors, chunk_start, n_tensors,
-                       total_chunks, run, sc);
+                       dim3(kBlockThreads), 0, st, scalars, tensors, chunk_start, n_tensors,
+                       total_chunks, run);
     return hipGetLastError();
 }
 
@@ -1647,13 +1652,14 @@ hipError_t dispatch(int master_bits, int states, const DevTensor *tensors,
     return hipErrorInvalidValue;
 }
 
+// List launches: the scalars are a device pointer into the staged table.
 template <int MB, int ST>
 struct AdamWLaunch {
     static constexpr bool kFp32Params = true;
     static hipError_t run(const DevTensor *t, const int32_t *cs, int n, int32_t total,
-                          const StepScalars &sc, hipStream_t st)
+                          const StepScalars *scalars, hipStream_t st)
     {
-        return step_variant<MB, ST>(t, cs, n, total, sc, st);
+        return step_variant<MB, ST>(t, cs, n, total, scalars, st);
     }
 };
 
@@ -1698,8 +1704,8 @@ struct SgdTensorLaunch {
 
 // ------------------------------------ scratch of the allocation-free step
 
-// The chunk table of flashopt_adamw_step_noalloc: a device array of this
-// file instead of a caller's workspace.  Every GPU the library runs on holds
+// The scalar block and chunk table of flashopt_adamw_step_noalloc: a device
+// array of this file instead of a caller's workspace.  Every GPU the library runs on holds
 // its own copy until the process ends.  In host code the name stands for a
 // host-side shadow, not a device address, so host code reaches the array only
 // through the address hipGetSymbolAddress returns for the current device.
@@ -1726,13 +1732,13 @@ hipError_t scratch_address(void **ptr)
     return hipSuccess;
 }
 
-hipError_t launch_adamw_step(const DevTensor *tensors, const int32_t *chunk_start, int n_tensors,
-                             int32_t total_chunks, const StepScalars &sc, int master_bits,
-                             int states, hipStream_t st)
+hipError_t launch_adamw_step(const StepScalars *scalars, const DevTensor *tensors,
+                             const int32_t *chunk_start, int n_tensors, int32_t total_chunks,
+                             int master_bits, int states, hipStream_t st)
 {
     if (total_chunks <= 0) return hipSuccess;
     return dispatch<AdamWLaunch>(master_bits, states, tensors, chunk_start, n_tensors,
-                                 total_chunks, sc, st);
+                                 total_chunks, scalars, st);
 }
 
 hipError_t launch_sgd_step(const DevTensor *tensors, const int32_t *chunk_start, int n_tensors,

@@ -31,7 +31,8 @@ EXPORTS = ("flashopt_quantize", "flashopt_dequantize", "flashopt_split",
            "flashopt_reconstruct", "flashopt_adamw_workspace_bytes",
            "flashopt_adamw_step", "flashopt_adamw_step_tensor", "flashopt_sgd_workspace_bytes",
            "flashopt_sgd_step", "flashopt_sgd_step_tensor", "flashopt_status_str",
-           "flashopt_abi_version", "flashopt_adamw_step_noalloc")
+           "flashopt_abi_version", "flashopt_adamw_step_noalloc", "flashopt_adamw_plan_bytes",
+           "flashopt_adamw_plan", "flashopt_adamw_plan_set_step", "flashopt_adamw_plan_launch")
 
 
 class FlashoptError(RuntimeError):
@@ -53,6 +54,12 @@ class flashopt_adamw_args(ctypes.Structure):
                 ("weight_decay", ctypes.c_double), ("step", ctypes.c_int64),
                 ("master_bits", ctypes.c_int), ("companded", ctypes.c_int),
                 ("fp32_states", ctypes.c_int), ("param_fp32", ctypes.c_int)]
+
+
+class flashopt_adamw_plan_info(ctypes.Structure):
+    _fields_ = [("n_tensors", ctypes.c_int32), ("total_chunks", ctypes.c_int32),
+                ("master_bits", ctypes.c_int32), ("companded", ctypes.c_int32),
+                ("fp32_states", ctypes.c_int32), ("param_fp32", ctypes.c_int32)]
 
 
 class flashopt_sgd_args(ctypes.Structure):
@@ -94,13 +101,22 @@ def lib() -> ctypes.CDLL:
                                                   ctypes.POINTER(flashopt_adamw_args), vp]
         L.flashopt_sgd_step_tensor.argtypes = [ctypes.POINTER(flashopt_tensor),
                                                ctypes.POINTER(flashopt_sgd_args), vp]
+        L.flashopt_adamw_plan_bytes.argtypes = [i]
+        L.flashopt_adamw_plan_bytes.restype = ctypes.c_size_t
+        L.flashopt_adamw_plan.argtypes = [ctypes.POINTER(flashopt_tensor), i,
+                                          ctypes.POINTER(flashopt_adamw_args), vp, ctypes.c_size_t,
+                                          ctypes.POINTER(flashopt_adamw_plan_info), vp]
+        L.flashopt_adamw_plan_set_step.argtypes = [ctypes.POINTER(flashopt_adamw_plan_info),
+                                                   ctypes.POINTER(flashopt_adamw_args), vp, vp]
+        L.flashopt_adamw_plan_launch.argtypes = [ctypes.POINTER(flashopt_adamw_plan_info), vp, vp]
         L.flashopt_status_str.argtypes = [i]
         L.flashopt_status_str.restype = ctypes.c_char_p
         L.flashopt_abi_version.argtypes = []
         for name in ("flashopt_quantize", "flashopt_dequantize", "flashopt_split",
                      "flashopt_reconstruct", "flashopt_adamw_step", "flashopt_sgd_step",
                      "flashopt_adamw_step_tensor", "flashopt_sgd_step_tensor",
-                     "flashopt_adamw_step_noalloc"):
+                     "flashopt_adamw_step_noalloc", "flashopt_adamw_plan",
+                     "flashopt_adamw_plan_set_step", "flashopt_adamw_plan_launch"):
             getattr(L, name).restype = i
         _lib = L
     return _lib
@@ -273,6 +289,66 @@ def flashopt_adamw_step_tensor(desc: flashopt_tensor, args: flashopt_adamw_args,
            "flashopt_adamw_step_tensor")
 
 
+def flashopt_adamw_plan_bytes(n_tensors: int) -> int:
+    return lib().flashopt_adamw_plan_bytes(n_tensors)
+
+
+def flashopt_adamw_plan(descriptors, args: flashopt_adamw_args, plan: torch.Tensor,
+                        stream=None) -> flashopt_adamw_plan_info:
+    """Stage the scalars of args and the tables of a descriptor array into
+    the device buffer `plan`; returns the plan's host info."""
+    info = flashopt_adamw_plan_info()
+    _check(lib().flashopt_adamw_plan(descriptors, len(descriptors), ctypes.byref(args),
+                                     _dev(plan, "plan"), plan.numel() * plan.element_size(),
+                                     ctypes.byref(info), _stream(stream)),
+           "flashopt_adamw_plan")
+    return info
+
+
+def flashopt_adamw_plan_set_step(info: flashopt_adamw_plan_info, args: flashopt_adamw_args,
+                                 plan: torch.Tensor, stream=None):
+    _check(lib().flashopt_adamw_plan_set_step(ctypes.byref(info), ctypes.byref(args),
+                                              _dev(plan, "plan"), _stream(stream)),
+           "flashopt_adamw_plan_set_step")
+
+
+def flashopt_adamw_plan_launch(info: flashopt_adamw_plan_info, plan: torch.Tensor, stream=None):
+    _check(lib().flashopt_adamw_plan_launch(ctypes.byref(info), _dev(plan, "plan"), _stream(stream)),
+           "flashopt_adamw_plan_launch")
+
+
+class StepPlan:
+    """The capture-safe list step of a FlashAdamW over fixed gradient
+    buffers (flashopt_adamw_plan): launch() enqueues the step kernel only, so
+    it can be recorded into a CUDA/HIP graph, and set_step(t), called outside
+    any capture before a launch or replay, writes the scalars of step t that
+    it uses.  The plan keeps references to the gradient tensors (their
+    addresses are in its table) and does not change the optimizer's step
+    counts."""
+
+    def __init__(self, opt, grads, step: int, stream=None):
+        grads = list(grads)
+        if len(grads) != len(opt.states):
+            raise ValueError(f"{len(grads)} gradients for {len(opt.states)} parameters")
+        self.opt = opt
+        self.grads = grads
+        desc = descriptor_array(opt.states, grads)
+        with torch.cuda.device(opt.device):
+            self.buffer = torch.empty(max(16, flashopt_adamw_plan_bytes(len(desc))), dtype=torch.uint8,
+                                      device=opt.device or "cuda")
+            self.info = flashopt_adamw_plan(desc, make_args(step, **opt.hp), self.buffer, stream)
+        self.t = step
+
+    def set_step(self, t: int, stream=None):
+        with torch.cuda.device(self.opt.device):
+            flashopt_adamw_plan_set_step(self.info, make_args(t, **self.opt.hp), self.buffer, stream)
+        self.t = t
+
+    def launch(self, stream=None):
+        with torch.cuda.device(self.opt.device):
+            flashopt_adamw_plan_launch(self.info, self.buffer, stream)
+
+
 class _Stepper:
     """Common driver of FlashAdamW / FlashSGD: a list step (one launch for all
     tensors) and a per-tensor step (one launch for one tensor, each tensor
@@ -437,6 +513,11 @@ class FlashAdamW(_Stepper):
 
     def _list_step(self, desc, t, stream):
         flashopt_adamw_step(desc, make_args(t, **self.hp), self.workspace(stream), stream)
+
+    def plan(self, grads, step: int, stream=None) -> StepPlan:
+        """A capture-safe list step over these gradient buffers, with the
+        scalars of `step` staged (StepPlan)."""
+        return StepPlan(self, grads, step, stream)
 
     def _tensor_step(self, desc, t, stream):
         flashopt_adamw_step_tensor(desc, make_args(t, **self.hp), stream)

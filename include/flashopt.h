@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define FLASHOPT_ABI_VERSION 5
+#define FLASHOPT_ABI_VERSION 6
 
 typedef enum {
     FLASHOPT_OK = 0,
@@ -158,7 +158,8 @@ typedef struct {
 } flashopt_adamw_args;
 
 /* Device workspace bytes that flashopt_adamw_step needs for this list (the
- * per-tensor descriptor and chunk table).  Returns 0 for n_tensors <= 0. */
+ * step's scalar block, then the per-tensor descriptor and chunk table).
+ * Returns 0 for n_tensors <= 0. */
 size_t flashopt_adamw_workspace_bytes(const flashopt_tensor *tensors, int n_tensors);
 
 /* One fused FlashAdamW step over a list of tensors, one kernel launch (page
@@ -181,11 +182,12 @@ size_t flashopt_adamw_workspace_bytes(const flashopt_tensor *tensors, int n_tens
  *   workspace DEVICE buffer of at least flashopt_adamw_workspace_bytes();
  *             overwritten; it must not be reused by another call until this
  *             step has run on `stream`
- * The descriptor table is staged through a pinned host buffer that the
- * library allocates once and reuses (hipHostMalloc).  That staging is an
- * ordinary asynchronous host-to-device copy from reused memory, so a call
- * captured into a HIP graph would replay whatever the buffer holds at replay
- * time: do not capture this call.  flashopt_adamw_step_tensor launches one
+ * The scalars and the descriptor table are staged through a pinned host
+ * buffer that the library allocates once and reuses (hipHostMalloc).  That
+ * staging is an ordinary asynchronous host-to-device copy from reused
+ * memory, so a call captured into a HIP graph would replay whatever the
+ * buffer holds at replay time: do not capture this call; the plan calls
+ * below are its capture-safe form.  flashopt_adamw_step_tensor launches one
  * kernel with its arguments by value and stages nothing.
  * Errors: EINVAL (n_tensors < 0, NULL tensors/args, numel < 0, NULL pointer
  * that the variant uses in a non-empty tensor, master_bits, companded,
@@ -201,8 +203,8 @@ flashopt_status flashopt_adamw_step(const flashopt_tensor *tensors, int n_tensor
 /* flashopt_adamw_step for callers that cannot allocate: code under HIP
  * graph capture, tight serving loops, harnesses that forbid allocation.  Same
  * arguments, results and validation as flashopt_adamw_step, without a
- * workspace: the chunk table goes to a device array inside the library (68
- * KiB per GPU, held until the process ends) through one pageable
+ * workspace: the scalars and the chunk table go to a device array inside
+ * the library (68 KiB per GPU, held until the process ends) through one pageable
  * hipMemcpyAsync from a static host buffer, and the call allocates nothing
  * (no hipMalloc, hipHostMalloc, hipFree or event creation; the first call on
  * a device looks the array's address up once).
@@ -216,6 +218,54 @@ flashopt_status flashopt_adamw_step(const flashopt_tensor *tensors, int n_tensor
  * Errors: as flashopt_adamw_step (EWORKSPACE only for n_tensors > 1024). */
 flashopt_status flashopt_adamw_step_noalloc(const flashopt_tensor *tensors, int n_tensors,
                                             const flashopt_adamw_args *args, void *stream);
+
+/* A capture-safe form of flashopt_adamw_step, for a training step captured
+ * into a HIP graph: the scalar block and the descriptor and chunk tables
+ * live in a caller-owned DEVICE buffer (the plan), and the launch reads them
+ * there.  Results are those of flashopt_adamw_step with the same tensors and
+ * arguments.
+ *
+ * flashopt_adamw_plan_bytes(n): bytes of a plan for n tensors (the same as
+ *   flashopt_adamw_workspace_bytes; 0 for n <= 0).
+ * flashopt_adamw_plan(tensors, n, args, plan, plan_bytes, info, stream):
+ *   validates the list and args as flashopt_adamw_step does, enqueues one
+ *   host-to-device copy on `stream` that writes the scalars of args->step
+ *   and the tables into `plan` (16-byte aligned), and fills *info (a host
+ *   struct: list size and the variant fields of args).  The tensors' buffers
+ *   must stay where they are for as long as the plan is launched.
+ * flashopt_adamw_plan_set_step(info, args, plan, stream): enqueues one
+ *   128-byte host-to-device copy of the scalars of args (any step and
+ *   hyper-parameters; master_bits, companded, fp32_states and param_fp32
+ *   must equal the plan's, else EINVAL).
+ * flashopt_adamw_plan_launch(info, plan, stream): enqueues the step kernel
+ *   only.  It copies nothing, allocates nothing and does not synchronize, so
+ *   it can be captured into a graph; a launch or graph replay steps with the
+ *   scalars that the last plan / plan_set_step copy wrote before it runs.
+ * The two staging calls copy from library-owned pinned buffers at the call
+ * and must not be captured: between replays, call plan_set_step with the
+ * next step count on the replay stream (or one ordered before it), then
+ * replay.  `info` must be the one flashopt_adamw_plan filled for `plan`.
+ * Errors: as flashopt_adamw_step (EWORKSPACE: plan NULL or smaller than
+ * flashopt_adamw_plan_bytes; EINVAL also for a NULL info or a variant
+ * mismatch). */
+size_t flashopt_adamw_plan_bytes(int n_tensors);
+typedef struct {
+    int32_t n_tensors;        /* tensors in the plan's table                  */
+    int32_t total_chunks;     /* their 1024-element chunks                    */
+    int32_t master_bits;      /* the variant fields of the planning args      */
+    int32_t companded;
+    int32_t fp32_states;
+    int32_t param_fp32;
+} flashopt_adamw_plan_info;
+flashopt_status flashopt_adamw_plan(const flashopt_tensor *tensors, int n_tensors,
+                                    const flashopt_adamw_args *args, void *plan,
+                                    size_t plan_bytes, flashopt_adamw_plan_info *info,
+                                    void *stream);
+flashopt_status flashopt_adamw_plan_set_step(const flashopt_adamw_plan_info *info,
+                                             const flashopt_adamw_args *args, void *plan,
+                                             void *stream);
+flashopt_status flashopt_adamw_plan_launch(const flashopt_adamw_plan_info *info,
+                                           const void *plan, void *stream);
 
 /* FlashSGD hyper-parameters.  FlashSGD appears on page
  * "code/flashsim/flash_adamw_sim.py" only in bytes_per_param ("flash_sgd":

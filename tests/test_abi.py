@@ -153,6 +153,65 @@ def test_noalloc_step_validation(L):
     assert step([_tensor(numel=(1 << 41) + 1)]) == F.FLASHOPT_EINVAL
 
 
+def test_plan_validation(L):
+    """The capture-safe plan calls validate like the list step, before any
+    HIP call; the plan buffer has the workspace's size (a 128-byte scalar
+    block, then the tables)."""
+    info = F.flashopt_adamw_plan_info()
+    args = F.make_args(1)
+
+    def plan(tensors, a=None, buf=A16, nbytes=1 << 20, inf=info, n=None):
+        arr = (F.flashopt_tensor * max(1, len(tensors)))(*tensors)
+        return L.flashopt_adamw_plan(arr if tensors else None, len(tensors) if n is None else n,
+                                     ctypes.byref(a or args), buf, nbytes,
+                                     ctypes.byref(inf) if inf is not None else None, None)
+
+    assert L.flashopt_adamw_plan_bytes(0) == 0
+    for n in (1, 3, 290):
+        assert L.flashopt_adamw_plan_bytes(n) == F.flashopt_adamw_workspace_bytes(n)
+        assert L.flashopt_adamw_plan_bytes(n) >= 128 + n * 64 + (n + 1) * 4
+    need = L.flashopt_adamw_plan_bytes(1)
+    assert plan([_tensor()], inf=None) == F.FLASHOPT_EINVAL
+    assert plan([], n=-1) == F.FLASHOPT_EINVAL
+    assert plan([_tensor()], F.make_args(0)) == F.FLASHOPT_EINVAL
+    assert plan([_tensor(numel=-1)]) == F.FLASHOPT_EINVAL
+    assert plan([_tensor(grad=None)]) == F.FLASHOPT_EINVAL
+    assert plan([_tensor()], buf=None) == F.FLASHOPT_EWORKSPACE
+    assert plan([_tensor()], nbytes=need - 1) == F.FLASHOPT_EWORKSPACE
+    assert plan([_tensor()], buf=A16 + 8, nbytes=need) == F.FLASHOPT_EALIGN
+    assert plan([]) == F.FLASHOPT_OK                      # nothing to stage
+    assert (info.n_tensors, info.total_chunks) == (0, 0)
+    assert L.flashopt_adamw_plan_launch(ctypes.byref(info), None, None) == F.FLASHOPT_OK
+
+    # set_step: the variant must be the plan's
+    good = F.flashopt_adamw_plan_info(1, 4, 24, 1, 0, 0)
+    for bad in (dict(master_bits=32), dict(companded=0), dict(fp32_states=1),
+                dict(master_bits=0, param_fp32=1)):
+        a = F.make_args(5)
+        for k, v in bad.items():
+            setattr(a, k, v)
+        assert L.flashopt_adamw_plan_set_step(ctypes.byref(good), ctypes.byref(a), A16,
+                                              None) == F.FLASHOPT_EINVAL, bad
+    assert L.flashopt_adamw_plan_set_step(None, ctypes.byref(F.make_args(5)), A16, None) == F.FLASHOPT_EINVAL
+    assert L.flashopt_adamw_plan_set_step(ctypes.byref(good), ctypes.byref(F.make_args(0)), A16,
+                                          None) == F.FLASHOPT_EINVAL
+    assert L.flashopt_adamw_plan_set_step(ctypes.byref(good), ctypes.byref(F.make_args(5)), None,
+                                          None) == F.FLASHOPT_EWORKSPACE
+    assert L.flashopt_adamw_plan_set_step(ctypes.byref(good), ctypes.byref(F.make_args(5)), A16 + 8,
+                                          None) == F.FLASHOPT_EALIGN
+
+    # launch: the info's fields are checked, the buffer must be there
+    def launch(fields, buf=A16):
+        return L.flashopt_adamw_plan_launch(ctypes.byref(F.flashopt_adamw_plan_info(*fields)), buf, None)
+    for bad in ((1, 4, 16, 1, 0, 0), (1, 4, 24, 2, 0, 0), (1, 4, 24, 1, 2, 0), (1, 4, 24, 1, 0, 1),
+                (-1, 4, 24, 1, 0, 0), (1, -4, 24, 1, 0, 0), (0, 4, 24, 1, 0, 0)):
+        assert launch(bad) == F.FLASHOPT_EINVAL, bad
+    assert launch((1, 4, 24, 1, 0, 0), buf=None) == F.FLASHOPT_EWORKSPACE
+    assert launch((1, 4, 24, 1, 0, 0), buf=A16 + 8) == F.FLASHOPT_EALIGN
+    assert launch((1, 0, 24, 1, 0, 0)) == F.FLASHOPT_OK    # an empty list launches nothing
+    assert L.flashopt_adamw_plan_launch(None, A16, None) == F.FLASHOPT_EINVAL
+
+
 def test_binding_refuses_host_tensors(L):
     import torch
     with pytest.raises(ValueError):
@@ -184,7 +243,7 @@ def test_sgd_step_validation(L):
     assert sgd([_tensor(m_scales=None)], F.make_sgd_args(1, quantize_states=False),
                ws_bytes=0) == F.FLASHOPT_EWORKSPACE
     assert sgd([_tensor(m_codes=A16 + 8)], F.make_sgd_args(1), ws_bytes=0) == F.FLASHOPT_EALIGN
-    assert F.flashopt_sgd_workspace_bytes(3) == F.flashopt_adamw_workspace_bytes(3)
+    assert F.flashopt_sgd_workspace_bytes(3) + 128 == F.flashopt_adamw_workspace_bytes(3)   # AdamW stages its scalars
 
 
 def test_single_tensor_validation(L):

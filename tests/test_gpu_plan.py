@@ -1,0 +1,100 @@
+"""The capture-safe list step (flashopt_adamw_plan, _plan_set_step,
+_plan_launch; FlashAdamW.plan in the binding).  A plan launch must leave the
+bits flashopt_adamw_step leaves with the same tensors, gradients and step
+(the list step is checked against the oracle elsewhere, so equality carries
+that parity over), and a launch captured once into a HIP graph must replay
+with the scalars each set_step wrote: every replay equals an eager list step
+at its own step count."""
+import pytest
+import torch
+
+from bit_companded_adam_amd import flashopt as F
+from bit_companded_adam_amd import workloads as W
+from tests._gpu import require_gpu
+
+pytestmark = pytest.mark.gpu
+
+SIZES = [1, 33, 1000, 1024, 1025, 70001, 1 << 17]
+# (master_bits, companded, quantize_states, parameter dtype)
+VARIANTS = [(24, True, True, torch.bfloat16), (32, False, True, torch.bfloat16),
+            (None, True, False, torch.bfloat16), (None, True, True, torch.float32)]
+IDS = ["mb24-comp", "mb32-lin", "mbNone-f32states", "fp32params"]
+
+
+def _pair(variant, seed):
+    mb, comp, qs, dt = variant
+    pa = [W.init_param(n, device="cuda", seed=seed + i, dtype=dt) for i, n in enumerate(SIZES)]
+    pb = [p.clone() for p in pa]
+    make = lambda ps: F.FlashAdamW(ps, master_bits=mb, companded=comp, quantize_states=qs,
+                                   **W.HP_DEFAULT)
+    return make(pa), make(pb), dt
+
+
+def _grads(t, dt):
+    return [W.make_grad(n, t, device="cuda", stream_id=i, dtype=dt) for i, n in enumerate(SIZES)]
+
+
+def _bits(x):
+    if x is None:
+        return None
+    return x.view(torch.int16) if x.element_size() == 2 else (x.view(torch.int32) if x.element_size() == 4 else x)
+
+
+def _assert_same(a: F.FlashAdamW, b: F.FlashAdamW, label):
+    for i, (sa, sb) in enumerate(zip(a.states, b.states)):
+        for name in ("param", "rho", "m_codes", "m_scales", "v_codes", "v_scales"):
+            x, y = getattr(sa, name), getattr(sb, name)
+            assert (x is None) == (y is None), f"{label} tensor {i}: {name}"
+            if x is not None:
+                assert torch.equal(_bits(x), _bits(y)), f"{label} tensor {i}: {name}"
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=IDS)
+def test_plan_launch_equals_list_step(variant):
+    """Steps 1..4 and then step 20001 (past the horizon where both bias
+    corrections round to 1), each through a plan launch over fixed gradient
+    buffers and through the list step."""
+    require_gpu()
+    a, b, dt = _pair(variant, 900)
+    bufs = [torch.empty(n, dtype=dt, device="cuda") for n in SIZES]
+    plan = b.plan(bufs, step=1)
+    for t in (1, 2, 3, 4, 20001):
+        grads = _grads(t, dt)
+        a.t = t - 1
+        a.step(grads)
+        for buf, g in zip(bufs, grads):
+            buf.copy_(g)
+        if t != 1:
+            plan.set_step(t)
+        plan.launch()
+        torch.cuda.synchronize()
+        _assert_same(a, b, f"step {t}")
+
+
+@pytest.mark.parametrize("variant", VARIANTS[:2], ids=IDS[:2])
+def test_plan_launch_replays_from_a_hip_graph(variant):
+    """One plan launch captured into a graph; four replays, each after new
+    gradients are copied into the plan's buffers and set_step writes the
+    next step's scalars, with eager work and a synchronize between replays:
+    every replay equals the list step at its step count."""
+    require_gpu()
+    a, b, dt = _pair(variant, 950)
+    bufs = [torch.zeros(n, dtype=dt, device="cuda") for n in SIZES]
+    plan = b.plan(bufs, step=1)
+    side = torch.randn(1 << 20, device="cuda")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan.launch()
+    torch.cuda.synchronize()
+    _assert_same(a, b, "after capture")            # capture runs nothing
+    for t in (1, 2, 3, 4):
+        grads = _grads(t, dt)
+        a.step(grads)
+        for buf, g in zip(bufs, grads):
+            buf.copy_(g)
+        plan.set_step(t)
+        graph.replay()
+        side.mul_(1.0001).add_(t)                   # eager work between replays
+        torch.cuda.synchronize()
+        _assert_same(a, b, f"replay at step {t}")
