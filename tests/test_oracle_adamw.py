@@ -16,8 +16,15 @@
 * The OpenMP slice driver equals the per-tensor step bit for bit.
 * 300 free-running steps with fp32 moments and the 32-bit master track
   torch.optim.AdamW within a derived rounding bound.
-A long trajectory with quantized states or the 24-bit master has no
-independent pin beyond this composition (parity unpinned for it)."""
+* A long trajectory with quantized states has a closed form in one special
+  case: a group whose 32 elements are equal always gets the code +-127
+  (momentum) or 255 (variance), whose dequantized value is exactly the
+  group's fp16 scale, so the stored moments follow m <- fp16(m1) and
+  v <- fp16(sqrt(v1))^2 (with the lossless 32-bit master, theta carries over
+  unchanged); 40 steps of four such groups follow that recursion bit for bit.
+A long trajectory with quantized states in general, or with the 24-bit
+master, has no independent pin beyond this composition (parity unpinned for
+it)."""
 import os
 
 import numpy as np
@@ -285,3 +292,52 @@ def test_long_trajectory_tracks_torch_adamw(orc):
             assert (np.abs(th - p.detach().numpy()) <= 3e-5).all(), t
             v_ref = opt.state[p]["exp_avg_sq"].numpy().astype(np.float64)
             assert (np.abs(st.v_codes - v_ref) <= 1e-4 * v_ref).all(), t
+
+
+def test_constant_group_trajectory_closed_form(orc):
+    """Four groups (the last one ragged), each holding one value repeated:
+    at every step its momentum code is +-127 and its variance code 255, since
+    the group maximum's fp16 rounding moves |m1| / scale and sqrt(v1) / scale
+    by at most 2^-11 from 1, and dequantize(+-127) = +-scale, dequantize(255)
+    = scale^2 exactly.  So the companded states follow m <- fp16(m1),
+    v <- fl(fp16(sqrt(v1))^2), and with the lossless 32-bit master theta
+    follows the update of page "code/flashsim/flash_adamw_sim.py"
+    (FlashAdamWSim.step) in float32.  The gradients keep every moment in
+    fp16's normal range, where these bounds hold."""
+    rng = np.random.default_rng(13)
+    sizes = [32, 32, 32, 7]
+    n, steps = sum(sizes), 40
+    group_of = np.repeat(np.arange(len(sizes)), sizes)
+    theta0 = _bits_to_f32(_bf16_bits((rng.standard_normal(len(sizes)) * 0.5).astype(np.float32)))
+    gs = [_bits_to_f32(_bf16_bits((rng.choice([-1.0, 1.0], len(sizes)) *
+                                   rng.uniform(0.02, 0.2, len(sizes))).astype(np.float32)))
+          for _ in range(steps)]
+    st = orc.State.zeros_like_param(_bf16_bits(theta0[group_of]), 32)
+    f32 = np.float32
+    lr, wd, (beta1, beta2), eps = HP["lr"], HP["weight_decay"], HP["betas"], HP["eps"]
+    cwd, b1, c1, b2, c2 = f32(1 - lr * wd), f32(beta1), f32(1 - beta1), f32(beta2), f32(1 - beta2)
+    th, m, v = theta0.copy(), np.zeros(len(sizes), f32), np.zeros(len(sizes), f32)
+    for t in range(1, steps + 1):
+        g = gs[t - 1]
+        orc.adamw_step(st, _bf16_bits(g[group_of]), orc.hparams(**HP, step=t, master_bits=32))
+        bc1, bc2 = f32(1 - beta1 ** t), f32(1 - beta2 ** t)
+        thd = th * cwd
+        m1 = b1 * m + c1 * g
+        v1 = b2 * v + (c2 * g) * g
+        mhat, vhat = m1 / bc1, v1 / bc2
+        th = thd - (f32(lr) * mhat) / (np.sqrt(vhat) + f32(eps))
+        sm = np.abs(m1).astype(np.float16)
+        sv = np.sqrt(v1).astype(np.float16)
+        assert (np.abs(sm.astype(f32)) > 6.2e-5).all() and (sv.astype(f32) > 6.2e-5).all()
+        m = np.copysign(sm.astype(f32), m1)
+        v = sv.astype(f32) * sv.astype(f32)
+        assert (st.m_codes == np.where(m1 < 0, -127, 127)[group_of]).all(), f"t{t}: m codes"
+        assert (st.v_codes == 255).all(), f"t{t}: v codes"
+        assert (st.m_scales == sm.view(np.uint16)).all(), f"t{t}: m scales"
+        assert (st.v_scales == sv.view(np.uint16)).all(), f"t{t}: v scales"
+        got = orc.reconstruct(st.param, st.rho, 32)
+        assert (got.view(np.uint32) == th[group_of].view(np.uint32)).all(), f"t{t}: theta"
+    # the states the oracle stores decode to the recursion's moments
+    assert (orc.dequantize(st.m_codes, st.m_scales, orc.MOMENTUM) == m[group_of]).all()
+    assert (orc.dequantize(st.v_codes, st.v_scales, orc.VARIANCE) == v[group_of]).all()
+
