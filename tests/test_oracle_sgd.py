@@ -13,8 +13,13 @@ torch.optim.SGD with momentum, the buffer stored with the momentum spec.
   cast of the fp32 update.
 * 300 free-running steps with an fp32 buffer and the 32-bit master track
   torch.optim.SGD within a derived rounding bound.
-A long trajectory with a quantized buffer or the 24-bit master has no
-independent pin beyond this composition (parity unpinned for it)."""
+* A group whose 32 elements are equal always gets the code +-127, which
+  dequantizes to exactly the group's fp16 scale, so a quantized buffer
+  follows buf <- fp16(buf1): 40 steps of four such groups follow that float32
+  recursion bit for bit.
+A long trajectory with a quantized buffer in general, or with the 24-bit
+master, has no independent pin beyond this composition (parity unpinned for
+it)."""
 import numpy as np
 import pytest
 import torch
@@ -158,3 +163,43 @@ def test_long_trajectory_tracks_torch_sgd(orc, dampening, nesterov, wd):
             th = orc.reconstruct(st.param, st.rho, 32).astype(np.float64)
             assert np.abs(th).max() < 0.25
             assert (np.abs(th - p.detach().numpy()) <= 1e-5).all(), t
+
+
+@pytest.mark.parametrize("dampening,nesterov", [(0.1, False), (0.0, True)])
+def test_constant_group_trajectory_closed_form(orc, dampening, nesterov):
+    """Four groups (the last one ragged), each holding one value repeated:
+    the momentum code is +-127 at every step (the fp16 rounding of the group
+    maximum moves |buf1| / scale by at most 2^-11 from 1) and dequantizes to
+    +-scale exactly, so the stored buffer follows buf <- fp16(buf1), and with
+    the lossless 32-bit master theta follows torch.optim.SGD's order in
+    float32 (d = g + wd theta; buf1 = d at step 1, else mu buf + (1 -
+    dampening) d; the direction buf1, or d + mu buf1 with Nesterov)."""
+    rng = np.random.default_rng(17)
+    sizes = [32, 32, 32, 9]
+    n, steps = sum(sizes), 40
+    lr, mu, wd = 1e-2, 0.9, 0.01
+    group_of = np.repeat(np.arange(len(sizes)), sizes)
+    theta0 = _bits_to_f32(_bf16_bits((rng.standard_normal(len(sizes)) * 0.5).astype(np.float32)))
+    gs = [_bits_to_f32(_bf16_bits((rng.choice([-1.0, 1.0], len(sizes)) *
+                                   rng.uniform(0.02, 0.2, len(sizes))).astype(np.float32)))
+          for _ in range(steps)]
+    st = orc.State.zeros_like_param(_bf16_bits(theta0[group_of]), 32)
+    f32 = np.float32
+    th, buf = theta0.copy(), np.zeros(len(sizes), f32)
+    for t in range(1, steps + 1):
+        g = gs[t - 1]
+        orc.sgd_step(st, _bf16_bits(g[group_of]),
+                     orc.sgd_hparams(lr=lr, momentum=mu, dampening=dampening, weight_decay=wd,
+                                     step=t, master_bits=32, nesterov=nesterov))
+        d = g + f32(wd) * th
+        b1 = d if t == 1 else f32(mu) * buf + f32(1 - dampening) * d
+        direction = d + f32(mu) * b1 if nesterov else b1
+        th = th - f32(lr) * direction
+        sc = np.abs(b1).astype(np.float16)
+        assert (sc.astype(f32) > 6.2e-5).all()
+        buf = np.copysign(sc.astype(f32), b1)
+        assert (st.m_codes == np.where(b1 < 0, -127, 127)[group_of]).all(), f"t{t}: codes"
+        assert (st.m_scales == sc.view(np.uint16)).all(), f"t{t}: scales"
+        got = orc.reconstruct(st.param, st.rho, 32)
+        assert (got.view(np.uint32) == th[group_of].view(np.uint32)).all(), f"t{t}: theta"
+
