@@ -16,16 +16,19 @@
 // states and the codec and split kernels use N = 4 (quantize's group
 // maximum spans 8 lanes).  The path is elementwise, so there is no MFMA; LDS
 // holds only the two 256-entry dequantization tables (compile-time constants
-// copied in per workgroup), and the per-tensor chunk table is read with
-// scalar loads.
+// copied in per workgroup), and the list steps' scalar block and per-tensor
+// chunk table are read with scalar loads.
 //
 // Arithmetic: fp32, one IEEE rounding per operation in the written order
 // (built with -ffp-contract=off, fp32 and fp16 denormals preserved), so the
-// results match a plain CPU evaluation bit for bit.  Division by a group
-// scale, the softsign division, the update division, the variance sqrt and
-// the byte conversions use the exact short sequences of flashopt_math.h
-// instead of the generic correctly rounded expansions; the momentum code uses
-// a guarded short sequence whose fallback is the correctly rounded chain.
+// results match a plain CPU evaluation bit for bit.  The update follows the
+// operation order FlashAdamWSim.step prints: the bias-correction quotients
+// come from fp64 products with host-computed reciprocals (exact once rounded
+// to fp32), and division by a group scale, the softsign division, the update
+// division, the sqrt and the byte conversions use the exact short sequences
+// of flashopt_math.h instead of the generic correctly rounded expansions.
+// The momentum and variance codes use two-sided short forms; a word whose two
+// evaluations disagree falls back to the correctly rounded chain.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -65,7 +68,7 @@ __device__ __forceinline__ float f16_value(uint32_t bits)
 }
 
 // The divisor of a group: 1 when the stored scale is zero (either sign),
-// else the scale itself (quantize(): `where(scales == 0, 1, scales)`).
+// else the scale itself, as quantize() divides by 1 for a zero scale.
 __device__ __forceinline__ float group_divisor(uint32_t s)
 {
     return (s & 0x7FFFu) ? f16_value(s) : 1.0f;
@@ -1705,10 +1708,11 @@ struct SgdTensorLaunch {
 // ------------------------------------ scratch of the allocation-free step
 
 // The scalar block and chunk table of flashopt_adamw_step_noalloc: a device
-// array of this file instead of a caller's workspace.  Every GPU the library runs on holds
-// its own copy until the process ends.  In host code the name stands for a
-// host-side shadow, not a device address, so host code reaches the array only
-// through the address hipGetSymbolAddress returns for the current device.
+// array of this file instead of a caller's workspace.  Every GPU the library
+// runs on holds its own copy until the process ends.  In host code the name
+// stands for a host-side shadow, not a device address, so host code reaches
+// the array only through the address hipGetSymbolAddress returns for the
+// current device.
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 hipError_t scratch_address(void **ptr)

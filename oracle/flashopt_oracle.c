@@ -35,7 +35,8 @@ static float float_of(uint32_t u) { float x; memcpy(&x, &u, 4); return x; }
 static float bf16_to_f32(uint16_t b) { return float_of((uint32_t)b << 16); }
 
 /* torch's float32 -> bfloat16 cast: round to nearest, ties to even (used only
- * when there is no master split, [SIM step()] `p.copy_(theta.to(p.dtype))`). */
+ * when there is no master split: [SIM step()] then writes theta back cast to
+ * the parameter's dtype). */
 static uint16_t bf16_rne(float x)
 {
     uint32_t u = bits_of(x);
@@ -95,8 +96,8 @@ float oracle_f32_from_f16(uint16_t h)
 
 /* R1.  The pages call the split (S.compress / S.decompress in [SIM step()]
  * and [EQ eq_ecc()]) but do not print it.  What they fix: theta' is the bf16
- * rounding of the fp32 master ([EQ eq_ecc()] feeds `x.to(torch.bfloat16)` to
- * the correction-bit routine), rho is int8 for a 24-bit and int16 for a 32-bit
+ * rounding of the fp32 master ([EQ eq_ecc()] passes the bf16 cast of the master
+ * to the correction-bit routine), rho is int8 for a 24-bit and int16 for a 32-bit
  * master ([SIM FlashAdamWSim.__init__]), and a bf16-exact parameter splits to
  * rho = 0 ([SIM step()], state init).  Reading:
  *   theta' = theta rounded to bf16, nearest, ties away from zero (on the
@@ -288,7 +289,7 @@ static void make_scalars(const oracle_hparams *h, step_scalars *s)
 /* Body of Alg. 4 [SIM step()], "Standard AdamW update", decoupled weight
  * decay, torch convention, one float32 rounding per operation in the order
  * the page writes it (Python evaluates left to right):
- *   theta <- theta * (1 - lr wd)                 (skipped by `if wd:`; R11:
+ *   theta <- theta * (1 - lr wd)                 (skipped when wd = 0; R11:
  *                                                 a factor of 1.0 is exact)
  *   m     <- beta1 * m + (1 - beta1) * g
  *   v     <- beta2 * v + ((1 - beta2) * g) * g
@@ -339,7 +340,7 @@ static unsigned variance_spec(int companded)
  * update is split again; without one and a bf16 parameter, theta is the bf16
  * value widened and the update is cast back with torch's bf16 cast (R14);
  * with an fp32 parameter (fp32_param), theta is the parameter itself, its
- * gradient is fp32, and `p.copy_(theta)` stores the update unchanged. */
+ * gradient is fp32, and the update is stored unchanged. */
 int oracle_adamw_step(void *param, const void *grad, void *rho,
                       void *m_codes, uint16_t *m_scales,
                       void *v_codes, uint16_t *v_scales,

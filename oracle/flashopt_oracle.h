@@ -48,7 +48,7 @@ extern "C" {
 
 /* fp32 -> IEEE binary16 bits, round to nearest even, subnormals kept,
  * |x| >= 65520 -> +-Inf, NaN -> quiet NaN 0x7E00|sign.  This is the
- * `.to(torch.float16)` that forms the per-group scale [QZ quantize()]. */
+ * fp16 cast that forms the per-group scale [QZ quantize()]. */
 uint16_t oracle_f16_from_f32(float x);
 /* The same conversion over an array. */
 void oracle_f16_array(const float *x, int64_t n, uint16_t *out);

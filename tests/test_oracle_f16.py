@@ -1,5 +1,5 @@
 """Pins for the oracle's fp32 -> binary16 conversion (the per-group scale is
-`.to(torch.float16)` of the group absmax, page "code/flashsim/quantization.py",
+torch's fp16 cast of the group absmax, page "code/flashsim/quantization.py",
 quantize()).
 
 Pinned against numpy.float16 (an independent library conversion, IEEE round

@@ -2,8 +2,8 @@
 int8/int16 rho) and its inverse.
 
 The pages do not print the split; they fix that theta' is the bf16 rounding of
-the master (page "code/gpu/equivalence.py", eq_ecc(): `x.to(torch.bfloat16)`
-feeds the correction-bit routine), that rho is int8 for a 24-bit master and
+the master (page "code/gpu/equivalence.py", eq_ecc() passes the bf16 cast of
+the master to the correction-bit routine), that rho is int8 for a 24-bit master and
 int16 for a 32-bit one (page "code/flashsim/flash_adamw_sim.py",
 FlashAdamWSim.__init__), and that a bf16-exact parameter splits to rho = 0
 (FlashAdamWSim.step, state init).  What pins the oracle here:
