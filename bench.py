@@ -180,20 +180,35 @@ def _mhz(text):
 
 
 def time_steps(opt, grads, steps: int, warmup: int, per_tensor: bool = False,
-               batch_below: int = 0, n_streams: int = 1):
+               batch_below: int = 0, n_streams: int = 1, graph: bool = False):
     """per_tensor: the gradient-release launch pattern, one single-tensor
     launch per tensor (the step is then the whole sequence of launches);
     tensors with fewer than batch_below elements are instead stepped together
     in one list launch after the others (attach_grad_release's batching).
     n_streams > 1: the single-tensor launches go round-robin to that many
     side streams, which start after and are joined back into the timed
-    stream (attach_grad_release's streams)."""
+    stream (attach_grad_release's streams).  graph: the capture-safe list
+    step (FlashAdamW.plan) captured once into a HIP graph; each step writes
+    its scalars (set_step, a 128-byte copy) and replays the graph."""
     small = [i for i, g in enumerate(grads) if g.numel() < batch_below]
     large = [i for i, g in enumerate(grads) if g.numel() >= batch_below]
     side = [torch.cuda.Stream() for _ in range(n_streams)] if per_tensor and n_streams > 1 else []
 
+    replay = None
+    if graph:
+        plan = opt.plan(grads, step=opt.t + 1)
+        torch.cuda.synchronize()
+        replay = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(replay):
+            plan.launch()
+        torch.cuda.synchronize()
+
     def one_step(stream=None):
-        if per_tensor:
+        if replay is not None:
+            opt.t += 1
+            plan.set_step(opt.t, stream)
+            replay.replay()
+        elif per_tensor:
             cur = stream or torch.cuda.current_stream()
             for s in side:
                 s.wait_stream(cur)
@@ -429,6 +444,8 @@ def main():
     ap.add_argument("--release-streams", type=int, default=F.RELEASE_STREAMS,
                     help="with --grad-release: spread the launches over this many streams "
                          "(default: attach_grad_release's)")
+    ap.add_argument("--graph", action="store_true",
+                    help="step through the capture-safe plan launch replayed from a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the oracle on the host cores")
     ap.add_argument("--cpu-threads", type=int, default=0,
@@ -475,8 +492,11 @@ def main():
     print(f"# workload ready: {len(opt.states)} tensors, {n} params, "
           f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated", file=sys.stderr, flush=True)
 
+    if args.graph and (args.optimizer != "adamw" or args.grad_release):
+        print("--graph times the AdamW list step (no --grad-release, no --optimizer sgd)", file=sys.stderr)
+        sys.exit(2)
     wall, per = time_steps(opt, grads, args.steps, args.warmup, args.grad_release, args.batch_below,
-                           args.release_streams)
+                           args.release_streams, args.graph)
     env = environment()                     # clocks read right after the timed steps
     ms_step = wall * 1e3 / args.steps
     ms_launch = float(np.mean(per))
@@ -493,14 +513,16 @@ def main():
     if not args.no_cpu_baseline and args.optimizer == "adamw":
         cpu = cpu_baseline(mb, comp, qs, args.cpu_threads, param_fp32=args.param_fp32)
     default = (args.workload, mb, comp, qs, args.optimizer, args.grad_release, args.param_fp32,
-               args.first_step) == ("decoder-8b-list", 24, True, True, "adamw", False, False, 1)
+               args.first_step, args.graph) == ("decoder-8b-list", 24, True, True, "adamw", False,
+                                                False, 1, False)
     name = args.workload + ("" if comp else "-linear") + ("" if qs else "-fp32-states") + \
         ("-fp32-params" if args.param_fp32 else ("-no-split" if mb == 0 else "")) + \
         ("-flashsgd" if args.optimizer == "sgd" else "") + \
         ("-per-tensor-launches" if args.grad_release else "") + \
         (f"-batched-below-{args.batch_below}" if args.grad_release and args.batch_below else "") + \
         (f"-{args.release_streams}-streams" if args.grad_release and args.release_streams > 1 else "") + \
-        (f"-from-step-{args.first_step}" if args.first_step != 1 else "")
+        (f"-from-step-{args.first_step}" if args.first_step != 1 else "") + \
+        ("-graph-replay" if args.graph else "")
 
     launches = 1
     if args.grad_release:

@@ -98,3 +98,33 @@ def test_plan_launch_replays_from_a_hip_graph(variant):
         side.mul_(1.0001).add_(t)                   # eager work between replays
         torch.cuda.synchronize()
         _assert_same(a, b, f"replay at step {t}")
+
+
+def test_decoder_8b_graph_replays_equal_list_steps():
+    """The whole 8.0B list (290 tensors) stepped twice through one captured
+    plan launch (set_step between replays) and twice through the list step
+    from the same seeded start: every stored byte equal after each step
+    (compared on the device)."""
+    require_gpu()
+    shapes = W.decoder_8b_shapes()
+    sizes = [W.numel(s) for _, s in shapes]
+    factors = W.grad_factors(len(shapes)).tolist()
+    params = [W.init_param(n, device="cuda", seed=W.PARAM_SEED + i) for i, n in enumerate(sizes)]
+    a = F.FlashAdamW(params, **W.HP_DEFAULT)
+    b = F.FlashAdamW([p.clone() for p in params], **W.HP_DEFAULT)
+    del params
+    grads = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for n in sizes]
+    plan = b.plan(grads, step=1)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan.launch()
+    for t in (1, 2):
+        for i, (g, n) in enumerate(zip(grads, sizes)):
+            g.copy_(W.make_grad(n, t, device="cuda", stream_id=i, factor=factors[i]))
+        a.step(grads)
+        plan.set_step(t)
+        graph.replay()
+        torch.cuda.synchronize()
+        _assert_same(a, b, f"8.0B list, step {t}")
+
