@@ -37,6 +37,27 @@ def test_exports_every_declared_symbol(L):
         assert hasattr(L, name), name
 
 
+def test_header_compiles_as_c(tmp_path):
+    """include/flashopt.h is plain C: a C11 translation unit that takes the
+    address of every declared entry point, with its exact prototype,
+    compiles with -Wall -Werror -pedantic (no C++ or HIP types leak into the
+    boundary)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not found")
+    names = _declared()
+    src = ["#include \"flashopt.h\"", "typedef void (*fn)(void);", "int main(void) {", "    fn p[] = {"]
+    src += [f"        (fn)&{n}," for n in names]
+    src += ["    };", "    return (int)(sizeof p / sizeof p[0]) == " + str(len(names)) + " ? 0 : 1;", "}"]
+    c = tmp_path / "abi.c"
+    c.write_text("\n".join(src) + "\n")
+    r = subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                        "-I", os.path.join(ROOT, "include"), "-c", str(c),
+                        "-o", str(tmp_path / "abi.o")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
 def test_abi_version_and_status_strings(L):
     ver = int(re.search(r"#define FLASHOPT_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
     assert L.flashopt_abi_version() == ver
