@@ -149,6 +149,21 @@ def n_groups(n: int) -> int:
     return (n + GROUP - 1) // GROUP
 
 
+def _buf(t: torch.Tensor, name: str, device, elem_sizes, numel: int, float32: bool = False):
+    """A caller-supplied buffer's address, after the checks the C ABI cannot
+    make on plain pointers: same device as the input, element width, enough
+    elements (a short buffer would be written past its end on the GPU)."""
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the input on {device}")
+    if float32 and t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32")
+    if t.element_size() not in elem_sizes:
+        raise ValueError(f"{name} must have {'/'.join(map(str, elem_sizes))}-byte elements")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, {numel} needed")
+    return _dev(t, name)
+
+
 def flashopt_abi_version() -> int:
     return lib().flashopt_abi_version()
 
@@ -160,27 +175,38 @@ def flashopt_quantize(x: torch.Tensor, spec: int, codes=None, scales=None, strea
     n = x.numel()
     if x.dtype != torch.float32:
         raise ValueError("x must be float32")
+    px = _dev(x, "x")
     if codes is None:
         codes = torch.empty(n, dtype=torch.int8 if spec & Q_SIGNED else torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty(n_groups(n), dtype=torch.int16, device=x.device)
-    _check(lib().flashopt_quantize(_dev(x, "x"), n, spec, _dev(codes, "codes"),
-                                   _dev(scales, "scales"), _stream(stream)), "flashopt_quantize")
+    pc = _buf(codes, "codes", x.device, (1,), n)
+    ps = _buf(scales, "scales", x.device, (2,), n_groups(n))
+    with torch.cuda.device(x.device):
+        _check(lib().flashopt_quantize(px, n, spec, pc, ps, _stream(stream)), "flashopt_quantize")
     return codes, scales
 
 
 def flashopt_dequantize(codes: torch.Tensor, scales: torch.Tensor, spec: int, out=None, stream=None):
+    """Group-32 dequantize codes with their fp16 scales (int16 bits) into fp32."""
     n = codes.numel()
+    if codes.element_size() != 1:
+        raise ValueError("codes must be int8 or uint8")
+    pc = _dev(codes, "codes")
+    ps = _buf(scales, "scales", codes.device, (2,), n_groups(n))
     if out is None:
         out = torch.empty(n, dtype=torch.float32, device=codes.device)
-    _check(lib().flashopt_dequantize(_dev(codes, "codes"), _dev(scales, "scales"), n, spec,
-                                     _dev(out, "out"), _stream(stream)), "flashopt_dequantize")
+    po = _buf(out, "out", codes.device, (4,), n, float32=True)
+    with torch.cuda.device(codes.device):
+        _check(lib().flashopt_dequantize(pc, ps, n, spec, po, _stream(stream)), "flashopt_dequantize")
     return out
 
 
 # --------------------------------------------------------------- split
 
 def rho_dtype(master_bits: int):
+    if master_bits not in (24, 32):
+        raise ValueError("master_bits must be 24 or 32")
     return {24: torch.int8, 32: torch.int16}[master_bits]
 
 
@@ -189,22 +215,34 @@ def flashopt_split(master: torch.Tensor, master_bits: int, param=None, rho=None,
     n = master.numel()
     if master.dtype != torch.float32:
         raise ValueError("master must be float32")
+    pm = _dev(master, "master")
+    rdt = rho_dtype(master_bits)
     if param is None:
         param = torch.empty(n, dtype=torch.bfloat16, device=master.device)
     if rho is None:
-        rho = torch.empty(n, dtype=rho_dtype(master_bits), device=master.device)
-    _check(lib().flashopt_split(_dev(master, "master"), n, master_bits, _dev(param, "param"),
-                                _dev(rho, "rho"), _stream(stream)), "flashopt_split")
+        rho = torch.empty(n, dtype=rdt, device=master.device)
+    pp = _buf(param, "param", master.device, (2,), n)
+    pr = _buf(rho, "rho", master.device, (rdt.itemsize,), n)
+    with torch.cuda.device(master.device):
+        _check(lib().flashopt_split(pm, n, master_bits, pp, pr, _stream(stream)), "flashopt_split")
     return param, rho
 
 
 def flashopt_reconstruct(param: torch.Tensor, rho: torch.Tensor, master_bits: int, out=None,
                          stream=None):
+    """(bf16 param, rho int8|int16) -> fp32 master."""
     n = param.numel()
+    if param.element_size() != 2:
+        raise ValueError("param must hold bf16 values")
+    rdt = rho_dtype(master_bits)
+    pp = _dev(param, "param")
+    pr = _buf(rho, "rho", param.device, (rdt.itemsize,), n)
     if out is None:
         out = torch.empty(n, dtype=torch.float32, device=param.device)
-    _check(lib().flashopt_reconstruct(_dev(param, "param"), _dev(rho, "rho"), n, master_bits,
-                                      _dev(out, "out"), _stream(stream)), "flashopt_reconstruct")
+    po = _buf(out, "out", param.device, (4,), n, float32=True)
+    with torch.cuda.device(param.device):
+        _check(lib().flashopt_reconstruct(pp, pr, n, master_bits, po, _stream(stream)),
+               "flashopt_reconstruct")
     return out
 
 

@@ -172,3 +172,45 @@ def test_list_launches_on_two_streams_use_their_own_workspaces():
         for name in ("param", "rho", "m_codes", "m_scales", "v_codes", "v_scales"):
             a, b = getattr(x, name), getattr(y, name)
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"tensor {i} {name}"
+
+
+def test_codec_and_split_wrappers_refuse_bad_buffers():
+    """The C ABI takes plain pointers, so the binding checks caller-supplied
+    buffers before it launches anything: a short or mistyped output buffer
+    raises ValueError instead of being written past its end."""
+    require_gpu()
+    n = 1000
+    x = torch.randn(n, device="cuda")
+    ok_codes = torch.empty(n, dtype=torch.int8, device="cuda")
+    ok_scales = torch.empty(F.n_groups(n), dtype=torch.int16, device="cuda")
+    bad = [
+        lambda: F.flashopt_quantize(x, F.SPEC_MOMENTUM, torch.empty(n - 1, dtype=torch.int8, device="cuda"), ok_scales),
+        lambda: F.flashopt_quantize(x, F.SPEC_MOMENTUM, torch.empty(n, dtype=torch.int16, device="cuda"), ok_scales),
+        lambda: F.flashopt_quantize(x, F.SPEC_MOMENTUM, ok_codes, ok_scales[:-1]),
+        lambda: F.flashopt_quantize(x, F.SPEC_MOMENTUM, torch.empty(n, dtype=torch.int8), ok_scales),
+        lambda: F.flashopt_dequantize(ok_codes, ok_scales, F.SPEC_MOMENTUM, torch.empty(n - 1, device="cuda")),
+        lambda: F.flashopt_dequantize(ok_codes, ok_scales, F.SPEC_MOMENTUM,
+                                      torch.empty(n, dtype=torch.float16, device="cuda")),
+        lambda: F.flashopt_dequantize(ok_codes.view(torch.int16), ok_scales, F.SPEC_MOMENTUM),
+        lambda: F.flashopt_dequantize(ok_codes, ok_scales[:-1], F.SPEC_MOMENTUM),
+        lambda: F.flashopt_split(x, 24, rho=torch.empty(n, dtype=torch.int16, device="cuda")[: n // 2]),
+        lambda: F.flashopt_split(x, 24, param=torch.empty(n, dtype=torch.float32, device="cuda")),
+        lambda: F.flashopt_split(x, 32, rho=torch.empty(n, dtype=torch.int8, device="cuda")),
+        lambda: F.flashopt_split(x, 16),
+        lambda: F.flashopt_reconstruct(torch.empty(n, dtype=torch.bfloat16, device="cuda"),
+                                       torch.empty(n - 1, dtype=torch.int8, device="cuda"), 24),
+        lambda: F.flashopt_reconstruct(torch.empty(n, dtype=torch.bfloat16, device="cuda"),
+                                       torch.empty(n, dtype=torch.int8, device="cuda"), 24,
+                                       out=torch.empty(n, dtype=torch.bfloat16, device="cuda")),
+    ]
+    for i, call in enumerate(bad):
+        with pytest.raises(ValueError):
+            call()
+        torch.cuda.synchronize()
+    # the same calls with good buffers run
+    q, s = F.flashopt_quantize(x, F.SPEC_MOMENTUM, ok_codes, ok_scales)
+    F.flashopt_dequantize(q, s, F.SPEC_MOMENTUM)
+    p, r = F.flashopt_split(x, 24)
+    F.flashopt_reconstruct(p, r, 24)
+    torch.cuda.synchronize()
+
