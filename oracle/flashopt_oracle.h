@@ -26,11 +26,14 @@
  * body's operation order is pinned bit for bit by six hand-derived elements
  * whose stored bf16 half and rho change under each plausible reordering.
  * The multi-step values of oracle_adamw_step() with quantized states or the
- * 24-bit master are pinned only by composition of pinned parts (parity
- * unpinned for that composite trajectory itself); with fp32 moments and the
- * 32-bit master a 300-step trajectory is pinned to torch.optim.AdamW within a
- * rounding bound, and the fp32-parameter step equals the lossless 32-bit
- * master step bit for bit.
+ * 24-bit master are pinned by composition of pinned parts; over many steps
+ * they are pinned independently only for groups of equal elements (whose
+ * codes stay +-127 / 255, so the stored moments follow fp16 roundings of
+ * closed form, for AdamW and FlashSGD): parity unpinned for the general
+ * composite trajectory itself.  With fp32 moments and the 32-bit master a
+ * 300-step trajectory is pinned to torch.optim.AdamW within a rounding
+ * bound, and the fp32-parameter step equals the lossless 32-bit master step
+ * bit for bit.
  */
 #ifndef FLASHOPT_ORACLE_H
 #define FLASHOPT_ORACLE_H
