@@ -13,7 +13,8 @@
  *   - Buffer pointers are DEVICE pointers owned by the caller.  The library
  *     never allocates or frees device memory and keeps no state between calls
  *     except a small cache of pinned host staging buffers (see
- *     flashopt_adamw_step).
+ *     flashopt_adamw_step) and the allocation-free step's static table (see
+ *     flashopt_adamw_step_noalloc).
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *     default stream).  Results are visible after the stream is synchronized.
  *     The stream and every buffer belong to the calling thread's current HIP
@@ -50,7 +51,8 @@ typedef enum {
     FLASHOPT_OK = 0,
     FLASHOPT_EINVAL = 1,      /* an argument is out of its documented range      */
     FLASHOPT_EALIGN = 2,      /* a buffer violates the alignment rule above      */
-    FLASHOPT_EWORKSPACE = 3,  /* the workspace is NULL or smaller than required  */
+    FLASHOPT_EWORKSPACE = 3,  /* the workspace or plan buffer is NULL or too small,
+                                 or a list exceeds a fixed table (noalloc)   */
     FLASHOPT_EHIP = 4         /* the HIP runtime reported an error on enqueue    */
 } flashopt_status;
 
