@@ -100,6 +100,38 @@ def test_plan_launch_replays_from_a_hip_graph(variant):
         _assert_same(a, b, f"replay at step {t}")
 
 
+def test_plan_set_step_takes_new_hyper_parameters():
+    """set_step writes any hyper-parameters of the plan's variant: a learning
+    rate schedule and a weight-decay change, through the C-ABI calls, over a
+    list that includes an empty tensor, equal list steps given the same
+    arguments."""
+    require_gpu()
+    sizes = [4096 + 5, 0, 70001, 33]
+    pa = [W.init_param(n, device="cuda", seed=980 + i) for i, n in enumerate(sizes)]
+    a = F.FlashAdamW(pa, **W.HP_DEFAULT)
+    b = F.FlashAdamW([p.clone() for p in pa], **W.HP_DEFAULT)
+    bufs = [torch.zeros(n, dtype=torch.bfloat16, device="cuda") for n in sizes]
+    desc_b = F.descriptor_array(b.states, bufs)
+    plan = torch.empty(F.flashopt_adamw_plan_bytes(len(sizes)), dtype=torch.uint8, device="cuda")
+    schedule = [(1e-3, 0.01), (5e-4, 0.01), (2.5e-4, 0.0), (1e-4, 0.1)]
+    base = {k: v for k, v in W.HP_DEFAULT.items() if k not in ("lr", "weight_decay")}
+    info = None
+    for t, (lr, wd) in enumerate(schedule, start=1):
+        args = F.make_args(t, lr=lr, weight_decay=wd, **base)
+        grads = [W.make_grad(n, t, device="cuda", stream_id=i) for i, n in enumerate(sizes)]
+        F.flashopt_adamw_step(F.descriptor_array(a.states, grads), args, a.workspace(), None)
+        for buf, g in zip(bufs, grads):
+            buf.copy_(g)
+        if info is None:
+            info = F.flashopt_adamw_plan(desc_b, args, plan)
+            assert (info.n_tensors, info.total_chunks) == (len(sizes), sum((n + 1023) // 1024 for n in sizes))
+        else:
+            F.flashopt_adamw_plan_set_step(info, args, plan)
+        F.flashopt_adamw_plan_launch(info, plan)
+        torch.cuda.synchronize()
+        _assert_same(a, b, f"step {t}, lr {lr}, wd {wd}")
+
+
 def test_decoder_8b_graph_replays_equal_list_steps():
     """The whole 8.0B list (290 tensors) stepped twice through one captured
     plan launch (set_step between replays) and twice through the list step
