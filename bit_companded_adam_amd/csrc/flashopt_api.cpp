@@ -52,20 +52,22 @@ size_t table_bytes(int n)
     return (b + 15) & ~static_cast<size_t>(15);
 }
 
-// Staged bytes of a list step: a header, then the table.  The AdamW steps
-// stage their scalar block (kScalarsBytes) as the header, FlashSGD passes
-// its scalars by value and stages none.
+// Staged bytes of a list step: a header (the step's scalar block), then the
+// table.
 size_t staged_bytes(int n, size_t header_bytes)
 {
     return n <= 0 ? 0 : header_bytes + table_bytes(n);
 }
 
-constexpr size_t kAdamwHeader = flashopt::kScalarsBytes;
+constexpr size_t kHeader = flashopt::kScalarsBytes;
 
-// The scalar block of an AdamW step: the StepScalars, zero padded.
-void fill_scalars(const StepScalars &sc, void *dst)
+// The scalar block of a list step: its StepScalars or SgdScalars, zero
+// padded.
+template <typename Sc>
+void fill_scalars(const Sc &sc, void *dst)
 {
-    std::memset(dst, 0, kAdamwHeader);
+    static_assert(sizeof(Sc) <= kHeader, "scalar block");
+    std::memset(dst, 0, kHeader);
     std::memcpy(dst, &sc, sizeof(sc));
 }
 
@@ -319,19 +321,87 @@ flashopt_status stage_and_launch(const flashopt_tensor *tensors, int n_tensors, 
     return hip_status(launch(base, d_desc, d_start, acc, st));
 }
 
-// The plan's variant fields, from step arguments.
-void plan_variant(const flashopt_adamw_args &a, flashopt_adamw_plan_info &info)
+// Plans (the capture-safe list steps): the tables and the scalar block of
+// a list staged once into a caller's device buffer, the scalar block
+// rewritten per step, and launches that only enqueue the kernel.
+
+// Validation of a plan's list, then its scalar block and tables staged into
+// `plan`; n_tensors and total_chunks of the plan go to info.
+template <typename Sc, typename Info>
+flashopt_status make_plan(const flashopt_tensor *tensors, int n_tensors, int master_bits, bool quant,
+                          bool v, const Sc &sc, void *plan, size_t plan_bytes, Info &info,
+                          void *stream)
 {
-    info.master_bits = a.master_bits;
-    info.companded = a.companded;
-    info.fp32_states = a.fp32_states;
-    info.param_fp32 = a.param_fp32;
+    int64_t total = 0;
+    const flashopt_status cs = check_list(tensors, n_tensors, master_bits, quant, v, total);
+    if (cs != FLASHOPT_OK) return cs;
+    const size_t need = staged_bytes(n_tensors, kHeader);
+    if (need > 0 && (!plan || plan_bytes < need)) return FLASHOPT_EWORKSPACE;
+    if (need > 0 && !aligned(plan, 16)) return FLASHOPT_EALIGN;
+    if (need > 0) {
+        const flashopt_status ss = stage_copy(plan, need, static_cast<hipStream_t>(stream), [&](void *host) {
+            fill_scalars(sc, host);
+            (void)fill_table(tensors, n_tensors, static_cast<unsigned char *>(host) + kHeader);
+        });
+        if (ss != FLASHOPT_OK) return ss;
+    }
+    info.n_tensors = n_tensors;
+    info.total_chunks = static_cast<int32_t>(total);
+    return FLASHOPT_OK;
+}
+
+// A new scalar block for a plan of n_tensors tensors.
+template <typename Sc>
+flashopt_status plan_scalars(int n_tensors, const Sc &sc, void *plan, void *stream)
+{
+    if (n_tensors <= 0) return n_tensors == 0 ? FLASHOPT_OK : FLASHOPT_EINVAL;
+    if (!plan) return FLASHOPT_EWORKSPACE;
+    if (!aligned(plan, 16)) return FLASHOPT_EALIGN;
+    return stage_copy(plan, kHeader, static_cast<hipStream_t>(stream),
+                      [&](void *host) { fill_scalars(sc, host); });
+}
+
+// The device pointers of a plan: scalar block, descriptors, chunk starts.
+struct PlanPtrs {
+    const void *scalars;
+    const DevTensor *desc;
+    const int32_t *start;
+};
+
+PlanPtrs plan_ptrs(const void *plan, int n_tensors)
+{
+    const unsigned char *base = static_cast<const unsigned char *>(plan);
+    const DevTensor *d = reinterpret_cast<const DevTensor *>(base + kHeader);
+    return PlanPtrs{base, d, reinterpret_cast<const int32_t *>(d + n_tensors)};
 }
 
 bool same_variant(const flashopt_adamw_args &a, const flashopt_adamw_plan_info &info)
 {
     return info.master_bits == a.master_bits && info.companded == a.companded &&
            info.fp32_states == a.fp32_states && info.param_fp32 == a.param_fp32;
+}
+
+bool same_variant(const flashopt_sgd_args &a, const flashopt_sgd_plan_info &info)
+{
+    return info.master_bits == a.master_bits && info.companded == a.companded &&
+           info.fp32_states == a.fp32_states && info.reserved == 0;
+}
+
+// The launch-time checks shared by both plan kinds: counts, then the buffer.
+flashopt_status plan_launch_checks(int32_t n_tensors, int32_t total_chunks, const void *plan)
+{
+    if (n_tensors < 0 || total_chunks < 0) return FLASHOPT_EINVAL;
+    if (total_chunks == 0) return FLASHOPT_OK;
+    if (n_tensors == 0) return FLASHOPT_EINVAL;
+    if (!plan) return FLASHOPT_EWORKSPACE;
+    if (!aligned(plan, 16)) return FLASHOPT_EALIGN;
+    return FLASHOPT_OK;
+}
+
+bool valid_variant(int master_bits, int companded, int fp32_states)
+{
+    return (master_bits == 24 || master_bits == 32 || master_bits == 0) &&
+           (companded == 0 || companded == 1) && (fp32_states == 0 || fp32_states == 1);
 }
 
 // Host image of the allocation-free step's scalar block and chunk table:
@@ -397,7 +467,7 @@ flashopt_status flashopt_reconstruct(const uint16_t *param_bf16, const void *rho
 size_t flashopt_adamw_workspace_bytes(const flashopt_tensor *tensors, int n_tensors)
 {
     (void)tensors;
-    return staged_bytes(n_tensors, kAdamwHeader);
+    return staged_bytes(n_tensors, kHeader);
 }
 
 flashopt_status flashopt_adamw_step(const flashopt_tensor *tensors, int n_tensors,
@@ -409,10 +479,10 @@ flashopt_status flashopt_adamw_step(const flashopt_tensor *tensors, int n_tensor
     const flashopt_status hs = adamw_scalars(a, sc);
     if (hs != FLASHOPT_OK) return hs;
     const int states = states_of(a->fp32_states, a->companded);
-    alignas(16) unsigned char header[kAdamwHeader];
+    alignas(16) unsigned char header[kHeader];
     fill_scalars(sc, header);
     return stage_and_launch(tensors, n_tensors, a->master_bits, a->fp32_states == 0, true,
-                            header, kAdamwHeader, workspace, ws_bytes, stream,
+                            header, kHeader, workspace, ws_bytes, stream,
                             [&](const unsigned char *h, const DevTensor *d, const int32_t *cs,
                                 int32_t total, hipStream_t st) {
                                 return flashopt::launch_adamw_step(
@@ -454,13 +524,13 @@ flashopt_status flashopt_adamw_step_noalloc(const flashopt_tensor *tensors, int 
     {
         std::lock_guard<std::mutex> lock(g_noalloc_mutex);
         fill_scalars(sc, g_noalloc_table);
-        acc = fill_table(tensors, n_tensors, g_noalloc_table + kAdamwHeader);
-        if (hipMemcpyAsync(scratch, g_noalloc_table, staged_bytes(n_tensors, kAdamwHeader),
+        acc = fill_table(tensors, n_tensors, g_noalloc_table + kHeader);
+        if (hipMemcpyAsync(scratch, g_noalloc_table, staged_bytes(n_tensors, kHeader),
                            hipMemcpyHostToDevice, st) != hipSuccess)
             return FLASHOPT_EHIP;
     }
     const unsigned char *base = static_cast<const unsigned char *>(scratch);
-    const DevTensor *d_desc = reinterpret_cast<const DevTensor *>(base + kAdamwHeader);
+    const DevTensor *d_desc = reinterpret_cast<const DevTensor *>(base + kHeader);
     const int32_t *d_start = reinterpret_cast<const int32_t *>(d_desc + n_tensors);
     return hip_status(flashopt::launch_adamw_step(reinterpret_cast<const StepScalars *>(base), d_desc,
                                                   d_start, n_tensors, acc, kernel_format(*a),
@@ -469,7 +539,7 @@ flashopt_status flashopt_adamw_step_noalloc(const flashopt_tensor *tensors, int 
 
 size_t flashopt_adamw_plan_bytes(int n_tensors)
 {
-    return staged_bytes(n_tensors, kAdamwHeader);
+    return staged_bytes(n_tensors, kHeader);
 }
 
 flashopt_status flashopt_adamw_plan(const flashopt_tensor *tensors, int n_tensors,
@@ -480,26 +550,15 @@ flashopt_status flashopt_adamw_plan(const flashopt_tensor *tensors, int n_tensor
     StepScalars sc;
     const flashopt_status hs = adamw_scalars(a, sc);
     if (hs != FLASHOPT_OK) return hs;
-    int64_t total = 0;
-    const flashopt_status cs = check_list(tensors, n_tensors, a->master_bits, a->fp32_states == 0,
-                                          true, total);
-    if (cs != FLASHOPT_OK) return cs;
-    const size_t need = staged_bytes(n_tensors, kAdamwHeader);
-    if (need > 0 && (!plan || plan_bytes < need)) return FLASHOPT_EWORKSPACE;
-    if (need > 0 && !aligned(plan, 16)) return FLASHOPT_EALIGN;
     flashopt_adamw_plan_info out{};
-    out.n_tensors = n_tensors;
-    out.total_chunks = static_cast<int32_t>(total);
-    plan_variant(*a, out);
-    if (need > 0) {
-        const flashopt_status ss = stage_copy(plan, need, static_cast<hipStream_t>(stream), [&](void *host) {
-            fill_scalars(sc, host);
-            (void)fill_table(tensors, n_tensors, static_cast<unsigned char *>(host) + kAdamwHeader);
-        });
-        if (ss != FLASHOPT_OK) return ss;
-    }
-    *info = out;
-    return FLASHOPT_OK;
+    out.master_bits = a->master_bits;
+    out.companded = a->companded;
+    out.fp32_states = a->fp32_states;
+    out.param_fp32 = a->param_fp32;
+    const flashopt_status ps = make_plan(tensors, n_tensors, a->master_bits, a->fp32_states == 0, true,
+                                         sc, plan, plan_bytes, out, stream);
+    if (ps == FLASHOPT_OK) *info = out;
+    return ps;
 }
 
 flashopt_status flashopt_adamw_plan_set_step(const flashopt_adamw_plan_info *info,
@@ -509,44 +568,33 @@ flashopt_status flashopt_adamw_plan_set_step(const flashopt_adamw_plan_info *inf
     StepScalars sc;
     const flashopt_status hs = adamw_scalars(a, sc);
     if (hs != FLASHOPT_OK) return hs;
-    if (info->n_tensors <= 0) return info->n_tensors == 0 ? FLASHOPT_OK : FLASHOPT_EINVAL;
-    if (!plan) return FLASHOPT_EWORKSPACE;
-    if (!aligned(plan, 16)) return FLASHOPT_EALIGN;
-    return stage_copy(plan, kAdamwHeader, static_cast<hipStream_t>(stream),
-                      [&](void *host) { fill_scalars(sc, host); });
+    return plan_scalars(info->n_tensors, sc, plan, stream);
 }
 
 flashopt_status flashopt_adamw_plan_launch(const flashopt_adamw_plan_info *info, const void *plan,
                                            void *stream)
 {
-    if (!info || info->n_tensors < 0 || info->total_chunks < 0) return FLASHOPT_EINVAL;
+    if (!info) return FLASHOPT_EINVAL;
+    if (!valid_variant(info->master_bits, info->companded, info->fp32_states) ||
+        (info->param_fp32 != 0 && info->param_fp32 != 1) || (info->param_fp32 && info->master_bits != 0))
+        return FLASHOPT_EINVAL;
+    const flashopt_status lc = plan_launch_checks(info->n_tensors, info->total_chunks, plan);
+    if (lc != FLASHOPT_OK || info->total_chunks == 0) return lc;
     flashopt_adamw_args a{};
     a.master_bits = info->master_bits;
-    a.companded = info->companded;
-    a.fp32_states = info->fp32_states;
     a.param_fp32 = info->param_fp32;
-    if ((a.master_bits != 24 && a.master_bits != 32 && a.master_bits != 0) ||
-        (a.companded != 0 && a.companded != 1) || (a.fp32_states != 0 && a.fp32_states != 1) ||
-        (a.param_fp32 != 0 && a.param_fp32 != 1) || (a.param_fp32 && a.master_bits != 0))
-        return FLASHOPT_EINVAL;
-    if (info->total_chunks == 0) return FLASHOPT_OK;
-    if (info->n_tensors == 0) return FLASHOPT_EINVAL;
-    if (!plan) return FLASHOPT_EWORKSPACE;
-    if (!aligned(plan, 16)) return FLASHOPT_EALIGN;
-    const unsigned char *base = static_cast<const unsigned char *>(plan);
-    const DevTensor *d_desc = reinterpret_cast<const DevTensor *>(base + kAdamwHeader);
-    const int32_t *d_start = reinterpret_cast<const int32_t *>(d_desc + info->n_tensors);
-    return hip_status(flashopt::launch_adamw_step(reinterpret_cast<const StepScalars *>(base), d_desc,
-                                                  d_start, info->n_tensors, info->total_chunks,
+    const PlanPtrs p = plan_ptrs(plan, info->n_tensors);
+    return hip_status(flashopt::launch_adamw_step(static_cast<const StepScalars *>(p.scalars), p.desc,
+                                                  p.start, info->n_tensors, info->total_chunks,
                                                   kernel_format(a),
-                                                  states_of(a.fp32_states, a.companded),
+                                                  states_of(info->fp32_states, info->companded),
                                                   static_cast<hipStream_t>(stream)));
 }
 
 size_t flashopt_sgd_workspace_bytes(const flashopt_tensor *tensors, int n_tensors)
 {
     (void)tensors;
-    return staged_bytes(n_tensors, 0);
+    return staged_bytes(n_tensors, kHeader);
 }
 
 flashopt_status flashopt_sgd_step(const flashopt_tensor *tensors, int n_tensors,
@@ -558,13 +606,65 @@ flashopt_status flashopt_sgd_step(const flashopt_tensor *tensors, int n_tensors,
     const flashopt_status hs = sgd_scalars(a, sc);
     if (hs != FLASHOPT_OK) return hs;
     const int states = states_of(a->fp32_states, a->companded);
+    alignas(16) unsigned char header[kHeader];
+    fill_scalars(sc, header);
     return stage_and_launch(tensors, n_tensors, a->master_bits, a->fp32_states == 0, false,
-                            nullptr, 0, workspace, ws_bytes, stream,
-                            [&](const unsigned char *, const DevTensor *d, const int32_t *cs,
+                            header, kHeader, workspace, ws_bytes, stream,
+                            [&](const unsigned char *h, const DevTensor *d, const int32_t *cs,
                                 int32_t total, hipStream_t st) {
-                                return flashopt::launch_sgd_step(d, cs, n_tensors, total, sc,
-                                                                 a->master_bits, states, st);
+                                return flashopt::launch_sgd_step(
+                                    reinterpret_cast<const SgdScalars *>(h), d, cs, n_tensors, total,
+                                    a->master_bits, states, st);
                             });
+}
+
+size_t flashopt_sgd_plan_bytes(int n_tensors)
+{
+    return staged_bytes(n_tensors, kHeader);
+}
+
+flashopt_status flashopt_sgd_plan(const flashopt_tensor *tensors, int n_tensors,
+                                  const flashopt_sgd_args *a, void *plan, size_t plan_bytes,
+                                  flashopt_sgd_plan_info *info, void *stream)
+{
+    if (!info || n_tensors < 0 || (n_tensors > 0 && !tensors)) return FLASHOPT_EINVAL;
+    SgdScalars sc;
+    const flashopt_status hs = sgd_scalars(a, sc);
+    if (hs != FLASHOPT_OK) return hs;
+    flashopt_sgd_plan_info out{};
+    out.master_bits = a->master_bits;
+    out.companded = a->companded;
+    out.fp32_states = a->fp32_states;
+    const flashopt_status ps = make_plan(tensors, n_tensors, a->master_bits, a->fp32_states == 0, false,
+                                         sc, plan, plan_bytes, out, stream);
+    if (ps == FLASHOPT_OK) *info = out;
+    return ps;
+}
+
+flashopt_status flashopt_sgd_plan_set_step(const flashopt_sgd_plan_info *info,
+                                           const flashopt_sgd_args *a, void *plan, void *stream)
+{
+    if (!info || !a || !same_variant(*a, *info)) return FLASHOPT_EINVAL;
+    SgdScalars sc;
+    const flashopt_status hs = sgd_scalars(a, sc);
+    if (hs != FLASHOPT_OK) return hs;
+    return plan_scalars(info->n_tensors, sc, plan, stream);
+}
+
+flashopt_status flashopt_sgd_plan_launch(const flashopt_sgd_plan_info *info, const void *plan,
+                                         void *stream)
+{
+    if (!info) return FLASHOPT_EINVAL;
+    if (!valid_variant(info->master_bits, info->companded, info->fp32_states) || info->reserved != 0)
+        return FLASHOPT_EINVAL;
+    const flashopt_status lc = plan_launch_checks(info->n_tensors, info->total_chunks, plan);
+    if (lc != FLASHOPT_OK || info->total_chunks == 0) return lc;
+    const PlanPtrs p = plan_ptrs(plan, info->n_tensors);
+    return hip_status(flashopt::launch_sgd_step(static_cast<const SgdScalars *>(p.scalars), p.desc,
+                                                p.start, info->n_tensors, info->total_chunks,
+                                                info->master_bits,
+                                                states_of(info->fp32_states, info->companded),
+                                                static_cast<hipStream_t>(stream)));
 }
 
 flashopt_status flashopt_sgd_step_tensor(const flashopt_tensor *tensor,

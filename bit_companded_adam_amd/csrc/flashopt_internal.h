@@ -67,11 +67,11 @@ struct StepScalars {
     int fast;           // 1 when eps lets the short route absorb vhat = 0 and subnormal vhat (eps >= 2^-38)
     int unit_bc;        // 1 when bc1 and bc2 are both exactly 1 (late in training)
 };
-// The list AdamW kernels read their StepScalars from device memory: a block
-// of kScalarsBytes at the start of the staged table (the workspace, the
-// allocation-free scratch array or a caller's plan), written by the same
-// host-to-device copy as the table or by a later one, so that a launch can
-// be captured once and replayed with new scalars.
+// The list step kernels (AdamW and FlashSGD) read their scalars from device
+// memory: a block of kScalarsBytes at the start of the staged table (the
+// workspace, the allocation-free scratch array or a caller's plan), written
+// by the same host-to-device copy as the table or by a later one, so that a
+// launch can be captured once and replayed with new scalars.
 constexpr size_t kScalarsBytes = 128;
 static_assert(sizeof(StepScalars) <= kScalarsBytes, "scalar block");
 // fp32 scalars of one FlashSGD step (SGD with momentum), formed in double
@@ -85,6 +85,7 @@ struct SgdScalars {
     int first;      // step == 1: the buffer is set to the gradient
     int nesterov;
 };
+static_assert(sizeof(SgdScalars) <= kScalarsBytes, "scalar block");
 
 // Allocation-free list step: its scalar block and chunk table (up to
 // kScratchTensors descriptors, then their chunk starts) live in a device
@@ -110,10 +111,9 @@ hipError_t launch_reconstruct(const uint16_t *param, const void *rho, int64_t n,
 hipError_t launch_adamw_step(const StepScalars *scalars, const DevTensor *tensors,
                              const int32_t *chunk_start, int n_tensors, int32_t total_chunks,
                              int master_bits, int states, hipStream_t stream);
-hipError_t launch_sgd_step(const DevTensor *tensors, const int32_t *chunk_start,
-                           int n_tensors, int32_t total_chunks,
-                           const SgdScalars &sc, int master_bits, int states,
-                           hipStream_t stream);
+hipError_t launch_sgd_step(const SgdScalars *scalars, const DevTensor *tensors,
+                           const int32_t *chunk_start, int n_tensors, int32_t total_chunks,
+                           int master_bits, int states, hipStream_t stream);
 // One tensor, its descriptor passed in the kernel arguments (no workspace).
 hipError_t launch_adamw_tensor(const DevTensor &d, const StepScalars &sc, int master_bits,
                                int states, hipStream_t stream);

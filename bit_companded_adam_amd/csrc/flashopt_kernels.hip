@@ -1405,12 +1405,15 @@ adamw_step_kernel(const StepScalars *__restrict__ scalars, const DevTensor *__re
     });
 }
 
-// The fused FlashSGD step (same grid and tables, momentum only).
+// The fused FlashSGD step (same grid and tables, momentum only; scalars read
+// from the staged table like the AdamW step's).
 template <int MB, int ST>
 __global__ void __launch_bounds__(kBlockThreads)
-sgd_step_kernel(const DevTensor *__restrict__ tensors, const int32_t *__restrict__ chunk_start,
-                int n_tensors, int32_t total_chunks, int32_t run, SgdScalars sc)
+sgd_step_kernel(const SgdScalars *__restrict__ scalars, const DevTensor *__restrict__ tensors,
+                const int32_t *__restrict__ chunk_start, int n_tensors, int32_t total_chunks,
+                int32_t run)
 {
+    const SgdScalars sc = *scalars;
     constexpr unsigned kMSpec =
         ST == kStatesCompanded ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
     constexpr int kN = unit_elems(MB, ST);
@@ -1616,12 +1619,12 @@ hipError_t step_variant(const DevTensor *tensors, const int32_t *chunk_start, in
 
 template <int MB, int ST>
 hipError_t sgd_variant(const DevTensor *tensors, const int32_t *chunk_start, int n_tensors,
-                       int32_t total_chunks, const SgdScalars &sc, hipStream_t st)
+                       int32_t total_chunks, const SgdScalars *scalars, hipStream_t st)
 {
     const int32_t run = chunks_per_wave();
     hipLaunchKernelGGL((sgd_step_kernel<MB, ST>), dim3(step_grid(total_chunks, run)),
-                       dim3(kBlockThreads), 0, st, tensors, chunk_start, n_tensors,
-                       total_chunks, run, sc);
+                       dim3(kBlockThreads), 0, st, scalars, tensors, chunk_start, n_tensors,
+                       total_chunks, run);
     return hipGetLastError();
 }
 
@@ -1670,9 +1673,9 @@ template <int MB, int ST>
 struct SgdLaunch {
     static constexpr bool kFp32Params = false;
     static hipError_t run(const DevTensor *t, const int32_t *cs, int n, int32_t total,
-                          const SgdScalars &sc, hipStream_t st)
+                          const SgdScalars *scalars, hipStream_t st)
     {
-        return sgd_variant<MB, ST>(t, cs, n, total, sc, st);
+        return sgd_variant<MB, ST>(t, cs, n, total, scalars, st);
     }
 };
 
@@ -1745,13 +1748,13 @@ hipError_t launch_adamw_step(const StepScalars *scalars, const DevTensor *tensor
                                  total_chunks, scalars, st);
 }
 
-hipError_t launch_sgd_step(const DevTensor *tensors, const int32_t *chunk_start, int n_tensors,
-                           int32_t total_chunks, const SgdScalars &sc, int master_bits,
-                           int states, hipStream_t st)
+hipError_t launch_sgd_step(const SgdScalars *scalars, const DevTensor *tensors,
+                           const int32_t *chunk_start, int n_tensors, int32_t total_chunks,
+                           int master_bits, int states, hipStream_t st)
 {
     if (total_chunks <= 0) return hipSuccess;
     return dispatch<SgdLaunch>(master_bits, states, tensors, chunk_start, n_tensors,
-                               total_chunks, sc, st);
+                               total_chunks, scalars, st);
 }
 
 hipError_t launch_adamw_tensor(const DevTensor &d, const StepScalars &sc, int master_bits,

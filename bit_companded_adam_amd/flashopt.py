@@ -32,7 +32,9 @@ EXPORTS = ("flashopt_quantize", "flashopt_dequantize", "flashopt_split",
            "flashopt_adamw_step", "flashopt_adamw_step_tensor", "flashopt_sgd_workspace_bytes",
            "flashopt_sgd_step", "flashopt_sgd_step_tensor", "flashopt_status_str",
            "flashopt_abi_version", "flashopt_adamw_step_noalloc", "flashopt_adamw_plan_bytes",
-           "flashopt_adamw_plan", "flashopt_adamw_plan_set_step", "flashopt_adamw_plan_launch")
+           "flashopt_adamw_plan", "flashopt_adamw_plan_set_step", "flashopt_adamw_plan_launch",
+           "flashopt_sgd_plan_bytes", "flashopt_sgd_plan", "flashopt_sgd_plan_set_step",
+           "flashopt_sgd_plan_launch")
 
 
 class FlashoptError(RuntimeError):
@@ -68,6 +70,12 @@ class flashopt_sgd_args(ctypes.Structure):
                 ("step", ctypes.c_int64), ("master_bits", ctypes.c_int),
                 ("companded", ctypes.c_int), ("fp32_states", ctypes.c_int),
                 ("nesterov", ctypes.c_int)]
+
+
+class flashopt_sgd_plan_info(ctypes.Structure):
+    _fields_ = [("n_tensors", ctypes.c_int32), ("total_chunks", ctypes.c_int32),
+                ("master_bits", ctypes.c_int32), ("companded", ctypes.c_int32),
+                ("fp32_states", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -109,6 +117,14 @@ def lib() -> ctypes.CDLL:
         L.flashopt_adamw_plan_set_step.argtypes = [ctypes.POINTER(flashopt_adamw_plan_info),
                                                    ctypes.POINTER(flashopt_adamw_args), vp, vp]
         L.flashopt_adamw_plan_launch.argtypes = [ctypes.POINTER(flashopt_adamw_plan_info), vp, vp]
+        L.flashopt_sgd_plan_bytes.argtypes = [i]
+        L.flashopt_sgd_plan_bytes.restype = ctypes.c_size_t
+        L.flashopt_sgd_plan.argtypes = [ctypes.POINTER(flashopt_tensor), i,
+                                        ctypes.POINTER(flashopt_sgd_args), vp, ctypes.c_size_t,
+                                        ctypes.POINTER(flashopt_sgd_plan_info), vp]
+        L.flashopt_sgd_plan_set_step.argtypes = [ctypes.POINTER(flashopt_sgd_plan_info),
+                                                 ctypes.POINTER(flashopt_sgd_args), vp, vp]
+        L.flashopt_sgd_plan_launch.argtypes = [ctypes.POINTER(flashopt_sgd_plan_info), vp, vp]
         L.flashopt_status_str.argtypes = [i]
         L.flashopt_status_str.restype = ctypes.c_char_p
         L.flashopt_abi_version.argtypes = []
@@ -116,7 +132,8 @@ def lib() -> ctypes.CDLL:
                      "flashopt_reconstruct", "flashopt_adamw_step", "flashopt_sgd_step",
                      "flashopt_adamw_step_tensor", "flashopt_sgd_step_tensor",
                      "flashopt_adamw_step_noalloc", "flashopt_adamw_plan",
-                     "flashopt_adamw_plan_set_step", "flashopt_adamw_plan_launch"):
+                     "flashopt_adamw_plan_set_step", "flashopt_adamw_plan_launch",
+                     "flashopt_sgd_plan", "flashopt_sgd_plan_set_step", "flashopt_sgd_plan_launch"):
             getattr(L, name).restype = i
         _lib = L
     return _lib
@@ -355,14 +372,39 @@ def flashopt_adamw_plan_launch(info: flashopt_adamw_plan_info, plan: torch.Tenso
            "flashopt_adamw_plan_launch")
 
 
+def flashopt_sgd_plan_bytes(n_tensors: int) -> int:
+    return lib().flashopt_sgd_plan_bytes(n_tensors)
+
+
+def flashopt_sgd_plan(descriptors, args, plan: torch.Tensor, stream=None) -> flashopt_sgd_plan_info:
+    """flashopt_adamw_plan for the FlashSGD step."""
+    info = flashopt_sgd_plan_info()
+    _check(lib().flashopt_sgd_plan(descriptors, len(descriptors), ctypes.byref(args),
+                                   _dev(plan, "plan"), plan.numel() * plan.element_size(),
+                                   ctypes.byref(info), _stream(stream)),
+           "flashopt_sgd_plan")
+    return info
+
+
+def flashopt_sgd_plan_set_step(info: flashopt_sgd_plan_info, args, plan: torch.Tensor, stream=None):
+    _check(lib().flashopt_sgd_plan_set_step(ctypes.byref(info), ctypes.byref(args),
+                                            _dev(plan, "plan"), _stream(stream)),
+           "flashopt_sgd_plan_set_step")
+
+
+def flashopt_sgd_plan_launch(info: flashopt_sgd_plan_info, plan: torch.Tensor, stream=None):
+    _check(lib().flashopt_sgd_plan_launch(ctypes.byref(info), _dev(plan, "plan"), _stream(stream)),
+           "flashopt_sgd_plan_launch")
+
+
 class StepPlan:
-    """The capture-safe list step of a FlashAdamW over fixed gradient
-    buffers (flashopt_adamw_plan): launch() enqueues the step kernel only, so
-    it can be recorded into a CUDA/HIP graph, and set_step(t), called outside
-    any capture before a launch or replay, writes the scalars of step t that
-    it uses.  The plan keeps references to the gradient tensors (their
-    addresses are in its table) and does not change the optimizer's step
-    counts."""
+    """The capture-safe list step of a FlashAdamW or FlashSGD over fixed
+    gradient buffers (flashopt_adamw_plan / flashopt_sgd_plan): launch()
+    enqueues the step kernel only, so it can be recorded into a CUDA/HIP
+    graph, and set_step(t), called outside any capture before a launch or
+    replay, writes the scalars of step t that it uses.  The plan keeps
+    references to the gradient tensors (their addresses are in its table)
+    and does not change the optimizer's step counts."""
 
     def __init__(self, opt, grads, step: int, stream=None):
         grads = list(grads)
@@ -370,21 +412,22 @@ class StepPlan:
             raise ValueError(f"{len(grads)} gradients for {len(opt.states)} parameters")
         self.opt = opt
         self.grads = grads
+        self._bytes, self._plan, self._set, self._launch = opt._plan_calls
         desc = descriptor_array(opt.states, grads)
         with torch.cuda.device(opt.device):
-            self.buffer = torch.empty(max(16, flashopt_adamw_plan_bytes(len(desc))), dtype=torch.uint8,
+            self.buffer = torch.empty(max(16, self._bytes(len(desc))), dtype=torch.uint8,
                                       device=opt.device or "cuda")
-            self.info = flashopt_adamw_plan(desc, make_args(step, **opt.hp), self.buffer, stream)
+            self.info = self._plan(desc, opt._args(step), self.buffer, stream)
         self.t = step
 
     def set_step(self, t: int, stream=None):
         with torch.cuda.device(self.opt.device):
-            flashopt_adamw_plan_set_step(self.info, make_args(t, **self.opt.hp), self.buffer, stream)
+            self._set(self.info, self.opt._args(t), self.buffer, stream)
         self.t = t
 
     def launch(self, stream=None):
         with torch.cuda.device(self.opt.device):
-            flashopt_adamw_plan_launch(self.info, self.buffer, stream)
+            self._launch(self.info, self.buffer, stream)
 
 
 class _Stepper:
@@ -458,6 +501,11 @@ class _Stepper:
             for t, ds in by_t.items():
                 arr = (flashopt_tensor * len(ds))(*ds)
                 self._list_step(arr, t, stream)
+
+    def plan(self, grads, step: int, stream=None) -> "StepPlan":
+        """A capture-safe list step over these gradient buffers, with the
+        scalars of `step` staged (StepPlan)."""
+        return StepPlan(self, grads, step, stream)
 
     def _check_stream(self, stream):
         dev = getattr(stream, "device", None)
@@ -552,10 +600,12 @@ class FlashAdamW(_Stepper):
     def _list_step(self, desc, t, stream):
         flashopt_adamw_step(desc, make_args(t, **self.hp), self.workspace(stream), stream)
 
-    def plan(self, grads, step: int, stream=None) -> StepPlan:
-        """A capture-safe list step over these gradient buffers, with the
-        scalars of `step` staged (StepPlan)."""
-        return StepPlan(self, grads, step, stream)
+    def _args(self, t):
+        return make_args(t, **self.hp)
+
+    # (a tuple of plain functions: looked up on an instance, they stay unbound)
+    _plan_calls = (flashopt_adamw_plan_bytes, flashopt_adamw_plan, flashopt_adamw_plan_set_step,
+                   flashopt_adamw_plan_launch)
 
     def _tensor_step(self, desc, t, stream):
         flashopt_adamw_step_tensor(desc, make_args(t, **self.hp), stream)
@@ -605,6 +655,12 @@ class FlashSGD(_Stepper):
 
     def _list_step(self, desc, t, stream):
         flashopt_sgd_step(desc, make_sgd_args(t, **self.hp), self.workspace(stream), stream)
+
+    def _args(self, t):
+        return make_sgd_args(t, **self.hp)
+
+    _plan_calls = (flashopt_sgd_plan_bytes, flashopt_sgd_plan, flashopt_sgd_plan_set_step,
+                   flashopt_sgd_plan_launch)
 
     def _tensor_step(self, desc, t, stream):
         flashopt_sgd_step_tensor(desc, make_sgd_args(t, **self.hp), stream)

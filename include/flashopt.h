@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FLASHOPT_ABI_VERSION 6
+#define FLASHOPT_ABI_VERSION 7
 
 typedef enum {
     FLASHOPT_OK = 0,
@@ -308,6 +308,33 @@ flashopt_status flashopt_sgd_step(const flashopt_tensor *tensors, int n_tensors,
                                   const flashopt_sgd_args *args,
                                   void *workspace, size_t workspace_bytes,
                                   void *stream);
+
+/* The capture-safe form of flashopt_sgd_step, with the contract of the
+ * flashopt_adamw_plan calls above: flashopt_sgd_plan stages the scalars of
+ * args and the tables into `plan` (flashopt_sgd_plan_bytes(n) bytes) and
+ * fills *info; flashopt_sgd_plan_set_step rewrites the scalars (any step and
+ * hyper-parameters; master_bits, companded and fp32_states must equal the
+ * plan's); flashopt_sgd_plan_launch enqueues the kernel only and can be
+ * captured into a graph.
+ * Errors: as flashopt_sgd_step (EWORKSPACE for a NULL or short plan; EINVAL
+ * also for a NULL info, a variant mismatch or a nonzero info->reserved). */
+size_t flashopt_sgd_plan_bytes(int n_tensors);
+typedef struct {
+    int32_t n_tensors;        /* tensors in the plan's table                  */
+    int32_t total_chunks;     /* their 1024-element chunks                    */
+    int32_t master_bits;      /* the variant fields of the planning args      */
+    int32_t companded;
+    int32_t fp32_states;
+    int32_t reserved;         /* 0                                            */
+} flashopt_sgd_plan_info;
+flashopt_status flashopt_sgd_plan(const flashopt_tensor *tensors, int n_tensors,
+                                  const flashopt_sgd_args *args, void *plan, size_t plan_bytes,
+                                  flashopt_sgd_plan_info *info, void *stream);
+flashopt_status flashopt_sgd_plan_set_step(const flashopt_sgd_plan_info *info,
+                                           const flashopt_sgd_args *args, void *plan,
+                                           void *stream);
+flashopt_status flashopt_sgd_plan_launch(const flashopt_sgd_plan_info *info, const void *plan,
+                                         void *stream);
 
 /* One tensor's FlashAdamW / FlashSGD step without a workspace: the
  * descriptor travels in the kernel arguments, so the call stages nothing and

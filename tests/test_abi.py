@@ -233,6 +233,52 @@ def test_plan_validation(L):
     assert L.flashopt_adamw_plan_launch(None, A16, None) == F.FLASHOPT_EINVAL
 
 
+def test_sgd_plan_validation(L):
+    """The FlashSGD plan calls validate like flashopt_sgd_step, before any
+    HIP call."""
+    info = F.flashopt_sgd_plan_info()
+
+    def plan(tensors, a=None, buf=A16, nbytes=1 << 20, inf=info):
+        arr = (F.flashopt_tensor * max(1, len(tensors)))(*tensors)
+        return L.flashopt_sgd_plan(arr if tensors else None, len(tensors),
+                                   ctypes.byref(a or F.make_sgd_args(1)), buf, nbytes,
+                                   ctypes.byref(inf) if inf is not None else None, None)
+
+    assert L.flashopt_sgd_plan_bytes(0) == 0
+    assert L.flashopt_sgd_plan_bytes(5) == F.flashopt_sgd_workspace_bytes(5)
+    sgd_tensor = lambda **kw: _tensor(v_codes=None, v_scales=None, **kw)
+    assert plan([sgd_tensor()], inf=None) == F.FLASHOPT_EINVAL
+    assert plan([sgd_tensor()], F.make_sgd_args(1, momentum=0.0)) == F.FLASHOPT_EINVAL
+    assert plan([sgd_tensor()], F.make_sgd_args(1, nesterov=True, dampening=0.1)) == F.FLASHOPT_EINVAL
+    assert plan([sgd_tensor(m_codes=None)]) == F.FLASHOPT_EINVAL
+    assert plan([sgd_tensor()], buf=None) == F.FLASHOPT_EWORKSPACE
+    assert plan([sgd_tensor()], nbytes=L.flashopt_sgd_plan_bytes(1) - 1) == F.FLASHOPT_EWORKSPACE
+    assert plan([sgd_tensor()], buf=A16 + 8) == F.FLASHOPT_EALIGN
+    assert plan([]) == F.FLASHOPT_OK and (info.n_tensors, info.total_chunks) == (0, 0)
+
+    good = F.flashopt_sgd_plan_info(1, 4, 24, 1, 0, 0)
+    set_step = lambda inf, a, buf=A16: L.flashopt_sgd_plan_set_step(
+        ctypes.byref(inf) if inf is not None else None, ctypes.byref(a), buf, None)
+    assert set_step(good, F.make_sgd_args(3, master_bits=32)) == F.FLASHOPT_EINVAL
+    assert set_step(good, F.make_sgd_args(3, companded=False)) == F.FLASHOPT_EINVAL
+    assert set_step(good, F.make_sgd_args(3, quantize_states=False)) == F.FLASHOPT_EINVAL
+    assert set_step(F.flashopt_sgd_plan_info(1, 4, 24, 1, 0, 7), F.make_sgd_args(3)) == F.FLASHOPT_EINVAL
+    assert set_step(None, F.make_sgd_args(3)) == F.FLASHOPT_EINVAL
+    assert set_step(good, F.make_sgd_args(0)) == F.FLASHOPT_EINVAL
+    assert set_step(good, F.make_sgd_args(3), buf=None) == F.FLASHOPT_EWORKSPACE
+    assert set_step(good, F.make_sgd_args(3), buf=A16 + 8) == F.FLASHOPT_EALIGN
+
+    def launch(fields, buf=A16):
+        return L.flashopt_sgd_plan_launch(ctypes.byref(F.flashopt_sgd_plan_info(*fields)), buf, None)
+    for bad in ((1, 4, 16, 1, 0, 0), (1, 4, 24, 2, 0, 0), (1, 4, 24, 1, 2, 0), (1, 4, 24, 1, 0, 1),
+                (1, 4, 1, 1, 0, 0), (-1, 4, 24, 1, 0, 0), (1, -4, 24, 1, 0, 0), (0, 4, 24, 1, 0, 0)):
+        assert launch(bad) == F.FLASHOPT_EINVAL, bad
+    assert launch((1, 4, 24, 1, 0, 0), buf=None) == F.FLASHOPT_EWORKSPACE
+    assert launch((1, 4, 24, 1, 0, 0), buf=A16 + 8) == F.FLASHOPT_EALIGN
+    assert launch((1, 0, 24, 1, 0, 0)) == F.FLASHOPT_OK
+    assert L.flashopt_sgd_plan_launch(None, A16, None) == F.FLASHOPT_EINVAL
+
+
 def test_binding_refuses_host_tensors(L):
     import torch
     with pytest.raises(ValueError):
@@ -264,7 +310,7 @@ def test_sgd_step_validation(L):
     assert sgd([_tensor(m_scales=None)], F.make_sgd_args(1, quantize_states=False),
                ws_bytes=0) == F.FLASHOPT_EWORKSPACE
     assert sgd([_tensor(m_codes=A16 + 8)], F.make_sgd_args(1), ws_bytes=0) == F.FLASHOPT_EALIGN
-    assert F.flashopt_sgd_workspace_bytes(3) + 128 == F.flashopt_adamw_workspace_bytes(3)   # AdamW stages its scalars
+    assert F.flashopt_sgd_workspace_bytes(3) == F.flashopt_adamw_workspace_bytes(3)   # both stage a scalar block
 
 
 def test_single_tensor_validation(L):

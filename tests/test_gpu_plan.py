@@ -1,10 +1,11 @@
-"""The capture-safe list step (flashopt_adamw_plan, _plan_set_step,
-_plan_launch; FlashAdamW.plan in the binding).  A plan launch must leave the
-bits flashopt_adamw_step leaves with the same tensors, gradients and step
-(the list step is checked against the oracle elsewhere, so equality carries
-that parity over), and a launch captured once into a HIP graph must replay
-with the scalars each set_step wrote: every replay equals an eager list step
-at its own step count."""
+"""The capture-safe list steps (flashopt_adamw_plan / flashopt_sgd_plan,
+_plan_set_step, _plan_launch; FlashAdamW.plan and FlashSGD.plan in the
+binding).  A plan launch must leave the bits the list step
+(flashopt_adamw_step / flashopt_sgd_step) leaves with the same tensors,
+gradients and step (the list steps are checked against the oracle elsewhere,
+so equality carries that parity over), and a launch captured once into a HIP
+graph must replay with the scalars each set_step wrote: every replay equals
+an eager list step at its own step count."""
 import pytest
 import torch
 
@@ -160,3 +161,65 @@ def test_decoder_8b_graph_replays_equal_list_steps():
         torch.cuda.synchronize()
         _assert_same(a, b, f"8.0B list, step {t}")
 
+
+
+SGD_VARIANTS = [(24, True, True, dict(weight_decay=0.0)), (32, False, True, dict(weight_decay=0.01)),
+                (None, True, False, dict(nesterov=True, weight_decay=0.01)),
+                (24, True, True, dict(dampening=0.1))]
+SGD_IDS = ["mb24-comp", "mb32-lin-wd", "mbNone-f32-nesterov", "mb24-comp-dampening"]
+
+
+def _sgd_pair(variant, seed):
+    mb, comp, qs, extra = variant
+    pa = [W.init_param(n, device="cuda", seed=seed + i) for i, n in enumerate(SIZES)]
+    pb = [p.clone() for p in pa]
+    make = lambda ps: F.FlashSGD(ps, master_bits=mb, companded=comp, quantize_states=qs,
+                                 **dict(W.SGD_DEFAULT, **extra))
+    return make(pa), make(pb)
+
+
+@pytest.mark.parametrize("variant", SGD_VARIANTS, ids=SGD_IDS)
+def test_sgd_plan_launch_equals_list_step(variant):
+    """FlashSGD: step 1 (the buffer set to the gradient) and steps 2..4
+    through a plan launch and through the list step."""
+    require_gpu()
+    a, b = _sgd_pair(variant, 1100)
+    bufs = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for n in SIZES]
+    plan = b.plan(bufs, step=1)
+    for t in (1, 2, 3, 4):
+        grads = _grads(t, torch.bfloat16)
+        a.step(grads)
+        for buf, g in zip(bufs, grads):
+            buf.copy_(g)
+        if t != 1:
+            plan.set_step(t)
+        plan.launch()
+        torch.cuda.synchronize()
+        _assert_same(a, b, f"sgd step {t}")
+
+
+def test_sgd_plan_launch_replays_from_a_hip_graph():
+    """FlashSGD: one captured plan launch replayed at steps 1..4 (the first
+    replay takes the first-step branch from the scalars set_step wrote), eager
+    work between replays; every replay equals the list step."""
+    require_gpu()
+    a, b = _sgd_pair(SGD_VARIANTS[2], 1150)
+    bufs = [torch.zeros(n, dtype=torch.bfloat16, device="cuda") for n in SIZES]
+    plan = b.plan(bufs, step=2)
+    side = torch.randn(1 << 20, device="cuda")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan.launch()
+    torch.cuda.synchronize()
+    _assert_same(a, b, "after capture")
+    for t in (1, 2, 3, 4):
+        grads = _grads(t, torch.bfloat16)
+        a.step(grads)
+        for buf, g in zip(bufs, grads):
+            buf.copy_(g)
+        plan.set_step(t)
+        graph.replay()
+        side.mul_(1.0001).add_(t)
+        torch.cuda.synchronize()
+        _assert_same(a, b, f"sgd replay at step {t}")
