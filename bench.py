@@ -390,13 +390,15 @@ def bench_codec(n: int, reps: int, warmup: int):
         ("flashopt_reconstruct", "32-bit", 8.0,
          lambda: F.flashopt_reconstruct(param, rho[32], 32, out)),
     ]
-    # context: plain torch streams over the same n-element fp32 buffers -- a
-    # write-only fill and a read + write negation -- to show the memory
-    # system's ceilings for the shapes above (dequantize writes 4 of its 5.06
-    # bytes per element)
+    # context: plain torch streams over the same n-element buffers -- a
+    # write-only fill, a read + write negation, and a uint8 -> fp32
+    # conversion, which has dequantize's mix (1 byte read, 4 written per
+    # element) -- to show the memory system's ceilings for the shapes above
     cases += [
         ("reference: torch fill_ (write-only)", "fp32", 4.0, lambda: out.fill_(0.5)),
         ("reference: torch neg (read + write)", "fp32", 8.0, lambda: torch.neg(x, out=out)),
+        ("reference: torch uint8 to fp32 copy_", "u8->f32", 5.0,
+         lambda: out.copy_(codes.view(torch.uint8))),
     ]
     stream = torch.cuda.current_stream()
     for op, variant, bpe, fn in cases:

@@ -7,10 +7,10 @@
 
 namespace flashopt {
 
-// Work decomposition: one wavefront (64 lanes) owns a 1024-element chunk, 16
-// elements per lane (processed in units of consecutive elements, see the
-// kernels); quantization groups are 32 elements; a 256-thread workgroup runs
-// four wavefronts.
+// Work decomposition: 1024-element chunks, 16 elements per lane of a
+// 64-lane wavefront, processed in units of consecutive elements (the step
+// kernels give each wavefront one unit, see the kernels); quantization
+// groups are 32 elements; a 256-thread workgroup runs four wavefronts.
 constexpr int kLaneElems = 16;
 constexpr int kWaveLanes = 64;
 constexpr int kChunkElems = kLaneElems * kWaveLanes;   // 1024

@@ -6,18 +6,19 @@
 // FlashAdamWSim.step(), bytes_per_param), "code/gpu/equivalence.py" (bf16
 // parameter and correction bits, eq_ecc()).
 //
-// Layout of the work: a wavefront owns a 1024-element chunk (the
-// multi-tensor steps renumber their workgroups so that each XCD streams one
-// contiguous region) and each lane 16 elements of it, taken as
-// units of N consecutive elements placed so that every memory instruction of
-// the wavefront covers one contiguous block of each stream (unit u of lane l
-// starts at element 64 N u + N l).  The quantized steps use N = 8 (a lane
-// quad owns a 32-element group; its maximum takes two DPP exchanges); fp32
-// states and the codec and split kernels use N = 4 (quantize's group
-// maximum spans 8 lanes).  The path is elementwise, so there is no MFMA; LDS
-// holds only the two 256-entry dequantization tables (compile-time constants
-// copied in per workgroup), and the list steps' scalar block and per-tensor
-// chunk table are read with scalar loads.
+// Layout of the work: tensors are cut into 1024-element chunks, each lane
+// taking 16 elements of a chunk as units of N consecutive elements placed so
+// that every memory instruction of a wavefront covers one contiguous block
+// of each stream (unit u of lane l starts at element 64 N u + N l).  The
+// codec and split kernels give a wavefront a whole chunk; the step kernels
+// give it one unit of one chunk (the multi-tensor steps renumber their
+// workgroups so that each XCD streams one contiguous region).  The
+// quantized steps use N = 8 (a lane quad owns a 32-element group; its
+// maximum takes two DPP exchanges); fp32 states and the codec and split
+// kernels use N = 4 (quantize's group maximum spans 8 lanes).  The path is
+// elementwise, so there is no MFMA; LDS holds only the two 256-entry
+// dequantization tables (built per workgroup), and the list steps' scalar
+// block and per-tensor chunk table are read with scalar loads.
 //
 // Arithmetic: fp32, one IEEE rounding per operation in the written order
 // (built with -ffp-contract=off, fp32 and fp16 denormals preserved), so the
@@ -130,39 +131,42 @@ __device__ __forceinline__ int32_t shalf(const uint32_t (&w)[W], int j)
 }
 
 // Dequantization before the scale: y = q/127 or q/255, then the softsign
-// inverse y / (2 - |y|) (dequantize()).  The 256 entries of each spec are
-// constants, evaluated at compile time with these fp32 operations (constant
-// evaluation rounds each one to nearest even, as the device does); every
-// workgroup copies the tables it uses into LDS.
-template <unsigned SPEC>
-struct DequantTable {
-    float v[256];
-};
-
-template <unsigned SPEC>
-constexpr DequantTable<SPEC> make_dequant_table()
-{
-    constexpr bool kSigned = (SPEC & FLASHOPT_Q_SIGNED) != 0;
-    DequantTable<SPEC> t{};
-    for (int c = 0; c < 256; ++c) {
-        const float q = kSigned ? static_cast<float>(static_cast<int8_t>(c)) : static_cast<float>(c);
-        float y = q / (kSigned ? 127.0f : 255.0f);
-        if (SPEC & FLASHOPT_Q_SOFTSIGN) {
-            const float den = 2.0f - (y < 0.0f ? -y : y);
-            y = y / den;
-        }
-        t.v[c] = y;
-    }
-    return t;
-}
-
-template <unsigned SPEC>
-__device__ const DequantTable<SPEC> kDequantTable = make_dequant_table<SPEC>();
+// inverse y / (2 - |y|) (dequantize()), each operation correctly rounded.
+// Every workgroup evaluates the 256 entries of the specs it uses into LDS,
+// one entry per thread, before its barrier, so the evaluation must be short:
+// it uses multiplies and FMAs only, no division sequence and no load.
+//  * q / D: y0 = q R with R = RN(1/D), then one Markstein correction,
+//    y = y0 + (q - D y0) R.
+//  * y / den with den = 2 - |y|: a reciprocal x of den from the linear
+//    estimate 48/17 - 32/17 (den/2) of 1/(den/2) and three Newton steps,
+//    then the same correction, z = z0 + (y - den z0) x with z0 = y x.
+// Both give the correctly rounded quotient for every code of every spec,
+// as an exact (rational) evaluation of each rounding shows; the tests
+// repeat that check.
+constexpr float kRecipLin0 = 0x1.69696ap+1f;   // 48/17 in fp32
+constexpr float kRecipLin1 = 0x1.e1e1e2p+0f;   // 32/17 in fp32
+constexpr int kRecipSteps = 3;
 
 template <unsigned SPEC>
 __device__ __forceinline__ float dequant_unit(int c)
 {
-    return kDequantTable<SPEC>.v[c];
+    constexpr bool kSigned = (SPEC & FLASHOPT_Q_SIGNED) != 0;
+    constexpr float kD = kSigned ? 127.0f : 255.0f;
+    constexpr float kR = 1.0f / kD;
+    const float q = kSigned ? static_cast<float>(static_cast<int8_t>(c)) : static_cast<float>(c);
+    const float y0 = q * kR;
+    float y = __builtin_fmaf(__builtin_fmaf(-kD, y0, q), kR, y0);
+    if constexpr ((SPEC & FLASHOPT_Q_SOFTSIGN) != 0) {
+        const float den = 2.0f - fabsf(y);
+        const float h = den * 0.5f;
+        float x = __builtin_fmaf(-kRecipLin1, h, kRecipLin0);
+#pragma unroll
+        for (int k = 0; k < kRecipSteps; ++k) x = __builtin_fmaf(x, __builtin_fmaf(-h, x, 1.0f), x);
+        x = x * 0.5f;
+        const float z0 = y * x;
+        y = __builtin_fmaf(__builtin_fmaf(-den, z0, y), x, z0);
+    }
+    return y;
 }
 
 // A group's divisor d (1 for a zero scale, else the scale) with its
@@ -961,7 +965,7 @@ __device__ __forceinline__ void element_moments(const UnitIn<MB, ST, N> &in, int
 }
 
 // The generic recomputation of one unit's updated parameter (and momentum
-// codes) for lanes outside the short sequences' domains (see step_unit):
+// codes) for lanes outside the short sequences' domains (see step_finish):
 // reload the unit's inputs, redo the element arithmetic with correctly
 // rounded division and sqrt, and encode and split with the NaN-safe element
 // routines.  The variance codes, fp32 moments and the group scales do not
@@ -1055,27 +1059,40 @@ __device__ __forceinline__ void variance_codes(const float (&sq)[N], const float
     }
 }
 
-// One unit of one lane: load every stream, dequantize m and v (or read them
-// as fp32), rebuild the master (or widen the bf16 parameter), apply AdamW,
-// find the group maxima (DPP exchanges among the group's lanes), and write
-// scales and codes (or fp32 moments) and the new parameter (re-split, or
-// cast to bf16).  Every lane of the wavefront calls this for the same u.
-// FULL units use straight-line streaming accesses; at the ragged end of a
-// tensor accesses are masked per element and groups padded with zeros.
+// Issue the loads of unit u of a chunk for one lane (its first element r and
+// count cnt are returned): straight-line streaming accesses for a full
+// chunk, accesses masked per element at the ragged end of a tensor (missing
+// elements read as zero).
+template <int MB, int ST, int N, bool V = true>
+__device__ __forceinline__ void load_chunk_unit(const ChunkPtrs &c, int u, int lane, uint32_t &r,
+                                                int &cnt, UnitIn<MB, ST, N> &in)
+{
+    r = unit_first<N>(u, lane);
+    if (c.rem == kChunkElems) {
+        cnt = N;
+        load_unit<MB, ST, N, true, V>(c, r, cnt, in);
+    } else {
+        cnt = unit_count<N>(c, r);
+        load_unit<MB, ST, N, false, V>(c, r, cnt, in);
+    }
+}
+
+// The rest of one unit of one lane, from its loaded inputs: dequantize m and
+// v (or read them as fp32), rebuild the master (or widen the bf16
+// parameter), apply AdamW, find the group maxima (DPP exchanges among the
+// group's lanes), and write scales and codes (or fp32 moments) and the new
+// parameter (re-split, or cast to bf16).  Every lane of the wavefront calls
+// this for the same unit.  FULL units use straight-line streaming stores; at
+// the ragged end of a tensor stores are masked per element and groups padded
+// with zeros.
 template <int MB, int ST, int N, bool FULL>
-__device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
-                                          const StepScalars &sc, const float *s_mu,
-                                          const float *s_vu)
+__device__ __forceinline__ void step_finish(const ChunkPtrs &c, uint32_t r, int cnt, int lane,
+                                            const UnitIn<MB, ST, N> &in, const StepScalars &sc,
+                                            const float *s_mu, const float *s_vu)
 {
     constexpr bool kQuant = ST != kStatesFp32;
     constexpr bool kComp = ST == kStatesCompanded;
     constexpr unsigned kVSpec = kComp ? FLASHOPT_SPEC_VARIANCE : FLASHOPT_SPEC_VARIANCE_LINEAR;
-    const uint32_t r = unit_first<N>(u, lane);
-    const int cnt = FULL ? N : unit_count<N>(c, r);
-
-    // ---- loads (missing elements read as zero)
-    UnitIn<MB, ST, N> in;
-    load_unit<MB, ST, N, FULL>(c, r, cnt, in);
     const float ms = f16_value(in.smb);
     const float vs = f16_value(in.svb);
 
@@ -1228,23 +1245,21 @@ __device__ __forceinline__ void step_unit(const ChunkPtrs &c, int u, int lane,
 
 // ------------------------------------------------------------ FlashSGD
 
-// One FlashSGD unit: SGD with momentum (the buffer set to the gradient at
-// step 1, coupled weight decay, optional dampening and Nesterov), the
-// momentum buffer stored as group-32 codes (or fp32), the master re-split.
+// The rest of one FlashSGD unit of one lane, from its loaded inputs (the
+// loads as load_chunk_unit with V = false): SGD with momentum (the buffer set
+// to the gradient at step 1, coupled weight decay, optional dampening and
+// Nesterov), the momentum buffer stored as group-32 codes (or fp32), the
+// master re-split.
 // There is no division: only non-finite values need the element-wise
 // NaN-safe encoders, which run on the same registers.
 template <int MB, int ST, int N, bool FULL>
-__device__ __forceinline__ void sgd_unit(const ChunkPtrs &c, int u, int lane,
-                                         const SgdScalars &sc, const float *s_mu)
+__device__ __forceinline__ void sgd_finish(const ChunkPtrs &c, uint32_t r, int cnt, int lane,
+                                           const UnitIn<MB, ST, N> &in, const SgdScalars &sc,
+                                           const float *s_mu)
 {
     constexpr bool kQuant = ST != kStatesFp32;
     constexpr bool kComp = ST == kStatesCompanded;
     constexpr unsigned kMSpec = kComp ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
-    const uint32_t r = unit_first<N>(u, lane);
-    const int cnt = FULL ? N : unit_count<N>(c, r);
-
-    UnitIn<MB, ST, N> in;
-    load_unit<MB, ST, N, FULL, false>(c, r, cnt, in);
     const float ms = f16_value(in.smb);
 
     float th1[N], b1[N];
@@ -1331,78 +1346,124 @@ __device__ __forceinline__ uint32_t xcd_contiguous_block()
     return lb;
 }
 
-// Grid: one wavefront per run of `run` consecutive chunks (the last run may be
-// shorter); a chunk never straddles two tensors.  The wavefront finds the
-// tensor owning its first chunk by binary search over the chunk table
-// (scalar loads, uniform across the wavefront) and walks forward from there,
-// calling f(chunk pointers) for each chunk.  Runs are numbered in
-// xcd_contiguous_block() order.
-template <typename F>
-__device__ __forceinline__ void for_each_chunk(const DevTensor *__restrict__ tensors,
-                                               const int32_t *__restrict__ chunk_start,
-                                               int n_tensors, int32_t total_chunks, int32_t run,
-                                               F &&f)
+// Grid: one wavefront per unit, W units to a chunk, for the chunks
+// [chunk_base, chunk_end) of the list (a list too long for one launch takes
+// several, see launch_units; wavefronts past chunk_end, from rounding the
+// grid up to whole workgroups, have no unit); a chunk never straddles two
+// tensors.  Wavefronts are numbered in xcd_contiguous_block() order.  A
+// wavefront finds the tensor owning its chunk by binary search over the
+// chunk table (scalar loads, uniform across the wavefront).
+//
+// One unit per wavefront rather than a whole chunk: a wavefront's loads wait
+// for its own earlier stores (one counter covers both), so a second unit in
+// the same wavefront would start only once the first unit's stores had
+// drained.  Split across wavefronts, a unit's loads go out while other
+// wavefronts' stores are still in flight.
+//
+// Order within a wavefront: locate the unit and issue its loads (load),
+// then build the workgroup's LDS tables and meet its barrier (tables: every
+// wavefront calls it exactly once, at this one point, with or without a
+// unit), then finish the unit (finish).  With the loads in flight first, the
+// table build and the barrier overlap their latency instead of delaying
+// them.
+template <int W, typename Load, typename Tables, typename Finish>
+__device__ __forceinline__ void for_each_unit(const DevTensor *__restrict__ tensors,
+                                              const int32_t *__restrict__ chunk_start,
+                                              int n_tensors, int32_t chunk_base,
+                                              int32_t chunk_end, Load &&load, Tables &&tables,
+                                              Finish &&finish)
 {
-    const int64_t wave = __builtin_amdgcn_readfirstlane(
+    // a launch has at most 2^24 workgroups (its work-items fit in 32 bits)
+    const int32_t wave = __builtin_amdgcn_readfirstlane(
         static_cast<int32_t>(xcd_contiguous_block()) * (kBlockThreads / kWaveLanes) +
-        (threadIdx.x >> 6));
-    const int64_t first = wave * run;
-    if (first >= total_chunks) return;
-    // chunk indices fit in int32 (the host caps the total), so the search
-    // below compares in scalar registers
-    const int32_t c0 = static_cast<int32_t>(first);
-    const int32_t c1 = static_cast<int32_t>(first + run < total_chunks ? first + run : total_chunks);
-
-    // last tensor whose first chunk is <= c0
-    int lo = 0, hi = n_tensors - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (chunk_start[mid] <= c0) lo = mid;
-        else hi = mid - 1;
+        static_cast<int32_t>(threadIdx.x >> 6));
+    const int unit = wave % W;
+    const int64_t c64 = static_cast<int64_t>(chunk_base) + wave / W;
+    const bool any = c64 < chunk_end;
+    ChunkPtrs cp{};
+    if (any) {
+        // chunk indices fit in int32 (the host caps the total), so the
+        // search compares in scalar registers: the last tensor whose first
+        // chunk is <= c
+        const int32_t c = static_cast<int32_t>(c64);
+        int lo = 0, hi = n_tensors - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (chunk_start[mid] <= c) lo = mid;
+            else hi = mid - 1;
+        }
+        const int t = __builtin_amdgcn_readfirstlane(lo);
+        cp = chunk_ptrs(tensors[t], c - chunk_start[t]);
+        load(cp, unit);
     }
-    int t = __builtin_amdgcn_readfirstlane(lo);
-    for (int32_t c = c0; c < c1; ++c) {
-        while (c >= chunk_start[t + 1]) ++t;
-        t = __builtin_amdgcn_readfirstlane(t);
-        const DevTensor d = tensors[t];
-        f(chunk_ptrs(d, c - chunk_start[t]));
+    tables();
+    if (any) finish(cp);
+}
+
+// The same for one tensor (no chunk table): chunk c starts at element 1024 c.
+template <int W, typename Load, typename Tables, typename Finish>
+__device__ __forceinline__ void for_each_unit_of(const DevTensor &d, int32_t chunk_base,
+                                                 int32_t chunk_end, Load &&load, Tables &&tables,
+                                                 Finish &&finish)
+{
+    const int32_t wave = __builtin_amdgcn_readfirstlane(
+        static_cast<int32_t>(blockIdx.x) * (kBlockThreads / kWaveLanes) +
+        static_cast<int32_t>(threadIdx.x >> 6));
+    const int unit = wave % W;
+    const int64_t c64 = static_cast<int64_t>(chunk_base) + wave / W;
+    const bool any = c64 < chunk_end;
+    ChunkPtrs cp{};
+    if (any) {
+        cp = chunk_ptrs(d, static_cast<int32_t>(c64));
+        load(cp, unit);
+    }
+    tables();
+    if (any) finish(cp);
+}
+
+// The dequantization tables of a workgroup in LDS, one entry per thread,
+// then the workgroup barrier (none for fp32 states, which use no tables).
+template <int ST>
+__device__ __forceinline__ void build_tables(float *s_mu, float *s_vu)
+{
+    if constexpr (ST != kStatesFp32) {
+        constexpr unsigned kMSpec =
+            ST == kStatesCompanded ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
+        s_mu[threadIdx.x] = dequant_unit<kMSpec>(static_cast<int>(threadIdx.x));
+        if (s_vu != nullptr) s_vu[threadIdx.x] = dequant_unit<0u>(static_cast<int>(threadIdx.x));
+        __syncthreads();
     }
 }
 
-// The fused FlashAdamW step.  With quantized states the two 256-entry
-// dequantization tables are built per workgroup in LDS from the exact fp32
-// operations of dequantize().  The step's scalars are read from the staged
-// table (scalar loads, uniform across the wavefront), not from the kernel
-// arguments, so that a captured launch steps with whatever scalars were
-// written there before it runs.
+// The fused FlashAdamW step.  With quantized states each workgroup builds
+// the two 256-entry dequantization tables in LDS (momentum: q/127, companded
+// / (2 - |.|); variance: q/255).  The step's scalars are read from the
+// staged table (scalar loads, uniform across the wavefront), not from the
+// kernel arguments, so that a captured launch steps with whatever scalars
+// were written there before it runs.
 template <int MB, int ST>
 __global__ void __launch_bounds__(kBlockThreads)
 adamw_step_kernel(const StepScalars *__restrict__ scalars, const DevTensor *__restrict__ tensors,
-                  const int32_t *__restrict__ chunk_start, int n_tensors, int32_t total_chunks,
-                  int32_t run)
+                  const int32_t *__restrict__ chunk_start, int n_tensors, int32_t chunk_base,
+                  int32_t chunk_end)
 {
     const StepScalars sc = *scalars;
-    constexpr unsigned kMSpec =
-        ST == kStatesCompanded ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
     constexpr int kN = unit_elems(MB, ST);
     constexpr int kUnits = kLaneElems / kN;
-    __shared__ float s_mu[256];   // momentum: q/127 (companded: / (2 - |.|))
-    __shared__ float s_vu[256];   // variance: q/255
-    if constexpr (ST != kStatesFp32) {
-        s_mu[threadIdx.x] = dequant_unit<kMSpec>(static_cast<int>(threadIdx.x));
-        s_vu[threadIdx.x] = dequant_unit<0u>(static_cast<int>(threadIdx.x));
-        __syncthreads();
-    }
+    __shared__ float s_mu[256];
+    __shared__ float s_vu[256];
     const int lane = threadIdx.x & (kWaveLanes - 1);
-    for_each_chunk(tensors, chunk_start, n_tensors, total_chunks, run, [&](const ChunkPtrs &cp) {
-        if (cp.rem == kChunkElems) {
-#pragma unroll
-            for (int u = 0; u < kUnits; ++u) step_unit<MB, ST, kN, true>(cp, u, lane, sc, s_mu, s_vu);
-        } else {
-#pragma unroll
-            for (int u = 0; u < kUnits; ++u) step_unit<MB, ST, kN, false>(cp, u, lane, sc, s_mu, s_vu);
-        }
-    });
+    UnitIn<MB, ST, kN> in;
+    uint32_t r = 0u;
+    int cnt = 0;
+    for_each_unit<kUnits>(
+        tensors, chunk_start, n_tensors, chunk_base, chunk_end,
+        [&](const ChunkPtrs &cp, int u) { load_chunk_unit<MB, ST, kN>(cp, u, lane, r, cnt, in); },
+        [&] { build_tables<ST>(s_mu, s_vu); },
+        [&](const ChunkPtrs &cp) {
+            if (cp.rem == kChunkElems) step_finish<MB, ST, kN, true>(cp, r, cnt, lane, in, sc, s_mu, s_vu);
+            else step_finish<MB, ST, kN, false>(cp, r, cnt, lane, in, sc, s_mu, s_vu);
+        });
 }
 
 // The fused FlashSGD step (same grid and tables, momentum only; scalars read
@@ -1410,95 +1471,70 @@ adamw_step_kernel(const StepScalars *__restrict__ scalars, const DevTensor *__re
 template <int MB, int ST>
 __global__ void __launch_bounds__(kBlockThreads)
 sgd_step_kernel(const SgdScalars *__restrict__ scalars, const DevTensor *__restrict__ tensors,
-                const int32_t *__restrict__ chunk_start, int n_tensors, int32_t total_chunks,
-                int32_t run)
+                const int32_t *__restrict__ chunk_start, int n_tensors, int32_t chunk_base,
+                int32_t chunk_end)
 {
     const SgdScalars sc = *scalars;
-    constexpr unsigned kMSpec =
-        ST == kStatesCompanded ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
     constexpr int kN = unit_elems(MB, ST);
     constexpr int kUnits = kLaneElems / kN;
     __shared__ float s_mu[256];
-    if constexpr (ST != kStatesFp32) {
-        s_mu[threadIdx.x] = dequant_unit<kMSpec>(static_cast<int>(threadIdx.x));
-        __syncthreads();
-    }
     const int lane = threadIdx.x & (kWaveLanes - 1);
-    for_each_chunk(tensors, chunk_start, n_tensors, total_chunks, run, [&](const ChunkPtrs &cp) {
-        if (cp.rem == kChunkElems) {
-#pragma unroll
-            for (int u = 0; u < kUnits; ++u) sgd_unit<MB, ST, kN, true>(cp, u, lane, sc, s_mu);
-        } else {
-#pragma unroll
-            for (int u = 0; u < kUnits; ++u) sgd_unit<MB, ST, kN, false>(cp, u, lane, sc, s_mu);
-        }
-    });
+    UnitIn<MB, ST, kN> in;
+    uint32_t r = 0u;
+    int cnt = 0;
+    for_each_unit<kUnits>(
+        tensors, chunk_start, n_tensors, chunk_base, chunk_end,
+        [&](const ChunkPtrs &cp, int u) { load_chunk_unit<MB, ST, kN, false>(cp, u, lane, r, cnt, in); },
+        [&] { build_tables<ST>(s_mu, nullptr); },
+        [&](const ChunkPtrs &cp) {
+            if (cp.rem == kChunkElems) sgd_finish<MB, ST, kN, true>(cp, r, cnt, lane, in, sc, s_mu);
+            else sgd_finish<MB, ST, kN, false>(cp, r, cnt, lane, in, sc, s_mu);
+        });
 }
 
 // Single-tensor forms (the descriptor travels in the kernel arguments, no
-// chunk table): chunk c of the tensor starts at element 1024 c.
-template <typename F>
-__device__ __forceinline__ void for_each_chunk_of(const DevTensor &d, int32_t total_chunks,
-                                                  int32_t run, F &&f)
-{
-    const int64_t wave = __builtin_amdgcn_readfirstlane(
-        static_cast<int32_t>(blockIdx.x) * (kBlockThreads / kWaveLanes) + (threadIdx.x >> 6));
-    const int64_t c0 = wave * run;
-    if (c0 >= total_chunks) return;
-    const int32_t c1 = static_cast<int32_t>(c0 + run < total_chunks ? c0 + run : total_chunks);
-    for (int32_t c = static_cast<int32_t>(c0); c < c1; ++c) f(chunk_ptrs(d, c));
-}
-
+// chunk table).
 template <int MB, int ST>
 __global__ void __launch_bounds__(kBlockThreads)
-adamw_tensor_kernel(DevTensor d, int32_t total_chunks, int32_t run, StepScalars sc)
+adamw_tensor_kernel(DevTensor d, StepScalars sc, int32_t chunk_base, int32_t chunk_end)
 {
-    constexpr unsigned kMSpec =
-        ST == kStatesCompanded ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
     constexpr int kN = unit_elems(MB, ST);
     constexpr int kUnits = kLaneElems / kN;
     __shared__ float s_mu[256];
     __shared__ float s_vu[256];
-    if constexpr (ST != kStatesFp32) {
-        s_mu[threadIdx.x] = dequant_unit<kMSpec>(static_cast<int>(threadIdx.x));
-        s_vu[threadIdx.x] = dequant_unit<0u>(static_cast<int>(threadIdx.x));
-        __syncthreads();
-    }
     const int lane = threadIdx.x & (kWaveLanes - 1);
-    for_each_chunk_of(d, total_chunks, run, [&](const ChunkPtrs &cp) {
-        if (cp.rem == kChunkElems) {
-#pragma unroll
-            for (int u = 0; u < kUnits; ++u) step_unit<MB, ST, kN, true>(cp, u, lane, sc, s_mu, s_vu);
-        } else {
-#pragma unroll
-            for (int u = 0; u < kUnits; ++u) step_unit<MB, ST, kN, false>(cp, u, lane, sc, s_mu, s_vu);
-        }
-    });
+    UnitIn<MB, ST, kN> in;
+    uint32_t r = 0u;
+    int cnt = 0;
+    for_each_unit_of<kUnits>(
+        d, chunk_base, chunk_end,
+        [&](const ChunkPtrs &cp, int u) { load_chunk_unit<MB, ST, kN>(cp, u, lane, r, cnt, in); },
+        [&] { build_tables<ST>(s_mu, s_vu); },
+        [&](const ChunkPtrs &cp) {
+            if (cp.rem == kChunkElems) step_finish<MB, ST, kN, true>(cp, r, cnt, lane, in, sc, s_mu, s_vu);
+            else step_finish<MB, ST, kN, false>(cp, r, cnt, lane, in, sc, s_mu, s_vu);
+        });
 }
 
 template <int MB, int ST>
 __global__ void __launch_bounds__(kBlockThreads)
-sgd_tensor_kernel(DevTensor d, int32_t total_chunks, int32_t run, SgdScalars sc)
+sgd_tensor_kernel(DevTensor d, SgdScalars sc, int32_t chunk_base, int32_t chunk_end)
 {
-    constexpr unsigned kMSpec =
-        ST == kStatesCompanded ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
     constexpr int kN = unit_elems(MB, ST);
     constexpr int kUnits = kLaneElems / kN;
     __shared__ float s_mu[256];
-    if constexpr (ST != kStatesFp32) {
-        s_mu[threadIdx.x] = dequant_unit<kMSpec>(static_cast<int>(threadIdx.x));
-        __syncthreads();
-    }
     const int lane = threadIdx.x & (kWaveLanes - 1);
-    for_each_chunk_of(d, total_chunks, run, [&](const ChunkPtrs &cp) {
-        if (cp.rem == kChunkElems) {
-#pragma unroll
-            for (int u = 0; u < kUnits; ++u) sgd_unit<MB, ST, kN, true>(cp, u, lane, sc, s_mu);
-        } else {
-#pragma unroll
-            for (int u = 0; u < kUnits; ++u) sgd_unit<MB, ST, kN, false>(cp, u, lane, sc, s_mu);
-        }
-    });
+    UnitIn<MB, ST, kN> in;
+    uint32_t r = 0u;
+    int cnt = 0;
+    for_each_unit_of<kUnits>(
+        d, chunk_base, chunk_end,
+        [&](const ChunkPtrs &cp, int u) { load_chunk_unit<MB, ST, kN, false>(cp, u, lane, r, cnt, in); },
+        [&] { build_tables<ST>(s_mu, nullptr); },
+        [&](const ChunkPtrs &cp) {
+            if (cp.rem == kChunkElems) sgd_finish<MB, ST, kN, true>(cp, r, cnt, lane, in, sc, s_mu);
+            else sgd_finish<MB, ST, kN, false>(cp, r, cnt, lane, in, sc, s_mu);
+        });
 }
 
 // ------------------------------------------------------------- launching
@@ -1584,48 +1620,56 @@ hipError_t launch_reconstruct(const uint16_t *param, const void *rho, int64_t n,
 
 namespace {
 
-// Consecutive chunks per wavefront: one (FLASHOPT_CHUNKS_PER_WAVE overrides
-// it).  On the 8.0B list one chunk beat two by 2.6-3.4% where the buffers
-// landed in a slow placement, for the list steps (workgroups in
-// XCD-contiguous order) and for single-tensor launches (plain order), and
-// lost at most 0.9% in fast placements.
-int32_t chunks_per_wave()
+// Chunks per launch: as many as one dispatch's 32-bit count of work-items
+// allows (2^24 - 1 workgroups of four wavefronts, one wavefront per unit),
+// or fewer when FLASHOPT_LAUNCH_CHUNKS asks for it (a test hook that makes
+// small lists take several launches).
+int64_t launch_chunks(int units_per_chunk)
 {
-    int32_t run = 1;
-    if (const char *env = getenv("FLASHOPT_CHUNKS_PER_WAVE")) {
-        const int v = atoi(env);
-        if (v >= 1 && v <= 1024) run = v;
+    int64_t n = (static_cast<int64_t>(UINT32_MAX) / kBlockThreads) * (kBlockThreads / kWaveLanes) /
+                units_per_chunk;
+    if (const char *env = getenv("FLASHOPT_LAUNCH_CHUNKS")) {
+        const long long v = atoll(env);
+        if (v >= 1 && v < n) n = v;
     }
-    return run;
+    return n;
 }
 
-unsigned step_grid(int32_t total_chunks, int32_t run)
+// Launches kernel K over chunks [0, total_chunks) of a list, in as many
+// launches as launch_chunks requires (one on any list that fits in HBM), each
+// given its chunk range after the arguments passed through.
+template <int MB, int ST, typename Kernel, typename... Args>
+hipError_t launch_units(Kernel kernel, int32_t total_chunks, hipStream_t st, Args... args)
 {
-    const int64_t waves = (total_chunks + run - 1) / run;
-    const int64_t waves_per_block = kBlockThreads / kWaveLanes;
-    return static_cast<unsigned>((waves + waves_per_block - 1) / waves_per_block);
+    constexpr int units = kLaneElems / unit_elems(MB, ST);
+    const int64_t per = launch_chunks(units);
+    for (int64_t base = 0; base < total_chunks; base += per) {
+        const int64_t n = total_chunks - base < per ? total_chunks - base : per;
+        const int64_t waves = n * units;
+        const unsigned grid = static_cast<unsigned>((waves + kBlockThreads / kWaveLanes - 1) /
+                                                    (kBlockThreads / kWaveLanes));
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlockThreads), 0, st, args...,
+                           static_cast<int32_t>(base), static_cast<int32_t>(base + n));
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int MB, int ST>
 hipError_t step_variant(const DevTensor *tensors, const int32_t *chunk_start, int n_tensors,
                         int32_t total_chunks, const StepScalars *scalars, hipStream_t st)
 {
-    const int32_t run = chunks_per_wave();
-    hipLaunchKernelGGL((adamw_step_kernel<MB, ST>), dim3(step_grid(total_chunks, run)),
-                       dim3(kBlockThreads), 0, st, scalars, tensors, chunk_start, n_tensors,
-                       total_chunks, run);
-    return hipGetLastError();
+    return launch_units<MB, ST>(adamw_step_kernel<MB, ST>, total_chunks, st, scalars, tensors,
+                                chunk_start, n_tensors);
 }
 
 template <int MB, int ST>
 hipError_t sgd_variant(const DevTensor *tensors, const int32_t *chunk_start, int n_tensors,
                        int32_t total_chunks, const SgdScalars *scalars, hipStream_t st)
 {
-    const int32_t run = chunks_per_wave();
-    hipLaunchKernelGGL((sgd_step_kernel<MB, ST>), dim3(step_grid(total_chunks, run)),
-                       dim3(kBlockThreads), 0, st, scalars, tensors, chunk_start, n_tensors,
-                       total_chunks, run);
-    return hipGetLastError();
+    return launch_units<MB, ST>(sgd_step_kernel<MB, ST>, total_chunks, st, scalars, tensors,
+                                chunk_start, n_tensors);
 }
 
 // The (master_bits, states) instantiations of one step kernel family: nine,
@@ -1686,10 +1730,7 @@ struct AdamWTensorLaunch {
     static hipError_t run(const DevTensor *t, const int32_t *, int, int32_t total,
                           const StepScalars &sc, hipStream_t st)
     {
-        const int32_t run = chunks_per_wave();
-        hipLaunchKernelGGL((adamw_tensor_kernel<MB, ST>), dim3(step_grid(total, run)),
-                           dim3(kBlockThreads), 0, st, *t, total, run, sc);
-        return hipGetLastError();
+        return launch_units<MB, ST>(adamw_tensor_kernel<MB, ST>, total, st, *t, sc);
     }
 };
 
@@ -1699,10 +1740,7 @@ struct SgdTensorLaunch {
     static hipError_t run(const DevTensor *t, const int32_t *, int, int32_t total,
                           const SgdScalars &sc, hipStream_t st)
     {
-        const int32_t run = chunks_per_wave();
-        hipLaunchKernelGGL((sgd_tensor_kernel<MB, ST>), dim3(step_grid(total, run)),
-                           dim3(kBlockThreads), 0, st, *t, total, run, sc);
-        return hipGetLastError();
+        return launch_units<MB, ST>(sgd_tensor_kernel<MB, ST>, total, st, *t, sc);
     }
 };
 

@@ -358,24 +358,43 @@ def test_lanes_outside_short_division_domain(orc, case, mb, comp, qs):
         _compare_nan_aware(_snap(opt.states[0]), want, mb, f"{case} mb{mb} comp{comp} t{t}")
 
 
-def test_deterministic_across_runs_and_launch_shapes():
+def test_deterministic_across_launch_splits():
+    """The same steps leave the same bits whether a list is stepped in one
+    launch or split into launches of 1 or 7 chunks (FLASHOPT_LAUNCH_CHUNKS
+    forces the split that a list too long for one dispatch takes; 7 chunks
+    of two wavefronts leave spare wavefronts in every launch's last
+    workgroup, which must not reach into the next launch's chunks): AdamW
+    list steps, single-tensor steps and FlashSGD list steps."""
     require_gpu()
     sizes = [1 << 16, 3000, 1 << 18]
     results = []
-    for run in (None, "1", "16"):
-        if run is None:
-            os.environ.pop("FLASHOPT_CHUNKS_PER_WAVE", None)
-        else:
-            os.environ["FLASHOPT_CHUNKS_PER_WAVE"] = run
-        params = [W.init_param(n, device="cuda", seed=70 + i) for i, n in enumerate(sizes)]
-        opt = F.FlashAdamW(params, master_bits=24, **HP)
-        for t in range(1, 4):
-            opt.step([W.make_grad(n, t, device="cuda", stream_id=i) for i, n in enumerate(sizes)])
-        torch.cuda.synchronize()
-        results.append([torch.cat([s.param.view(torch.int16).float(), s.rho.float(),
-                                   s.m_codes.float(), s.v_codes.float()]).cpu()
-                        for s in opt.states])
-    os.environ.pop("FLASHOPT_CHUNKS_PER_WAVE", None)
+    try:
+        for per in (None, "1", "7"):
+            if per is None:
+                os.environ.pop("FLASHOPT_LAUNCH_CHUNKS", None)
+            else:
+                os.environ["FLASHOPT_LAUNCH_CHUNKS"] = per
+            make = lambda seed: [W.init_param(n, device="cuda", seed=seed + i) for i, n in enumerate(sizes)]
+            opt = F.FlashAdamW(make(70), master_bits=24, **HP)
+            single = F.FlashAdamW(make(80), master_bits=24, **HP)
+            sgd = F.FlashSGD(make(90), **W.SGD_DEFAULT)
+            for t in range(1, 4):
+                grads = [W.make_grad(n, t, device="cuda", stream_id=i) for i, n in enumerate(sizes)]
+                opt.step(grads)
+                for i, g in enumerate(grads):
+                    single.step_tensor(i, g)
+                sgd.step(grads)
+            torch.cuda.synchronize()
+            out = []
+            for s in opt.states + single.states:
+                out.append(torch.cat([s.param.view(torch.int16).float(), s.rho.float(),
+                                      s.m_codes.float(), s.v_codes.float()]).cpu())
+            for s in sgd.states:
+                out.append(torch.cat([s.param.view(torch.int16).float(), s.rho.float(),
+                                      s.m_codes.float()]).cpu())
+            results.append(out)
+    finally:
+        os.environ.pop("FLASHOPT_LAUNCH_CHUNKS", None)
     for r in results[1:]:
         for a, b in zip(results[0], r):
             assert torch.equal(a, b)
