@@ -34,6 +34,12 @@
  *   - Alignment: every element stream (fp32, bf16, codes, rho) must start on a
  *     16-byte boundary, scale arrays on a 2-byte boundary; otherwise
  *     FLASHOPT_EALIGN.  Allocations from hipMalloc / torch satisfy this.
+ *   - A step call launches its step kernel once.  A list (or tensor) of more
+ *     than 2^25 - 2 chunks of 1024 elements (2^24 - 1 with fp32 states or
+ *     fp32 parameters) does not fit one dispatch's 32-bit count of
+ *     work-items and is stepped by one launch per such range of chunks, in
+ *     order on the same stream.  Should a later launch of such a split fail,
+ *     the earlier ones have already been enqueued.
  */
 #ifndef FLASHOPT_H
 #define FLASHOPT_H
@@ -164,7 +170,8 @@ typedef struct {
  * Returns 0 for n_tensors <= 0. */
 size_t flashopt_adamw_workspace_bytes(const flashopt_tensor *tensors, int n_tensors);
 
-/* One fused FlashAdamW step over a list of tensors, one kernel launch (page
+/* One fused FlashAdamW step over a list of tensors, one kernel launch (see
+ * the conventions for lists too long for one dispatch) (page
  * "code/flashsim/flash_adamw_sim.py", FlashAdamWSim.step, Alg. 4).  Per
  * element, in one pass over memory:
  *   m0 = dequantize(m), v0 = dequantize(v)      (momentum / variance spec, or
@@ -296,7 +303,8 @@ typedef struct {
 /* Device workspace bytes that flashopt_sgd_step needs for this list. */
 size_t flashopt_sgd_workspace_bytes(const flashopt_tensor *tensors, int n_tensors);
 
-/* One fused FlashSGD step over a list of tensors, one kernel launch.  The
+/* One fused FlashSGD step over a list of tensors, one kernel launch (see the
+ * conventions for lists too long for one dispatch).  The
  * momentum buffer lives in each descriptor's m_codes / m_scales; v_codes and
  * v_scales are unused (may be NULL).  Ownership, staging, workspace and
  * alignment rules as flashopt_adamw_step.
@@ -338,7 +346,8 @@ flashopt_status flashopt_sgd_plan_launch(const flashopt_sgd_plan_info *info, con
 
 /* One tensor's FlashAdamW / FlashSGD step without a workspace: the
  * descriptor travels in the kernel arguments, so the call stages nothing and
- * enqueues exactly one kernel.  Meant for launching each tensor's step as
+ * enqueues one kernel launch (see the conventions for a tensor too long for
+ * one dispatch).  Meant for launching each tensor's step as
  * soon as its gradient is complete (gradient release: a post-accumulate-grad
  * hook steps the parameter and frees its gradient, so a full set of
  * gradients is never held; page "code/flashsim/flash_adamw_sim.py",
