@@ -132,9 +132,10 @@ __device__ __forceinline__ int32_t shalf(const uint32_t (&w)[W], int j)
 
 // Dequantization before the scale: y = q/127 or q/255, then the softsign
 // inverse y / (2 - |y|) (dequantize()), each operation correctly rounded.
-// Every workgroup evaluates the 256 entries of the specs it uses into LDS,
-// one entry per thread, before its barrier, so the evaluation must be short:
-// it uses multiplies and FMAs only, no division sequence and no load.
+// The dequantize kernel evaluates the 256 entries of its spec into LDS, one
+// entry per thread, before its barrier, so the evaluation must be short: it
+// uses multiplies and FMAs only, no division sequence and no load (2.8%
+// faster than loading the entries there).
 //  * q / D: y0 = q R with R = RN(1/D), then one Markstein correction,
 //    y = y0 + (q - D y0) R.
 //  * y / den with den = 2 - |y|: a reciprocal x of den from the linear
@@ -168,6 +169,37 @@ __device__ __forceinline__ float dequant_unit(int c)
     }
     return y;
 }
+
+// The same entries as compile-time constants in device memory (constant
+// evaluation rounds each operation to nearest even, as the device does), for
+// the step kernels: each thread loads its entries before its unit's stream
+// loads and writes them to LDS once those have arrived, so an entry costs a
+// load and no arithmetic.  Computing them there instead added about 2.4 VALU
+// instructions per element and cost the 8.0B list step 0.4-1.4%.
+template <unsigned SPEC>
+struct alignas(16) DequantTable {
+    float v[256];
+};
+
+template <unsigned SPEC>
+constexpr DequantTable<SPEC> make_dequant_table()
+{
+    constexpr bool kSigned = (SPEC & FLASHOPT_Q_SIGNED) != 0;
+    DequantTable<SPEC> t{};
+    for (int c = 0; c < 256; ++c) {
+        const float q = kSigned ? static_cast<float>(static_cast<int8_t>(c)) : static_cast<float>(c);
+        float y = q / (kSigned ? 127.0f : 255.0f);
+        if (SPEC & FLASHOPT_Q_SOFTSIGN) {
+            const float den = 2.0f - (y < 0.0f ? -y : y);
+            y = y / den;
+        }
+        t.v[c] = y;
+    }
+    return t;
+}
+
+template <unsigned SPEC>
+__device__ const DequantTable<SPEC> kDequantTable = make_dequant_table<SPEC>();
 
 // A group's divisor d (1 for a zero scale, else the scale) with its
 // correctly rounded reciprocal r.  An infinite scale yields d = r = 0, for
@@ -1421,23 +1453,39 @@ __device__ __forceinline__ void for_each_unit_of(const DevTensor &d, int32_t chu
     if (any) finish(cp);
 }
 
-// The dequantization tables of a workgroup in LDS, one entry per thread,
-// then the workgroup barrier (none for fp32 states, which use no tables).
-template <int ST>
-__device__ __forceinline__ void build_tables(float *s_mu, float *s_vu)
+// This thread's entries of the workgroup's dequantization tables (momentum:
+// q/127, companded / (2 - |.|); variance: q/255), loaded at the start of a
+// step kernel; build_tables writes them to LDS and meets the workgroup
+// barrier (neither for fp32 states, which use no tables).
+struct TableEntries {
+    float mu, vu;
+};
+
+template <int ST, bool V>
+__device__ __forceinline__ TableEntries table_entries()
 {
+    TableEntries e{0.0f, 0.0f};
     if constexpr (ST != kStatesFp32) {
         constexpr unsigned kMSpec =
             ST == kStatesCompanded ? FLASHOPT_SPEC_MOMENTUM : FLASHOPT_SPEC_MOMENTUM_LINEAR;
-        s_mu[threadIdx.x] = dequant_unit<kMSpec>(static_cast<int>(threadIdx.x));
-        if (s_vu != nullptr) s_vu[threadIdx.x] = dequant_unit<0u>(static_cast<int>(threadIdx.x));
+        e.mu = kDequantTable<kMSpec>.v[threadIdx.x];
+        if constexpr (V) e.vu = kDequantTable<0u>.v[threadIdx.x];
+    }
+    return e;
+}
+
+template <int ST, bool V>
+__device__ __forceinline__ void build_tables(const TableEntries &e, float *s_mu, float *s_vu)
+{
+    if constexpr (ST != kStatesFp32) {
+        s_mu[threadIdx.x] = e.mu;
+        if constexpr (V) s_vu[threadIdx.x] = e.vu;
         __syncthreads();
     }
 }
 
-// The fused FlashAdamW step.  With quantized states each workgroup builds
-// the two 256-entry dequantization tables in LDS (momentum: q/127, companded
-// / (2 - |.|); variance: q/255).  The step's scalars are read from the
+// The fused FlashAdamW step.  With quantized states each workgroup holds
+// the two 256-entry dequantization tables in LDS.  The step's scalars are read from the
 // staged table (scalar loads, uniform across the wavefront), not from the
 // kernel arguments, so that a captured launch steps with whatever scalars
 // were written there before it runs.
@@ -1452,6 +1500,7 @@ adamw_step_kernel(const StepScalars *__restrict__ scalars, const DevTensor *__re
     constexpr int kUnits = kLaneElems / kN;
     __shared__ float s_mu[256];
     __shared__ float s_vu[256];
+    const TableEntries te = table_entries<ST, true>();
     const int lane = threadIdx.x & (kWaveLanes - 1);
     UnitIn<MB, ST, kN> in;
     uint32_t r = 0u;
@@ -1459,7 +1508,7 @@ adamw_step_kernel(const StepScalars *__restrict__ scalars, const DevTensor *__re
     for_each_unit<kUnits>(
         tensors, chunk_start, n_tensors, chunk_base, chunk_end,
         [&](const ChunkPtrs &cp, int u) { load_chunk_unit<MB, ST, kN>(cp, u, lane, r, cnt, in); },
-        [&] { build_tables<ST>(s_mu, s_vu); },
+        [&] { build_tables<ST, true>(te, s_mu, s_vu); },
         [&](const ChunkPtrs &cp) {
             if (cp.rem == kChunkElems) step_finish<MB, ST, kN, true>(cp, r, cnt, lane, in, sc, s_mu, s_vu);
             else step_finish<MB, ST, kN, false>(cp, r, cnt, lane, in, sc, s_mu, s_vu);
@@ -1478,6 +1527,7 @@ sgd_step_kernel(const SgdScalars *__restrict__ scalars, const DevTensor *__restr
     constexpr int kN = unit_elems(MB, ST);
     constexpr int kUnits = kLaneElems / kN;
     __shared__ float s_mu[256];
+    const TableEntries te = table_entries<ST, false>();
     const int lane = threadIdx.x & (kWaveLanes - 1);
     UnitIn<MB, ST, kN> in;
     uint32_t r = 0u;
@@ -1485,7 +1535,7 @@ sgd_step_kernel(const SgdScalars *__restrict__ scalars, const DevTensor *__restr
     for_each_unit<kUnits>(
         tensors, chunk_start, n_tensors, chunk_base, chunk_end,
         [&](const ChunkPtrs &cp, int u) { load_chunk_unit<MB, ST, kN, false>(cp, u, lane, r, cnt, in); },
-        [&] { build_tables<ST>(s_mu, nullptr); },
+        [&] { build_tables<ST, false>(te, s_mu, nullptr); },
         [&](const ChunkPtrs &cp) {
             if (cp.rem == kChunkElems) sgd_finish<MB, ST, kN, true>(cp, r, cnt, lane, in, sc, s_mu);
             else sgd_finish<MB, ST, kN, false>(cp, r, cnt, lane, in, sc, s_mu);
@@ -1502,6 +1552,7 @@ adamw_tensor_kernel(DevTensor d, StepScalars sc, int32_t chunk_base, int32_t chu
     constexpr int kUnits = kLaneElems / kN;
     __shared__ float s_mu[256];
     __shared__ float s_vu[256];
+    const TableEntries te = table_entries<ST, true>();
     const int lane = threadIdx.x & (kWaveLanes - 1);
     UnitIn<MB, ST, kN> in;
     uint32_t r = 0u;
@@ -1509,7 +1560,7 @@ adamw_tensor_kernel(DevTensor d, StepScalars sc, int32_t chunk_base, int32_t chu
     for_each_unit_of<kUnits>(
         d, chunk_base, chunk_end,
         [&](const ChunkPtrs &cp, int u) { load_chunk_unit<MB, ST, kN>(cp, u, lane, r, cnt, in); },
-        [&] { build_tables<ST>(s_mu, s_vu); },
+        [&] { build_tables<ST, true>(te, s_mu, s_vu); },
         [&](const ChunkPtrs &cp) {
             if (cp.rem == kChunkElems) step_finish<MB, ST, kN, true>(cp, r, cnt, lane, in, sc, s_mu, s_vu);
             else step_finish<MB, ST, kN, false>(cp, r, cnt, lane, in, sc, s_mu, s_vu);
@@ -1523,6 +1574,7 @@ sgd_tensor_kernel(DevTensor d, SgdScalars sc, int32_t chunk_base, int32_t chunk_
     constexpr int kN = unit_elems(MB, ST);
     constexpr int kUnits = kLaneElems / kN;
     __shared__ float s_mu[256];
+    const TableEntries te = table_entries<ST, false>();
     const int lane = threadIdx.x & (kWaveLanes - 1);
     UnitIn<MB, ST, kN> in;
     uint32_t r = 0u;
@@ -1530,7 +1582,7 @@ sgd_tensor_kernel(DevTensor d, SgdScalars sc, int32_t chunk_base, int32_t chunk_
     for_each_unit_of<kUnits>(
         d, chunk_base, chunk_end,
         [&](const ChunkPtrs &cp, int u) { load_chunk_unit<MB, ST, kN, false>(cp, u, lane, r, cnt, in); },
-        [&] { build_tables<ST>(s_mu, nullptr); },
+        [&] { build_tables<ST, false>(te, s_mu, nullptr); },
         [&](const ChunkPtrs &cp) {
             if (cp.rem == kChunkElems) sgd_finish<MB, ST, kN, true>(cp, r, cnt, lane, in, sc, s_mu);
             else sgd_finish<MB, ST, kN, false>(cp, r, cnt, lane, in, sc, s_mu);

@@ -1,14 +1,15 @@
-"""The step kernels build their dequantization tables (q/127 or q/255, then
-the softsign inverse y / (2 - |y|), dequantize() on page
-"code/flashsim/quantization.py") with multiplies and FMAs only: a Markstein
-correction of q R for the quotient by a constant, and a Newton reciprocal of
-2 - |y| followed by the same correction for the softsign inverse.  This test
+"""The dequantize kernel builds its table (q/127 or q/255, then the softsign
+inverse y / (2 - |y|), dequantize() on page "code/flashsim/quantization.py")
+with multiplies and FMAs only: a Markstein correction of q R for the
+quotient by a constant, and a Newton reciprocal of 2 - |y| followed by the
+same correction for the softsign inverse.  This test
 evaluates every rounding of those sequences exactly (rational arithmetic,
 fp32 round-to-nearest-even; an FMA rounds once) for every code of the
 signed and unsigned specs, with the constants read from the kernel source,
 and requires the correctly rounded quotient each time, which is what
-dequantize() computes in fp32.  (The GPU codec and step tests compare the
-kernels' tables with the oracle on every code as well.)"""
+dequantize() computes in fp32.  (The GPU codec tests compare the kernel's
+tables with the oracle on every code as well; the step kernels load
+compile-time constants of the same entries.)"""
 import os
 import re
 from fractions import Fraction as Fr
