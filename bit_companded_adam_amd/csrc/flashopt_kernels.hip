@@ -10,7 +10,7 @@
 // taking 16 elements of a chunk as units of N consecutive elements placed so
 // that every memory instruction of a wavefront covers one contiguous block
 // of each stream (unit u of lane l starts at element 64 N u + N l).  The
-// codec and split kernels give a wavefront a whole chunk; the step kernels
+// codec kernels give a wavefront a whole chunk; the split and step kernels
 // give it one unit of one chunk (the multi-tensor steps renumber their
 // workgroups so that each XCD streams one contiguous region).  The
 // quantized steps use N = 8 (a lane quad owns a 32-element group; its
@@ -495,8 +495,8 @@ __device__ __forceinline__ void encode_s8_softsign_fast(const float (&a)[N], uin
 // Element offset of unit u (0..3) of the calling lane in its wavefront's
 // 1024-element chunk: 4 consecutive elements, the 64 lanes of a unit covering
 // 256 consecutive elements, so that every access instruction of the
-// wavefront touches one contiguous block of each stream.  The codec
-// and split kernels use it (16 bytes of fp32 per lane and unit).
+// wavefront touches one contiguous block of each stream.  The quantize and
+// dequantize kernels use it (16 bytes of fp32 per lane and unit).
 __device__ __forceinline__ int64_t quad_first(int u)
 {
     const int64_t chunk =
@@ -605,16 +605,27 @@ dequantize_kernel(const void *__restrict__ codes, const uint16_t *__restrict__ s
 
 // ------------------------------------------------------- standalone split
 
+// Element offset of the calling lane in the split and reconstruct kernels:
+// one 256-element unit per wavefront, 4 consecutive elements per lane (16
+// bytes of fp32), so that every access instruction of the wavefront covers
+// one contiguous block of each stream; a workgroup takes one 1024-element
+// chunk, a launch the chunks from `base` on.  One unit per wavefront streams
+// faster here than a whole chunk per wavefront (one load and one store
+// instruction per stream and wavefront).
+__device__ __forceinline__ int64_t split_lane_first(int64_t base)
+{
+    return (base + blockIdx.x) * kChunkElems + 4 * static_cast<int64_t>(threadIdx.x);
+}
+
 template <int MB>
 __global__ void __launch_bounds__(kBlockThreads)
 split_kernel(const float *__restrict__ master, int64_t n, uint16_t *__restrict__ param,
-             void *__restrict__ rho)
+             void *__restrict__ rho, int64_t base)
 {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int64_t e = quad_first(u);
+    {
+        const int64_t e = split_lane_first(base);
         const int cnt = quad_count(n, e);
-        if (cnt == 0) continue;
+        if (cnt == 0) return;
         float x[4];
         if (cnt == 4) {
             const uint4 v = ld16s(master + e);
@@ -650,13 +661,12 @@ split_kernel(const float *__restrict__ master, int64_t n, uint16_t *__restrict__
 template <int MB>
 __global__ void __launch_bounds__(kBlockThreads)
 reconstruct_kernel(const uint16_t *__restrict__ param, const void *__restrict__ rho, int64_t n,
-                   float *__restrict__ master)
+                   float *__restrict__ master, int64_t base)
 {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int64_t e = quad_first(u);
+    {
+        const int64_t e = split_lane_first(base);
         const int cnt = quad_count(n, e);
-        if (cnt == 0) continue;
+        if (cnt == 0) return;
         uint32_t pw[2] = {0u, 0u}, rw[MB == 32 ? 2 : 1] = {};
         if (cnt == 4) {
             const u32x2 p2 = ld8s(param + e);
@@ -1597,6 +1607,27 @@ unsigned grid_for(int64_t n)
     return static_cast<unsigned>((n + per_block - 1) / per_block);
 }
 
+int64_t launch_chunks(int units_per_chunk);
+
+// Launches of a split or reconstruct kernel over the 1024-element chunks of
+// n elements, one workgroup per chunk and at most launch_chunks(4) chunks per
+// launch (in order on one stream); each launch gets its first chunk after
+// the arguments passed through.
+template <typename Kernel, typename... Args>
+hipError_t launch_flat(Kernel kernel, int64_t n, hipStream_t st, Args... args)
+{
+    const int64_t chunks = (n + kChunkElems - 1) / kChunkElems;
+    const int64_t per = launch_chunks(kLaneElems / 4);
+    for (int64_t base = 0; base < chunks; base += per) {
+        const int64_t k = chunks - base < per ? chunks - base : per;
+        hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(k)), dim3(kBlockThreads), 0, st,
+                           args..., base);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 template <unsigned SPEC>
 hipError_t quantize_spec(const float *x, int64_t n, void *codes, uint16_t *scales, hipStream_t st)
 {
@@ -1649,25 +1680,15 @@ hipError_t launch_dequantize(const void *codes, const uint16_t *scales, int64_t 
 hipError_t launch_split(const float *master, int64_t n, int master_bits, uint16_t *param,
                         void *rho, hipStream_t st)
 {
-    if (master_bits == 32)
-        hipLaunchKernelGGL(split_kernel<32>, dim3(grid_for(n)), dim3(kBlockThreads), 0, st,
-                           master, n, param, rho);
-    else
-        hipLaunchKernelGGL(split_kernel<24>, dim3(grid_for(n)), dim3(kBlockThreads), 0, st,
-                           master, n, param, rho);
-    return hipGetLastError();
+    if (master_bits == 32) return launch_flat(split_kernel<32>, n, st, master, n, param, rho);
+    return launch_flat(split_kernel<24>, n, st, master, n, param, rho);
 }
 
 hipError_t launch_reconstruct(const uint16_t *param, const void *rho, int64_t n, int master_bits,
                               float *master, hipStream_t st)
 {
-    if (master_bits == 32)
-        hipLaunchKernelGGL(reconstruct_kernel<32>, dim3(grid_for(n)), dim3(kBlockThreads), 0, st,
-                           param, rho, n, master);
-    else
-        hipLaunchKernelGGL(reconstruct_kernel<24>, dim3(grid_for(n)), dim3(kBlockThreads), 0, st,
-                           param, rho, n, master);
-    return hipGetLastError();
+    if (master_bits == 32) return launch_flat(reconstruct_kernel<32>, n, st, param, rho, n, master);
+    return launch_flat(reconstruct_kernel<24>, n, st, param, rho, n, master);
 }
 
 namespace {

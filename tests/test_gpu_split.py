@@ -119,3 +119,22 @@ def test_tensor_past_2_31_elements(orc, mb):
     print(f"split {mb}-bit, 2^31 + 1101 elements: samples bit-exact", flush=True)
     del x, p, r, back
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mb", [24, 32])
+def test_split_across_launches(orc, mb, monkeypatch):
+    """A split and reconstruct cut into launches of 7 chunks of 1024
+    elements (FLASHOPT_LAUNCH_CHUNKS, the launch-size hook): every element
+    of a ragged 100-chunk tensor matches the oracle."""
+    require_gpu()
+    monkeypatch.setenv("FLASHOPT_LAUNCH_CHUNKS", "7")
+    n = 99 * 1024 + 333
+    gen = torch.Generator(device="cuda").manual_seed(7 + mb)
+    x = torch.randn(n, generator=gen, device="cuda").mul_(0.02)
+    p, r = F.flashopt_split(x, mb)
+    back = F.flashopt_reconstruct(p, r, mb)
+    torch.cuda.synchronize()
+    hp, hr = orc.split(host(x), mb)
+    assert (u16(p) == hp).all() and (host(r) == hr).all()
+    ob = orc.reconstruct(hp, hr, mb)
+    assert (host(back).view(np.uint32) == ob.view(np.uint32)).all()
