@@ -605,27 +605,37 @@ dequantize_kernel(const void *__restrict__ codes, const uint16_t *__restrict__ s
 
 // ------------------------------------------------------- standalone split
 
-// Element offset of the calling lane in the split and reconstruct kernels:
-// one 256-element unit per wavefront, 4 consecutive elements per lane (16
-// bytes of fp32), so that every access instruction of the wavefront covers
-// one contiguous block of each stream; a workgroup takes one 1024-element
-// chunk, a launch the chunks from `base` on.  One unit per wavefront streams
-// faster here than a whole chunk per wavefront (one load and one store
-// instruction per stream and wavefront).
-__device__ __forceinline__ int64_t split_lane_first(int64_t base)
+// Element offset of unit u of the calling lane in the split and reconstruct
+// kernels: a wavefront takes U consecutive 256-element units, 4 consecutive
+// elements per lane and unit (16 bytes of fp32), so that every access
+// instruction of the wavefront covers one contiguous block of each stream; a
+// workgroup takes 1024 U elements (a "block" of launch_flat), a launch the
+// blocks from `base` on.  One unit per wavefront streams faster for the
+// split and the 24-bit reconstruct (one load and one store instruction per
+// stream and wavefront; 6-8% over four units), four units for the 32-bit
+// reconstruct (3%).
+template <int U>
+__device__ __forceinline__ int64_t split_lane_first(int64_t base, int u)
 {
-    return (base + blockIdx.x) * kChunkElems + 4 * static_cast<int64_t>(threadIdx.x);
+    const int64_t wave = (base + blockIdx.x) * (kBlockThreads / kWaveLanes) + (threadIdx.x >> 6);
+    return wave * (256 * U) + 256 * u + 4 * static_cast<int64_t>(threadIdx.x & 63u);
 }
+
+// Units per wavefront of the split (S) and reconstruct (R) kernels, by
+// master width.
+constexpr int split_units(int mb, bool reconstruct) { return reconstruct && mb == 32 ? 4 : 1; }
 
 template <int MB>
 __global__ void __launch_bounds__(kBlockThreads)
 split_kernel(const float *__restrict__ master, int64_t n, uint16_t *__restrict__ param,
              void *__restrict__ rho, int64_t base)
 {
-    {
-        const int64_t e = split_lane_first(base);
+    constexpr int U = split_units(MB, false);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t e = split_lane_first<U>(base, u);
         const int cnt = quad_count(n, e);
-        if (cnt == 0) return;
+        if (cnt == 0) continue;
         float x[4];
         if (cnt == 4) {
             const uint4 v = ld16s(master + e);
@@ -663,10 +673,12 @@ __global__ void __launch_bounds__(kBlockThreads)
 reconstruct_kernel(const uint16_t *__restrict__ param, const void *__restrict__ rho, int64_t n,
                    float *__restrict__ master, int64_t base)
 {
-    {
-        const int64_t e = split_lane_first(base);
+    constexpr int U = split_units(MB, true);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t e = split_lane_first<U>(base, u);
         const int cnt = quad_count(n, e);
-        if (cnt == 0) return;
+        if (cnt == 0) continue;
         uint32_t pw[2] = {0u, 0u}, rw[MB == 32 ? 2 : 1] = {};
         if (cnt == 4) {
             const u32x2 p2 = ld8s(param + e);
@@ -1609,17 +1621,18 @@ unsigned grid_for(int64_t n)
 
 int64_t launch_chunks(int units_per_chunk);
 
-// Launches of a split or reconstruct kernel over the 1024-element chunks of
-// n elements, one workgroup per chunk and at most launch_chunks(4) chunks per
-// launch (in order on one stream); each launch gets its first chunk after
-// the arguments passed through.
-template <typename Kernel, typename... Args>
+// Launches of a split or reconstruct kernel with U units per wavefront over
+// n elements: one workgroup per block of 1024 U elements, at most
+// launch_chunks(4) blocks per launch (in order on one stream); each launch
+// gets its first block after the arguments passed through.
+template <int U, typename Kernel, typename... Args>
 hipError_t launch_flat(Kernel kernel, int64_t n, hipStream_t st, Args... args)
 {
-    const int64_t chunks = (n + kChunkElems - 1) / kChunkElems;
-    const int64_t per = launch_chunks(kLaneElems / 4);
-    for (int64_t base = 0; base < chunks; base += per) {
-        const int64_t k = chunks - base < per ? chunks - base : per;
+    const int64_t per_block = static_cast<int64_t>(kChunkElems) * U;
+    const int64_t blocks = (n + per_block - 1) / per_block;
+    const int64_t per = launch_chunks(kBlockThreads / kWaveLanes);
+    for (int64_t base = 0; base < blocks; base += per) {
+        const int64_t k = blocks - base < per ? blocks - base : per;
         hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(k)), dim3(kBlockThreads), 0, st,
                            args..., base);
         const hipError_t e = hipGetLastError();
@@ -1680,15 +1693,17 @@ hipError_t launch_dequantize(const void *codes, const uint16_t *scales, int64_t 
 hipError_t launch_split(const float *master, int64_t n, int master_bits, uint16_t *param,
                         void *rho, hipStream_t st)
 {
-    if (master_bits == 32) return launch_flat(split_kernel<32>, n, st, master, n, param, rho);
-    return launch_flat(split_kernel<24>, n, st, master, n, param, rho);
+    if (master_bits == 32)
+        return launch_flat<split_units(32, false)>(split_kernel<32>, n, st, master, n, param, rho);
+    return launch_flat<split_units(24, false)>(split_kernel<24>, n, st, master, n, param, rho);
 }
 
 hipError_t launch_reconstruct(const uint16_t *param, const void *rho, int64_t n, int master_bits,
                               float *master, hipStream_t st)
 {
-    if (master_bits == 32) return launch_flat(reconstruct_kernel<32>, n, st, param, rho, n, master);
-    return launch_flat(reconstruct_kernel<24>, n, st, param, rho, n, master);
+    if (master_bits == 32)
+        return launch_flat<split_units(32, true)>(reconstruct_kernel<32>, n, st, param, rho, n, master);
+    return launch_flat<split_units(24, true)>(reconstruct_kernel<24>, n, st, param, rho, n, master);
 }
 
 namespace {

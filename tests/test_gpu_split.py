@@ -123,9 +123,10 @@ def test_tensor_past_2_31_elements(orc, mb):
 
 @pytest.mark.parametrize("mb", [24, 32])
 def test_split_across_launches(orc, mb, monkeypatch):
-    """A split and reconstruct cut into launches of 7 chunks of 1024
-    elements (FLASHOPT_LAUNCH_CHUNKS, the launch-size hook): every element
-    of a ragged 100-chunk tensor matches the oracle."""
+    """A split and reconstruct cut into launches of 7 workgroups
+    (FLASHOPT_LAUNCH_CHUNKS, the launch-size hook; a workgroup takes 1024
+    elements, 4096 in the 32-bit reconstruct): every element of a ragged
+    tensor of 99 * 1024 + 333 elements matches the oracle."""
     require_gpu()
     monkeypatch.setenv("FLASHOPT_LAUNCH_CHUNKS", "7")
     n = 99 * 1024 + 333
