@@ -92,10 +92,15 @@ def traffic_per_launch():
 
 def valu_roofline(ms_launch: float, sclk_mhz=None):
     """The step's second roof: its VALU wavefront instructions per launch
-    (committed counter record) at the peak issue rate, against the measured
+    (committed counter record) at a modelled peak issue rate (one wavefront
+    instruction per SIMD every 4 cycles at 2.4 GHz), against the measured
     launch time; also at the shader clock the GPU reported right after the
-    timed steps (the chip runs below 2.4 GHz under this load).  None when the
-    record is stale."""
+    timed steps and at the clock the counters saw during the step
+    (GRBM_GUI_ACTIVE cycles over the launch's duration).  The counters also
+    give the VALU instructions each SIMD issued per 4 cycles of the step: a
+    value above 1 means that the hardware co-issues VALU instructions and the
+    one-per-4-cycles model overstates the VALU time.  None when the record is
+    stale."""
     rec = _counter_record()
     if rec is None or not rec.get("valu_insts_per_launch"):
         return None
@@ -109,6 +114,11 @@ def valu_roofline(ms_launch: float, sclk_mhz=None):
         peak_clk = PEAK_VALU_LANE_INSTS * sclk_mhz / 2400.0
         out.update(sclk_mhz=sclk_mhz, peak_at_sclk=peak_clk, frac_at_sclk=achieved / peak_clk,
                    ms_at_sclk=lane_insts / peak_clk * 1e3)
+    step_clk = rec.get("sclk_mhz_during_step")
+    if step_clk:
+        peak_step = PEAK_VALU_LANE_INSTS * step_clk / 2400.0
+        out.update(sclk_mhz_during_step=step_clk, frac_at_step_clock=achieved / peak_step,
+                   valu_insts_per_simd_quad_cycle=rec.get("valu_insts_per_simd_quad_cycle"))
     return out
 
 
