@@ -163,21 +163,42 @@ flashopt_status adamw_scalars(const flashopt_adamw_args *a, StepScalars &sc)
     sc.lr = static_cast<float>(a->lr);
     sc.eps = static_cast<float>(a->eps);
     // 1 - beta^t >= 1 - beta >= 2^-53 for beta in [0, 1): positive and normal
-    sc.inv_bc1 = 1.0 / static_cast<double>(sc.bc1);
-    sc.inv_bc2 = 1.0 / static_cast<double>(sc.bc2);
     sc.inv_bc2s = 0x1p64 / static_cast<double>(sc.bc2);
+    {
+        // 1 / bc1 correctly rounded to fp32: the neighbour of the double
+        // quotient rounded to float with the smallest residual |r bc1 - 1|
+        // (exact in double: a product of two floats)
+        float r = static_cast<float>(1.0 / static_cast<double>(sc.bc1));
+        const float cand[3] = {std::nextafter(r, 0.0f), r, std::nextafter(r, INFINITY)};
+        double best = INFINITY;
+        for (float c : cand) {
+            const double e = std::fabs(static_cast<double>(c) * static_cast<double>(sc.bc1) - 1.0);
+            if (e < best) { best = e; r = c; }
+        }
+        sc.rbc1 = r;
+    }
     sc.unit_bc = (sc.bc1 == 1.0f && sc.bc2 == 1.0f) ? 1 : 0;
     sc.lr2 = sc.lr * 0x1p32f;
     sc.eps2 = sc.eps * 0x1p32f;
     sc.kv = static_cast<float>(255.0 * std::sqrt(static_cast<double>(sc.bc2)) * 0x1p-32);
-    // The kernel's short route (see step_unit): its sqrt returns sqrt(vhat)
-    // 2^32, except a value below 2^-31 (not the exact root) for a subnormal or
-    // zero vhat, which vanishes next to eps2 (half an ulp of eps2 is at least
-    // 2^-30 while eps >= 2^-38); the short division
-    // needs denominators in [2^-100, 2^100] (eps2 >= 2^-6 and sqrt(vhat)
-    // 2^32 < 2^64) and numerators of at most 2^100 eps2 and, when nonzero, at
-    // least 2^-61.
-    sc.fast = (sc.eps >= 0x1p-38f && sc.eps <= 0x1p60f) ? 1 : 0;
+    // The kernel's short route (step_finish) is exact under these bounds.
+    // Its sqrt returns sqrt(vhat) 2^32, except a value below 2^-31 (not the
+    // exact root) for a subnormal or zero vhat, which vanishes next to eps2
+    // (half an ulp of eps2 is at least 2^-30 while eps >= 2^-38).  The short
+    // division needs denominators in [2^-100, 2^100] (eps2 >= 2^-6 and
+    // sqrt(vhat) 2^32 < 2^64) and numerators of at most 2^100 eps2 and, when
+    // nonzero, at least 2^-61 (the lane checks both).  mhat = m1 / bc1 comes
+    // from div_markstein with rbc1, exact for m1 = 0 and for 2^-102 <= |m1|
+    // <= 2^100 bc1 (bc1 is in [2^-53, 1]); |m1| <= m1_max <= 2^99 bc1 covers
+    // the upper end.  A nonzero |m1| below 2^-102 gives |mhat| < 2^-101 / bc1
+    // (up to a few units of 2^-149), so with lr <= 2^6 bc1 its numerator
+    // lr2 mhat stays below 2^-61 and the lane takes the generic route; with
+    // lr >= 2^-32 (lr2 >= 1) no nonzero mhat gives a zero numerator, and
+    // lr = 0 gives the zero numerator of the exact evaluation.
+    sc.fast = (sc.eps >= 0x1p-38f && sc.eps <= 0x1p60f &&
+               (sc.lr == 0.0f ||
+                (sc.lr >= 0x1p-32f && static_cast<double>(sc.lr) <= 0x1p6 * static_cast<double>(sc.bc1))))
+                  ? 1 : 0;
     // vhat = v1 / bc2 < 2^63  <=  v1 < 2^63 bc2 (rounded down to fp32)
     {
         float vb = static_cast<float>(0x1p63 * static_cast<double>(sc.bc2));
@@ -187,11 +208,13 @@ flashopt_status adamw_scalars(const flashopt_adamw_args *a, StepScalars &sc)
         std::memcpy(&bits, &vb, 4);
         sc.v1_bound = bits;
     }
-    // |lr2 mhat| <= 2^100 eps2 holds when lr2 |m1| / bc1 (1 + 2^-20) does
+    // |lr2 mhat| <= 2^100 eps2 holds when lr2 |m1| / bc1 (1 + 2^-20) does;
+    // |m1| <= 2^99 bc1 keeps mhat's division in its exact range
     sc.m1_max = sc.lr2 > 0.0f
         ? static_cast<float>(0x1p100 * static_cast<double>(sc.eps2) * static_cast<double>(sc.bc1) /
                              (static_cast<double>(sc.lr2) * (1.0 + 0x1p-20)))
         : INFINITY;
+    sc.m1_max = std::fmin(sc.m1_max, static_cast<float>(0x1p99 * static_cast<double>(sc.bc1)));
     {
         const float tmin = 0x1p-61f;
         uint32_t bits;

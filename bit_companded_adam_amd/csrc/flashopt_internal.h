@@ -42,12 +42,10 @@ struct DevTensor {
 static_assert(sizeof(DevTensor) == 64, "descriptor layout");
 
 // Scalars of one step.  The fp32 ones are formed in double on the host and
-// rounded once (a Python float meeting a float32 tensor); the fp64 ones are
-// the reciprocals of the fp32 bias corrections, for the exact quotient route
-// of the kernel (div_by_f64_recip).
+// rounded once (a Python float meeting a float32 tensor); rbc1 and inv_bc2s
+// serve the kernel's exact short routes for the bias-correction quotients
+// (div_markstein with rbc1; sqrt_quot_x2p32 with inv_bc2s).
 struct StepScalars {
-    double inv_bc1;     // 1 / bc1 in double (bc1 the fp32 value below)
-    double inv_bc2;     // 1 / bc2 in double
     double inv_bc2s;    // 2^64 / bc2 in double: vhat 2^64 inside sqrt_quot_x2p32
     float cwd;          // 1 - lr * wd
     float b1;           // beta1
@@ -60,11 +58,12 @@ struct StepScalars {
     float eps;
     float lr2;          // lr 2^32 (exact): the numerator's scale on the short route
     float eps2;         // eps 2^32 (exact): the denominator's scale on the short route
+    float rbc1;         // 1 / bc1 correctly rounded to fp32
     float kv;           // 255 sqrt(bc2) 2^-32: the variance codes' factor from sqrt(vhat) 2^32
-    float m1_max;       // |m1| up to this keeps every |lr mhat 2^32| <= 2^100 eps2
+    float m1_max;       // |m1| up to this keeps |lr mhat 2^32| <= 2^100 eps2 and |m1| <= 2^99 bc1
     uint32_t v1_bound;  // v1 bit patterns below this keep vhat below 2^63
     uint32_t num_key;   // (pattern << 1) - 1 of the smallest nonzero |lr mhat 2^32| allowed
-    int fast;           // 1 when eps lets the short route absorb vhat = 0 and subnormal vhat (eps >= 2^-38)
+    int fast;           // 1 when eps and lr keep the short routes exact (see adamw_scalars)
     int unit_bc;        // 1 when bc1 and bc2 are both exactly 1 (late in training)
 };
 // The list step kernels (AdamW and FlashSGD) read their scalars from device

@@ -24,10 +24,11 @@
 // (built with -ffp-contract=off, fp32 and fp16 denormals preserved), so the
 // results match a plain CPU evaluation bit for bit.  The update follows the
 // operation order FlashAdamWSim.step prints: the bias-correction quotients
-// come from fp64 products with host-computed reciprocals (exact once rounded
-// to fp32), and division by a group scale, the softsign division, the update
-// division, the sqrt and the byte conversions use the exact short sequences
-// of flashopt_math.h instead of the generic correctly rounded expansions.
+// use host-computed reciprocals (a Markstein step for m / bc1, one fp64 fma
+// for v / bc2, both exact), and division by a group scale, the softsign
+// division, the update division, the sqrt and the byte conversions use the
+// exact short sequences of flashopt_math.h instead of the generic correctly
+// rounded expansions.
 // The momentum and variance codes use two-sided short forms; a word whose two
 // evaluations disagree falls back to the correctly rounded chain.
 
@@ -287,6 +288,14 @@ __device__ __forceinline__ float reconstruct_elem(uint32_t hi_shifted, int32_t r
 {
     const uint32_t add = (MB == 24) ? (static_cast<uint32_t>(rho) << 8) : static_cast<uint32_t>(rho);
     return __uint_as_float(hi_shifted + add);
+}
+
+// p + e elements with the byte offset formed in 32 bits, so that the access
+// takes the scalar base plus a 32-bit lane offset (e sizeof(T) < 2^32).
+template <typename T>
+__device__ __forceinline__ T *at(T *p, uint32_t e)
+{
+    return reinterpret_cast<T *>(reinterpret_cast<uintptr_t>(p) + static_cast<uint32_t>(e * sizeof(T)));
 }
 
 // Global-address-space views: loads and stores become global_* with an
@@ -917,17 +926,17 @@ __device__ __forceinline__ void load_unit(const ChunkPtrs &c, uint32_t r, int cn
     in.svb = 0u;
     if (FULL) {
         if constexpr (MB == kParamF32) {
-            ld_words<4 * N>(c.param32 + r, in.pw);
-            ld_words<4 * N>(c.grad32 + r, in.gw);
+            ld_words<4 * N>(at(c.param32, r), in.pw);
+            ld_words<4 * N>(at(c.grad32, r), in.gw);
         } else {
-            ld_words<2 * N>(c.param + r, in.pw);
-            ld_words<2 * N>(c.grad + r, in.gw);
+            ld_words<2 * N>(at(c.param, r), in.pw);
+            ld_words<2 * N>(at(c.grad, r), in.gw);
         }
         if constexpr (MB == 24) ld_words<N>(c.rho8 + r, in.rw);
-        if constexpr (MB == 32) ld_words<2 * N>(c.rho16 + r, in.rw);
+        if constexpr (MB == 32) ld_words<2 * N>(at(c.rho16, r), in.rw);
         if constexpr (ST == kStatesFp32) {
-            ld_words<4 * N>(c.mf + r, in.mf);
-            if constexpr (V) ld_words<4 * N>(c.vf + r, in.vf);
+            ld_words<4 * N>(at(c.mf, r), in.mf);
+            if constexpr (V) ld_words<4 * N>(at(c.vf, r), in.vf);
         } else {
             ld_words<N>(c.mc + r, in.mw);
             in.smb = ld_u16(c.ms + r / kGroup);
@@ -1174,8 +1183,9 @@ __device__ __forceinline__ void step_finish(const ChunkPtrs &c, uint32_t r, int 
     for (int j = 1; j < N; ++j) am = fmaxf(am, fabsf(m1[j]));
 
     // ---- the update in the page's order: mhat = m1 / bc1, vhat = v1 / bc2,
-    // theta1 = thd - (lr mhat) / (sqrt(vhat) + eps).  mhat is an exact
-    // fp64-reciprocal quotient; sq = sqrt(vhat) 2^32 comes from
+    // theta1 = thd - (lr mhat) / (sqrt(vhat) + eps).  mhat comes from
+    // div_markstein with the correctly rounded 1 / bc1 (exact for the m1 the
+    // checks below let through, with the host's bound on lr); sq = sqrt(vhat) 2^32 comes from
     // sqrt_quot_x2p32 (vhat formed inside it; a subnormal or zero vhat gives
     // sq below 2^-31 instead of its exact root, lost in sq + eps2 while
     // eps >= 2^-38), and the division runs on the
@@ -1203,7 +1213,7 @@ __device__ __forceinline__ void step_finish(const ChunkPtrs &c, uint32_t r, int 
     } else {
 #pragma unroll
         for (int j = 0; j < N; ++j) {
-            const float mhat = math::div_by_f64_recip(m1[j], sc.inv_bc1);
+            const float mhat = math::div_markstein(m1[j], sc.bc1, sc.rbc1);
             sq[j] = math::sqrt_quot_x2p32(v1[j], sc.inv_bc2s);
             const float den = sq[j] + sc.eps2;
             const float num = sc.lr2 * mhat;
@@ -1266,16 +1276,16 @@ __device__ __forceinline__ void step_finish(const ChunkPtrs &c, uint32_t r, int 
 #pragma unroll
     for (int j = 0; j < N; ++j) { mb[j] = __float_as_uint(m1[j]); vb[j] = __float_as_uint(v1[j]); }
     if (FULL) {
-        if constexpr (MB == kParamF32) st_words<4 * N>(c.param32 + r, po);
-        else st_words<2 * N>(c.param + r, po);
+        if constexpr (MB == kParamF32) st_words<4 * N>(at(c.param32, r), po);
+        else st_words<2 * N>(at(c.param, r), po);
         if constexpr (MB == 24) st_words<N>(c.rho8 + r, ro);
-        if constexpr (MB == 32) st_words<2 * N>(c.rho16 + r, ro);
+        if constexpr (MB == 32) st_words<2 * N>(at(c.rho16, r), ro);
         if constexpr (kQuant) {
             st_words<N>(c.mc + r, mo);
             st_words<N>(c.vc + r, vo);
         } else {
-            st_words<4 * N>(c.mf + r, mb);
-            st_words<4 * N>(c.vf + r, vb);
+            st_words<4 * N>(at(c.mf, r), mb);
+            st_words<4 * N>(at(c.vf, r), vb);
         }
     } else {
         if constexpr (MB == kParamF32) st_elems<4, N>(c.param32 + r, cnt, po);
@@ -1368,9 +1378,9 @@ __device__ __forceinline__ void sgd_finish(const ChunkPtrs &c, uint32_t r, int c
 #pragma unroll
     for (int j = 0; j < N; ++j) bb[j] = __float_as_uint(b1[j]);
     if (FULL) {
-        st_words<2 * N>(c.param + r, po);
+        st_words<2 * N>(at(c.param, r), po);
         if constexpr (MB == 24) st_words<N>(c.rho8 + r, ro);
-        if constexpr (MB == 32) st_words<2 * N>(c.rho16 + r, ro);
+        if constexpr (MB == 32) st_words<2 * N>(at(c.rho16, r), ro);
         if constexpr (kQuant) st_words<N>(c.mc + r, mo);
         else st_words<4 * N>(c.mf + r, bb);
     } else {
@@ -1427,19 +1437,20 @@ __device__ __forceinline__ void for_each_unit(const DevTensor *__restrict__ tens
                                               int32_t chunk_end, Load &&load, Tables &&tables,
                                               Finish &&finish)
 {
-    // a launch has at most 2^24 workgroups (its work-items fit in 32 bits)
-    const int32_t wave = __builtin_amdgcn_readfirstlane(
-        static_cast<int32_t>(xcd_contiguous_block()) * (kBlockThreads / kWaveLanes) +
-        static_cast<int32_t>(threadIdx.x >> 6));
-    const int unit = wave % W;
-    const int64_t c64 = static_cast<int64_t>(chunk_base) + wave / W;
-    const bool any = c64 < chunk_end;
+    // a launch has at most 2^24 workgroups (its work-items fit in 32 bits);
+    // every quantity here is uniform and stays in scalar registers
+    const uint32_t wave = xcd_contiguous_block() * (kBlockThreads / kWaveLanes) +
+                          (__builtin_amdgcn_readfirstlane(threadIdx.x) >> 6);
+    const int unit = static_cast<int>(wave % W);
+    // chunk_base + wave / W < 2^31 + 2^25 fits in 32 unsigned bits
+    const uint32_t cu = static_cast<uint32_t>(chunk_base) + wave / W;
+    const bool any = cu < static_cast<uint32_t>(chunk_end);
     ChunkPtrs cp{};
     if (any) {
         // chunk indices fit in int32 (the host caps the total), so the
         // search compares in scalar registers: the last tensor whose first
         // chunk is <= c
-        const int32_t c = static_cast<int32_t>(c64);
+        const int32_t c = static_cast<int32_t>(cu);
         int lo = 0, hi = n_tensors - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;

@@ -15,8 +15,9 @@
 //                  NaN -> 0);
 //   div_markstein  2^32 random pairs of its stated domain plus every divisor
 //                  significand at the domain's edges;
-//   div_by_f64_recip  every fp32 dividend significand (both signs, normal and
-//                  subnormal) x a set of bias-correction and random divisors;
+//   div_markstein with a bias correction as divisor  every dividend
+//                  significand (both signs, hashed exponents over the step's
+//                  range) x a set of bias-correction and random divisors;
 //   code_s8_magic  every fp32 p (low byte == clamp(rint(p), -127, 127) as a
 //                  two's-complement byte, for non-NaN p);
 //   softsign_code_bytes  (not exact itself: two-sided) 4095 fp16 divisors x
@@ -25,7 +26,7 @@
 //                  the byte is the correctly rounded chain's code (and the
 //                  sweep reaches inputs where the bytes disagree).
 // Only fma, mul, add, v_rcp_f32 / v_rsq_f32, fp32 <-> fp64 conversions, an
-// fp64 multiply and integer ops are used, so the results do not depend on the
+// fp64 fma and integer ops are used, so the results do not depend on the
 // FP mode beyond round-to-nearest-even with fp32 and fp64 denormals kept.
 #pragma once
 
@@ -85,20 +86,6 @@ __device__ __forceinline__ float div_markstein(float num, float den, float r)
     const float q0 = num * r;
     const float e = __builtin_fmaf(q0, den, -num);
     return __builtin_fmaf(-e, r, q0);
-}
-
-// Correctly rounded fp32 quotient a / b for an fp32 divisor b > 0, given
-// inv = 1 / b rounded to double: the double product a inv lies within
-// 2^-51.9 |a / b| of the quotient, while no quotient of two fp32 numbers lies
-// that close to a rounding boundary of fp32 without being on it (for a
-// midpoint M of the result's binade, a - b M is a nonzero multiple of
-// ulp(b) ulp(M) / 2, so |a / b - M| > 2^-25 ulp(M) >= 2^-49 |a / b|; in the
-// subnormal range the bound is absolute and far larger than the error).
-// Rounding the product to fp32 therefore gives a / b correctly rounded, for
-// every fp32 a: subnormal quotients, signed zeros, overflow to infinity.
-__device__ __forceinline__ float div_by_f64_recip(float a, double inv)
-{
-    return static_cast<float>(static_cast<double>(a) * inv);
 }
 
 // Signed 8-bit code of p = y * 127 in the low byte of the result: clamp to
@@ -204,8 +191,12 @@ __device__ __forceinline__ float sqrt_x2p32_zero_tiny(float x)
 // quotient and the 2^64 input scaling of sqrt_cr_x2p32 come out of one fp64
 // fma: xs = fl(v inv_s + 2^-126).  Where q is normal, v inv_s >= 2^-62, so
 // the added 2^-126 moves it by at most 2^-64 relative and the double result
-// lies within 2^-51.9 + 2^-64 relative of the scaled quotient, closer than
-// any fp32 rounding boundary (div_by_f64_recip): xs = q 2^64 exactly.  Where
+// lies within 2^-51.9 + 2^-64 relative of the scaled quotient.  No quotient
+// of two fp32 numbers lies that close to an fp32 rounding boundary without
+// being on it (for a midpoint M of the result's binade, v - b M is a nonzero
+// multiple of ulp(b) ulp(M) / 2, so |v / b - M| > 2^-25 ulp(M) >= 2^-49
+// |v / b|), and none lies on one (b M would need 25 significant bits), so
+// rounding to fp32 gives xs = q 2^64 exactly.  Where
 // q is subnormal or zero, xs <= 2^-62 (2^-126 for v = 0, a normal number,
 // which keeps v_rsq_f32 finite: it flushes subnormal inputs) and the result
 // is below 2^-31 rather than q's exact root.  Domain: q < 2^63.

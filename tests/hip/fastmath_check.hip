@@ -219,25 +219,33 @@ __device__ __forceinline__ float bias_divisor(uint32_t k)
     return __uint_as_float(((107u + h % 21u) << 23) | (h >> 9));
 }
 
-// div_by_f64_recip against the correctly rounded division for every divisor
-// above x every dividend significand in [1, 2) with both signs, plus 2^16
-// subnormal dividends per divisor and dividends near the top of the range.
-__global__ void k_div_f64_recip(unsigned long long *bad)
+// The bias-correction quotient m / bc of the step: div_markstein with the
+// correctly rounded reciprocal of bc (recip_cr) against the correctly rounded
+// division, for every divisor above x every dividend significand with both
+// signs, at a hashed exponent per significand from 2^-102 up to 2^85 (the
+// range where the step takes this route: |m| >= 2^-102 and |m| <= 2^99 bc,
+// bc >= 1e-4 here), plus the range's two ends and zero.
+__global__ void k_div_bias(unsigned long long *bad)
 {
     unsigned long long c = 0;
     for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (8192ull << 23);
          i += (uint64_t)gridDim.x * blockDim.x) {
         const float d = bias_divisor((uint32_t)(i >> 23));
-        const double inv = 1.0 / (double)d;
+        const float r = recip_cr(d);
         const uint32_t sig = (uint32_t)i & 0x7FFFFFu;
-        const float a = __uint_as_float(0x3F800000u | sig);
-        c += !same(div_by_f64_recip(a, inv), a / d);
-        c += !same(div_by_f64_recip(-a, inv), (-a) / d);
-        if (sig < 65536u) {
-            const float s = __uint_as_float(mix(i, 5) & 0x807FFFFFu);          // subnormal or zero
-            c += !same(div_by_f64_recip(s, inv), s / d);
-            const float big = __uint_as_float(0x7E800000u | (mix(i, 6) & 0x807FFFFFu));  // 2^126 .. 2^127
-            c += !same(div_by_f64_recip(big, inv), big / d);
+        const uint32_t e = 25u + mix(i, 7) % 188u;                  // biased exponent: 2^-102 .. 2^85
+        const float a = __uint_as_float((e << 23) | sig);
+        c += !same(div_markstein(a, d, r), a / d);
+        c += !same(div_markstein(-a, d, r), (-a) / d);
+        if (sig < 4096u) {
+            const float lo = __uint_as_float((25u << 23) | (mix(i, 8) & 0x807FFFFFu));   // |a| in [2^-102, 2^-101)
+            c += !same(div_markstein(lo, d, r), lo / d);
+            const float hi = __uint_as_float((212u << 23) | (mix(i, 9) & 0x807FFFFFu));  // |a| in [2^85, 2^86)
+            c += !same(div_markstein(hi, d, r), hi / d);
+        }
+        if (sig == 0u) {
+            c += !same(div_markstein(0.0f, d, r), 0.0f / d);
+            c += !same(div_markstein(-0.0f, d, r), -0.0f / d);
         }
     }
     flush(bad, c);
@@ -287,7 +295,7 @@ long long fastmath_check_div_by_recip(void) { return run(k_div_by_recip, 65536);
 long long fastmath_check_softsign(void) { return run(k_softsign, 65536); }
 long long fastmath_check_cvt_pk_u8(void) { return run(k_cvt_pk_u8, 65536); }
 long long fastmath_check_div_markstein(void) { return run(k_div_markstein, 65536); }
-long long fastmath_check_div_f64_recip(void) { return run(k_div_f64_recip, 65536); }
+long long fastmath_check_div_bias(void) { return run(k_div_bias, 65536); }
 long long fastmath_check_sqrt_quot(void) { return run(k_sqrt_quot, 65536); }
 long long fastmath_check_magic_code(void) { return run(k_magic_code, 65536); }
 long long fastmath_check_softsign_code(void) { return run(k_softsign_code<true>, 65536); }

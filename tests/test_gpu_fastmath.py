@@ -24,7 +24,7 @@ from tests._gpu import require_gpu
 pytestmark = pytest.mark.gpu
 
 LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hip", "libfastmath_check.so")
-CHECKS = ["sqrt", "recip", "div_by_recip", "softsign", "cvt_pk_u8", "div_markstein", "div_f64_recip",
+CHECKS = ["sqrt", "recip", "div_by_recip", "softsign", "cvt_pk_u8", "div_markstein", "div_bias",
           "sqrt_quot", "magic_code", "softsign_code"]
 
 

@@ -161,7 +161,9 @@ def test_ragged_list(orc, mb, comp, qs):
 # step).  beta 0 (no averaging), beta2 0.9999 (a small bias correction),
 # bias corrections at 1 (step 10^6; and steps 17320-17322, where the second
 # one reaches 1 and the step switches to its late-training route), learning
-# rates 0 and 1e-6 to 1, no weight decay, a large eps.
+# rates 0, 1e-10 and 1e-6 to 1 (1e-10, and 1e-2 with beta1 0.9999 at step 1,
+# lie outside the short route's learning-rate range: the whole step takes the
+# generic route), no weight decay, a large eps.
 HP_GRID = [
     ("betas_zero", dict(betas=(0.0, 0.0)), 1),
     ("beta2_0.9999", dict(betas=(0.5, 0.9999)), 1),
@@ -172,6 +174,10 @@ HP_GRID = [
     ("lr_1e-6_wd_0", dict(lr=1e-6, weight_decay=0.0), 5),
     ("eps_1e-3", dict(eps=1e-3), 2),
     ("lr_0", dict(lr=0.0, weight_decay=0.1), 1),       # the master must come back unchanged
+    # lr above 2^6 (1 - beta1^t): the whole step takes the generic route
+    ("beta1_0.9999_lr_1e-2", dict(betas=(0.9999, 0.999), lr=1e-2), 1),
+    # lr below 2^-32: the generic route as well
+    ("lr_1e-10", dict(lr=1e-10), 1),
 ]
 
 
