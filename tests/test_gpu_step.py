@@ -330,6 +330,13 @@ def _edge_grad(case: str, n: int, t: int) -> torch.Tensor:
                                                           # short routes' range: all lanes generic
     elif case == "eps_zero":
         g[lane % 4 == 3] = 0.0                            # 0 / 0 without eps
+    elif case == "tiny_at_lr_bound":
+        # lr just below 2^6 (1 - beta1^t) at t = 1 (beta1 0.9999): |m1| below
+        # 2^-102, where m1 / bc1 may be inexact, must still reach the generic
+        # route through its numerator
+        g[(lane % 3 == 0) & (idx % 16 == 5)] *= 1e-33
+        g[lane % 7 == 1] *= 1e-30
+        g[lane % 11 == 4] *= 1e-35                        # bf16 subnormals among them
     elif case == "nonfinite":
         g[100 * 16 + 3] = float("inf")
         g[130 * 16 + 9] = float("nan")
@@ -337,7 +344,9 @@ def _edge_grad(case: str, n: int, t: int) -> torch.Tensor:
     return g.to(torch.bfloat16).to("cuda")
 
 
-EDGE_EPS = {"tiny_mixed": 1e-8, "large_m_small_eps": 1e-30, "eps_zero": 0.0, "nonfinite": 1e-8}
+EDGE_EPS = {"tiny_mixed": 1e-8, "large_m_small_eps": 1e-30, "eps_zero": 0.0, "nonfinite": 1e-8,
+            "tiny_at_lr_bound": 1e-8}
+EDGE_HP = {"tiny_at_lr_bound": dict(betas=(0.9999, 0.999), lr=6e-3)}
 
 
 @pytest.mark.parametrize("mb,comp,qs", [(24, True, True), (32, False, True), (None, True, False)],
@@ -350,7 +359,7 @@ def test_lanes_outside_short_division_domain(orc, case, mb, comp, qs):
     match the oracle (ragged size: 17 chunks, the last one partial)."""
     require_gpu()
     n = 16 * 1024 + 77
-    hp = dict(HP, eps=EDGE_EPS[case])
+    hp = dict(HP, eps=EDGE_EPS[case], **EDGE_HP.get(case, {}))
     p = W.init_param(n, device="cuda", seed=90)
     (want,) = _start([p], mb, qs)
     opt = F.FlashAdamW([p], master_bits=mb, companded=comp, quantize_states=qs, **hp)
