@@ -3,8 +3,10 @@
 Workload: the 8,030,257,152-parameter decoder-shaped list (290 bf16 tensors:
 embedding and LM head 128256x4096, 32 layers of q/o 4096x4096, k/v
 4096x1024, gate/up 4096x14336, down 14336x4096, two norms of 4096), 24-bit
-master (int8 rho), companded int8/uint8 states with fp16 group-32 scales;
-one multi-tensor launch per step.  Inputs are synthetic and resident in HBM
+master (int8 rho), companded int8/uint8 states with fp16 group-32 scales
+(the optimizer's default chunk-blocked state layout; --state-layout streams
+keeps them as five arrays per tensor); one multi-tensor launch per step.
+Inputs are synthetic and resident in HBM
 before timing starts (bf16 weights ~ N(0, 0.02^2); one bf16 gradient set
 N(0, 1e-3^2) times a per-tensor lognormal factor, reused by every step).
 
@@ -128,7 +130,9 @@ WORKLOADS = {"decoder-8b-list": W.decoder_8b_shapes, "decoder-1b-list": W.decode
 
 def build_workload(master_bits: int, companded: bool, quantize_states: bool = True,
                    workload: str = "decoder-8b-list", optimizer: str = "adamw",
-                   param_fp32: bool = False):
+                   param_fp32: bool = False, state_layout=None):
+    """state_layout None: the binding's default (chunk-blocked for
+    FlashAdamW's quantized states, the per-tensor streams otherwise)."""
     shapes = WORKLOADS[workload]()
     dt = torch.float32 if param_fp32 else torch.bfloat16
     params = [W.init_param(W.numel(s), device="cuda", seed=W.PARAM_SEED + i, dtype=dt)
@@ -138,10 +142,12 @@ def build_workload(master_bits: int, companded: bool, quantize_states: bool = Tr
              for i, (_, s) in enumerate(shapes)]
     if optimizer == "sgd":
         opt = F.FlashSGD(params, master_bits=master_bits or None, companded=companded,
-                         quantize_states=quantize_states, **W.SGD_DEFAULT)
+                         quantize_states=quantize_states, state_layout=state_layout,
+                         **W.SGD_DEFAULT)
     else:
         opt = F.FlashAdamW(params, master_bits=master_bits or None, companded=companded,
-                           quantize_states=quantize_states, **W.HP_DEFAULT)
+                           quantize_states=quantize_states, state_layout=state_layout,
+                           **W.HP_DEFAULT)
     return opt, grads
 
 
@@ -465,6 +471,9 @@ def main():
     ap.add_argument("--first-step", type=int, default=1,
                     help="step count of the first (warm-up) step; from about 17321 on, with the "
                          "default betas, both bias corrections are 1 in fp32")
+    ap.add_argument("--state-layout", choices=["blocked", "streams"], default=None,
+                    help="optimizer state layout (default: the binding's: chunk-blocked for "
+                         "FlashAdamW's quantized states, the streams otherwise)")
     ap.add_argument("--param-fp32", action="store_true",
                     help="fp32 parameters and gradients (never split; needs --master-bits 0)")
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
@@ -496,7 +505,9 @@ def main():
         print("--param-fp32 needs --master-bits 0 and the AdamW step", file=sys.stderr)
         sys.exit(2)
     copy_gbs = None if args.no_copy_ref else copy_reference()
-    opt, grads = build_workload(mb, comp, qs, args.workload, args.optimizer, args.param_fp32)
+    opt, grads = build_workload(mb, comp, qs, args.workload, args.optimizer, args.param_fp32,
+                                args.state_layout)
+    layout = opt.states[0].state_layout if opt.states else "streams"
     opt.t = args.first_step - 1
     opt.ts = [opt.t] * len(opt.states)
     n = sum(s.param.numel() for s in opt.states)
@@ -525,8 +536,8 @@ def main():
     if not args.no_cpu_baseline and args.optimizer == "adamw":
         cpu = cpu_baseline(mb, comp, qs, args.cpu_threads, param_fp32=args.param_fp32)
     default = (args.workload, mb, comp, qs, args.optimizer, args.grad_release, args.param_fp32,
-               args.first_step, args.graph) == ("decoder-8b-list", 24, True, True, "adamw", False,
-                                                False, 1, False)
+               args.first_step, args.graph, layout) == ("decoder-8b-list", 24, True, True, "adamw",
+                                                        False, False, 1, False, "blocked")
     name = args.workload + ("" if comp else "-linear") + ("" if qs else "-fp32-states") + \
         ("-fp32-params" if args.param_fp32 else ("-no-split" if mb == 0 else "")) + \
         ("-flashsgd" if args.optimizer == "sgd" else "") + \
@@ -534,7 +545,9 @@ def main():
         (f"-batched-below-{args.batch_below}" if args.grad_release and args.batch_below else "") + \
         (f"-{args.release_streams}-streams" if args.grad_release and args.release_streams > 1 else "") + \
         (f"-from-step-{args.first_step}" if args.first_step != 1 else "") + \
-        ("-graph-replay" if args.graph else "")
+        ("-graph-replay" if args.graph else "") + \
+        (f"-{layout}-layout" if layout != ("blocked" if qs and args.optimizer == "adamw" else "streams")
+         else "")
 
     launches = 1
     if args.grad_release:
@@ -560,6 +573,7 @@ def main():
                    "master_bits": mb, "companded": comp, "quantized_states": qs,
                    "param_dtype": "fp32" if args.param_fp32 else "bf16",
                    "first_step": args.first_step,
+                   "state_layout": layout,
                    "bytes_per_param": bpp,
                    "launches_per_step": launches},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,

@@ -93,22 +93,61 @@ std::mutex g_ring_mutex;
 Ring g_rings[kMaxDevices];
 
 // Validation of one tensor of a step.  split: rho is used; quant: scales are
-// used; v: the variance streams are used.
-flashopt_status check_tensor(const flashopt_tensor &t, bool split, bool quant, bool v)
+// used; v: the variance streams are used; blocked: the state is one
+// chunk-blocked buffer at rho, and the other state pointers are NULL.
+flashopt_status check_tensor(const flashopt_tensor &t, bool split, bool quant, bool v, bool blocked)
 {
     if (t.numel < 0) return FLASHOPT_EINVAL;
     if (t.numel == 0) return FLASHOPT_OK;
-    if (!t.param || !t.grad || !t.m_codes) return FLASHOPT_EINVAL;
-    if (v && !t.v_codes) return FLASHOPT_EINVAL;
-    if (split && !t.rho) return FLASHOPT_EINVAL;
-    if (quant && (!t.m_scales || (v && !t.v_scales))) return FLASHOPT_EINVAL;
-    if (!aligned(t.param, 16) || !aligned(t.grad, 16) || !aligned(t.m_codes, 16))
-        return FLASHOPT_EALIGN;
-    if (v && !aligned(t.v_codes, 16)) return FLASHOPT_EALIGN;
-    if (split && !aligned(t.rho, 16)) return FLASHOPT_EALIGN;
-    if (quant && (!aligned(t.m_scales, 2) || (v && !aligned(t.v_scales, 2)))) return FLASHOPT_EALIGN;
+    if (!t.param || !t.grad) return FLASHOPT_EINVAL;
+    if (blocked) {
+        if (!t.rho || t.m_codes || t.m_scales || t.v_codes || t.v_scales) return FLASHOPT_EINVAL;
+        if (!aligned(t.param, 16) || !aligned(t.grad, 16) || !aligned(t.rho, 16)) return FLASHOPT_EALIGN;
+    } else {
+        if (!t.m_codes) return FLASHOPT_EINVAL;
+        if (v && !t.v_codes) return FLASHOPT_EINVAL;
+        if (split && !t.rho) return FLASHOPT_EINVAL;
+        if (quant && (!t.m_scales || (v && !t.v_scales))) return FLASHOPT_EINVAL;
+        if (!aligned(t.param, 16) || !aligned(t.grad, 16) || !aligned(t.m_codes, 16))
+            return FLASHOPT_EALIGN;
+        if (v && !aligned(t.v_codes, 16)) return FLASHOPT_EALIGN;
+        if (split && !aligned(t.rho, 16)) return FLASHOPT_EALIGN;
+        if (quant && (!aligned(t.m_scales, 2) || (v && !aligned(t.v_scales, 2)))) return FLASHOPT_EALIGN;
+    }
     if ((t.numel + flashopt::kChunkElems - 1) / flashopt::kChunkElems > INT32_MAX) return FLASHOPT_EINVAL;
     return FLASHOPT_OK;
+}
+
+// Rho bytes of one 1024-element chunk: int8 or int16 correction bits, none
+// without a split (master_bits 0).
+uint32_t chunk_rho_bytes(int master_bits)
+{
+    return master_bits == 24 ? 1024u : (master_bits == 32 ? 2048u : 0u);
+}
+
+// The byte offsets of the blocked state layout (all zero for the streams):
+// per chunk rho, m codes, v codes (with_v), m scales, v scales (with_v), the
+// block padded to whole 128-byte cache lines, so that no line holds the
+// state of two chunks (two wavefronts).
+flashopt::StateLayout state_layout(int layout, int master_bits, bool with_v)
+{
+    flashopt::StateLayout L{0u, 0u, 0u, 0u, 0u};
+    if (layout != FLASHOPT_STATE_BLOCKED) return L;
+    const uint32_t r = chunk_rho_bytes(master_bits);
+    const uint32_t codes = flashopt::kChunkElems;                          // one byte each
+    const uint32_t scales = flashopt::kChunkElems / flashopt::kGroup * 2;  // fp16 each
+    L.m = r;
+    if (with_v) {
+        L.v = r + codes;
+        L.ms = r + 2 * codes;
+        L.vs = r + 2 * codes + scales;
+        L.bytes = r + 2 * codes + 2 * scales;
+    } else {
+        L.ms = r + codes;
+        L.bytes = r + codes + scales;
+    }
+    L.bytes = (L.bytes + 127u) & ~127u;
+    return L;
 }
 
 DevTensor device_descriptor(const flashopt_tensor &s)
@@ -147,12 +186,16 @@ flashopt_status adamw_scalars(const flashopt_adamw_args *a, StepScalars &sc)
     if (a->fp32_states != 0 && a->fp32_states != 1) return FLASHOPT_EINVAL;
     if (a->param_fp32 != 0 && a->param_fp32 != 1) return FLASHOPT_EINVAL;
     if (a->param_fp32 && a->master_bits != 0) return FLASHOPT_EINVAL;
+    if (a->state_layout != FLASHOPT_STATE_STREAMS && a->state_layout != FLASHOPT_STATE_BLOCKED)
+        return FLASHOPT_EINVAL;
+    if (a->state_layout == FLASHOPT_STATE_BLOCKED && a->fp32_states) return FLASHOPT_EINVAL;
     if (a->step < 1) return FLASHOPT_EINVAL;
     if (!(a->lr >= 0.0) || !std::isfinite(a->lr)) return FLASHOPT_EINVAL;
     if (!(a->beta1 >= 0.0 && a->beta1 < 1.0) || !(a->beta2 >= 0.0 && a->beta2 < 1.0)) return FLASHOPT_EINVAL;
     if (!(a->eps >= 0.0) || !std::isfinite(a->eps)) return FLASHOPT_EINVAL;
     if (!std::isfinite(a->weight_decay)) return FLASHOPT_EINVAL;
     const double t = static_cast<double>(a->step);
+    sc.blk = state_layout(a->state_layout, a->master_bits, true);
     sc.cwd = static_cast<float>(1.0 - a->lr * a->weight_decay);
     sc.b1 = static_cast<float>(a->beta1);
     sc.c1 = static_cast<float>(1.0 - a->beta1);
@@ -236,6 +279,10 @@ flashopt_status sgd_scalars(const flashopt_sgd_args *a, SgdScalars &sc)
     if (!(a->momentum > 0.0) || !std::isfinite(a->momentum)) return FLASHOPT_EINVAL;
     if (!std::isfinite(a->dampening) || !std::isfinite(a->weight_decay)) return FLASHOPT_EINVAL;
     if (a->nesterov && a->dampening != 0.0) return FLASHOPT_EINVAL;
+    if (a->state_layout != FLASHOPT_STATE_STREAMS && a->state_layout != FLASHOPT_STATE_BLOCKED)
+        return FLASHOPT_EINVAL;
+    if (a->state_layout == FLASHOPT_STATE_BLOCKED && a->fp32_states) return FLASHOPT_EINVAL;
+    sc.blk = state_layout(a->state_layout, a->master_bits, false);
     sc.lr = static_cast<float>(a->lr);
     sc.mu = static_cast<float>(a->momentum);
     sc.cd = static_cast<float>(1.0 - a->dampening);
@@ -248,14 +295,14 @@ flashopt_status sgd_scalars(const flashopt_sgd_args *a, SgdScalars &sc)
 
 // Validation of a step's tensor list; total = its chunks of 1024 elements.
 // split: rho is used; quant: scales are used; v: the variance streams are
-// used.
+// used; blocked: the chunk-blocked state layout.
 flashopt_status check_list(const flashopt_tensor *tensors, int n_tensors, int master_bits,
-                           bool quant, bool v, int64_t &total)
+                           bool quant, bool v, bool blocked, int64_t &total)
 {
     const bool split = master_bits != 0;
     total = 0;
     for (int i = 0; i < n_tensors; ++i) {
-        const flashopt_status st = check_tensor(tensors[i], split, quant, v);
+        const flashopt_status st = check_tensor(tensors[i], split, quant, v, blocked);
         if (st != FLASHOPT_OK) return st;
         total += (tensors[i].numel + flashopt::kChunkElems - 1) / flashopt::kChunkElems;
         if (total > INT32_MAX) return FLASHOPT_EINVAL;
@@ -319,11 +366,12 @@ flashopt_status stage_copy(void *dst, size_t bytes, hipStream_t st, Fill &&fill)
 // total_chunks, stream).
 template <typename Launch>
 flashopt_status stage_and_launch(const flashopt_tensor *tensors, int n_tensors, int master_bits,
-                                 bool quant, bool v, const void *header, size_t header_bytes,
-                                 void *workspace, size_t ws_bytes, void *stream, Launch &&launch)
+                                 bool quant, bool v, bool blocked, const void *header,
+                                 size_t header_bytes, void *workspace, size_t ws_bytes, void *stream,
+                                 Launch &&launch)
 {
     int64_t total = 0;
-    const flashopt_status cs = check_list(tensors, n_tensors, master_bits, quant, v, total);
+    const flashopt_status cs = check_list(tensors, n_tensors, master_bits, quant, v, blocked, total);
     if (cs != FLASHOPT_OK) return cs;
     if (total == 0) return FLASHOPT_OK;
     const size_t need = staged_bytes(n_tensors, header_bytes);
@@ -352,11 +400,11 @@ flashopt_status stage_and_launch(const flashopt_tensor *tensors, int n_tensors, 
 // `plan`; n_tensors and total_chunks of the plan go to info.
 template <typename Sc, typename Info>
 flashopt_status make_plan(const flashopt_tensor *tensors, int n_tensors, int master_bits, bool quant,
-                          bool v, const Sc &sc, void *plan, size_t plan_bytes, Info &info,
-                          void *stream)
+                          bool v, bool blocked, const Sc &sc, void *plan, size_t plan_bytes,
+                          Info &info, void *stream)
 {
     int64_t total = 0;
-    const flashopt_status cs = check_list(tensors, n_tensors, master_bits, quant, v, total);
+    const flashopt_status cs = check_list(tensors, n_tensors, master_bits, quant, v, blocked, total);
     if (cs != FLASHOPT_OK) return cs;
     const size_t need = staged_bytes(n_tensors, kHeader);
     if (need > 0 && (!plan || plan_bytes < need)) return FLASHOPT_EWORKSPACE;
@@ -401,13 +449,14 @@ PlanPtrs plan_ptrs(const void *plan, int n_tensors)
 bool same_variant(const flashopt_adamw_args &a, const flashopt_adamw_plan_info &info)
 {
     return info.master_bits == a.master_bits && info.companded == a.companded &&
-           info.fp32_states == a.fp32_states && info.param_fp32 == a.param_fp32;
+           info.fp32_states == a.fp32_states && info.param_fp32 == a.param_fp32 &&
+           info.state_layout == a.state_layout;
 }
 
 bool same_variant(const flashopt_sgd_args &a, const flashopt_sgd_plan_info &info)
 {
     return info.master_bits == a.master_bits && info.companded == a.companded &&
-           info.fp32_states == a.fp32_states && info.reserved == 0;
+           info.fp32_states == a.fp32_states && info.state_layout == a.state_layout;
 }
 
 // The launch-time checks shared by both plan kinds: counts, then the buffer.
@@ -427,6 +476,13 @@ bool valid_variant(int master_bits, int companded, int fp32_states)
            (companded == 0 || companded == 1) && (fp32_states == 0 || fp32_states == 1);
 }
 
+// A state layout, and whether the storage variant allows it (the blocked
+// layout holds quantized states only).
+bool valid_layout(int layout, int fp32_states)
+{
+    return layout == FLASHOPT_STATE_STREAMS || (layout == FLASHOPT_STATE_BLOCKED && fp32_states == 0);
+}
+
 // Host image of the allocation-free step's scalar block and chunk table:
 // built under the mutex and copied (pageable hipMemcpyAsync, which has
 // consumed the buffer when it returns) into the device scratch array.
@@ -438,6 +494,14 @@ alignas(64) unsigned char g_noalloc_table[flashopt::kScratchBytes];
 extern "C" {
 
 int flashopt_abi_version(void) { return FLASHOPT_ABI_VERSION; }
+
+size_t flashopt_blocked_state_bytes(int64_t numel, int master_bits, int with_variance)
+{
+    if (numel <= 0 || (master_bits != 24 && master_bits != 32 && master_bits != 0)) return 0;
+    const flashopt::StateLayout L = state_layout(FLASHOPT_STATE_BLOCKED, master_bits, with_variance != 0);
+    const int64_t chunks = (numel + flashopt::kChunkElems - 1) / flashopt::kChunkElems;
+    return static_cast<size_t>(chunks) * L.bytes;
+}
 
 const char *flashopt_status_str(flashopt_status s)
 {
@@ -505,7 +569,8 @@ flashopt_status flashopt_adamw_step(const flashopt_tensor *tensors, int n_tensor
     alignas(16) unsigned char header[kHeader];
     fill_scalars(sc, header);
     return stage_and_launch(tensors, n_tensors, a->master_bits, a->fp32_states == 0, true,
-                            header, kHeader, workspace, ws_bytes, stream,
+                            a->state_layout == FLASHOPT_STATE_BLOCKED, header, kHeader, workspace,
+                            ws_bytes, stream,
                             [&](const unsigned char *h, const DevTensor *d, const int32_t *cs,
                                 int32_t total, hipStream_t st) {
                                 return flashopt::launch_adamw_step(
@@ -521,7 +586,8 @@ flashopt_status flashopt_adamw_step_tensor(const flashopt_tensor *tensor,
     StepScalars sc;
     const flashopt_status hs = adamw_scalars(a, sc);
     if (hs != FLASHOPT_OK) return hs;
-    const flashopt_status ts = check_tensor(*tensor, a->master_bits != 0, a->fp32_states == 0, true);
+    const flashopt_status ts = check_tensor(*tensor, a->master_bits != 0, a->fp32_states == 0, true,
+                                            a->state_layout == FLASHOPT_STATE_BLOCKED);
     if (ts != FLASHOPT_OK || tensor->numel == 0) return ts;
     return hip_status(flashopt::launch_adamw_tensor(device_descriptor(*tensor), sc, kernel_format(*a),
                                                     states_of(a->fp32_states, a->companded),
@@ -538,7 +604,7 @@ flashopt_status flashopt_adamw_step_noalloc(const flashopt_tensor *tensors, int 
     if (hs != FLASHOPT_OK) return hs;
     int64_t total = 0;
     const flashopt_status cs = check_list(tensors, n_tensors, a->master_bits, a->fp32_states == 0,
-                                          true, total);
+                                          true, a->state_layout == FLASHOPT_STATE_BLOCKED, total);
     if (cs != FLASHOPT_OK || total == 0) return cs;
     void *scratch = nullptr;
     if (flashopt::scratch_address(&scratch) != hipSuccess) return FLASHOPT_EHIP;
@@ -578,8 +644,10 @@ flashopt_status flashopt_adamw_plan(const flashopt_tensor *tensors, int n_tensor
     out.companded = a->companded;
     out.fp32_states = a->fp32_states;
     out.param_fp32 = a->param_fp32;
+    out.state_layout = a->state_layout;
     const flashopt_status ps = make_plan(tensors, n_tensors, a->master_bits, a->fp32_states == 0, true,
-                                         sc, plan, plan_bytes, out, stream);
+                                         a->state_layout == FLASHOPT_STATE_BLOCKED, sc, plan,
+                                         plan_bytes, out, stream);
     if (ps == FLASHOPT_OK) *info = out;
     return ps;
 }
@@ -599,7 +667,8 @@ flashopt_status flashopt_adamw_plan_launch(const flashopt_adamw_plan_info *info,
 {
     if (!info) return FLASHOPT_EINVAL;
     if (!valid_variant(info->master_bits, info->companded, info->fp32_states) ||
-        (info->param_fp32 != 0 && info->param_fp32 != 1) || (info->param_fp32 && info->master_bits != 0))
+        (info->param_fp32 != 0 && info->param_fp32 != 1) || (info->param_fp32 && info->master_bits != 0) ||
+        !valid_layout(info->state_layout, info->fp32_states))
         return FLASHOPT_EINVAL;
     const flashopt_status lc = plan_launch_checks(info->n_tensors, info->total_chunks, plan);
     if (lc != FLASHOPT_OK || info->total_chunks == 0) return lc;
@@ -632,7 +701,8 @@ flashopt_status flashopt_sgd_step(const flashopt_tensor *tensors, int n_tensors,
     alignas(16) unsigned char header[kHeader];
     fill_scalars(sc, header);
     return stage_and_launch(tensors, n_tensors, a->master_bits, a->fp32_states == 0, false,
-                            header, kHeader, workspace, ws_bytes, stream,
+                            a->state_layout == FLASHOPT_STATE_BLOCKED, header, kHeader, workspace,
+                            ws_bytes, stream,
                             [&](const unsigned char *h, const DevTensor *d, const int32_t *cs,
                                 int32_t total, hipStream_t st) {
                                 return flashopt::launch_sgd_step(
@@ -658,8 +728,10 @@ flashopt_status flashopt_sgd_plan(const flashopt_tensor *tensors, int n_tensors,
     out.master_bits = a->master_bits;
     out.companded = a->companded;
     out.fp32_states = a->fp32_states;
+    out.state_layout = a->state_layout;
     const flashopt_status ps = make_plan(tensors, n_tensors, a->master_bits, a->fp32_states == 0, false,
-                                         sc, plan, plan_bytes, out, stream);
+                                         a->state_layout == FLASHOPT_STATE_BLOCKED, sc, plan,
+                                         plan_bytes, out, stream);
     if (ps == FLASHOPT_OK) *info = out;
     return ps;
 }
@@ -678,7 +750,8 @@ flashopt_status flashopt_sgd_plan_launch(const flashopt_sgd_plan_info *info, con
                                          void *stream)
 {
     if (!info) return FLASHOPT_EINVAL;
-    if (!valid_variant(info->master_bits, info->companded, info->fp32_states) || info->reserved != 0)
+    if (!valid_variant(info->master_bits, info->companded, info->fp32_states) ||
+        !valid_layout(info->state_layout, info->fp32_states))
         return FLASHOPT_EINVAL;
     const flashopt_status lc = plan_launch_checks(info->n_tensors, info->total_chunks, plan);
     if (lc != FLASHOPT_OK || info->total_chunks == 0) return lc;
@@ -697,7 +770,8 @@ flashopt_status flashopt_sgd_step_tensor(const flashopt_tensor *tensor,
     SgdScalars sc;
     const flashopt_status hs = sgd_scalars(a, sc);
     if (hs != FLASHOPT_OK) return hs;
-    const flashopt_status ts = check_tensor(*tensor, a->master_bits != 0, a->fp32_states == 0, false);
+    const flashopt_status ts = check_tensor(*tensor, a->master_bits != 0, a->fp32_states == 0, false,
+                                            a->state_layout == FLASHOPT_STATE_BLOCKED);
     if (ts != FLASHOPT_OK || tensor->numel == 0) return ts;
     return hip_status(flashopt::launch_sgd_tensor(device_descriptor(*tensor), sc, a->master_bits,
                                                   states_of(a->fp32_states, a->companded),

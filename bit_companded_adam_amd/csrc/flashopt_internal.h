@@ -41,6 +41,14 @@ struct DevTensor {
 };
 static_assert(sizeof(DevTensor) == 64, "descriptor layout");
 
+// Byte offsets of a chunk's state in the blocked state layout (bytes = 0:
+// the per-tensor streams): block c of a tensor starts at rho + c * bytes and
+// holds rho at 0, the m codes at m, the v codes at v, the m scales at ms and
+// the v scales at vs.
+struct StateLayout {
+    uint32_t bytes, m, v, ms, vs;
+};
+
 // Scalars of one step.  The fp32 ones are formed in double on the host and
 // rounded once (a Python float meeting a float32 tensor); rbc1 and inv_bc2s
 // serve the kernel's exact short routes for the bias-correction quotients
@@ -65,6 +73,7 @@ struct StepScalars {
     uint32_t num_key;   // (pattern << 1) - 1 of the smallest nonzero |lr mhat 2^32| allowed
     int fast;           // 1 when eps and lr keep the short routes exact (see adamw_scalars)
     int unit_bc;        // 1 when bc1 and bc2 are both exactly 1 (late in training)
+    StateLayout blk;    // the state layout
 };
 // The list step kernels (AdamW and FlashSGD) read their scalars from device
 // memory: a block of kScalarsBytes at the start of the staged table (the
@@ -83,6 +92,7 @@ struct SgdScalars {
     int has_wd;     // weight_decay != 0
     int first;      // step == 1: the buffer is set to the gradient
     int nesterov;
+    StateLayout blk;    // the state layout (no v parts)
 };
 static_assert(sizeof(SgdScalars) <= kScalarsBytes, "scalar block");
 

@@ -18,7 +18,11 @@
 // kernels use N = 4 (quantize's group maximum spans 8 lanes).  The path is
 // elementwise, so there is no MFMA; LDS holds only the two 256-entry
 // dequantization tables (built per workgroup), and the list steps' scalar
-// block and per-tensor chunk table are read with scalar loads.
+// block and per-tensor chunk table are read with scalar loads.  A tensor's
+// quantized state is five streams (rho, m codes, v codes, m scales, v
+// scales) or, in the blocked layout, one buffer of per-chunk blocks that
+// holds the same five parts; chunk_ptrs resolves either, with scalar
+// arithmetic, so the per-element code is the same.
 //
 // Arithmetic: fp32, one IEEE rounding per operation in the written order
 // (built with -ffp-contract=off, fp32 and fp16 denormals preserved), so the
@@ -630,8 +634,8 @@ __device__ __forceinline__ int64_t split_lane_first(int64_t base, int u)
     return wave * (256 * U) + 256 * u + 4 * static_cast<int64_t>(threadIdx.x & 63u);
 }
 
-// Units per wavefront of the split (S) and reconstruct (R) kernels, by
-// master width.
+// Units per wavefront of the split and reconstruct kernels, by master
+// width (measured, see split_lane_first).
 constexpr int split_units(int mb, bool reconstruct) { return reconstruct && mb == 32 ? 4 : 1; }
 
 template <int MB>
@@ -882,10 +886,12 @@ struct ChunkPtrs {
     int rem;
 };
 
-// Pointers of chunk k of a tensor.  Whether the chunk is full is decided on
-// 32-bit chunk indices (scalar compares; gfx9 has no 64-bit scalar
-// less-than).
-__device__ __forceinline__ ChunkPtrs chunk_ptrs(const DevTensor &d, int32_t k)
+// Pointers of chunk k of a tensor, in the per-tensor streams or, with a
+// blocked state layout (L.bytes != 0), in the chunk's block of the state
+// buffer at d.rho (uniform: scalar arithmetic).  Whether the chunk is full
+// is decided on 32-bit chunk indices (scalar compares; gfx9 has no 64-bit
+// scalar less-than).
+__device__ __forceinline__ ChunkPtrs chunk_ptrs(const DevTensor &d, int32_t k, const StateLayout &L)
 {
     const int64_t off = static_cast<int64_t>(k) * kChunkElems;
     ChunkPtrs c;
@@ -893,14 +899,24 @@ __device__ __forceinline__ ChunkPtrs chunk_ptrs(const DevTensor &d, int32_t k)
     c.grad = d.grad + off;
     c.param32 = reinterpret_cast<uint32_t *>(d.param) + off;
     c.grad32 = reinterpret_cast<const uint32_t *>(d.grad) + off;
-    c.rho8 = static_cast<uint8_t *>(d.rho) + off;
-    c.rho16 = static_cast<uint16_t *>(d.rho) + off;
-    c.mc = reinterpret_cast<uint8_t *>(d.m_codes) + off;
-    c.vc = d.v_codes + off;
     c.mf = reinterpret_cast<uint32_t *>(d.m_codes) + off;
     c.vf = reinterpret_cast<uint32_t *>(d.v_codes) + off;
-    c.ms = d.m_scales + off / kGroup;
-    c.vs = d.v_scales + off / kGroup;
+    if (L.bytes != 0u) {
+        uint8_t *b = static_cast<uint8_t *>(d.rho) + static_cast<int64_t>(k) * L.bytes;
+        c.rho8 = b;
+        c.rho16 = reinterpret_cast<uint16_t *>(b);
+        c.mc = b + L.m;
+        c.vc = b + L.v;
+        c.ms = reinterpret_cast<uint16_t *>(b + L.ms);
+        c.vs = reinterpret_cast<uint16_t *>(b + L.vs);
+    } else {
+        c.rho8 = static_cast<uint8_t *>(d.rho) + off;
+        c.rho16 = static_cast<uint16_t *>(d.rho) + off;
+        c.mc = reinterpret_cast<uint8_t *>(d.m_codes) + off;
+        c.vc = d.v_codes + off;
+        c.ms = d.m_scales + off / kGroup;
+        c.vs = d.v_scales + off / kGroup;
+    }
     const int32_t full = static_cast<int32_t>(d.numel / kChunkElems);
     c.rem = k < full ? kChunkElems : static_cast<int>(d.numel % kChunkElems);
     return c;
@@ -1434,8 +1450,8 @@ template <int W, typename Load, typename Tables, typename Finish>
 __device__ __forceinline__ void for_each_unit(const DevTensor *__restrict__ tensors,
                                               const int32_t *__restrict__ chunk_start,
                                               int n_tensors, int32_t chunk_base,
-                                              int32_t chunk_end, Load &&load, Tables &&tables,
-                                              Finish &&finish)
+                                              int32_t chunk_end, const StateLayout &L, Load &&load,
+                                              Tables &&tables, Finish &&finish)
 {
     // a launch has at most 2^24 workgroups (its work-items fit in 32 bits);
     // every quantity here is uniform and stays in scalar registers
@@ -1458,7 +1474,7 @@ __device__ __forceinline__ void for_each_unit(const DevTensor *__restrict__ tens
             else hi = mid - 1;
         }
         const int t = __builtin_amdgcn_readfirstlane(lo);
-        cp = chunk_ptrs(tensors[t], c - chunk_start[t]);
+        cp = chunk_ptrs(tensors[t], c - chunk_start[t], L);
         load(cp, unit);
     }
     tables();
@@ -1468,8 +1484,8 @@ __device__ __forceinline__ void for_each_unit(const DevTensor *__restrict__ tens
 // The same for one tensor (no chunk table): chunk c starts at element 1024 c.
 template <int W, typename Load, typename Tables, typename Finish>
 __device__ __forceinline__ void for_each_unit_of(const DevTensor &d, int32_t chunk_base,
-                                                 int32_t chunk_end, Load &&load, Tables &&tables,
-                                                 Finish &&finish)
+                                                 int32_t chunk_end, const StateLayout &L,
+                                                 Load &&load, Tables &&tables, Finish &&finish)
 {
     const int32_t wave = __builtin_amdgcn_readfirstlane(
         static_cast<int32_t>(blockIdx.x) * (kBlockThreads / kWaveLanes) +
@@ -1479,7 +1495,7 @@ __device__ __forceinline__ void for_each_unit_of(const DevTensor &d, int32_t chu
     const bool any = c64 < chunk_end;
     ChunkPtrs cp{};
     if (any) {
-        cp = chunk_ptrs(d, static_cast<int32_t>(c64));
+        cp = chunk_ptrs(d, static_cast<int32_t>(c64), L);
         load(cp, unit);
     }
     tables();
@@ -1539,7 +1555,7 @@ adamw_step_kernel(const StepScalars *__restrict__ scalars, const DevTensor *__re
     uint32_t r = 0u;
     int cnt = 0;
     for_each_unit<kUnits>(
-        tensors, chunk_start, n_tensors, chunk_base, chunk_end,
+        tensors, chunk_start, n_tensors, chunk_base, chunk_end, sc.blk,
         [&](const ChunkPtrs &cp, int u) { load_chunk_unit<MB, ST, kN>(cp, u, lane, r, cnt, in); },
         [&] { build_tables<ST, true>(te, s_mu, s_vu); },
         [&](const ChunkPtrs &cp) {
@@ -1566,7 +1582,7 @@ sgd_step_kernel(const SgdScalars *__restrict__ scalars, const DevTensor *__restr
     uint32_t r = 0u;
     int cnt = 0;
     for_each_unit<kUnits>(
-        tensors, chunk_start, n_tensors, chunk_base, chunk_end,
+        tensors, chunk_start, n_tensors, chunk_base, chunk_end, sc.blk,
         [&](const ChunkPtrs &cp, int u) { load_chunk_unit<MB, ST, kN, false>(cp, u, lane, r, cnt, in); },
         [&] { build_tables<ST, false>(te, s_mu, nullptr); },
         [&](const ChunkPtrs &cp) {
@@ -1591,7 +1607,7 @@ adamw_tensor_kernel(DevTensor d, StepScalars sc, int32_t chunk_base, int32_t chu
     uint32_t r = 0u;
     int cnt = 0;
     for_each_unit_of<kUnits>(
-        d, chunk_base, chunk_end,
+        d, chunk_base, chunk_end, sc.blk,
         [&](const ChunkPtrs &cp, int u) { load_chunk_unit<MB, ST, kN>(cp, u, lane, r, cnt, in); },
         [&] { build_tables<ST, true>(te, s_mu, s_vu); },
         [&](const ChunkPtrs &cp) {
@@ -1613,7 +1629,7 @@ sgd_tensor_kernel(DevTensor d, SgdScalars sc, int32_t chunk_base, int32_t chunk_
     uint32_t r = 0u;
     int cnt = 0;
     for_each_unit_of<kUnits>(
-        d, chunk_base, chunk_end,
+        d, chunk_base, chunk_end, sc.blk,
         [&](const ChunkPtrs &cp, int u) { load_chunk_unit<MB, ST, kN, false>(cp, u, lane, r, cnt, in); },
         [&] { build_tables<ST, false>(te, s_mu, nullptr); },
         [&](const ChunkPtrs &cp) {

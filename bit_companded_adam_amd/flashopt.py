@@ -26,6 +26,8 @@ SPEC_MOMENTUM_LINEAR = Q_SIGNED
 SPEC_VARIANCE_LINEAR = 0
 GROUP = 32
 CHUNK_ELEMS = 1024
+STATE_STREAMS, STATE_BLOCKED = 0, 1
+STATE_LAYOUTS = {"streams": STATE_STREAMS, "blocked": STATE_BLOCKED}
 
 EXPORTS = ("flashopt_quantize", "flashopt_dequantize", "flashopt_split",
            "flashopt_reconstruct", "flashopt_adamw_workspace_bytes",
@@ -34,7 +36,7 @@ EXPORTS = ("flashopt_quantize", "flashopt_dequantize", "flashopt_split",
            "flashopt_abi_version", "flashopt_adamw_step_noalloc", "flashopt_adamw_plan_bytes",
            "flashopt_adamw_plan", "flashopt_adamw_plan_set_step", "flashopt_adamw_plan_launch",
            "flashopt_sgd_plan_bytes", "flashopt_sgd_plan", "flashopt_sgd_plan_set_step",
-           "flashopt_sgd_plan_launch")
+           "flashopt_sgd_plan_launch", "flashopt_blocked_state_bytes")
 
 
 class FlashoptError(RuntimeError):
@@ -55,13 +57,15 @@ class flashopt_adamw_args(ctypes.Structure):
                 ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
                 ("weight_decay", ctypes.c_double), ("step", ctypes.c_int64),
                 ("master_bits", ctypes.c_int), ("companded", ctypes.c_int),
-                ("fp32_states", ctypes.c_int), ("param_fp32", ctypes.c_int)]
+                ("fp32_states", ctypes.c_int), ("param_fp32", ctypes.c_int),
+                ("state_layout", ctypes.c_int)]
 
 
 class flashopt_adamw_plan_info(ctypes.Structure):
     _fields_ = [("n_tensors", ctypes.c_int32), ("total_chunks", ctypes.c_int32),
                 ("master_bits", ctypes.c_int32), ("companded", ctypes.c_int32),
-                ("fp32_states", ctypes.c_int32), ("param_fp32", ctypes.c_int32)]
+                ("fp32_states", ctypes.c_int32), ("param_fp32", ctypes.c_int32),
+                ("state_layout", ctypes.c_int32)]
 
 
 class flashopt_sgd_args(ctypes.Structure):
@@ -69,13 +73,13 @@ class flashopt_sgd_args(ctypes.Structure):
                 ("dampening", ctypes.c_double), ("weight_decay", ctypes.c_double),
                 ("step", ctypes.c_int64), ("master_bits", ctypes.c_int),
                 ("companded", ctypes.c_int), ("fp32_states", ctypes.c_int),
-                ("nesterov", ctypes.c_int)]
+                ("nesterov", ctypes.c_int), ("state_layout", ctypes.c_int)]
 
 
 class flashopt_sgd_plan_info(ctypes.Structure):
     _fields_ = [("n_tensors", ctypes.c_int32), ("total_chunks", ctypes.c_int32),
                 ("master_bits", ctypes.c_int32), ("companded", ctypes.c_int32),
-                ("fp32_states", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("fp32_states", ctypes.c_int32), ("state_layout", ctypes.c_int32)]
 
 
 _lib = None
@@ -125,6 +129,8 @@ def lib() -> ctypes.CDLL:
         L.flashopt_sgd_plan_set_step.argtypes = [ctypes.POINTER(flashopt_sgd_plan_info),
                                                  ctypes.POINTER(flashopt_sgd_args), vp, vp]
         L.flashopt_sgd_plan_launch.argtypes = [ctypes.POINTER(flashopt_sgd_plan_info), vp, vp]
+        L.flashopt_blocked_state_bytes.argtypes = [i64, i, i]
+        L.flashopt_blocked_state_bytes.restype = ctypes.c_size_t
         L.flashopt_status_str.argtypes = [i]
         L.flashopt_status_str.restype = ctypes.c_char_p
         L.flashopt_abi_version.argtypes = []
@@ -265,15 +271,29 @@ def flashopt_reconstruct(param: torch.Tensor, rho: torch.Tensor, master_bits: in
 
 # --------------------------------------------------------------- step
 
+def flashopt_blocked_state_bytes(numel: int, master_bits, variance: bool = True) -> int:
+    """Bytes of a chunk-blocked state buffer (FLASHOPT_STATE_BLOCKED) for
+    numel elements; master_bits 24 | 32 | None."""
+    return lib().flashopt_blocked_state_bytes(numel, 0 if master_bits is None else master_bits,
+                                              int(variance))
+
+
 class TensorState:
     """Device state of one parameter tensor: bf16 or fp32 param (updated in
     place; fp32 only without a split), rho (master_bits 24 | 32; none for
     master_bits None), and the momentum
     and variance as codes with fp16 scales, or as fp32 arrays when
-    quantize_states is False.  Fresh state is zero."""
+    quantize_states is False.  Fresh state is zero.
+
+    state_layout "streams" keeps rho, the codes and the scales as five
+    tensors (the page's per-parameter state); "blocked" keeps the same
+    values chunk by chunk in one uint8 buffer (`block`; quantized states
+    only), which the step streams faster.  The attributes rho, m_codes,
+    m_scales, v_codes and v_scales then return copies in the streams
+    format (for reading)."""
 
     def __init__(self, param: torch.Tensor, master_bits=24, quantize_states: bool = True,
-                 variance: bool = True):
+                 variance: bool = True, state_layout: str = "streams"):
         if param.dtype not in (torch.bfloat16, torch.float32) or not param.is_contiguous() \
                 or not param.is_cuda:
             raise ValueError("param must be a contiguous bf16 or fp32 device tensor")
@@ -281,20 +301,86 @@ class TensorState:
             raise ValueError("master_bits must be 24, 32 or None")
         if param.dtype == torch.float32 and master_bits is not None:
             raise ValueError("an fp32 parameter is never split: use master_bits=None")
+        if state_layout not in STATE_LAYOUTS:
+            raise ValueError("state_layout must be 'streams' or 'blocked'")
+        if state_layout == "blocked" and not quantize_states:
+            raise ValueError("the blocked state layout holds quantized states only")
         n, dev = param.numel(), param.device
         self.param = param
-        self.rho = None if master_bits is None else torch.zeros(n, dtype=rho_dtype(master_bits), device=dev)
-        if quantize_states:
-            self.m_codes = torch.zeros(n, dtype=torch.int8, device=dev)
-            self.m_scales = torch.zeros(n_groups(n), dtype=torch.int16, device=dev)
-            self.v_codes = torch.zeros(n, dtype=torch.uint8, device=dev) if variance else None
-            self.v_scales = torch.zeros(n_groups(n), dtype=torch.int16, device=dev) if variance else None
-        else:
-            self.m_codes = torch.zeros(n, dtype=torch.float32, device=dev)
-            self.v_codes = torch.zeros(n, dtype=torch.float32, device=dev) if variance else None
-            self.m_scales = self.v_scales = None
         self.master_bits = master_bits
         self.quantize_states = quantize_states
+        self.variance = variance
+        self.state_layout = state_layout
+        self.block = None
+        if state_layout == "blocked":
+            self.block = torch.zeros(max(16, flashopt_blocked_state_bytes(n, master_bits, variance)),
+                                     dtype=torch.uint8, device=dev)
+            return
+        self._rho = None if master_bits is None else torch.zeros(n, dtype=rho_dtype(master_bits), device=dev)
+        if quantize_states:
+            self._m_codes = torch.zeros(n, dtype=torch.int8, device=dev)
+            self._m_scales = torch.zeros(n_groups(n), dtype=torch.int16, device=dev)
+            self._v_codes = torch.zeros(n, dtype=torch.uint8, device=dev) if variance else None
+            self._v_scales = torch.zeros(n_groups(n), dtype=torch.int16, device=dev) if variance else None
+        else:
+            self._m_codes = torch.zeros(n, dtype=torch.float32, device=dev)
+            self._v_codes = torch.zeros(n, dtype=torch.float32, device=dev) if variance else None
+            self._m_scales = self._v_scales = None
+
+    # ---- the blocked layout's parts, as copies in the streams format
+    def _block_part(self, offset: int, width: int, dtype, count: int) -> torch.Tensor:
+        """Bytes [offset, offset + width) of every chunk's block, joined, as
+        `count` elements of dtype."""
+        n = self.param.numel()
+        chunks = (n + CHUNK_ELEMS - 1) // CHUNK_ELEMS
+        size = flashopt_blocked_state_bytes(n, self.master_bits, self.variance) // max(chunks, 1)
+        if n == 0:
+            return torch.zeros(0, dtype=dtype, device=self.param.device)
+        rows = self.block[:chunks * size].view(chunks, size)[:, offset:offset + width]
+        return rows.contiguous().view(-1).view(dtype)[:count]
+
+    def _offsets(self):
+        r = {24: 1024, 32: 2048, None: 0}[self.master_bits]
+        if self.variance:
+            return r, r, r + 1024, r + 2048, r + 2112
+        return r, r, None, r + 1024, None
+
+    @property
+    def rho(self):
+        if self.block is None:
+            return self._rho
+        if self.master_bits is None:
+            return None
+        r = self._offsets()[0]
+        return self._block_part(0, r, rho_dtype(self.master_bits), self.param.numel())
+
+    @property
+    def m_codes(self):
+        if self.block is None:
+            return self._m_codes
+        return self._block_part(self._offsets()[1], CHUNK_ELEMS, torch.int8, self.param.numel())
+
+    @property
+    def v_codes(self):
+        if self.block is None:
+            return self._v_codes
+        off = self._offsets()[2]
+        return None if off is None else self._block_part(off, CHUNK_ELEMS, torch.uint8,
+                                                         self.param.numel())
+
+    @property
+    def m_scales(self):
+        if self.block is None:
+            return self._m_scales
+        return self._block_part(self._offsets()[3], 64, torch.int16, n_groups(self.param.numel()))
+
+    @property
+    def v_scales(self):
+        if self.block is None:
+            return self._v_scales
+        off = self._offsets()[4]
+        return None if off is None else self._block_part(off, 64, torch.int16,
+                                                         n_groups(self.param.numel()))
 
     def descriptor(self, grad: torch.Tensor) -> flashopt_tensor:
         if grad.dtype != self.param.dtype or grad.numel() != self.param.numel():
@@ -302,20 +388,25 @@ class TensorState:
         if grad.device != self.param.device:
             raise ValueError(f"grad is on {grad.device}, its parameter on {self.param.device}")
         opt = lambda t, name: 0 if t is None else _dev(t, name)
+        if self.block is not None:
+            return flashopt_tensor(_dev(self.param, "param"), _dev(grad, "grad"),
+                                   _dev(self.block, "block"), 0, 0, 0, 0, self.param.numel())
         return flashopt_tensor(_dev(self.param, "param"), _dev(grad, "grad"),
-                               opt(self.rho, "rho"), _dev(self.m_codes, "m_codes"),
-                               opt(self.m_scales, "m_scales"), opt(self.v_codes, "v_codes"),
-                               opt(self.v_scales, "v_scales"), self.param.numel())
+                               opt(self._rho, "rho"), _dev(self._m_codes, "m_codes"),
+                               opt(self._m_scales, "m_scales"), opt(self._v_codes, "v_codes"),
+                               opt(self._v_scales, "v_scales"), self.param.numel())
 
 
 def make_args(step: int, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0,
               master_bits=24, companded=True, quantize_states=True,
-              param_fp32=False) -> flashopt_adamw_args:
+              param_fp32=False, state_layout="streams") -> flashopt_adamw_args:
     """master_bits 24 | 32 | None (no split); quantize_states False: fp32 m, v;
-    param_fp32: fp32 parameters and gradients (needs master_bits None)."""
+    param_fp32: fp32 parameters and gradients (needs master_bits None);
+    state_layout "streams" | "blocked"."""
     return flashopt_adamw_args(lr, betas[0], betas[1], eps, weight_decay, step,
                                0 if master_bits is None else master_bits, int(companded),
-                               0 if quantize_states else 1, int(param_fp32))
+                               0 if quantize_states else 1, int(param_fp32),
+                               STATE_LAYOUTS[state_layout])
 
 
 def flashopt_adamw_workspace_bytes(n_tensors: int) -> int:
@@ -579,21 +670,36 @@ def attach_grad_release(opt, params, batch_below: int = RELEASE_BATCH_BELOW,
     return [p.register_post_accumulate_grad_hook(hook) for p in params]
 
 
+def _layout(state_layout, quantize_states: bool, default: str) -> str:
+    """An optimizer's state layout: its default for quantized states, the
+    streams for fp32 states (the blocked layout holds quantized states
+    only)."""
+    if state_layout is None:
+        return default if quantize_states else "streams"
+    return state_layout
+
+
 class FlashAdamW(_Stepper):
     """A list of TensorStates stepped together by one launch per step.  The
     parameters share one dtype: bf16 (split per master_bits, or cast back
-    with master_bits None) or fp32 (master_bits None; fp32 gradients)."""
+    with master_bits None) or fp32 (master_bits None; fp32 gradients).
+    state_layout: "blocked" (the default for quantized states: in
+    in-process A/B runs on the 8.0B list 0.2-2.6% faster than the streams
+    for the 24-bit master, 0.5-1.5% for the 32-bit one) or "streams" (see
+    TensorState); the stored values are the same."""
 
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0,
-                 master_bits=24, companded=True, quantize_states=True):
-        self.states = [TensorState(p, master_bits, quantize_states) for p in params]
+                 master_bits=24, companded=True, quantize_states=True, state_layout=None):
+        state_layout = _layout(state_layout, quantize_states, "blocked")
+        self.states = [TensorState(p, master_bits, quantize_states, state_layout=state_layout)
+                       for p in params]
         dtypes = {s.param.dtype for s in self.states}
         if len(dtypes) > 1:
             raise ValueError("all parameters of one FlashAdamW must share a dtype (bf16 or fp32)")
         self.hp = dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay,
                        master_bits=master_bits, companded=companded,
                        quantize_states=quantize_states,
-                       param_fp32=dtypes == {torch.float32})
+                       param_fp32=dtypes == {torch.float32}, state_layout=state_layout)
         self._init_common()
         self._workspace_bytes = max(16, flashopt_adamw_workspace_bytes(len(self.states)))
 
@@ -615,10 +721,11 @@ class FlashAdamW(_Stepper):
 
 def make_sgd_args(step: int, lr=1e-2, momentum=0.9, dampening=0.0, weight_decay=0.0,
                   nesterov=False, master_bits=24, companded=True,
-                  quantize_states=True) -> flashopt_sgd_args:
+                  quantize_states=True, state_layout="streams") -> flashopt_sgd_args:
     return flashopt_sgd_args(lr, momentum, dampening, weight_decay, step,
                              0 if master_bits is None else master_bits, int(companded),
-                             0 if quantize_states else 1, int(nesterov))
+                             0 if quantize_states else 1, int(nesterov),
+                             STATE_LAYOUTS[state_layout])
 
 
 def flashopt_sgd_workspace_bytes(n_tensors: int) -> int:
@@ -642,14 +749,18 @@ def flashopt_sgd_step(descriptors, args: flashopt_sgd_args, workspace: torch.Ten
 
 class FlashSGD(_Stepper):
     """A list of TensorStates (momentum buffer only) stepped together by one
-    launch per step."""
+    launch per step.  state_layout: "streams" (the default: with one state
+    the blocked layout measured 0.6-1.1% slower) or "blocked"."""
 
     def __init__(self, params, lr=1e-2, momentum=0.9, dampening=0.0, weight_decay=0.0,
-                 nesterov=False, master_bits=24, companded=True, quantize_states=True):
-        self.states = [TensorState(p, master_bits, quantize_states, variance=False) for p in params]
+                 nesterov=False, master_bits=24, companded=True, quantize_states=True,
+                 state_layout=None):
+        state_layout = _layout(state_layout, quantize_states, "streams")
+        self.states = [TensorState(p, master_bits, quantize_states, variance=False,
+                                   state_layout=state_layout) for p in params]
         self.hp = dict(lr=lr, momentum=momentum, dampening=dampening, weight_decay=weight_decay,
                        nesterov=nesterov, master_bits=master_bits, companded=companded,
-                       quantize_states=quantize_states)
+                       quantize_states=quantize_states, state_layout=state_layout)
         self._init_common()
         self._workspace_bytes = max(16, flashopt_sgd_workspace_bytes(len(self.states)))
 

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define FLASHOPT_ABI_VERSION 7
+#define FLASHOPT_ABI_VERSION 8
 
 typedef enum {
     FLASHOPT_OK = 0,
@@ -130,7 +130,29 @@ flashopt_status flashopt_reconstruct(const uint16_t *param_bf16, const void *rho
  * With args.fp32_states = 1 (the page's quantize_states=False ablation),
  * m_codes and v_codes point to float [numel] moments and the scale pointers
  * are unused (may be NULL).  With args.master_bits = 0 (the page's
- * master_weight_bits=None) rho is unused (may be NULL). */
+ * master_weight_bits=None) rho is unused (may be NULL).
+ *
+ * State layouts (args.state_layout).  FLASHOPT_STATE_STREAMS: rho, m_codes,
+ * m_scales, v_codes and v_scales are five arrays as above (the page's
+ * per-parameter tensors).  FLASHOPT_STATE_BLOCKED: the same values, stored
+ * chunk by chunk in one buffer that `rho` points to (16-byte aligned; the
+ * other four state pointers must be NULL): ceil(numel / 1024) blocks of
+ * equal size in chunk order, each padded to a multiple of 128 bytes (one
+ * cache line never holds two chunks' state), block c holding, for elements
+ * 1024 c .. 1024 c + 1023,
+ *   rho      1024 bytes (24-bit master) | 2048 (32-bit) | none (no split)
+ *   m codes  1024 bytes
+ *   v codes  1024 bytes                      (AdamW only)
+ *   m scales 32 fp16 (64 bytes)
+ *   v scales 32 fp16 (64 bytes)              (AdamW only)
+ * (flashopt_blocked_state_bytes gives the buffer size).  Bytes past numel in
+ * the last block are neither read nor written.  The step reads and writes
+ * three streams per element instead of six; the arithmetic and every stored
+ * value are the same.  Quantized states only (not with fp32_states). */
+enum {
+    FLASHOPT_STATE_STREAMS = 0,
+    FLASHOPT_STATE_BLOCKED = 1
+};
 typedef struct {
     uint16_t *param;          /* [numel] bf16 theta'                          */
     const uint16_t *grad;     /* [numel] bf16 gradient                        */
@@ -163,7 +185,15 @@ typedef struct {
                                  parameter): theta is the parameter and the
                                  update is stored unchanged; needs
                                  master_bits 0 (rho unused)                   */
+    int state_layout;         /* FLASHOPT_STATE_STREAMS | FLASHOPT_STATE_BLOCKED */
 } flashopt_adamw_args;
+
+/* Bytes of a FLASHOPT_STATE_BLOCKED state buffer for a tensor of numel
+ * elements: ceil(numel / 1024) blocks of (rho bytes for master_bits 24 | 32
+ * | 0: 1024 | 2048 | 0) + 1024 + 64 bytes, plus 1024 + 64 with_variance
+ * (AdamW: 1; FlashSGD: 0), rounded up to a multiple of 128.  Returns 0 for
+ * numel <= 0 or another master_bits. */
+size_t flashopt_blocked_state_bytes(int64_t numel, int master_bits, int with_variance);
 
 /* Device workspace bytes that flashopt_adamw_step needs for this list (the
  * step's scalar block, then the per-tensor descriptor and chunk table).
@@ -200,7 +230,9 @@ size_t flashopt_adamw_workspace_bytes(const flashopt_tensor *tensors, int n_tens
  * kernel with its arguments by value and stages nothing.
  * Errors: EINVAL (n_tensors < 0, NULL tensors/args, numel < 0, NULL pointer
  * that the variant uses in a non-empty tensor, master_bits, companded,
- * fp32_states, param_fp32 not 0 or 1, param_fp32 with master_bits != 0,
+ * fp32_states, param_fp32, state_layout not 0 or 1, param_fp32 with
+ * master_bits != 0, a blocked layout with fp32_states or with a non-NULL
+ * m_codes, m_scales, v_codes or v_scales,
  * step < 1, lr < 0, beta outside
  * [0, 1), eps < 0, non-finite weight_decay, more than 2^31 - 1 chunks of
  * 1024 elements in total), EALIGN, EWORKSPACE, EHIP. */
@@ -244,8 +276,8 @@ flashopt_status flashopt_adamw_step_noalloc(const flashopt_tensor *tensors, int 
  *   must stay where they are for as long as the plan is launched.
  * flashopt_adamw_plan_set_step(info, args, plan, stream): enqueues one
  *   128-byte host-to-device copy of the scalars of args (any step and
- *   hyper-parameters; master_bits, companded, fp32_states and param_fp32
- *   must equal the plan's, else EINVAL).
+ *   hyper-parameters; master_bits, companded, fp32_states, param_fp32 and
+ *   state_layout must equal the plan's, else EINVAL).
  * flashopt_adamw_plan_launch(info, plan, stream): enqueues the step kernel
  *   only.  It copies nothing, allocates nothing and does not synchronize, so
  *   it can be captured into a graph; a launch or graph replay steps with the
@@ -265,6 +297,7 @@ typedef struct {
     int32_t companded;
     int32_t fp32_states;
     int32_t param_fp32;
+    int32_t state_layout;
 } flashopt_adamw_plan_info;
 flashopt_status flashopt_adamw_plan(const flashopt_tensor *tensors, int n_tensors,
                                     const flashopt_adamw_args *args, void *plan,
@@ -298,6 +331,8 @@ typedef struct {
     int companded;            /* 1: softsign momentum spec; 0: linear         */
     int fp32_states;          /* 0: codes + fp16 scales; 1: fp32 buffer       */
     int nesterov;             /* 0 | 1                                        */
+    int state_layout;         /* FLASHOPT_STATE_STREAMS | FLASHOPT_STATE_BLOCKED
+                                 (the blocked buffer without the v parts)     */
 } flashopt_sgd_args;
 
 /* Device workspace bytes that flashopt_sgd_step needs for this list. */
@@ -305,12 +340,14 @@ size_t flashopt_sgd_workspace_bytes(const flashopt_tensor *tensors, int n_tensor
 
 /* One fused FlashSGD step over a list of tensors, one kernel launch (see the
  * conventions for lists too long for one dispatch).  The
- * momentum buffer lives in each descriptor's m_codes / m_scales; v_codes and
- * v_scales are unused (may be NULL).  Ownership, staging, workspace and
+ * momentum buffer lives in each descriptor's m_codes / m_scales (or in the
+ * blocked buffer at rho); v_codes and v_scales are unused (may be NULL;
+ * NULL with the blocked layout).  Ownership, staging, workspace and
  * alignment rules as flashopt_adamw_step.
  * Errors: EINVAL (as flashopt_adamw_step for the list; momentum <= 0,
  * non-finite dampening or weight_decay, nesterov with dampening != 0, bad
- * nesterov / companded / fp32_states / master_bits, step < 1, lr < 0),
+ * nesterov / companded / fp32_states / master_bits / state_layout, step < 1,
+ * lr < 0),
  * EALIGN, EWORKSPACE, EHIP. */
 flashopt_status flashopt_sgd_step(const flashopt_tensor *tensors, int n_tensors,
                                   const flashopt_sgd_args *args,
@@ -321,11 +358,11 @@ flashopt_status flashopt_sgd_step(const flashopt_tensor *tensors, int n_tensors,
  * flashopt_adamw_plan calls above: flashopt_sgd_plan stages the scalars of
  * args and the tables into `plan` (flashopt_sgd_plan_bytes(n) bytes) and
  * fills *info; flashopt_sgd_plan_set_step rewrites the scalars (any step and
- * hyper-parameters; master_bits, companded and fp32_states must equal the
- * plan's); flashopt_sgd_plan_launch enqueues the kernel only and can be
- * captured into a graph.
+ * hyper-parameters; master_bits, companded, fp32_states and state_layout
+ * must equal the plan's); flashopt_sgd_plan_launch enqueues the kernel only
+ * and can be captured into a graph.
  * Errors: as flashopt_sgd_step (EWORKSPACE for a NULL or short plan; EINVAL
- * also for a NULL info, a variant mismatch or a nonzero info->reserved). */
+ * also for a NULL info or a variant mismatch). */
 size_t flashopt_sgd_plan_bytes(int n_tensors);
 typedef struct {
     int32_t n_tensors;        /* tensors in the plan's table                  */
@@ -333,7 +370,7 @@ typedef struct {
     int32_t master_bits;      /* the variant fields of the planning args      */
     int32_t companded;
     int32_t fp32_states;
-    int32_t reserved;         /* 0                                            */
+    int32_t state_layout;
 } flashopt_sgd_plan_info;
 flashopt_status flashopt_sgd_plan(const flashopt_tensor *tensors, int n_tensors,
                                   const flashopt_sgd_args *args, void *plan, size_t plan_bytes,

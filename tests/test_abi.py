@@ -207,7 +207,7 @@ def test_plan_validation(L):
     # set_step: the variant must be the plan's
     good = F.flashopt_adamw_plan_info(1, 4, 24, 1, 0, 0)
     for bad in (dict(master_bits=32), dict(companded=0), dict(fp32_states=1),
-                dict(master_bits=0, param_fp32=1)):
+                dict(master_bits=0, param_fp32=1), dict(state_layout=1)):
         a = F.make_args(5)
         for k, v in bad.items():
             setattr(a, k, v)
@@ -225,6 +225,7 @@ def test_plan_validation(L):
     def launch(fields, buf=A16):
         return L.flashopt_adamw_plan_launch(ctypes.byref(F.flashopt_adamw_plan_info(*fields)), buf, None)
     for bad in ((1, 4, 16, 1, 0, 0), (1, 4, 24, 2, 0, 0), (1, 4, 24, 1, 2, 0), (1, 4, 24, 1, 0, 1),
+                (1, 4, 24, 1, 0, 0, 2), (1, 4, 24, 1, 1, 0, 1),
                 (-1, 4, 24, 1, 0, 0), (1, -4, 24, 1, 0, 0), (0, 4, 24, 1, 0, 0)):
         assert launch(bad) == F.FLASHOPT_EINVAL, bad
     assert launch((1, 4, 24, 1, 0, 0), buf=None) == F.FLASHOPT_EWORKSPACE
@@ -262,7 +263,8 @@ def test_sgd_plan_validation(L):
     assert set_step(good, F.make_sgd_args(3, master_bits=32)) == F.FLASHOPT_EINVAL
     assert set_step(good, F.make_sgd_args(3, companded=False)) == F.FLASHOPT_EINVAL
     assert set_step(good, F.make_sgd_args(3, quantize_states=False)) == F.FLASHOPT_EINVAL
-    assert set_step(F.flashopt_sgd_plan_info(1, 4, 24, 1, 0, 7), F.make_sgd_args(3)) == F.FLASHOPT_EINVAL
+    assert set_step(F.flashopt_sgd_plan_info(1, 4, 24, 1, 0, 1), F.make_sgd_args(3)) == F.FLASHOPT_EINVAL
+    assert set_step(good, F.make_sgd_args(3, state_layout="blocked")) == F.FLASHOPT_EINVAL
     assert set_step(None, F.make_sgd_args(3)) == F.FLASHOPT_EINVAL
     assert set_step(good, F.make_sgd_args(0)) == F.FLASHOPT_EINVAL
     assert set_step(good, F.make_sgd_args(3), buf=None) == F.FLASHOPT_EWORKSPACE
@@ -270,8 +272,9 @@ def test_sgd_plan_validation(L):
 
     def launch(fields, buf=A16):
         return L.flashopt_sgd_plan_launch(ctypes.byref(F.flashopt_sgd_plan_info(*fields)), buf, None)
-    for bad in ((1, 4, 16, 1, 0, 0), (1, 4, 24, 2, 0, 0), (1, 4, 24, 1, 2, 0), (1, 4, 24, 1, 0, 1),
-                (1, 4, 1, 1, 0, 0), (-1, 4, 24, 1, 0, 0), (1, -4, 24, 1, 0, 0), (0, 4, 24, 1, 0, 0)):
+    for bad in ((1, 4, 16, 1, 0, 0), (1, 4, 24, 2, 0, 0), (1, 4, 24, 1, 2, 0), (1, 4, 24, 1, 0, 2),
+                (1, 4, 24, 1, 1, 1), (1, 4, 1, 1, 0, 0), (-1, 4, 24, 1, 0, 0), (1, -4, 24, 1, 0, 0),
+                (0, 4, 24, 1, 0, 0)):
         assert launch(bad) == F.FLASHOPT_EINVAL, bad
     assert launch((1, 4, 24, 1, 0, 0), buf=None) == F.FLASHOPT_EWORKSPACE
     assert launch((1, 4, 24, 1, 0, 0), buf=A16 + 8) == F.FLASHOPT_EALIGN
@@ -333,3 +336,43 @@ def test_single_tensor_validation(L):
     assert sg(ctypes.byref(_tensor(m_codes=A16 + 8)), ctypes.byref(s), None) == F.FLASHOPT_EALIGN
     bad_s = F.make_sgd_args(1, momentum=0.0)
     assert sg(ctypes.byref(_tensor()), ctypes.byref(bad_s), None) == F.FLASHOPT_EINVAL
+
+
+def test_blocked_state_validation(L):
+    """The chunk-blocked state layout: one 16-byte aligned buffer at rho, the
+    other state pointers NULL, quantized states only, and the buffer size of
+    flashopt_blocked_state_bytes; a bad layout code is EINVAL."""
+    blocked = F.make_args(1, state_layout="blocked")
+    blk = lambda **kw: _tensor(**dict(dict(m_codes=None, m_scales=None, v_codes=None, v_scales=None), **kw))
+    # valid: validation passes and stops at the missing workspace
+    assert _step(L, [blk()], blocked, ws_bytes=0) == F.FLASHOPT_EWORKSPACE
+    assert _step(L, [blk()], F.make_args(1, master_bits=None, state_layout="blocked"),
+                 ws_bytes=0) == F.FLASHOPT_EWORKSPACE
+    # a stream pointer next to the block, a missing or misaligned block
+    for field in ("m_codes", "m_scales", "v_codes", "v_scales"):
+        assert _step(L, [blk(**{field: A16})], blocked) == F.FLASHOPT_EINVAL, field
+    assert _step(L, [blk(rho=None)], blocked) == F.FLASHOPT_EINVAL
+    assert _step(L, [blk(rho=A16 + 8)], blocked) == F.FLASHOPT_EALIGN
+    # the blocked layout holds quantized states only; layout codes are 0 | 1
+    a = F.make_args(1, quantize_states=False)
+    a.state_layout = 1
+    assert _step(L, [blk()], a) == F.FLASHOPT_EINVAL
+    a = F.make_args(1)
+    a.state_layout = 2
+    assert _step(L, [_tensor()], a) == F.FLASHOPT_EINVAL
+    s = F.make_sgd_args(1)
+    s.state_layout = 2
+    arr = (F.flashopt_tensor * 1)(_tensor())
+    assert L.flashopt_sgd_step(arr, 1, ctypes.byref(s), A16, 1 << 20, None) == F.FLASHOPT_EINVAL
+    one = (F.flashopt_tensor * 1)(blk(rho=None))
+    assert L.flashopt_adamw_step_tensor(one, ctypes.byref(blocked), None) == F.FLASHOPT_EINVAL
+    # sizes: per 1024-element chunk, rho (1024 | 2048 | 0) + codes and scales
+    assert F.flashopt_blocked_state_bytes(1, 24) == 1024 + 2 * (1024 + 64)
+    assert F.flashopt_blocked_state_bytes(1025, 24) == 2 * 3200
+    assert F.flashopt_blocked_state_bytes(2048, 32) == 2 * (2048 + 2176)
+    assert F.flashopt_blocked_state_bytes(3000, None) == 3 * 2176
+    assert F.flashopt_blocked_state_bytes(1024, 24, variance=False) == 2176      # 2112 in 128-byte lines
+    assert F.flashopt_blocked_state_bytes(1024, 32, variance=False) == 3200      # 3136 likewise
+    assert F.flashopt_blocked_state_bytes(1024, None, variance=False) == 1152    # 1088 likewise
+    assert F.flashopt_blocked_state_bytes(0, 24) == 0
+    assert L.flashopt_blocked_state_bytes(10, 16, 1) == 0

@@ -16,18 +16,20 @@ from tests._gpu import require_gpu
 pytestmark = pytest.mark.gpu
 
 SIZES = [1, 33, 1000, 1024, 1025, 70001, 1 << 17]
-# (master_bits, companded, quantize_states, parameter dtype)
-VARIANTS = [(24, True, True, torch.bfloat16), (32, False, True, torch.bfloat16),
-            (None, True, False, torch.bfloat16), (None, True, True, torch.float32)]
-IDS = ["mb24-comp", "mb32-lin", "mbNone-f32states", "fp32params"]
+# (master_bits, companded, quantize_states, parameter dtype, state layout;
+# None: the binding's default, blocked for quantized states)
+VARIANTS = [(24, True, True, torch.bfloat16, None), (32, False, True, torch.bfloat16, None),
+            (None, True, False, torch.bfloat16, None), (None, True, True, torch.float32, None),
+            (24, True, True, torch.bfloat16, "streams")]
+IDS = ["mb24-comp", "mb32-lin", "mbNone-f32states", "fp32params", "mb24-comp-streams"]
 
 
 def _pair(variant, seed):
-    mb, comp, qs, dt = variant
+    mb, comp, qs, dt, layout = variant
     pa = [W.init_param(n, device="cuda", seed=seed + i, dtype=dt) for i, n in enumerate(SIZES)]
     pb = [p.clone() for p in pa]
     make = lambda ps: F.FlashAdamW(ps, master_bits=mb, companded=comp, quantize_states=qs,
-                                   **W.HP_DEFAULT)
+                                   state_layout=layout, **W.HP_DEFAULT)
     return make(pa), make(pb), dt
 
 
@@ -118,7 +120,7 @@ def test_plan_set_step_takes_new_hyper_parameters():
     base = {k: v for k, v in W.HP_DEFAULT.items() if k not in ("lr", "weight_decay")}
     info = None
     for t, (lr, wd) in enumerate(schedule, start=1):
-        args = F.make_args(t, lr=lr, weight_decay=wd, **base)
+        args = F.make_args(t, lr=lr, weight_decay=wd, state_layout=a.states[0].state_layout, **base)
         grads = [W.make_grad(n, t, device="cuda", stream_id=i) for i, n in enumerate(sizes)]
         F.flashopt_adamw_step(F.descriptor_array(a.states, grads), args, a.workspace(), None)
         for buf, g in zip(bufs, grads):
@@ -165,8 +167,9 @@ def test_decoder_8b_graph_replays_equal_list_steps():
 
 SGD_VARIANTS = [(24, True, True, dict(weight_decay=0.0)), (32, False, True, dict(weight_decay=0.01)),
                 (None, True, False, dict(nesterov=True, weight_decay=0.01)),
-                (24, True, True, dict(dampening=0.1))]
-SGD_IDS = ["mb24-comp", "mb32-lin-wd", "mbNone-f32-nesterov", "mb24-comp-dampening"]
+                (24, True, True, dict(dampening=0.1)),
+                (32, True, True, dict(weight_decay=0.01, state_layout="blocked"))]
+SGD_IDS = ["mb24-comp", "mb32-lin-wd", "mbNone-f32-nesterov", "mb24-comp-dampening", "mb32-comp-blocked"]
 
 
 def _sgd_pair(variant, seed):

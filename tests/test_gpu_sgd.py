@@ -90,14 +90,20 @@ def _orc_hp(t, hp, mb, comp, qs):
                               master_bits=mb, companded=comp, quantize_states=qs)
 
 
+# each storage variant in each state layout it has (blocked: quantized only)
+STORAGE_LAYOUTS = [(*v, l) for v in STORAGE for l in (("blocked", "streams") if v[2] else ("streams",))]
+
+
 @pytest.mark.parametrize("setting", sorted(SETTINGS))
-@pytest.mark.parametrize("mb,comp,qs", STORAGE, ids=[_sid(v) for v in STORAGE])
-def test_ragged_list(orc, mb, comp, qs, setting):
+@pytest.mark.parametrize("mb,comp,qs,layout", STORAGE_LAYOUTS,
+                         ids=[f"{_sid(v[:3])}-{v[3]}" for v in STORAGE_LAYOUTS])
+def test_ragged_list(orc, mb, comp, qs, layout, setting):
     require_gpu()
     hp = dict(HP, **SETTINGS[setting])
     params = [W.init_param(n, device="cuda", seed=200 + i) for i, n in enumerate(RAGGED)]
     want = _start(params, mb, qs)
-    opt = F.FlashSGD(params, master_bits=mb, companded=comp, quantize_states=qs, **hp)
+    opt = F.FlashSGD(params, master_bits=mb, companded=comp, quantize_states=qs,
+                     state_layout=layout, **hp)
     for t in range(1, 4):
         grads = [W.make_grad(n, t, device="cuda", stream_id=i, factor=float(np.exp(i - 6)))
                  for i, n in enumerate(RAGGED)]

@@ -84,14 +84,16 @@ def _compare(got: oracle.State, want: oracle.State, mb, label: str):
     assert (np.abs(a - b) <= 1e-6 * np.abs(b)).all(), f"{label}: master"
 
 
-def test_single_tensor_10_steps(orc):
+@pytest.mark.parametrize("layout", ["blocked", "streams"])
+def test_single_tensor_10_steps(orc, layout):
     """2^20 params, bf16 N(0, 0.02^2), grads N(0, 1e-3^2) fresh each step,
-    24-bit master, companded, lr 1e-3, betas (0.9, 0.999), eps 1e-8, wd 0.01."""
+    24-bit master, companded, lr 1e-3, betas (0.9, 0.999), eps 1e-8, wd 0.01;
+    the state in either layout."""
     require_gpu()
     n = 1 << 20
     p = W.init_param(n, device="cuda")
     (free,) = _start([p], 24)
-    opt = F.FlashAdamW([p], master_bits=24, companded=True, **HP)
+    opt = F.FlashAdamW([p], master_bits=24, companded=True, state_layout=layout, **HP)
     for t in range(1, 11):
         g = W.make_grad(n, t, device="cuda")
         opt.step([g])
@@ -141,12 +143,19 @@ def _vid(v):
     return f"mb{mb}-{'comp' if comp else 'lin'}-{'q' if qs else 'f32'}"
 
 
-@pytest.mark.parametrize("mb,comp,qs", VARIANTS, ids=[_vid(v) for v in VARIANTS])
-def test_ragged_list(orc, mb, comp, qs):
+# every variant in each state layout it has (the blocked layout holds
+# quantized states only)
+VARIANT_LAYOUTS = [(v, layout) for v in VARIANTS for layout in (("blocked", "streams") if v[2] else ("streams",))]
+
+
+@pytest.mark.parametrize("mb,comp,qs,layout", [(*v, l) for v, l in VARIANT_LAYOUTS],
+                         ids=[f"{_vid(v)}-{l}" for v, l in VARIANT_LAYOUTS])
+def test_ragged_list(orc, mb, comp, qs, layout):
     require_gpu()
     params = [W.init_param(n, device="cuda", seed=10 + i) for i, n in enumerate(RAGGED)]
     want = _start(params, mb, qs)
-    opt = F.FlashAdamW(params, master_bits=mb, companded=comp, quantize_states=qs, **HP)
+    opt = F.FlashAdamW(params, master_bits=mb, companded=comp, quantize_states=qs,
+                       state_layout=layout, **HP)
     for t in range(1, 4):
         grads = [W.make_grad(n, t, device="cuda", stream_id=i, factor=float(np.exp(i - 6)))
                  for i, n in enumerate(RAGGED)]
@@ -415,10 +424,11 @@ def test_deterministic_across_launch_splits():
             assert torch.equal(a, b)
 
 
-def _build_list(shapes, mb, comp, seed_base, qs=True):
+def _build_list(shapes, mb, comp, seed_base, qs=True, layout=None):
     params = [W.init_param(W.numel(s), device="cuda", seed=seed_base + i)
               for i, (_, s) in enumerate(shapes)]
-    return F.FlashAdamW(params, master_bits=mb, companded=comp, quantize_states=qs, **HP)
+    return F.FlashAdamW(params, master_bits=mb, companded=comp, quantize_states=qs,
+                        state_layout=layout, **HP)
 
 
 def _grads(shapes, t, factors):
@@ -436,11 +446,11 @@ def _sample_ranges(n, rng, k=2):
     return r
 
 
-def _sampled_parity(orc, shapes, mb, comp, label, qs=True):
+def _sampled_parity(orc, shapes, mb, comp, label, qs=True, layout=None):
     """Two list steps over the whole list; after each, every sample is
     compared with the oracle stepping that slice from the same seeded start
     (step 1 starts from zero moments, step 2 from non-trivial ones)."""
-    opt = _build_list(shapes, mb, comp, seed_base=1000, qs=qs)
+    opt = _build_list(shapes, mb, comp, seed_base=1000, qs=qs, layout=layout)
     factors = W.grad_factors(len(shapes)).numpy()
     rng = np.random.default_rng(7)
     ranges = [_sample_ranges(s.param.numel(), rng) for s in opt.states]
@@ -463,9 +473,11 @@ def _sampled_parity(orc, shapes, mb, comp, label, qs=True):
     torch.cuda.empty_cache()
 
 
-def test_decoder_1b_sampled(orc):
+@pytest.mark.parametrize("layout", ["blocked", "streams"])
+def test_decoder_1b_sampled(orc, layout):
     require_gpu()
-    _sampled_parity(orc, W.decoder_1b_shapes(), 24, True, "1.2B list, 24-bit")
+    _sampled_parity(orc, W.decoder_1b_shapes(), 24, True, f"1.2B list, 24-bit, {layout}",
+                    layout=layout)
 
 
 def test_decoder_1b_full(orc):
@@ -501,10 +513,12 @@ def test_decoder_1b_sampled_ablations(orc, mb, qs):
     _sampled_parity(orc, W.decoder_1b_shapes(), mb, True, f"1.2B list, mb {mb}, quantized {qs}", qs=qs)
 
 
-@pytest.mark.parametrize("mb,comp", [(24, True), (32, True), (24, False)])
-def test_decoder_8b_sampled(orc, mb, comp):
+@pytest.mark.parametrize("mb,comp,layout", [(24, True, "blocked"), (32, True, "blocked"),
+                                            (24, False, "blocked"), (24, True, "streams")])
+def test_decoder_8b_sampled(orc, mb, comp, layout):
     require_gpu()
-    _sampled_parity(orc, W.decoder_8b_shapes(), mb, comp, f"8.0B list, {mb}-bit, companded={comp}")
+    _sampled_parity(orc, W.decoder_8b_shapes(), mb, comp,
+                    f"8.0B list, {mb}-bit, companded={comp}, {layout}", layout=layout)
 
 
 @pytest.mark.parametrize("mb,qs", [(None, True), (24, False)], ids=["mb_none", "fp32_states"])
