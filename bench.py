@@ -23,16 +23,22 @@ single-tensor launch per tensor, the gradient-release launch pattern).
 Prints one JSON line: Gparam/s over the K timed steps, the roofline of the
 step kernel (algorithmic bytes per param of the configuration against
 8 TB/s), the oracle's throughput on host cores (the 1.2B list in full on all
-threads, and a sixteenth of it on one thread), and the GPU, CPU, ROCm and
-clock readings.
+threads, and a sixteenth of it on one thread), the GPU, CPU, ROCm and
+clock readings, and the board power and shader clock that sysfs reports
+while the same step runs for a few more (untimed) seconds after the timed
+steps.
 """
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
+import re
+import statistics
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -193,6 +199,97 @@ def _mhz(text):
         return float(str(text).lower().replace("mhz", "").strip())
     except (TypeError, ValueError):
         return None
+
+
+def _gpu_hwmon():
+    """(hwmon directory, DRM device directory) of the GPU torch calls device
+    0, matched by PCI domain and bus (or the only GPU with a power sensor);
+    (None, None) where sysfs does not show them."""
+    try:
+        prop = torch.cuda.get_device_properties(0)
+        want = (prop.pci_domain_id, prop.pci_bus_id)
+    except Exception:
+        want = None
+    found = []
+    for card in sorted(glob.glob("/sys/class/drm/card*")):
+        if not re.fullmatch(r"card\d+", os.path.basename(card)):
+            continue                            # connectors such as card0-DP-1
+        dev = os.path.join(card, "device")
+        mons = [m for m in sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*")))
+                if os.path.exists(os.path.join(m, "power1_input"))]
+        if not mons:
+            continue
+        parts = os.path.basename(os.path.realpath(dev)).split(":")   # "0000:75:00.0"
+        try:
+            key = (int(parts[0], 16), int(parts[1], 16))
+        except (ValueError, IndexError):
+            key = None
+        found.append((key, mons[0], dev))
+    for key, mon, dev in found:
+        if want is not None and key == want:
+            return mon, dev
+    return (found[0][1], found[0][2]) if len(found) == 1 else (None, None)
+
+
+def _read_sclk(dev):
+    """The shader clock level marked current in pp_dpm_sclk, in MHz."""
+    try:
+        with open(os.path.join(dev, "pp_dpm_sclk")) as f:
+            for line in f:
+                if "*" in line:
+                    return _mhz(line.split(":", 1)[1].replace("*", ""))
+    except OSError:
+        pass
+    return None
+
+
+def power_during(run, seconds: float):
+    """Board power (hwmon power1_input) and shader clock (pp_dpm_sclk),
+    sampled every 20 ms from sysfs while run() is called for `seconds`
+    (each call runs a few more steps and returns their per-launch ms); the
+    first second is dropped as the ramp.  None where sysfs has no power
+    sensor for the GPU."""
+    mon, dev = _gpu_hwmon()
+    if mon is None or seconds <= 0:
+        return None
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                with open(os.path.join(mon, "power1_input")) as f:
+                    w = int(f.read()) / 1e6             # microwatts
+                samples.append((time.perf_counter(), w, _read_sclk(dev)))
+            except (OSError, ValueError):
+                pass
+            stop.wait(0.02)
+
+    th = threading.Thread(target=sample, daemon=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    th.start()
+    per = []
+    while time.perf_counter() - t0 < seconds:
+        per.extend(run())
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stop.set()
+    th.join()
+    sel = [x for x in samples if t0 + min(1.0, seconds / 3) <= x[0] <= t1]
+    if not sel:
+        return None
+    cap = None
+    try:
+        with open(os.path.join(mon, "power1_cap")) as f:
+            cap = int(f.read()) / 1e6
+    except (OSError, ValueError):
+        pass
+    clk = [x[2] for x in sel if x[2]]
+    return {"board_w": statistics.mean(x[1] for x in sel), "board_w_max": max(x[1] for x in sel),
+            "cap_w": cap, "sclk_mhz": statistics.mean(clk) if clk else None,
+            "seconds": t1 - t0, "samples": len(sel),
+            "ms_per_launch_median": statistics.median(per) if per else None,
+            "source": "sysfs hwmon power1_input and pp_dpm_sclk, every 20 ms"}
 
 
 def time_steps(opt, grads, steps: int, warmup: int, per_tensor: bool = False,
@@ -479,6 +576,9 @@ def main():
     ap.add_argument("--calibrate-copy", type=float, default=0.0, metavar="GIB",
                     help="only run one device copy of GIB GiB (for counter scaling) and exit")
     ap.add_argument("--no-copy-ref", action="store_true")
+    ap.add_argument("--power-seconds", type=float, default=3.0,
+                    help="after the timed steps, run the step this many more seconds while "
+                         "sampling board power and shader clock (0: skip)")
     ap.add_argument("--codec", action="store_true",
                     help="instead of the step, time the codec and split entry points on one "
                          "flat tensor (one JSON line each)")
@@ -523,6 +623,12 @@ def main():
     env = environment()                     # clocks read right after the timed steps
     ms_step = wall * 1e3 / args.steps
     ms_launch = float(np.mean(per))
+    power = None
+    if not args.graph and "rocprof" not in os.environ.get("LD_PRELOAD", ""):
+        k = max(1, min(500, int(200.0 / max(ms_launch, 1e-3))))
+        power = power_during(lambda: time_steps(opt, grads, k, 0, args.grad_release,
+                                                args.batch_below, args.release_streams)[1],
+                             args.power_seconds)
     bpp = bytes_per_param(mb, qs, 1 if args.optimizer == "sgd" else 2, 4 if args.param_fp32 else 2)
     alg_bytes = bpp * n
     achieved = alg_bytes / (ms_launch * 1e-3) / 1e9
@@ -583,6 +689,7 @@ def main():
         "valu_roofline": valu_roofline(ms_launch, _mhz(env.get("clocks", {}).get("sclk")))
                          if default else None,
         "cpu_baseline": cpu,
+        "power": power,
         "env": env,
     }
     print(json.dumps(out), flush=True)

@@ -220,7 +220,7 @@ flashopt_status adamw_scalars(const flashopt_adamw_args *a, StepScalars &sc)
         }
         sc.rbc1 = r;
     }
-    sc.unit_bc = (sc.bc1 == 1.0f && sc.bc2 == 1.0f) ? 1 : 0;
+    sc.unit_bc = (sc.bc1 == 1.0f ? 1 : 0) | (sc.bc2 == 1.0f ? 2 : 0);
     sc.lr2 = sc.lr * 0x1p32f;
     sc.eps2 = sc.eps * 0x1p32f;
     sc.kv = static_cast<float>(255.0 * std::sqrt(static_cast<double>(sc.bc2)) * 0x1p-32);

@@ -72,7 +72,7 @@ struct StepScalars {
     uint32_t v1_bound;  // v1 bit patterns below this keep vhat below 2^63
     uint32_t num_key;   // (pattern << 1) - 1 of the smallest nonzero |lr mhat 2^32| allowed
     int fast;           // 1 when eps and lr keep the short routes exact (see adamw_scalars)
-    int unit_bc;        // 1 when bc1 and bc2 are both exactly 1 (late in training)
+    int unit_bc;        // bit 0: bc1 is exactly 1, bit 1: bc2 is exactly 1 (later in training)
     StateLayout blk;    // the state layout
 };
 // The list step kernels (AdamW and FlashSGD) read their scalars from device

@@ -1156,6 +1156,33 @@ __device__ __forceinline__ void load_chunk_unit(const ChunkPtrs &c, int u, int l
     }
 }
 
+// The short route's update terms of one unit of one lane: th1 = thd -
+// (lr2 mhat) / (sq + eps2) with sq = sqrt(vhat) 2^32, and the smallest key
+// of the nonzero numerators (see step_finish).  Once a bias correction
+// rounds to 1 in fp32, dividing by it is exact: BC1 takes mhat = m1 (from
+// t = 165 with beta1 = 0.9), BC2 vhat = v1 (from t = 17321 with beta2 =
+// 0.999; the short sqrt then takes v1 itself, subnormal values included).
+// The BC1-only form converts v1 to fp64 opaquely: it then keeps its own
+// copy of the quotient's sqrt, where the compiler would otherwise share the
+// general form's and hold 16 more VGPRs (one wavefront per SIMD fewer).
+template <int N, bool BC1, bool BC2>
+__device__ __forceinline__ void update_terms(const float (&m1)[N], const float (&v1)[N],
+                                             const float (&thd)[N], const StepScalars &sc,
+                                             float (&th1)[N], float (&sq)[N], uint32_t &kmin)
+{
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        const float mhat = BC1 ? m1[j] : math::div_markstein(m1[j], sc.bc1, sc.rbc1);
+        sq[j] = BC2 ? math::sqrt_x2p32_zero_tiny(v1[j])
+                    : math::sqrt_quot_x2p32<BC1>(v1[j], sc.inv_bc2s);
+        const float den = sq[j] + sc.eps2;
+        const float num = sc.lr2 * mhat;
+        th1[j] = thd[j] - math::div_markstein(num, den, math::recip_cr(den));
+        const uint32_t key = (__float_as_uint(num) << 1) - 1u;
+        kmin = key < kmin ? key : kmin;
+    }
+}
+
 // The rest of one unit of one lane, from its loaded inputs: dequantize m and
 // v (or read them as fp32), rebuild the master (or widen the bf16
 // parameter), apply AdamW, find the group maxima (DPP exchanges among the
@@ -1213,31 +1240,9 @@ __device__ __forceinline__ void step_finish(const ChunkPtrs &c, uint32_t r, int 
     // unscaled product lr mhat is normal, so scaling it was exact)
     uint32_t kmin = 0xFFFFFFFFu;          // min over nonzero |num| of its doubled pattern - 1
     float th1[N], sq[N];
-    if (sc.unit_bc) {
-        // late in training both bias corrections round to 1 in fp32, and
-        // dividing by 1 is exact: mhat = m1, vhat = v1 (the short sqrt takes
-        // v1 itself, subnormal values included)
-#pragma unroll
-        for (int j = 0; j < N; ++j) {
-            sq[j] = math::sqrt_x2p32_zero_tiny(v1[j]);
-            const float den = sq[j] + sc.eps2;
-            const float num = sc.lr2 * m1[j];
-            th1[j] = thd[j] - math::div_markstein(num, den, math::recip_cr(den));
-            const uint32_t key = (__float_as_uint(num) << 1) - 1u;
-            kmin = key < kmin ? key : kmin;
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < N; ++j) {
-            const float mhat = math::div_markstein(m1[j], sc.bc1, sc.rbc1);
-            sq[j] = math::sqrt_quot_x2p32(v1[j], sc.inv_bc2s);
-            const float den = sq[j] + sc.eps2;
-            const float num = sc.lr2 * mhat;
-            th1[j] = thd[j] - math::div_markstein(num, den, math::recip_cr(den));
-            const uint32_t key = (__float_as_uint(num) << 1) - 1u;
-            kmin = key < kmin ? key : kmin;
-        }
-    }
+    if (sc.unit_bc == 3) update_terms<N, true, true>(m1, v1, thd, sc, th1, sq, kmin);
+    else if (sc.unit_bc & 1) update_terms<N, true, false>(m1, v1, thd, sc, th1, sq, kmin);
+    else update_terms<N, false, false>(m1, v1, thd, sc, th1, sq, kmin);
     // NaN-propagating maximum (v_maximum3_f32): NaN iff some th1 is NaN
     float tnan = th1[0];
 #pragma unroll

@@ -200,9 +200,16 @@ __device__ __forceinline__ float sqrt_x2p32_zero_tiny(float x)
 // q is subnormal or zero, xs <= 2^-62 (2^-126 for v = 0, a normal number,
 // which keeps v_rsq_f32 finite: it flushes subnormal inputs) and the result
 // is below 2^-31 rather than q's exact root.  Domain: q < 2^63.
+// OPAQUE: the (exact) conversion of v to fp64 is written as inline
+// assembly, which the compiler neither merges with nor moves across other
+// code; the arithmetic is the same.
+template <bool OPAQUE = false>
 __device__ __forceinline__ float sqrt_quot_x2p32(float v, double inv_s)
 {
-    const float xs = static_cast<float>(__builtin_fma(static_cast<double>(v), inv_s, 0x1p-126));
+    double vd;
+    if (OPAQUE) asm("v_cvt_f64_f32 %0, %1" : "=v"(vd) : "v"(v));
+    else vd = static_cast<double>(v);
+    const float xs = static_cast<float>(__builtin_fma(vd, inv_s, 0x1p-126));
     const float y = __builtin_amdgcn_rsqf(xs);
     const float s = xs * y;
     const float h = 0.5f * y;

@@ -254,7 +254,8 @@ __global__ void k_div_bias(unsigned long long *bad)
 // sqrt_quot_x2p32 for 16 bias-correction divisors (bias_divisor: t = 1, 2,
 // 3, 512 of four betas) over every v pattern in [0, 2^64): where fl(v / b) is
 // normal and below 2^63 it must equal sqrt_cr_x2p32(fl(v / b)); where the
-// quotient is zero or subnormal it must be finite and below 2^-31.
+// quotient is zero or subnormal it must be finite and below 2^-31.  The
+// form with the opaque conversion must give the same bits everywhere.
 __global__ void k_sqrt_quot(unsigned long long *bad)
 {
     unsigned long long c = 0;
@@ -267,6 +268,7 @@ __global__ void k_sqrt_quot(unsigned long long *bad)
         const float q = v / b;
         if (!(q < 0x1p63f)) continue;
         const float got = sqrt_quot_x2p32(v, 0x1p64 / (double)b);
+        c += !same(got, sqrt_quot_x2p32<true>(v, 0x1p64 / (double)b));
         if (q >= 0x1p-126f) c += !same(got, sqrt_cr_x2p32(q));
         else c += !(got >= 0.0f && got < 0x1p-31f);
     }

@@ -178,6 +178,7 @@ HP_GRID = [
     ("beta2_0.9999", dict(betas=(0.5, 0.9999)), 1),
     ("step_1e6", dict(betas=(0.95, 0.99)), 1_000_000),
     ("step_100", dict(), 100),
+    ("step_163", dict(), 163),         # 1 - 0.9^t reaches 1 in fp32 at t = 165
     ("step_17320", dict(), 17320),     # 1 - 0.999^t reaches 1 in fp32 at t = 17321
     ("lr_1_wd_0.1", dict(lr=1.0, weight_decay=0.1), 1),
     ("lr_1e-6_wd_0", dict(lr=1e-6, weight_decay=0.0), 5),
