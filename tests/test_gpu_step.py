@@ -362,7 +362,10 @@ EDGE_HP = {"tiny_at_lr_bound": dict(betas=(0.9999, 0.999), lr=6e-3)}
 @pytest.mark.parametrize("mb,comp,qs", [(24, True, True), (32, False, True), (None, True, False)],
                          ids=["mb24-comp", "mb32-lin", "mbnone-f32"])
 @pytest.mark.parametrize("case", sorted(EDGE_EPS))
-def test_lanes_outside_short_division_domain(orc, case, mb, comp, qs):
+# from step 1 (both quotients), 200 (bc1 = 1 with beta1 = 0.9) and 20001
+# (both bias corrections 1): the three forms of the short route
+@pytest.mark.parametrize("t0", [1, 200, 20001], ids=["t1", "t200", "t20001"])
+def test_lanes_outside_short_division_domain(orc, case, mb, comp, qs, t0):
     """Lanes whose numerators or denominators leave the range where the
     kernel's short division is exact, or whose values are not finite, take
     the generic path; their neighbours in the same group do not.  Both must
@@ -373,7 +376,8 @@ def test_lanes_outside_short_division_domain(orc, case, mb, comp, qs):
     p = W.init_param(n, device="cuda", seed=90)
     (want,) = _start([p], mb, qs)
     opt = F.FlashAdamW([p], master_bits=mb, companded=comp, quantize_states=qs, **hp)
-    for t in range(1, 4):
+    opt.t = t0 - 1
+    for t in range(t0, t0 + 3):
         g = _edge_grad(case, n, t)
         opt.step([g])
         torch.cuda.synchronize()
