@@ -146,9 +146,10 @@ flashopt_status flashopt_reconstruct(const uint16_t *param_bf16, const void *rho
  *   m scales 32 fp16 (64 bytes)
  *   v scales 32 fp16 (64 bytes)              (AdamW only)
  * (flashopt_blocked_state_bytes gives the buffer size).  Bytes past numel in
- * the last block are neither read nor written.  The step reads and writes
- * three streams per element instead of six; the arithmetic and every stored
- * value are the same.  Quantized states only (not with fp32_states). */
+ * the last block are neither read nor written.  The step then reads and
+ * writes three regions per chunk (parameter, gradient, state block) instead
+ * of seven arrays; the arithmetic and every stored value are the same.
+ * Quantized states only (not with fp32_states). */
 enum {
     FLASHOPT_STATE_STREAMS = 0,
     FLASHOPT_STATE_BLOCKED = 1
