@@ -1,9 +1,12 @@
-"""Host-side parts of bench.py (CPU only): the sysfs power and clock
-readers against a synthetic sysfs tree, and the one-GPU guard."""
+"""Host-side parts of bench.py: the sysfs power and clock readers against a
+synthetic sysfs tree and the one-GPU guard (CPU), and the readers on a GPU
+host (gpu)."""
 import os
 import subprocess
 import sys
 import time
+
+import pytest
 
 import bench
 
@@ -50,3 +53,27 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+@pytest.mark.gpu
+def test_power_during_on_the_gpu():
+    """On a GPU host the sensor of device 0 is found (where sysfs shows it)
+    and reads a plausible board power and shader clock while a kernel runs."""
+    if not bench.torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    x = bench.torch.empty(1 << 26, device="cuda")
+
+    def run():
+        for _ in range(20):
+            x.neg_()
+        bench.torch.cuda.synchronize()
+        return [1.0]
+
+    p = bench.power_during(run, 1.5)
+    mon, _ = bench._gpu_hwmon()
+    if mon is None:
+        assert p is None
+        return
+    assert p is not None and p["samples"] > 0
+    assert 50.0 < p["board_w"] <= (p["cap_w"] or 5000.0) * 1.1
+    assert p["sclk_mhz"] is None or 50.0 <= p["sclk_mhz"] <= 3000.0
